@@ -1,0 +1,123 @@
+"""Reference dequantization and W4A16 linear (oracle; test infrastructure only).
+
+What the method computes ("native MXFP4 keep-quant", vllm.cpp PR #38, commit
+list: the device W4A16 GEMM is checked against an independent CPU dequant to
+f32 followed by an f32 matmul; "keep the ModelOpt NVFP4 lm_head packed",
+vllm.cpp PR #263, section "Why this row matters": the packed weight is
+consumed directly by a W4A16 GEMM):
+
+  w[n, k] = fl32( fl32( E2M1(code[n, k]) * S(n, k // g) ) * G )
+  y[m, n] = sum_k x[m, k] * w[n, k]
+
+with code[n, k] the nibble (k & 1) of byte W[n, k >> 1] (low nibble first),
+S the decoded block scale (E4M3FN for NVFP4, g = 16; E8M0 for MXFP4, g = 32),
+G the float32 global scale for NVFP4 (a multiplier, as in "re-verify 27B NVFP4
+on the nvidia ModelOpt checkpoint", vllm.cpp PR #178, section "Layer 3 -
+ModelOpt NVFP4 naming") and 1 for MXFP4 (no global scale, "native MXFP4
+keep-quant", commit list).  x is bf16, widened exactly to float.
+
+Readings taken where the pages are silent:
+* The multiplication order is (E2M1 * S) * G: the first product is exact, the
+  second rounds once to float32.
+* The sum over k is taken in float64 here (each product of two float32 values
+  is exact in float64); the GPU result is compared against it with the
+  tolerance |y - y_ref| <= 2^-7 |y_ref| + 1e-3 rms(y_ref).
+* The fused gate_up output is [gate(x) | up(x)] along the output dimension
+  ("MXFP4 decode-graph + gate_up FUSION default-ON", vllm.cpp PR #54, step 2),
+  each half with its own global scale for NVFP4.
+"""
+
+import math
+
+import numpy as np
+
+from .formats import E2M1_TABLE, E4M3FN_TABLE, E8M0_TABLE
+
+FMT_NVFP4 = 0
+FMT_MXFP4 = 1
+GROUP = {FMT_NVFP4: 16, FMT_MXFP4: 32}
+
+
+def bf16_bits_to_f32(bits):
+    """Widen bf16 bit patterns (uint16) to float32: the bf16 bits are the top half."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 to bf16 (round to nearest, ties to even), returning uint16 bits.
+
+    bf16 keeps float32's sign and exponent and the top 7 mantissa bits; the
+    dropped 16 bits decide the rounding.  NaN stays a (quiet) NaN.
+    """
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = x.view(np.uint32).astype(np.uint64)
+    upper = u >> np.uint64(16)
+    lower = u & np.uint64(0xFFFF)
+    round_up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & np.uint64(1)) == 1))
+    out = upper + round_up.astype(np.uint64)
+    nan = np.isnan(x)
+    out = np.where(nan, (upper | np.uint64(0x40)), out)
+    return out.astype(np.uint16)
+
+
+def unpack_codes(packed, k):
+    """Packed bytes [N, K/2] -> codes [N, K]; element 2j is the low nibble of byte j."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    n = packed.shape[0]
+    codes = np.empty((n, k), dtype=np.uint8)
+    codes[:, 0::2] = packed & 0x0F
+    codes[:, 1::2] = packed >> 4
+    return codes
+
+
+def _scale_values(scales, fmt):
+    table = E4M3FN_TABLE if fmt == FMT_NVFP4 else E8M0_TABLE
+    return table[np.asarray(scales, dtype=np.uint8)]
+
+
+def dequantize(packed, scales, k, fmt, global_scale=1.0):
+    """Dequantized float32 weights [N, K]: fl32(fl32(E2M1 * S) * G)."""
+    if fmt not in GROUP:
+        raise ValueError("unknown format")
+    g = GROUP[fmt]
+    codes = unpack_codes(packed, k)
+    elem = E2M1_TABLE[codes]                                    # float32
+    s = np.repeat(_scale_values(scales, fmt), g, axis=1)[:, :k]  # scale of element k is S[k // g]
+    gs = np.float32(global_scale) if fmt == FMT_NVFP4 else np.float32(1.0)
+    with np.errstate(over="ignore", invalid="ignore", under="ignore"):
+        prod = (elem * s).astype(np.float32)
+        return (prod * gs).astype(np.float32)
+
+
+def linear(x, packed, scales, k, fmt, global_scale=1.0):
+    """y = x @ w.T with x float32 [M, K] (bf16 values), w from ``dequantize``; float64 result."""
+    x = np.asarray(x, dtype=np.float32)
+    w = dequantize(packed, scales, k, fmt, global_scale)
+    return x.astype(np.float64) @ w.astype(np.float64).T
+
+
+def linear_rows(x, packed, scales, k, fmt, global_scale, rows):
+    """y[:, rows] only: dequantizes just the selected output rows of W (for sampled checks)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return linear(x, np.asarray(packed)[rows], np.asarray(scales)[rows], k, fmt, global_scale)
+
+
+def gate_up(x, packed_gate, scales_gate, packed_up, scales_up, k, fmt,
+            global_gate=1.0, global_up=1.0):
+    """Fused gate_up reference: [linear(x, gate) | linear(x, up)] along the output axis."""
+    yg = linear(x, packed_gate, scales_gate, k, fmt, global_gate)
+    yu = linear(x, packed_up, scales_up, k, fmt, global_up)
+    return np.concatenate([yg, yu], axis=1)
+
+
+def linear_f64_bruteforce(x, packed, scales, k, fmt, global_scale=1.0):
+    """Sequential, correctly rounded dot products (math.fsum of exact products); tiny inputs only."""
+    x = np.asarray(x, dtype=np.float32)
+    w = dequantize(packed, scales, k, fmt, global_scale)
+    m, n = x.shape[0], w.shape[0]
+    y = np.zeros((m, n), dtype=np.float64)
+    for i in range(m):
+        for j in range(n):
+            y[i, j] = math.fsum(float(x[i, t]) * float(w[j, t]) for t in range(k))
+    return y
