@@ -1,0 +1,221 @@
+"""Python binding of libfp4w4a16: W4A16 FP4 weight-only linear layers on MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI declared in include/fp4w4a16.h; every
+function here has the name of the C entry point it calls.  PyTorch supplies
+device memory and the current HIP stream; all computation happens in the
+library's HIP kernels.  There is no fallback: if the library cannot be loaded,
+or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+FMT_NVFP4 = 0
+FMT_MXFP4 = 1
+GROUP = {FMT_NVFP4: 16, FMT_MXFP4: 32}
+
+FP4_OK = 0
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4w4a16.so")
+
+
+class Fp4Error(RuntimeError):
+    """A libfp4w4a16 call returned an error status."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (fn, fp4_status_string(status), status))
+
+
+class fp4_dispatch_info(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("splits", ctypes.c_int), ("grid_x", ctypes.c_int),
+                ("grid_y", ctypes.c_int), ("block", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i = ctypes.c_int
+_f = ctypes.c_float
+_SIGNATURES = {
+    "fp4_prepared_bytes": (_i, [_i, _i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "fp4_prepare": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "fp4_prepare_gate_up": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "fp4_workspace_bytes": (_i, [_i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "fp4_w4a16_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _i, _vp, _vp, _sz, _vp,
+                              ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_w4a16_gate_up": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _f, _i, _vp, _vp, _sz, _vp,
+                               ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_dequantize": (_i, [_vp, _vp, _i, _i, _f, _i, _vp, _vp]),
+    "fp4_status_string": (ctypes.c_char_p, [_i]),
+}
+
+_lib = None
+
+
+def load_library():
+    """Load (building first only if no library exists) libfp4w4a16.so and declare its symbols."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def fp4_status_string(status):
+    return load_library().fp4_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != FP4_OK:
+        raise Fp4Error(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor on the GPU" % (name, dtype))
+
+
+def fp4_prepared_bytes(n, k, fmt):
+    """(code_bytes, scale_bytes) of a prepared weight of n rows and k columns."""
+    cb, sb = _sz(), _sz()
+    _check("fp4_prepared_bytes", load_library().fp4_prepared_bytes(n, k, fmt, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def fp4_workspace_bytes(m, n, k, fmt, projections=1):
+    out = _sz()
+    _check("fp4_workspace_bytes", load_library().fp4_workspace_bytes(m, n, k, fmt, projections, ctypes.byref(out)))
+    return out.value
+
+
+def fp4_prepare(codes, scales, n, k, fmt, prep_codes=None, prep_scales=None, stream=None):
+    """Repack canonical codes uint8 [n, k/2] and scales uint8 [n, k/g] into the prepared layout."""
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if codes.numel() != n * (k // 2) or scales.numel() != n * (k // GROUP[fmt]):
+        raise ValueError("codes / scales do not have the canonical [n, k/2] / [n, k/g] sizes")
+    cb, sb = fp4_prepared_bytes(n, k, fmt)
+    if prep_codes is None:
+        prep_codes = torch.empty(cb, dtype=torch.uint8, device=codes.device)
+    if prep_scales is None:
+        prep_scales = torch.empty(sb, dtype=torch.uint8, device=codes.device)
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    if prep_codes.numel() < cb or prep_scales.numel() < sb:
+        raise ValueError("prepared buffers too small")
+    _check("fp4_prepare", load_library().fp4_prepare(_ptr(codes), _ptr(scales), n, k, fmt, _ptr(prep_codes),
+                                                     _ptr(prep_scales), _stream(stream)))
+    return prep_codes, prep_scales
+
+
+def fp4_prepare_gate_up(gate_codes, gate_scales, up_codes, up_scales, n_half, k, fmt,
+                        prep_codes=None, prep_scales=None, stream=None):
+    """Prepare the fused [gate; up] weight (gate rows, then up rows)."""
+    for t, nm in ((gate_codes, "gate_codes"), (gate_scales, "gate_scales"), (up_codes, "up_codes"),
+                  (up_scales, "up_scales")):
+        _need(t, torch.uint8, nm)
+    if gate_codes.numel() != n_half * (k // 2) or up_codes.numel() != n_half * (k // 2):
+        raise ValueError("gate / up codes do not have the canonical [n_half, k/2] size")
+    if gate_scales.numel() != n_half * (k // GROUP[fmt]) or up_scales.numel() != n_half * (k // GROUP[fmt]):
+        raise ValueError("gate / up scales do not have the canonical [n_half, k/g] size")
+    cb, sb = fp4_prepared_bytes(n_half, k, fmt)
+    if prep_codes is None:
+        prep_codes = torch.empty(2 * cb, dtype=torch.uint8, device=gate_codes.device)
+    if prep_scales is None:
+        prep_scales = torch.empty(2 * sb, dtype=torch.uint8, device=gate_codes.device)
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    if prep_codes.numel() < 2 * cb or prep_scales.numel() < 2 * sb:
+        raise ValueError("prepared buffers too small")
+    _check("fp4_prepare_gate_up", load_library().fp4_prepare_gate_up(
+        _ptr(gate_codes), _ptr(gate_scales), _ptr(up_codes), _ptr(up_scales), n_half, k, fmt,
+        _ptr(prep_codes), _ptr(prep_scales), _stream(stream)))
+    return prep_codes, prep_scales
+
+
+def _linear_common(x, n_out, workspace, ws_need, y):
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m, k]")
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n_out), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y")
+    if y.numel() != m * n_out:
+        raise ValueError("y must hold m x n values")
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return m, y, workspace, ws_bytes
+
+
+def fp4_w4a16_linear(x, prep_codes, prep_scales, n, global_scale, fmt, y=None, workspace=None,
+                     stream=None, info=None):
+    """y = x @ w.T for bf16 x [m, k] and a prepared FP4 weight of n rows; returns y bf16 [m, n].
+
+    ``info``, if given, is an fp4_dispatch_info filled with the kernel choice.
+    """
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    k = x.shape[1]
+    cb, sb = fp4_prepared_bytes(n, k, fmt)
+    if prep_codes.numel() < cb or prep_scales.numel() < sb:
+        raise ValueError("prepared buffers smaller than fp4_prepared_bytes(n, k, fmt)")
+    m, y, workspace, ws_bytes = _linear_common(x, n, workspace, fp4_workspace_bytes(x.shape[0], n, k, fmt, 1), y)
+    _check("fp4_w4a16_linear", load_library().fp4_w4a16_linear(
+        _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n, float(global_scale), fmt, _ptr(y),
+        _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
+    return y
+
+
+def fp4_w4a16_gate_up(x, prep_codes, prep_scales, n_half, global_gate, global_up, fmt, y=None,
+                      workspace=None, stream=None, info=None):
+    """Fused gate_up: returns bf16 [m, 2*n_half] = [x @ gate.T | x @ up.T]."""
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    k = x.shape[1]
+    cb, sb = fp4_prepared_bytes(n_half, k, fmt)
+    if prep_codes.numel() < 2 * cb or prep_scales.numel() < 2 * sb:
+        raise ValueError("prepared buffers smaller than twice fp4_prepared_bytes(n_half, k, fmt)")
+    m, y, workspace, ws_bytes = _linear_common(
+        x, 2 * n_half, workspace, fp4_workspace_bytes(x.shape[0], n_half, k, fmt, 2), y)
+    _check("fp4_w4a16_gate_up", load_library().fp4_w4a16_gate_up(
+        _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n_half, float(global_gate), float(global_up), fmt,
+        _ptr(y), _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
+    return y
+
+
+def fp4_dequantize(prep_codes, prep_scales, n, k, global_scale, fmt, out=None, stream=None):
+    """Dequantize a prepared weight to float32 [n, k] with the kernels' decoders."""
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=prep_codes.device)
+    _need(out, torch.float32, "out")
+    _check("fp4_dequantize", load_library().fp4_dequantize(
+        _ptr(prep_codes), _ptr(prep_scales), n, k, float(global_scale), fmt, _ptr(out), _stream(stream)))
+    return out

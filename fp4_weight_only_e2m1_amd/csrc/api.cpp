@@ -1,0 +1,228 @@
+// C ABI of the W4A16 FP4 linear library: argument checks, dispatch on m, and
+// workspace sizing.  Every check runs on the host before any launch, so an
+// invalid call enqueues nothing; no HIP runtime call happens before the
+// arguments are known to be good.  The library keeps no global state.
+//
+// Rejecting what it cannot run, instead of falling through to some other
+// path, follows the pages' lessons: an unknown scale layout is rejected rather
+// than read silently wrong ("re-verify 27B NVFP4 on the nvidia ModelOpt
+// checkpoint", section "Layer 2 - FP8 tower tensors"), and an impossible
+// weight state aborts instead of quietly rebuilding ("keep the ModelOpt NVFP4
+// lm_head packed", section "Round-3 findings resolved", item 4).
+#include "../../include/fp4w4a16.h"
+
+#include "fp4_common.hpp"
+
+namespace {
+
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_fmt(int fmt) { return (fmt == FP4_FMT_NVFP4 || fmt == FP4_FMT_MXFP4) ? FP4_OK : FP4_EFMT; }
+
+int check_nk(int n, int k) {
+  if (n < 1 || n > FP4_MAX_N) return FP4_EINVAL;
+  if (k < 32 || k > FP4_MAX_K || (k % 32) != 0) return FP4_EINVAL;
+  return FP4_OK;
+}
+
+int check_m(int m) { return (m < 0 || m > FP4_MAX_M) ? FP4_EINVAL : FP4_OK; }
+
+size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
+  if (m < 1 || m > fp4::kGemvMaxM) return 0;
+  const int splits = fp4::gemv_splits(n_proj, k, fmt);
+  if (splits <= 1) return 0;
+  const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
+  return static_cast<size_t>(splits) * static_cast<size_t>(m) * static_cast<size_t>(rows_total) * sizeof(float);
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_EHIP; }
+
+// Shared body of fp4_w4a16_linear and fp4_w4a16_gate_up.
+int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_t* scales, int n_proj,
+               int projections, const float* gscales, int fmt, uint16_t* y, void* ws, size_t ws_bytes,
+               hipStream_t stream, fp4_dispatch_info* info) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n_proj, k))) return st;
+  if ((st = check_m(m))) return st;
+  if (static_cast<int64_t>(n_proj) * projections > FP4_MAX_N) return FP4_EINVAL;
+  if (m == 0) {
+    if (info) *info = fp4_dispatch_info{m <= fp4::kGemvMaxM ? 0 : 1, 0, 0, 0, 0};
+    return FP4_OK;
+  }
+  if (!x || !codes || !scales || !y) return FP4_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y)) return FP4_EALIGN;
+  const size_t need = workspace_for(m, n_proj, k, fmt, projections);
+  if (need > 0) {
+    if (ws_bytes < need) return FP4_EWORKSPACE;
+    if (!ws) return FP4_EINVAL;
+    if (!aligned16(ws)) return FP4_EALIGN;
+  }
+
+  const fp4::PreparedShape ps = fp4::prepared_shape(n_proj, k, fmt);
+  const bool mx = fmt == FP4_FMT_MXFP4;
+  dim3 grid, block;
+  if (m <= fp4::kGemvMaxM) {
+    fp4::GemvArgs a{};
+    a.x = x;
+    a.codes = codes;
+    a.scales = scales;
+    a.y = y;
+    a.partial = static_cast<float*>(ws);
+    a.m = m;
+    a.k = k;
+    a.k_pad = ps.k_pad;
+    a.kgroups = ps.kgroups;
+    a.nslab = static_cast<int>(ps.k_pad / fp4::kSlabK);
+    a.splits = fp4::gemv_splits(n_proj, k, fmt);
+    a.n_proj = n_proj;
+    a.n_proj_pad = ps.n_pad;
+    a.projections = projections;
+    a.rows_total = ps.n_pad * projections;
+    a.ldy = static_cast<int64_t>(n_proj) * projections;
+    a.gscale[0] = mx ? 1.0f : gscales[0];
+    a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
+    hipError_t e = fp4::launch_gemv(a, fmt, stream, &grid, &block);
+    if (e != hipSuccess) return FP4_EHIP;
+    if (a.splits > 1) {
+      fp4::ReduceArgs r{};
+      r.partial = a.partial;
+      r.y = y;
+      r.m = m;
+      r.splits = a.splits;
+      r.n_proj = n_proj;
+      r.n_proj_pad = ps.n_pad;
+      r.rows_total = a.rows_total;
+      r.ldy = a.ldy;
+      r.projections = projections;
+      r.gscale[0] = a.gscale[0];
+      r.gscale[1] = a.gscale[1];
+      e = fp4::launch_reduce(r, stream);
+      if (e != hipSuccess) return FP4_EHIP;
+    }
+    if (info) *info = fp4_dispatch_info{0, a.splits, static_cast<int>(grid.x), static_cast<int>(grid.y),
+                                        static_cast<int>(block.x)};
+  } else {
+    fp4::MfmaArgs a{};
+    a.x = x;
+    a.codes = codes;
+    a.scales = scales;
+    a.y = y;
+    a.m = m;
+    a.k = k;
+    a.k_pad = ps.k_pad;
+    a.kgroups = ps.kgroups;
+    a.n_proj = n_proj;
+    a.n_proj_pad = ps.n_pad;
+    a.projections = projections;
+    a.rows_total = ps.n_pad * projections;
+    a.ldy = static_cast<int64_t>(n_proj) * projections;
+    a.gscale[0] = mx ? 1.0f : gscales[0];
+    a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
+    hipError_t e = fp4::launch_mfma(a, fmt, stream, &grid, &block);
+    if (e != hipSuccess) return FP4_EHIP;
+    if (info) *info = fp4_dispatch_info{1, 1, static_cast<int>(grid.x), static_cast<int>(grid.y),
+                                        static_cast<int>(block.x)};
+  }
+  return FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4_prepared_bytes(int n, int k, int fmt, size_t* code_bytes_out, size_t* scale_bytes_out) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if (!code_bytes_out || !scale_bytes_out) return FP4_EINVAL;
+  const fp4::PreparedShape s = fp4::prepared_shape(n, k, fmt);
+  *code_bytes_out = static_cast<size_t>(s.code_bytes);
+  *scale_bytes_out = static_cast<size_t>(s.scale_bytes);
+  return FP4_OK;
+}
+
+int fp4_prepare(const uint8_t* codes_dev, const uint8_t* scales_dev, int n, int k, int fmt, uint8_t* prep_codes_dev,
+                uint8_t* prep_scales_dev, hipStream_t stream) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if (!codes_dev || !scales_dev || !prep_codes_dev || !prep_scales_dev) return FP4_EINVAL;
+  if (!aligned16(codes_dev) || !aligned16(scales_dev) || !aligned16(prep_codes_dev) || !aligned16(prep_scales_dev))
+    return FP4_EALIGN;
+  return to_status(fp4::launch_prepare(codes_dev, scales_dev, n, k, fmt, prep_codes_dev, prep_scales_dev, stream));
+}
+
+int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scales_dev, const uint8_t* up_codes_dev,
+                        const uint8_t* up_scales_dev, int n_half, int k, int fmt, uint8_t* prep_codes_dev,
+                        uint8_t* prep_scales_dev, hipStream_t stream) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n_half, k))) return st;
+  if (static_cast<int64_t>(n_half) * 2 > FP4_MAX_N) return FP4_EINVAL;
+  if (!gate_codes_dev || !gate_scales_dev || !up_codes_dev || !up_scales_dev || !prep_codes_dev || !prep_scales_dev)
+    return FP4_EINVAL;
+  if (!aligned16(gate_codes_dev) || !aligned16(gate_scales_dev) || !aligned16(up_codes_dev) ||
+      !aligned16(up_scales_dev) || !aligned16(prep_codes_dev) || !aligned16(prep_scales_dev))
+    return FP4_EALIGN;
+  const fp4::PreparedShape s = fp4::prepared_shape(n_half, k, fmt);
+  hipError_t e = fp4::launch_prepare(gate_codes_dev, gate_scales_dev, n_half, k, fmt, prep_codes_dev,
+                                     prep_scales_dev, stream);
+  if (e != hipSuccess) return FP4_EHIP;
+  e = fp4::launch_prepare(up_codes_dev, up_scales_dev, n_half, k, fmt, prep_codes_dev + s.code_bytes,
+                          prep_scales_dev + s.scale_bytes, stream);
+  return to_status(e);
+}
+
+int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* bytes_out) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if ((st = check_m(m))) return st;
+  if (projections != 1 && projections != 2) return FP4_EINVAL;
+  if (!bytes_out) return FP4_EINVAL;
+  *bytes_out = workspace_for(m, n, k, fmt, projections);
+  return FP4_OK;
+}
+
+int fp4_w4a16_linear(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                     const uint8_t* prep_scales_dev, int n, float global_scale, int fmt, uint16_t* y_dev,
+                     void* workspace_dev, size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out) {
+  const float g[1] = {global_scale};
+  return run_linear(x_dev, m, k, prep_codes_dev, prep_scales_dev, n, 1, g, fmt, y_dev, workspace_dev,
+                    workspace_bytes, stream, info_out);
+}
+
+int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                      const uint8_t* prep_scales_dev, int n_half, float global_gate, float global_up, int fmt,
+                      uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
+                      fp4_dispatch_info* info_out) {
+  const float g[2] = {global_gate, global_up};
+  return run_linear(x_dev, m, k, prep_codes_dev, prep_scales_dev, n_half, 2, g, fmt, y_dev, workspace_dev,
+                    workspace_bytes, stream, info_out);
+}
+
+int fp4_dequantize(const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int k, float global_scale,
+                   int fmt, float* out_dev, hipStream_t stream) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if (!prep_codes_dev || !prep_scales_dev || !out_dev) return FP4_EINVAL;
+  if (!aligned16(prep_codes_dev) || !aligned16(prep_scales_dev) || !aligned16(out_dev)) return FP4_EALIGN;
+  return to_status(fp4::launch_dequant(prep_codes_dev, prep_scales_dev, n, k, fmt, global_scale, out_dev, stream));
+}
+
+const char* fp4_status_string(int status) {
+  switch (status) {
+    case FP4_OK: return "ok";
+    case FP4_EINVAL: return "invalid argument (null pointer, size out of range, or k not a multiple of 32)";
+    case FP4_EFMT: return "unknown weight format";
+    case FP4_EALIGN: return "device pointer not 16-byte aligned";
+    case FP4_EWORKSPACE: return "workspace too small";
+    case FP4_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

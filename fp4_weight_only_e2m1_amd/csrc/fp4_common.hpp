@@ -1,0 +1,117 @@
+// Shared host/device definitions of the prepared weight layout and the launch
+// interface between the C ABI (api.cpp) and the kernels (*.hip).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+namespace fp4 {
+
+constexpr int kFmtNvfp4 = 0;
+constexpr int kFmtMxfp4 = 1;
+
+// Prepared layout granules.  Rows are padded to kRowAlign so every kernel tile
+// is full; k is padded to kSlabK, the k-extent one 32-lane GEMV team covers per
+// step (32 lanes x 32 codes = 16 bytes per lane).
+constexpr int kRowAlign = 256;
+constexpr int kSlabK = 1024;
+constexpr int kRowGroup = 8;         // rows whose scale bytes are interleaved
+constexpr int kGemvRowsPerTeam = 8;  // rows one 32-lane team processes at once
+constexpr int kGemvTeams = 8;        // teams per 256-thread workgroup
+constexpr int kGemvTileRows = kGemvRowsPerTeam * kGemvTeams;  // 64
+constexpr int kGemvMaxSlabsPerSplit = 4;  // x staged in LDS: 8 rows * 4096 k * 2 B = 64 KiB
+constexpr int kGemvMaxM = 8;
+constexpr int kTargetCUs = 256;      // MI355X compute units
+
+inline constexpr int group_size(int fmt) { return fmt == kFmtNvfp4 ? 16 : 32; }
+inline constexpr int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+struct PreparedShape {
+  int n, k, fmt;
+  int64_t n_pad, k_pad;
+  int64_t code_bytes, scale_bytes;
+  int64_t kgroups;  // k_pad / g: scale bytes per row
+};
+
+inline PreparedShape prepared_shape(int n, int k, int fmt) {
+  PreparedShape s;
+  s.n = n;
+  s.k = k;
+  s.fmt = fmt;
+  s.n_pad = round_up(n, kRowAlign);
+  s.k_pad = round_up(k, kSlabK);
+  s.kgroups = s.k_pad / group_size(fmt);
+  s.code_bytes = s.n_pad * s.k_pad / 2;
+  s.scale_bytes = s.n_pad * s.kgroups;
+  return s;
+}
+
+// Number of K splits for the decode GEMV.  A function of (k, fmt, n per
+// projection) only -- never of m or of how many projections share the launch --
+// so a row's summation order is the same at every m <= 8 and in the fused
+// gate_up launch as in the separate ones.
+inline int gemv_splits(int n_proj, int k, int fmt) {
+  (void)fmt;
+  const int64_t nslab = round_up(k, kSlabK) / kSlabK;
+  const int64_t tiles = round_up(n_proj, kRowAlign) / kGemvTileRows;
+  int64_t s = (nslab + kGemvMaxSlabsPerSplit - 1) / kGemvMaxSlabsPerSplit;
+  // Enough workgroups to cover the chip twice over.
+  while (s < nslab && tiles * s < 2 * kTargetCUs) ++s;
+  return static_cast<int>(s);
+}
+
+struct GemvArgs {
+  const uint16_t* x;      // bf16 [m][k]
+  const uint8_t* codes;   // prepared codes
+  const uint8_t* scales;  // prepared scales
+  uint16_t* y;            // bf16 [m][ldy]
+  float* partial;         // fp32 [splits][m][rows_total] when splits > 1
+  int m, k;
+  int64_t k_pad;          // prepared row length in codes
+  int64_t kgroups;        // prepared scale bytes per row
+  int nslab;              // k_pad / kSlabK
+  int splits;
+  int n_proj;             // real rows per projection
+  int64_t n_proj_pad;     // padded rows per projection
+  int projections;        // 1 (linear) or 2 (gate_up)
+  int64_t rows_total;     // projections * n_proj_pad
+  int64_t ldy;            // projections * n_proj
+  float gscale[2];        // global scale per projection (1 for MXFP4)
+};
+
+struct ReduceArgs {
+  const float* partial;
+  uint16_t* y;
+  int m, splits;
+  int n_proj;
+  int64_t n_proj_pad, rows_total, ldy;
+  int projections;
+  float gscale[2];
+};
+
+struct MfmaArgs {
+  const uint16_t* x;      // bf16 [m][k]
+  const uint8_t* codes;
+  const uint8_t* scales;
+  uint16_t* y;
+  int m, k;
+  int64_t k_pad, kgroups;
+  int n_proj;
+  int64_t n_proj_pad;
+  int projections;
+  int64_t rows_total, ldy;
+  float gscale[2];
+};
+
+// Launchers (defined in the .hip files).  Each returns the hipError_t of its
+// launch; the grid/block it used is written to *grid / *block when non-null.
+hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,
+                          uint8_t* prep_codes, uint8_t* prep_scales, hipStream_t stream);
+hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,
+                          float gscale, float* out, hipStream_t stream);
+
+}  // namespace fp4

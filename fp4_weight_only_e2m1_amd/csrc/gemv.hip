@@ -1,0 +1,310 @@
+// Decode-shaped W4A16 FP4 GEMV (m <= 8 activation rows) for gfx950, plus the
+// deterministic split-K reduce.
+//
+// What it computes: y[m, n] = G * sum_k x[m, k] * E2M1(code[n, k]) * S(n, k/g)
+// ("native MXFP4 keep-quant", vllm.cpp PR #38, commit list: W4A16 GEMM at
+// decode, M=1 and M=8; "keep the ModelOpt NVFP4 lm_head packed", vllm.cpp
+// PR #263, section "Why this row matters": the packed head is a W4A16 GEMM).
+//
+// The weight stream is the whole cost at decode ("MXFP4 decode-graph +
+// gate_up FUSION default-ON", vllm.cpp PR #54: W4A16 is memory-bound), so the
+// kernel is built around it:
+//   * A 256-thread workgroup owns 64 weight rows and one K split.  It is 8
+//     teams of 32 lanes; a team owns 8 rows.  Lane l of a team covers codes
+//     [32l, 32l + 32) of each 1024-code slab, so each row's slab is one 16-byte
+//     load per lane and 512 contiguous bytes per team (coalesced).
+//   * The 8 scale bytes of the team's 8 rows for one k-group are contiguous in
+//     the prepared layout: one 8-byte (MXFP4) or 16-byte (NVFP4, two groups)
+//     load per lane per slab.
+//   * x for the split is staged once into LDS (at most 8 x 4096 bf16 = 64 KiB)
+//     and read back 16 bytes at a time; each read serves 8 rows.  The 16-byte
+//     chunks of a lane are rotated by (lane >> 1) so that 8 consecutive lanes
+//     hit 8 distinct 16-byte bank groups.
+//   * Decode: v_cvt_scalef32_pk_bf16_fp4 turns each code byte into a bf16
+//     pair.  For MXFP4 the E8M0 scale is folded into that conversion (the
+//     products are powers-of-two multiples of E2M1 values, exact in bf16).
+//     For NVFP4 the conversion is unscaled; the group partial (16 codes) is
+//     multiplied by its E4M3 scale with one f32 FMA per row and activation
+//     row, because the conversion ignores a scale's mantissa.
+//   * Contraction: v_dot2c_f32_bf16, f32 accumulation.
+//   * Reduction over the 32 lanes of a team: a transposing butterfly.  At each
+//     step a lane keeps half of its partial sums and trades the other half
+//     with its partner, so 8*M sums take about 2*8*M shuffles instead of
+//     5*8*M.
+//   * K split: partial sums go to a caller workspace [splits][m][rows] and a
+//     second kernel adds them in split order.  The split count depends on
+//     (k, fmt, rows per projection) only, so summation order -- and hence
+//     every output bit -- is the same for any m <= 8 and for the fused gate_up
+//     launch as for the two separate ones.  There are no atomics or locks, so
+//     the workspace never needs zeroing (unlike the spin-lock workspace whose
+//     missing memset hung the pages' engine: "re-verify 27B NVFP4 on the
+//     nvidia ModelOpt checkpoint", section "Rewrite/binding grid").
+#include "fp4_common.hpp"
+#include "fp4_device.hpp"
+
+namespace fp4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTeamLanes = 32;
+constexpr int kChunksPerSlab = kSlabK / 8;  // 16-byte x chunks (8 bf16) per slab
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int c) {
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
+// Rotated position of 16-byte chunk `sub` (0..3) of lane block `lb` in LDS.
+__device__ __forceinline__ int xs_index(int lb, int sub) {
+  return (lb << 2) | ((sub + (lb >> 1)) & 3);
+}
+
+template <int M, int FMT>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
+  __shared__ uint4 xs[M][kGemvMaxSlabsPerSplit * kChunksPerSlab];
+
+  const int tid = threadIdx.x;
+  const int team = tid >> 5;
+  const int lane = tid & (kTeamLanes - 1);
+  const int split = blockIdx.y;
+  const int slab0 = static_cast<int>(static_cast<int64_t>(split) * a.nslab / a.splits);
+  const int slab1 = static_cast<int>(static_cast<int64_t>(split + 1) * a.nslab / a.splits);
+  const int nsl = slab1 - slab0;
+
+  // ---- stage x[:, 1024*slab0 : 1024*slab1) in LDS, zero beyond k ----
+  const int chunks = nsl * kChunksPerSlab;
+  for (int c = tid; c < M * chunks; c += kThreads) {
+    const int m = c / chunks;
+    const int cc = c - m * chunks;
+    const int64_t kk = static_cast<int64_t>(slab0) * kSlabK + cc * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (kk < a.k) v = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(m) * a.k + kk);
+    xs[m][xs_index(cc >> 2, cc & 3)] = v;
+  }
+  __syncthreads();
+
+  // ---- this team's 8 rows ----
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kGemvTileRows + team * kGemvRowsPerTeam;
+  const int64_t row_bytes = a.k_pad / 2;
+  const uint8_t* cptr = a.codes + row0 * row_bytes + lane * 16;
+  const uint8_t* sptr = a.scales + (row0 / kRowGroup) * a.kgroups * kRowGroup;
+
+  float acc[kGemvRowsPerTeam][M];
+#pragma unroll
+  for (int r = 0; r < kGemvRowsPerTeam; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+  uint4 q[kGemvRowsPerTeam];
+  uint4 sc;
+  auto load_slab = [&](int slab, uint4* qq, uint4& s) {
+#pragma unroll
+    for (int r = 0; r < kGemvRowsPerTeam; ++r)
+      qq[r] = load_stream16(cptr + r * row_bytes + static_cast<int64_t>(slab) * (kSlabK / 2));
+    if constexpr (FMT == kFmtMxfp4) {
+      const uint2 t = *reinterpret_cast<const uint2*>(
+          sptr + (static_cast<int64_t>(slab) * kTeamLanes + lane) * kRowGroup);
+      s = make_uint4(t.x, t.y, 0u, 0u);
+    } else {
+      s = *reinterpret_cast<const uint4*>(
+          sptr + (static_cast<int64_t>(slab) * kTeamLanes + lane) * 2 * kRowGroup);
+    }
+  };
+
+  load_slab(slab0, q, sc);
+  for (int j = 0; j < nsl; ++j) {
+    uint4 qn[kGemvRowsPerTeam];
+    uint4 scn = sc;
+    if (j + 1 < nsl) load_slab(slab0 + j + 1, qn, scn);
+    const int lb = j * kTeamLanes + lane;  // lane block within the staged x
+
+    if constexpr (FMT == kFmtMxfp4) {
+      float sop[kGemvRowsPerTeam];
+#pragma unroll
+      for (int r = 0; r < kGemvRowsPerTeam; ++r)
+        sop[r] = e8m0_as_scale_operand((r < 4 ? sc.x : sc.y) >> (8 * (r & 3)));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint4 xv[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m] = xs[m][xs_index(lb, c)];
+#pragma unroll
+        for (int r = 0; r < kGemvRowsPerTeam; ++r) {
+          const uint32_t word = u4_get(q[r], c);
+          const bf16x2_t w0 = cvt_fp4x2_bf16<0>(word, sop[r]);
+          const bf16x2_t w1 = cvt_fp4x2_bf16<1>(word, sop[r]);
+          const bf16x2_t w2 = cvt_fp4x2_bf16<2>(word, sop[r]);
+          const bf16x2_t w3 = cvt_fp4x2_bf16<3>(word, sop[r]);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float t = acc[r][m];
+            t = dot2_bf16(w0, xv[m].x, t);
+            t = dot2_bf16(w1, xv[m].y, t);
+            t = dot2_bf16(w2, xv[m].z, t);
+            t = dot2_bf16(w3, xv[m].w, t);
+            acc[r][m] = t;
+          }
+        }
+      }
+    } else {
+      // Two NVFP4 groups of 16 codes per lane per slab: chunks {0,1} and {2,3}.
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp) {
+        uint4 xv[2][M];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int m = 0; m < M; ++m) xv[h][m] = xs[m][xs_index(lb, 2 * grp + h)];
+        const uint32_t sword = grp == 0 ? (sc.x) : (sc.z);
+        const uint32_t sword_hi = grp == 0 ? (sc.y) : (sc.w);
+#pragma unroll
+        for (int r = 0; r < kGemvRowsPerTeam; ++r) {
+          const uint32_t sw = r < 4 ? sword : sword_hi;
+          float s;
+          switch (r & 3) {
+            case 0: s = e4m3_to_f32<0>(sw); break;
+            case 1: s = e4m3_to_f32<1>(sw); break;
+            case 2: s = e4m3_to_f32<2>(sw); break;
+            default: s = e4m3_to_f32<3>(sw); break;
+          }
+          bf16x2_t w[8];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t word = u4_get(q[r], 2 * grp + h);
+            w[4 * h + 0] = cvt_fp4x2_bf16<0>(word, 1.0f);
+            w[4 * h + 1] = cvt_fp4x2_bf16<1>(word, 1.0f);
+            w[4 * h + 2] = cvt_fp4x2_bf16<2>(word, 1.0f);
+            w[4 * h + 3] = cvt_fp4x2_bf16<3>(word, 1.0f);
+          }
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float p = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              p = dot2_bf16(w[4 * h + 0], xv[h][m].x, p);
+              p = dot2_bf16(w[4 * h + 1], xv[h][m].y, p);
+              p = dot2_bf16(w[4 * h + 2], xv[h][m].z, p);
+              p = dot2_bf16(w[4 * h + 3], xv[h][m].w, p);
+            }
+            acc[r][m] = __builtin_fmaf(p, s, acc[r][m]);
+          }
+        }
+      }
+    }
+    if (j + 1 < nsl) {
+#pragma unroll
+      for (int r = 0; r < kGemvRowsPerTeam; ++r) q[r] = qn[r];
+      sc = scn;
+    }
+  }
+
+  // ---- transposing butterfly over the team's 32 lanes ----
+  // V partial sums per lane (index r*M + m), padded with zeros to a power of
+  // two so that every halving step splits evenly.
+  constexpr int V = kGemvRowsPerTeam * M;
+  constexpr int VP = V <= 8 ? 8 : V <= 16 ? 16 : V <= 32 ? 32 : 64;
+  float v[VP];
+#pragma unroll
+  for (int i = 0; i < VP; ++i) v[i] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kGemvRowsPerTeam; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) v[r * M + m] = acc[r][m];
+
+  int base = 0;        // index of v[0] in the original numbering
+  int plain_mask = 0;  // lane bits summed over without halving
+  constexpr int kFinal = VP > 32 ? VP / 32 : 1;
+#pragma unroll
+  for (int step = 0; step < 5; ++step) {
+    const int o = 16 >> step;
+    const bool upper = (lane & o) != 0;
+    const int count = VP >> step;  // values held before this step
+    if (count > 1) {
+      const int half = count >> 1;
+#pragma unroll
+      for (int i = 0; i < VP / 2; ++i) {
+        if (i < half) {
+          const float send = upper ? v[i] : v[i + half];
+          const float keep = upper ? v[i + half] : v[i];
+          v[i] = keep + __shfl_xor(send, o, kTeamLanes);
+        }
+      }
+      if (upper) base += half;
+    } else {
+      v[0] += __shfl_xor(v[0], o, kTeamLanes);
+      plain_mask |= o;
+    }
+  }
+
+  if ((lane & plain_mask) == 0) {
+#pragma unroll
+    for (int i = 0; i < kFinal; ++i) {
+      const int idx = base + i;
+      if (idx < V) {
+        const int r = idx / M;
+        const int m = idx - r * M;
+        const int64_t row = row0 + r;
+        const int h = static_cast<int>(row / a.n_proj_pad);
+        const int64_t lr = row - static_cast<int64_t>(h) * a.n_proj_pad;
+        if (a.splits == 1) {
+          if (lr < a.n_proj)
+            a.y[static_cast<int64_t>(m) * a.ldy + static_cast<int64_t>(h) * a.n_proj + lr] =
+                f32_to_bf16_rne(v[i] * a.gscale[h]);
+        } else {
+          a.partial[(static_cast<int64_t>(split) * M + m) * a.rows_total + row] = v[i];
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void reduce_kernel(const ReduceArgs a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.m) * a.rows_total;
+  if (i >= total) return;
+  const int m = static_cast<int>(i / a.rows_total);
+  const int64_t row = i - static_cast<int64_t>(m) * a.rows_total;
+  const int h = static_cast<int>(row / a.n_proj_pad);
+  const int64_t lr = row - static_cast<int64_t>(h) * a.n_proj_pad;
+  if (lr >= a.n_proj) return;
+  const int64_t stride = static_cast<int64_t>(a.m) * a.rows_total;
+  float s = a.partial[i];
+  for (int sp = 1; sp < a.splits; ++sp) s += a.partial[i + sp * stride];
+  a.y[static_cast<int64_t>(m) * a.ldy + static_cast<int64_t>(h) * a.n_proj + lr] =
+      f32_to_bf16_rne(s * a.gscale[h]);
+}
+
+template <int FMT>
+hipError_t launch_gemv_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
+  switch (a.m) {
+    case 1: hipLaunchKernelGGL((gemv_kernel<1, FMT>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<2, FMT>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((gemv_kernel<3, FMT>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<4, FMT>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((gemv_kernel<5, FMT>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((gemv_kernel<6, FMT>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((gemv_kernel<7, FMT>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemv_kernel<8, FMT>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
+  const dim3 grid(static_cast<unsigned>(a.rows_total / kGemvTileRows), static_cast<unsigned>(a.splits));
+  if (grid_out) *grid_out = grid;
+  if (block_out) *block_out = dim3(kThreads);
+  return fmt == kFmtNvfp4 ? launch_gemv_fmt<kFmtNvfp4>(a, grid, stream)
+                          : launch_gemv_fmt<kFmtMxfp4>(a, grid, stream);
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(a.m) * a.rows_total;
+  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
+  hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fp4

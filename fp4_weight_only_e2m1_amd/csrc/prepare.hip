@@ -1,0 +1,128 @@
+// Repack a canonical packed FP4 weight into the prepared layout, and the
+// dequantize export that tests compare bit for bit against the oracle.
+//
+// Canonical input ("keep the ModelOpt NVFP4 lm_head packed", vllm.cpp PR #263,
+// section "Why this row matters": U8 [N, K/2] codes plus one scale byte per
+// group; "native MXFP4 keep-quant", vllm.cpp PR #38, commit list: E8M0 scales
+// [N, K/32]):
+//   codes [n][k/2], scales [n][k/g], both row-major.
+// Prepared output (one layout read by both the decode GEMV and the MFMA GEMM,
+// so a weight is stored once):
+//   codes  [n_pad][k_pad/2]: the same bytes, rows padded to a multiple of 256
+//          and each row padded to a multiple of 1024 codes, padding zero;
+//   scales [n_pad/8][k_pad/g][8]: within each group of 8 rows, the 8 scale
+//          bytes of one k-group are adjacent, so a GEMV lane fetches the scales
+//          of its 8 rows with one 8- or 16-byte load; padding zero.
+// Zero padding decodes to zero weights (code 0 is +0), so padded rows and
+// columns add nothing to any sum.
+#include "fp4_common.hpp"
+#include "fp4_device.hpp"
+
+namespace fp4 {
+namespace {
+
+// One thread per 16-byte chunk of the prepared codes.
+__global__ __launch_bounds__(256) void prepare_codes_kernel(const uint8_t* __restrict__ in, int n, int k,
+                                                            int64_t n_pad, int64_t k_pad,
+                                                            uint8_t* __restrict__ out) {
+  const int64_t chunks_per_row = k_pad / 32;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n_pad * chunks_per_row) return;
+  const int64_t row = i / chunks_per_row;
+  const int64_t c = i - row * chunks_per_row;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < n && c < k / 32)
+    v = *reinterpret_cast<const uint4*>(in + row * (k / 2) + c * 16);
+  *reinterpret_cast<uint4*>(out + row * (k_pad / 2) + c * 16) = v;
+}
+
+// One thread per (row group, k-group): gathers 8 rows' scale bytes.
+__global__ __launch_bounds__(256) void prepare_scales_kernel(const uint8_t* __restrict__ in, int n,
+                                                             int64_t kg_real, int64_t n_pad, int64_t kgroups,
+                                                             uint8_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= (n_pad / kRowGroup) * kgroups) return;
+  const int64_t rg = i / kgroups;
+  const int64_t kg = i - rg * kgroups;
+  uint32_t lo = 0, hi = 0;
+  for (int r = 0; r < kRowGroup; ++r) {
+    const int64_t row = rg * kRowGroup + r;
+    uint32_t b = 0;
+    if (row < n && kg < kg_real) b = in[row * kg_real + kg];
+    if (r < 4) lo |= b << (8 * r);
+    else hi |= b << (8 * (r - 4));
+  }
+  *reinterpret_cast<uint2*>(out + i * kRowGroup) = make_uint2(lo, hi);
+}
+
+// One thread per 8 consecutive weights (one 32-bit code word).
+//   NVFP4: fl32(fl32(E2M1 * S) * G); MXFP4: E2M1 * 2^(b-127).
+template <int FMT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales, int n, int k,
+                                                      int64_t k_pad, int64_t kgroups, float gscale,
+                                                      float* __restrict__ out) {
+  constexpr int G = group_size(FMT);
+  const int64_t words_per_row = k / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(n) * words_per_row) return;
+  const int64_t row = i / words_per_row;
+  const int64_t wi = i - row * words_per_row;
+  const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + row * (k_pad / 2) + wi * 4);
+  const int64_t kg = (wi * 8) / G;
+  const uint32_t sb = scales[((row / kRowGroup) * kgroups + kg) * kRowGroup + (row % kRowGroup)];
+  f32x2_t p[4];
+  if constexpr (FMT == kFmtMxfp4) {
+    const float sop = e8m0_as_scale_operand(sb);
+    p[0] = cvt_fp4x2_f32<0>(word, sop);
+    p[1] = cvt_fp4x2_f32<1>(word, sop);
+    p[2] = cvt_fp4x2_f32<2>(word, sop);
+    p[3] = cvt_fp4x2_f32<3>(word, sop);
+  } else {
+    const float s = e4m3_to_f32<0>(sb);
+    p[0] = cvt_fp4x2_f32<0>(word, 1.0f);
+    p[1] = cvt_fp4x2_f32<1>(word, 1.0f);
+    p[2] = cvt_fp4x2_f32<2>(word, 1.0f);
+    p[3] = cvt_fp4x2_f32<3>(word, 1.0f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j].x = (p[j].x * s) * gscale;
+      p[j].y = (p[j].y * s) * gscale;
+    }
+  }
+  float4* o = reinterpret_cast<float4*>(out + row * k + wi * 8);
+  o[0] = make_float4(p[0].x, p[0].y, p[1].x, p[1].y);
+  o[1] = make_float4(p[2].x, p[2].y, p[3].x, p[3].y);
+}
+
+}  // namespace
+
+hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,
+                          uint8_t* prep_codes, uint8_t* prep_scales, hipStream_t stream) {
+  const PreparedShape s = prepared_shape(n, k, fmt);
+  const int64_t code_chunks = s.n_pad * (s.k_pad / 32);
+  hipLaunchKernelGGL(prepare_codes_kernel, dim3(static_cast<unsigned>((code_chunks + 255) / 256)), dim3(256), 0,
+                     stream, codes, n, k, s.n_pad, s.k_pad, prep_codes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items = (s.n_pad / kRowGroup) * s.kgroups;
+  hipLaunchKernelGGL(prepare_scales_kernel, dim3(static_cast<unsigned>((items + 255) / 256)), dim3(256), 0, stream,
+                     scales, n, static_cast<int64_t>(k / group_size(fmt)), s.n_pad, s.kgroups, prep_scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt, float gscale,
+                          float* out, hipStream_t stream) {
+  const PreparedShape s = prepared_shape(n, k, fmt);
+  const int64_t items = static_cast<int64_t>(n) * (k / 8);
+  const dim3 grid(static_cast<unsigned>((items + 255) / 256));
+  if (fmt == kFmtNvfp4)
+    hipLaunchKernelGGL(dequant_kernel<kFmtNvfp4>, grid, dim3(256), 0, stream, codes, scales, n, k, s.k_pad,
+                       s.kgroups, gscale, out);
+  else
+    hipLaunchKernelGGL(dequant_kernel<kFmtMxfp4>, grid, dim3(256), 0, stream, codes, scales, n, k, s.k_pad,
+                       s.kgroups, 1.0f, out);
+  return hipGetLastError();
+}
+
+}  // namespace fp4

@@ -1,0 +1,174 @@
+/*
+ * fp4w4a16.h - W4A16 FP4 weight-only linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer: y[m, n] = sum_k x[m, k] * w[n, k], with x bf16 and w stored as
+ * packed 4-bit E2M1 codes plus block scales, dequantized in registers:
+ *
+ *   w[n, k] = E2M1(code[n, k]) * S(n, k / g) * G
+ *
+ *   NVFP4: g = 16, S is an FP8 E4M3FN byte, G is a float32 global scale that
+ *          multiplies ("re-verify 27B NVFP4 on the nvidia ModelOpt checkpoint",
+ *          vllm.cpp PR #178, section "Layer 3 - ModelOpt NVFP4 naming").
+ *   MXFP4: g = 32, S is an E8M0 byte (2^(b-127)), no global scale
+ *          ("native MXFP4 keep-quant", vllm.cpp PR #38, commit list).
+ *
+ * Canonical packed input (what a checkpoint holds; "keep the ModelOpt NVFP4
+ * lm_head packed", vllm.cpp PR #263, section "Why this row matters"):
+ *   codes  uint8 [n][k/2], row-major; byte j of a row holds element 2j in
+ *          bits 3..0 and element 2j+1 in bits 7..4;
+ *   scales uint8 [n][k/g], row-major; element k of a row uses scale k/g.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers owned by the caller; the library
+ *     never allocates, frees or caches device memory and keeps no global state,
+ *     so calls are reentrant.  Out-parameters named *_out are host pointers.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Work is enqueued on `stream` and is asynchronous; argument checks happen
+ *     on the host before anything is enqueued, and an invalid call enqueues
+ *     nothing.  After a launch the library checks hipGetLastError.
+ *   - Sizes: 1 <= n <= FP4_MAX_N, 32 <= k <= FP4_MAX_K with k % 32 == 0,
+ *     0 <= m <= FP4_MAX_M (m == 0 is valid and does nothing).
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - A workspace is never assumed to hold anything (it need not be zeroed).
+ *   - Return value: FP4_OK or a negative fp4_status.
+ */
+#ifndef FP4W4A16_H
+#define FP4W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats. */
+enum fp4_fmt {
+  FP4_FMT_NVFP4 = 0, /* group 16, E4M3FN block scale, float32 global scale */
+  FP4_FMT_MXFP4 = 1  /* group 32, E8M0 block scale, no global scale */
+};
+
+/* Status codes. */
+enum fp4_status {
+  FP4_OK = 0,
+  FP4_EINVAL = -1,     /* null pointer, size out of range, k not a multiple of 32 */
+  FP4_EFMT = -2,       /* unknown format */
+  FP4_EALIGN = -3,     /* a device pointer is not 16-byte aligned */
+  FP4_EWORKSPACE = -4, /* workspace smaller than fp4_workspace_bytes() asks for */
+  FP4_EHIP = -5        /* the HIP runtime reported an error for a launch */
+};
+
+#define FP4_MAX_N (1 << 24)
+#define FP4_MAX_K (1 << 20)
+#define FP4_MAX_M (1 << 20)
+
+/* Which kernel a call ran (filled when the caller passes a non-null pointer). */
+typedef struct fp4_dispatch_info {
+  int kernel;  /* 0 = decode GEMV (m <= 8), 1 = MFMA tile GEMM (m > 8) */
+  int splits;  /* number of K splits (1 = no split, no reduce launch) */
+  int grid_x;  /* workgroups along the output rows */
+  int grid_y;  /* workgroups along the second grid axis (splits or m tiles) */
+  int block;   /* threads per workgroup */
+} fp4_dispatch_info;
+
+/*
+ * Size of a prepared weight of n rows and k columns.
+ * The prepared layout (written by fp4_prepare, read by every compute call):
+ *   codes: uint8 [n_pad][k_pad/2], the canonical code bytes, zero padded,
+ *          with n_pad = n rounded up to 256 and k_pad = k rounded up to 1024;
+ *   scales: uint8 [n_pad/8][k_pad/g][8]: within each group of 8 rows, the 8
+ *          scale bytes of one k-group are contiguous; zero padded.
+ * A prepared gate_up weight is a prepared gate weight followed by a prepared
+ * up weight, in both buffers (twice these sizes).
+ * Pure host function; never touches the GPU.
+ */
+int fp4_prepared_bytes(int n, int k, int fmt, size_t* code_bytes_out, size_t* scale_bytes_out);
+
+/*
+ * Repack a canonical packed weight (codes_dev [n][k/2], scales_dev [n][k/g])
+ * into the prepared layout (prep_codes_dev, prep_scales_dev, sized by
+ * fp4_prepared_bytes).  Integer byte moves only; run once per weight.
+ * The canonical buffers are only read and may be released after the stream
+ * reaches this call.  Input and output must not overlap.
+ * Cite: the packed weight is consumed as is, never expanded to bf16 ("keep the
+ * ModelOpt NVFP4 lm_head packed", section "Round-2 findings resolved": the
+ * prepare step may only write state it owns).
+ */
+int fp4_prepare(const uint8_t* codes_dev, const uint8_t* scales_dev, int n, int k, int fmt,
+                uint8_t* prep_codes_dev, uint8_t* prep_scales_dev, hipStream_t stream);
+
+/*
+ * Prepare a fused gate_up weight: gate rows then up rows, each n_half x k.
+ * Equivalent to two fp4_prepare calls into the two halves of the output.
+ * Cite: "MXFP4 decode-graph + gate_up FUSION default-ON" (vllm.cpp PR #54),
+ * step 2: one GEMM over the concatenated [gate; up] weight.
+ */
+int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scales_dev,
+                        const uint8_t* up_codes_dev, const uint8_t* up_scales_dev,
+                        int n_half, int k, int fmt,
+                        uint8_t* prep_codes_dev, uint8_t* prep_scales_dev, hipStream_t stream);
+
+/*
+ * Workspace a compute call needs, in bytes (0 when none).  `projections` is 1
+ * for fp4_w4a16_linear (n = output features) and 2 for fp4_w4a16_gate_up
+ * (n = n_half).  Pure host function.
+ */
+int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* bytes_out);
+
+/*
+ * y = x * w^T.
+ *   x_dev   bf16 [m][k] row-major;
+ *   prep_*  the prepared weight of n rows (fp4_prepare);
+ *   global_scale  G for NVFP4 (a multiplier, applied after the sum over k);
+ *                 ignored for MXFP4;
+ *   y_dev   bf16 [m][n] row-major, rounded to nearest even from float32;
+ *   workspace_dev / workspace_bytes  scratch of fp4_workspace_bytes(m, n, k, fmt, 1);
+ *   info_out  optional, may be NULL.
+ * Accumulation is float32.  The order of every sum depends only on (k, fmt, n)
+ * and the kernel chosen by m (m <= 8 or m > 8), so results are deterministic
+ * run to run and row m of a call with m <= 8 rows equals the same row computed
+ * alone.
+ * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list (the W4A16
+ * entry points take bf16 x and the packed weight to bf16 y); "keep the ModelOpt
+ * NVFP4 lm_head packed" (vllm.cpp PR #263), section "Why this row matters"
+ * (the 248320 x 5120 head run as a W4A16 GEMM).
+ */
+int fp4_w4a16_linear(const uint16_t* x_dev, int m, int k,
+                     const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n,
+                     float global_scale, int fmt,
+                     uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes,
+                     hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
+ * Fused gate_up: y[:, 0:n_half] = x * gate^T, y[:, n_half:2 n_half] = x * up^T,
+ * in one launch over the prepared [gate; up] weight (fp4_prepare_gate_up).
+ * global_gate / global_up are the two NVFP4 global scales (ignored for MXFP4).
+ * y_dev is bf16 [m][2 n_half].  Workspace: fp4_workspace_bytes(m, n_half, k, fmt, 2).
+ * Bitwise equal to two fp4_w4a16_linear calls on the halves.
+ * Cite: "MXFP4 decode-graph + gate_up FUSION default-ON" (vllm.cpp PR #54), step 2.
+ */
+int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k,
+                      const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n_half,
+                      float global_gate, float global_up, int fmt,
+                      uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes,
+                      hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
+ * Dequantize a prepared weight to float32 out_dev [n][k]:
+ * out = fl32(fl32(E2M1 * S) * G), G = 1 for MXFP4.  Uses the same decoders as
+ * the compute kernels; exists so tests can compare the decode bit for bit.
+ * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list (the CPU
+ * dequant reference the device GEMM is checked against).
+ */
+int fp4_dequantize(const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int k,
+                   float global_scale, int fmt, float* out_dev, hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char* fp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4W4A16_H */

@@ -1,0 +1,71 @@
+"""Helpers shared by the GPU tests: device transfer, the layer's tolerance,
+and cached synthetic weights.  Inputs come from synth; expected values come
+from the oracle; the HIP path is only ever the thing under test."""
+
+import functools
+
+import numpy as np
+import torch
+
+import fp4_weight_only_e2m1_amd as fp4
+import oracle
+import synth
+
+DEV = torch.device("cuda:0")
+
+
+def u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
+
+
+def x_dev(xbits):
+    xbits = np.ascontiguousarray(xbits, dtype=np.uint16)
+    return torch.from_numpy(xbits.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def y_host_bits(y):
+    torch.cuda.synchronize()
+    return y.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def y_host(y):
+    return oracle.bf16_bits_to_f32(y_host_bits(y)).astype(np.float64)
+
+
+def tolerance_violations(y, y_ref):
+    """Elements outside |y - y_ref| <= 2^-7 |y_ref| + 1e-3 rms(y_ref), rms over the whole call."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    bound = 2.0 ** -7 * np.abs(y_ref) + 1e-3 * rms
+    return np.abs(y - y_ref) > bound, rms
+
+
+def assert_close(y, y_ref, what=""):
+    bad, rms = tolerance_violations(y, y_ref)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        detail = ", ".join("%s: got %.6g want %.6g" % (tuple(i), y[tuple(i)], y_ref[tuple(i)]) for i in idx)
+        raise AssertionError("%s: %d of %d outside tolerance (rms %.4g); %s" %
+                             (what, int(bad.sum()), bad.size, rms, detail))
+
+
+@functools.lru_cache(maxsize=8)
+def weight(workload, tensor, n, k, fmt):
+    """Canonical packed weight (codes, scales, G) from synth, cached per test session."""
+    return synth.packed_weight(workload, tensor, n, k, fmt)
+
+
+@functools.lru_cache(maxsize=16)
+def prepared(workload, tensor, n, k, fmt):
+    packed, scales, g = weight(workload, tensor, n, k, fmt)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    torch.cuda.synchronize()
+    return pc, ps, g
+
+
+def sample_rows(n, count, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(n, size=min(count, n), replace=False).tolist())
+    rows.update([0, 1, n - 1, n - 2] if n > 2 else range(n))
+    return np.array(sorted(rows), dtype=np.int64)

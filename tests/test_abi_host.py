@@ -1,0 +1,140 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every
+symbol include/fp4w4a16.h declares, sizes buffers as documented, and rejects
+bad arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_weight_only_e2m1_amd as fp4
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fp4w4a16.h")
+ST = {"OK": 0, "EINVAL": -1, "EFMT": -2, "EALIGN": -3, "EWORKSPACE": -4, "EHIP": -5}
+NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fp4.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(fp4_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("fp4_prepared_bytes", "fp4_prepare", "fp4_prepare_gate_up", "fp4_workspace_bytes",
+                 "fp4_w4a16_linear", "fp4_w4a16_gate_up", "fp4_dequantize", "fp4_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in fp4._SIGNATURES, name
+
+
+def test_status_values_match_header():
+    text = open(HEADER).read()
+    for key, val in ST.items():
+        assert re.search(r"FP4_%s\s*=\s*%d" % (key, val), text), key
+    assert fp4.fp4_status_string(0) == "ok"
+    assert "workspace" in fp4.fp4_status_string(ST["EWORKSPACE"])
+
+
+@pytest.mark.parametrize("n,k,fmt", [(512, 256, NV), (24576, 4096, MX), (248320, 5120, NV), (5120, 17408, NV),
+                                     (17408, 5120, MX), (1, 32, NV), (300, 1056, MX)])
+def test_prepared_bytes(n, k, fmt):
+    g = 16 if fmt == NV else 32
+    n_pad = -(-n // 256) * 256
+    k_pad = -(-k // 1024) * 1024
+    cb, sb = fp4.fp4_prepared_bytes(n, k, fmt)
+    assert cb == n_pad * k_pad // 2
+    assert sb == n_pad * k_pad // g
+
+
+def test_lm_head_prepared_bytes_equal_packed_bytes():
+    # The 248320 x 5120 head needs no padding: the prepared weight is exactly
+    # the packed checkpoint's 0.6660 GiB ("keep the ModelOpt NVFP4 lm_head packed").
+    cb, sb = fp4.fp4_prepared_bytes(248320, 5120, NV)
+    assert cb + sb == 248320 * 2560 + 248320 * 320
+
+
+@pytest.mark.parametrize("n,k,fmt,bad", [(0, 256, NV, "EINVAL"), (512, 0, NV, "EINVAL"), (512, 48, NV, "EINVAL"),
+                                         (512, 256, 2, "EFMT"), (512, 256, -1, "EFMT"),
+                                         (1 << 25, 256, NV, "EINVAL"), (512, (1 << 20) + 32, MX, "EINVAL")])
+def test_prepared_bytes_rejects(lib, n, k, fmt, bad):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.fp4_prepared_bytes(n, k, fmt, ctypes.byref(cb), ctypes.byref(sb)) == ST[bad]
+
+
+def test_workspace_bytes_policy():
+    # m > 8 runs the MFMA kernel without a workspace; the lm_head GEMV splits
+    # K=5120 (5 slabs of 1024) in two; splitting never depends on m.
+    assert fp4.fp4_workspace_bytes(16, 17408, 5120, NV) == 0
+    ws1 = fp4.fp4_workspace_bytes(1, 248320, 5120, NV)
+    ws8 = fp4.fp4_workspace_bytes(8, 248320, 5120, NV)
+    assert ws1 == 2 * 1 * 248320 * 4 and ws8 == 8 * ws1
+    # gate_up: two projections, each split like the separate linear.
+    one = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 1)
+    two = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 2)
+    assert two == 2 * one
+    assert fp4.fp4_workspace_bytes(1, 512, 256, NV) == 0
+
+
+FAKE = 0x10000  # an aligned address that is never dereferenced: every call below fails validation first
+
+
+def _linear(lib, m=1, k=256, n=512, fmt=NV, x=FAKE, c=FAKE, s=FAKE, y=FAKE, ws=None, ws_bytes=0):
+    return lib.fp4_w4a16_linear(x, m, k, c, s, n, 1.0, fmt, y, ws, ws_bytes, None, None)
+
+
+def test_linear_argument_checks(lib):
+    assert _linear(lib, fmt=7) == ST["EFMT"]
+    assert _linear(lib, k=48) == ST["EINVAL"]
+    assert _linear(lib, k=0) == ST["EINVAL"]
+    assert _linear(lib, n=0) == ST["EINVAL"]
+    assert _linear(lib, m=-1) == ST["EINVAL"]
+    assert _linear(lib, x=None) == ST["EINVAL"]
+    assert _linear(lib, y=None) == ST["EINVAL"]
+    assert _linear(lib, x=FAKE + 2) == ST["EALIGN"]
+    assert _linear(lib, c=FAKE + 8) == ST["EALIGN"]
+    assert _linear(lib, y=FAKE + 4) == ST["EALIGN"]
+    # m == 0 is a valid empty call: nothing to do, nothing enqueued.
+    assert _linear(lib, m=0, x=None, y=None) == ST["OK"]
+    # A split-K shape needs a workspace.
+    need = fp4.fp4_workspace_bytes(1, 5120, 17408, NV)
+    assert need > 0
+    assert _linear(lib, k=17408, n=5120, ws=FAKE, ws_bytes=need - 1) == ST["EWORKSPACE"]
+    assert _linear(lib, k=17408, n=5120, ws=None, ws_bytes=need) == ST["EINVAL"]
+    assert _linear(lib, k=17408, n=5120, ws=FAKE + 4, ws_bytes=need) == ST["EALIGN"]
+
+
+def test_gate_up_and_prepare_argument_checks(lib):
+    assert lib.fp4_w4a16_gate_up(FAKE, 1, 100, FAKE, FAKE, 512, 1.0, 1.0, NV, FAKE, None, 0, None, None) == \
+        ST["EINVAL"]
+    assert lib.fp4_w4a16_gate_up(FAKE, 1, 256, FAKE, FAKE, 512, 1.0, 1.0, 3, FAKE, None, 0, None, None) == ST["EFMT"]
+    assert lib.fp4_w4a16_gate_up(FAKE, 1, 256, FAKE, FAKE, 1 << 24, 1.0, 1.0, NV, FAKE, None, 0, None, None) == \
+        ST["EINVAL"]
+    assert lib.fp4_prepare(FAKE, FAKE, 512, 256, NV, FAKE + 1, FAKE, None) == ST["EALIGN"]
+    assert lib.fp4_prepare(None, FAKE, 512, 256, NV, FAKE, FAKE, None) == ST["EINVAL"]
+    assert lib.fp4_prepare(FAKE, FAKE, 512, 250, NV, FAKE, FAKE, None) == ST["EINVAL"]
+    assert lib.fp4_prepare_gate_up(FAKE, FAKE, FAKE, None, 512, 256, MX, FAKE, FAKE, None) == ST["EINVAL"]
+    assert lib.fp4_dequantize(FAKE, FAKE, 512, 256, 1.0, 9, FAKE, None) == ST["EFMT"]
+    assert lib.fp4_dequantize(FAKE, FAKE, 512, 256, 1.0, NV, FAKE + 4, None) == ST["EALIGN"]
+    sz = ctypes.c_size_t()
+    assert lib.fp4_workspace_bytes(1, 512, 256, NV, 3, ctypes.byref(sz)) == ST["EINVAL"]
+
+
+def test_split_count_independent_of_m_and_fusion():
+    # The workspace is splits * m * rows * 4 bytes; dividing out m and rows
+    # recovers the split count, which must not change with m.
+    for n, k, fmt in [(5120, 17408, NV), (5120, 6144, NV), (12288, 4096, MX), (248320, 5120, NV)]:
+        rows = -(-n // 256) * 256
+        counts = {fp4.fp4_workspace_bytes(m, n, k, fmt) // (4 * m * rows) for m in range(1, 9)}
+        assert len(counts) == 1

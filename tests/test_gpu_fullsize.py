@@ -1,0 +1,66 @@
+"""GPU parity at the workloads' full sizes, through the same entry points and
+launch configuration the benchmark times.  The oracle computes a sample of
+output columns one by one (every activation row, a few hundred weight rows
+spread over n, plus both ends); fused gate_up is also checked bit for bit
+against the two separate launches at full size."""
+
+import numpy as np
+import pytest
+
+import fp4_weight_only_e2m1_amd as fp4
+import oracle
+import synth
+from gpu_util import assert_close, prepared, sample_rows, weight, x_dev, y_host, y_host_bits
+
+pytestmark = pytest.mark.gpu
+
+NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
+
+# name, workload, tensor, fmt, n, k, activation rows
+CASES = [
+    ("tiny_nvfp4", synth.TINY, 0, NV, 512, 256, [1]),
+    ("lm_head", synth.LM_HEAD, 0, NV, 248320, 5120, [1, 8]),
+    ("down_proj", synth.DECODE_27B, 0, NV, 5120, 17408, [1, 2, 4, 8]),
+    ("o_proj", synth.DECODE_27B, 1, NV, 5120, 6144, [1, 2, 4, 8]),
+    ("prefill_nvfp4", synth.PREFILL, 0, NV, 17408, 5120, [256, 1024, 4096]),
+    ("prefill_mxfp4", synth.PREFILL, 1, MX, 17408, 5120, [256, 1024, 4096]),
+]
+
+
+@pytest.mark.parametrize("name,workload,tensor,fmt,n,k,ms", CASES, ids=[c[0] for c in CASES])
+def test_full_size_sampled(name, workload, tensor, fmt, n, k, ms):
+    packed, scales, g = weight(workload, tensor, n, k, fmt)
+    pc, ps, _ = prepared(workload, tensor, n, k, fmt)
+    rows = sample_rows(n, 512 if n > 512 else n, seed=workload)
+    for m in ms:
+        xbits = synth.activations(workload, m, k)
+        y = y_host(fp4.fp4_w4a16_linear(x_dev(xbits), pc, ps, n, float(g), fmt))
+        y_ref = oracle.linear_rows(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g, rows)
+        assert np.isfinite(y).all()
+        assert_close(y[:, rows], y_ref, "%s m=%d" % (name, m))
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_gate_up_full_size(m):
+    nh, k, fmt = 12288, 4096, MX
+    pg, sg, gg = weight(synth.GATE_UP, 0, nh, k, fmt)
+    pu, su, gu = weight(synth.GATE_UP, 1, nh, k, fmt)
+    cg, cs, _ = prepared(synth.GATE_UP, 0, nh, k, fmt)
+    uc, us, _ = prepared(synth.GATE_UP, 1, nh, k, fmt)
+    import torch
+    fc = torch.cat([cg, uc])
+    fs = torch.cat([cs, us])
+    xbits = synth.activations(synth.GATE_UP, m, k)
+    xd = x_dev(xbits)
+    y = y_host_bits(fp4.fp4_w4a16_gate_up(xd, fc, fs, nh, float(gg), float(gu), fmt))
+    yg = y_host_bits(fp4.fp4_w4a16_linear(xd, cg, cs, nh, float(gg), fmt))
+    yu = y_host_bits(fp4.fp4_w4a16_linear(xd, uc, us, nh, float(gu), fmt))
+    assert np.array_equal(y[:, :nh], yg)
+    assert np.array_equal(y[:, nh:], yu)
+    rows = sample_rows(nh, 384, seed=m)
+    x = oracle.bf16_bits_to_f32(xbits)
+    yf = oracle.bf16_bits_to_f32(y).astype(np.float64)
+    ref_g = oracle.linear_rows(x, pg, sg, k, fmt, gg, rows)
+    ref_u = oracle.linear_rows(x, pu, su, k, fmt, gu, rows)
+    assert_close(np.concatenate([yf[:, rows], yf[:, nh + rows]], axis=1),
+                 np.concatenate([ref_g, ref_u], axis=1), "gate_up m=%d" % m)

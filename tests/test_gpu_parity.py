@@ -1,0 +1,212 @@
+"""GPU parity of the HIP path against the oracle, at sizes the oracle finishes
+in seconds: bitwise dequantization, the linear layer within the layer's
+tolerance, and the invariants the kernels promise (one-hot layout, fused ==
+split, batch invariance, determinism, poisoned workspace)."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_weight_only_e2m1_amd as fp4
+import oracle
+import synth
+from gpu_util import DEV, assert_close, u8, x_dev, y_host, y_host_bits
+
+pytestmark = pytest.mark.gpu
+
+NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
+GS = {NV: 16, MX: 32}
+
+
+def _canon_bits(a):
+    """float32 bits with every NaN made the same quiet NaN."""
+    a = np.ascontiguousarray(a, dtype=np.float32).copy()
+    a[np.isnan(a)] = np.float32(np.nan)
+    return a.view(np.uint32)
+
+
+def _quantized(fmt, n, k, tensor=0, workload=synth.TINY):
+    packed, scales, g = synth.packed_weight(workload, 50 + tensor, n, k, fmt)
+    return packed, scales, g
+
+
+def _run_linear(packed, scales, g, fmt, n, k, xbits, info=None):
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    y = fp4.fp4_w4a16_linear(x_dev(xbits), pc, ps, n, float(g), fmt, info=info)
+    return y
+
+
+# ---------------------------------------------------------------- dequant
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+@pytest.mark.parametrize("g", [1.0, 2.0 ** -7, 0.0123 / 2688])
+def test_dequant_exhaustive_codes_and_scales(fmt, g):
+    # Row r uses scale byte r for every group; each group holds all 16 codes.
+    n, k = 256, 64
+    codes = np.tile(np.arange(16, dtype=np.uint8), (n, k // 16))
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], k // GS[fmt], axis=1)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    out = fp4.fp4_dequantize(pc, ps, n, k, np.float32(g), fmt).cpu().numpy()
+    want = oracle.dequantize(packed, scales, k, fmt, np.float32(g))
+    mism = _canon_bits(out) != _canon_bits(want)
+    if mism.any():
+        r, c = np.argwhere(mism)[0]
+        raise AssertionError("%d mismatches; first: scale byte %#x code %#x got %r want %r" %
+                             (int(mism.sum()), r, codes[r, c], out[r, c], want[r, c]))
+
+
+@pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 512, 256), (NV, 300, 1056), (MX, 77, 2080)])
+def test_dequant_synthetic_weights(fmt, n, k):
+    packed, scales, g = _quantized(fmt, n, k)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    out = fp4.fp4_dequantize(pc, ps, n, k, float(g), fmt).cpu().numpy()
+    assert np.array_equal(_canon_bits(out), _canon_bits(oracle.dequantize(packed, scales, k, fmt, g)))
+
+
+def test_prepared_layout_bytes():
+    # Codes: canonical bytes, zero padded to [n_pad, k_pad/2]; scales: within
+    # groups of 8 rows the 8 bytes of one k-group are adjacent.
+    n, k, fmt = 300, 1056, NV
+    packed, scales, _ = _quantized(fmt, n, k)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    n_pad, k_pad = 512, 2048
+    want_c = np.zeros((n_pad, k_pad // 2), np.uint8)
+    want_c[:n, :k // 2] = packed
+    kg_pad = k_pad // 16
+    s_pad = np.zeros((n_pad, kg_pad), np.uint8)
+    s_pad[:n, :k // 16] = scales
+    want_s = s_pad.reshape(n_pad // 8, 8, kg_pad).transpose(0, 2, 1).reshape(-1)
+    assert np.array_equal(pc.cpu().numpy(), want_c.reshape(-1))
+    assert np.array_equal(ps.cpu().numpy(), want_s)
+
+
+# ---------------------------------------------------------------- linear
+
+
+SHAPES = [
+    (NV, 512, 256),     # the tiny NVFP4 workload
+    (MX, 512, 256),
+    (NV, 640, 2048),    # two slabs
+    (MX, 384, 3072),    # three slabs
+    (NV, 300, 1056),    # ragged n and a ragged last slab
+    (MX, 257, 96),      # k below one slab
+    (NV, 256, 5120),    # k split in two (lm_head's k)
+    (NV, 128, 17408),   # many splits (down_proj's k)
+]
+
+
+@pytest.mark.parametrize("fmt,n,k", SHAPES)
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
+def test_gemv_matches_oracle(fmt, n, k, m):
+    packed, scales, g = _quantized(fmt, n, k)
+    xbits = synth.activations(synth.TINY, m, k)
+    info = fp4.fp4_dispatch_info()
+    y = _run_linear(packed, scales, g, fmt, n, k, xbits, info)
+    assert info.kernel == 0
+    y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
+    assert_close(y_host(y), y_ref, "gemv fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
+
+
+@pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 640, 2048), (NV, 300, 1056), (MX, 256, 5120)])
+@pytest.mark.parametrize("m", [9, 16, 33, 128, 200])
+def test_mfma_matches_oracle(fmt, n, k, m):
+    packed, scales, g = _quantized(fmt, n, k)
+    xbits = synth.activations(synth.TINY, m, k)
+    info = fp4.fp4_dispatch_info()
+    y = _run_linear(packed, scales, g, fmt, n, k, xbits, info)
+    assert info.kernel == 1
+    y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
+    assert_close(y_host(y), y_ref, "mfma fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
+
+
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 2048, 1), (MX, 512, 2048, 4), (NV, 300, 5120, 8),
+                                       (NV, 512, 2048, 16), (MX, 384, 1056, 40)])
+def test_one_hot_selects_weight_column(fmt, n, k, m):
+    # x row i = e_{k_i}: y[i, :] is bf16(w[:, k_i]) exactly (the global scale is
+    # applied after the sum, and every other product is zero).
+    packed, scales, g = _quantized(fmt, n, k, tensor=3)
+    ks = np.linspace(0, k - 1, m).astype(np.int64)
+    x = np.zeros((m, k), np.float32)
+    x[np.arange(m), ks] = 1.0
+    xbits = oracle.f32_to_bf16_bits(x)
+    y = y_host(_run_linear(packed, scales, g, fmt, n, k, xbits))
+    w = oracle.dequantize(packed, scales, k, fmt, g)
+    want = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(w[:, ks].T)).astype(np.float64)
+    assert np.array_equal(y, want)   # +0 and -0 compare equal
+
+
+@pytest.mark.parametrize("fmt,nh,k", [(MX, 640, 2048), (NV, 300, 1056), (MX, 1024, 4096), (NV, 256, 17408)])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 24])
+def test_gate_up_fused_equals_split(fmt, nh, k, m):
+    pg, sg, gg = synth.packed_weight(synth.TINY, 60, nh, k, fmt)
+    pu, su, gu = synth.packed_weight(synth.TINY, 61, nh, k, fmt)
+    xbits = synth.activations(synth.TINY, m, k)
+    pc, ps = fp4.fp4_prepare_gate_up(u8(pg), u8(sg), u8(pu), u8(su), nh, k, fmt)
+    y = y_host_bits(fp4.fp4_w4a16_gate_up(x_dev(xbits), pc, ps, nh, float(gg), float(gu), fmt))
+    yg = y_host_bits(_run_linear(pg, sg, gg, fmt, nh, k, xbits))
+    yu = y_host_bits(_run_linear(pu, su, gu, fmt, nh, k, xbits))
+    assert np.array_equal(y[:, :nh], yg) and np.array_equal(y[:, nh:], yu)
+    y_ref = oracle.gate_up(oracle.bf16_bits_to_f32(xbits), pg, sg, pu, su, k, fmt, gg, gu)
+    assert_close(oracle.bf16_bits_to_f32(y).astype(np.float64), y_ref, "gate_up")
+
+
+@pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 384, 3072), (NV, 256, 17408), (NV, 300, 5120)])
+def test_gemv_batch_invariance(fmt, n, k):
+    # Row i of an m-row call equals the same row computed alone, bit for bit.
+    packed, scales, g = _quantized(fmt, n, k)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    x8 = synth.activations(synth.TINY, 8, k)
+    y8 = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x8), pc, ps, n, float(g), fmt))
+    for m in range(1, 9):
+        ym = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x8[:m]), pc, ps, n, float(g), fmt))
+        assert np.array_equal(ym, y8[:m]), m
+
+
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 300, 5120, 8), (MX, 256, 17408, 3), (NV, 640, 2048, 64)])
+def test_deterministic_and_workspace_poison(fmt, n, k, m):
+    packed, scales, g = _quantized(fmt, n, k)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    xd = x_dev(synth.activations(synth.TINY, m, k))
+    need = fp4.fp4_workspace_bytes(m, n, k, fmt)
+    outs = []
+    for fill in (0x00, 0xFF, 0x7F):
+        ws = torch.full((max(need, 16),), fill, dtype=torch.uint8, device=DEV)
+        outs.append(y_host_bits(fp4.fp4_w4a16_linear(xd, pc, ps, n, float(g), fmt, workspace=ws)))
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_zero_rows_is_a_no_op():
+    n, k = 512, 256
+    packed, scales, g = _quantized(NV, n, k)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, NV)
+    x = torch.empty((0, k), dtype=torch.bfloat16, device=DEV)
+    y = fp4.fp4_w4a16_linear(x, pc, ps, n, float(g), NV)
+    torch.cuda.synchronize()
+    assert y.shape == (0, n)
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_minimal_shape(fmt):
+    n, k, m = 1, 32, 1
+    packed, scales, g = _quantized(fmt, 8, k)
+    packed, scales = packed[:1], scales[:1]
+    xbits = synth.activations(synth.TINY, m, k)
+    y = _run_linear(packed, scales, g, fmt, n, k, xbits)
+    y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
+    assert_close(y_host(y), y_ref, "n=1 k=32")
+
+
+def test_unit_scales_sum_of_x():
+    # Every code 1.0, unit scales, G = 1: y[m, n] = sum_k x[m, k] (closed form).
+    n, k = 256, 1024
+    packed = np.full((n, k // 2), 0x22, np.uint8)
+    xbits = synth.activations(synth.TINY, 4, k)
+    for fmt, sb in ((NV, 0x38), (MX, 0x7F)):
+        scales = np.full((n, k // GS[fmt]), sb, np.uint8)
+        for m in (4, 20):
+            xb = np.tile(xbits, (m // 4, 1))
+            y = y_host(_run_linear(packed, scales, 1.0, fmt, n, k, xb))
+            want = oracle.bf16_bits_to_f32(xb).astype(np.float64).sum(axis=1)
+            assert_close(y, np.repeat(want[:, None], n, axis=1), "unit scales m=%d" % m)
