@@ -1,0 +1,323 @@
+"""Benchmark of the W4A16 FP4 linear layer on one MI355X.
+
+Prints ONE JSON line (rank 0, one GPU):
+  metric  "W4A16 FP4 linear achieved HBM GB/s at M=1..8; TFLOP/s at M=1024"
+  value   whole-job throughput over the timed steps: algorithmic bytes / s in
+          GB/s for the decode workloads, 2*m*n*k / s in TFLOP/s for prefill.
+A step is one call of the layer at each activation-row count m in the list
+(default m = 1, 2, 4, 8 for the decode workloads, 1024 for prefill), on
+synthetic activations, with the prepared weights already resident in HBM.
+Each m is timed with its own HIP events; by default the timed calls are
+replayed from a captured HIP graph so the per-call launch gaps of the host
+runtime do not count against the kernels.
+The weights are rotated over enough device copies (>= 1 GiB in total) that
+the 256 MB Infinity Cache cannot hold them, so the bytes come from HBM.
+
+Workloads (synthetic weights and activations at the pages' shapes):
+  gate_up        MXFP4 fused gate_up, k=4096, n=2x12288          (default)
+  lm_head        NVFP4 packed lm_head, k=5120, n=248320
+  down_proj      NVFP4, k=17408, n=5120
+  o_proj         NVFP4, k=6144, n=5120
+  prefill_nvfp4  NVFP4, k=5120, n=17408 (m=1024 by default)
+  prefill_mxfp4  MXFP4, k=5120, n=17408
+  tiny           NVFP4, k=256, n=512
+
+Algorithmic bytes per call: packed codes (n*k/2) + scale bytes (n*k/g)
++ global scales (4 B each, NVFP4) + x (2*m*k) + y (2*m*n).  Split-K
+partials, padding and rotation copies are not counted.
+
+The roofline object covers the kernel that dominates the step (the longest
+per-launch time): its average duration comes from HIP events around its timed
+launches on the stream they run on; `traffic` is filled from a committed rocprofv3 counter summary in
+profiles/ only when that summary was taken on the current kernel source.
+
+cpu_baseline: the oracle (NumPy, float64 sums), as it stands, timed on this
+host's cores on a bounded sample of the same workload (a slice of the weight
+rows), scaled to the same unit.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 FP4 linear achieved HBM GB/s at M=1..8; TFLOP/s at M=1024"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30
+
+# name: (workload id, fmt, n per projection, k, projections, default m)
+WORKLOADS = {
+    "gate_up": (1, 1, 12288, 4096, 2, 8),
+    "lm_head": (2, 0, 248320, 5120, 1, 8),
+    "down_proj": (3, 0, 5120, 17408, 1, 8),
+    "o_proj": (3, 0, 5120, 6144, 1, 8),
+    "prefill_nvfp4": (4, 0, 17408, 5120, 1, 1024),
+    "prefill_mxfp4": (4, 1, 17408, 5120, 1, 1024),
+    "tiny": (0, 0, 512, 256, 1, 1),
+}
+TENSOR = {"o_proj": 1, "prefill_mxfp4": 1}
+
+
+def algorithmic_bytes(fmt, n_proj, k, projections, m):
+    g = 16 if fmt == 0 else 32
+    n = n_proj * projections
+    w = n * k // 2 + n * k // g + (4 * projections if fmt == 0 else 0)
+    return w + 2 * m * k + 2 * m * n
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_weight_only_e2m1_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, m, kernel_hash):
+    """Counter-derived HBM bytes per launch from profiles/traffic.json, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    e = data.get("%s_m%d" % (workload, m))
+    if not e or e.get("kernel_source") != kernel_hash:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def make_inputs(name, m, torch, fp4, synth):
+    wid, fmt, n, k, proj, _ = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    import numpy as np
+
+    def upload(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if proj == 2:
+        pg, sg, gg = synth.packed_weight(wid, 0, n, k, fmt)
+        pu, su, gu = synth.packed_weight(wid, 1, n, k, fmt)
+        pc, ps = fp4.fp4_prepare_gate_up(upload(pg), upload(sg), upload(pu), upload(su), n, k, fmt)
+        gs = (float(gg), float(gu))
+        host = {"packed": (pg, pu), "scales": (sg, su), "g": (gg, gu)}
+    else:
+        p, s, g = synth.packed_weight(wid, TENSOR.get(name, 0), n, k, fmt)
+        pc, ps = fp4.fp4_prepare(upload(p), upload(s), n, k, fmt)
+        gs = (float(g),)
+        host = {"packed": (p,), "scales": (s,), "g": (g,)}
+    xb = synth.activations(wid, m, k)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    torch.cuda.synchronize()
+    return pc, ps, gs, x, xb, host
+
+
+def cpu_baseline(name, xbs, host, budget_s):
+    """Time the oracle on a bounded slice of weight rows, one call per m of the step.
+
+    xbs: list of (m, bf16 bits of x).  Returns the cpu_baseline JSON object,
+    with the value scaled from the slice to the whole step.
+    """
+    import numpy as np
+    import oracle
+    wid, fmt, n, k, proj, _ = WORKLOADS[name]
+    xs = [(m, oracle.bf16_bits_to_f32(xb)) for m, xb in xbs]
+    packed, scales, g = host["packed"][0], host["scales"][0], host["g"][0]
+
+    def one_step(sl):
+        for _, x in xs:
+            oracle.linear(x, packed[sl], scales[sl], k, fmt, g)
+
+    rows, spent = 256, 0.0
+    # Grow the slice until one step takes a measurable time, then repeat within the budget.
+    while True:
+        sl = slice(0, min(rows, n))
+        t0 = time.perf_counter()
+        one_step(sl)
+        dt = time.perf_counter() - t0
+        spent += dt
+        if dt > 0.5 or sl.stop == n or spent > budget_s:
+            break
+        rows *= 4
+    reps = min(50, max(1, int((budget_s - spent) / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        one_step(sl)
+    dt = (time.perf_counter() - t0) / reps
+    frac = sl.stop / (n * proj)
+    if name.startswith("prefill"):
+        value = sum(2.0 * m * sl.stop * k for m, _ in xs) / dt / 1e12
+        unit = "TFLOP/s"
+    else:
+        value = sum(algorithmic_bytes(fmt, n, k, proj, m) for m, _ in xs) * frac / dt / 1e9
+        unit = "GB/s"
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = cores
+    return {"value": round(value, 4), "unit": unit, "cores": int(threads or cores), "kind": "oracle",
+            "sample": "oracle.linear (dequant + float64 matmul) over weight rows [0, %d) of %d, one call per "
+                      "m in %s, %d timed repetitions; value scaled by the row fraction"
+                      % (sl.stop, n * proj, [m for m, _ in xs], reps),
+            "host_cpus": cores}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gate_up", choices=sorted(WORKLOADS))
+    ap.add_argument("--m", default=None,
+                    help="activation rows, comma separated (default: 1,2,4,8 for decode, 1024 for prefill)")
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="replay the timed calls from a captured HIP graph, or launch them one by one")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the layer's kernels run on a single MI355X and no "
+              "multi-GPU path is built (sharding over n is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import numpy as np
+    import fp4_weight_only_e2m1_amd as fp4
+    import synth
+
+    name = args.workload
+    wid, fmt, n, k, proj, m_default = WORKLOADS[name]
+    if args.m is None:
+        ms = [1, 2, 4, 8] if m_default <= 8 else [m_default]
+    else:
+        ms = [int(v) for v in args.m.split(",")]
+    dev = torch.device("cuda:0")
+    pc, ps, gs, x0, xb0, host = make_inputs(name, ms[0], torch, fp4, synth)
+
+    # Rotate over device copies of the prepared weight so the timed reads come from HBM.
+    footprint = pc.numel() + ps.numel()
+    copies = max(2, math.ceil(ROTATE_BYTES / footprint))
+    weights = [(pc, ps)] + [(pc.clone(), ps.clone()) for _ in range(copies - 1)]
+    nout = n * proj
+
+    per_m = []
+    for m in ms:
+        xb = synth.activations(wid, m, k)
+        x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((m, nout), dtype=torch.bfloat16, device=dev)
+        ws_bytes = fp4.fp4_workspace_bytes(m, n, k, fmt, proj)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        per_m.append({"m": m, "x": x, "xb": xb, "y": y, "ws": ws, "info": fp4.fp4_dispatch_info()})
+
+    def call(d, i):
+        c, s = weights[i % copies]
+        if proj == 2:
+            fp4.fp4_w4a16_gate_up(d["x"], c, s, n, gs[0], gs[1], fmt, y=d["y"], workspace=d["ws"], info=d["info"])
+        else:
+            fp4.fp4_w4a16_linear(d["x"], c, s, n, gs[0], fmt, y=d["y"], workspace=d["ws"], info=d["info"])
+
+    for d in per_m:
+        for i in range(args.warmup):
+            call(d, i)
+    torch.cuda.synchronize()
+
+    graphs = []
+    if args.launch == "graph":
+        for d in per_m:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(args.steps):
+                    call(d, args.warmup + i)
+            graphs.append(g)
+        for g in graphs:   # one untimed replay each
+            g.replay()
+        torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in per_m]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for j, d in enumerate(per_m):
+        evs[j][0].record(stream)
+        if graphs:
+            graphs[j].replay()
+        else:
+            for i in range(args.steps):
+                call(d, args.warmup + i)
+        evs[j][1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+
+    total_ms = 0.0
+    total_bytes = 0
+    total_flops = 0.0
+    rows = []
+    for j, d in enumerate(per_m):
+        ms_m = evs[j][0].elapsed_time(evs[j][1])
+        m = d["m"]
+        b = algorithmic_bytes(fmt, n, k, proj, m)
+        f = 2.0 * m * nout * k
+        total_ms += ms_m
+        total_bytes += b * args.steps
+        total_flops += f * args.steps
+        info = d["info"]
+        kern = {0: "gemv_kernel", 2: "decode_mfma_kernel", 1: "mfma_kernel"}[info.kernel]
+        us = ms_m * 1e3 / args.steps
+        rows.append({"m": m, "kernel": "%s<%d,%s>" % (kern, m, "nvfp4" if fmt == 0 else "mxfp4")
+                     if info.kernel != 1 else "%s<%s>" % (kern, "nvfp4" if fmt == 0 else "mxfp4"),
+                     "us_per_launch": round(us, 3), "gbs": round(b / (us * 1e-6) / 1e9, 2),
+                     "tflops": round(f / (us * 1e-6) / 1e12, 3), "splits": info.splits,
+                     "grid": [info.grid_x, info.grid_y], "block": info.block,
+                     "algorithmic_bytes": b, "flops": f})
+
+    prefill = max(ms) > 8
+    if prefill:
+        value = total_flops / (total_ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    else:
+        value = total_bytes / (total_ms * 1e-3) / 1e9
+        unit = "GB/s"
+    dom = max(rows, key=lambda r: r["us_per_launch"])
+    if prefill:
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4)}
+    roof.update({"kernel": dom["kernel"], "m": dom["m"], "avg_launch_us": dom["us_per_launch"],
+                 "units_per_launch": dom["flops"] if prefill else dom["algorithmic_bytes"],
+                 "traffic": read_traffic(name, dom["m"], kernel_source_hash())})
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "fmt": "nvfp4" if fmt == 0 else "mxfp4", "m": ms, "n": nout, "k": k,
+                   "projections": proj, "launch": args.launch, "rotated_weight_copies": copies,
+                   "step": "one call at each m in the list", "per_m": rows,
+                   "wall_s_timed": round(t_wall, 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(name, [(d["m"], d["xb"]) for d in per_m], host, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

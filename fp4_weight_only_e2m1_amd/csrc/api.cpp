@@ -11,6 +11,8 @@
 // lm_head packed", section "Round-3 findings resolved", item 4).
 #include "../../include/fp4w4a16.h"
 
+#include <atomic>
+
 #include "fp4_common.hpp"
 
 namespace {
@@ -31,9 +33,16 @@ int check_m(int m) { return (m < 0 || m > FP4_MAX_M) ? FP4_EINVAL : FP4_OK; }
 size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
   if (m < 1 || m > fp4::kGemvMaxM) return 0;
   const int splits = fp4::gemv_splits(n_proj, k, fmt);
-  if (splits <= 1) return 0;
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
-  return static_cast<size_t>(splits) * static_cast<size_t>(m) * static_cast<size_t>(rows_total) * sizeof(float);
+  return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total));
+}
+
+// A token no earlier call of this process used, for tagging the split-K
+// arrival flags in a workspace.  The fixed top byte keeps it from ever equalling
+// a memory fill of one repeated byte (0x00, 0xFF, ...).
+uint64_t next_token() {
+  static std::atomic<uint64_t> calls{0};
+  return (0x5Aull << 56) | ((calls.fetch_add(1, std::memory_order_relaxed) + 1) & 0x00FFFFFFFFFFFFFFull);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_EHIP; }
@@ -74,6 +83,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.k = k;
     a.k_pad = ps.k_pad;
     a.kgroups = ps.kgroups;
+    a.ksegs = ps.ksegs;
     a.nslab = static_cast<int>(ps.k_pad / fp4::kSlabK);
     a.splits = fp4::gemv_splits(n_proj, k, fmt);
     a.n_proj = n_proj;
@@ -83,26 +93,17 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.ldy = static_cast<int64_t>(n_proj) * projections;
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
-    hipError_t e = fp4::launch_gemv(a, fmt, stream, &grid, &block);
-    if (e != hipSuccess) return FP4_EHIP;
     if (a.splits > 1) {
-      fp4::ReduceArgs r{};
-      r.partial = a.partial;
-      r.y = y;
-      r.m = m;
-      r.splits = a.splits;
-      r.n_proj = n_proj;
-      r.n_proj_pad = ps.n_pad;
-      r.rows_total = a.rows_total;
-      r.ldy = a.ldy;
-      r.projections = projections;
-      r.gscale[0] = a.gscale[0];
-      r.gscale[1] = a.gscale[1];
-      e = fp4::launch_reduce(r, stream);
-      if (e != hipSuccess) return FP4_EHIP;
+      a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
+                                            static_cast<int64_t>(a.splits) * m * a.rows_total * 4);
+      a.token = next_token();
     }
-    if (info) *info = fp4_dispatch_info{0, a.splits, static_cast<int>(grid.x), static_cast<int>(grid.y),
-                                        static_cast<int>(block.x)};
+    const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
+    hipError_t e = on_mfma ? fp4::launch_decode_mfma(a, fmt, stream, &grid, &block)
+                           : fp4::launch_gemv(a, fmt, stream, &grid, &block);
+    if (e != hipSuccess) return FP4_EHIP;
+    if (info) *info = fp4_dispatch_info{on_mfma ? 2 : 0, a.splits, static_cast<int>(grid.x),
+                                        static_cast<int>(grid.y), static_cast<int>(block.x)};
   } else {
     fp4::MfmaArgs a{};
     a.x = x;
@@ -113,6 +114,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.k = k;
     a.k_pad = ps.k_pad;
     a.kgroups = ps.kgroups;
+    a.ksegs = ps.ksegs;
     a.n_proj = n_proj;
     a.n_proj_pad = ps.n_pad;
     a.projections = projections;

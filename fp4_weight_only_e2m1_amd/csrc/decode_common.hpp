@@ -1,0 +1,124 @@
+// Pieces shared by the two decode kernels (VALU GEMV and MFMA decode):
+// staging x in LDS, and the single-launch, lock-free split-K finish.
+#pragma once
+
+#include "fp4_common.hpp"
+#include "fp4_device.hpp"
+
+namespace fp4 {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kChunksPerSlab = kSlabK / 8;  // 16-byte chunks of x (8 bf16) per slab
+
+// First and one-past-last slab of K split `split`.
+struct SlabRange {
+  int first, count;
+};
+__device__ __forceinline__ SlabRange split_slabs(const GemvArgs& a, int split) {
+  const int s0 = static_cast<int>(static_cast<int64_t>(split) * a.nslab / a.splits);
+  const int s1 = static_cast<int>(static_cast<int64_t>(split + 1) * a.nslab / a.splits);
+  return {s0, s1 - s0};
+}
+
+// Copy x[0:M, 1024*slab0 : 1024*(slab0+nsl)) into xs (16-byte chunks, zero
+// beyond k), chunk q of row m at index Swz(m, q).  All global loads are issued
+// before the first LDS store, so the copy costs one L2 round trip rather than
+// one per chunk.  Ends with a workgroup barrier.
+template <int M, typename Swz>
+__device__ __forceinline__ void stage_x(const GemvArgs& a, int slab0, int nsl,
+                                        uint4 (*xs)[kGemvMaxSlabsPerSplit * kChunksPerSlab], Swz swz) {
+  constexpr int kPer = kGemvMaxSlabsPerSplit * kChunksPerSlab / kDecodeThreads;
+  const int chunks = nsl * kChunksPerSlab;
+  const int64_t k0 = static_cast<int64_t>(slab0) * kSlabK;
+  uint4 v[M][kPer];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int cc = threadIdx.x + i * kDecodeThreads;
+      const int64_t kk = k0 + cc * 8;
+      v[m][i] = make_uint4(0u, 0u, 0u, 0u);
+      if (cc < chunks && kk < a.k) v[m][i] = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(m) * a.k + kk);
+    }
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int cc = threadIdx.x + i * kDecodeThreads;
+      if (cc < chunks) xs[m][swz(m, cc)] = v[m][i];
+    }
+  __syncthreads();
+}
+
+// Output column of prepared row `row` (projection h, local row lr), or -1 for
+// a padding row.
+__device__ __forceinline__ int64_t out_col(const GemvArgs& a, int64_t row, int& h) {
+  h = static_cast<int>(row / a.n_proj_pad);
+  const int64_t lr = row - static_cast<int64_t>(h) * a.n_proj_pad;
+  return lr < a.n_proj ? static_cast<int64_t>(h) * a.n_proj + lr : -1;
+}
+
+// Split-K partial sums and arrival flags are exchanged between workgroups that
+// may sit on different XCDs, whose L2 caches are not coherent with each other.
+// They are therefore written and read with device-coherent (sc1) accesses --
+// relaxed atomics at agent scope -- which go to the coherence point instead of
+// a local L2 line.  Ordering comes from waiting for those stores to complete
+// (s_waitcnt 0) before the next step, not from device-scope fences, which on
+// this target write back and invalidate the whole L2.
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_partial(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Split-K finish for one 64-row tile, called by every thread of the workgroup
+// after it has stored (store_partial) this split's sums partial[split][m][row].
+//
+// Each (tile, split) workgroup publishes a flag = the call's 64-bit token once
+// its partials are complete, then reads the flags of all splits of its tile.
+// Store, wait for completion, then load: the last workgroup to publish sees
+// every flag (two may both see them; they then compute the same bytes).  A
+// workgroup that sees all flags adds the partials in split order 0, 1, ...,
+// S-1 -- a fixed order, so the output does not depend on which workgroup
+// finishes last -- applies the global scale, writes bf16 y and clears the
+// tile's flags.  Flags left by earlier calls either were cleared or hold older
+// tokens, so they never match: the workspace needs no zeroing, a captured
+// graph can replay the same token, and no workgroup ever waits for another.
+template <int M>
+__device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, int split) {
+  __shared__ int s_last;
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t* f = a.flags + tile * a.splits;
+    __hip_atomic_store(f + split, a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_memory();
+    int all = 1;
+    for (int s = 0; s < a.splits; ++s)
+      all &= __hip_atomic_load(f + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.token ? 1 : 0;
+    s_last = all;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  for (int s = threadIdx.x; s < a.splits; s += kDecodeThreads)
+    __hip_atomic_store(a.flags + tile * a.splits + s, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t stride = static_cast<int64_t>(M) * a.rows_total;
+  for (int i = threadIdx.x; i < M * kGemvTileRows; i += kDecodeThreads) {
+    const int m = i / kGemvTileRows;
+    const int64_t row = tile * kGemvTileRows + (i - m * kGemvTileRows);
+    int h;
+    const int64_t col = out_col(a, row, h);
+    if (col < 0) continue;
+    const float* p = a.partial + static_cast<int64_t>(m) * a.rows_total + row;
+    float s = load_partial(p);
+    for (int sp = 1; sp < a.splits; ++sp) s += load_partial(p + sp * stride);
+    a.y[static_cast<int64_t>(m) * a.ldy + col] = f32_to_bf16_rne(s * a.gscale[h]);
+  }
+}
+
+}  // namespace fp4

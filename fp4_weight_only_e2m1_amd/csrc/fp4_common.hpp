@@ -16,22 +16,35 @@ constexpr int kFmtMxfp4 = 1;
 // step (32 lanes x 32 codes = 16 bytes per lane).
 constexpr int kRowAlign = 256;
 constexpr int kSlabK = 1024;
-constexpr int kRowGroup = 8;         // rows whose scale bytes are interleaved
+constexpr int kRowGroup = 16;        // rows whose scale bytes are interleaved
 constexpr int kGemvRowsPerTeam = 8;  // rows one 32-lane team processes at once
 constexpr int kGemvTeams = 8;        // teams per 256-thread workgroup
 constexpr int kGemvTileRows = kGemvRowsPerTeam * kGemvTeams;  // 64
 constexpr int kGemvMaxSlabsPerSplit = 4;  // x staged in LDS: 8 rows * 4096 k * 2 B = 64 KiB
 constexpr int kGemvMaxM = 8;
+// m from which the decode path contracts on MFMA instead of VALU v_dot2
+// (measured crossover on MI355X: the VALU GEMV is faster at m = 1, 2).
+constexpr int kDecodeMfmaMinM = 3;
 constexpr int kTargetCUs = 256;      // MI355X compute units
 
 inline constexpr int group_size(int fmt) { return fmt == kFmtNvfp4 ? 16 : 32; }
+// Scale bytes per 32-code segment of a row: 2 for NVFP4, 1 for MXFP4.
+inline constexpr int scales_per_seg(int fmt) { return 32 / group_size(fmt); }
 inline constexpr int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Byte offset of the scale of (row, k-group kg) in the prepared scale layout
+// [n_pad/16][k_pad/32][16][P], P = scales_per_seg: for every 16-row group and
+// every 32-code segment, the 16 rows' P scale bytes are adjacent.
+__host__ __device__ inline int64_t scale_offset(int64_t row, int64_t kg, int64_t ksegs, int p) {
+  return (((row >> 4) * ksegs + kg / p) * kRowGroup + (row & 15)) * p + (kg % p);
+}
 
 struct PreparedShape {
   int n, k, fmt;
   int64_t n_pad, k_pad;
   int64_t code_bytes, scale_bytes;
   int64_t kgroups;  // k_pad / g: scale bytes per row
+  int64_t ksegs;    // k_pad / 32: 32-code segments per row
 };
 
 inline PreparedShape prepared_shape(int n, int k, int fmt) {
@@ -42,6 +55,7 @@ inline PreparedShape prepared_shape(int n, int k, int fmt) {
   s.n_pad = round_up(n, kRowAlign);
   s.k_pad = round_up(k, kSlabK);
   s.kgroups = s.k_pad / group_size(fmt);
+  s.ksegs = s.k_pad / 32;
   s.code_bytes = s.n_pad * s.k_pad / 2;
   s.scale_bytes = s.n_pad * s.kgroups;
   return s;
@@ -51,6 +65,12 @@ inline PreparedShape prepared_shape(int n, int k, int fmt) {
 // projection) only -- never of m or of how many projections share the launch --
 // so a row's summation order is the same at every m <= 8 and in the fused
 // gate_up launch as in the separate ones.
+// Workspace of a decode call: the split-K partials, then the arrival flags.
+inline int64_t decode_workspace_bytes(int64_t splits, int m, int64_t rows_total) {
+  if (splits <= 1) return 0;
+  return splits * m * rows_total * 4 + (rows_total / kGemvTileRows) * splits * 8;
+}
+
 inline int gemv_splits(int n_proj, int k, int fmt) {
   (void)fmt;
   const int64_t nslab = round_up(k, kSlabK) / kSlabK;
@@ -67,9 +87,12 @@ struct GemvArgs {
   const uint8_t* scales;  // prepared scales
   uint16_t* y;            // bf16 [m][ldy]
   float* partial;         // fp32 [splits][m][rows_total] when splits > 1
+  uint64_t* flags;        // [rows_total / 64][splits] split-K arrival flags
+  uint64_t token;         // unique per call; tags this call's flags
   int m, k;
   int64_t k_pad;          // prepared row length in codes
   int64_t kgroups;        // prepared scale bytes per row
+  int64_t ksegs;          // 32-code segments per prepared row
   int nslab;              // k_pad / kSlabK
   int splits;
   int n_proj;             // real rows per projection
@@ -80,23 +103,13 @@ struct GemvArgs {
   float gscale[2];        // global scale per projection (1 for MXFP4)
 };
 
-struct ReduceArgs {
-  const float* partial;
-  uint16_t* y;
-  int m, splits;
-  int n_proj;
-  int64_t n_proj_pad, rows_total, ldy;
-  int projections;
-  float gscale[2];
-};
-
 struct MfmaArgs {
   const uint16_t* x;      // bf16 [m][k]
   const uint8_t* codes;
   const uint8_t* scales;
   uint16_t* y;
   int m, k;
-  int64_t k_pad, kgroups;
+  int64_t k_pad, kgroups, ksegs;
   int n_proj;
   int64_t n_proj_pad;
   int projections;
@@ -109,7 +122,7 @@ struct MfmaArgs {
 hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,
                           uint8_t* prep_codes, uint8_t* prep_scales, hipStream_t stream);
 hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
-hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,
                           float gscale, float* out, hipStream_t stream);

@@ -1,5 +1,5 @@
-// Decode-shaped W4A16 FP4 GEMV (m <= 8 activation rows) for gfx950, plus the
-// deterministic split-K reduce.
+// Decode-shaped W4A16 FP4 GEMV on the VALU (m = 1, 2 activation rows) for
+// gfx950, with a deterministic split-K reduction in the same launch.
 //
 // What it computes: y[m, n] = G * sum_k x[m, k] * E2M1(code[n, k]) * S(n, k/g)
 // ("native MXFP4 keep-quant", vllm.cpp PR #38, commit list: W4A16 GEMM at
@@ -31,23 +31,24 @@
 //     step a lane keeps half of its partial sums and trades the other half
 //     with its partner, so 8*M sums take about 2*8*M shuffles instead of
 //     5*8*M.
-//   * K split: partial sums go to a caller workspace [splits][m][rows] and a
-//     second kernel adds them in split order.  The split count depends on
-//     (k, fmt, rows per projection) only, so summation order -- and hence
-//     every output bit -- is the same for any m <= 8 and for the fused gate_up
-//     launch as for the two separate ones.  There are no atomics or locks, so
-//     the workspace never needs zeroing (unlike the spin-lock workspace whose
-//     missing memset hung the pages' engine: "re-verify 27B NVFP4 on the
-//     nvidia ModelOpt checkpoint", section "Rewrite/binding grid").
-#include "fp4_common.hpp"
-#include "fp4_device.hpp"
+//   * K split: each (tile, split) workgroup stores its partial sums in a
+//     caller workspace [splits][m][rows]; the last workgroup of a tile to
+//     arrive adds them in split order and writes y, in the same launch (see
+//     splitk_finish).  The split count depends on (k, fmt, rows per
+//     projection) only, so summation order -- and hence every output bit -- is
+//     the same for any m handled by this kernel and for the fused gate_up
+//     launch as for the two separate ones.  There are no locks and nothing
+//     waits, so the workspace never needs zeroing (unlike the spin-lock
+//     workspace whose missing memset hung the pages' engine: "re-verify 27B
+//     NVFP4 on the nvidia ModelOpt checkpoint", section "Rewrite/binding
+//     grid").
+#include "decode_common.hpp"
 
 namespace fp4 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kDecodeThreads;
 constexpr int kTeamLanes = 32;
-constexpr int kChunksPerSlab = kSlabK / 8;  // 16-byte x chunks (8 bf16) per slab
 
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int c) {
   return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
@@ -58,6 +59,52 @@ __device__ __forceinline__ int xs_index(int lb, int sub) {
   return (lb << 2) | ((sub + (lb >> 1)) & 3);
 }
 
+// Value of `v` held by lane (lane ^ o) of the same 32-lane team.  o = 1, 2:
+// DPP quad permutes; o = 4, 8: DPP half-row / row mirrors, which pair lane i
+// with 7 - i / 15 - i -- not lane ^ o, but the same partition into a lower
+// (bit o clear) and an upper half, which is all the butterfly needs;
+// o = 16: ds_swizzle-free bpermute across the two 16-lane rows.
+template <int O>
+__device__ __forceinline__ float partner(float v) {
+  const int iv = __float_as_int(v);
+  int r;
+  if constexpr (O == 1) r = __builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);       // quad_perm [1,0,3,2]
+  else if constexpr (O == 2) r = __builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  else if constexpr (O == 4) r = __builtin_amdgcn_update_dpp(0, iv, 0x141, 0xF, 0xF, false); // row_half_mirror
+  else if constexpr (O == 8) r = __builtin_amdgcn_update_dpp(0, iv, 0x140, 0xF, 0xF, false); // row_mirror
+  else return __shfl_xor(v, O, kTeamLanes);
+  return __int_as_float(r);
+}
+
+// One butterfly step per lane bit o = 16, 8, 4, 2, 1.  While a lane holds
+// more than one partial sum it keeps one half (the upper half if bit o of its
+// lane is set) and adds the partner's copy of that half; with one sum left it
+// adds the partner's sum.  COUNT is the number of sums held before the step.
+template <int COUNT, int VP, int STEP>
+struct Butterfly {
+  __device__ __forceinline__ static void run(float (&v)[VP], int lane, int& base, int& plain_mask) {
+    if constexpr (STEP < 5) {
+      constexpr int O = 16 >> STEP;
+      const bool upper = (lane & O) != 0;
+      if constexpr (COUNT > 1) {
+        constexpr int HALF = COUNT / 2;
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+          const float send = upper ? v[i] : v[i + HALF];
+          const float keep = upper ? v[i + HALF] : v[i];
+          v[i] = keep + partner<O>(send);
+        }
+        if (upper) base += HALF;
+        Butterfly<HALF, VP, STEP + 1>::run(v, lane, base, plain_mask);
+      } else {
+        v[0] += partner<O>(v[0]);
+        plain_mask |= O;
+        Butterfly<1, VP, STEP + 1>::run(v, lane, base, plain_mask);
+      }
+    }
+  }
+};
+
 template <int M, int FMT>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   __shared__ uint4 xs[M][kGemvMaxSlabsPerSplit * kChunksPerSlab];
@@ -66,27 +113,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   const int team = tid >> 5;
   const int lane = tid & (kTeamLanes - 1);
   const int split = blockIdx.y;
-  const int slab0 = static_cast<int>(static_cast<int64_t>(split) * a.nslab / a.splits);
-  const int slab1 = static_cast<int>(static_cast<int64_t>(split + 1) * a.nslab / a.splits);
-  const int nsl = slab1 - slab0;
-
-  // ---- stage x[:, 1024*slab0 : 1024*slab1) in LDS, zero beyond k ----
-  const int chunks = nsl * kChunksPerSlab;
-  for (int c = tid; c < M * chunks; c += kThreads) {
-    const int m = c / chunks;
-    const int cc = c - m * chunks;
-    const int64_t kk = static_cast<int64_t>(slab0) * kSlabK + cc * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (kk < a.k) v = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(m) * a.k + kk);
-    xs[m][xs_index(cc >> 2, cc & 3)] = v;
-  }
-  __syncthreads();
-
+  const SlabRange sr = split_slabs(a, split);
+  const int slab0 = sr.first;
+  const int nsl = sr.count;
   // ---- this team's 8 rows ----
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kGemvTileRows + team * kGemvRowsPerTeam;
   const int64_t row_bytes = a.k_pad / 2;
   const uint8_t* cptr = a.codes + row0 * row_bytes + lane * 16;
-  const uint8_t* sptr = a.scales + (row0 / kRowGroup) * a.kgroups * kRowGroup;
+  // Scales: this team's 8 rows are one half (h) of a 16-row scale group.
+  const uint8_t* sptr = a.scales + ((row0 / kRowGroup) * a.ksegs * kRowGroup + (row0 & 8)) * scales_per_seg(FMT);
 
   float acc[kGemvRowsPerTeam][M];
 #pragma unroll
@@ -100,17 +135,20 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
     for (int r = 0; r < kGemvRowsPerTeam; ++r)
       qq[r] = load_stream16(cptr + r * row_bytes + static_cast<int64_t>(slab) * (kSlabK / 2));
+    // Segment (slab * 32 + lane): MXFP4 8 bytes (row r at byte r), NVFP4 16
+    // bytes (row r, group j at byte 2r + j).
+    const uint8_t* sp = sptr + (static_cast<int64_t>(slab) * kTeamLanes + lane) * kRowGroup * scales_per_seg(FMT);
     if constexpr (FMT == kFmtMxfp4) {
-      const uint2 t = *reinterpret_cast<const uint2*>(
-          sptr + (static_cast<int64_t>(slab) * kTeamLanes + lane) * kRowGroup);
+      const uint2 t = *reinterpret_cast<const uint2*>(sp);
       s = make_uint4(t.x, t.y, 0u, 0u);
     } else {
-      s = *reinterpret_cast<const uint4*>(
-          sptr + (static_cast<int64_t>(slab) * kTeamLanes + lane) * 2 * kRowGroup);
+      s = *reinterpret_cast<const uint4*>(sp);
     }
   };
 
+  // Start the weight stream first, then stage x while those loads fly.
   load_slab(slab0, q, sc);
+  stage_x<M>(a, slab0, nsl, xs, [](int, int cc) { return xs_index(cc >> 2, cc & 3); });
   for (int j = 0; j < nsl; ++j) {
     uint4 qn[kGemvRowsPerTeam];
     uint4 scn = sc;
@@ -154,13 +192,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int m = 0; m < M; ++m) xv[h][m] = xs[m][xs_index(lb, 2 * grp + h)];
-        const uint32_t sword = grp == 0 ? (sc.x) : (sc.z);
-        const uint32_t sword_hi = grp == 0 ? (sc.y) : (sc.w);
 #pragma unroll
         for (int r = 0; r < kGemvRowsPerTeam; ++r) {
-          const uint32_t sw = r < 4 ? sword : sword_hi;
+          const uint32_t sw = u4_get(sc, r >> 1);
           float s;
-          switch (r & 3) {
+          switch (2 * (r & 1) + grp) {
             case 0: s = e4m3_to_f32<0>(sw); break;
             case 1: s = e4m3_to_f32<1>(sw); break;
             case 2: s = e4m3_to_f32<2>(sw); break;
@@ -213,27 +249,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   int base = 0;        // index of v[0] in the original numbering
   int plain_mask = 0;  // lane bits summed over without halving
   constexpr int kFinal = VP > 32 ? VP / 32 : 1;
-#pragma unroll
-  for (int step = 0; step < 5; ++step) {
-    const int o = 16 >> step;
-    const bool upper = (lane & o) != 0;
-    const int count = VP >> step;  // values held before this step
-    if (count > 1) {
-      const int half = count >> 1;
-#pragma unroll
-      for (int i = 0; i < VP / 2; ++i) {
-        if (i < half) {
-          const float send = upper ? v[i] : v[i + half];
-          const float keep = upper ? v[i + half] : v[i];
-          v[i] = keep + __shfl_xor(send, o, kTeamLanes);
-        }
-      }
-      if (upper) base += half;
-    } else {
-      v[0] += __shfl_xor(v[0], o, kTeamLanes);
-      plain_mask |= o;
-    }
-  }
+  Butterfly<VP, VP, 0>::run(v, lane, base, plain_mask);
 
   if ((lane & plain_mask) == 0) {
 #pragma unroll
@@ -250,27 +266,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
             a.y[static_cast<int64_t>(m) * a.ldy + static_cast<int64_t>(h) * a.n_proj + lr] =
                 f32_to_bf16_rne(v[i] * a.gscale[h]);
         } else {
-          a.partial[(static_cast<int64_t>(split) * M + m) * a.rows_total + row] = v[i];
+          store_partial(a.partial + (static_cast<int64_t>(split) * M + m) * a.rows_total + row, v[i]);
         }
       }
     }
   }
-}
-
-__global__ __launch_bounds__(256) void reduce_kernel(const ReduceArgs a) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(a.m) * a.rows_total;
-  if (i >= total) return;
-  const int m = static_cast<int>(i / a.rows_total);
-  const int64_t row = i - static_cast<int64_t>(m) * a.rows_total;
-  const int h = static_cast<int>(row / a.n_proj_pad);
-  const int64_t lr = row - static_cast<int64_t>(h) * a.n_proj_pad;
-  if (lr >= a.n_proj) return;
-  const int64_t stride = static_cast<int64_t>(a.m) * a.rows_total;
-  float s = a.partial[i];
-  for (int sp = 1; sp < a.splits; ++sp) s += a.partial[i + sp * stride];
-  a.y[static_cast<int64_t>(m) * a.ldy + static_cast<int64_t>(h) * a.n_proj + lr] =
-      f32_to_bf16_rne(s * a.gscale[h]);
+  if (a.splits > 1) splitk_finish<M>(a, blockIdx.x, split);
 }
 
 template <int FMT>
@@ -279,12 +280,6 @@ hipError_t launch_gemv_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
   switch (a.m) {
     case 1: hipLaunchKernelGGL((gemv_kernel<1, FMT>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((gemv_kernel<2, FMT>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((gemv_kernel<3, FMT>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((gemv_kernel<4, FMT>), grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((gemv_kernel<5, FMT>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((gemv_kernel<6, FMT>), grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL((gemv_kernel<7, FMT>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((gemv_kernel<8, FMT>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -298,13 +293,6 @@ hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* gri
   if (block_out) *block_out = dim3(kThreads);
   return fmt == kFmtNvfp4 ? launch_gemv_fmt<kFmtNvfp4>(a, grid, stream)
                           : launch_gemv_fmt<kFmtMxfp4>(a, grid, stream);
-}
-
-hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream) {
-  const int64_t total = static_cast<int64_t>(a.m) * a.rows_total;
-  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
-  hipLaunchKernelGGL(reduce_kernel, grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
 }
 
 }  // namespace fp4

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(const MfmaArgs a) {
     for (int j = 0; j < kWaveTiles; ++j) {
       const int64_t row = n0 + 16 * j + li;
       const uint32_t word = *reinterpret_cast<const uint32_t*>(a.codes + row * row_bytes + kk / 2);
-      const uint32_t sb = a.scales[((row / kRowGroup) * a.kgroups + kk / G) * kRowGroup + (row % kRowGroup)];
+      const uint32_t sb = a.scales[scale_offset(row, kk / G, a.ksegs, scales_per_seg(FMT))];
       decode_b<FMT>(word, sb, bf[j]);
     }
 #pragma unroll

@@ -10,9 +10,11 @@
 // so a weight is stored once):
 //   codes  [n_pad][k_pad/2]: the same bytes, rows padded to a multiple of 256
 //          and each row padded to a multiple of 1024 codes, padding zero;
-//   scales [n_pad/8][k_pad/g][8]: within each group of 8 rows, the 8 scale
-//          bytes of one k-group are adjacent, so a GEMV lane fetches the scales
-//          of its 8 rows with one 8- or 16-byte load; padding zero.
+//   scales [n_pad/16][k_pad/32][16][P]: for each group of 16 rows and each
+//          32-code segment, the 16 rows' P scale bytes are adjacent (P = 2 for
+//          NVFP4, 1 for MXFP4), so a decode lane fetches the scales of its rows
+//          with one 8- or 16-byte load and a wave's loads are contiguous;
+//          padding zero.
 // Zero padding decodes to zero weights (code 0 is +0), so padded rows and
 // columns add nothing to any sum.
 #include "fp4_common.hpp"
@@ -36,23 +38,32 @@ __global__ __launch_bounds__(256) void prepare_codes_kernel(const uint8_t* __res
   *reinterpret_cast<uint4*>(out + row * (k_pad / 2) + c * 16) = v;
 }
 
-// One thread per (row group, k-group): gathers 8 rows' scale bytes.
+// One thread per (16-row group, 32-code segment): gathers the 16 rows' P
+// scale bytes of the segment (P = 2 for NVFP4, 1 for MXFP4).
+template <int P>
 __global__ __launch_bounds__(256) void prepare_scales_kernel(const uint8_t* __restrict__ in, int n,
-                                                             int64_t kg_real, int64_t n_pad, int64_t kgroups,
+                                                             int64_t kg_real, int64_t n_pad, int64_t ksegs,
                                                              uint8_t* __restrict__ out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= (n_pad / kRowGroup) * kgroups) return;
-  const int64_t rg = i / kgroups;
-  const int64_t kg = i - rg * kgroups;
-  uint32_t lo = 0, hi = 0;
+  if (i >= (n_pad / kRowGroup) * ksegs) return;
+  const int64_t rg = i / ksegs;
+  const int64_t seg = i - rg * ksegs;
+  uint32_t w[4 * P] = {};
+#pragma unroll
   for (int r = 0; r < kRowGroup; ++r) {
     const int64_t row = rg * kRowGroup + r;
-    uint32_t b = 0;
-    if (row < n && kg < kg_real) b = in[row * kg_real + kg];
-    if (r < 4) lo |= b << (8 * r);
-    else hi |= b << (8 * (r - 4));
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int64_t kg = seg * P + j;
+      uint32_t b = 0;
+      if (row < n && kg < kg_real) b = in[row * kg_real + kg];
+      const int byte = r * P + j;
+      w[byte >> 2] |= b << (8 * (byte & 3));
+    }
   }
-  *reinterpret_cast<uint2*>(out + i * kRowGroup) = make_uint2(lo, hi);
+  uint4* o = reinterpret_cast<uint4*>(out + i * kRowGroup * P);
+#pragma unroll
+  for (int q = 0; q < P; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 
 // One thread per 8 consecutive weights (one 32-bit code word).
@@ -60,7 +71,7 @@ __global__ __launch_bounds__(256) void prepare_scales_kernel(const uint8_t* __re
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, int n, int k,
-                                                      int64_t k_pad, int64_t kgroups, float gscale,
+                                                      int64_t k_pad, int64_t ksegs, float gscale,
                                                       float* __restrict__ out) {
   constexpr int G = group_size(FMT);
   const int64_t words_per_row = k / 8;
@@ -70,7 +81,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t wi = i - row * words_per_row;
   const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + row * (k_pad / 2) + wi * 4);
   const int64_t kg = (wi * 8) / G;
-  const uint32_t sb = scales[((row / kRowGroup) * kgroups + kg) * kRowGroup + (row % kRowGroup)];
+  const uint32_t sb = scales[scale_offset(row, kg, ksegs, scales_per_seg(FMT))];
   f32x2_t p[4];
   if constexpr (FMT == kFmtMxfp4) {
     const float sop = e8m0_as_scale_operand(sb);
@@ -105,9 +116,15 @@ hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, in
                      stream, codes, n, k, s.n_pad, s.k_pad, prep_codes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t items = (s.n_pad / kRowGroup) * s.kgroups;
-  hipLaunchKernelGGL(prepare_scales_kernel, dim3(static_cast<unsigned>((items + 255) / 256)), dim3(256), 0, stream,
-                     scales, n, static_cast<int64_t>(k / group_size(fmt)), s.n_pad, s.kgroups, prep_scales);
+  const int64_t items = (s.n_pad / kRowGroup) * s.ksegs;
+  const dim3 grid(static_cast<unsigned>((items + 255) / 256));
+  const int64_t kg_real = k / group_size(fmt);
+  if (fmt == kFmtNvfp4)
+    hipLaunchKernelGGL(prepare_scales_kernel<2>, grid, dim3(256), 0, stream, scales, n, kg_real, s.n_pad, s.ksegs,
+                       prep_scales);
+  else
+    hipLaunchKernelGGL(prepare_scales_kernel<1>, grid, dim3(256), 0, stream, scales, n, kg_real, s.n_pad, s.ksegs,
+                       prep_scales);
   return hipGetLastError();
 }
 
@@ -118,10 +135,10 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n, in
   const dim3 grid(static_cast<unsigned>((items + 255) / 256));
   if (fmt == kFmtNvfp4)
     hipLaunchKernelGGL(dequant_kernel<kFmtNvfp4>, grid, dim3(256), 0, stream, codes, scales, n, k, s.k_pad,
-                       s.kgroups, gscale, out);
+                       s.ksegs, gscale, out);
   else
     hipLaunchKernelGGL(dequant_kernel<kFmtMxfp4>, grid, dim3(256), 0, stream, codes, scales, n, k, s.k_pad,
-                       s.kgroups, 1.0f, out);
+                       s.ksegs, 1.0f, out);
   return hipGetLastError();
 }
 

@@ -65,7 +65,8 @@ enum fp4_status {
 
 /* Which kernel a call ran (filled when the caller passes a non-null pointer). */
 typedef struct fp4_dispatch_info {
-  int kernel;  /* 0 = decode GEMV (m <= 8), 1 = MFMA tile GEMM (m > 8) */
+  int kernel;  /* 0 = VALU decode GEMV, 2 = MFMA decode GEMV (both m <= 8),
+                  1 = MFMA tile GEMM (m > 8) */
   int splits;  /* number of K splits (1 = no split, no reduce launch) */
   int grid_x;  /* workgroups along the output rows */
   int grid_y;  /* workgroups along the second grid axis (splits or m tiles) */
@@ -77,8 +78,9 @@ typedef struct fp4_dispatch_info {
  * The prepared layout (written by fp4_prepare, read by every compute call):
  *   codes: uint8 [n_pad][k_pad/2], the canonical code bytes, zero padded,
  *          with n_pad = n rounded up to 256 and k_pad = k rounded up to 1024;
- *   scales: uint8 [n_pad/8][k_pad/g][8]: within each group of 8 rows, the 8
- *          scale bytes of one k-group are contiguous; zero padded.
+ *   scales: uint8 [n_pad/16][k_pad/32][16][32/g]: for each group of 16 rows
+ *          and each 32-code segment, the 16 rows' scale bytes of the segment
+ *          (2 per row for NVFP4, 1 for MXFP4) are contiguous; zero padded.
  * A prepared gate_up weight is a prepared gate weight followed by a prepared
  * up weight, in both buffers (twice these sizes).
  * Pure host function; never touches the GPU.
@@ -126,9 +128,9 @@ int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* b
  *   workspace_dev / workspace_bytes  scratch of fp4_workspace_bytes(m, n, k, fmt, 1);
  *   info_out  optional, may be NULL.
  * Accumulation is float32.  The order of every sum depends only on (k, fmt, n)
- * and the kernel chosen by m (m <= 8 or m > 8), so results are deterministic
- * run to run and row m of a call with m <= 8 rows equals the same row computed
- * alone.
+ * and on which kernel m selects (fp4_dispatch_info.kernel), so results are
+ * deterministic run to run, and a row's result does not depend on the other
+ * rows of the call as long as m selects the same kernel.
  * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list (the W4A16
  * entry points take bf16 x and the packed weight to bf16 y); "keep the ModelOpt
  * NVFP4 lm_head packed" (vllm.cpp PR #263), section "Why this row matters"

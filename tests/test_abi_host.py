@@ -77,9 +77,11 @@ def test_workspace_bytes_policy():
     # m > 8 runs the MFMA kernel without a workspace; the lm_head GEMV splits
     # K=5120 (5 slabs of 1024) in two; splitting never depends on m.
     assert fp4.fp4_workspace_bytes(16, 17408, 5120, NV) == 0
+    # splits * m * rows fp32 partials, then one 8-byte flag per (64-row tile, split).
     ws1 = fp4.fp4_workspace_bytes(1, 248320, 5120, NV)
     ws8 = fp4.fp4_workspace_bytes(8, 248320, 5120, NV)
-    assert ws1 == 2 * 1 * 248320 * 4 and ws8 == 8 * ws1
+    flags = 248320 // 64 * 2 * 8
+    assert ws1 == 2 * 1 * 248320 * 4 + flags and ws8 == 2 * 8 * 248320 * 4 + flags
     # gate_up: two projections, each split like the separate linear.
     one = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 1)
     two = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 2)
@@ -136,5 +138,10 @@ def test_split_count_independent_of_m_and_fusion():
     # recovers the split count, which must not change with m.
     for n, k, fmt in [(5120, 17408, NV), (5120, 6144, NV), (12288, 4096, MX), (248320, 5120, NV)]:
         rows = -(-n // 256) * 256
-        counts = {fp4.fp4_workspace_bytes(m, n, k, fmt) // (4 * m * rows) for m in range(1, 9)}
+        counts = set()
+        for m in range(1, 9):
+            ws = fp4.fp4_workspace_bytes(m, n, k, fmt)
+            per_split = 4 * m * rows + rows // 64 * 8
+            assert ws % per_split == 0
+            counts.add(ws // per_split)
         assert len(counts) == 1

@@ -16,6 +16,7 @@ pytestmark = pytest.mark.gpu
 
 NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
 GS = {NV: 16, MX: 32}
+DECODE_MFMA_MIN_M = 3   # m at which the decode path switches from v_dot2 to MFMA
 
 
 def _canon_bits(a):
@@ -67,7 +68,7 @@ def test_dequant_synthetic_weights(fmt, n, k):
 
 def test_prepared_layout_bytes():
     # Codes: canonical bytes, zero padded to [n_pad, k_pad/2]; scales: within
-    # groups of 8 rows the 8 bytes of one k-group are adjacent.
+    # groups of 16 rows, the rows' bytes of one 32-code segment are adjacent.
     n, k, fmt = 300, 1056, NV
     packed, scales, _ = _quantized(fmt, n, k)
     pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
@@ -77,7 +78,8 @@ def test_prepared_layout_bytes():
     kg_pad = k_pad // 16
     s_pad = np.zeros((n_pad, kg_pad), np.uint8)
     s_pad[:n, :k // 16] = scales
-    want_s = s_pad.reshape(n_pad // 8, 8, kg_pad).transpose(0, 2, 1).reshape(-1)
+    # [n_pad/16][k_pad/32][16][2] for NVFP4 (two 16-code groups per segment)
+    want_s = s_pad.reshape(n_pad // 16, 16, kg_pad // 2, 2).transpose(0, 2, 1, 3).reshape(-1)
     assert np.array_equal(pc.cpu().numpy(), want_c.reshape(-1))
     assert np.array_equal(ps.cpu().numpy(), want_s)
 
@@ -104,7 +106,7 @@ def test_gemv_matches_oracle(fmt, n, k, m):
     xbits = synth.activations(synth.TINY, m, k)
     info = fp4.fp4_dispatch_info()
     y = _run_linear(packed, scales, g, fmt, n, k, xbits, info)
-    assert info.kernel == 0
+    assert info.kernel == (0 if m < DECODE_MFMA_MIN_M else 2)
     y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
     assert_close(y_host(y), y_ref, "gemv fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
 
@@ -154,14 +156,17 @@ def test_gate_up_fused_equals_split(fmt, nh, k, m):
 
 @pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 384, 3072), (NV, 256, 17408), (NV, 300, 5120)])
 def test_gemv_batch_invariance(fmt, n, k):
-    # Row i of an m-row call equals the same row computed alone, bit for bit.
+    # Within one decode kernel, row i of an m-row call equals the same row of
+    # a call with more rows, bit for bit (the summation order never depends on m).
     packed, scales, g = _quantized(fmt, n, k)
     pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
     x8 = synth.activations(synth.TINY, 8, k)
     y8 = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x8), pc, ps, n, float(g), fmt))
+    ylo = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x8[:DECODE_MFMA_MIN_M - 1]), pc, ps, n, float(g), fmt))
     for m in range(1, 9):
         ym = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x8[:m]), pc, ps, n, float(g), fmt))
-        assert np.array_equal(ym, y8[:m]), m
+        ref = y8 if m >= DECODE_MFMA_MIN_M else ylo
+        assert np.array_equal(ym, ref[:m]), m
 
 
 @pytest.mark.parametrize("fmt,n,k,m", [(NV, 300, 5120, 8), (MX, 256, 17408, 3), (NV, 640, 2048, 64)])
@@ -175,6 +180,23 @@ def test_deterministic_and_workspace_poison(fmt, n, k, m):
         ws = torch.full((max(need, 16),), fill, dtype=torch.uint8, device=DEV)
         outs.append(y_host_bits(fp4.fp4_w4a16_linear(xd, pc, ps, n, float(g), fmt, workspace=ws)))
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 17408, 1), (NV, 640, 6144, 8), (MX, 1024, 4096, 4)])
+def test_split_k_handshake_repeated(fmt, n, k, m):
+    # The split-K finish exchanges partials between workgroups in one launch;
+    # 40 back-to-back calls on one workspace must all give the same bytes.
+    packed, scales, g = _quantized(fmt, n, k, tensor=5)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    xd = x_dev(synth.activations(synth.TINY, m, k))
+    info = fp4.fp4_dispatch_info()
+    ws = torch.full((fp4.fp4_workspace_bytes(m, n, k, fmt),), 0x5A, dtype=torch.uint8, device=DEV)
+    ys = [fp4.fp4_w4a16_linear(xd, pc, ps, n, float(g), fmt, workspace=ws, info=info) for _ in range(40)]
+    assert info.splits > 1
+    first = y_host_bits(ys[0])
+    assert all(np.array_equal(first, y_host_bits(y)) for y in ys[1:])
+    y_ref = oracle.linear(oracle.bf16_bits_to_f32(synth.activations(synth.TINY, m, k)), packed, scales, k, fmt, g)
+    assert_close(oracle.bf16_bits_to_f32(first).astype(np.float64), y_ref, "split-K repeated")
 
 
 def test_zero_rows_is_a_no_op():
