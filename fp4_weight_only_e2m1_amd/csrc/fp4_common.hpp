@@ -61,10 +61,12 @@ inline PreparedShape prepared_shape(int n, int k, int fmt) {
   return s;
 }
 
-// Number of K splits for the decode GEMV.  A function of (k, fmt, n per
-// projection) only -- never of m or of how many projections share the launch --
-// so a row's summation order is the same at every m <= 8 and in the fused
-// gate_up launch as in the separate ones.
+// Number of K splits of the decode kernels: as few as the LDS budget for x
+// allows (4 slabs of 1024 codes per split).  Splitting further only adds the
+// cross-workgroup finish; measured on MI355X it never paid for the extra
+// parallelism at the decode shapes.  A function of k alone, so summation order
+// -- and every output bit -- is the same at every m a kernel serves and in the
+// fused gate_up launch as in the separate ones.
 // Workspace of a decode call: the split-K partials, then the arrival flags.
 inline int64_t decode_workspace_bytes(int64_t splits, int m, int64_t rows_total) {
   if (splits <= 1) return 0;
@@ -72,13 +74,10 @@ inline int64_t decode_workspace_bytes(int64_t splits, int m, int64_t rows_total)
 }
 
 inline int gemv_splits(int n_proj, int k, int fmt) {
+  (void)n_proj;
   (void)fmt;
   const int64_t nslab = round_up(k, kSlabK) / kSlabK;
-  const int64_t tiles = round_up(n_proj, kRowAlign) / kGemvTileRows;
-  int64_t s = (nslab + kGemvMaxSlabsPerSplit - 1) / kGemvMaxSlabsPerSplit;
-  // Enough workgroups to cover the chip twice over.
-  while (s < nslab && tiles * s < 2 * kTargetCUs) ++s;
-  return static_cast<int>(s);
+  return static_cast<int>((nslab + kGemvMaxSlabsPerSplit - 1) / kGemvMaxSlabsPerSplit);
 }
 
 struct GemvArgs {
