@@ -187,6 +187,9 @@ def main():
                     help="replay the timed calls from a captured HIP graph, or launch them one by one")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device-to-device copies of MIB MiB (reference for the HBM "
+                         "byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -198,6 +201,16 @@ def main():
     import numpy as np
     import fp4_weight_only_e2m1_amd as fp4
     import synth
+
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 10}), flush=True)
+        return
 
     name = args.workload
     wid, fmt, n, k, proj, m_default = WORKLOADS[name]
