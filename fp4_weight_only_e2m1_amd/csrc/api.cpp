@@ -31,7 +31,9 @@ int check_nk(int n, int k) {
 int check_m(int m) { return (m < 0 || m > FP4_MAX_M) ? FP4_EINVAL : FP4_OK; }
 
 size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
-  if (m < 1 || m > fp4::kGemvMaxM) return 0;
+  // Only the VALU GEMV (m below the MFMA-decode crossover) splits K across
+  // workgroups; the MFMA kernels keep all of K in one workgroup.
+  if (m < 1 || m >= fp4::kDecodeMfmaMinM) return 0;
   const int splits = fp4::gemv_splits(n_proj, k, fmt);
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
   return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total));
@@ -84,8 +86,9 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.k_pad = ps.k_pad;
     a.kgroups = ps.kgroups;
     a.ksegs = ps.ksegs;
+    const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
     a.nslab = static_cast<int>(ps.k_pad / fp4::kSlabK);
-    a.splits = fp4::gemv_splits(n_proj, k, fmt);
+    a.splits = on_mfma ? 1 : fp4::gemv_splits(n_proj, k, fmt);
     a.n_proj = n_proj;
     a.n_proj_pad = ps.n_pad;
     a.projections = projections;
@@ -98,7 +101,6 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
                                             static_cast<int64_t>(a.splits) * m * a.rows_total * 4);
       a.token = next_token();
     }
-    const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
     hipError_t e = on_mfma ? fp4::launch_decode_mfma(a, fmt, stream, &grid, &block)
                            : fp4::launch_gemv(a, fmt, stream, &grid, &block);
     if (e != hipSuccess) return FP4_EHIP;

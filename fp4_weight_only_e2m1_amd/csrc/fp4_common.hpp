@@ -22,10 +22,26 @@ constexpr int kGemvTeams = 8;        // teams per 256-thread workgroup
 constexpr int kGemvTileRows = kGemvRowsPerTeam * kGemvTeams;  // 64
 constexpr int kGemvMaxSlabsPerSplit = 4;  // x staged in LDS: 8 rows * 4096 k * 2 B = 64 KiB
 constexpr int kGemvMaxM = 8;
+constexpr int kTargetCUs = 256;      // MI355X compute units
 // m from which the decode path contracts on MFMA instead of VALU v_dot2
 // (measured crossover on MI355X: the VALU GEMV is faster at m = 1, 2).
 constexpr int kDecodeMfmaMinM = 3;
-constexpr int kTargetCUs = 256;      // MI355X compute units
+// Waves of an MFMA-decode workgroup; K is dealt to them in 128-code blocks.
+constexpr int kDecodeMfmaWaves = 8;
+// k-blocks each MFMA-decode wave keeps in flight.
+constexpr int kDecodeMfmaDepth = 2;
+
+// 16-row blocks per MFMA-decode workgroup.  More rows per workgroup means
+// each activation fragment a wave loads serves more weight rows (activation
+// traffic is 4m/rows of the weight traffic); fewer means more workgroups.
+// Measured on MI355X: 4 rows blocks once that still leaves one workgroup per
+// CU, else 2 down to half a workgroup per CU.  Only changes which rows a
+// workgroup holds, never an output's summation order.
+inline int decode_mfma_row_blocks(int64_t rows_total) {
+  if (rows_total / 64 >= kTargetCUs) return 4;
+  if (rows_total / 32 >= kTargetCUs / 2) return 2;
+  return 1;
+}
 
 inline constexpr int group_size(int fmt) { return fmt == kFmtNvfp4 ? 16 : 32; }
 // Scale bytes per 32-code segment of a row: 2 for NVFP4, 1 for MXFP4.

@@ -112,7 +112,8 @@ int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scale
                         uint8_t* prep_codes_dev, uint8_t* prep_scales_dev, hipStream_t stream);
 
 /*
- * Workspace a compute call needs, in bytes (0 when none).  `projections` is 1
+ * Workspace a compute call needs, in bytes (0 when none; only the m = 1, 2
+ * decode kernel with k > 4096 uses one, for split-K partials and flags).  `projections` is 1
  * for fp4_w4a16_linear (n = output features) and 2 for fp4_w4a16_gate_up
  * (n = n_half).  Pure host function.
  */

@@ -182,7 +182,7 @@ def test_deterministic_and_workspace_poison(fmt, n, k, m):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-@pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 17408, 1), (NV, 640, 6144, 8), (MX, 1024, 5120, 4)])
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 17408, 1), (NV, 640, 6144, 2), (MX, 1024, 5120, 1)])
 def test_split_k_handshake_repeated(fmt, n, k, m):
     # The split-K finish exchanges partials between workgroups in one launch;
     # 40 back-to-back calls on one workspace must all give the same bytes.
