@@ -31,11 +31,13 @@ int check_nk(int n, int k) {
 int check_m(int m) { return (m < 0 || m > FP4_MAX_M) ? FP4_EINVAL : FP4_OK; }
 
 size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
-  // Only the VALU GEMV (m below the MFMA-decode crossover) splits K across
-  // workgroups; the MFMA kernels keep all of K in one workgroup.
-  if (m < 1 || m >= fp4::kDecodeMfmaMinM) return 0;
-  const int splits = fp4::gemv_splits(n_proj, k, fmt);
+  // The VALU GEMV (m below the MFMA-decode crossover) splits K across
+  // workgroups; the MFMA decode kernel keeps all of K in one workgroup; the
+  // prefill GEMM splits K only for the tail tiles that do not fill a round.
+  if (m < 1 || (m >= fp4::kDecodeMfmaMinM && m <= fp4::kGemvMaxM)) return 0;
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
+  if (m > fp4::kGemvMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
+  const int splits = fp4::gemv_splits(n_proj, k, fmt);
   return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total));
 }
 
@@ -124,9 +126,11 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.ldy = static_cast<int64_t>(n_proj) * projections;
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
+    a.plan = fp4::gemm_plan(m, a.rows_total, k);
+    if (a.plan.tail_tiles > 0) a.partial = static_cast<float*>(ws);
     hipError_t e = fp4::launch_mfma(a, fmt, stream, &grid, &block);
     if (e != hipSuccess) return FP4_EHIP;
-    if (info) *info = fp4_dispatch_info{1, 1, static_cast<int>(grid.x), static_cast<int>(grid.y),
+    if (info) *info = fp4_dispatch_info{1, a.plan.splits, static_cast<int>(grid.x), static_cast<int>(grid.y),
                                         static_cast<int>(block.x)};
   }
   return FP4_OK;

@@ -118,11 +118,64 @@ struct GemvArgs {
   float gscale[2];        // global scale per projection (1 for MXFP4)
 };
 
+// Prefill GEMM tiling.  A workgroup of kGemmWavesM x 4 waves computes a
+// kGemmBM (activation rows) x kGemmBN (weight rows) tile of y, each wave a
+// 128 x 64 block of it, stepping K by kGemmBK.  kGemmSlots workgroups are
+// resident on the chip at once (two per CU for a 4-wave workgroup).
+constexpr int kGemmWavesM = 1;
+constexpr int kGemmBM = 128 * kGemmWavesM;
+constexpr int kGemmBN = 256;
+constexpr int kGemmBK = 64;
+constexpr int kGemmSlots = kTargetCUs * (kGemmWavesM == 1 ? 2 : 1);
+// Fewest K steps a split of a tail tile is given.
+constexpr int kGemmMinSplitSteps = 8;
+
+// How a prefill call's tiles are spread over the resident workgroups.  Tiles
+// are taken whole while they fill complete rounds of kGemmSlots workgroups
+// ("data-parallel" tiles); the remaining tail tiles, too few to fill the last
+// round, are each cut into `splits` K ranges run by separate workgroups, whose
+// fp32 partial tiles a final launch adds in split order.
+struct GemmPlan {
+  int m_tiles, n_tiles, tiles;
+  int dp_tiles;    // tiles computed whole
+  int tail_tiles;  // tiles computed as `splits` K ranges
+  int splits;
+  int ksteps;      // K steps of a whole tile
+};
+
+inline GemmPlan gemm_plan(int m, int64_t rows_total, int k) {
+  GemmPlan p;
+  p.m_tiles = static_cast<int>((m + kGemmBM - 1) / kGemmBM);
+  p.n_tiles = static_cast<int>(rows_total / kGemmBN);
+  p.tiles = p.m_tiles * p.n_tiles;
+  p.ksteps = static_cast<int>((k + kGemmBK - 1) / kGemmBK);
+  const int tail = p.tiles % kGemmSlots;
+  int s = tail > 0 ? kGemmSlots / tail : 1;
+  const int by_k = p.ksteps / kGemmMinSplitSteps;
+  if (s > by_k) s = by_k;
+  if (s <= 1) {
+    p.dp_tiles = p.tiles;
+    p.tail_tiles = 0;
+    p.splits = 1;
+  } else {
+    p.dp_tiles = p.tiles - tail;
+    p.tail_tiles = tail;
+    p.splits = s;
+  }
+  return p;
+}
+
+// Workspace of a prefill call: fp32 partial tiles [tail_tiles][splits][BM][BN].
+inline int64_t gemm_workspace_bytes(const GemmPlan& p) {
+  return static_cast<int64_t>(p.tail_tiles) * p.splits * kGemmBM * kGemmBN * 4;
+}
+
 struct MfmaArgs {
   const uint16_t* x;      // bf16 [m][k]
   const uint8_t* codes;
   const uint8_t* scales;
   uint16_t* y;
+  float* partial;         // tail partial tiles (workspace)
   int m, k;
   int64_t k_pad, kgroups, ksegs;
   int n_proj;
@@ -130,6 +183,7 @@ struct MfmaArgs {
   int projections;
   int64_t rows_total, ldy;
   float gscale[2];
+  GemmPlan plan;
 };
 
 // Launchers (defined in the .hip files).  Each returns the hipError_t of its

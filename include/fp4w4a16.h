@@ -67,9 +67,12 @@ enum fp4_status {
 typedef struct fp4_dispatch_info {
   int kernel;  /* 0 = VALU decode GEMV, 2 = MFMA decode GEMV (both m <= 8),
                   1 = MFMA tile GEMM (m > 8) */
-  int splits;  /* number of K splits (1 = no split, no reduce launch) */
-  int grid_x;  /* workgroups along the output rows */
-  int grid_y;  /* workgroups along the second grid axis (splits or m tiles) */
+  int splits;  /* K splits: decode kernels split every tile, the tile GEMM only
+                  its tail tiles (1 = no split) */
+  int grid_x;  /* decode: workgroups along the output rows; tile GEMM:
+                  workgroups of its whole-tile launch */
+  int grid_y;  /* decode: workgroups along the second grid axis; tile GEMM:
+                  workgroups of its tail launch (tail tiles x splits, 0 if none) */
   int block;   /* threads per workgroup */
 } fp4_dispatch_info;
 
@@ -112,9 +115,12 @@ int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scale
                         uint8_t* prep_codes_dev, uint8_t* prep_scales_dev, hipStream_t stream);
 
 /*
- * Workspace a compute call needs, in bytes (0 when none; only the m = 1, 2
- * decode kernel with k > 4096 uses one, for split-K partials and flags).  `projections` is 1
- * for fp4_w4a16_linear (n = output features) and 2 for fp4_w4a16_gate_up
+ * Workspace a compute call needs, in bytes (0 when none).  Two kernels use
+ * one, for split-K fp32 partials and arrival flags: the m = 1, 2 decode GEMV
+ * with k > 4096, and the m > 8 tile GEMM when its 128 x 256 output tiles do
+ * not fill whole rounds of the 512 workgroups resident on the chip (the tail
+ * tiles are then split along K; at most 64 MiB).  `projections` is 1 for
+ * fp4_w4a16_linear (n = output features) and 2 for fp4_w4a16_gate_up
  * (n = n_half).  Pure host function.
  */
 int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* bytes_out);
@@ -129,9 +135,11 @@ int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* b
  *   workspace_dev / workspace_bytes  scratch of fp4_workspace_bytes(m, n, k, fmt, 1);
  *   info_out  optional, may be NULL.
  * Accumulation is float32.  The order of every sum depends only on (k, fmt, n)
- * and on which kernel m selects (fp4_dispatch_info.kernel), so results are
- * deterministic run to run, and a row's result does not depend on the other
- * rows of the call as long as m selects the same kernel.
+ * and on which kernel m selects (fp4_dispatch_info.kernel) -- for the tile
+ * GEMM (m > 8) also on m, which decides the tiles summed in K splits -- so
+ * results are deterministic run to run, and for m <= 8 a row's result does
+ * not depend on the other rows of the call as long as m selects the same
+ * kernel.
  * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list (the W4A16
  * entry points take bf16 x and the packed weight to bf16 y); "keep the ModelOpt
  * NVFP4 lm_head packed" (vllm.cpp PR #263), section "Why this row matters"

@@ -73,10 +73,25 @@ def test_prepared_bytes_rejects(lib, n, k, fmt, bad):
     assert lib.fp4_prepared_bytes(n, k, fmt, ctypes.byref(cb), ctypes.byref(sb)) == ST[bad]
 
 
+def _prefill_workspace(m, n, k, projections=1):
+    # Prefill tiles are 128 x 256; 512 workgroups are resident at once.  Tiles
+    # that do not fill a whole round are split along K (at most 512 / tail
+    # ways, at least 8 K steps of 64 each) into fp32 partial tiles.
+    tiles = -(-m // 128) * (projections * (-(-n // 256) * 256) // 256)
+    tail = tiles % 512
+    s = min(512 // tail, -(-k // 64) // 8) if tail else 1
+    return 0 if s <= 1 else tail * s * 128 * 256 * 4
+
+
 def test_workspace_bytes_policy():
-    # m > 8 runs the MFMA kernel without a workspace; the lm_head GEMV splits
-    # K=5120 (5 slabs of 1024) in two; splitting never depends on m.
-    assert fp4.fp4_workspace_bytes(16, 17408, 5120, NV) == 0
+    # m > 8 runs the prefill GEMM, whose tail tiles split K.
+    assert fp4.fp4_workspace_bytes(16, 17408, 5120, NV) == _prefill_workspace(16, 17408, 5120) == 68 * 7 * 131072
+    assert fp4.fp4_workspace_bytes(1024, 17408, 5120, MX) == _prefill_workspace(1024, 17408, 5120) == 32 * 10 * 131072
+    assert fp4.fp4_workspace_bytes(4096, 17408, 5120, NV) == _prefill_workspace(4096, 17408, 5120)
+    assert fp4.fp4_workspace_bytes(65536, 256, 5120, NV) == 0      # 512 tiles: one full round, no tail
+    assert fp4.fp4_workspace_bytes(200, 300, 256, NV) == 0         # 4 K steps: too short to split
+    assert fp4.fp4_workspace_bytes(9, 1024, 12288, MX, 2) == _prefill_workspace(9, 1024, 12288, 2)
+    # The lm_head GEMV splits K=5120 (5 slabs of 1024) in two; splitting never depends on m.
     # splits * m * rows fp32 partials, then one 8-byte flag per (64-row tile, split).
     ws1 = fp4.fp4_workspace_bytes(1, 248320, 5120, NV)
     ws8 = fp4.fp4_workspace_bytes(8, 248320, 5120, NV)

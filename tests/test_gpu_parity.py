@@ -182,10 +182,13 @@ def test_deterministic_and_workspace_poison(fmt, n, k, m):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-@pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 17408, 1), (NV, 640, 6144, 2), (MX, 1024, 5120, 1)])
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 17408, 1), (NV, 640, 6144, 2), (MX, 1024, 5120, 1),
+                                        (NV, 512, 5120, 100), (MX, 300, 4096, 300), (NV, 256, 2080, 40)])
 def test_split_k_handshake_repeated(fmt, n, k, m):
-    # The split-K finish exchanges partials between workgroups in one launch;
-    # 40 back-to-back calls on one workspace must all give the same bytes.
+    # The split-K finish exchanges partials between workgroups in one launch
+    # (decode GEMV splits; prefill tail tiles, the last case with a ragged
+    # final K step); 40 back-to-back calls on one workspace must all give the
+    # same bytes.
     packed, scales, g = _quantized(fmt, n, k, tensor=5)
     pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
     xd = x_dev(synth.activations(synth.TINY, m, k))
