@@ -288,7 +288,7 @@ def main():
         total_bytes += b * args.steps
         total_flops += f * args.steps
         info = d["info"]
-        kern = {0: "gemv_kernel", 2: "decode_mfma_kernel", 1: "mfma_kernel"}[info.kernel]
+        kern = {0: "gemv_kernel", 2: "decode_mfma_kernel", 1: "gemm_kernel"}[info.kernel]
         us = ms_m * 1e3 / args.steps
         rows.append({"m": m, "kernel": "%s<%d,%s>" % (kern, m, "nvfp4" if fmt == 0 else "mxfp4")
                      if info.kernel != 1 else "%s<%s>" % (kern, "nvfp4" if fmt == 0 else "mxfp4"),
