@@ -54,9 +54,12 @@ static_assert(kAChunks % kThreads == 0 && kBChunks % kThreads == 0, "stage split
 template <int FMT>
 struct Cfg {
   static constexpr int P = scales_per_seg(FMT);
-  static constexpr int kSChunks = kGemmBN / kRowGroup * 2 * kRowGroup * P / 16;  // 64 NVFP4, 32 MXFP4
-  static constexpr int kSPerWave = kSChunks / kWaves;
-  static_assert(kSChunks % kWaves == 0, "scale split");
+  // 16-byte chunks of a scale stage: 32 P (64 NVFP4, 32 MXFP4), copied by
+  // the 64 lanes of wave 0 (MXFP4: lanes 32..63 repeat lanes 0..31 into the
+  // second half of a 64-chunk area).
+  static constexpr int kSUsed = kGemmBN / kRowGroup * 2 * kRowGroup * P / 16;
+  static constexpr int kSChunks = 64;
+  static_assert(kSUsed <= kSChunks, "scale stage");
 };
 
 template <int FMT>
@@ -94,22 +97,20 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 // Global -> LDS copies of 16 bytes per lane: lane l's bytes land at LDS
-// address m0 + 16 l, m0 being the same for the whole wave.  Issued as inline
+// address M0 + 16 l, M0 being the same for the whole wave.  Issued as inline
 // asm so that the compiler, which would otherwise guard every later LDS read
 // with a wait for all copies in flight, leaves the waits to the pipeline
-// (wait_vm_barrier); M0 is restored after.  Device code only: the host pass of
-// the compiler cannot parse the asm.
+// (wait_vm_barrier).  M0 is left holding the last LDS address: nothing else in
+// these kernels reads M0 (no LDS-DMA builtins, no s_movrel or GWS).  Device
+// code only: the host pass of the compiler cannot parse the asm.
 //   copy16_sbase: address = 64-bit base (wave-uniform) + 32-bit lane offset.
 //   copy16_vaddr: address = 64-bit per-lane pointer.
 __device__ __forceinline__ void copy16_sbase(const void* base, uint32_t off, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(off), "s"(base), "s"(lds)
       : "memory");
 #else
@@ -121,13 +122,10 @@ __device__ __forceinline__ void copy16_sbase(const void* base, uint32_t off, uin
 
 __device__ __forceinline__ void copy16_vaddr(const void* g, uint32_t lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
       : "v"(g), "s"(lds)
       : "memory");
 #else
@@ -141,8 +139,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-// Load-to-LDS copies issued per wave per stage (x, codes, one for scales).
-constexpr int kLoadsPerStage = kAPer + kBPer + 1;
+// Load-to-LDS copies a wave issues per stage: x and codes, plus one for the
+// scales in wave 0.
+constexpr int kLoadsPerStage = kAPer + kBPer;
+
+// Wait until this wave's copies of all but the newest `stages` stages have
+// landed, then join the workgroup barrier.
+template <int STAGES>
+__device__ __forceinline__ void wait_stages_barrier(int wave) {
+  if (wave == 0)
+    wait_vm_barrier<STAGES * (kLoadsPerStage + 1)>();
+  else
+    wait_vm_barrier<STAGES * kLoadsPerStage>();
+}
 
 // The stage copies of one workgroup tile.  Chunk positions in LDS are fixed by
 // lane order, so the swizzles are applied by choosing which global chunk each
@@ -165,7 +174,7 @@ struct Copier {
   uint32_t xoff[kAPer], coff[kBPer], soff;
   int xk[kAPer];         // first k of this lane's x chunks within a stage
   int k;
-  uint32_t lds_wave_a, lds_wave_b, lds_wave_s;  // this wave's chunk offsets within a stage
+  uint32_t lds_wave_a, lds_wave_b;  // this wave's chunk offsets within a stage
 
   __device__ __forceinline__ Copier(const MfmaArgs& a, int64_t m0, int64_t n0, int t, int wave) {
     const int64_t row_bytes = a.k_pad / 2;
@@ -191,20 +200,19 @@ struct Copier {
       coff[i] = static_cast<uint32_t>(r * row_bytes + 16 * h);
     }
     // Scales: 16 row groups x 2 segments x 16 rows x P bytes, contiguous per
-    // row group in the prepared layout; lanes past the wave's share idle.
+    // row group in the prepared layout.
     const int lane = t & 63;
-    const int ps = wave * Cfg<FMT>::kSPerWave + (lane < Cfg<FMT>::kSPerWave ? lane : 0);
+    const int ps = lane % Cfg<FMT>::kSUsed;
     soff = static_cast<uint32_t>((ps / (2 * P)) * a.ksegs * kRowGroup * P + 16 * (ps % (2 * P)));
     lds_wave_a = 64 * 16 * wave;
     lds_wave_b = 64 * 16 * wave;
-    lds_wave_s = Cfg<FMT>::kSPerWave * 16 * wave;
   }
 
-  __device__ __forceinline__ void issue(int64_t k0, Stage<FMT>& sb, int lane) const {
+  // Copies of the stage at code k0; `ragged` = the stage straddles k.
+  __device__ __forceinline__ void issue(int64_t k0, bool ragged, Stage<FMT>& sb, int wave) const {
     const uint32_t la = lds_addr(sb.a) + lds_wave_a;
     const uint32_t lb = lds_addr(sb.b) + lds_wave_b;
-    const uint32_t ls = lds_addr(sb.s) + lds_wave_s;
-    if (k0 + kGemmBK <= k) {
+    if (!ragged) {
       const uint16_t* xb = xt + k0;
 #pragma unroll
       for (int i = 0; i < kAPer; ++i) copy16_sbase(xb, xoff[i], la + i * kThreads * 16);
@@ -219,7 +227,7 @@ struct Copier {
     const uint8_t* cb = ct + k0 / 2;
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) copy16_sbase(cb, coff[i], lb + i * kThreads * 16);
-    if (lane < Cfg<FMT>::kSPerWave) copy16_sbase(st + (k0 / 32) * kRowGroup * P, soff, ls);
+    if (wave == 0) copy16_sbase(st + (k0 / 32) * kRowGroup * P, soff, lds_addr(sb.s));
   }
 };
 
@@ -250,92 +258,128 @@ constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// One stage of the contraction for this wave: 4 MFMA steps of 16 k, each
-// over its 2 x 32 weight rows and 4 activation row blocks.  Software
-// pipelined: the x fragments and decoded weights of step kk + 1 are read and
-// decoded while the MFMAs of step kk run, and the schedule interleaves one
-// MFMA with a few VALU decode instructions so decoding hides under the matrix
-// core.
+// Register state a wave carries from one stage to the next: the stage's
+// codes and scale bytes of its 2 x 32 weight rows, and, for the MFMA step
+// about to run, the 4 x fragments and 2 decoded weight fragments.
 template <int FMT>
-__device__ __forceinline__ void compute_stage(const Stage<FMT>& st, int xr0, int wr0, int lh, f32x16_t (&acc)[4][2]) {
-  constexpr int P = Cfg<FMT>::P;
-  const uint8_t* sb = reinterpret_cast<const uint8_t*>(st.s);
+struct Regs {
   uint4 code[2];
   uint32_t sc[2];
+  Frag xf[4], wf[2];
+};
+
+// Read this wave's codes and scale bytes of a stage.
+template <int FMT>
+__device__ __forceinline__ void read_codes(const Stage<FMT>& st, int wr0, int lh, Regs<FMT>& r) {
+  constexpr int P = Cfg<FMT>::P;
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(st.s);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int r = wr0 + 32 * j;
-    code[j] = st.b[b_slot(r, lh)];
-    const int so = (((r >> 4) * 2 + lh) * kRowGroup + (r & 15)) * P;
+    const int row = wr0 + 32 * j;
+    r.code[j] = st.b[b_slot(row, lh)];
+    const int so = (((row >> 4) * 2 + lh) * kRowGroup + (row & 15)) * P;
     if constexpr (P == 2)
-      sc[j] = *reinterpret_cast<const uint16_t*>(sb + so);
+      r.sc[j] = *reinterpret_cast<const uint16_t*>(sb + so);
     else
-      sc[j] = sb[so];
-  }
-  Frag xf[2][4], wf[2][2];
-  auto load_x = [&](int kk, Frag (&f)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 q = st.a[a_slot(xr0 + 32 * i, 4 * lh + kk)];
-      f[i].u[0] = q.x;
-      f[i].u[1] = q.y;
-      f[i].u[2] = q.z;
-      f[i].u[3] = q.w;
-    }
-  };
-  auto decode = [&](int kk, Frag (&f)[2]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t word = kk == 0 ? code[j].x : kk == 1 ? code[j].y : kk == 2 ? code[j].z : code[j].w;
-      const uint32_t sbyte = P == 2 ? (kk < 2 ? sc[j] & 0xFFu : sc[j] >> 8) : sc[j];
-      decode8<FMT>(word, sbyte, f[j]);
-    }
-  };
-  load_x(0, xf[0]);
-  decode(0, wf[0]);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    if (kk < 3) {
-      load_x(kk + 1, xf[(kk + 1) & 1]);
-      decode(kk + 1, wf[(kk + 1) & 1]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][j].v, xf[kk & 1][i].v, acc[i][j], 0, 0, 0);
-  }
-  // Schedule: the stage's first LDS reads and decode, then per MFMA step its
-  // successor's four x reads and eight (MFMA, VALU) pairs.
-  constexpr int kDecodeValu = FMT == kFmtMxfp4 ? 8 : 36;  // VALU per step's decode
-  constexpr int kValuPerMfma = (kDecodeValu + 7) / 8;
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-  __builtin_amdgcn_sched_group_barrier(kSchedValu, kDecodeValu, 0);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    if (kk < 3) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (kk < 3) __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
-    }
+      r.sc[j] = sb[so];
   }
 }
 
-// Pipeline step for the stage `ks` held in buffer `cur`: wait for it to land
-// (leaving the next stage's copies in flight), then refill buffer `nxt2` --
-// read two stages ago, which the barrier just proved every wave has finished
-// with -- with stage ks + 2, and consume `cur`.
+// Read the x fragments of MFMA step kk (4 activation row blocks).
 template <int FMT>
-__device__ __forceinline__ void pipeline_step(const Copier<FMT>& cp, int ks, int k_end, const Stage<FMT>& cur,
-                                              Stage<FMT>& nxt2, int lane, int xr0, int wr0, int lh,
-                                              f32x16_t (&acc)[4][2]) {
-  if (ks + 1 < k_end)
-    wait_vm_barrier<kLoadsPerStage>();
+__device__ __forceinline__ void read_x(const Stage<FMT>& st, int xr0, int lh, int kk, Frag (&f)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 q = st.a[a_slot(xr0 + 32 * i, 4 * lh + kk)];
+    f[i].u[0] = q.x;
+    f[i].u[1] = q.y;
+    f[i].u[2] = q.z;
+    f[i].u[3] = q.w;
+  }
+}
+
+// Decode the weight fragments of MFMA step kk from the carried codes.
+template <int FMT>
+__device__ __forceinline__ void decode_step(const Regs<FMT>& r, int kk, Frag (&f)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t word = kk == 0 ? r.code[j].x : kk == 1 ? r.code[j].y : kk == 2 ? r.code[j].z : r.code[j].w;
+    const uint32_t sbyte = Cfg<FMT>::P == 2 ? (kk < 2 ? r.sc[j] & 0xFFu : r.sc[j] >> 8) : r.sc[j];
+    decode8<FMT>(word, sbyte, f[j]);
+  }
+}
+
+__device__ __forceinline__ void mfma_step(const Frag (&wf)[2], const Frag (&xf)[4], f32x16_t (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j].v, xf[i].v, acc[i][j], 0, 0, 0);
+}
+
+// VALU instructions of one MFMA step's weight decode (2 x 8 codes).
+template <int FMT>
+constexpr int kDecodeValu = FMT == kFmtMxfp4 ? 8 : 36;
+
+// Interleave hint for a run of 8 MFMAs that overlaps `reads` LDS reads and
+// one step's decode.
+// The run ends with a full scheduling barrier: left free, the scheduler
+// merges consecutive steps and issues MFMAs on the same accumulator back to
+// back, each then waiting for the previous one's result.
+template <int FMT, int READS>
+__device__ __forceinline__ void schedule_step() {
+  constexpr int kValuPerMfma = (kDecodeValu<FMT> + 7) / 8;
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One stage for this wave: 4 MFMA steps of 16 k over its 2 x 32 weight rows
+// and 4 activation row blocks.  Entry: r holds the stage's codes and step 0's
+// fragments.  Steps 0..2 each read and decode the next step's fragments while
+// their 8 MFMAs run.  Then comes the stage's one workgroup barrier, after the
+// wave's last LDS read of `cur` and before its last 8 MFMAs: once every wave
+// has passed it, `cur` is free and is refilled with stage ks + 3, and stage
+// ks + 1 (whose copies the wait before the barrier saw land) is complete in
+// `nxt`, so its codes and step-0 fragments are read and decoded under the
+// last MFMAs -- the next stage starts with its MFMAs ready to issue.
+template <int FMT>
+__device__ __forceinline__ void pipeline_step(const Copier<FMT>& cp, int ks, int k_end, int ragged_ks,
+                                              Stage<FMT>& cur, const Stage<FMT>& nxt, int wave, int xr0, int wr0,
+                                              int lh, Regs<FMT>& r, f32x16_t (&acc)[4][2]) {
+  Frag xn[4], wn[2];
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    read_x<FMT>(cur, xr0, lh, kk + 1, xn);
+    decode_step<FMT>(r, kk + 1, wn);
+    mfma_step(r.wf, r.xf, acc);
+    schedule_step<FMT, 4>();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.xf[i] = xn[i];
+    r.wf[0] = wn[0];
+    r.wf[1] = wn[1];
+  }
+  // Stage ks + 1 landed when at most the copies of stage ks + 2 are in flight.
+  if (ks + 2 < k_end)
+    wait_stages_barrier<1>(wave);
   else
-    wait_vm_barrier<0>();
-  if (ks + 2 < k_end) cp.issue(static_cast<int64_t>(ks + 2) * kGemmBK, nxt2, lane);
-  compute_stage<FMT>(cur, xr0, wr0, lh, acc);
+    wait_stages_barrier<0>(wave);
+  if (ks + 3 < k_end) cp.issue(static_cast<int64_t>(ks + 3) * kGemmBK, ks + 3 == ragged_ks, cur, wave);
+  // Unconditional, so it shares a basic block (and the interleaved schedule)
+  // with the MFMAs; after the last stage it reads a stale buffer, unused.
+  read_codes<FMT>(nxt, wr0, lh, r);
+  read_x<FMT>(nxt, xr0, lh, 0, xn);
+  decode_step<FMT>(r, 0, wn);
+  mfma_step(r.wf, r.xf, acc);
+  schedule_step<FMT, 8>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.xf[i] = xn[i];
+  r.wf[0] = wn[0];
+  r.wf[1] = wn[1];
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -350,57 +394,35 @@ __device__ __forceinline__ int64_t out_col(const MfmaArgs& a, int64_t row, int& 
 }
 
 
-// TAIL = false: workgroup b computes data-parallel tile b (in XCD order) over
-// all of K.  TAIL = true: workgroup u computes split u % splits of tail tile
-// u / splits and stores it as an fp32 partial.  Two kernels rather than one with a
-// branch keep the register allocation of the data-parallel loop free of the
-// finish code.
-template <int FMT, bool TAIL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_kernel(const MfmaArgs a) {
-  __shared__ Stage<FMT> st0, st1, st2;
-
-  const GemmPlan& pl = a.plan;
-  const int bid = blockIdx.x;
-  int tile, k_begin, k_end;
-  if constexpr (!TAIL) {
-    // XCD-aware order: workgroup b runs on XCD b % 8, so XCD x gets the ids
-    // x, x + 8, ...; give it the contiguous run of tiles starting at
-    // x * q + min(x, r) (q = tiles / 8, r = tiles % 8).  Tiles are numbered
-    // weight-tile-major, so a run shares weight and x tiles in that XCD's L2.
-    const int xcd = bid % 8;
-    const int q = pl.dp_tiles / 8;
-    const int r = pl.dp_tiles % 8;
-    tile = xcd * q + (xcd < r ? xcd : r) + bid / 8;
-    k_begin = 0;
-    k_end = pl.ksteps;
-  } else {
-    const int split = bid % pl.splits;
-    tile = pl.dp_tiles + bid / pl.splits;
-    k_begin = static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits);
-    k_end = static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits);
-  }
-  // Tile order: groups of kGroupM activation-row tiles, weight-tile-major
-  // inside a group, so the 64 tiles an XCD holds at once form an 8 x 8 block
-  // that shares 8 x tiles and 8 weight tiles in its L2 (x is re-read from
-  // outside the XCD once per 8 weight tiles instead of once per 2).
-  const int group = tile / (kGroupM * pl.n_tiles);
-  const int in_group = tile - group * kGroupM * pl.n_tiles;
+// (m_tile, n_tile) of tile t.  Tiles are ordered in groups of kGroupM
+// activation-row tiles, weight-tile-major inside a group, so the 64 tiles an
+// XCD holds at once form an 8 x 8 block that shares 8 x tiles and 8 weight
+// tiles in its L2 (x is re-read from outside the XCD once per 8 weight tiles).
+__device__ __forceinline__ void tile_coords(const GemmPlan& pl, int t, int64_t& m0, int64_t& n0) {
+  const int group = t / (kGroupM * pl.n_tiles);
+  const int in_group = t - group * kGroupM * pl.n_tiles;
   const int rows = pl.m_tiles - group * kGroupM < kGroupM ? pl.m_tiles - group * kGroupM : kGroupM;
   const int n_tile = in_group / rows;
   const int m_tile = group * kGroupM + (in_group - n_tile * rows);
-  const int64_t m0 = static_cast<int64_t>(m_tile) * kGemmBM;
-  const int64_t n0 = static_cast<int64_t>(n_tile) * kGemmBN;
+  m0 = static_cast<int64_t>(m_tile) * kGemmBM;
+  n0 = static_cast<int64_t>(n_tile) * kGemmBN;
+}
 
+// acc = the (m0, n0) tile's sums over K steps [k_begin, k_end).
+template <int FMT>
+__device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t n0, int k_begin, int k_end,
+                                         Stage<FMT>& st0, Stage<FMT>& st1, Stage<FMT>& st2,
+                                         f32x16_t (&acc)[4][2]) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int l32 = lane & 31;
   const int lh = lane >> 5;
-  const int wm = wave / 4;
-  const int wn = wave % 4;
+  const int xr0 = (wave / 4) * 128 + l32;  // x row of this lane's first activation block
+  const int wr0 = (wave % 4) * 64 + l32;   // weight row of this lane's first weight block
+  // The last stage straddles k when k is an odd multiple of 32.
+  const int ragged_ks = (a.k % kGemmBK) != 0 ? a.plan.ksteps - 1 : -1;
 
-  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -409,22 +431,63 @@ void gemm_kernel(const MfmaArgs a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const Copier<FMT> cp(a, m0, n0, t, wave);
-  const int xr0 = wm * 128 + l32;  // x row of this lane's first activation block
-  const int wr0 = wn * 64 + l32;   // weight row of this lane's first weight block
-  cp.issue(static_cast<int64_t>(k_begin) * kGemmBK, st0, lane);
-  if (k_begin + 1 < k_end) cp.issue(static_cast<int64_t>(k_begin + 1) * kGemmBK, st1, lane);
+  // Prologue: three stages in flight, wait for the first, read its codes
+  // and step-0 fragments.
+  cp.issue(static_cast<int64_t>(k_begin) * kGemmBK, k_begin == ragged_ks, st0, wave);
+  if (k_begin + 1 < k_end) cp.issue(static_cast<int64_t>(k_begin + 1) * kGemmBK, k_begin + 1 == ragged_ks, st1, wave);
+  if (k_begin + 2 < k_end) cp.issue(static_cast<int64_t>(k_begin + 2) * kGemmBK, k_begin + 2 == ragged_ks, st2, wave);
+  if (k_begin + 2 < k_end)
+    wait_stages_barrier<2>(wave);
+  else if (k_begin + 1 < k_end)
+    wait_stages_barrier<1>(wave);
+  else
+    wait_stages_barrier<0>(wave);
+  Regs<FMT> r;
+  read_codes<FMT>(st0, wr0, lh, r);
+  read_x<FMT>(st0, xr0, lh, 0, r.xf);
+  decode_step<FMT>(r, 0, r.wf);
   for (int ks = k_begin; ks < k_end; ks += kStages) {
-    pipeline_step<FMT>(cp, ks, k_end, st0, st2, lane, xr0, wr0, lh, acc);
+    pipeline_step<FMT>(cp, ks, k_end, ragged_ks, st0, st1, wave, xr0, wr0, lh, r, acc);
     if (ks + 1 >= k_end) break;
-    pipeline_step<FMT>(cp, ks + 1, k_end, st1, st0, lane, xr0, wr0, lh, acc);
+    pipeline_step<FMT>(cp, ks + 1, k_end, ragged_ks, st1, st2, wave, xr0, wr0, lh, r, acc);
     if (ks + 2 >= k_end) break;
-    pipeline_step<FMT>(cp, ks + 2, k_end, st2, st1, lane, xr0, wr0, lh, acc);
+    pipeline_step<FMT>(cp, ks + 2, k_end, ragged_ks, st2, st0, wave, xr0, wr0, lh, r, acc);
   }
+}
 
-  if constexpr (!TAIL) {
-    // Whole tile: scale by the projection's global scale and store bf16 y,
-    // four consecutive output columns (weight rows) of one activation row per
-    // lane and (i, j, e4).
+// One launch for all tiles.  Workgroup b < dp_tiles computes data-parallel
+// tile b (in XCD order) over all of K and stores bf16 y.  The last `units` =
+// tail_tiles x splits workgroups of the grid -- the last round, after their
+// own tile if they have one -- then each compute split u % splits of tail tile
+// u / splits and store it as an fp32 partial, which tail_reduce_kernel adds.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_kernel(const MfmaArgs a) {
+  __shared__ Stage<FMT> st0, st1, st2;
+  const GemmPlan& pl = a.plan;
+  const int bid = blockIdx.x;
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const int l32 = lane & 31;
+  const int lh = lane >> 5;
+  const int wm = wave / 4;
+  const int wn = wave % 4;
+  f32x16_t acc[4][2];
+
+  if (bid < pl.dp_tiles) {
+    // XCD-aware order: workgroup b runs on XCD b % 8, so XCD x gets the ids
+    // x, x + 8, ...; give it the contiguous run of tiles starting at
+    // x * q + min(x, r) (q = tiles / 8, r = tiles % 8).
+    const int xcd = bid % 8;
+    const int q = pl.dp_tiles / 8;
+    const int rr = pl.dp_tiles % 8;
+    int64_t m0, n0;
+    tile_coords(pl, xcd * q + (xcd < rr ? xcd : rr) + bid / 8, m0, n0);
+    run_tile<FMT>(a, m0, n0, 0, pl.ksteps, st0, st1, st2, acc);
+    // Scale by the projection's global scale and store bf16 y, four
+    // consecutive output columns (weight rows) of one activation row per lane
+    // and (i, j, e4).
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -447,20 +510,27 @@ void gemm_kernel(const MfmaArgs a) {
           } else {
             const float w[4] = {v0, v1, v2, v3};
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (lr + q < a.n_proj) dst[q] = f32_to_bf16_rne(w[q]);
+            for (int q2 = 0; q2 < 4; ++q2)
+              if (lr + q2 < a.n_proj) dst[q2] = f32_to_bf16_rne(w[q2]);
           }
         }
       }
-    return;
   }
 
-  // Tail unit: store this K range's fp32 partial tile [x row][weight row];
-  // tail_reduce_kernel, the next launch, adds the splits.  Written with
-  // buffer stores: with plain stores here the compiler's register allocation
-  // of the K loop above spills.
+  const int units = pl.tail_tiles * pl.splits;
+  const int u = bid - (static_cast<int>(gridDim.x) - units);
+  if (u < 0) return;
+  __syncthreads();  // the stage buffers are reused
+  const int split = u % pl.splits;
+  int64_t m0, n0;
+  tile_coords(pl, pl.dp_tiles + u / pl.splits, m0, n0);
+  run_tile<FMT>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
+                static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st0, st1, st2, acc);
+  // Store the K range's fp32 partial tile [x row][weight row].  Buffer
+  // stores: with plain stores the compiler's register allocation of the K
+  // loop spills.
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      a.partial + static_cast<int64_t>(bid) * kGemmBM * kGemmBN, 0, kGemmBM * kGemmBN * 4, kBufferRsrcWord3);
+      a.partial + static_cast<int64_t>(u) * kGemmBM * kGemmBN, 0, kGemmBM * kGemmBN * 4, kBufferRsrcWord3);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -490,16 +560,12 @@ __global__ __launch_bounds__(kReduceThreads) void tail_reduce_kernel(const MfmaA
   const int it = static_cast<int>(gi - static_cast<int64_t>(tail_tile) * kReduceItems);
   const int mr = it / (kGemmBN / 4);
   const int nr = 4 * (it % (kGemmBN / 4));
-  const int tile = pl.dp_tiles + tail_tile;
-  const int group = tile / (kGroupM * pl.n_tiles);
-  const int in_group = tile - group * kGroupM * pl.n_tiles;
-  const int rows = pl.m_tiles - group * kGroupM < kGroupM ? pl.m_tiles - group * kGroupM : kGroupM;
-  const int n_tile = in_group / rows;
-  const int m_tile = group * kGroupM + (in_group - n_tile * rows);
-  const int64_t m = static_cast<int64_t>(m_tile) * kGemmBM + mr;
+  int64_t m0, n0;
+  tile_coords(pl, pl.dp_tiles + tail_tile, m0, n0);
+  const int64_t m = m0 + mr;
   if (m >= a.m) return;
   int h;
-  const int64_t col = out_col(a, static_cast<int64_t>(n_tile) * kGemmBN + nr, h);
+  const int64_t col = out_col(a, n0 + nr, h);
   if (col < 0) return;
 
   constexpr int kBatch = 8;
@@ -533,27 +599,18 @@ __global__ __launch_bounds__(kReduceThreads) void tail_reduce_kernel(const MfmaA
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
   const GemmPlan& p = a.plan;
   const dim3 block(kThreads);
-  const unsigned units = static_cast<unsigned>(p.tail_tiles * p.splits);
-  if (grid_out) *grid_out = dim3(static_cast<unsigned>(p.dp_tiles), units);
+  const int units = p.tail_tiles * p.splits;
+  const dim3 grid(static_cast<unsigned>(p.dp_tiles > units ? p.dp_tiles : units));
+  if (grid_out) *grid_out = dim3(grid.x, static_cast<unsigned>(units));
   if (block_out) *block_out = block;
-  if (p.dp_tiles > 0) {
-    if (fmt == kFmtNvfp4)
-      hipLaunchKernelGGL((gemm_kernel<kFmtNvfp4, false>), dim3(p.dp_tiles), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_kernel<kFmtMxfp4, false>), dim3(p.dp_tiles), block, 0, stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (units > 0) {
-    if (fmt == kFmtNvfp4)
-      hipLaunchKernelGGL((gemm_kernel<kFmtNvfp4, true>), dim3(units), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((gemm_kernel<kFmtMxfp4, true>), dim3(units), block, 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const unsigned reduce_blocks = static_cast<unsigned>(p.tail_tiles * (kReduceItems / kReduceThreads));
-    hipLaunchKernelGGL(tail_reduce_kernel, dim3(reduce_blocks), dim3(kReduceThreads), 0, stream, a);
-  }
+  if (fmt == kFmtNvfp4)
+    hipLaunchKernelGGL(gemm_kernel<kFmtNvfp4>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(gemm_kernel<kFmtMxfp4>, grid, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || units == 0) return e;
+  const unsigned reduce_blocks = static_cast<unsigned>(p.tail_tiles * (kReduceItems / kReduceThreads));
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(reduce_blocks), dim3(kReduceThreads), 0, stream, a);
   return hipGetLastError();
 }
 
