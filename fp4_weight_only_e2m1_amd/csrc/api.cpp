@@ -31,13 +31,13 @@ int check_nk(int n, int k) {
 int check_m(int m) { return (m < 0 || m > FP4_MAX_M) ? FP4_EINVAL : FP4_OK; }
 
 size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
-  // The VALU GEMV (m below the MFMA-decode crossover) splits K across
-  // workgroups; the MFMA decode kernel keeps all of K in one workgroup; the
-  // prefill GEMM splits K only for the tail tiles that do not fill a round.
-  if (m < 1 || (m >= fp4::kDecodeMfmaMinM && m <= fp4::kGemvMaxM)) return 0;
+  // Both decode kernels split K across workgroups for some shapes (partials
+  // + flags); the prefill GEMM splits K only for the tail tiles that do not
+  // fill a round.
+  if (m < 1) return 0;
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
   if (m > fp4::kGemvMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
-  const int splits = fp4::gemv_splits(n_proj, k, fmt);
+  const int splits = m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
   return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total));
 }
 
@@ -90,7 +90,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.ksegs = ps.ksegs;
     const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
     a.nslab = static_cast<int>(ps.k_pad / fp4::kSlabK);
-    a.splits = on_mfma ? 1 : fp4::gemv_splits(n_proj, k, fmt);
+    a.splits = on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
     a.n_proj = n_proj;
     a.n_proj_pad = ps.n_pad;
     a.projections = projections;

@@ -7,34 +7,38 @@
 // bytes.  (Why decode is memory-bound: "MXFP4 decode-graph + gate_up FUSION
 // default-ON", vllm.cpp PR #54, step 2.)
 //
-// Work split.  A 512-thread workgroup (8 waves) owns 16 * NB weight rows and
-// all of K.  K is cut into 128-code blocks dealt round-robin to the 8 waves.
-// For each of its k-blocks a wave loads the x fragments once (global memory;
-// x is small and stays in L2) and reuses them for its NB row blocks of 16
-// rows: per row block one 16-byte code load per lane, one scale load, 16
-// conversions and 4 MFMAs.  Each wave keeps a ring of 2 k-blocks in flight:
-// a block's slot is refilled as soon as the block is consumed.  At the end
-// the 8 waves' partial tiles are added in LDS in wave order 0..7.
+// Work split.  A 256-thread workgroup (4 waves) owns a 64-row tile and one K
+// split; wave w owns rows 16w .. 16w + 15.  K advances 256 codes per stage.
+// Each stage is copied global -> LDS by the load-to-LDS path, so the weight
+// stream needs no registers and three stages are in flight while a fourth is
+// consumed:
+//   codes   64 rows x 128 bytes  (8 KiB: one full 128-byte line per row)
+//   x       8 rows x 256 bf16    (4 KiB; rows >= m are never read back)
+//   scales  of those codes       (1 KiB)
+// A wave then reads, per 128-code block, one 16-byte code chunk per lane,
+// decodes its 4 words and issues 4 MFMAs against x fragments read from LDS.
 //
-// Lane l handles row r = l % 16 of a row block and the 32-code segment
-// g = l / 16 of a k-block, so a wave-wide code load covers 16 rows x 64
-// contiguous bytes.  Word c (8 codes) of the load is the MFMA's B fragment for
-// k index 8g..8g+7; the A fragment is x[r][same 8 codes] (zero for r >= m).
-// Both operands use that k assignment, so each MFMA sums exactly the 32 codes
-// of words c of the 4 segments.
+// Lane l handles row r = l % 16 of the wave's rows and the 32-code segment
+// g = l / 16 of a 128-code block.  Word c (8 codes) of the lane's chunk is the
+// MFMA's B fragment for k index 8g..8g+7; the A fragment is x[r][same 8 codes]
+// (zero for r >= m).  Both operands use that k assignment, so each MFMA sums
+// exactly the 32 codes of words c of the 4 segments.
 //
-// Summation order of an output: per wave, its k-blocks in order (MFMA
-// accumulation); then waves 0..7.  It depends only on k -- not on m, not on
-// which rows a workgroup holds (NB), not on fusion -- so results are
-// deterministic, batch invariant for every m this kernel serves, and the
-// fused gate_up launch equals the two separate ones bit for bit.
+// K is split over workgroups when one K range per 64-row tile would leave the
+// chip underfilled; the split count depends on (k, rows per projection) only
+// (decode_mfma_splits).  Splits meet in the lock-free split-K finish of the
+// decode kernels (decode_common.hpp).  Summation order of an output: its
+// split's stages in order (MFMA accumulation), then splits in order.  It does
+// not depend on m or on fusion, so results are deterministic, batch invariant
+// for every m this kernel serves, and the fused gate_up launch equals the two
+// separate ones bit for bit.
 //
 // Scales: MXFP4 is folded into v_cvt_scalef32_pk_bf16_fp4 (the E8M0 byte is
 // the exponent operand).  NVFP4's E4M3 scale has a mantissa the conversion
 // ignores, so each code pair is converted to f32, multiplied by the scale
 // (exact: at most 6 significant bits) and packed to bf16.
-#include "fp4_common.hpp"
-#include "fp4_device.hpp"
+#include "decode_common.hpp"
+#include "lds_copy.hpp"
 
 namespace fp4 {
 namespace {
@@ -42,27 +46,123 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = kDecodeMfmaWaves;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kThreads = kDecodeThreads;  // 4 waves
+constexpr int kRows = kGemvTileRows;       // 64
+constexpr int kStageK = kDecodeStageK;     // 256 codes
+constexpr int kBuffers = 4;
+constexpr int kWChunks = kRows * kStageK / 2 / 16;  // 512 code chunks per stage
+constexpr int kXChunks = 8 * kStageK * 2 / 16;      // 256 x chunks per stage (8 rows)
+constexpr int kSChunks = 64;                        // scale chunks per stage (1 KiB)
+constexpr int kWPer = kWChunks / kThreads;          // 2 copies per lane
+static_assert(kXChunks == kThreads, "one x copy per lane");
+static_assert(kRows == 64 && kStageK == 256, "layout below assumes 64 x 256 stages");
+
+struct alignas(16) Stage {
+  uint4 w[kWChunks];
+  uint4 x[kXChunks];
+  uint4 s[kSChunks];
+};
 
 union Frag {
   bf16x8_t v;
   uint32_t u[4];
-  uint4 q;
 };
 
-__device__ __forceinline__ uint32_t u4_word(const uint4& v, int c) {
-  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+// LDS bank layout on gfx950: 64 banks of 4 bytes; a 16-byte-per-lane read is
+// served 16 lanes at a time and is conflict-free when those 16 lanes touch 16
+// different 16-byte bank groups (address / 16 mod 16).
+//
+// Codes: row rr holds 8 chunks of 16 bytes at rr * 128, chunk c in slot
+// c ^ ((rr >> 1) & 7); the 16 lanes reading one chunk index of 16 consecutive
+// rows hit bank groups 8 (rr & 1) + slot, all distinct.
+__device__ __forceinline__ int w_slot(int rr, int c) { return rr * 8 + (c ^ ((rr >> 1) & 7)); }
+// x: row xr (0..7) holds 32 chunks of 8 bf16 at xr * 512, chunk ch in slot
+// ch ^ xr: the 8 rows read together hit 8 distinct bank groups (lanes past
+// row 7 read row r & 7 again, the same address).
+__device__ __forceinline__ int x_slot(int xr, int ch) { return xr * 32 + (ch ^ xr); }
+
+// Load-to-LDS copies a wave issues per stage: 2 code chunks and 1 x chunk
+// per lane, plus one scale chunk per lane in wave 0.
+constexpr int kLoadsPerStage = kWPer + 1;
+
+template <int STAGES>
+__device__ __forceinline__ void wait_stages_barrier(int wave) {
+  if (wave == 0)
+    wait_vm_barrier<STAGES * (kLoadsPerStage + 1)>();
+  else
+    wait_vm_barrier<STAGES * kLoadsPerStage>();
 }
 
+// The stage copies of one workgroup: 32-bit lane offsets from wave-uniform
+// bases that advance with k.  x rows >= m all fetch the first 16 bytes of x
+// (never read back).  In a stage that straddles k (k not a multiple of 256),
+// x chunks at or past k are fetched from the zero padding of the prepared
+// code rows: every code row then holds at least 32 zero codes from code k on.
+template <int M, int FMT>
+struct Copier {
+  static constexpr int P = scales_per_seg(FMT);
+  const uint16_t* x;
+  const uint8_t* ct;     // code row row0
+  const uint8_t* st;     // scale row group row0 / 16
+  const uint8_t* zeros;  // 16 zero bytes
+  uint32_t woff[kWPer], xoff, soff;
+  int xk;                // first code of this lane's x chunk within a stage
+  bool xrow_ok;
+  int k;
+  uint32_t lds_wave;     // this wave's 1 KiB slice of a stage area
+
+  __device__ __forceinline__ Copier(const GemvArgs& a, int64_t row0, int t, int wave) {
+    const int64_t row_bytes = a.k_pad / 2;
+    k = a.k;
+    x = a.x;
+    ct = a.codes + row0 * row_bytes;
+    st = a.scales + (row0 / kRowGroup) * a.ksegs * kRowGroup * P;
+    zeros = ct + a.k / 2;
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int p = i * kThreads + t;
+      const int rr = p >> 3;
+      const int c = (p & 7) ^ ((rr >> 1) & 7);
+      woff[i] = static_cast<uint32_t>(rr * row_bytes + 16 * c);
+    }
+    const int xr = t >> 5;
+    const int ch = (t & 31) ^ xr;
+    xrow_ok = xr < M;
+    xoff = xrow_ok ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
+    xk = 8 * ch;
+    // Scales: 4 row groups x 8 segments x 16 rows x P bytes, 128 P contiguous
+    // bytes per row group.  MXFP4 fills 32 chunks; lanes 32..63 repeat them.
+    const int lane = t & 63;
+    const int cpg = 8 * P;  // chunks per row group
+    const int ps = lane % (4 * cpg);
+    soff = static_cast<uint32_t>((ps / cpg) * a.ksegs * kRowGroup * P + 16 * (ps % cpg));
+    lds_wave = 64 * 16 * wave;
+  }
+
+  __device__ __forceinline__ void issue(int64_t k0, Stage& sb, int wave) const {
+    const uint32_t lw = lds_addr(sb.w) + lds_wave;
+    const uint8_t* cb = ct + k0 / 2;
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) copy16_sbase(cb, woff[i], lw + i * kThreads * 16);
+    const bool in_k = k0 + xk < k;
+    const void* xs = !xrow_ok ? static_cast<const void*>(x)
+                     : in_k   ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff)
+                              : static_cast<const void*>(zeros);
+    copy16_vaddr(xs, lds_addr(sb.x) + lds_wave);
+    if (wave == 0) copy16_sbase(st + (k0 / 32) * kRowGroup * P, soff, lds_addr(sb.s));
+  }
+};
+
 template <int FMT>
-__device__ __forceinline__ void decode_word(uint32_t word, float s, Frag& f) {
+__device__ __forceinline__ void decode_word(uint32_t word, uint32_t sbyte, Frag& f) {
   if constexpr (FMT == kFmtMxfp4) {
-    f.u[0] = bf16x2_bits(cvt_fp4x2_bf16<0>(word, s));
-    f.u[1] = bf16x2_bits(cvt_fp4x2_bf16<1>(word, s));
-    f.u[2] = bf16x2_bits(cvt_fp4x2_bf16<2>(word, s));
-    f.u[3] = bf16x2_bits(cvt_fp4x2_bf16<3>(word, s));
+    const float sop = e8m0_as_scale_operand(sbyte);
+    f.u[0] = bf16x2_bits(cvt_fp4x2_bf16<0>(word, sop));
+    f.u[1] = bf16x2_bits(cvt_fp4x2_bf16<1>(word, sop));
+    f.u[2] = bf16x2_bits(cvt_fp4x2_bf16<2>(word, sop));
+    f.u[3] = bf16x2_bits(cvt_fp4x2_bf16<3>(word, sop));
   } else {
+    const float s = e4m3_to_f32<0>(sbyte);
     const f32x2_t p0 = cvt_fp4x2_f32<0>(word, 1.0f);
     const f32x2_t p1 = cvt_fp4x2_f32<1>(word, 1.0f);
     const f32x2_t p2 = cvt_fp4x2_f32<2>(word, 1.0f);
@@ -74,168 +174,131 @@ __device__ __forceinline__ void decode_word(uint32_t word, float s, Frag& f) {
   }
 }
 
-// Everything one lane loads for one k-block.
-template <int NB>
-struct Block {
-  uint4 x[4];       // x[r][kb*128 + 32g + 8c .. +8], c = 0..3
-  uint4 code[NB];   // row block b: codes of (row r, segment g)
-  uint32_t sb[NB];  // the segment's scale byte(s)
-};
-
-// Loads are branch-free (rows >= m and codes past k read a valid address and
-// are zeroed afterwards), so every k-block issues the same number of memory
-// instructions and the wait for the oldest block of the ring can be exact.
-template <int M, int FMT, int NB>
-__device__ __forceinline__ void load_block(const GemvArgs& a, int64_t row0, int kb, int r, int g, Block<NB>& blk) {
+// One stage for this wave: 2 blocks of 128 codes x 4 MFMA steps.
+template <int M, int FMT>
+__device__ __forceinline__ void compute_stage(const Stage& sb, int wave, int r, int g, f32x4_t& acc) {
   constexpr int P = scales_per_seg(FMT);
-  const int64_t kx = static_cast<int64_t>(kb) * 128 + 32 * g;
+  const int rr = 16 * wave + r;
+  const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sb.s);
+  const uint32_t keep = r < M ? ~0u : 0u;  // zero the A fragment of padding rows
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const bool ok = r < M && kx + 8 * c < a.k;
-    const int64_t off = ok ? static_cast<int64_t>(r) * a.k + kx + 8 * c : 0;
-    const uint4 v = *reinterpret_cast<const uint4*>(a.x + off);
-    const uint32_t keep = ok ? ~0u : 0u;  // an AND, not a select: keeps the load unconditional
-    blk.x[c] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-  }
-  const int64_t row_bytes = a.k_pad / 2;
-  const int64_t seg = static_cast<int64_t>(kb) * 4 + g;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int64_t row = row0 + 16 * b + r;
-    blk.code[b] = load_stream16(a.codes + row * row_bytes + seg * 16);
-    const uint8_t* sp = a.scales + (((row0 / kRowGroup + b) * a.ksegs + seg) * kRowGroup + r) * P;
-    if constexpr (P == 1) blk.sb[b] = *sp;
-    else blk.sb[b] = *reinterpret_cast<const uint16_t*>(sp);
-  }
-}
-
-template <int FMT, int NB>
-__device__ __forceinline__ void compute_block(const Block<NB>& blk, f32x4_t (&acc)[NB]) {
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float s0, s1;
-    if constexpr (FMT == kFmtMxfp4) {
-      s0 = s1 = e8m0_as_scale_operand(blk.sb[b]);
+  for (int q = 0; q < 2; ++q) {
+    const uint4 code = sb.w[w_slot(rr, 4 * q + g)];
+    const int so = ((wave * 8 + 4 * q + g) * kRowGroup + r) * P;
+    uint32_t s0, s1;
+    if constexpr (P == 2) {
+      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sbytes + so);
+      s0 = s2 & 0xFFu;
+      s1 = s2 >> 8;
     } else {
-      s0 = e4m3_to_f32<0>(blk.sb[b]);
-      s1 = e4m3_to_f32<1>(blk.sb[b]);
+      s0 = s1 = sbytes[so];
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      Frag af, bfr;
-      af.q = blk.x[c];
-      decode_word<FMT>(u4_word(blk.code[b], c), c < 2 ? s0 : s1, bfr);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, bfr.v, acc[b], 0, 0, 0);
+      const uint4 xv = sb.x[x_slot(r & 7, 16 * q + 4 * g + c)];
+      Frag af, wf;
+      af.u[0] = xv.x & keep;
+      af.u[1] = xv.y & keep;
+      af.u[2] = xv.z & keep;
+      af.u[3] = xv.w & keep;
+      const uint32_t word = c == 0 ? code.x : c == 1 ? code.y : c == 2 ? code.z : code.w;
+      decode_word<FMT>(word, c < 2 ? s0 : s1, wf);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, wf.v, acc, 0, 0, 0);
     }
   }
 }
 
-template <int M, int FMT, int NB>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a) {
-  constexpr int D = kDecodeMfmaDepth;
-  __shared__ f32x4_t red[kWaves][NB][64];
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16 * NB;
-  // This wave's k-blocks are wave, wave + 8, wave + 16, ...
-  const int kblocks = static_cast<int>(a.k_pad / 128);
-  const int nk = (kblocks - wave + kWaves - 1) / kWaves;
-
-  f32x4_t acc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Ring of D k-blocks in flight: block i lives in slot i % D.  The steady
-  // state is straight-line code (consume slot j, refill it with block i + D),
-  // so the wait before each use counts exactly the younger blocks' loads.
-  Block<NB> ring[D];
-  auto kblock = [&](int i) { return wave + i * kWaves; };
-  if (nk >= D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) load_block<M, FMT, NB>(a, row0, kblock(j), r, g, ring[j]);
-    int i0 = 0;
-    for (; i0 + 2 * D <= nk; i0 += D) {
-#pragma unroll
-      for (int j = 0; j < D; ++j) {
-        compute_block<FMT, NB>(ring[j], acc);
-        load_block<M, FMT, NB>(a, row0, kblock(i0 + j + D), r, g, ring[j]);
-      }
-    }
-    // D .. 2D-1 blocks remain: the first D are in the ring.
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      compute_block<FMT, NB>(ring[j], acc);
-      if (i0 + j + D < nk) load_block<M, FMT, NB>(a, row0, kblock(i0 + j + D), r, g, ring[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (i0 + D + j < nk) compute_block<FMT, NB>(ring[j], acc);
-  } else {
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (j < nk) load_block<M, FMT, NB>(a, row0, kblock(j), r, g, ring[j]);
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (j < nk) compute_block<FMT, NB>(ring[j], acc);
-  }
-
-  // Lane l holds C[m = 4g + i][n = r] of each row block; add the waves' tiles
-  // in wave order.
-#pragma unroll
-  for (int b = 0; b < NB; ++b) red[wave][b][lane] = acc[b];
-  __syncthreads();
-  for (int o = threadIdx.x; o < NB * 16 * M; o += kThreads) {
-    const int b = o / (16 * M);
-    const int rem = o - b * 16 * M;
-    const int m = rem / 16;
-    const int n = rem - m * 16;
-    const int src_lane = n + 16 * (m >> 2);
-    float s = red[0][b][src_lane][m & 3];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) s += red[w][b][src_lane][m & 3];
-    const int64_t row = row0 + 16 * b + n;
-    const int h = static_cast<int>(row / a.n_proj_pad);
-    const int64_t lr = row - static_cast<int64_t>(h) * a.n_proj_pad;
-    if (lr < a.n_proj)
-      a.y[static_cast<int64_t>(m) * a.ldy + static_cast<int64_t>(h) * a.n_proj + lr] =
-          f32_to_bf16_rne(s * a.gscale[h]);
-  }
+// Step for stage s in buffer `cur`: wait for it (leaving the younger stages
+// in flight) at the workgroup barrier, refill the buffer consumed one step
+// ago (`prev`; every wave is past it) with stage s + 3, consume `cur`.
+template <int M, int FMT>
+__device__ __forceinline__ void pipeline_step(const Copier<M, FMT>& cp, int s, int s1, const Stage& cur, Stage& prev,
+                                              int wave, int r, int g, f32x4_t& acc) {
+  if (s + 2 < s1)
+    wait_stages_barrier<2>(wave);
+  else if (s + 1 < s1)
+    wait_stages_barrier<1>(wave);
+  else
+    wait_stages_barrier<0>(wave);
+  if (s + 3 < s1) cp.issue(static_cast<int64_t>(s + 3) * kStageK, prev, wave);
+  compute_stage<M, FMT>(cur, wave, r, g, acc);
 }
 
 template <int M, int FMT>
-hipError_t launch_nb(const GemvArgs& a, int nb, hipStream_t stream, dim3* grid_out) {
-  const dim3 grid(static_cast<unsigned>(a.rows_total / (16 * nb)));
-  if (grid_out) *grid_out = grid;
-  const dim3 block(kThreads);
-  if (nb == 4) hipLaunchKernelGGL((decode_mfma_kernel<M, FMT, 4>), grid, block, 0, stream, a);
-  else if (nb == 2) hipLaunchKernelGGL((decode_mfma_kernel<M, FMT, 2>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((decode_mfma_kernel<M, FMT, 1>), grid, block, 0, stream, a);
-  return hipGetLastError();
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a) {
+  __shared__ Stage st0, st1, st2, st3;
+
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int tile = blockIdx.x;
+  const int split = blockIdx.y;
+  const int64_t row0 = static_cast<int64_t>(tile) * kRows;
+  const int ksteps = (a.k + kStageK - 1) / kStageK;
+  const int s0 = static_cast<int>(static_cast<int64_t>(split) * ksteps / a.splits);
+  const int s1 = static_cast<int>(static_cast<int64_t>(split + 1) * ksteps / a.splits);
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const Copier<M, FMT> cp(a, row0, t, wave);
+  cp.issue(static_cast<int64_t>(s0) * kStageK, st0, wave);
+  if (s0 + 1 < s1) cp.issue(static_cast<int64_t>(s0 + 1) * kStageK, st1, wave);
+  if (s0 + 2 < s1) cp.issue(static_cast<int64_t>(s0 + 2) * kStageK, st2, wave);
+  for (int s = s0; s < s1; s += kBuffers) {
+    pipeline_step<M, FMT>(cp, s, s1, st0, st3, wave, r, g, acc);
+    if (s + 1 >= s1) break;
+    pipeline_step<M, FMT>(cp, s + 1, s1, st1, st0, wave, r, g, acc);
+    if (s + 2 >= s1) break;
+    pipeline_step<M, FMT>(cp, s + 2, s1, st2, st1, wave, r, g, acc);
+    if (s + 3 >= s1) break;
+    pipeline_step<M, FMT>(cp, s + 3, s1, st3, st2, wave, r, g, acc);
+  }
+
+  // Lane (r, g) holds C[m = 4g + i][row 16 wave + r].
+  const int64_t row = row0 + 16 * wave + r;
+  if (a.splits == 1) {
+    int h;
+    const int64_t col = out_col(a, row, h);
+    if (col >= 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < M) a.y[static_cast<int64_t>(m) * a.ldy + col] = f32_to_bf16_rne(acc[i] * a.gscale[h]);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * g + i;
+    if (m < M) store_partial(a.partial + (static_cast<int64_t>(split) * M + m) * a.rows_total + row, acc[i]);
+  }
+  splitk_finish<M>(a, tile, split);
 }
 
 template <int FMT>
-hipError_t launch_fmt(const GemvArgs& a, int nb, hipStream_t stream, dim3* grid_out) {
+hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
   switch (a.m) {
-    case 3: return launch_nb<3, FMT>(a, nb, stream, grid_out);
-    case 4: return launch_nb<4, FMT>(a, nb, stream, grid_out);
-    case 5: return launch_nb<5, FMT>(a, nb, stream, grid_out);
-    case 6: return launch_nb<6, FMT>(a, nb, stream, grid_out);
-    case 7: return launch_nb<7, FMT>(a, nb, stream, grid_out);
-    case 8: return launch_nb<8, FMT>(a, nb, stream, grid_out);
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, FMT>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, FMT>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, FMT>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, FMT>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((decode_mfma_kernel<7, FMT>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, FMT>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
-  const int nb = decode_mfma_row_blocks(a.rows_total);
+  const dim3 grid(static_cast<unsigned>(a.rows_total / kRows), static_cast<unsigned>(a.splits));
+  if (grid_out) *grid_out = grid;
   if (block_out) *block_out = dim3(kThreads);
-  return fmt == kFmtNvfp4 ? launch_fmt<kFmtNvfp4>(a, nb, stream, grid_out)
-                          : launch_fmt<kFmtMxfp4>(a, nb, stream, grid_out);
+  return fmt == kFmtNvfp4 ? launch_fmt<kFmtNvfp4>(a, grid, stream) : launch_fmt<kFmtMxfp4>(a, grid, stream);
 }
 
 }  // namespace fp4

@@ -26,22 +26,8 @@ constexpr int kTargetCUs = 256;      // MI355X compute units
 // m from which the decode path contracts on MFMA instead of VALU v_dot2
 // (measured crossover on MI355X: the VALU GEMV is faster at m = 1, 2).
 constexpr int kDecodeMfmaMinM = 3;
-// Waves of an MFMA-decode workgroup; K is dealt to them in 128-code blocks.
-constexpr int kDecodeMfmaWaves = 8;
-// k-blocks each MFMA-decode wave keeps in flight.
-constexpr int kDecodeMfmaDepth = 2;
-
-// 16-row blocks per MFMA-decode workgroup.  More rows per workgroup means
-// each activation fragment a wave loads serves more weight rows (activation
-// traffic is 4m/rows of the weight traffic); fewer means more workgroups.
-// Measured on MI355X: 4 rows blocks once that still leaves one workgroup per
-// CU, else 2 down to half a workgroup per CU.  Only changes which rows a
-// workgroup holds, never an output's summation order.
-inline int decode_mfma_row_blocks(int64_t rows_total) {
-  if (rows_total / 64 >= kTargetCUs) return 4;
-  if (rows_total / 32 >= kTargetCUs / 2) return 2;
-  return 1;
-}
+// k-extent of one stage of the MFMA decode kernel (codes).
+constexpr int kDecodeStageK = 256;
 
 inline constexpr int group_size(int fmt) { return fmt == kFmtNvfp4 ? 16 : 32; }
 // Scale bytes per 32-code segment of a row: 2 for NVFP4, 1 for MXFP4.
@@ -94,6 +80,20 @@ inline int gemv_splits(int n_proj, int k, int fmt) {
   (void)fmt;
   const int64_t nslab = round_up(k, kSlabK) / kSlabK;
   return static_cast<int>((nslab + kGemvMaxSlabsPerSplit - 1) / kGemvMaxSlabsPerSplit);
+}
+
+// K splits of the MFMA decode kernel.  A 64-row tile per workgroup fills
+// the chip only for large n; smaller layers (5120 rows: 80 tiles) split K so
+// that one projection has about 512 workgroups, keeping at least 8 stages of
+// 256 codes per split.  A function of (rows per projection, k) only, so the
+// summation order is the same at every m the kernel serves and in the fused
+// gate_up launch as in the separate ones.
+inline int decode_mfma_splits(int n_proj, int k) {
+  const int64_t tiles = round_up(n_proj, kRowAlign) / kGemvTileRows;
+  const int ksteps = static_cast<int>((k + kDecodeStageK - 1) / kDecodeStageK);
+  int s = static_cast<int>(512 / tiles);
+  if (s > ksteps / 8) s = ksteps / 8;
+  return s < 1 ? 1 : s;
 }
 
 struct GemvArgs {

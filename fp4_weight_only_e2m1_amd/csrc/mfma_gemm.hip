@@ -34,6 +34,7 @@
 // 16-byte read.
 #include "fp4_common.hpp"
 #include "fp4_device.hpp"
+#include "lds_copy.hpp"
 
 namespace fp4 {
 namespace {
@@ -87,57 +88,6 @@ __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ ((r >>
 // h ^ ((r >> 3) & 1).  16 lanes on 16 consecutive rows reading one half hit
 // bank groups 2 r + slot (mod 16): rows r and r + 8 take opposite slots.
 __device__ __forceinline__ int b_slot(int r, int h) { return 2 * r + (h ^ ((r >> 3) & 1)); }
-
-// Wait until at most N of this wave's vector-memory operations are in flight
-// and its LDS operations are done, then join the workgroup barrier.  Written
-// as one asm statement so the compiler moves no memory access across it.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// Global -> LDS copies of 16 bytes per lane: lane l's bytes land at LDS
-// address M0 + 16 l, M0 being the same for the whole wave.  Issued as inline
-// asm so that the compiler, which would otherwise guard every later LDS read
-// with a wait for all copies in flight, leaves the waits to the pipeline
-// (wait_vm_barrier).  M0 is left holding the last LDS address: nothing else in
-// these kernels reads M0 (no LDS-DMA builtins, no s_movrel or GWS).  Device
-// code only: the host pass of the compiler cannot parse the asm.
-//   copy16_sbase: address = 64-bit base (wave-uniform) + 32-bit lane offset.
-//   copy16_vaddr: address = 64-bit per-lane pointer.
-__device__ __forceinline__ void copy16_sbase(const void* base, uint32_t off, uint32_t lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(off), "s"(base), "s"(lds)
-      : "memory");
-#else
-  (void)base;
-  (void)off;
-  (void)lds;
-#endif
-}
-
-__device__ __forceinline__ void copy16_vaddr(const void* g, uint32_t lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(g), "s"(lds)
-      : "memory");
-#else
-  (void)g;
-  (void)lds;
-#endif
-}
-
-// LDS byte address of a __shared__ object (the low half of its generic address).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
 
 // Load-to-LDS copies a wave issues per stage: x and codes, plus one for the
 // scales in wave 0.
