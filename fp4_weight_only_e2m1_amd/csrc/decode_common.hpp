@@ -69,10 +69,6 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float load_partial(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -89,34 +85,62 @@ __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // tile's flags.  Flags left by earlier calls either were cleared or hold older
 // tokens, so they never match: the workspace needs no zeroing, a captured
 // graph can replay the same token, and no workgroup ever waits for another.
+//
+// Every step is one memory round trip: the flags are read by one lane each
+// (wave 0), and each thread issues all the partial loads of its outputs before
+// it adds them.  The loads go through a buffer descriptor with the sc1
+// (device-coherent) policy -- the policy of the agent-scope atomics above --
+// because atomic loads would be issued one after another.
+constexpr int kCoherentPolicy = 16;           // sc1
+constexpr int kBufferRsrcWord3 = 0x00020000;  // raw 32-bit buffer accesses
+
 template <int M>
 __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, int split) {
   __shared__ int s_last;
   wait_memory();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t* f = a.flags + tile * a.splits;
-    __hip_atomic_store(f + split, a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t* flags = a.flags + tile * a.splits;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (lane == 0) __hip_atomic_store(flags + split, a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_memory();
-    int all = 1;
-    for (int s = 0; s < a.splits; ++s)
-      all &= __hip_atomic_load(f + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.token ? 1 : 0;
-    s_last = all;
+    bool mine = true;
+    for (int s = lane; s < a.splits; s += 64)
+      mine = mine && __hip_atomic_load(flags + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.token;
+    const bool all = __all(mine);
+    if (lane == 0) s_last = all ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
   for (int s = threadIdx.x; s < a.splits; s += kDecodeThreads)
-    __hip_atomic_store(a.flags + tile * a.splits + s, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int64_t stride = static_cast<int64_t>(M) * a.rows_total;
+    __hip_atomic_store(flags + s, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // One buffer descriptor per split: partial[split] is [m][row], at most
+  // 8 x 2^24 floats, so 32-bit offsets suffice within it.
+  const int64_t split_floats = static_cast<int64_t>(M) * a.rows_total;
+  constexpr int kBatch = 8;
   for (int i = threadIdx.x; i < M * kGemvTileRows; i += kDecodeThreads) {
     const int m = i / kGemvTileRows;
     const int64_t row = tile * kGemvTileRows + (i - m * kGemvTileRows);
     int h;
     const int64_t col = out_col(a, row, h);
     if (col < 0) continue;
-    const float* p = a.partial + static_cast<int64_t>(m) * a.rows_total + row;
-    float s = load_partial(p);
-    for (int sp = 1; sp < a.splits; ++sp) s += load_partial(p + sp * stride);
+    const int off = static_cast<int>((static_cast<int64_t>(m) * a.rows_total + row) * 4);
+    float s = 0.0f;
+    for (int s0 = 0; s0 < a.splits; s0 += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        v[b] = 0.0f;
+        if (s0 + b < a.splits) {
+          const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+              a.partial + (s0 + b) * split_floats, 0, static_cast<int>(split_floats * 4), kBufferRsrcWord3);
+          v[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, kCoherentPolicy));
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+        if (s0 + b < a.splits) s = s0 + b == 0 ? v[b] : s + v[b];
+    }
     a.y[static_cast<int64_t>(m) * a.ldy + col] = f32_to_bf16_rne(s * a.gscale[h]);
   }
 }

@@ -10,8 +10,10 @@
 // Work split.  A 256-thread workgroup (4 waves) owns a 64-row tile and one K
 // split; wave w owns rows 16w .. 16w + 15.  K advances 256 codes per stage.
 // Each stage is copied global -> LDS by the load-to-LDS path, so the weight
-// stream needs no registers and three stages are in flight while a fourth is
-// consumed:
+// stream needs no registers; of kDecodeBuffers stage buffers all but the one
+// being consumed are in flight (3 buffers measured best on MI355X: 4
+// workgroups fit a CU, and more workgroups beat deeper per-workgroup
+// pipelines):
 //   codes   64 rows x 128 bytes  (8 KiB: one full 128-byte line per row)
 //   x       8 rows x 256 bf16    (4 KiB; rows >= m are never read back)
 //   scales  of those codes       (1 KiB)
@@ -49,7 +51,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = kDecodeThreads;  // 4 waves
 constexpr int kRows = kGemvTileRows;       // 64
 constexpr int kStageK = kDecodeStageK;     // 256 codes
-constexpr int kBuffers = 4;
 constexpr int kWChunks = kRows * kStageK / 2 / 16;  // 512 code chunks per stage
 constexpr int kXChunks = 8 * kStageK * 2 / 16;      // 256 x chunks per stage (8 rows)
 constexpr int kSChunks = 64;                        // scale chunks per stage (1 KiB)
@@ -77,8 +78,7 @@ union Frag {
 // rows hit bank groups 8 (rr & 1) + slot, all distinct.
 __device__ __forceinline__ int w_slot(int rr, int c) { return rr * 8 + (c ^ ((rr >> 1) & 7)); }
 // x: row xr (0..7) holds 32 chunks of 8 bf16 at xr * 512, chunk ch in slot
-// ch ^ xr: the 8 rows read together hit 8 distinct bank groups (lanes past
-// row 7 read row r & 7 again, the same address).
+// ch ^ xr: the m <= 8 rows read together hit distinct bank groups.
 __device__ __forceinline__ int x_slot(int xr, int ch) { return xr * 32 + (ch ^ xr); }
 
 // Load-to-LDS copies a wave issues per stage: 2 code chunks and 1 x chunk
@@ -174,13 +174,23 @@ __device__ __forceinline__ void decode_word(uint32_t word, uint32_t sbyte, Frag&
   }
 }
 
-// One stage for this wave: 2 blocks of 128 codes x 4 MFMA steps.
+// A fragments of the padding rows r >= m come from a 512-byte zero row in
+// LDS instead of the stage (no per-read masking).  All such lanes read the
+// same chunk address; the row sits at 128 mod 256 bytes, so its bank group
+// (ch + 8 mod 16) differs from those of the real rows (ch ^ r, r < 8).
+struct alignas(256) ZeroRow {
+  uint4 pad[8];
+  uint4 z[32];
+};
+
+// One stage for this wave: 2 blocks of 128 codes x 4 MFMA steps.  xrow: this
+// lane's x row (r < m: its slots in the stage; else the zero row).
 template <int M, int FMT>
-__device__ __forceinline__ void compute_stage(const Stage& sb, int wave, int r, int g, f32x4_t& acc) {
+__device__ __forceinline__ void compute_stage(const Stage& sb, const uint4* zrow, int wave, int r, int g,
+                                              f32x4_t& acc) {
   constexpr int P = scales_per_seg(FMT);
   const int rr = 16 * wave + r;
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sb.s);
-  const uint32_t keep = r < M ? ~0u : 0u;  // zero the A fragment of padding rows
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const uint4 code = sb.w[w_slot(rr, 4 * q + g)];
@@ -195,12 +205,13 @@ __device__ __forceinline__ void compute_stage(const Stage& sb, int wave, int r, 
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 xv = sb.x[x_slot(r & 7, 16 * q + 4 * g + c)];
+      const int ch = 16 * q + 4 * g + c;
+      const uint4 xv = r < M ? sb.x[x_slot(r, ch)] : zrow[ch];
       Frag af, wf;
-      af.u[0] = xv.x & keep;
-      af.u[1] = xv.y & keep;
-      af.u[2] = xv.z & keep;
-      af.u[3] = xv.w & keep;
+      af.u[0] = xv.x;
+      af.u[1] = xv.y;
+      af.u[2] = xv.z;
+      af.u[3] = xv.w;
       const uint32_t word = c == 0 ? code.x : c == 1 ? code.y : c == 2 ? code.z : code.w;
       decode_word<FMT>(word, c < 2 ? s0 : s1, wf);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, wf.v, acc, 0, 0, 0);
@@ -208,25 +219,36 @@ __device__ __forceinline__ void compute_stage(const Stage& sb, int wave, int r, 
   }
 }
 
-// Step for stage s in buffer `cur`: wait for it (leaving the younger stages
-// in flight) at the workgroup barrier, refill the buffer consumed one step
-// ago (`prev`; every wave is past it) with stage s + 3, consume `cur`.
-template <int M, int FMT>
-__device__ __forceinline__ void pipeline_step(const Copier<M, FMT>& cp, int s, int s1, const Stage& cur, Stage& prev,
-                                              int wave, int r, int g, f32x4_t& acc) {
-  if (s + 2 < s1)
-    wait_stages_barrier<2>(wave);
-  else if (s + 1 < s1)
-    wait_stages_barrier<1>(wave);
-  else
+// Wait until stage s has landed -- with NB buffers, up to NB - 2 younger
+// stages stay in flight -- and join the workgroup barrier.
+template <int NB>
+__device__ __forceinline__ void wait_for_stage(int s, int s1, int wave) {
+  if constexpr (NB > 2) {
+    if (s + NB - 2 < s1) {
+      wait_stages_barrier<NB - 2>(wave);
+      return;
+    }
+    wait_for_stage<NB - 1>(s, s1, wave);
+  } else {
     wait_stages_barrier<0>(wave);
-  if (s + 3 < s1) cp.issue(static_cast<int64_t>(s + 3) * kStageK, prev, wave);
-  compute_stage<M, FMT>(cur, wave, r, g, acc);
+  }
 }
 
-template <int M, int FMT>
+// Step for stage s in buffer `cur`: wait for it at the workgroup barrier,
+// refill the buffer consumed one step ago (`prev`; every wave is past it)
+// with stage s + NB - 1, consume `cur`.
+template <int M, int FMT, int NB>
+__device__ __forceinline__ void pipeline_step(const Copier<M, FMT>& cp, int s, int s1, const Stage& cur, Stage& prev,
+                                              const uint4* zrow, int wave, int r, int g, f32x4_t& acc) {
+  wait_for_stage<NB>(s, s1, wave);
+  if (s + NB - 1 < s1) cp.issue(static_cast<int64_t>(s + NB - 1) * kStageK, prev, wave);
+  compute_stage<M, FMT>(cur, zrow, wave, r, g, acc);
+}
+
+template <int M, int FMT, int NB>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a) {
-  __shared__ Stage st0, st1, st2, st3;
+  __shared__ Stage st[NB];
+  __shared__ ZeroRow zero_row;
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -241,18 +263,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
   const int s1 = static_cast<int>(static_cast<int64_t>(split + 1) * ksteps / a.splits);
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (t < 32) zero_row.z[t] = make_uint4(0u, 0u, 0u, 0u);  // visible after the first stage barrier
   const Copier<M, FMT> cp(a, row0, t, wave);
-  cp.issue(static_cast<int64_t>(s0) * kStageK, st0, wave);
-  if (s0 + 1 < s1) cp.issue(static_cast<int64_t>(s0 + 1) * kStageK, st1, wave);
-  if (s0 + 2 < s1) cp.issue(static_cast<int64_t>(s0 + 2) * kStageK, st2, wave);
-  for (int s = s0; s < s1; s += kBuffers) {
-    pipeline_step<M, FMT>(cp, s, s1, st0, st3, wave, r, g, acc);
-    if (s + 1 >= s1) break;
-    pipeline_step<M, FMT>(cp, s + 1, s1, st1, st0, wave, r, g, acc);
-    if (s + 2 >= s1) break;
-    pipeline_step<M, FMT>(cp, s + 2, s1, st2, st1, wave, r, g, acc);
-    if (s + 3 >= s1) break;
-    pipeline_step<M, FMT>(cp, s + 3, s1, st3, st2, wave, r, g, acc);
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j)
+    if (s0 + j < s1) cp.issue(static_cast<int64_t>(s0 + j) * kStageK, st[j], wave);
+  for (int s = s0; s < s1; s += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (s + j >= s1) break;
+      pipeline_step<M, FMT, NB>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g, acc);
+    }
   }
 
   // Lane (r, g) holds C[m = 4g + i][row 16 wave + r].
@@ -281,12 +302,12 @@ template <int FMT>
 hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(kThreads);
   switch (a.m) {
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, FMT>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, FMT>), grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, FMT>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, FMT>), grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL((decode_mfma_kernel<7, FMT>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, FMT>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((decode_mfma_kernel<7, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

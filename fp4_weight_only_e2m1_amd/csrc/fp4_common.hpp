@@ -26,8 +26,10 @@ constexpr int kTargetCUs = 256;      // MI355X compute units
 // m from which the decode path contracts on MFMA instead of VALU v_dot2
 // (measured crossover on MI355X: the VALU GEMV is faster at m = 1, 2).
 constexpr int kDecodeMfmaMinM = 3;
-// k-extent of one stage of the MFMA decode kernel (codes).
+// k-extent of one stage of the MFMA decode kernel (codes), and its LDS stage
+// buffers (all but one in flight).
 constexpr int kDecodeStageK = 256;
+constexpr int kDecodeBuffers = 3;
 
 inline constexpr int group_size(int fmt) { return fmt == kFmtNvfp4 ? 16 : 32; }
 // Scale bytes per 32-code segment of a row: 2 for NVFP4, 1 for MXFP4.
