@@ -37,8 +37,10 @@ size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
   if (m < 1) return 0;
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
   if (m > fp4::kGemvMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
-  const int splits = m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
-  return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total));
+  const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
+  const int splits = on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
+  const int tile_rows = on_mfma ? fp4::kDecodeTileRows : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
+  return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total, tile_rows));
 }
 
 // A token no earlier call of this process used, for tagging the split-K
@@ -98,6 +100,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.ldy = static_cast<int64_t>(n_proj) * projections;
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
+    a.tile_rows = on_mfma ? fp4::kDecodeTileRows : fp4::kGemvTeams * fp4::gemv_rows_per_team(a.rows_total);
     if (a.splits > 1) {
       a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
                                             static_cast<int64_t>(a.splits) * m * a.rows_total * 4);

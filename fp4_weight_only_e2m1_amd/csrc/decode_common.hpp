@@ -72,8 +72,9 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Split-K finish for one 64-row tile, called by every thread of the workgroup
-// after it has stored (store_partial) this split's sums partial[split][m][row].
+// Split-K finish for one tile (a.tile_rows rows), called by every thread of the
+// workgroup after it has stored (store_partial) this split's sums
+// partial[split][m][row].
 //
 // Each (tile, split) workgroup publishes a flag = the call's 64-bit token once
 // its partials are complete, then reads the flags of all splits of its tile.
@@ -118,9 +119,9 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
   // 8 x 2^24 floats, so 32-bit offsets suffice within it.
   const int64_t split_floats = static_cast<int64_t>(M) * a.rows_total;
   constexpr int kBatch = 8;
-  for (int i = threadIdx.x; i < M * kGemvTileRows; i += kDecodeThreads) {
-    const int m = i / kGemvTileRows;
-    const int64_t row = tile * kGemvTileRows + (i - m * kGemvTileRows);
+  for (int i = threadIdx.x; i < M * a.tile_rows; i += kDecodeThreads) {
+    const int m = i / a.tile_rows;
+    const int64_t row = tile * a.tile_rows + (i - m * a.tile_rows);
     int h;
     const int64_t col = out_col(a, row, h);
     if (col < 0) continue;

@@ -49,7 +49,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = kDecodeThreads;  // 4 waves
-constexpr int kRows = kGemvTileRows;       // 64
+constexpr int kRows = kDecodeTileRows;     // 64
 constexpr int kStageK = kDecodeStageK;     // 256 codes
 constexpr int kWChunks = kRows * kStageK / 2 / 16;  // 512 code chunks per stage
 constexpr int kXChunks = 8 * kStageK * 2 / 16;      // 256 x chunks per stage (8 rows)

@@ -17,9 +17,8 @@ constexpr int kFmtMxfp4 = 1;
 constexpr int kRowAlign = 256;
 constexpr int kSlabK = 1024;
 constexpr int kRowGroup = 16;        // rows whose scale bytes are interleaved
-constexpr int kGemvRowsPerTeam = 8;  // rows one 32-lane team processes at once
-constexpr int kGemvTeams = 8;        // teams per 256-thread workgroup
-constexpr int kGemvTileRows = kGemvRowsPerTeam * kGemvTeams;  // 64
+constexpr int kGemvTeams = 8;        // 32-lane teams per 256-thread GEMV workgroup
+constexpr int kDecodeTileRows = 64;  // rows of an MFMA-decode workgroup
 constexpr int kGemvMaxSlabsPerSplit = 4;  // x staged in LDS: 8 rows * 4096 k * 2 B = 64 KiB
 constexpr int kGemvMaxM = 8;
 constexpr int kTargetCUs = 256;      // MI355X compute units
@@ -65,18 +64,27 @@ inline PreparedShape prepared_shape(int n, int k, int fmt) {
   return s;
 }
 
-// Number of K splits of the decode kernels: as few as the LDS budget for x
-// allows (4 slabs of 1024 codes per split).  Splitting further only adds the
+// Rows one 32-lane GEMV team processes at once (its workgroup owns 8 teams'
+// rows): 8 for layers of at least 512 such 64-row tiles, else 4 (twice the
+// workgroups; measured faster on MI355X for the 24576-, 12288- and 5120-row
+// decode layers, slightly slower for the 248320-row head).  It changes which
+// rows a workgroup holds, never an output's summation order.
+inline int gemv_rows_per_team(int64_t rows_total) { return rows_total / 64 >= 512 ? 8 : 4; }
+
+// Workspace of a decode call with `tile_rows` rows per workgroup: the split-K
+// partials [splits][m][rows_total] fp32, then the arrival flags
+// [rows_total / tile_rows][splits].
+inline int64_t decode_workspace_bytes(int64_t splits, int m, int64_t rows_total, int tile_rows) {
+  if (splits <= 1) return 0;
+  return splits * m * rows_total * 4 + (rows_total / tile_rows) * splits * 8;
+}
+
+// Number of K splits of the GEMV: as few as the LDS budget for x allows (4
+// slabs of 1024 codes per split).  Splitting further only adds the
 // cross-workgroup finish; measured on MI355X it never paid for the extra
 // parallelism at the decode shapes.  A function of k alone, so summation order
 // -- and every output bit -- is the same at every m a kernel serves and in the
 // fused gate_up launch as in the separate ones.
-// Workspace of a decode call: the split-K partials, then the arrival flags.
-inline int64_t decode_workspace_bytes(int64_t splits, int m, int64_t rows_total) {
-  if (splits <= 1) return 0;
-  return splits * m * rows_total * 4 + (rows_total / kGemvTileRows) * splits * 8;
-}
-
 inline int gemv_splits(int n_proj, int k, int fmt) {
   (void)n_proj;
   (void)fmt;
@@ -91,7 +99,7 @@ inline int gemv_splits(int n_proj, int k, int fmt) {
 // summation order is the same at every m the kernel serves and in the fused
 // gate_up launch as in the separate ones.
 inline int decode_mfma_splits(int n_proj, int k) {
-  const int64_t tiles = round_up(n_proj, kRowAlign) / kGemvTileRows;
+  const int64_t tiles = round_up(n_proj, kRowAlign) / kDecodeTileRows;
   const int ksteps = static_cast<int>((k + kDecodeStageK - 1) / kDecodeStageK);
   int s = static_cast<int>(512 / tiles);
   if (s > ksteps / 8) s = ksteps / 8;
@@ -118,6 +126,7 @@ struct GemvArgs {
   int64_t rows_total;     // projections * n_proj_pad
   int64_t ldy;            // projections * n_proj
   float gscale[2];        // global scale per projection (1 for MXFP4)
+  int tile_rows;          // rows per workgroup (the split-K finish tile)
 };
 
 // Prefill GEMM tiling.  A workgroup of kGemmWavesM x 4 waves computes a

@@ -9,15 +9,16 @@
 // The weight stream is the whole cost at decode ("MXFP4 decode-graph +
 // gate_up FUSION default-ON", vllm.cpp PR #54: W4A16 is memory-bound), so the
 // kernel is built around it:
-//   * A 256-thread workgroup owns 64 weight rows and one K split.  It is 8
-//     teams of 32 lanes; a team owns 8 rows.  Lane l of a team covers codes
+//   * A 256-thread workgroup owns 8 ROWS weight rows and one K split.  It is 8
+//     teams of 32 lanes; a team owns ROWS rows (8 for the largest layers, 4
+//     otherwise: gemv_rows_per_team).  Lane l of a team covers codes
 //     [32l, 32l + 32) of each 1024-code slab, so each row's slab is one 16-byte
 //     load per lane and 512 contiguous bytes per team (coalesced).
-//   * The 8 scale bytes of the team's 8 rows for one k-group are contiguous in
-//     the prepared layout: one 8-byte (MXFP4) or 16-byte (NVFP4, two groups)
-//     load per lane per slab.
+//   * The scale bytes of the team's rows for one k-group are contiguous in
+//     the prepared layout: one ROWS-byte (MXFP4) or 2 ROWS-byte (NVFP4, two
+//     groups) load per lane per slab.
 //   * x for the split is staged once into LDS (at most 8 x 4096 bf16 = 64 KiB)
-//     and read back 16 bytes at a time; each read serves 8 rows.  The 16-byte
+//     and read back 16 bytes at a time; each read serves ROWS rows.  The 16-byte
 //     chunks of a lane are rotated by (lane >> 1) so that 8 consecutive lanes
 //     hit 8 distinct 16-byte bank groups.
 //   * Decode: v_cvt_scalef32_pk_bf16_fp4 turns each code byte into a bf16
@@ -105,8 +106,9 @@ struct Butterfly {
   }
 };
 
-template <int M, int FMT>
+template <int M, int FMT, int ROWS>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
+  static_assert(ROWS == 4 || ROWS == 8, "a team's rows are a half or a quarter of a 16-row scale group");
   __shared__ uint4 xs[M][kGemvMaxSlabsPerSplit * kChunksPerSlab];
 
   const int tid = threadIdx.x;
@@ -116,29 +118,32 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   const SlabRange sr = split_slabs(a, split);
   const int slab0 = sr.first;
   const int nsl = sr.count;
-  // ---- this team's 8 rows ----
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kGemvTileRows + team * kGemvRowsPerTeam;
+  // ---- this team's ROWS rows ----
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (kGemvTeams * ROWS) + team * ROWS;
   const int64_t row_bytes = a.k_pad / 2;
   const uint8_t* cptr = a.codes + row0 * row_bytes + lane * 16;
-  // Scales: this team's 8 rows are one half (h) of a 16-row scale group.
-  const uint8_t* sptr = a.scales + ((row0 / kRowGroup) * a.ksegs * kRowGroup + (row0 & 8)) * scales_per_seg(FMT);
+  // Scales: this team's rows are a half (ROWS = 8) or a quarter (ROWS = 4) of
+  // a 16-row scale group, starting at row0 & 15.
+  const uint8_t* sptr = a.scales + ((row0 / kRowGroup) * a.ksegs * kRowGroup + (row0 & 15)) * scales_per_seg(FMT);
 
-  float acc[kGemvRowsPerTeam][M];
+  float acc[ROWS][M];
 #pragma unroll
-  for (int r = 0; r < kGemvRowsPerTeam; ++r)
+  for (int r = 0; r < ROWS; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-  uint4 q[kGemvRowsPerTeam];
+  uint4 q[ROWS];
   uint4 sc;
   auto load_slab = [&](int slab, uint4* qq, uint4& s) {
 #pragma unroll
-    for (int r = 0; r < kGemvRowsPerTeam; ++r)
+    for (int r = 0; r < ROWS; ++r)
       qq[r] = load_stream16(cptr + r * row_bytes + static_cast<int64_t>(slab) * (kSlabK / 2));
-    // Segment (slab * 32 + lane): MXFP4 8 bytes (row r at byte r), NVFP4 16
-    // bytes (row r, group j at byte 2r + j).
+    // Segment (slab * 32 + lane): MXFP4 ROWS bytes (row r at byte r), NVFP4
+    // 2 ROWS bytes (row r, group j at byte 2r + j).
     const uint8_t* sp = sptr + (static_cast<int64_t>(slab) * kTeamLanes + lane) * kRowGroup * scales_per_seg(FMT);
-    if constexpr (FMT == kFmtMxfp4) {
+    if constexpr (FMT == kFmtMxfp4 && ROWS == 4) {
+      s = make_uint4(*reinterpret_cast<const uint32_t*>(sp), 0u, 0u, 0u);
+    } else if constexpr (FMT == kFmtMxfp4 || ROWS == 4) {
       const uint2 t = *reinterpret_cast<const uint2*>(sp);
       s = make_uint4(t.x, t.y, 0u, 0u);
     } else {
@@ -150,15 +155,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   load_slab(slab0, q, sc);
   stage_x<M>(a, slab0, nsl, xs, [](int, int cc) { return xs_index(cc >> 2, cc & 3); });
   for (int j = 0; j < nsl; ++j) {
-    uint4 qn[kGemvRowsPerTeam];
+    uint4 qn[ROWS];
     uint4 scn = sc;
     if (j + 1 < nsl) load_slab(slab0 + j + 1, qn, scn);
     const int lb = j * kTeamLanes + lane;  // lane block within the staged x
 
     if constexpr (FMT == kFmtMxfp4) {
-      float sop[kGemvRowsPerTeam];
+      float sop[ROWS];
 #pragma unroll
-      for (int r = 0; r < kGemvRowsPerTeam; ++r)
+      for (int r = 0; r < ROWS; ++r)
         sop[r] = e8m0_as_scale_operand((r < 4 ? sc.x : sc.y) >> (8 * (r & 3)));
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
         for (int m = 0; m < M; ++m) xv[m] = xs[m][xs_index(lb, c)];
 #pragma unroll
-        for (int r = 0; r < kGemvRowsPerTeam; ++r) {
+        for (int r = 0; r < ROWS; ++r) {
           const uint32_t word = u4_get(q[r], c);
           const bf16x2_t w0 = cvt_fp4x2_bf16<0>(word, sop[r]);
           const bf16x2_t w1 = cvt_fp4x2_bf16<1>(word, sop[r]);
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
           for (int m = 0; m < M; ++m) xv[h][m] = xs[m][xs_index(lb, 2 * grp + h)];
 #pragma unroll
-        for (int r = 0; r < kGemvRowsPerTeam; ++r) {
+        for (int r = 0; r < ROWS; ++r) {
           const uint32_t sw = u4_get(sc, r >> 1);
           float s;
           switch (2 * (r & 1) + grp) {
@@ -228,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
     }
     if (j + 1 < nsl) {
 #pragma unroll
-      for (int r = 0; r < kGemvRowsPerTeam; ++r) q[r] = qn[r];
+      for (int r = 0; r < ROWS; ++r) q[r] = qn[r];
       sc = scn;
     }
   }
@@ -236,13 +241,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   // ---- transposing butterfly over the team's 32 lanes ----
   // V partial sums per lane (index r*M + m), padded with zeros to a power of
   // two so that every halving step splits evenly.
-  constexpr int V = kGemvRowsPerTeam * M;
+  constexpr int V = ROWS * M;
   constexpr int VP = V <= 8 ? 8 : V <= 16 ? 16 : V <= 32 ? 32 : 64;
   float v[VP];
 #pragma unroll
   for (int i = 0; i < VP; ++i) v[i] = 0.0f;
 #pragma unroll
-  for (int r = 0; r < kGemvRowsPerTeam; ++r)
+  for (int r = 0; r < ROWS; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) v[r * M + m] = acc[r][m];
 
@@ -274,21 +279,28 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   if (a.splits > 1) splitk_finish<M>(a, blockIdx.x, split);
 }
 
-template <int FMT>
-hipError_t launch_gemv_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
+template <int FMT, int ROWS>
+hipError_t launch_gemv_rows(const GemvArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(kThreads);
   switch (a.m) {
-    case 1: hipLaunchKernelGGL((gemv_kernel<1, FMT>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<2, FMT>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((gemv_kernel<1, FMT, ROWS>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<2, FMT, ROWS>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int FMT>
+hipError_t launch_gemv_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
+  return a.tile_rows == kGemvTeams * 8 ? launch_gemv_rows<FMT, 8>(a, grid, stream)
+                                       : launch_gemv_rows<FMT, 4>(a, grid, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
-  const dim3 grid(static_cast<unsigned>(a.rows_total / kGemvTileRows), static_cast<unsigned>(a.splits));
+  if (a.tile_rows != kGemvTeams * 8 && a.tile_rows != kGemvTeams * 4) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.rows_total / a.tile_rows), static_cast<unsigned>(a.splits));
   if (grid_out) *grid_out = grid;
   if (block_out) *block_out = dim3(kThreads);
   return fmt == kFmtNvfp4 ? launch_gemv_fmt<kFmtNvfp4>(a, grid, stream)

@@ -155,14 +155,18 @@ def test_gate_up_and_prepare_argument_checks(lib):
 
 
 def test_split_count_independent_of_m_and_fusion():
-    # The workspace is splits * m * rows * 4 bytes; dividing out m and rows
-    # recovers the split count, which must not change with m.
+    # The workspace is splits * (m * rows * 4 + one 8-byte flag per workgroup
+    # tile); dividing out recovers the split count, which must not change with
+    # m within a kernel: the VALU GEMV (m = 1, 2; 64-row tiles for layers of at
+    # least 512 of them, else 32-row tiles) and the MFMA decode kernel (m = 3..8,
+    # 64-row tiles).
     for n, k, fmt in [(5120, 17408, NV), (5120, 6144, NV), (12288, 4096, MX), (248320, 5120, NV)]:
         rows = -(-n // 256) * 256
-        counts = set()
-        for m in range(1, 3):   # the split-K (VALU) decode kernel serves m = 1, 2
-            ws = fp4.fp4_workspace_bytes(m, n, k, fmt)
-            per_split = 4 * m * rows + rows // 64 * 8
-            assert ws % per_split == 0
-            counts.add(ws // per_split)
-        assert len(counts) == 1
+        for ms, tile in [(range(1, 3), 64 if rows // 64 >= 512 else 32), (range(3, 9), 64)]:
+            counts = set()
+            for m in ms:
+                ws = fp4.fp4_workspace_bytes(m, n, k, fmt)
+                per_split = 4 * m * rows + rows // tile * 8
+                assert ws % per_split == 0
+                counts.add(ws // per_split)
+            assert len(counts) == 1
