@@ -97,8 +97,8 @@ def test_workspace_bytes_policy():
     ws8 = fp4.fp4_workspace_bytes(8, 248320, 5120, NV)
     flags = 248320 // 64 * 2 * 8
     assert ws1 == 2 * 1 * 248320 * 4 + flags
-    # m >= 3 runs the MFMA decode kernel: 64-row tiles, K split only while one
-    # projection has fewer than 512 tiles (at least 8 stages of 256 codes each).
+    # m >= 3 runs the MFMA decode kernel: 64-row tiles, K split only for layers
+    # under 128 tiles, to about 512 workgroups (at least 8 stages of 256 codes each).
     assert ws8 == 0                                             # 3880 tiles: no split
     down = fp4.fp4_workspace_bytes(8, 5120, 17408, NV)          # 80 tiles: 6 splits
     assert down == 6 * 8 * 5120 * 4 + 5120 // 64 * 6 * 8
