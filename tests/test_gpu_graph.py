@@ -1,0 +1,60 @@
+"""HIP-graph replay of the layer: a captured call replayed several times, with
+new activations written in place and eager calls on the same workspace in
+between, must give every time the bytes an eager call gives for the same
+inputs.  Covers the split-K finish of both decode kernels (whose arrival
+flags carry a token fixed at capture time) and the prefill GEMM's tail
+reduce, next to an unsplit call."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_weight_only_e2m1_amd as fp4
+import synth
+from gpu_util import DEV, u8, x_dev, y_host_bits
+
+pytestmark = pytest.mark.gpu
+
+NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
+
+
+@pytest.mark.parametrize("fmt,n,k,m,split", [
+    (NV, 512, 17408, 1, True),    # VALU GEMV, K split 5 ways
+    (NV, 300, 5120, 8, True),     # MFMA decode, K split
+    (MX, 8192, 1024, 4, False),   # MFMA decode, unsplit (128 row tiles)
+    (NV, 512, 5120, 100, True),   # prefill GEMM, tail tiles split along K
+])
+def test_graph_replay_matches_eager(fmt, n, k, m, split):
+    packed, scales, g = synth.packed_weight(synth.TINY, 70, n, k, fmt)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    need = fp4.fp4_workspace_bytes(m, n, k, fmt)
+    assert (need > 0) == split
+    ws = torch.full((max(need, 16),), 0xA5, dtype=torch.uint8, device=DEV)
+    x = x_dev(synth.activations(synth.TINY, m, k))
+    y_graph = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    y_eager = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+
+    def call(y):
+        fp4.fp4_w4a16_linear(x, pc, ps, n, float(g), fmt, y=y, workspace=ws)
+
+    call(y_graph)  # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(y_graph)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(7)
+    for rep in range(4):
+        xb = (rng.standard_normal((m, k), dtype=np.float32)).astype(np.float32)
+        bits = (xb.view(np.uint32) >> 16).astype(np.uint16)  # truncated to bf16: any bf16 input will do
+        x.copy_(x_dev(bits))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = y_host_bits(y_graph)
+        call(y_eager)  # eager call on the same workspace, new token
+        want = y_host_bits(y_eager)
+        assert np.array_equal(got, want), "replay %d differs from eager" % rep
+        # An eager call between replays must not disturb the next replay.
+        call(y_eager)
+        torch.cuda.synchronize()
