@@ -39,7 +39,8 @@ size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
   if (m > fp4::kGemvMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
   const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
   const int splits = on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
-  const int tile_rows = on_mfma ? fp4::kDecodeTileRows : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
+  const int tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(rows_total)
+                                : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
   return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total, tile_rows));
 }
 
@@ -100,7 +101,9 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.ldy = static_cast<int64_t>(n_proj) * projections;
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
-    a.tile_rows = on_mfma ? fp4::kDecodeTileRows : fp4::kGemvTeams * fp4::gemv_rows_per_team(a.rows_total);
+    a.tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(a.rows_total)
+                          : fp4::kGemvTeams * fp4::gemv_rows_per_team(a.rows_total);
+    if (on_mfma && a.tile_rows != fp4::kDecodeTileRows && a.splits != 1) return FP4_EINVAL;
     if (a.splits > 1) {
       a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
                                             static_cast<int64_t>(a.splits) * m * a.rows_total * 4);

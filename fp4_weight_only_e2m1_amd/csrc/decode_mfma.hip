@@ -49,19 +49,31 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = kDecodeThreads;  // 4 waves
-constexpr int kRows = kDecodeTileRows;     // 64
 constexpr int kStageK = kDecodeStageK;     // 256 codes
-constexpr int kWChunks = kRows * kStageK / 2 / 16;  // 512 code chunks per stage
-constexpr int kXChunks = 8 * kStageK * 2 / 16;      // 256 x chunks per stage (8 rows)
-constexpr int kSChunks = 64;                        // scale chunks per stage (1 KiB)
-constexpr int kWPer = kWChunks / kThreads;          // 2 copies per lane
+constexpr int kXChunks = 8 * kStageK * 2 / 16;  // 256 x chunks per stage (8 rows)
 static_assert(kXChunks == kThreads, "one x copy per lane");
-static_assert(kRows == 64 && kStageK == 256, "layout below assumes 64 x 256 stages");
+static_assert(kStageK == 256, "layout below assumes stages of 256 codes");
 
+// Tile geometry for RB row blocks of 16 per wave (a 64 RB-row tile).
+template <int RB, int FMT>
+struct Geo {
+  static constexpr int kRows = 64 * RB;
+  static constexpr int kWChunks = kRows * kStageK / 2 / 16;  // 512 RB code chunks per stage
+  static constexpr int kWPer = kWChunks / kThreads;           // 2 RB copies per lane
+  static constexpr int P = scales_per_seg(FMT);
+  static constexpr int kSReal = 32 * P * RB;                  // scale chunks of a stage
+  static constexpr int kSWaves = kSReal > 64 ? kSReal / 64 : 1;  // waves that copy them
+  static constexpr int kSChunks = 64 * kSWaves;               // incl. unused duplicates
+  // Load-to-LDS copies per lane per stage: codes and x, plus one scale chunk
+  // in waves < kSWaves.
+  static constexpr int kLoads = kWPer + 1;
+};
+
+template <int RB, int FMT>
 struct alignas(16) Stage {
-  uint4 w[kWChunks];
+  uint4 w[Geo<RB, FMT>::kWChunks];
   uint4 x[kXChunks];
-  uint4 s[kSChunks];
+  uint4 s[Geo<RB, FMT>::kSChunks];
 };
 
 union Frag {
@@ -81,16 +93,13 @@ __device__ __forceinline__ int w_slot(int rr, int c) { return rr * 8 + (c ^ ((rr
 // ch ^ xr: the m <= 8 rows read together hit distinct bank groups.
 __device__ __forceinline__ int x_slot(int xr, int ch) { return xr * 32 + (ch ^ xr); }
 
-// Load-to-LDS copies a wave issues per stage: 2 code chunks and 1 x chunk
-// per lane, plus one scale chunk per lane in wave 0.
-constexpr int kLoadsPerStage = kWPer + 1;
-
-template <int STAGES>
+template <int RB, int FMT, int STAGES>
 __device__ __forceinline__ void wait_stages_barrier(int wave) {
-  if (wave == 0)
-    wait_vm_barrier<STAGES * (kLoadsPerStage + 1)>();
+  using G = Geo<RB, FMT>;
+  if (wave < G::kSWaves)
+    wait_vm_barrier<STAGES * (G::kLoads + 1)>();
   else
-    wait_vm_barrier<STAGES * kLoadsPerStage>();
+    wait_vm_barrier<STAGES * G::kLoads>();
 }
 
 // The stage copies of one workgroup: 32-bit lane offsets from wave-uniform
@@ -98,14 +107,17 @@ __device__ __forceinline__ void wait_stages_barrier(int wave) {
 // (never read back).  In a stage that straddles k (k not a multiple of 256),
 // x chunks at or past k are fetched from the zero padding of the prepared
 // code rows: every code row then holds at least 32 zero codes from code k on.
-template <int M, int FMT>
+// Code chunks are fetched with the non-temporal hint (read once); x and the
+// scales with the default policy.
+template <int M, int FMT, int RB>
 struct Copier {
-  static constexpr int P = scales_per_seg(FMT);
+  using G = Geo<RB, FMT>;
+  static constexpr int P = G::P;
   const uint16_t* x;
   const uint8_t* ct;     // code row row0
   const uint8_t* st;     // scale row group row0 / 16
   const uint8_t* zeros;  // 16 zero bytes
-  uint32_t woff[kWPer], xoff, soff;
+  uint32_t woff[G::kWPer], xoff, soff;
   int xk;                // first code of this lane's x chunk within a stage
   bool xrow_ok;
   int k;
@@ -119,7 +131,7 @@ struct Copier {
     st = a.scales + (row0 / kRowGroup) * a.ksegs * kRowGroup * P;
     zeros = ct + a.k / 2;
 #pragma unroll
-    for (int i = 0; i < kWPer; ++i) {
+    for (int i = 0; i < G::kWPer; ++i) {
       const int p = i * kThreads + t;
       const int rr = p >> 3;
       const int c = (p & 7) ^ ((rr >> 1) & 7);
@@ -130,26 +142,29 @@ struct Copier {
     xrow_ok = xr < M;
     xoff = xrow_ok ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
     xk = 8 * ch;
-    // Scales: 4 row groups x 8 segments x 16 rows x P bytes, 128 P contiguous
-    // bytes per row group.  MXFP4 fills 32 chunks; lanes 32..63 repeat them.
+    // Scales of a stage: 4 RB row groups x 8 segments x 16 rows x P bytes,
+    // 128 P contiguous bytes per row group (cpg chunks).  Lane l of scale
+    // wave w lands at chunk 64 w + l of the stage's scale area and fetches
+    // chunk (64 w + l) mod kSReal; when kSReal < 64 (MXFP4, 64-row tiles) the
+    // upper lanes fetch duplicates into unused chunks.
     const int lane = t & 63;
-    const int cpg = 8 * P;  // chunks per row group
-    const int ps = lane % (4 * cpg);
-    soff = static_cast<uint32_t>((ps / cpg) * a.ksegs * kRowGroup * P + 16 * (ps % cpg));
+    const int cpg = 8 * P;
+    const int q = (64 * (wave < G::kSWaves ? wave : 0) + lane) % G::kSReal;
+    soff = static_cast<uint32_t>((q / cpg) * a.ksegs * kRowGroup * P + 16 * (q % cpg));
     lds_wave = 64 * 16 * wave;
   }
 
-  __device__ __forceinline__ void issue(int64_t k0, Stage& sb, int wave) const {
+  __device__ __forceinline__ void issue(int64_t k0, Stage<RB, FMT>& sb, int wave) const {
     const uint32_t lw = lds_addr(sb.w) + lds_wave;
     const uint8_t* cb = ct + k0 / 2;
 #pragma unroll
-    for (int i = 0; i < kWPer; ++i) copy16_sbase(cb, woff[i], lw + i * kThreads * 16);
+    for (int i = 0; i < G::kWPer; ++i) copy16_sbase_nt(cb, woff[i], lw + i * kThreads * 16);
     const bool in_k = k0 + xk < k;
     const void* xs = !xrow_ok ? static_cast<const void*>(x)
                      : in_k   ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff)
                               : static_cast<const void*>(zeros);
     copy16_vaddr(xs, lds_addr(sb.x) + lds_wave);
-    if (wave == 0) copy16_sbase(st + (k0 / 32) * kRowGroup * P, soff, lds_addr(sb.s));
+    if (wave < G::kSWaves) copy16_sbase(st + (k0 / 32) * kRowGroup * P, soff, lds_addr(sb.s) + lds_wave);
   }
 };
 
@@ -183,72 +198,83 @@ struct alignas(256) ZeroRow {
   uint4 z[32];
 };
 
-// One stage for this wave: 2 blocks of 128 codes x 4 MFMA steps.  xrow: this
-// lane's x row (r < m: its slots in the stage; else the zero row).
-template <int M, int FMT>
-__device__ __forceinline__ void compute_stage(const Stage& sb, const uint4* zrow, int wave, int r, int g,
-                                              f32x4_t& acc) {
+// One stage for this wave: 2 blocks of 128 codes x 4 MFMA steps for each of
+// its RB row blocks; each x fragment read from LDS feeds RB MFMAs.  zrow: the
+// zero row the lanes of rows r >= m read instead of x.
+template <int M, int FMT, int RB>
+__device__ __forceinline__ void compute_stage(const Stage<RB, FMT>& sb, const uint4* zrow, int wave, int r, int g,
+                                              f32x4_t (&acc)[RB]) {
   constexpr int P = scales_per_seg(FMT);
-  const int rr = 16 * wave + r;
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sb.s);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const uint4 code = sb.w[w_slot(rr, 4 * q + g)];
-    const int so = ((wave * 8 + 4 * q + g) * kRowGroup + r) * P;
-    uint32_t s0, s1;
-    if constexpr (P == 2) {
-      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sbytes + so);
-      s0 = s2 & 0xFFu;
-      s1 = s2 >> 8;
-    } else {
-      s0 = s1 = sbytes[so];
+    uint4 code[RB];
+    uint32_t s0[RB], s1[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int blk = RB * wave + b;  // row group of this block
+      code[b] = sb.w[w_slot(16 * blk + r, 4 * q + g)];
+      const int so = ((blk * 8 + 4 * q + g) * kRowGroup + r) * P;
+      if constexpr (P == 2) {
+        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sbytes + so);
+        s0[b] = s2 & 0xFFu;
+        s1[b] = s2 >> 8;
+      } else {
+        s0[b] = s1[b] = sbytes[so];
+      }
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int ch = 16 * q + 4 * g + c;
       const uint4 xv = r < M ? sb.x[x_slot(r, ch)] : zrow[ch];
-      Frag af, wf;
+      Frag af;
       af.u[0] = xv.x;
       af.u[1] = xv.y;
       af.u[2] = xv.z;
       af.u[3] = xv.w;
-      const uint32_t word = c == 0 ? code.x : c == 1 ? code.y : c == 2 ? code.z : code.w;
-      decode_word<FMT>(word, c < 2 ? s0 : s1, wf);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, wf.v, acc, 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        Frag wf;
+        const uint32_t word = c == 0 ? code[b].x : c == 1 ? code[b].y : c == 2 ? code[b].z : code[b].w;
+        decode_word<FMT>(word, c < 2 ? s0[b] : s1[b], wf);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, wf.v, acc[b], 0, 0, 0);
+      }
     }
   }
 }
 
 // Wait until stage s has landed -- with NB buffers, up to NB - 2 younger
 // stages stay in flight -- and join the workgroup barrier.
-template <int NB>
+template <int RB, int FMT, int NB>
 __device__ __forceinline__ void wait_for_stage(int s, int s1, int wave) {
   if constexpr (NB > 2) {
     if (s + NB - 2 < s1) {
-      wait_stages_barrier<NB - 2>(wave);
+      wait_stages_barrier<RB, FMT, NB - 2>(wave);
       return;
     }
-    wait_for_stage<NB - 1>(s, s1, wave);
+    wait_for_stage<RB, FMT, NB - 1>(s, s1, wave);
   } else {
-    wait_stages_barrier<0>(wave);
+    wait_stages_barrier<RB, FMT, 0>(wave);
   }
 }
 
 // Step for stage s in buffer `cur`: wait for it at the workgroup barrier,
 // refill the buffer consumed one step ago (`prev`; every wave is past it)
 // with stage s + NB - 1, consume `cur`.
-template <int M, int FMT, int NB>
-__device__ __forceinline__ void pipeline_step(const Copier<M, FMT>& cp, int s, int s1, const Stage& cur, Stage& prev,
-                                              const uint4* zrow, int wave, int r, int g, f32x4_t& acc) {
-  wait_for_stage<NB>(s, s1, wave);
+template <int M, int FMT, int RB, int NB>
+__device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB>& cp, int s, int s1,
+                                              const Stage<RB, FMT>& cur, Stage<RB, FMT>& prev, const uint4* zrow,
+                                              int wave, int r, int g, f32x4_t (&acc)[RB]) {
+  wait_for_stage<RB, FMT, NB>(s, s1, wave);
   if (s + NB - 1 < s1) cp.issue(static_cast<int64_t>(s + NB - 1) * kStageK, prev, wave);
-  compute_stage<M, FMT>(cur, zrow, wave, r, g, acc);
+  compute_stage<M, FMT, RB>(cur, zrow, wave, r, g, acc);
 }
 
-template <int M, int FMT, int NB>
+template <int M, int FMT, int RB, int NB>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a) {
-  __shared__ Stage st[NB];
+  __shared__ Stage<RB, FMT> st[NB];
   __shared__ ZeroRow zero_row;
+  constexpr int kRows = Geo<RB, FMT>::kRows;
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -262,9 +288,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
   const int s0 = static_cast<int>(static_cast<int64_t>(split) * ksteps / a.splits);
   const int s1 = static_cast<int>(static_cast<int64_t>(split + 1) * ksteps / a.splits);
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (t < 32) zero_row.z[t] = make_uint4(0u, 0u, 0u, 0u);  // visible after the first stage barrier
-  const Copier<M, FMT> cp(a, row0, t, wave);
+  const Copier<M, FMT, RB> cp(a, row0, t, wave);
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j)
     if (s0 + j < s1) cp.issue(static_cast<int64_t>(s0 + j) * kStageK, st[j], wave);
@@ -272,42 +300,50 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (s + j >= s1) break;
-      pipeline_step<M, FMT, NB>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g, acc);
+      pipeline_step<M, FMT, RB, NB>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g, acc);
     }
   }
 
-  // Lane (r, g) holds C[m = 4g + i][row 16 wave + r].
-  const int64_t row = row0 + 16 * wave + r;
+  // Lane (r, g) holds C[m = 4g + i][row 16 (RB wave + b) + r] in acc[b][i].
   if (a.splits == 1) {
-    int h;
-    const int64_t col = out_col(a, row, h);
-    if (col >= 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        if (m < M) a.y[static_cast<int64_t>(m) * a.ldy + col] = f32_to_bf16_rne(acc[i] * a.gscale[h]);
+    for (int b = 0; b < RB; ++b) {
+      const int64_t row = row0 + 16 * (RB * wave + b) + r;
+      int h;
+      const int64_t col = out_col(a, row, h);
+      if (col >= 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * g + i;
+          if (m < M) a.y[static_cast<int64_t>(m) * a.ldy + col] = f32_to_bf16_rne(acc[b][i] * a.gscale[h]);
+        }
       }
     }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 4 * g + i;
-    if (m < M) store_partial(a.partial + (static_cast<int64_t>(split) * M + m) * a.rows_total + row, acc[i]);
+  for (int b = 0; b < RB; ++b) {
+    const int64_t row = row0 + 16 * (RB * wave + b) + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < M) store_partial(a.partial + (static_cast<int64_t>(split) * M + m) * a.rows_total + row, acc[b][i]);
+    }
   }
   splitk_finish<M>(a, tile, split);
 }
 
-template <int FMT>
+template <int FMT, int RB>
 hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(kThreads);
+  constexpr int NB = kDecodeBuffers;
   switch (a.m) {
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL((decode_mfma_kernel<7, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, FMT, kDecodeBuffers>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, FMT, RB, NB>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, FMT, RB, NB>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, FMT, RB, NB>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, FMT, RB, NB>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((decode_mfma_kernel<7, FMT, RB, NB>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, FMT, RB, NB>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -316,10 +352,13 @@ hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
-  const dim3 grid(static_cast<unsigned>(a.rows_total / kRows), static_cast<unsigned>(a.splits));
+  if (a.tile_rows != 64 && a.tile_rows != 128) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.rows_total / a.tile_rows), static_cast<unsigned>(a.splits));
   if (grid_out) *grid_out = grid;
   if (block_out) *block_out = dim3(kThreads);
-  return fmt == kFmtNvfp4 ? launch_fmt<kFmtNvfp4>(a, grid, stream) : launch_fmt<kFmtMxfp4>(a, grid, stream);
+  if (a.tile_rows == 128)
+    return fmt == kFmtNvfp4 ? launch_fmt<kFmtNvfp4, 2>(a, grid, stream) : launch_fmt<kFmtMxfp4, 2>(a, grid, stream);
+  return fmt == kFmtNvfp4 ? launch_fmt<kFmtNvfp4, 1>(a, grid, stream) : launch_fmt<kFmtMxfp4, 1>(a, grid, stream);
 }
 
 }  // namespace fp4

@@ -109,13 +109,21 @@ inline int decode_mfma_splits(int n_proj, int k) {
   return s < 1 ? 1 : s;
 }
 
+// Rows of an MFMA-decode workgroup: 64 (one 16-row block per wave), or 128
+// (two blocks per wave, each x fragment read from LDS feeding two MFMAs: half
+// the x copies per weight byte) for layers of at least 2048 64-row tiles,
+// where 128-row tiles still leave thousands of workgroups.  Such layers are
+// never split along K (decode_mfma_splits), and the tile size changes which
+// rows a workgroup holds, never an output's summation order.
+inline int decode_mfma_tile_rows(int64_t rows_total) { return rows_total / kDecodeTileRows >= 2048 ? 128 : 64; }
+
 struct GemvArgs {
   const uint16_t* x;      // bf16 [m][k]
   const uint8_t* codes;   // prepared codes
   const uint8_t* scales;  // prepared scales
   uint16_t* y;            // bf16 [m][ldy]
   float* partial;         // fp32 [splits][m][rows_total] when splits > 1
-  uint64_t* flags;        // [rows_total / 64][splits] split-K arrival flags
+  uint64_t* flags;        // [rows_total / tile_rows][splits] split-K arrival flags
   uint64_t token;         // unique per call; tags this call's flags
   int m, k;
   int64_t k_pad;          // prepared row length in codes

@@ -235,3 +235,38 @@ def test_unit_scales_sum_of_x():
             y = y_host(_run_linear(packed, scales, 1.0, fmt, n, k, xb))
             want = oracle.bf16_bits_to_f32(xb).astype(np.float64).sum(axis=1)
             assert_close(y, np.repeat(want[:, None], n, axis=1), "unit scales m=%d" % m)
+
+
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 131000, 320, 8), (MX, 131072, 544, 3), (NV, 131072, 512, 5)])
+def test_decode_mfma_wide_tiles(fmt, n, k, m):
+    # Layers of >= 131072 rows run the MFMA decode kernel on 128-row tiles (two
+    # 16-row blocks per wave share each x fragment); ragged n and k included.
+    packed, scales, g = _quantized(fmt, n, k, tensor=7)
+    xbits = synth.activations(synth.TINY, m, k)
+    info = fp4.fp4_dispatch_info()
+    y = _run_linear(packed, scales, g, fmt, n, k, xbits, info)
+    assert info.kernel == 2 and info.splits == 1
+    assert info.grid_x == -(-n // 256) * 256 // 128
+    y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
+    assert_close(y_host(y), y_ref, "wide tiles fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
+
+
+@pytest.mark.parametrize("fmt,nh,k,m", [(MX, 65536, 256, 4), (NV, 65536, 320, 8)])
+def test_wide_tile_fused_equals_split(fmt, nh, k, m):
+    # The fused launch (131072 rows: 128-row tiles) equals the two separate
+    # 65536-row launches (64-row tiles) bit for bit: the tile size never
+    # changes an output's summation order.
+    pg, sg, gg = synth.packed_weight(synth.TINY, 62, nh, k, fmt)
+    pu, su, gu = synth.packed_weight(synth.TINY, 63, nh, k, fmt)
+    xbits = synth.activations(synth.TINY, m, k)
+    pc, ps = fp4.fp4_prepare_gate_up(u8(pg), u8(sg), u8(pu), u8(su), nh, k, fmt)
+    info = fp4.fp4_dispatch_info()
+    y = y_host_bits(fp4.fp4_w4a16_gate_up(x_dev(xbits), pc, ps, nh, float(gg), float(gu), fmt, info=info))
+    assert info.kernel == 2 and info.grid_x == 2 * nh // 128
+    info1 = fp4.fp4_dispatch_info()
+    yg = y_host_bits(_run_linear(pg, sg, gg, fmt, nh, k, xbits, info1))
+    assert info1.grid_x == nh // 64
+    yu = y_host_bits(_run_linear(pu, su, gu, fmt, nh, k, xbits))
+    assert np.array_equal(y[:, :nh], yg) and np.array_equal(y[:, nh:], yu)
+    y_ref = oracle.gate_up(oracle.bf16_bits_to_f32(xbits), pg, sg, pu, su, k, fmt, gg, gu)
+    assert_close(oracle.bf16_bits_to_f32(y).astype(np.float64), y_ref, "wide gate_up")
