@@ -31,6 +31,12 @@ per-launch time): its average duration comes from HIP events around its timed
 launches on the stream they run on; `traffic` is filled from a committed rocprofv3 counter summary in
 profiles/ only when that summary was taken on the current kernel source.
 
+Cross-checks per m (after the timed region, not part of value):
+us_per_launch_differenced = (T(N2) - T(N1)) / (N2 - N1) from graphs of
+N2 = steps and N1 = steps / 4 calls; for the fused gate_up,
+us_split_launches = the same step with the gate and up halves launched as
+two separate calls.
+
 cpu_baseline: the oracle (NumPy, float64 sums), as it stands, timed on this
 host's cores on a bounded sample of the same workload (a slice of the weight
 rows), scaled to the same unit.
@@ -175,6 +181,31 @@ def cpu_baseline(name, xbs, host, budget_s):
             "host_cpus": cores}
 
 
+def timed_calls(torch, fn, count, graph):
+    """Milliseconds for `count` calls fn(0..count-1) on the current stream:
+    one replay of a graph that captured them (after an untimed replay), or
+    direct launches."""
+    stream = torch.cuda.current_stream()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                fn(i)
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    if g is not None:
+        g.replay()
+    else:
+        for i in range(count):
+            fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +312,7 @@ def main():
     rows = []
     for j, d in enumerate(per_m):
         ms_m = evs[j][0].elapsed_time(evs[j][1])
+        d["t_ms"] = ms_m
         m = d["m"]
         b = algorithmic_bytes(fmt, n, k, proj, m)
         f = 2.0 * m * nout * k
@@ -296,6 +328,34 @@ def main():
                      "tflops": round(f / (us * 1e-6) / 1e12, 3), "splits": info.splits,
                      "grid": [info.grid_x, info.grid_y], "block": info.block,
                      "algorithmic_bytes": b, "flops": f})
+
+    # Cross-checks, after (and not part of) the timed region:
+    # * two-length differencing: the per-call time from graphs of N1 and N2
+    #   calls, (T2 - T1) / (N2 - N1), which cancels any fixed cost per replay;
+    # * fused gate_up only: the same step with the gate and up halves launched
+    #   separately (two calls per step, the halves of the same prepared weight).
+    n1 = max(1, args.steps // 4)
+    for j, d in enumerate(per_m):
+        t1 = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), n1, args.launch == "graph")
+        if args.steps > n1:
+            rows[j]["us_per_launch_differenced"] = round((d["t_ms"] - t1) * 1e3 / (args.steps - n1), 3)
+        if proj == 2:
+            cb, sb = fp4.fp4_prepared_bytes(n, k, fmt)
+            yg = torch.empty((d["m"], n), dtype=torch.bfloat16, device=dev)
+            yu = torch.empty((d["m"], n), dtype=torch.bfloat16, device=dev)
+            wsb = fp4.fp4_workspace_bytes(d["m"], n, k, fmt, 1)
+            wsg = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+            wsu = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+
+            def split_call(i, d=d, yg=yg, yu=yu, wsg=wsg, wsu=wsu, cb=cb, sb=sb):
+                c, s = weights[(args.warmup + i) % copies]
+                fp4.fp4_w4a16_linear(d["x"], c[:cb], s[:sb], n, gs[0], fmt, y=yg, workspace=wsg)
+                fp4.fp4_w4a16_linear(d["x"], c[cb:], s[sb:], n, gs[1], fmt, y=yu, workspace=wsu)
+
+            for i in range(args.warmup):
+                split_call(i)
+            ts = timed_calls(torch, split_call, args.steps, args.launch == "graph")
+            rows[j]["us_split_launches"] = round(ts * 1e3 / args.steps, 3)
 
     prefill = max(ms) > 8
     if prefill:
