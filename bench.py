@@ -165,6 +165,24 @@ def cpu_baseline(name, xbs, host, budget_s):
     else:
         value = sum(algorithmic_bytes(fmt, n, k, proj, m) for m, _ in xs) * frac / dt / 1e9
         unit = "GB/s"
+    # The same slice at m = 1 on one BLAS thread (a second, single-core figure).
+    single = None
+    x1 = [x for m, x in xs if m == 1]
+    if x1:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                r1 = 0
+                while r1 < 50 and (r1 == 0 or time.perf_counter() - t0 < min(4.0, budget_s / 3)):
+                    oracle.linear(x1[0], packed[sl], scales[sl], k, fmt, g)
+                    r1 += 1
+                d1 = (time.perf_counter() - t0) / r1
+            v1 = (2.0 * sl.stop * k / d1 / 1e12 if name.startswith("prefill")
+                  else algorithmic_bytes(fmt, n, k, proj, 1) * frac / d1 / 1e9)
+            single = {"value": round(v1, 4), "unit": unit, "cores": 1, "m": 1, "repetitions": r1}
+        except ImportError:
+            single = None
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -178,7 +196,7 @@ def cpu_baseline(name, xbs, host, budget_s):
             "sample": "oracle.linear (dequant + float64 matmul) over weight rows [0, %d) of %d, one call per "
                       "m in %s, %d timed repetitions; value scaled by the row fraction"
                       % (sl.stop, n * proj, [m for m, _ in xs], reps),
-            "host_cpus": cores}
+            "host_cpus": cores, "single_thread": single}
 
 
 def timed_calls(torch, fn, count, graph):
