@@ -121,3 +121,30 @@ def linear_f64_bruteforce(x, packed, scales, k, fmt, global_scale=1.0):
         for j in range(n):
             y[i, j] = math.fsum(float(x[i, t]) * float(w[j, t]) for t in range(k))
     return y
+
+
+def greedy_argmax(logits):
+    """Greedy token per row: the index of the row's largest value, the lowest
+    such index when several are equal.
+
+    The lowest-index rule for exact ties is the one the reference engine's
+    sampler applies ("re-verify 27B NVFP4 on the nvidia ModelOpt checkpoint",
+    vllm.cpp PR #178, section on the 35B correctness result: at the divergence
+    position two logits were the same float and the lower token id won).
+    Values compare as numbers (-0 equals +0); a NaN counts as larger than every
+    number, so the first NaN of a row wins.  A plain loop over each row.
+    """
+    a = np.asarray(logits, dtype=np.float64)
+    if a.ndim == 1:
+        a = a[None, :]
+    out = np.empty(a.shape[0], dtype=np.int64)
+    for i in range(a.shape[0]):
+        best = 0
+        for j in range(1, a.shape[1]):
+            v, b = a[i, j], a[i, best]
+            if math.isnan(b):
+                break
+            if math.isnan(v) or v > b:
+                best = j
+        out[i] = best
+    return out
