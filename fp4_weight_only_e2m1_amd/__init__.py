@@ -51,6 +51,9 @@ _SIGNATURES = {
                               ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_w4a16_gate_up": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _f, _i, _vp, _vp, _sz, _vp,
                                ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_argmax_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "fp4_w4a16_linear_argmax": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _i, _vp, _vp, _vp, _vp, _sz, _vp,
+                                     ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_dequantize": (_i, [_vp, _vp, _i, _i, _f, _i, _vp, _vp]),
     "fp4_status_string": (ctypes.c_char_p, [_i]),
 }
@@ -207,6 +210,53 @@ def fp4_w4a16_gate_up(x, prep_codes, prep_scales, n_half, global_gate, global_up
         _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n_half, float(global_gate), float(global_up), fmt,
         _ptr(y), _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
     return y
+
+
+def fp4_argmax_workspace_bytes(m, n, k, fmt):
+    out = _sz()
+    _check("fp4_argmax_workspace_bytes", load_library().fp4_argmax_workspace_bytes(m, n, k, fmt, ctypes.byref(out)))
+    return out.value
+
+
+def fp4_w4a16_linear_argmax(x, prep_codes, prep_scales, n, global_scale, fmt, logits=False, y=None,
+                            idx=None, val=None, workspace=None, stream=None, info=None):
+    """Greedy token per activation row of the decode logits x @ w.T (m <= 8).
+
+    Returns (idx int32 [m], val bf16 [m], y) where val holds the winning logits
+    and y is the bf16 [m, n] logits when ``logits`` is true (or ``y`` is given),
+    else None.  Exact ties go to the lowest index.
+    """
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m, k]")
+    m, k = x.shape
+    cb, sb = fp4_prepared_bytes(n, k, fmt)
+    if prep_codes.numel() < cb or prep_scales.numel() < sb:
+        raise ValueError("prepared buffers smaller than fp4_prepared_bytes(n, k, fmt)")
+    if y is None and logits:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    if y is not None:
+        _need(y, torch.bfloat16, "y")
+        if y.numel() != m * n:
+            raise ValueError("y must hold m x n values")
+    if idx is None:
+        idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    if val is None:
+        val = torch.empty(m, dtype=torch.bfloat16, device=x.device)
+    _need(idx, torch.int32, "idx")
+    _need(val, torch.bfloat16, "val")
+    if idx.numel() != m or val.numel() != m:
+        raise ValueError("idx and val must hold m values")
+    need = fp4_argmax_workspace_bytes(m, n, k, fmt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("fp4_w4a16_linear_argmax", load_library().fp4_w4a16_linear_argmax(
+        _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n, float(global_scale), fmt, _ptr(y), _ptr(idx),
+        _ptr(val), _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
+    return idx, val, y
 
 
 def fp4_dequantize(prep_codes, prep_scales, n, k, global_scale, fmt, out=None, stream=None):

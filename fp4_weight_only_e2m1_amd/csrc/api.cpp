@@ -54,22 +54,44 @@ uint64_t next_token() {
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_EHIP; }
 
-// Shared body of fp4_w4a16_linear and fp4_w4a16_gate_up.
+// Rows per workgroup of the decode kernel m selects (m = 1..8).
+int decode_tile_rows(int m, int64_t rows_total) {
+  return m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_tile_rows(rows_total)
+                                   : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
+}
+
+// Workspace of a greedy-argmax decode call: the call's own workspace, then
+// (256-byte aligned) one 8-byte key per (tile, activation row).
+size_t argmax_workspace_for(int m, int n, int k, int fmt, size_t* keys_offset) {
+  const size_t base = fp4::round_up(static_cast<int64_t>(workspace_for(m, n, k, fmt, 1)), 256);
+  const int64_t rows_total = fp4::round_up(n, fp4::kRowAlign);
+  if (keys_offset) *keys_offset = base;
+  return base + static_cast<size_t>(rows_total / decode_tile_rows(m, rows_total)) * m * 8;
+}
+
+// Shared body of fp4_w4a16_linear, fp4_w4a16_gate_up and
+// fp4_w4a16_linear_argmax (idx non-null: greedy argmax, y optional).
 int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_t* scales, int n_proj,
                int projections, const float* gscales, int fmt, uint16_t* y, void* ws, size_t ws_bytes,
-               hipStream_t stream, fp4_dispatch_info* info) {
+               hipStream_t stream, fp4_dispatch_info* info, int32_t* idx = nullptr, uint16_t* val = nullptr) {
   int st = check_fmt(fmt);
   if (st) return st;
   if ((st = check_nk(n_proj, k))) return st;
   if ((st = check_m(m))) return st;
   if (static_cast<int64_t>(n_proj) * projections > FP4_MAX_N) return FP4_EINVAL;
+  const bool argmax = idx != nullptr;
+  if (argmax && (m > fp4::kGemvMaxM || projections != 1)) return FP4_EINVAL;
   if (m == 0) {
     if (info) *info = fp4_dispatch_info{m <= fp4::kGemvMaxM ? 0 : 1, 0, 0, 0, 0};
     return FP4_OK;
   }
-  if (!x || !codes || !scales || !y) return FP4_EINVAL;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y)) return FP4_EALIGN;
-  const size_t need = workspace_for(m, n_proj, k, fmt, projections);
+  if (!x || !codes || !scales || (!y && !argmax)) return FP4_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || (y && !aligned16(y))) return FP4_EALIGN;
+  if (argmax && (reinterpret_cast<uintptr_t>(idx) % 4 != 0 || reinterpret_cast<uintptr_t>(val) % 2 != 0))
+    return FP4_EALIGN;
+  size_t keys_offset = 0;
+  const size_t need = argmax ? argmax_workspace_for(m, n_proj, k, fmt, &keys_offset)
+                             : workspace_for(m, n_proj, k, fmt, projections);
   if (need > 0) {
     if (ws_bytes < need) return FP4_EWORKSPACE;
     if (!ws) return FP4_EINVAL;
@@ -101,17 +123,21 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.ldy = static_cast<int64_t>(n_proj) * projections;
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
-    a.tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(a.rows_total)
-                          : fp4::kGemvTeams * fp4::gemv_rows_per_team(a.rows_total);
+    a.tile_rows = decode_tile_rows(m, a.rows_total);
     if (on_mfma && a.tile_rows != fp4::kDecodeTileRows && a.splits != 1) return FP4_EINVAL;
     if (a.splits > 1) {
       a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
                                             static_cast<int64_t>(a.splits) * m * a.rows_total * 4);
       a.token = next_token();
     }
+    if (argmax) a.keys = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + keys_offset);
     hipError_t e = on_mfma ? fp4::launch_decode_mfma(a, fmt, stream, &grid, &block)
                            : fp4::launch_gemv(a, fmt, stream, &grid, &block);
     if (e != hipSuccess) return FP4_EHIP;
+    if (argmax) {
+      e = fp4::launch_argmax_reduce(a.keys, static_cast<int>(grid.x), m, idx, val, stream);
+      if (e != hipSuccess) return FP4_EHIP;
+    }
     if (info) *info = fp4_dispatch_info{on_mfma ? 2 : 0, a.splits, static_cast<int>(grid.x),
                                         static_cast<int>(grid.y), static_cast<int>(block.x)};
   } else {
@@ -215,6 +241,25 @@ int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_c
   const float g[2] = {global_gate, global_up};
   return run_linear(x_dev, m, k, prep_codes_dev, prep_scales_dev, n_half, 2, g, fmt, y_dev, workspace_dev,
                     workspace_bytes, stream, info_out);
+}
+
+int fp4_argmax_workspace_bytes(int m, int n, int k, int fmt, size_t* bytes_out) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if (m < 0 || m > fp4::kGemvMaxM || !bytes_out) return FP4_EINVAL;
+  *bytes_out = m == 0 ? 0 : argmax_workspace_for(m, n, k, fmt, nullptr);
+  return FP4_OK;
+}
+
+int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                            const uint8_t* prep_scales_dev, int n, float global_scale, int fmt, uint16_t* y_dev,
+                            int32_t* idx_out_dev, uint16_t* val_out_dev, void* workspace_dev,
+                            size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out) {
+  if (!idx_out_dev) return FP4_EINVAL;
+  const float g[1] = {global_scale};
+  return run_linear(x_dev, m, k, prep_codes_dev, prep_scales_dev, n, 1, g, fmt, y_dev, workspace_dev,
+                    workspace_bytes, stream, info_out, idx_out_dev, val_out_dev);
 }
 
 int fp4_dequantize(const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int k, float global_scale,

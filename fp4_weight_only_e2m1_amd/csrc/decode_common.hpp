@@ -58,6 +58,42 @@ __device__ __forceinline__ int64_t out_col(const GemvArgs& a, int64_t row, int& 
   return lr < a.n_proj ? static_cast<int64_t>(h) * a.n_proj + lr : -1;
 }
 
+// Greedy argmax over a call's logits (the decode epilogue's optional output).
+// Each logit -- the bf16 value y would hold -- becomes a 64-bit key that is
+// larger exactly when the (value, index) pair wins: the value's bits mapped
+// to an unsigned order (negative values flipped, -0 made +0, every NaN made
+// the largest) in the top half, the inverted output index in the bottom half,
+// so equal values prefer the lower index.  A maximum under this total order
+// does not depend on the order of the reduction ("re-verify 27B NVFP4 on the
+// nvidia ModelOpt checkpoint", section on the 35B correctness result: exact
+// ties go to the lowest token id).
+__device__ __forceinline__ uint64_t argmax_key(uint16_t b, int64_t col) {
+  if ((b & 0x7FFFu) == 0) b = 0;                              // -0 == +0
+  if ((b & 0x7F80u) == 0x7F80u && (b & 0x7Fu) != 0) b = 0x7FC0u;  // any NaN: largest
+  const uint32_t o = (b & 0x8000u) ? (~static_cast<uint32_t>(b) & 0xFFFFu) : (b | 0x8000u);
+  return (static_cast<uint64_t>(o) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(col));
+}
+
+// Workgroup-wide argmax of one tile: every thread offers keys for activation
+// row m (tile_argmax_offer) between tile_argmax_begin and tile_argmax_end,
+// which all threads reach; the tile's best key per row goes to
+// keys[tile][m].  LDS 64-bit max is order-independent.
+struct TileArgmax {
+  unsigned long long best[kGemvMaxM];
+};
+__device__ __forceinline__ void tile_argmax_begin(TileArgmax& ta) {
+  if (threadIdx.x < kGemvMaxM) ta.best[threadIdx.x] = 0ull;
+  __syncthreads();
+}
+__device__ __forceinline__ void tile_argmax_offer(TileArgmax& ta, int m, uint64_t key) {
+  atomicMax(&ta.best[m], static_cast<unsigned long long>(key));
+}
+template <int M>
+__device__ __forceinline__ void tile_argmax_end(TileArgmax& ta, uint64_t* keys, int64_t tile) {
+  __syncthreads();
+  if (threadIdx.x < M) keys[tile * M + threadIdx.x] = ta.best[threadIdx.x];
+}
+
 // Split-K partial sums and arrival flags are exchanged between workgroups that
 // may sit on different XCDs, whose L2 caches are not coherent with each other.
 // They are therefore written and read with device-coherent (sc1) accesses --
@@ -115,6 +151,8 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
   if (!s_last) return;
   for (int s = threadIdx.x; s < a.splits; s += kDecodeThreads)
     __hip_atomic_store(flags + s, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __shared__ TileArgmax ta;
+  if (a.keys) tile_argmax_begin(ta);
   // One buffer descriptor per split: partial[split] is [m][row], at most
   // 8 x 2^24 floats, so 32-bit offsets suffice within it.
   const int64_t split_floats = static_cast<int64_t>(M) * a.rows_total;
@@ -142,8 +180,11 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
       for (int b = 0; b < kBatch; ++b)
         if (s0 + b < a.splits) s = s0 + b == 0 ? v[b] : s + v[b];
     }
-    a.y[static_cast<int64_t>(m) * a.ldy + col] = f32_to_bf16_rne(s * a.gscale[h]);
+    const uint16_t yb = f32_to_bf16_rne(s * a.gscale[h]);
+    if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
+    if (a.keys) tile_argmax_offer(ta, m, argmax_key(yb, col));
   }
+  if (a.keys) tile_argmax_end<M>(ta, a.keys, tile);
 }
 
 }  // namespace fp4

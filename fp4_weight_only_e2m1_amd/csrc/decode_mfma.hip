@@ -306,6 +306,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
 
   // Lane (r, g) holds C[m = 4g + i][row 16 (RB wave + b) + r] in acc[b][i].
   if (a.splits == 1) {
+    __shared__ TileArgmax ta;
+    if (a.keys) tile_argmax_begin(ta);
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       const int64_t row = row0 + 16 * (RB * wave + b) + r;
@@ -315,10 +317,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = 4 * g + i;
-          if (m < M) a.y[static_cast<int64_t>(m) * a.ldy + col] = f32_to_bf16_rne(acc[b][i] * a.gscale[h]);
+          if (m < M) {
+            const uint16_t yb = f32_to_bf16_rne(acc[b][i] * a.gscale[h]);
+            if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
+            if (a.keys) tile_argmax_offer(ta, m, argmax_key(yb, col));
+          }
         }
       }
     }
+    if (a.keys) tile_argmax_end<M>(ta, a.keys, tile);
     return;
   }
 #pragma unroll

@@ -125,6 +125,7 @@ struct GemvArgs {
   float* partial;         // fp32 [splits][m][rows_total] when splits > 1
   uint64_t* flags;        // [rows_total / tile_rows][splits] split-K arrival flags
   uint64_t token;         // unique per call; tags this call's flags
+  uint64_t* keys;         // greedy argmax: [tiles][m] best key per tile, or null
   int m, k;
   int64_t k_pad;          // prepared row length in codes
   int64_t kgroups;        // prepared scale bytes per row
@@ -215,6 +216,8 @@ hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, in
 hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
+hipError_t launch_argmax_reduce(const uint64_t* keys, int tiles, int m, int32_t* idx, uint16_t* val,
+                                hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,
                           float gscale, float* out, hipStream_t stream);
 

@@ -256,6 +256,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   constexpr int kFinal = VP > 32 ? VP / 32 : 1;
   Butterfly<VP, VP, 0>::run(v, lane, base, plain_mask);
 
+  __shared__ TileArgmax ta;
+  const bool argmax_here = a.keys != nullptr && a.splits == 1;
+  if (argmax_here) tile_argmax_begin(ta);
   if ((lane & plain_mask) == 0) {
 #pragma unroll
     for (int i = 0; i < kFinal; ++i) {
@@ -267,15 +270,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
         const int h = static_cast<int>(row / a.n_proj_pad);
         const int64_t lr = row - static_cast<int64_t>(h) * a.n_proj_pad;
         if (a.splits == 1) {
-          if (lr < a.n_proj)
-            a.y[static_cast<int64_t>(m) * a.ldy + static_cast<int64_t>(h) * a.n_proj + lr] =
-                f32_to_bf16_rne(v[i] * a.gscale[h]);
+          if (lr < a.n_proj) {
+            const int64_t col = static_cast<int64_t>(h) * a.n_proj + lr;
+            const uint16_t yb = f32_to_bf16_rne(v[i] * a.gscale[h]);
+            if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
+            if (argmax_here) tile_argmax_offer(ta, m, argmax_key(yb, col));
+          }
         } else {
           store_partial(a.partial + (static_cast<int64_t>(split) * M + m) * a.rows_total + row, v[i]);
         }
       }
     }
   }
+  if (argmax_here) tile_argmax_end<M>(ta, a.keys, blockIdx.x);
   if (a.splits > 1) splitk_finish<M>(a, blockIdx.x, split);
 }
 

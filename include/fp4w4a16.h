@@ -115,11 +115,12 @@ int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scale
                         uint8_t* prep_codes_dev, uint8_t* prep_scales_dev, hipStream_t stream);
 
 /*
- * Workspace a compute call needs, in bytes (0 when none).  Two kernels use
- * one, for split-K fp32 partials and arrival flags: the m = 1, 2 decode GEMV
- * with k > 4096, and the m > 8 tile GEMM when its 128 x 256 output tiles do
- * not fill whole rounds of the 512 workgroups resident on the chip (the tail
- * tiles are then split along K; at most 64 MiB).  `projections` is 1 for
+ * Workspace a compute call needs, in bytes (0 when none), for split-K fp32
+ * partials and arrival flags: the m = 1, 2 decode GEMV with k > 4096, the
+ * m = 3..8 MFMA decode on layers of fewer than 8192 rows per projection, and
+ * the m > 8 tile GEMM when its 128 x 256 output tiles do not fill whole
+ * rounds of the 512 workgroups resident on the chip (the tail tiles are then
+ * split along K; at most 64 MiB).  It never needs zeroing.  `projections` is 1 for
  * fp4_w4a16_linear (n = output features) and 2 for fp4_w4a16_gate_up
  * (n = n_half).  Pure host function.
  */
@@ -164,6 +165,32 @@ int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k,
                       float global_gate, float global_up, int fmt,
                       uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes,
                       hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
+ * Greedy token of a decode call: idx_out_dev[i] (int32) = the index j of the
+ * largest logit y[i][j] -- the bf16 value fp4_w4a16_linear gives for the same
+ * arguments -- and the lowest such j when several are equal; -0 equals +0
+ * and a NaN counts as larger than every number.  m = 1..8 only (FP4_EINVAL
+ * otherwise).  The argmax is the decode kernels' epilogue: each workgroup
+ * reduces its logits to one (value, index) per activation row, a second
+ * launch reduces those over the workgroups.  A maximum under that total
+ * order does not depend on the reduction order, so the result is
+ * deterministic and equals the argmax of fp4_w4a16_linear's y.
+ *   y_dev        NULL, or bf16 [m][n] to receive the logits as well;
+ *   idx_out_dev  int32 [m], 4-byte aligned;
+ *   val_out_dev  NULL, or bf16 [m]: the winning logits;
+ *   workspace_dev / workspace_bytes  scratch of fp4_argmax_workspace_bytes(m, n, k, fmt).
+ * Cite: "re-verify 27B NVFP4 on the nvidia ModelOpt checkpoint" (vllm.cpp
+ * PR #178), section on the 35B correctness result (exact logit ties go to the
+ * lowest token id; an argmax reduction is order-independent).
+ */
+int fp4_argmax_workspace_bytes(int m, int n, int k, int fmt, size_t* bytes_out);
+int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k,
+                            const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n,
+                            float global_scale, int fmt, uint16_t* y_dev,
+                            int32_t* idx_out_dev, uint16_t* val_out_dev,
+                            void* workspace_dev, size_t workspace_bytes,
+                            hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
  * Dequantize a prepared weight to float32 out_dev [n][k]:

@@ -170,3 +170,35 @@ def test_split_count_independent_of_m_and_fusion():
                 assert ws % per_split == 0
                 counts.add(ws // per_split)
             assert len(counts) == 1
+
+
+def test_argmax_workspace_bytes():
+    # The call's own workspace (256-byte aligned), then one 8-byte key per
+    # (workgroup tile, activation row).
+    # lm_head m = 1: the GEMV, 64-row tiles (3880), K split 2 ways.
+    base = 2 * 1 * 248320 * 4 + 3880 * 2 * 8
+    assert fp4.fp4_argmax_workspace_bytes(1, 248320, 5120, NV) == -(-base // 256) * 256 + 3880 * 1 * 8
+    # lm_head m = 8: the MFMA decode on 128-row tiles (1940), unsplit.
+    assert fp4.fp4_argmax_workspace_bytes(8, 248320, 5120, NV) == 1940 * 8 * 8
+    # A small layer at m = 4: 64-row tiles, 8 of them, no split.
+    assert fp4.fp4_argmax_workspace_bytes(4, 512, 256, MX) == 8 * 4 * 8
+    assert fp4.fp4_argmax_workspace_bytes(0, 512, 256, MX) == 0
+
+
+def _argmax(lib, m=1, k=256, n=512, fmt=NV, x=FAKE, y=None, idx=FAKE, val=None, ws=FAKE, ws_bytes=1 << 20):
+    return lib.fp4_w4a16_linear_argmax(x, m, k, FAKE, FAKE, n, 1.0, fmt, y, idx, val, ws, ws_bytes, None, None)
+
+
+def test_argmax_argument_checks(lib):
+    sz = ctypes.c_size_t()
+    assert lib.fp4_argmax_workspace_bytes(9, 512, 256, NV, ctypes.byref(sz)) == ST["EINVAL"]
+    assert _argmax(lib, m=9) == ST["EINVAL"]          # decode rows only
+    assert _argmax(lib, idx=None) == ST["EINVAL"]
+    assert _argmax(lib, x=None) == ST["EINVAL"]
+    assert _argmax(lib, fmt=5) == ST["EFMT"]
+    assert _argmax(lib, idx=FAKE + 2) == ST["EALIGN"]
+    assert _argmax(lib, val=FAKE + 1) == ST["EALIGN"]
+    assert _argmax(lib, y=FAKE + 4) == ST["EALIGN"]
+    need = fp4.fp4_argmax_workspace_bytes(1, 512, 256, NV)
+    assert _argmax(lib, ws_bytes=need - 1) == ST["EWORKSPACE"]
+    assert _argmax(lib, ws=None) == ST["EINVAL"]
