@@ -16,6 +16,8 @@ the 256 MB Infinity Cache cannot hold them, so the bytes come from HBM.
 Workloads (synthetic weights and activations at the pages' shapes):
   gate_up        MXFP4 fused gate_up, k=4096, n=2x12288          (default)
   lm_head        NVFP4 packed lm_head, k=5120, n=248320
+  lm_head_argmax the same head with the fused greedy argmax (token ids out,
+                 no logits)
   down_proj      NVFP4, k=17408, n=5120
   o_proj         NVFP4, k=6144, n=5120
   prefill_nvfp4  NVFP4, k=5120, n=17408 (m=1024 by default)
@@ -63,6 +65,7 @@ ROTATE_BYTES = 1 << 30
 WORKLOADS = {
     "gate_up": (1, 1, 12288, 4096, 2, 8),
     "lm_head": (2, 0, 248320, 5120, 1, 8),
+    "lm_head_argmax": (2, 0, 248320, 5120, 1, 8),
     "down_proj": (3, 0, 5120, 17408, 1, 8),
     "o_proj": (3, 0, 5120, 6144, 1, 8),
     "prefill_nvfp4": (4, 0, 17408, 5120, 1, 1024),
@@ -70,13 +73,17 @@ WORKLOADS = {
     "tiny": (0, 0, 512, 256, 1, 1),
 }
 TENSOR = {"o_proj": 1, "prefill_mxfp4": 1}
+# Workloads that run the greedy-argmax entry point (no logits written).
+ARGMAX = {"lm_head_argmax"}
 
 
-def algorithmic_bytes(fmt, n_proj, k, projections, m):
+def algorithmic_bytes(fmt, n_proj, k, projections, m, argmax=False):
+    """Weights + scales + global scales + x + output: y (2 m n), or for the
+    greedy argmax the token id and winning logit per row (6 m)."""
     g = 16 if fmt == 0 else 32
     n = n_proj * projections
     w = n * k // 2 + n * k // g + (4 * projections if fmt == 0 else 0)
-    return w + 2 * m * k + 2 * m * n
+    return w + 2 * m * k + (6 * m if argmax else 2 * m * n)
 
 
 def kernel_source_hash():
@@ -140,7 +147,9 @@ def cpu_baseline(name, xbs, host, budget_s):
 
     def one_step(sl):
         for _, x in xs:
-            oracle.linear(x, packed[sl], scales[sl], k, fmt, g)
+            y = oracle.linear(x, packed[sl], scales[sl], k, fmt, g)
+            if name in ARGMAX:
+                oracle.greedy_argmax(y)
 
     rows, spent = 256, 0.0
     # Grow the slice until one step takes a measurable time, then repeat within the budget.
@@ -163,7 +172,7 @@ def cpu_baseline(name, xbs, host, budget_s):
         value = sum(2.0 * m * sl.stop * k for m, _ in xs) / dt / 1e12
         unit = "TFLOP/s"
     else:
-        value = sum(algorithmic_bytes(fmt, n, k, proj, m) for m, _ in xs) * frac / dt / 1e9
+        value = sum(algorithmic_bytes(fmt, n, k, proj, m, name in ARGMAX) for m, _ in xs) * frac / dt / 1e9
         unit = "GB/s"
     # The same slice at m = 1 on one BLAS thread (a second, single-core figure).
     single = None
@@ -179,7 +188,7 @@ def cpu_baseline(name, xbs, host, budget_s):
                     r1 += 1
                 d1 = (time.perf_counter() - t0) / r1
             v1 = (2.0 * sl.stop * k / d1 / 1e12 if name.startswith("prefill")
-                  else algorithmic_bytes(fmt, n, k, proj, 1) * frac / d1 / 1e9)
+                  else algorithmic_bytes(fmt, n, k, proj, 1, name in ARGMAX) * frac / d1 / 1e9)
             single = {"value": round(v1, 4), "unit": unit, "cores": 1, "m": 1, "repetitions": r1}
         except ImportError:
             single = None
@@ -281,14 +290,22 @@ def main():
         xb = synth.activations(wid, m, k)
         x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
         y = torch.empty((m, nout), dtype=torch.bfloat16, device=dev)
-        ws_bytes = fp4.fp4_workspace_bytes(m, n, k, fmt, proj)
+        if name in ARGMAX:
+            ws_bytes = fp4.fp4_argmax_workspace_bytes(m, n, k, fmt)
+        else:
+            ws_bytes = fp4.fp4_workspace_bytes(m, n, k, fmt, proj)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-        per_m.append({"m": m, "x": x, "xb": xb, "y": y, "ws": ws, "info": fp4.fp4_dispatch_info()})
+        per_m.append({"m": m, "x": x, "xb": xb, "y": y, "ws": ws, "info": fp4.fp4_dispatch_info(),
+                      "idx": torch.empty(m, dtype=torch.int32, device=dev),
+                      "val": torch.empty(m, dtype=torch.bfloat16, device=dev)})
 
     def call(d, i):
         c, s = weights[i % copies]
         if proj == 2:
             fp4.fp4_w4a16_gate_up(d["x"], c, s, n, gs[0], gs[1], fmt, y=d["y"], workspace=d["ws"], info=d["info"])
+        elif name in ARGMAX:
+            fp4.fp4_w4a16_linear_argmax(d["x"], c, s, n, gs[0], fmt, idx=d["idx"], val=d["val"],
+                                        workspace=d["ws"], info=d["info"])
         else:
             fp4.fp4_w4a16_linear(d["x"], c, s, n, gs[0], fmt, y=d["y"], workspace=d["ws"], info=d["info"])
 
@@ -332,7 +349,7 @@ def main():
         ms_m = evs[j][0].elapsed_time(evs[j][1])
         d["t_ms"] = ms_m
         m = d["m"]
-        b = algorithmic_bytes(fmt, n, k, proj, m)
+        b = algorithmic_bytes(fmt, n, k, proj, m, name in ARGMAX)
         f = 2.0 * m * nout * k
         total_ms += ms_m
         total_bytes += b * args.steps
@@ -340,8 +357,11 @@ def main():
         info = d["info"]
         kern = {0: "gemv_kernel", 2: "decode_mfma_kernel", 1: "gemm_kernel"}[info.kernel]
         us = ms_m * 1e3 / args.steps
-        rows.append({"m": m, "kernel": "%s<%d,%s>" % (kern, m, "nvfp4" if fmt == 0 else "mxfp4")
-                     if info.kernel != 1 else "%s<%s>" % (kern, "nvfp4" if fmt == 0 else "mxfp4"),
+        kname = ("%s<%d,%s>" % (kern, m, "nvfp4" if fmt == 0 else "mxfp4") if info.kernel != 1
+                 else "%s<%s>" % (kern, "nvfp4" if fmt == 0 else "mxfp4"))
+        if name in ARGMAX:
+            kname += " + argmax_reduce_kernel"
+        rows.append({"m": m, "kernel": kname,
                      "us_per_launch": round(us, 3), "gbs": round(b / (us * 1e-6) / 1e9, 2),
                      "tflops": round(f / (us * 1e-6) / 1e12, 3), "splits": info.splits,
                      "grid": [info.grid_x, info.grid_y], "block": info.block,

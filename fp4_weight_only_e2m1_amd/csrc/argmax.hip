@@ -11,7 +11,8 @@
 namespace fp4 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
+constexpr int kPerThread = 4;  // keys per thread per pass, loaded before any is compared
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
@@ -29,12 +30,23 @@ __device__ __forceinline__ uint16_t key_value(uint64_t key) {
   return static_cast<uint16_t>((o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu));
 }
 
-// Workgroup `row`: the maximum of keys[t][row] over t < tiles.
+// Workgroup `row`: the maximum of keys[t][row] over t < tiles.  Each pass
+// issues kPerThread independent loads per thread before comparing, so a
+// layer of up to kThreads * kPerThread tiles takes one memory round trip.
 __global__ __launch_bounds__(kThreads) void argmax_reduce_kernel(const uint64_t* keys, int tiles, int m,
                                                                  int32_t* idx, uint16_t* val) {
   const int row = blockIdx.x;
   uint64_t best = 0;
-  for (int t = threadIdx.x; t < tiles; t += kThreads) best = max_u64(best, keys[static_cast<int64_t>(t) * m + row]);
+  for (int t0 = 0; t0 < tiles; t0 += kThreads * kPerThread) {
+    uint64_t v[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int t = t0 + i * kThreads + static_cast<int>(threadIdx.x);
+      v[i] = t < tiles ? keys[static_cast<int64_t>(t) * m + row] : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) best = max_u64(best, v[i]);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) best = max_u64(best, shfl_xor_u64(best, o));
   __shared__ uint64_t wave_best[kThreads / 64];

@@ -74,22 +74,50 @@ __device__ __forceinline__ uint64_t argmax_key(uint16_t b, int64_t col) {
   return (static_cast<uint64_t>(o) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(col));
 }
 
-// Workgroup-wide argmax of one tile: every thread offers keys for activation
-// row m (tile_argmax_offer) between tile_argmax_begin and tile_argmax_end,
-// which all threads reach; the tile's best key per row goes to
-// keys[tile][m].  LDS 64-bit max is order-independent.
+// Workgroup-wide argmax of one tile.  Between tile_argmax_begin and
+// tile_argmax_end (both reached by every thread) each thread folds the keys
+// it produces into its own running maximum per activation row
+// (tile_argmax_offer); the end takes the maximum over each wave by lane
+// exchanges, over the waves by one LDS 64-bit max per wave and row, and
+// writes the tile's best key per row to keys[tile][m].  Every step is a
+// maximum, so the order does not matter.
 struct TileArgmax {
   unsigned long long best[kGemvMaxM];
 };
-__device__ __forceinline__ void tile_argmax_begin(TileArgmax& ta) {
+template <int M>
+struct ArgmaxLocal {
+  uint64_t best[M];
+};
+template <int M>
+__device__ __forceinline__ void tile_argmax_begin(TileArgmax& ta, ArgmaxLocal<M>& l) {
+#pragma unroll
+  for (int mm = 0; mm < M; ++mm) l.best[mm] = 0;
   if (threadIdx.x < kGemvMaxM) ta.best[threadIdx.x] = 0ull;
   __syncthreads();
 }
-__device__ __forceinline__ void tile_argmax_offer(TileArgmax& ta, int m, uint64_t key) {
-  atomicMax(&ta.best[m], static_cast<unsigned long long>(key));
+template <int M>
+__device__ __forceinline__ void tile_argmax_offer(ArgmaxLocal<M>& l, int m, uint64_t key) {
+#pragma unroll
+  for (int mm = 0; mm < M; ++mm)
+    if (mm == m && key > l.best[mm]) l.best[mm] = key;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const int lo = __shfl_xor(static_cast<int>(static_cast<uint32_t>(v)), o);
+  const int hi = __shfl_xor(static_cast<int>(static_cast<uint32_t>(v >> 32)), o);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
 }
 template <int M>
-__device__ __forceinline__ void tile_argmax_end(TileArgmax& ta, uint64_t* keys, int64_t tile) {
+__device__ __forceinline__ void tile_argmax_end(TileArgmax& ta, ArgmaxLocal<M>& l, uint64_t* keys, int64_t tile) {
+#pragma unroll
+  for (int mm = 0; mm < M; ++mm) {
+    uint64_t v = l.best[mm];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t w = shfl_xor_u64(v, o);
+      v = w > v ? w : v;
+    }
+    if ((threadIdx.x & 63) == 0) atomicMax(&ta.best[mm], static_cast<unsigned long long>(v));
+  }
   __syncthreads();
   if (threadIdx.x < M) keys[tile * M + threadIdx.x] = ta.best[threadIdx.x];
 }
@@ -152,7 +180,8 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
   for (int s = threadIdx.x; s < a.splits; s += kDecodeThreads)
     __hip_atomic_store(flags + s, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __shared__ TileArgmax ta;
-  if (a.keys) tile_argmax_begin(ta);
+  ArgmaxLocal<M> al;
+  if (a.keys) tile_argmax_begin(ta, al);
   // One buffer descriptor per split: partial[split] is [m][row], at most
   // 8 x 2^24 floats, so 32-bit offsets suffice within it.
   const int64_t split_floats = static_cast<int64_t>(M) * a.rows_total;
@@ -182,9 +211,9 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
     }
     const uint16_t yb = f32_to_bf16_rne(s * a.gscale[h]);
     if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
-    if (a.keys) tile_argmax_offer(ta, m, argmax_key(yb, col));
+    if (a.keys) tile_argmax_offer(al, m, argmax_key(yb, col));
   }
-  if (a.keys) tile_argmax_end<M>(ta, a.keys, tile);
+  if (a.keys) tile_argmax_end(ta, al, a.keys, tile);
 }
 
 }  // namespace fp4

@@ -306,8 +306,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
 
   // Lane (r, g) holds C[m = 4g + i][row 16 (RB wave + b) + r] in acc[b][i].
   if (a.splits == 1) {
+    // Greedy-argmax keys: lane (r, g) only ever holds activation rows
+    // 4g .. 4g + 3, so each row's maximum is taken over the 16 lanes of
+    // group g (lane exchanges within the group), then across the waves.
     __shared__ TileArgmax ta;
-    if (a.keys) tile_argmax_begin(ta);
+    uint64_t best[4] = {0, 0, 0, 0};
+    if (a.keys) {
+      if (t < kGemvMaxM) ta.best[t] = 0ull;
+      __syncthreads();
+    }
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       const int64_t row = row0 + 16 * (RB * wave + b) + r;
@@ -320,12 +327,25 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
           if (m < M) {
             const uint16_t yb = f32_to_bf16_rne(acc[b][i] * a.gscale[h]);
             if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
-            if (a.keys) tile_argmax_offer(ta, m, argmax_key(yb, col));
+            const uint64_t key = argmax_key(yb, col);
+            if (key > best[i]) best[i] = key;
           }
         }
       }
     }
-    if (a.keys) tile_argmax_end<M>(ta, a.keys, tile);
+    if (a.keys) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const uint64_t w = shfl_xor_u64(best[i], o);
+          if (w > best[i]) best[i] = w;
+        }
+        if (r == 0 && 4 * g + i < M) atomicMax(&ta.best[4 * g + i], static_cast<unsigned long long>(best[i]));
+      }
+      __syncthreads();
+      if (t < M) a.keys[static_cast<int64_t>(tile) * M + t] = ta.best[t];
+    }
     return;
   }
 #pragma unroll

@@ -257,8 +257,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   Butterfly<VP, VP, 0>::run(v, lane, base, plain_mask);
 
   __shared__ TileArgmax ta;
+  ArgmaxLocal<M> al;
   const bool argmax_here = a.keys != nullptr && a.splits == 1;
-  if (argmax_here) tile_argmax_begin(ta);
+  if (argmax_here) tile_argmax_begin(ta, al);
   if ((lane & plain_mask) == 0) {
 #pragma unroll
     for (int i = 0; i < kFinal; ++i) {
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
             const int64_t col = static_cast<int64_t>(h) * a.n_proj + lr;
             const uint16_t yb = f32_to_bf16_rne(v[i] * a.gscale[h]);
             if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
-            if (argmax_here) tile_argmax_offer(ta, m, argmax_key(yb, col));
+            if (argmax_here) tile_argmax_offer(al, m, argmax_key(yb, col));
           }
         } else {
           store_partial(a.partial + (static_cast<int64_t>(split) * M + m) * a.rows_total + row, v[i]);
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
       }
     }
   }
-  if (argmax_here) tile_argmax_end<M>(ta, a.keys, blockIdx.x);
+  if (argmax_here) tile_argmax_end(ta, al, a.keys, blockIdx.x);
   if (a.splits > 1) splitk_finish<M>(a, blockIdx.x, split);
 }
 

@@ -64,3 +64,30 @@ def test_gate_up_full_size(m):
     ref_u = oracle.linear_rows(x, pu, su, k, fmt, gu, rows)
     assert_close(np.concatenate([yf[:, rows], yf[:, nh + rows]], axis=1),
                  np.concatenate([ref_g, ref_u], axis=1), "gate_up m=%d" % m)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_lm_head_argmax_full_size(m):
+    # The fused greedy argmax over all 248320 logits equals the argmax of the
+    # unfused call's logits (lowest index on ties), and the winner's oracle
+    # value is within tolerance of the oracle's value at the unfused maximum.
+    n, k, fmt = 248320, 5120, NV
+    packed, scales, g = weight(synth.LM_HEAD, 0, n, k, fmt)
+    pc, ps, _ = prepared(synth.LM_HEAD, 0, n, k, fmt)
+    xbits = synth.activations(synth.LM_HEAD, m, k)
+    xd = x_dev(xbits)
+    ybits = y_host_bits(fp4.fp4_w4a16_linear(xd, pc, ps, n, float(g), fmt))
+    idx, val, _ = fp4.fp4_w4a16_linear_argmax(xd, pc, ps, n, float(g), fmt)
+    got = idx.cpu().numpy()
+    want = oracle.greedy_argmax(oracle.bf16_bits_to_f32(ybits))
+    assert got.tolist() == want.tolist()
+    import torch
+    assert val.view(torch.int16).cpu().numpy().view(np.uint16).tolist() == ybits[np.arange(m), got].tolist()
+    # Oracle values at the winner and at a sample of other rows.
+    rows = np.unique(np.concatenate([sample_rows(n, 512, seed=m), got]))
+    y_ref = oracle.linear_rows(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g, rows)
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    for i in range(m):
+        at = y_ref[i, np.searchsorted(rows, got[i])]
+        top = y_ref[i].max()
+        assert at >= top - (2.0 ** -7 * abs(top) + 1e-3 * rms), i

@@ -58,3 +58,36 @@ def test_graph_replay_matches_eager(fmt, n, k, m, split):
         # An eager call between replays must not disturb the next replay.
         call(y_eager)
         torch.cuda.synchronize()
+
+
+def test_graph_replay_argmax():
+    # The greedy-argmax call (decode kernel epilogue + reduce launch) replayed
+    # from a graph with new activations gives the eager call's token ids.
+    fmt, n, k, m = NV, 9000, 5120, 2
+    packed, scales, g = synth.packed_weight(synth.TINY, 71, n, k, fmt)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
+    ws = torch.full((fp4.fp4_argmax_workspace_bytes(m, n, k, fmt),), 0xA5, dtype=torch.uint8, device=DEV)
+    x = x_dev(synth.activations(synth.TINY, m, k))
+    idx = torch.empty(m, dtype=torch.int32, device=DEV)
+    val = torch.empty(m, dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        fp4.fp4_w4a16_linear_argmax(x, pc, ps, n, float(g), fmt, idx=idx, val=val, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    for rep in range(4):
+        xb = rng.standard_normal((m, k), dtype=np.float32)
+        x.copy_(x_dev((xb.view(np.uint32) >> 16).astype(np.uint16)))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy().tolist()
+        call()
+        torch.cuda.synchronize()
+        assert got == idx.cpu().numpy().tolist(), rep
+
