@@ -245,6 +245,9 @@ def main():
                     help="replay the timed calls from a captured HIP graph, or launch them one by one")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-crosscheck", action="store_true",
+                    help="skip the differencing and split-launch cross-checks (e.g. under a counter "
+                         "profiler, where their launches would mix with the timed ones)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device-to-device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -373,7 +376,7 @@ def main():
     # * fused gate_up only: the same step with the gate and up halves launched
     #   separately (two calls per step, the halves of the same prepared weight).
     n1 = max(1, args.steps // 4)
-    for j, d in enumerate(per_m):
+    for j, d in enumerate(per_m if not args.no_crosscheck else []):
         t1 = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), n1, args.launch == "graph")
         if args.steps > n1:
             rows[j]["us_per_launch_differenced"] = round((d["t_ms"] - t1) * 1e3 / (args.steps - n1), 3)
