@@ -148,3 +148,25 @@ def greedy_argmax(logits):
                 best = j
         out[i] = best
     return out
+
+
+def moe_decode(x, experts, k, fmt, expert_offsets, pair_tokens):
+    """Grouped MoE W4A16 reference: for every routed (token, expert) pair p,
+    y[p] = linear(x[pair_tokens[p]], W_e) with e the expert whose range
+    [expert_offsets[e], expert_offsets[e + 1]) holds p.
+
+    The grouped route computes, per expert, the same W4A16 product as the
+    dense layer ("MXFP4 decode-graph + gate_up FUSION default-ON", vllm.cpp
+    PR #54, the later commit on the dense-template marlin port: the dense
+    projections had run as the single-expert case of the grouped MoE route).
+    experts: list of (packed, scales, global_scale) per expert.  Plain loops.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    offsets = [int(v) for v in expert_offsets]
+    tokens = [int(v) for v in pair_tokens]
+    n = np.asarray(experts[0][0]).shape[0]
+    y = np.zeros((len(tokens), n), dtype=np.float64)
+    for e, (packed, scales, g) in enumerate(experts):
+        for p in range(offsets[e], offsets[e + 1]):
+            y[p] = linear(x[tokens[p]:tokens[p] + 1], packed, scales, k, fmt, g)[0]
+    return y
