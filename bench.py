@@ -18,6 +18,9 @@ Workloads (synthetic weights and activations at the pages' shapes):
   lm_head        NVFP4 packed lm_head, k=5120, n=248320
   lm_head_argmax the same head with the fused greedy argmax (token ids out,
                  no logits)
+  moe_gate_up    grouped MoE decode, NVFP4, 128 experts of n=1536, k=2048,
+                 top-8 routing of m tokens (m = 1, 2, 4, 8); bytes counted
+                 over the experts the routing activates
   down_proj      NVFP4, k=17408, n=5120
   o_proj         NVFP4, k=6144, n=5120
   prefill_nvfp4  NVFP4, k=5120, n=17408 (m=1024 by default)
@@ -66,6 +69,7 @@ WORKLOADS = {
     "gate_up": (1, 1, 12288, 4096, 2, 8),
     "lm_head": (2, 0, 248320, 5120, 1, 8),
     "lm_head_argmax": (2, 0, 248320, 5120, 1, 8),
+    "moe_gate_up": (0, 0, 1536, 2048, 1, 8),
     "down_proj": (3, 0, 5120, 17408, 1, 8),
     "o_proj": (3, 0, 5120, 6144, 1, 8),
     "prefill_nvfp4": (4, 0, 17408, 5120, 1, 1024),
@@ -75,6 +79,10 @@ WORKLOADS = {
 TENSOR = {"o_proj": 1, "prefill_mxfp4": 1}
 # Workloads that run the greedy-argmax entry point (no logits written).
 ARGMAX = {"lm_head_argmax"}
+# Grouped MoE decode: 128 experts, top-8 routing per token, each expert a
+# gate_up weight of 2 x 768 rows over k = 2048 (an A3B-class MoE block's
+# shape; synthetic).  8 distinct expert weights are repeated over the 128.
+MOE_EXPERTS, MOE_TOPK, MOE_DISTINCT = 128, 8, 8
 
 
 def algorithmic_bytes(fmt, n_proj, k, projections, m, argmax=False):
@@ -233,6 +241,110 @@ def timed_calls(torch, fn, count, graph):
     return e0.elapsed_time(e1)
 
 
+def moe_routing(np, tokens, seed):
+    """Top-MOE_TOPK distinct experts per token (seeded), pairs sorted by expert."""
+    rng = np.random.default_rng(seed)
+    pairs = sorted((int(e), t) for t in range(tokens)
+                   for e in rng.choice(MOE_EXPERTS, size=MOE_TOPK, replace=False))
+    offsets = np.searchsorted([p[0] for p in pairs], np.arange(MOE_EXPERTS + 1)).astype(np.int32)
+    return offsets, np.array([p[1] for p in pairs], dtype=np.int32), sorted({p[0] for p in pairs})
+
+
+def run_moe(args, torch, np, fp4, synth):
+    """The grouped MoE decode workload: one fp4_w4a16_moe_decode call per step and m."""
+    name = args.workload
+    wid, fmt, n, k, _, _ = WORKLOADS[name]
+    ms = [1, 2, 4, 8] if args.m is None else [int(v) for v in args.m.split(",")]
+    dev = torch.device("cuda:0")
+    host, codes, scales, gvals = [], [], [], []
+    for e in range(MOE_DISTINCT):
+        p, s, g = synth.packed_weight(wid, 200 + e, n, k, fmt)
+        pc, ps = fp4.fp4_prepare(torch.from_numpy(p).to(dev), torch.from_numpy(s).to(dev), n, k, fmt)
+        host.append((p, s, g))
+        codes.append(pc)
+        scales.append(ps)
+        gvals.append(float(g))
+    rep_idx = [e % MOE_DISTINCT for e in range(MOE_EXPERTS)]
+    pc_all = torch.cat([codes[i] for i in rep_idx])
+    ps_all = torch.cat([scales[i] for i in rep_idx])
+    gs = torch.tensor([gvals[i] for i in rep_idx], dtype=torch.float32, device=dev)
+    footprint = pc_all.numel() + ps_all.numel()
+    copies = max(2, math.ceil(ROTATE_BYTES / footprint))
+    weights = [(pc_all, ps_all)] + [(pc_all.clone(), ps_all.clone()) for _ in range(copies - 1)]
+    cb, sb = fp4.fp4_prepared_bytes(n, k, fmt)
+    g_div = 16 if fmt == 0 else 32
+    per_expert = n * k // 2 + n * k // g_div + (4 if fmt == 0 else 0)
+
+    per_m = []
+    for m in ms:
+        offsets, ptok, active = moe_routing(np, m, seed=1000 + m)
+        xb = synth.activations(wid, m, k)
+        d = {"m": m, "x": torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16), "xb": xb,
+             "offsets": torch.from_numpy(offsets).to(dev), "ptok": torch.from_numpy(ptok).to(dev),
+             "offsets_h": offsets, "ptok_h": ptok, "active": active, "pairs": len(ptok),
+             "y": torch.empty((len(ptok), n), dtype=torch.bfloat16, device=dev),
+             "ws": torch.empty(fp4.fp4_moe_workspace_bytes(len(ptok), k), dtype=torch.uint8, device=dev),
+             "info": fp4.fp4_dispatch_info()}
+        d["bytes"] = len(active) * per_expert + 2 * m * k + 2 * len(ptok) * n
+        per_m.append(d)
+
+    def call(d, i):
+        c, s = weights[i % copies]
+        fp4.fp4_w4a16_moe_decode(d["x"], c, s, n, MOE_EXPERTS, gs if fmt == 0 else None, fmt, d["offsets"],
+                                 d["ptok"], y=d["y"], workspace=d["ws"], info=d["info"])
+
+    for d in per_m:
+        for i in range(args.warmup):
+            call(d, i)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for d in per_m:
+        d["t_ms"] = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), args.steps, args.launch == "graph")
+    t_wall = time.perf_counter() - t_wall0
+    rows, total_ms, total_bytes = [], 0.0, 0
+    for d in per_m:
+        us = d["t_ms"] * 1e3 / args.steps
+        total_ms += d["t_ms"]
+        total_bytes += d["bytes"] * args.steps
+        info = d["info"]
+        rows.append({"m": d["m"], "kernel": "moe_decode_kernel<%s>" % ("nvfp4" if fmt == 0 else "mxfp4"),
+                     "us_per_launch": round(us, 3), "gbs": round(d["bytes"] / (us * 1e-6) / 1e9, 2),
+                     "pairs": d["pairs"], "active_experts": len(d["active"]),
+                     "grid": [info.grid_x, info.grid_y], "block": info.block, "algorithmic_bytes": d["bytes"]})
+    dom = max(rows, key=lambda r: r["us_per_launch"])
+    out = {
+        "metric": METRIC, "value": round(total_bytes / (total_ms * 1e-3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "fmt": "nvfp4" if fmt == 0 else "mxfp4", "m": ms, "n": n, "k": k,
+                   "experts": MOE_EXPERTS, "topk": MOE_TOPK, "distinct_expert_weights": MOE_DISTINCT,
+                   "launch": args.launch, "rotated_weight_copies": copies,
+                   "step": "one grouped call per m (m tokens, top-%d routing)" % MOE_TOPK, "per_m": rows,
+                   "wall_s_timed": round(t_wall, 4)},
+        "roofline": {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4), "kernel": dom["kernel"], "m": dom["m"],
+                     "avg_launch_us": dom["us_per_launch"], "units_per_launch": dom["algorithmic_bytes"],
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        d = per_m[0]
+        xs = oracle.bf16_bits_to_f32(d["xb"])
+        experts = [host[i] for i in rep_idx]
+        t0 = time.perf_counter()
+        reps = 0
+        while reps == 0 or (time.perf_counter() - t0 < args.cpu_budget and reps < 20):
+            oracle.moe_decode(xs, experts, k, fmt, d["offsets_h"], d["ptok_h"])
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        out["cpu_baseline"] = {"value": round(d["bytes"] / dt / 1e9, 4), "unit": "GB/s",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": "oracle.moe_decode of the m = %d call (%d pairs over %d experts), %d "
+                                         "repetitions" % (d["m"], d["pairs"], len(d["active"]), reps)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +386,8 @@ def main():
         return
 
     name = args.workload
+    if name == "moe_gate_up":
+        return run_moe(args, torch, np, fp4, synth)
     wid, fmt, n, k, proj, m_default = WORKLOADS[name]
     if args.m is None:
         ms = [1, 2, 4, 8] if m_default <= 8 else [m_default]

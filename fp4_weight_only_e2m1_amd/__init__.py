@@ -54,6 +54,9 @@ _SIGNATURES = {
     "fp4_argmax_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fp4_w4a16_linear_argmax": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _i, _vp, _vp, _vp, _vp, _sz, _vp,
                                      ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_moe_workspace_bytes": (_i, [_i, _i, ctypes.POINTER(_sz)]),
+    "fp4_w4a16_moe_decode": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _sz, _vp,
+                                  ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_dequantize": (_i, [_vp, _vp, _i, _i, _f, _i, _vp, _vp]),
     "fp4_status_string": (ctypes.c_char_p, [_i]),
 }
@@ -257,6 +260,50 @@ def fp4_w4a16_linear_argmax(x, prep_codes, prep_scales, n, global_scale, fmt, lo
         _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n, float(global_scale), fmt, _ptr(y), _ptr(idx),
         _ptr(val), _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
     return idx, val, y
+
+
+def fp4_moe_workspace_bytes(pairs, k):
+    out = _sz()
+    _check("fp4_moe_workspace_bytes", load_library().fp4_moe_workspace_bytes(pairs, k, ctypes.byref(out)))
+    return out.value
+
+
+def fp4_w4a16_moe_decode(x, prep_codes, prep_scales, n, experts, global_scales, fmt, expert_offsets,
+                         pair_tokens, y=None, workspace=None, stream=None, info=None):
+    """Grouped MoE decode: y[p] = x[pair_tokens[p]] @ w_e.T for every routed pair p (sorted by expert,
+    expert e owning pairs expert_offsets[e] .. expert_offsets[e + 1]).  prep_codes / prep_scales hold
+    the experts' prepared weights stacked; global_scales is float32 [experts] (NVFP4) or None (MXFP4).
+    Returns y bf16 [pairs, n]."""
+    _need(x, torch.bfloat16, "x")
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    _need(pair_tokens, torch.int32, "pair_tokens")
+    if global_scales is not None:
+        _need(global_scales, torch.float32, "global_scales")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [tokens, k]")
+    tokens, k = x.shape
+    pairs = pair_tokens.numel()
+    cb, sb = fp4_prepared_bytes(n, k, fmt)
+    if prep_codes.numel() < experts * cb or prep_scales.numel() < experts * sb:
+        raise ValueError("stacked prepared buffers smaller than experts x fp4_prepared_bytes(n, k, fmt)")
+    if expert_offsets.numel() != experts + 1:
+        raise ValueError("expert_offsets must hold experts + 1 values")
+    if y is None:
+        y = torch.empty((pairs, n), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y")
+    if y.numel() != pairs * n:
+        raise ValueError("y must hold pairs x n values")
+    need = fp4_moe_workspace_bytes(pairs, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("fp4_w4a16_moe_decode", load_library().fp4_w4a16_moe_decode(
+        _ptr(x), tokens, k, _ptr(prep_codes), _ptr(prep_scales), n, experts, _ptr(global_scales), fmt,
+        _ptr(expert_offsets), _ptr(pair_tokens), pairs, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream),
+        None if info is None else ctypes.byref(info)))
+    return y
 
 
 def fp4_dequantize(prep_codes, prep_scales, n, k, global_scale, fmt, out=None, stream=None):

@@ -262,6 +262,75 @@ int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k, const uint8_t* 
                     workspace_bytes, stream, info_out, idx_out_dev, val_out_dev);
 }
 
+int fp4_moe_workspace_bytes(int pairs, int k, size_t* bytes_out) {
+  if (pairs < 0 || pairs > FP4_MAX_M || k <= 0 || k > FP4_MAX_K || k % 32 != 0 || !bytes_out) return FP4_EINVAL;
+  *bytes_out = static_cast<size_t>(fp4::round_up(static_cast<int64_t>(pairs) * k * 2, 256));
+  return FP4_OK;
+}
+
+int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_codes_dev,
+                         const uint8_t* prep_scales_dev, int n, int experts, const float* global_scales_dev, int fmt,
+                         const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
+                         uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
+                         fp4_dispatch_info* info_out) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if (tokens < 0 || tokens > FP4_MAX_M || pairs < 0 || pairs > FP4_MAX_M) return FP4_EINVAL;
+  if (experts < 1 || experts > 65535) return FP4_EINVAL;
+  const bool mx = fmt == FP4_FMT_MXFP4;
+  if (pairs == 0) {
+    if (info_out) *info_out = fp4_dispatch_info{3, 1, 0, 0, 0};
+    return FP4_OK;
+  }
+  if (tokens == 0 || !x_dev || !prep_codes_dev || !prep_scales_dev || !expert_offsets_dev || !pair_tokens_dev ||
+      !y_dev || (!mx && !global_scales_dev))
+    return FP4_EINVAL;
+  if (!aligned16(x_dev) || !aligned16(prep_codes_dev) || !aligned16(prep_scales_dev) || !aligned16(y_dev) ||
+      reinterpret_cast<uintptr_t>(expert_offsets_dev) % 4 != 0 || reinterpret_cast<uintptr_t>(pair_tokens_dev) % 4 != 0 ||
+      (!mx && reinterpret_cast<uintptr_t>(global_scales_dev) % 4 != 0))
+    return FP4_EALIGN;
+  size_t need = 0;
+  if ((st = fp4_moe_workspace_bytes(pairs, k, &need))) return st;
+  if (workspace_bytes < need) return FP4_EWORKSPACE;
+  if (!workspace_dev) return FP4_EINVAL;
+  if (!aligned16(workspace_dev)) return FP4_EALIGN;
+
+  const fp4::PreparedShape ps = fp4::prepared_shape(n, k, fmt);
+  fp4::GemvArgs a{};
+  a.codes = prep_codes_dev;
+  a.scales = prep_scales_dev;
+  a.y = y_dev;
+  a.m = fp4::kGemvMaxM;
+  a.k = k;
+  a.k_pad = ps.k_pad;
+  a.kgroups = ps.kgroups;
+  a.ksegs = ps.ksegs;
+  a.nslab = static_cast<int>(ps.k_pad / fp4::kSlabK);
+  a.splits = 1;
+  a.n_proj = n;
+  a.n_proj_pad = ps.n_pad;
+  a.projections = 1;
+  a.rows_total = ps.n_pad;
+  a.ldy = n;
+  a.gscale[0] = a.gscale[1] = 1.0f;
+  a.tile_rows = fp4::kDecodeTileRows;
+  fp4::MoeArgs moe{};
+  moe.offsets = expert_offsets_dev;
+  moe.x_sorted = static_cast<const uint16_t*>(workspace_dev);
+  moe.gscales = mx ? nullptr : global_scales_dev;
+  moe.code_stride = ps.code_bytes;
+  moe.scale_stride = ps.scale_bytes;
+  moe.pairs = pairs;
+  dim3 grid, block;
+  const hipError_t e = fp4::launch_moe_decode(a, moe, experts, x_dev, pair_tokens_dev, tokens,
+                                              static_cast<uint16_t*>(workspace_dev), fmt, stream, &grid, &block);
+  if (e != hipSuccess) return FP4_EHIP;
+  if (info_out) *info_out = fp4_dispatch_info{3, 1, static_cast<int>(grid.x), static_cast<int>(grid.y),
+                                              static_cast<int>(block.x)};
+  return FP4_OK;
+}
+
 int fp4_dequantize(const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int k, float global_scale,
                    int fmt, float* out_dev, hipStream_t stream) {
   int st = check_fmt(fmt);

@@ -209,7 +209,7 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
       for (int b = 0; b < kBatch; ++b)
         if (s0 + b < a.splits) s = s0 + b == 0 ? v[b] : s + v[b];
     }
-    const uint16_t yb = f32_to_bf16_rne(s * a.gscale[h]);
+    const uint16_t yb = f32_to_bf16_rne(s * (h == 0 ? a.gscale[0] : a.gscale[1]));
     if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
     if (a.keys) tile_argmax_offer(al, m, argmax_key(yb, col));
   }

@@ -123,7 +123,7 @@ struct Copier {
   int k;
   uint32_t lds_wave;     // this wave's 1 KiB slice of a stage area
 
-  __device__ __forceinline__ Copier(const GemvArgs& a, int64_t row0, int t, int wave) {
+  __device__ __forceinline__ Copier(const GemvArgs& a, int64_t row0, int t, int wave, int mrows) {
     const int64_t row_bytes = a.k_pad / 2;
     k = a.k;
     x = a.x;
@@ -139,7 +139,7 @@ struct Copier {
     }
     const int xr = t >> 5;
     const int ch = (t & 31) ^ xr;
-    xrow_ok = xr < M;
+    xrow_ok = xr < mrows;
     xoff = xrow_ok ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
     xk = 8 * ch;
     // Scales of a stage: 4 RB row groups x 8 segments x 16 rows x P bytes,
@@ -203,7 +203,7 @@ struct alignas(256) ZeroRow {
 // zero row the lanes of rows r >= m read instead of x.
 template <int M, int FMT, int RB>
 __device__ __forceinline__ void compute_stage(const Stage<RB, FMT>& sb, const uint4* zrow, int wave, int r, int g,
-                                              f32x4_t (&acc)[RB]) {
+                                              int mrows, f32x4_t (&acc)[RB]) {
   constexpr int P = scales_per_seg(FMT);
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sb.s);
 #pragma unroll
@@ -226,7 +226,7 @@ __device__ __forceinline__ void compute_stage(const Stage<RB, FMT>& sb, const ui
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int ch = 16 * q + 4 * g + c;
-      const uint4 xv = r < M ? sb.x[x_slot(r, ch)] : zrow[ch];
+      const uint4 xv = r < mrows ? sb.x[x_slot(r, ch)] : zrow[ch];
       Frag af;
       af.u[0] = xv.x;
       af.u[1] = xv.y;
@@ -264,14 +264,16 @@ __device__ __forceinline__ void wait_for_stage(int s, int s1, int wave) {
 template <int M, int FMT, int RB, int NB>
 __device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB>& cp, int s, int s1,
                                               const Stage<RB, FMT>& cur, Stage<RB, FMT>& prev, const uint4* zrow,
-                                              int wave, int r, int g, f32x4_t (&acc)[RB]) {
+                                              int wave, int r, int g, int mrows, f32x4_t (&acc)[RB]) {
   wait_for_stage<RB, FMT, NB>(s, s1, wave);
   if (s + NB - 1 < s1) cp.issue(static_cast<int64_t>(s + NB - 1) * kStageK, prev, wave);
-  compute_stage<M, FMT, RB>(cur, zrow, wave, r, g, acc);
+  compute_stage<M, FMT, RB>(cur, zrow, wave, r, g, mrows, acc);
 }
 
+// One (tile, split) of a decode call with mrows <= M activation rows (M when
+// launched per call; the rows of one expert in the grouped MoE launch).
 template <int M, int FMT, int RB, int NB>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a) {
+__device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int split, int mrows) {
   __shared__ Stage<RB, FMT> st[NB];
   __shared__ ZeroRow zero_row;
   constexpr int kRows = Geo<RB, FMT>::kRows;
@@ -281,8 +283,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
   const int lane = t & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int tile = blockIdx.x;
-  const int split = blockIdx.y;
   const int64_t row0 = static_cast<int64_t>(tile) * kRows;
   const int ksteps = (a.k + kStageK - 1) / kStageK;
   const int s0 = static_cast<int>(static_cast<int64_t>(split) * ksteps / a.splits);
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
 #pragma unroll
   for (int b = 0; b < RB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (t < 32) zero_row.z[t] = make_uint4(0u, 0u, 0u, 0u);  // visible after the first stage barrier
-  const Copier<M, FMT, RB> cp(a, row0, t, wave);
+  const Copier<M, FMT, RB> cp(a, row0, t, wave, mrows);
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j)
     if (s0 + j < s1) cp.issue(static_cast<int64_t>(s0 + j) * kStageK, st[j], wave);
@@ -300,7 +300,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (s + j >= s1) break;
-      pipeline_step<M, FMT, RB, NB>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g, acc);
+      pipeline_step<M, FMT, RB, NB>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g, mrows,
+                                    acc);
     }
   }
 
@@ -324,8 +325,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = 4 * g + i;
-          if (m < M) {
-            const uint16_t yb = f32_to_bf16_rne(acc[b][i] * a.gscale[h]);
+          if (m < mrows) {
+            const uint16_t yb = f32_to_bf16_rne(acc[b][i] * (h == 0 ? a.gscale[0] : a.gscale[1]));
             if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
             const uint64_t key = argmax_key(yb, col);
             if (key > best[i]) best[i] = key;
@@ -360,6 +361,58 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
   splitk_finish<M>(a, tile, split);
 }
 
+template <int M, int FMT, int RB, int NB>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a) {
+  decode_tile<M, FMT, RB, NB>(a, blockIdx.x, blockIdx.y, M);
+}
+
+// Grouped MoE decode: workgroup (tile, e) computes 64-row tile `tile` of
+// expert e for the routed pairs [offsets[e], offsets[e + 1]) -- their x rows
+// gathered in pair order (x_sorted) and their outputs at the same pair rows
+// of y -- 8 pairs per pass.  Expert e's prepared weight sits at e times the
+// prepared size in the stacked buffers; an expert with no pairs exits.  The
+// offsets are clamped to [0, pairs], so no routing table can make a workgroup
+// read or write outside x_sorted and y.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs base, const MoeArgs moe) {
+  const int e = blockIdx.y;
+  // Workgroup-uniform values: kept in scalar registers (the copy bases built
+  // from them must be).
+  int p0 = __builtin_amdgcn_readfirstlane(moe.offsets[e]);
+  int p1 = __builtin_amdgcn_readfirstlane(moe.offsets[e + 1]);
+  p0 = p0 < 0 ? 0 : p0 > moe.pairs ? moe.pairs : p0;
+  p1 = p1 < p0 ? p0 : p1 > moe.pairs ? moe.pairs : p1;
+  if (p1 <= p0) return;
+  GemvArgs a = base;
+  a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
+  a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
+  a.gscale[0] = a.gscale[1] = moe.gscales ? moe.gscales[e] : 1.0f;
+  for (int c0 = p0; c0 < p1; c0 += kGemvMaxM) {
+    a.x = moe.x_sorted + static_cast<int64_t>(c0) * a.k;
+    a.y = base.y + static_cast<int64_t>(c0) * a.ldy;
+    decode_tile<kGemvMaxM, FMT, 1, kDecodeBuffers>(a, blockIdx.x, 0, p1 - c0 < kGemvMaxM ? p1 - c0 : kGemvMaxM);
+    __syncthreads();  // the stage buffers are reused by the next pass
+  }
+}
+
+// x_sorted[p] = x[tokens[p]]: 16-byte chunks, one per thread.  A token id
+// outside [0, tokens_total) gathers a zero row.
+__global__ __launch_bounds__(256) void moe_gather_kernel(const uint16_t* x, const int32_t* tokens, int pairs, int k,
+                                                         int tokens_total, uint16_t* x_sorted) {
+  const int64_t chunks = static_cast<int64_t>(k) / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= chunks * pairs) return;
+  const int p = static_cast<int>(i / chunks);
+  const int64_t c = i - static_cast<int64_t>(p) * chunks;
+  const int tok = tokens[p];
+  if (tok < 0 || tok >= tokens_total) {
+    *reinterpret_cast<uint4*>(x_sorted + static_cast<int64_t>(p) * k + 8 * c) = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  *reinterpret_cast<uint4*>(x_sorted + static_cast<int64_t>(p) * k + 8 * c) =
+      *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(tok) * k + 8 * c);
+}
+
 template <int FMT, int RB>
 hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
   const dim3 block(kThreads);
@@ -377,6 +430,24 @@ hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, const uint16_t* x, const int32_t* tokens,
+                             int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid_out,
+                             dim3* block_out) {
+  const int64_t chunks = static_cast<int64_t>(moe.pairs) * (a.k / 8);
+  hipLaunchKernelGGL(moe_gather_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0, stream, x,
+                     tokens, moe.pairs, a.k, tokens_total, x_sorted);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>(a.rows_total / kDecodeTileRows), static_cast<unsigned>(experts));
+  if (grid_out) *grid_out = grid;
+  if (block_out) *block_out = dim3(kThreads);
+  if (fmt == kFmtNvfp4)
+    hipLaunchKernelGGL(moe_decode_kernel<kFmtNvfp4>, grid, dim3(kThreads), 0, stream, a, moe);
+  else
+    hipLaunchKernelGGL(moe_decode_kernel<kFmtMxfp4>, grid, dim3(kThreads), 0, stream, a, moe);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
   if (a.tile_rows != 64 && a.tile_rows != 128) return hipErrorInvalidValue;

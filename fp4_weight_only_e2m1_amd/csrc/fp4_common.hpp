@@ -141,6 +141,16 @@ struct GemvArgs {
   int tile_rows;          // rows per workgroup (the split-K finish tile)
 };
 
+// Grouped MoE decode: routed (token, expert) pairs sorted by expert.
+struct MoeArgs {
+  const int32_t* offsets;    // [experts + 1]: expert e's pairs are [offsets[e], offsets[e + 1])
+  const uint16_t* x_sorted;  // bf16 [pairs][k]: x row of each pair (gathered)
+  const float* gscales;      // [experts] NVFP4 global scales, or null (MXFP4)
+  int64_t code_stride;       // bytes between experts' prepared codes
+  int64_t scale_stride;      // bytes between experts' prepared scales
+  int pairs;
+};
+
 // Prefill GEMM tiling.  A workgroup of kGemmWavesM x 4 waves computes a
 // kGemmBM (activation rows) x kGemmBN (weight rows) tile of y, each wave a
 // 128 x 64 block of it, stepping K by kGemmBK.  kGemmSlots workgroups are
@@ -215,6 +225,9 @@ hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, in
                           uint8_t* prep_codes, uint8_t* prep_scales, hipStream_t stream);
 hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
+hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, const uint16_t* x, const int32_t* tokens,
+                             int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid,
+                             dim3* block);
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_argmax_reduce(const uint64_t* keys, int tiles, int m, int32_t* idx, uint16_t* val,
                                 hipStream_t stream);

@@ -66,7 +66,7 @@ enum fp4_status {
 /* Which kernel a call ran (filled when the caller passes a non-null pointer). */
 typedef struct fp4_dispatch_info {
   int kernel;  /* 0 = VALU decode GEMV, 2 = MFMA decode GEMV (both m <= 8),
-                  1 = MFMA tile GEMM (m > 8) */
+                  1 = MFMA tile GEMM (m > 8), 3 = grouped MoE decode */
   int splits;  /* K splits: decode kernels split every tile, the tile GEMM only
                   its tail tiles (1 = no split) */
   int grid_x;  /* decode: workgroups along the output rows; tile GEMM:
@@ -191,6 +191,47 @@ int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k,
                             int32_t* idx_out_dev, uint16_t* val_out_dev,
                             void* workspace_dev, size_t workspace_bytes,
                             hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
+ * Grouped MoE decode: for each routed (token, expert) pair p,
+ *   y[p][:] = x[pair_tokens[p]] * w_e^T   (e = the expert of pair p),
+ * computed as fp4_w4a16_linear would for that expert's weight (float32
+ * accumulation, the expert's NVFP4 global scale applied after the sum,
+ * bf16 round to nearest even).  Routing and the weighted combine of the
+ * pairs are the caller's.
+ *   x_dev              bf16 [tokens][k];
+ *   prep_codes_dev / prep_scales_dev  the experts' prepared weights (n rows
+ *                      each, fp4_prepare) stacked: expert e at e times the
+ *                      sizes fp4_prepared_bytes(n, k, fmt) gives;
+ *   global_scales_dev  float32 [experts] NVFP4 global scales (device memory);
+ *                      ignored and may be NULL for MXFP4;
+ *   expert_offsets_dev int32 [experts + 1]: the pairs are sorted by expert,
+ *                      expert e's are [offsets[e], offsets[e + 1]);
+ *   pair_tokens_dev    int32 [pairs]: the token (row of x) of each pair;
+ *   y_dev              bf16 [pairs][n];
+ *   workspace_dev      fp4_moe_workspace_bytes(pairs, k) (the gathered x rows).
+ * Device-side routing data is not validated on the host: offsets are clamped
+ * to [0, pairs] and a token id outside [0, tokens) reads a zero row, so no
+ * table can make the kernels access memory outside these buffers.  Two
+ * launches: a gather of the pairs' x rows, then one workgroup per (64-row
+ * tile, expert) -- experts without pairs exit at once -- on the matrix cores
+ * (the m = 3..8 decode kernel, up to 8 pairs of an expert per pass).  The sum
+ * order of an output depends only on (k, fmt): a pair's result does not
+ * depend on the other pairs.
+ * Cite: "MXFP4 decode-graph + gate_up FUSION default-ON" (vllm.cpp PR #54),
+ * the later commit on the dense-template marlin port: the dense projections
+ * had run as the single-expert case of the grouped MoE W4A16 route, the same
+ * per-expert product; "re-verify 27B NVFP4 on the nvidia ModelOpt checkpoint"
+ * (vllm.cpp PR #178), section on the 35B result: the MoE model's grouped
+ * W4A16 operations have their own test gates.
+ */
+int fp4_moe_workspace_bytes(int pairs, int k, size_t* bytes_out);
+int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k,
+                         const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int experts,
+                         const float* global_scales_dev, int fmt,
+                         const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
+                         uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes,
+                         hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
  * Dequantize a prepared weight to float32 out_dev [n][k]:

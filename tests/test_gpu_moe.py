@@ -1,0 +1,107 @@
+"""GPU parity of the grouped MoE decode (fp4_w4a16_moe_decode) against the
+oracle's per-pair reference: random top-k routings over several experts
+(empty experts, an expert with more than 8 pairs), pair independence bit for
+bit, and routing tables that point outside the buffers."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_weight_only_e2m1_amd as fp4
+import oracle
+import synth
+from gpu_util import DEV, assert_close, u8, x_dev, y_host, y_host_bits
+
+pytestmark = pytest.mark.gpu
+
+NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
+
+
+def _stacked(experts, n, k, fmt, seed):
+    host, codes, scales = [], [], []
+    for e in range(experts):
+        packed, sc, g = synth.packed_weight(synth.TINY, 100 + seed + e, n, k, fmt)
+        pc, ps = fp4.fp4_prepare(u8(packed), u8(sc), n, k, fmt)
+        host.append((packed, sc, g))
+        codes.append(pc)
+        scales.append(ps)
+    gs = torch.tensor([float(h[2]) for h in host], dtype=torch.float32, device=DEV)
+    return host, torch.cat(codes), torch.cat(scales), gs
+
+
+def _routing(tokens, experts, topk, seed):
+    """Top-k distinct experts per token, pairs sorted by expert (then token)."""
+    rng = np.random.default_rng(seed)
+    pairs = sorted((int(e), t) for t in range(tokens) for e in rng.choice(experts, size=topk, replace=False))
+    offsets = np.searchsorted([p[0] for p in pairs], np.arange(experts + 1)).astype(np.int32)
+    return offsets, np.array([p[1] for p in pairs], dtype=np.int32)
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+@pytest.mark.parametrize("fmt,n,k", [(NV, 768, 2048), (MX, 300, 1056), (NV, 520, 4096), (MX, 1024, 512)])
+@pytest.mark.parametrize("tokens,experts,topk", [(1, 16, 4), (4, 16, 4), (8, 32, 8), (8, 4, 3)])
+def test_moe_decode_matches_oracle(fmt, n, k, tokens, experts, topk):
+    host, pc, ps, gs = _stacked(experts, n, k, fmt, 0)
+    offsets, ptok = _routing(tokens, experts, topk, seed=tokens * 100 + experts)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    info = fp4.fp4_dispatch_info()
+    y = fp4.fp4_w4a16_moe_decode(x_dev(xbits), pc, ps, n, experts, gs if fmt == NV else None, fmt,
+                                 _i32(offsets), _i32(ptok), info=info)
+    assert info.kernel == 3 and info.grid_y == experts and info.grid_x == -(-n // 256) * 256 // 64
+    y_ref = oracle.moe_decode(oracle.bf16_bits_to_f32(xbits), host, k, fmt, offsets, ptok)
+    assert_close(y_host(y), y_ref, "moe fmt=%d n=%d k=%d T=%d E=%d" % (fmt, n, k, tokens, experts))
+
+
+def test_moe_pairs_independent_and_long_expert():
+    # 12 tokens all routed to expert 2 (two passes of 8 and 4), plus others;
+    # dropping pairs leaves every remaining pair's output bit for bit.
+    fmt, n, k, experts, tokens = NV, 640, 2048, 5, 12
+    host, pc, ps, gs = _stacked(experts, n, k, fmt, 7)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    xd = x_dev(xbits)
+    full = [(0, 3), (0, 7)] + [(2, t) for t in range(tokens)] + [(4, 1), (4, 5), (4, 11)]
+    sub = [p for i, p in enumerate(full) if i % 3 != 1]
+
+    def run(pairs):
+        e_of = np.array([p[0] for p in pairs])
+        offsets = np.searchsorted(e_of, np.arange(experts + 1)).astype(np.int32)
+        ptok = np.array([p[1] for p in pairs], dtype=np.int32)
+        y = y_host_bits(fp4.fp4_w4a16_moe_decode(xd, pc, ps, n, experts, gs, fmt, _i32(offsets), _i32(ptok)))
+        return offsets, ptok, y
+
+    off, ptok, y_full = run(full)
+    _, _, y_sub = run(sub)
+    rows = {p: i for i, p in enumerate(full)}
+    for j, p in enumerate(sub):
+        assert np.array_equal(y_sub[j], y_full[rows[p]]), p
+    y_ref = oracle.moe_decode(oracle.bf16_bits_to_f32(xbits), host, k, fmt, off, ptok)
+    assert_close(oracle.bf16_bits_to_f32(y_full).astype(np.float64), y_ref, "moe long expert")
+
+
+def test_moe_out_of_range_routing_is_contained():
+    # Offsets beyond the pair count are clamped; token ids outside x read zero
+    # rows (their outputs are exactly zero); nothing else is touched.
+    fmt, n, k, experts, tokens = MX, 256, 1024, 3, 2
+    host, pc, ps, _ = _stacked(experts, n, k, fmt, 9)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    offsets = np.array([0, 2, 9, 1 << 30], dtype=np.int32)
+    ptok = np.array([0, -5, 1, 7], dtype=np.int32)
+    y = torch.full((4, n), 3.0, dtype=torch.bfloat16, device=DEV)
+    fp4.fp4_w4a16_moe_decode(x_dev(xbits), pc, ps, n, experts, None, fmt, _i32(offsets), _i32(ptok), y=y)
+    got = y_host(y)
+    assert np.isfinite(got).all()
+    assert (got[1] == 0).all() and (got[3] == 0).all()
+    ref = oracle.moe_decode(oracle.bf16_bits_to_f32(xbits), host, k, fmt, [0, 2, 4, 4], [0, 0, 1, 0])
+    assert_close(got[[0, 2]], ref[[0, 2]], "moe clamped")
+
+
+def test_moe_no_pairs_is_a_no_op():
+    fmt, n, k = NV, 256, 512
+    _, pc, ps, gs = _stacked(2, n, k, fmt, 11)
+    y = fp4.fp4_w4a16_moe_decode(x_dev(synth.activations(synth.TINY, 1, k)), pc, ps, n, 2, gs, fmt,
+                                 _i32([0, 0, 0]), torch.empty(0, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert y.shape == (0, n)
