@@ -50,6 +50,8 @@ from .reference import (
     linear_f64_bruteforce,
     greedy_argmax,
     moe_decode,
+    silu,
+    gate_up_swiglu,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
 )
@@ -59,6 +61,6 @@ __all__ = [
     "e2m1_value", "e4m3fn_value", "e8m0_value", "e2m1_encode", "e4m3fn_encode",
     "quantize_nvfp4", "quantize_mxfp4",
     "FMT_NVFP4", "FMT_MXFP4", "GROUP",
-    "unpack_codes", "dequantize", "linear", "linear_rows", "gate_up", "greedy_argmax", "moe_decode",
+    "unpack_codes", "dequantize", "linear", "linear_rows", "gate_up", "greedy_argmax", "moe_decode", "silu", "gate_up_swiglu",
     "linear_f64_bruteforce", "bf16_bits_to_f32", "f32_to_bf16_bits",
 ]

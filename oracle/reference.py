@@ -170,3 +170,24 @@ def moe_decode(x, experts, k, fmt, expert_offsets, pair_tokens):
         for p in range(offsets[e], offsets[e + 1]):
             y[p] = linear(x[tokens[p]:tokens[p] + 1], packed, scales, k, fmt, g)[0]
     return y
+
+
+def silu(v):
+    """silu(v) = v / (1 + e^-v) = v * sigmoid(v), float64."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def gate_up_swiglu(x, packed_gate, scales_gate, packed_up, scales_up, k, fmt, global_gate=1.0, global_up=1.0):
+    """The MLP step after the fused gate_up: silu(x W_gate^T) * (x W_up^T), with
+    each product the layer's exact result (float64 sums).
+
+    Reading taken: the pages feed the fused gate_up into the MLP of the model
+    family they run ("MXFP4 decode-graph + gate_up FUSION default-ON",
+    vllm.cpp PR #54, step 2) without naming its activation; the gated silu
+    MLP of that family is used.
+    """
+    g = linear(x, packed_gate, scales_gate, k, fmt, global_gate)
+    u = linear(x, packed_up, scales_up, k, fmt, global_up)
+    return silu(g) * u
