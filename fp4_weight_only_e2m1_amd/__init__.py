@@ -54,6 +54,10 @@ _SIGNATURES = {
     "fp4_argmax_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fp4_w4a16_linear_argmax": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _i, _vp, _vp, _vp, _vp, _sz, _vp,
                                      ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_prepare_gate_up_interleaved": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
+    "fp4_swiglu_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "fp4_w4a16_gate_up_swiglu": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _f, _i, _vp, _vp, _sz, _vp,
+                                      ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_moe_workspace_bytes": (_i, [_i, _i, ctypes.POINTER(_sz)]),
     "fp4_w4a16_moe_decode": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _sz, _vp,
                                   ctypes.POINTER(fp4_dispatch_info)]),
@@ -260,6 +264,55 @@ def fp4_w4a16_linear_argmax(x, prep_codes, prep_scales, n, global_scale, fmt, lo
         _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n, float(global_scale), fmt, _ptr(y), _ptr(idx),
         _ptr(val), _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
     return idx, val, y
+
+
+def fp4_prepare_gate_up_interleaved(gate_codes, gate_scales, up_codes, up_scales, n_half, k, fmt,
+                                    prep_codes=None, prep_scales=None, stream=None):
+    """Prepare a gate_up weight for fp4_w4a16_gate_up_swiglu (gate and up rows interleaved by 16)."""
+    for t, nm in ((gate_codes, "gate_codes"), (gate_scales, "gate_scales"), (up_codes, "up_codes"),
+                  (up_scales, "up_scales")):
+        _need(t, torch.uint8, nm)
+    if gate_codes.numel() != n_half * (k // 2) or up_codes.numel() != n_half * (k // 2):
+        raise ValueError("gate / up codes do not have the canonical [n_half, k/2] size")
+    if gate_scales.numel() != n_half * (k // GROUP[fmt]) or up_scales.numel() != n_half * (k // GROUP[fmt]):
+        raise ValueError("gate / up scales do not have the canonical [n_half, k/g] size")
+    cb, sb = fp4_prepared_bytes(n_half, k, fmt)
+    if prep_codes is None:
+        prep_codes = torch.empty(2 * cb, dtype=torch.uint8, device=gate_codes.device)
+    if prep_scales is None:
+        prep_scales = torch.empty(2 * sb, dtype=torch.uint8, device=gate_codes.device)
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    if prep_codes.numel() < 2 * cb or prep_scales.numel() < 2 * sb:
+        raise ValueError("prepared buffers too small")
+    _check("fp4_prepare_gate_up_interleaved", load_library().fp4_prepare_gate_up_interleaved(
+        _ptr(gate_codes), _ptr(gate_scales), _ptr(up_codes), _ptr(up_scales), n_half, k, fmt,
+        _ptr(prep_codes), _ptr(prep_scales), _stream(stream)))
+    return prep_codes, prep_scales
+
+
+def fp4_swiglu_workspace_bytes(m, n_half, k, fmt):
+    out = _sz()
+    _check("fp4_swiglu_workspace_bytes", load_library().fp4_swiglu_workspace_bytes(m, n_half, k, fmt,
+                                                                                   ctypes.byref(out)))
+    return out.value
+
+
+def fp4_w4a16_gate_up_swiglu(x, prep_codes, prep_scales, n_half, global_gate, global_up, fmt, y=None,
+                             workspace=None, stream=None, info=None):
+    """y bf16 [m, n_half] = silu(x @ gate.T) * (x @ up.T) over an interleaved prepared gate_up weight."""
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    k = x.shape[1]
+    cb, sb = fp4_prepared_bytes(n_half, k, fmt)
+    if prep_codes.numel() < 2 * cb or prep_scales.numel() < 2 * sb:
+        raise ValueError("prepared buffers smaller than twice fp4_prepared_bytes(n_half, k, fmt)")
+    m, y, workspace, ws_bytes = _linear_common(x, n_half, workspace, fp4_swiglu_workspace_bytes(x.shape[0], n_half,
+                                                                                              k, fmt), y)
+    _check("fp4_w4a16_gate_up_swiglu", load_library().fp4_w4a16_gate_up_swiglu(
+        _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n_half, float(global_gate), float(global_up), fmt,
+        _ptr(y), _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
+    return y
 
 
 def fp4_moe_workspace_bytes(pairs, k):

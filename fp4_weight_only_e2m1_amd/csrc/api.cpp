@@ -69,11 +69,30 @@ size_t argmax_workspace_for(int m, int n, int k, int fmt, size_t* keys_offset) {
   return base + static_cast<size_t>(rows_total / decode_tile_rows(m, rows_total)) * m * 8;
 }
 
-// Shared body of fp4_w4a16_linear, fp4_w4a16_gate_up and
-// fp4_w4a16_linear_argmax (idx non-null: greedy argmax, y optional).
+// Tile plan of a SwiGLU gate_up call at m > 8: every tile runs as a one-split
+// "tail" unit, so its float32 results reach the reduce launch, which pairs
+// gate and up rows and applies the activation.
+fp4::GemmPlan act_gemm_plan(int m, int64_t rows_total, int k) {
+  fp4::GemmPlan p = fp4::gemm_plan(m, rows_total, k);
+  p.dp_tiles = 0;
+  p.tail_tiles = p.tiles;
+  p.splits = 1;
+  return p;
+}
+
+size_t act_workspace_for(int m, int n_half, int k, int fmt) {
+  if (m <= fp4::kGemvMaxM) return workspace_for(m, n_half, k, fmt, 2);
+  const int64_t rows_total = 2 * fp4::round_up(n_half, fp4::kRowAlign);
+  return static_cast<size_t>(fp4::gemm_workspace_bytes(act_gemm_plan(m, rows_total, k)));
+}
+
+// Shared body of fp4_w4a16_linear, fp4_w4a16_gate_up, fp4_w4a16_linear_argmax
+// (idx non-null: greedy argmax, y optional) and fp4_w4a16_gate_up_swiglu
+// (act: interleaved gate_up weight, y = silu(gate) * up of n_proj columns).
 int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_t* scales, int n_proj,
                int projections, const float* gscales, int fmt, uint16_t* y, void* ws, size_t ws_bytes,
-               hipStream_t stream, fp4_dispatch_info* info, int32_t* idx = nullptr, uint16_t* val = nullptr) {
+               hipStream_t stream, fp4_dispatch_info* info, int32_t* idx = nullptr, uint16_t* val = nullptr,
+               int act = 0) {
   int st = check_fmt(fmt);
   if (st) return st;
   if ((st = check_nk(n_proj, k))) return st;
@@ -91,6 +110,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     return FP4_EALIGN;
   size_t keys_offset = 0;
   const size_t need = argmax ? argmax_workspace_for(m, n_proj, k, fmt, &keys_offset)
+                      : act  ? act_workspace_for(m, n_proj, k, fmt)
                              : workspace_for(m, n_proj, k, fmt, projections);
   if (need > 0) {
     if (ws_bytes < need) return FP4_EWORKSPACE;
@@ -120,9 +140,10 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.n_proj_pad = ps.n_pad;
     a.projections = projections;
     a.rows_total = ps.n_pad * projections;
-    a.ldy = static_cast<int64_t>(n_proj) * projections;
+    a.ldy = act ? n_proj : static_cast<int64_t>(n_proj) * projections;
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
+    a.act = act;
     a.tile_rows = decode_tile_rows(m, a.rows_total);
     if (on_mfma && a.tile_rows != fp4::kDecodeTileRows && a.splits != 1) return FP4_EINVAL;
     if (a.splits > 1) {
@@ -155,10 +176,11 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.n_proj_pad = ps.n_pad;
     a.projections = projections;
     a.rows_total = ps.n_pad * projections;
-    a.ldy = static_cast<int64_t>(n_proj) * projections;
+    a.ldy = act ? n_proj : static_cast<int64_t>(n_proj) * projections;
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
-    a.plan = fp4::gemm_plan(m, a.rows_total, k);
+    a.act = act;
+    a.plan = act ? act_gemm_plan(m, a.rows_total, k) : fp4::gemm_plan(m, a.rows_total, k);
     if (a.plan.tail_tiles > 0) a.partial = static_cast<float*>(ws);
     hipError_t e = fp4::launch_mfma(a, fmt, stream, &grid, &block);
     if (e != hipSuccess) return FP4_EHIP;
@@ -241,6 +263,41 @@ int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_c
   const float g[2] = {global_gate, global_up};
   return run_linear(x_dev, m, k, prep_codes_dev, prep_scales_dev, n_half, 2, g, fmt, y_dev, workspace_dev,
                     workspace_bytes, stream, info_out);
+}
+
+int fp4_prepare_gate_up_interleaved(const uint8_t* gate_codes_dev, const uint8_t* gate_scales_dev,
+                                    const uint8_t* up_codes_dev, const uint8_t* up_scales_dev, int n_half, int k,
+                                    int fmt, uint8_t* prep_codes_dev, uint8_t* prep_scales_dev, hipStream_t stream) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n_half, k))) return st;
+  if (static_cast<int64_t>(n_half) * 2 > FP4_MAX_N) return FP4_EINVAL;
+  if (!gate_codes_dev || !gate_scales_dev || !up_codes_dev || !up_scales_dev || !prep_codes_dev || !prep_scales_dev)
+    return FP4_EINVAL;
+  if (!aligned16(gate_codes_dev) || !aligned16(gate_scales_dev) || !aligned16(up_codes_dev) ||
+      !aligned16(up_scales_dev) || !aligned16(prep_codes_dev) || !aligned16(prep_scales_dev))
+    return FP4_EALIGN;
+  return to_status(fp4::launch_prepare_interleaved(gate_codes_dev, gate_scales_dev, up_codes_dev, up_scales_dev,
+                                                   n_half, k, fmt, prep_codes_dev, prep_scales_dev, stream));
+}
+
+int fp4_swiglu_workspace_bytes(int m, int n_half, int k, int fmt, size_t* bytes_out) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n_half, k))) return st;
+  if ((st = check_m(m))) return st;
+  if (static_cast<int64_t>(n_half) * 2 > FP4_MAX_N || !bytes_out) return FP4_EINVAL;
+  *bytes_out = m == 0 ? 0 : act_workspace_for(m, n_half, k, fmt);
+  return FP4_OK;
+}
+
+int fp4_w4a16_gate_up_swiglu(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                             const uint8_t* prep_scales_dev, int n_half, float global_gate, float global_up, int fmt,
+                             uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
+                             fp4_dispatch_info* info_out) {
+  const float g[2] = {global_gate, global_up};
+  return run_linear(x_dev, m, k, prep_codes_dev, prep_scales_dev, n_half, 2, g, fmt, y_dev, workspace_dev,
+                    workspace_bytes, stream, info_out, nullptr, nullptr, 1);
 }
 
 int fp4_argmax_workspace_bytes(int m, int n, int k, int fmt, size_t* bytes_out) {

@@ -122,6 +122,36 @@ __device__ __forceinline__ void tile_argmax_end(TileArgmax& ta, ArgmaxLocal<M>& 
   if (threadIdx.x < M) keys[tile * M + threadIdx.x] = ta.best[threadIdx.x];
 }
 
+// SwiGLU epilogue of a fused gate_up call on the interleaved weight (prepared
+// row R: gate row 16 (R / 32) + R % 16 if R % 32 < 16, else the up row with
+// that index).  A tile's float32 results (global scale applied) go to LDS;
+// then y[m][j] = bf16(silu(gate[m][j]) * up[m][j]), silu(v) = v / (1 + e^-v)
+// (hardware exp and reciprocal, about 1 ulp each), with one rounding to bf16.  Tiles hold whole 32-row blocks, so both operands of an
+// output are in the same workgroup.
+__device__ __forceinline__ int il_proj(int64_t row) { return static_cast<int>((row >> 4) & 1); }
+__device__ __forceinline__ int64_t il_col(int64_t row) { return (row >> 5) * 16 + (row & 15); }
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
+
+template <int M>
+struct ActTile {
+  float v[M][128];  // [activation row][row within the tile], up to 128-row tiles
+};
+// y for the tile of `tile_rows` rows starting at prepared row row0, after
+// every thread has stored its results; all threads must call it.
+template <int M>
+__device__ __forceinline__ void act_store(ActTile<M>& at, const GemvArgs& a, int64_t row0, int tile_rows, int mrows) {
+  __syncthreads();
+  const int pairs = tile_rows / 2;
+  for (int i = threadIdx.x; i < M * pairs; i += blockDim.x) {
+    const int m = i / pairs;
+    const int p = i - m * pairs;
+    const int gl = 32 * (p >> 4) + (p & 15);  // the gate row; its up row is gl + 16
+    const int64_t col = il_col(row0 + gl);
+    if (m < mrows && col < a.n_proj)
+      a.y[static_cast<int64_t>(m) * a.ldy + col] = f32_to_bf16_rne(silu(at.v[m][gl]) * at.v[m][gl + 16]);
+  }
+}
+
 // Split-K partial sums and arrival flags are exchanged between workgroups that
 // may sit on different XCDs, whose L2 caches are not coherent with each other.
 // They are therefore written and read with device-coherent (sc1) accesses --
@@ -180,6 +210,7 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
   for (int s = threadIdx.x; s < a.splits; s += kDecodeThreads)
     __hip_atomic_store(flags + s, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __shared__ TileArgmax ta;
+  __shared__ ActTile<M> at;
   ArgmaxLocal<M> al;
   if (a.keys) tile_argmax_begin(ta, al);
   // One buffer descriptor per split: partial[split] is [m][row], at most
@@ -189,8 +220,8 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
   for (int i = threadIdx.x; i < M * a.tile_rows; i += kDecodeThreads) {
     const int m = i / a.tile_rows;
     const int64_t row = tile * a.tile_rows + (i - m * a.tile_rows);
-    int h;
-    const int64_t col = out_col(a, row, h);
+    int h = 0;
+    const int64_t col = a.act ? 0 : out_col(a, row, h);
     if (col < 0) continue;
     const int off = static_cast<int>((static_cast<int64_t>(m) * a.rows_total + row) * 4);
     float s = 0.0f;
@@ -209,11 +240,16 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
       for (int b = 0; b < kBatch; ++b)
         if (s0 + b < a.splits) s = s0 + b == 0 ? v[b] : s + v[b];
     }
+    if (a.act) {
+      at.v[m][row - tile * a.tile_rows] = s * (il_proj(row) == 0 ? a.gscale[0] : a.gscale[1]);
+      continue;
+    }
     const uint16_t yb = f32_to_bf16_rne(s * (h == 0 ? a.gscale[0] : a.gscale[1]));
     if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
     if (a.keys) tile_argmax_offer(al, m, argmax_key(yb, col));
   }
   if (a.keys) tile_argmax_end(ta, al, a.keys, tile);
+  if (a.act) act_store(at, a, tile * a.tile_rows, a.tile_rows, M);
 }
 
 }  // namespace fp4

@@ -311,7 +311,20 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
     // 4g .. 4g + 3, so each row's maximum is taken over the 16 lanes of
     // group g (lane exchanges within the group), then across the waves.
     __shared__ TileArgmax ta;
+    __shared__ ActTile<M> at;
     uint64_t best[4] = {0, 0, 0, 0};
+    if (a.act) {
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int rl = 16 * (RB * wave + b) + r;
+        const float gs = il_proj(row0 + rl) == 0 ? a.gscale[0] : a.gscale[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * g + i < mrows) at.v[4 * g + i][rl] = acc[b][i] * gs;
+      }
+      act_store(at, a, row0, kRows, mrows);
+      return;
+    }
     if (a.keys) {
       if (t < kGemvMaxM) ta.best[t] = 0ull;
       __syncthreads();

@@ -126,6 +126,7 @@ struct GemvArgs {
   uint64_t* flags;        // [rows_total / tile_rows][splits] split-K arrival flags
   uint64_t token;         // unique per call; tags this call's flags
   uint64_t* keys;         // greedy argmax: [tiles][m] best key per tile, or null
+  int act;                // 1: interleaved gate_up weight, y = silu(gate) * up [m][n_proj]
   int m, k;
   int64_t k_pad;          // prepared row length in codes
   int64_t kgroups;        // prepared scale bytes per row
@@ -217,12 +218,16 @@ struct MfmaArgs {
   int64_t rows_total, ldy;
   float gscale[2];
   GemmPlan plan;
+  int act;                // 1: interleaved gate_up weight, y = silu(gate) * up [m][n_proj]
 };
 
 // Launchers (defined in the .hip files).  Each returns the hipError_t of its
 // launch; the grid/block it used is written to *grid / *block when non-null.
 hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,
                           uint8_t* prep_codes, uint8_t* prep_scales, hipStream_t stream);
+hipError_t launch_prepare_interleaved(const uint8_t* gate_codes, const uint8_t* gate_scales, const uint8_t* up_codes,
+                                      const uint8_t* up_scales, int n, int k, int fmt, uint8_t* prep_codes,
+                                      uint8_t* prep_scales, hipStream_t stream);
 hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, const uint16_t* x, const int32_t* tokens,

@@ -257,8 +257,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   Butterfly<VP, VP, 0>::run(v, lane, base, plain_mask);
 
   __shared__ TileArgmax ta;
+  __shared__ ActTile<M> at;
   ArgmaxLocal<M> al;
   const bool argmax_here = a.keys != nullptr && a.splits == 1;
+  const bool act_here = a.act != 0 && a.splits == 1;
   if (argmax_here) tile_argmax_begin(ta, al);
   if ((lane & plain_mask) == 0) {
 #pragma unroll
@@ -270,7 +272,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
         const int64_t row = row0 + r;
         const int h = static_cast<int>(row / a.n_proj_pad);
         const int64_t lr = row - static_cast<int64_t>(h) * a.n_proj_pad;
-        if (a.splits == 1) {
+        if (act_here) {
+          at.v[m][team * ROWS + r] = v[i] * (il_proj(row) == 0 ? a.gscale[0] : a.gscale[1]);
+        } else if (a.splits == 1) {
           if (lr < a.n_proj) {
             const int64_t col = static_cast<int64_t>(h) * a.n_proj + lr;
             const uint16_t yb = f32_to_bf16_rne(v[i] * a.gscale[h]);
@@ -284,6 +288,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
     }
   }
   if (argmax_here) tile_argmax_end(ta, al, a.keys, blockIdx.x);
+  if (act_here) act_store(at, a, static_cast<int64_t>(blockIdx.x) * (kGemvTeams * ROWS), kGemvTeams * ROWS, M);
   if (a.splits > 1) splitk_finish<M>(a, blockIdx.x, split);
 }
 

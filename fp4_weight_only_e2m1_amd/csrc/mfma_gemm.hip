@@ -336,6 +336,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // Buffer descriptor word 3 for raw (unformatted) 32-bit accesses.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// silu(v) = v / (1 + e^-v), for the SwiGLU epilogue of an interleaved gate_up weight.
+__device__ __forceinline__ float act_silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
+
 // Output column of prepared weight row `row`, or -1 for a padding row.
 __device__ __forceinline__ int64_t out_col(const MfmaArgs& a, int64_t row, int& h) {
   h = static_cast<int>(row / a.n_proj_pad);
@@ -514,6 +517,36 @@ __global__ __launch_bounds__(kReduceThreads) void tail_reduce_kernel(const MfmaA
   tile_coords(pl, pl.dp_tiles + tail_tile, m0, n0);
   const int64_t m = m0 + mr;
   if (m >= a.m) return;
+  if (a.act) {
+    // Interleaved gate_up (every tile runs as a "tail" unit, so all results
+    // come through here): items on gate rows also add their up rows (+16)
+    // and write y = silu(gate) * up.
+    if ((nr & 31) >= 16) return;
+    const int64_t grow = n0 + nr;
+    const int64_t col = (grow >> 5) * 16 + (grow & 15);
+    if (col >= a.n_proj) return;
+    const int64_t unit_floats = static_cast<int64_t>(kGemmBM) * kGemmBN;
+    const float* p = a.partial + static_cast<int64_t>(tail_tile) * pl.splits * unit_floats + mr * kGemmBN + nr;
+    f32x4_t gsum = *reinterpret_cast<const f32x4_t*>(p);
+    f32x4_t usum = *reinterpret_cast<const f32x4_t*>(p + 16);
+    for (int s = 1; s < pl.splits; ++s) {
+      gsum += *reinterpret_cast<const f32x4_t*>(p + s * unit_floats);
+      usum += *reinterpret_cast<const f32x4_t*>(p + s * unit_floats + 16);
+    }
+    const float w[4] = {act_silu(gsum.x * a.gscale[0]) * (usum.x * a.gscale[1]),
+                        act_silu(gsum.y * a.gscale[0]) * (usum.y * a.gscale[1]),
+                        act_silu(gsum.z * a.gscale[0]) * (usum.z * a.gscale[1]),
+                        act_silu(gsum.w * a.gscale[0]) * (usum.w * a.gscale[1])};
+    uint16_t* dst = a.y + m * a.ldy + col;
+    if (col + 4 <= a.n_proj && ((col | a.ldy) & 3) == 0) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(f32x2_to_bf16x2_rne(w[0], w[1]), f32x2_to_bf16x2_rne(w[2], w[3]));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (col + q < a.n_proj) dst[q] = f32_to_bf16_rne(w[q]);
+    }
+    return;
+  }
   int h;
   const int64_t col = out_col(a, n0 + nr, h);
   if (col < 0) return;

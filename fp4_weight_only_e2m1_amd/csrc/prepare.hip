@@ -106,7 +106,82 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   o[1] = make_float4(p[2].x, p[2].y, p[3].x, p[3].y);
 }
 
+// Interleaved gate_up layout: prepared row R holds gate row 16 (R / 32) +
+// R % 16 when R % 32 < 16, else the up row with that index, so each 32-row
+// block pairs 16 gate rows with the same 16 up rows.  Per-projection row
+// padding to n_pad as in the plain layout (2 n_pad prepared rows).
+__device__ __forceinline__ int64_t il_source_row(int64_t R, int& h) {
+  h = static_cast<int>((R >> 4) & 1);
+  return (R >> 5) * 16 + (R & 15);
+}
+
+__global__ __launch_bounds__(256) void prepare_codes_il_kernel(const uint8_t* __restrict__ gate,
+                                                               const uint8_t* __restrict__ up, int n, int k,
+                                                               int64_t n_pad, int64_t k_pad,
+                                                               uint8_t* __restrict__ out) {
+  const int64_t chunks_per_row = k_pad / 32;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= 2 * n_pad * chunks_per_row) return;
+  const int64_t R = i / chunks_per_row;
+  const int64_t c = i - R * chunks_per_row;
+  int h;
+  const int64_t row = il_source_row(R, h);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < n && c < k / 32) v = *reinterpret_cast<const uint4*>((h ? up : gate) + row * (k / 2) + c * 16);
+  *reinterpret_cast<uint4*>(out + R * (k_pad / 2) + c * 16) = v;
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void prepare_scales_il_kernel(const uint8_t* __restrict__ gate,
+                                                                const uint8_t* __restrict__ up, int n,
+                                                                int64_t kg_real, int64_t n_pad, int64_t ksegs,
+                                                                uint8_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= (2 * n_pad / kRowGroup) * ksegs) return;
+  const int64_t rg = i / ksegs;  // prepared 16-row group: all gate or all up rows
+  const int64_t seg = i - rg * ksegs;
+  const uint8_t* in = (rg & 1) ? up : gate;
+  const int64_t row0 = (rg >> 1) * kRowGroup;
+  uint32_t w[4 * P] = {};
+#pragma unroll
+  for (int r = 0; r < kRowGroup; ++r) {
+    const int64_t row = row0 + r;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int64_t kg = seg * P + j;
+      uint32_t b = 0;
+      if (row < n && kg < kg_real) b = in[row * kg_real + kg];
+      const int byte = r * P + j;
+      w[byte >> 2] |= b << (8 * (byte & 3));
+    }
+  }
+  uint4* o = reinterpret_cast<uint4*>(out + i * kRowGroup * P);
+#pragma unroll
+  for (int q = 0; q < P; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+}
+
 }  // namespace
+
+hipError_t launch_prepare_interleaved(const uint8_t* gate_codes, const uint8_t* gate_scales, const uint8_t* up_codes,
+                                      const uint8_t* up_scales, int n, int k, int fmt, uint8_t* prep_codes,
+                                      uint8_t* prep_scales, hipStream_t stream) {
+  const PreparedShape s = prepared_shape(n, k, fmt);
+  const int64_t code_chunks = 2 * s.n_pad * (s.k_pad / 32);
+  hipLaunchKernelGGL(prepare_codes_il_kernel, dim3(static_cast<unsigned>((code_chunks + 255) / 256)), dim3(256), 0,
+                     stream, gate_codes, up_codes, n, k, s.n_pad, s.k_pad, prep_codes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items = (2 * s.n_pad / kRowGroup) * s.ksegs;
+  const dim3 grid(static_cast<unsigned>((items + 255) / 256));
+  const int64_t kg_real = k / group_size(fmt);
+  if (fmt == kFmtNvfp4)
+    hipLaunchKernelGGL(prepare_scales_il_kernel<2>, grid, dim3(256), 0, stream, gate_scales, up_scales, n, kg_real,
+                       s.n_pad, s.ksegs, prep_scales);
+  else
+    hipLaunchKernelGGL(prepare_scales_il_kernel<1>, grid, dim3(256), 0, stream, gate_scales, up_scales, n, kg_real,
+                       s.n_pad, s.ksegs, prep_scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,
                           uint8_t* prep_codes, uint8_t* prep_scales, hipStream_t stream) {

@@ -167,6 +167,36 @@ int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k,
                       hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
+ * SwiGLU gate_up: y[m][j] = bf16(silu(g) * u), g = x * gate[j]^T * global_gate,
+ * u = x * up[j]^T * global_up (float32 sums, as fp4_w4a16_gate_up computes
+ * them before rounding), silu(v) = v / (1 + e^-v), one rounding to bf16;
+ * y_dev is bf16 [m][n_half].  The weight is prepared by
+ * fp4_prepare_gate_up_interleaved (same buffer sizes as fp4_prepare_gate_up:
+ * twice fp4_prepared_bytes(n_half, k, fmt)), which interleaves gate and up
+ * rows in groups of 16 (prepared row R: gate row 16 (R / 32) + R % 16 when
+ * R % 32 < 16, else the up row with that index) so that both operands of an
+ * output are computed by one workgroup.  m <= 8: the decode kernels form y in
+ * their epilogue; m > 8: the tile GEMM leaves every tile's float32 results in
+ * the workspace and its reduce launch forms y.  Workspace:
+ * fp4_swiglu_workspace_bytes (at m > 8, m x 2 n_half x 4 bytes, rounded to
+ * tiles).  silu uses the hardware exp and reciprocal (about 1 ulp each).
+ * Reading taken: the pages name the MLP block after the fused gate_up but not
+ * its activation; silu(gate) * up is the gated MLP of the model family they
+ * run ("MXFP4 decode-graph + gate_up FUSION default-ON", vllm.cpp PR #54,
+ * step 2: gate_up feeds the MLP of Qwen3-8B-MXFP4).
+ */
+int fp4_prepare_gate_up_interleaved(const uint8_t* gate_codes_dev, const uint8_t* gate_scales_dev,
+                                    const uint8_t* up_codes_dev, const uint8_t* up_scales_dev,
+                                    int n_half, int k, int fmt,
+                                    uint8_t* prep_codes_dev, uint8_t* prep_scales_dev, hipStream_t stream);
+int fp4_swiglu_workspace_bytes(int m, int n_half, int k, int fmt, size_t* bytes_out);
+int fp4_w4a16_gate_up_swiglu(const uint16_t* x_dev, int m, int k,
+                             const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n_half,
+                             float global_gate, float global_up, int fmt,
+                             uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes,
+                             hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
  * Greedy token of a decode call: idx_out_dev[i] (int32) = the index j of the
  * largest logit y[i][j] -- the bf16 value fp4_w4a16_linear gives for the same
  * arguments -- and the lowest such j when several are equal; -0 equals +0
