@@ -15,6 +15,7 @@ the 256 MB Infinity Cache cannot hold them, so the bytes come from HBM.
 
 Workloads (synthetic weights and activations at the pages' shapes):
   gate_up        MXFP4 fused gate_up, k=4096, n=2x12288          (default)
+  gate_up_swiglu the same weight interleaved, y = silu(gate) * up [m, 12288]
   lm_head        NVFP4 packed lm_head, k=5120, n=248320
   lm_head_argmax the same head with the fused greedy argmax (token ids out,
                  no logits)
@@ -67,6 +68,7 @@ ROTATE_BYTES = 1 << 30
 # name: (workload id, fmt, n per projection, k, projections, default m)
 WORKLOADS = {
     "gate_up": (1, 1, 12288, 4096, 2, 8),
+    "gate_up_swiglu": (1, 1, 12288, 4096, 2, 8),
     "lm_head": (2, 0, 248320, 5120, 1, 8),
     "lm_head_argmax": (2, 0, 248320, 5120, 1, 8),
     "moe_gate_up": (0, 0, 1536, 2048, 1, 8),
@@ -79,19 +81,23 @@ WORKLOADS = {
 TENSOR = {"o_proj": 1, "prefill_mxfp4": 1}
 # Workloads that run the greedy-argmax entry point (no logits written).
 ARGMAX = {"lm_head_argmax"}
+# Workloads that run the SwiGLU gate_up (interleaved weight, y = silu(gate) * up).
+SWIGLU = {"gate_up_swiglu"}
 # Grouped MoE decode: 128 experts, top-8 routing per token, each expert a
 # gate_up weight of 2 x 768 rows over k = 2048 (an A3B-class MoE block's
 # shape; synthetic).  8 distinct expert weights are repeated over the 128.
 MOE_EXPERTS, MOE_TOPK, MOE_DISTINCT = 128, 8, 8
 
 
-def algorithmic_bytes(fmt, n_proj, k, projections, m, argmax=False):
-    """Weights + scales + global scales + x + output: y (2 m n), or for the
-    greedy argmax the token id and winning logit per row (6 m)."""
+def algorithmic_bytes(fmt, n_proj, k, projections, m, argmax=False, swiglu=False):
+    """Weights + scales + global scales + x + output: y (2 m n), for the
+    greedy argmax the token id and winning logit per row (6 m), for the
+    SwiGLU gate_up y of one projection's width (2 m n_proj)."""
     g = 16 if fmt == 0 else 32
     n = n_proj * projections
     w = n * k // 2 + n * k // g + (4 * projections if fmt == 0 else 0)
-    return w + 2 * m * k + (6 * m if argmax else 2 * m * n)
+    out = 6 * m if argmax else 2 * m * (n_proj if swiglu else n)
+    return w + 2 * m * k + out
 
 
 def kernel_source_hash():
@@ -127,7 +133,8 @@ def make_inputs(name, m, torch, fp4, synth):
     if proj == 2:
         pg, sg, gg = synth.packed_weight(wid, 0, n, k, fmt)
         pu, su, gu = synth.packed_weight(wid, 1, n, k, fmt)
-        pc, ps = fp4.fp4_prepare_gate_up(upload(pg), upload(sg), upload(pu), upload(su), n, k, fmt)
+        prep = fp4.fp4_prepare_gate_up_interleaved if name in SWIGLU else fp4.fp4_prepare_gate_up
+        pc, ps = prep(upload(pg), upload(sg), upload(pu), upload(su), n, k, fmt)
         gs = (float(gg), float(gu))
         host = {"packed": (pg, pu), "scales": (sg, su), "g": (gg, gu)}
     else:
@@ -155,6 +162,10 @@ def cpu_baseline(name, xbs, host, budget_s):
 
     def one_step(sl):
         for _, x in xs:
+            if name in SWIGLU:
+                oracle.gate_up_swiglu(x, host["packed"][0][sl], host["scales"][0][sl], host["packed"][1][sl],
+                                      host["scales"][1][sl], k, fmt, host["g"][0], host["g"][1])
+                continue
             y = oracle.linear(x, packed[sl], scales[sl], k, fmt, g)
             if name in ARGMAX:
                 oracle.greedy_argmax(y)
@@ -175,12 +186,13 @@ def cpu_baseline(name, xbs, host, budget_s):
     for _ in range(reps):
         one_step(sl)
     dt = (time.perf_counter() - t0) / reps
-    frac = sl.stop / (n * proj)
+    frac = sl.stop / (n * proj) * (2 if name in SWIGLU else 1)  # SwiGLU: the slice of both projections
     if name.startswith("prefill"):
         value = sum(2.0 * m * sl.stop * k for m, _ in xs) / dt / 1e12
         unit = "TFLOP/s"
     else:
-        value = sum(algorithmic_bytes(fmt, n, k, proj, m, name in ARGMAX) for m, _ in xs) * frac / dt / 1e9
+        value = sum(algorithmic_bytes(fmt, n, k, proj, m, name in ARGMAX, name in SWIGLU)
+                    for m, _ in xs) * frac / dt / 1e9
         unit = "GB/s"
     # The same slice at m = 1 on one BLAS thread (a second, single-core figure).
     single = None
@@ -406,8 +418,10 @@ def main():
     for m in ms:
         xb = synth.activations(wid, m, k)
         x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
-        y = torch.empty((m, nout), dtype=torch.bfloat16, device=dev)
-        if name in ARGMAX:
+        y = torch.empty((m, n if name in SWIGLU else nout), dtype=torch.bfloat16, device=dev)
+        if name in SWIGLU:
+            ws_bytes = fp4.fp4_swiglu_workspace_bytes(m, n, k, fmt)
+        elif name in ARGMAX:
             ws_bytes = fp4.fp4_argmax_workspace_bytes(m, n, k, fmt)
         else:
             ws_bytes = fp4.fp4_workspace_bytes(m, n, k, fmt, proj)
@@ -418,7 +432,10 @@ def main():
 
     def call(d, i):
         c, s = weights[i % copies]
-        if proj == 2:
+        if name in SWIGLU:
+            fp4.fp4_w4a16_gate_up_swiglu(d["x"], c, s, n, gs[0], gs[1], fmt, y=d["y"], workspace=d["ws"],
+                                         info=d["info"])
+        elif proj == 2:
             fp4.fp4_w4a16_gate_up(d["x"], c, s, n, gs[0], gs[1], fmt, y=d["y"], workspace=d["ws"], info=d["info"])
         elif name in ARGMAX:
             fp4.fp4_w4a16_linear_argmax(d["x"], c, s, n, gs[0], fmt, idx=d["idx"], val=d["val"],
@@ -466,7 +483,7 @@ def main():
         ms_m = evs[j][0].elapsed_time(evs[j][1])
         d["t_ms"] = ms_m
         m = d["m"]
-        b = algorithmic_bytes(fmt, n, k, proj, m, name in ARGMAX)
+        b = algorithmic_bytes(fmt, n, k, proj, m, name in ARGMAX, name in SWIGLU)
         f = 2.0 * m * nout * k
         total_ms += ms_m
         total_bytes += b * args.steps
@@ -478,6 +495,8 @@ def main():
                  else "%s<%s>" % (kern, "nvfp4" if fmt == 0 else "mxfp4"))
         if name in ARGMAX:
             kname += " + argmax_reduce_kernel"
+        if name in SWIGLU:
+            kname += " swiglu" if info.kernel != 1 else " + tail_reduce_kernel swiglu"
         rows.append({"m": m, "kernel": kname,
                      "us_per_launch": round(us, 3), "gbs": round(b / (us * 1e-6) / 1e9, 2),
                      "tflops": round(f / (us * 1e-6) / 1e12, 3), "splits": info.splits,
@@ -494,7 +513,7 @@ def main():
         t1 = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), n1, args.launch == "graph")
         if args.steps > n1:
             rows[j]["us_per_launch_differenced"] = round((d["t_ms"] - t1) * 1e3 / (args.steps - n1), 3)
-        if proj == 2:
+        if proj == 2 and name not in SWIGLU:
             cb, sb = fp4.fp4_prepared_bytes(n, k, fmt)
             yg = torch.empty((d["m"], n), dtype=torch.bfloat16, device=dev)
             yu = torch.empty((d["m"], n), dtype=torch.bfloat16, device=dev)
