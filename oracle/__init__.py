@@ -52,6 +52,10 @@ from .reference import (
     moe_decode,
     silu,
     gate_up_swiglu,
+    e2m1_nearest_even,
+    quantize_act_mxfp4,
+    dequantize_act_mxfp4,
+    w4a4_linear,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
 )
@@ -62,5 +66,6 @@ __all__ = [
     "quantize_nvfp4", "quantize_mxfp4",
     "FMT_NVFP4", "FMT_MXFP4", "GROUP",
     "unpack_codes", "dequantize", "linear", "linear_rows", "gate_up", "greedy_argmax", "moe_decode", "silu", "gate_up_swiglu",
+    "e2m1_nearest_even", "quantize_act_mxfp4", "dequantize_act_mxfp4", "w4a4_linear",
     "linear_f64_bruteforce", "bf16_bits_to_f32", "f32_to_bf16_bits",
 ]

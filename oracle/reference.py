@@ -191,3 +191,87 @@ def gate_up_swiglu(x, packed_gate, scales_gate, packed_up, scales_up, k, fmt, gl
     g = linear(x, packed_gate, scales_gate, k, fmt, global_gate)
     u = linear(x, packed_up, scales_up, k, fmt, global_up)
     return silu(g) * u
+
+
+# --- W4A4 variant: MXFP4 activations against MXFP4 weights ------------------
+#
+# The pages describe a second numerics contract next to the weight-only one:
+# the compressed-tensors MXFP4 scheme with its activations also quantized
+# (W4A4), run by a GEMM that takes both operands as 4-bit codes with
+# block-32 E8M0 scales ("native MXFP4 keep-quant", vllm.cpp PR #38, commit
+# list: the W0 vehicle's scheme and the W1 kernel, block 32 with non-NVFP4
+# scales).  The pages keep it off the default path; here it is a separate,
+# opt-in entry point.
+#
+# Readings taken where the pages are silent (they name the scheme, not its
+# activation quantizer):
+# * Activations are quantized per row, per block of 32 consecutive k, at call
+#   time, by the OCP MX v1.0 conversion: shared scale X = 2^e with
+#   e = floor(log2(amax)) - 2 (2 = the largest exponent of E2M1), clamped to
+#   at least -127; amax = 0 gives e = -127.  Elements become E2M1(x / X):
+#   nearest magnitude, ties to the even code, saturating at 6; the sign bit
+#   follows the input, so a small negative value becomes code 0x8.
+# * A block holding an Inf or NaN gets scale byte 0xFF (E8M0 NaN) and codes 0.
+# * The product is the exact sum of (E2M1 * X)(x) * w over k, w the MXFP4
+#   weight as the weight-only oracle dequantizes it (float64 here).
+
+# E2M1 magnitudes by code 0..7 (sign-magnitude, increasing).
+_E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def e2m1_nearest_even(v):
+    """E2M1 codes of float64 values: nearest magnitude, ties to the even code,
+    saturating at 6, sign bit from the input's sign bit.  Vectorized form of
+    ``e2m1_encode`` (the two are checked against each other)."""
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.abs(v)
+    lo = np.clip(np.searchsorted(_E2M1_MAGS, mag, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    d_lo = mag - _E2M1_MAGS[lo]
+    d_hi = _E2M1_MAGS[hi] - mag
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 3)
+
+
+def quantize_act_mxfp4(x):
+    """Dynamic MXFP4 quantization of activation rows.
+
+    x: float32 [M, K] holding bf16 values, K a multiple of 32.  Returns
+    (codes uint8 [M, K], one E2M1 code per element; scales uint8 [M, K/32],
+    E8M0 bytes), block by block as the readings above state.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    codes = np.zeros((m, k), dtype=np.uint8)
+    scales = np.zeros((m, k // 32), dtype=np.uint8)
+    for b in range(k // 32):
+        blk = x[:, 32 * b:32 * b + 32].astype(np.float64)
+        finite = np.all(np.isfinite(blk), axis=1)
+        amax = np.max(np.abs(np.where(np.isfinite(blk), blk, 0.0)), axis=1)
+        _, ex = np.frexp(amax)                        # amax = f 2^ex, f in [0.5, 1)
+        e = np.where(amax > 0, ex - 1 - 2, -127)      # floor(log2 amax) - 2
+        e = np.maximum(e, -127)
+        scales[:, b] = np.where(finite, e + 127, 0xFF).astype(np.uint8)
+        v = np.ldexp(blk, -e[:, None])                # exact: a power-of-two scaling
+        c = e2m1_nearest_even(np.where(finite[:, None], v, 0.0))
+        codes[:, 32 * b:32 * b + 32] = np.where(finite[:, None], c, 0)
+    return codes, scales
+
+
+def dequantize_act_mxfp4(codes, scales):
+    """float64 [M, K]: E2M1(code) * 2^(scale byte - 127); NaN where the byte is 0xFF."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    sv = E8M0_TABLE[np.asarray(scales, dtype=np.uint8)].astype(np.float64)
+    return E2M1_TABLE[codes].astype(np.float64) * np.repeat(sv, 32, axis=1)
+
+
+def w4a4_linear(x, packed, scales, k):
+    """W4A4 MXFP4 product: y = Q(x) @ w.T in float64, Q = ``quantize_act_mxfp4``
+    and w the MXFP4 weight [N, K] (``dequantize``, group 32, no global scale)."""
+    xc, xs = quantize_act_mxfp4(x)
+    xq = dequantize_act_mxfp4(xc, xs)
+    w = dequantize(packed, scales, k, FMT_MXFP4).astype(np.float64)
+    return xq @ w.T
