@@ -61,6 +61,11 @@ _SIGNATURES = {
     "fp4_moe_workspace_bytes": (_i, [_i, _i, ctypes.POINTER(_sz)]),
     "fp4_w4a16_moe_decode": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _sz, _vp,
                                   ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_w4a4_act_bytes": (_i, [_i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "fp4_quantize_act_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "fp4_w4a4_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "fp4_w4a4_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp, ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_w4a4_gate_up": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp, ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_dequantize": (_i, [_vp, _vp, _i, _i, _f, _i, _vp, _vp]),
     "fp4_status_string": (ctypes.c_char_p, [_i]),
 }
@@ -358,6 +363,73 @@ def fp4_w4a16_moe_decode(x, prep_codes, prep_scales, n, experts, global_scales, 
         None if info is None else ctypes.byref(info)))
     return y
 
+
+
+def fp4_w4a4_act_bytes(m, k):
+    """(code_bytes, scale_bytes) of the quantized activations of m rows of k values (W4A4 variant)."""
+    cb, sb = _sz(), _sz()
+    _check("fp4_w4a4_act_bytes", load_library().fp4_w4a4_act_bytes(m, k, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def fp4_quantize_act_mxfp4(x, codes=None, scales=None, stream=None):
+    """MXFP4 quantization of bf16 x [m, k] as the W4A4 variant does it; returns (codes, scales)
+    uint8 buffers in the documented layout (rows padded to 128, k to 128)."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m, k]")
+    m, k = x.shape
+    cb, sb = fp4_w4a4_act_bytes(m, k)
+    if codes is None:
+        codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if codes.numel() < cb or scales.numel() < sb:
+        raise ValueError("buffers smaller than fp4_w4a4_act_bytes(m, k)")
+    _check("fp4_quantize_act_mxfp4", load_library().fp4_quantize_act_mxfp4(
+        _ptr(x), m, k, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def fp4_w4a4_workspace_bytes(m, n, k, projections=1):
+    out = _sz()
+    _check("fp4_w4a4_workspace_bytes", load_library().fp4_w4a4_workspace_bytes(m, n, k, projections,
+                                                                                ctypes.byref(out)))
+    return out.value
+
+
+def fp4_w4a4_linear(x, prep_codes, prep_scales, n, fmt=FMT_MXFP4, y=None, workspace=None, stream=None, info=None):
+    """W4A4 variant: y = Q(x) @ w.T, Q the MXFP4 activation quantization, w a prepared MXFP4 weight."""
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    k = x.shape[1]
+    cb, sb = fp4_prepared_bytes(n, k, FMT_MXFP4)
+    if prep_codes.numel() < cb or prep_scales.numel() < sb:
+        raise ValueError("prepared buffers smaller than fp4_prepared_bytes(n, k, FMT_MXFP4)")
+    m, y, workspace, ws_bytes = _linear_common(x, n, workspace, fp4_w4a4_workspace_bytes(x.shape[0], n, k, 1), y)
+    _check("fp4_w4a4_linear", load_library().fp4_w4a4_linear(
+        _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n, fmt, _ptr(y), _ptr(workspace), ws_bytes,
+        _stream(stream), None if info is None else ctypes.byref(info)))
+    return y
+
+
+def fp4_w4a4_gate_up(x, prep_codes, prep_scales, n_half, fmt=FMT_MXFP4, y=None, workspace=None, stream=None,
+                     info=None):
+    """W4A4 variant of the fused gate_up: returns bf16 [m, 2*n_half] = [Q(x) @ gate.T | Q(x) @ up.T]."""
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    k = x.shape[1]
+    cb, sb = fp4_prepared_bytes(n_half, k, FMT_MXFP4)
+    if prep_codes.numel() < 2 * cb or prep_scales.numel() < 2 * sb:
+        raise ValueError("prepared buffers smaller than twice fp4_prepared_bytes(n_half, k, FMT_MXFP4)")
+    m, y, workspace, ws_bytes = _linear_common(
+        x, 2 * n_half, workspace, fp4_w4a4_workspace_bytes(x.shape[0], n_half, k, 2), y)
+    _check("fp4_w4a4_gate_up", load_library().fp4_w4a4_gate_up(
+        _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n_half, fmt, _ptr(y), _ptr(workspace), ws_bytes,
+        _stream(stream), None if info is None else ctypes.byref(info)))
+    return y
 
 def fp4_dequantize(prep_codes, prep_scales, n, k, global_scale, fmt, out=None, stream=None):
     """Dequantize a prepared weight to float32 [n, k] with the kernels' decoders."""

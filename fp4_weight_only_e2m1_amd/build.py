@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4w4a16.so")
-SOURCES = ["api.cpp", "prepare.hip", "gemv.hip", "decode_mfma.hip", "mfma_gemm.hip", "argmax.hip"]
+SOURCES = ["api.cpp", "prepare.hip", "gemv.hip", "decode_mfma.hip", "mfma_gemm.hip", "argmax.hip", "w4a4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

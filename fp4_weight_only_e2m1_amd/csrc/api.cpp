@@ -190,6 +190,65 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
   return FP4_OK;
 }
 
+// Workspace of a W4A4 call: the quantized activations (codes, then scales),
+// then, 256-byte aligned, the tile GEMM's tail partials.
+size_t w4a4_workspace_for(int m, int n_proj, int k, int projections, size_t* partial_offset) {
+  if (m < 1) return 0;
+  const int64_t act = fp4::round_up(fp4::w4a4_act_code_bytes(m, k) + fp4::w4a4_act_scale_bytes(m, k), 256);
+  const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
+  if (partial_offset) *partial_offset = static_cast<size_t>(act);
+  return static_cast<size_t>(act + fp4::gemm_workspace_bytes(fp4::w4a4_plan(m, rows_total, k)));
+}
+
+// Shared body of fp4_w4a4_linear and fp4_w4a4_gate_up.
+int run_w4a4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_t* scales, int n_proj, int projections,
+             int fmt, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream, fp4_dispatch_info* info) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if (fmt != FP4_FMT_MXFP4) return FP4_EFMT;  // the block-scaled MFMA takes E8M0 block-32 scales only
+  if ((st = check_nk(n_proj, k))) return st;
+  if ((st = check_m(m))) return st;
+  if (static_cast<int64_t>(n_proj) * projections > FP4_MAX_N) return FP4_EINVAL;
+  if (m == 0) {
+    if (info) *info = fp4_dispatch_info{4, 0, 0, 0, 0};
+    return FP4_OK;
+  }
+  if (!x || !codes || !scales || !y || !ws) return FP4_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y) || !aligned16(ws)) return FP4_EALIGN;
+  size_t partial_offset = 0;
+  if (ws_bytes < w4a4_workspace_for(m, n_proj, k, projections, &partial_offset)) return FP4_EWORKSPACE;
+
+  const fp4::PreparedShape ps = fp4::prepared_shape(n_proj, k, fmt);
+  uint8_t* xq_codes = static_cast<uint8_t*>(ws);
+  uint8_t* xq_scales = xq_codes + fp4::w4a4_act_code_bytes(m, k);
+  if (fp4::launch_act_quant_mxfp4(x, m, k, xq_codes, xq_scales, stream) != hipSuccess) return FP4_EHIP;
+  fp4::MfmaArgs a{};
+  a.codes = codes;
+  a.scales = scales;
+  a.y = y;
+  a.m = m;
+  a.k = k;
+  a.k_pad = ps.k_pad;
+  a.kgroups = ps.kgroups;
+  a.ksegs = ps.ksegs;
+  a.n_proj = n_proj;
+  a.n_proj_pad = ps.n_pad;
+  a.projections = projections;
+  a.rows_total = ps.n_pad * projections;
+  a.ldy = static_cast<int64_t>(n_proj) * projections;
+  a.gscale[0] = a.gscale[1] = 1.0f;
+  a.plan = fp4::w4a4_plan(m, a.rows_total, k);
+  if (a.plan.tail_tiles > 0) a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + partial_offset);
+  a.xq_codes = xq_codes;
+  a.xq_scales = xq_scales;
+  a.act_k = fp4::w4a4_act_k(k);
+  dim3 grid, block;
+  if (fp4::launch_w4a4(a, stream, &grid, &block) != hipSuccess) return FP4_EHIP;
+  if (info) *info = fp4_dispatch_info{4, a.plan.splits, static_cast<int>(grid.x), static_cast<int>(grid.y),
+                                      static_cast<int>(block.x)};
+  return FP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -386,6 +445,47 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t
   if (info_out) *info_out = fp4_dispatch_info{3, 1, static_cast<int>(grid.x), static_cast<int>(grid.y),
                                               static_cast<int>(block.x)};
   return FP4_OK;
+}
+
+int fp4_w4a4_act_bytes(int m, int k, size_t* code_bytes_out, size_t* scale_bytes_out) {
+  if (m < 0 || m > FP4_MAX_M || k < 32 || k > FP4_MAX_K || k % 32 != 0 || !code_bytes_out || !scale_bytes_out)
+    return FP4_EINVAL;
+  *code_bytes_out = m == 0 ? 0 : static_cast<size_t>(fp4::w4a4_act_code_bytes(m, k));
+  *scale_bytes_out = m == 0 ? 0 : static_cast<size_t>(fp4::w4a4_act_scale_bytes(m, k));
+  return FP4_OK;
+}
+
+int fp4_quantize_act_mxfp4(const uint16_t* x_dev, int m, int k, uint8_t* codes_dev, uint8_t* scales_dev,
+                           hipStream_t stream) {
+  if (m < 0 || m > FP4_MAX_M || k < 32 || k > FP4_MAX_K || k % 32 != 0) return FP4_EINVAL;
+  if (m == 0) return FP4_OK;
+  if (!x_dev || !codes_dev || !scales_dev) return FP4_EINVAL;
+  if (!aligned16(x_dev) || !aligned16(codes_dev) || !aligned16(scales_dev)) return FP4_EALIGN;
+  return to_status(fp4::launch_act_quant_mxfp4(x_dev, m, k, codes_dev, scales_dev, stream));
+}
+
+int fp4_w4a4_workspace_bytes(int m, int n, int k, int projections, size_t* bytes_out) {
+  int st = check_nk(n, k);
+  if (st) return st;
+  if ((st = check_m(m))) return st;
+  if (projections != 1 && projections != 2) return FP4_EINVAL;
+  if (static_cast<int64_t>(n) * projections > FP4_MAX_N || !bytes_out) return FP4_EINVAL;
+  *bytes_out = w4a4_workspace_for(m, n, k, projections, nullptr);
+  return FP4_OK;
+}
+
+int fp4_w4a4_linear(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev,
+                    int n, int fmt, uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
+                    fp4_dispatch_info* info_out) {
+  return run_w4a4(x_dev, m, k, prep_codes_dev, prep_scales_dev, n, 1, fmt, y_dev, workspace_dev, workspace_bytes,
+                  stream, info_out);
+}
+
+int fp4_w4a4_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                     const uint8_t* prep_scales_dev, int n_half, int fmt, uint16_t* y_dev, void* workspace_dev,
+                     size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out) {
+  return run_w4a4(x_dev, m, k, prep_codes_dev, prep_scales_dev, n_half, 2, fmt, y_dev, workspace_dev, workspace_bytes,
+                  stream, info_out);
 }
 
 int fp4_dequantize(const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int k, float global_scale,

@@ -177,15 +177,16 @@ struct GemmPlan {
   int ksteps;      // K steps of a whole tile
 };
 
-inline GemmPlan gemm_plan(int m, int64_t rows_total, int k) {
+// Plan over K steps of `step_k` codes, splits of at least `min_split_steps`.
+inline GemmPlan tile_plan(int m, int64_t rows_total, int k, int step_k, int min_split_steps) {
   GemmPlan p;
   p.m_tiles = static_cast<int>((m + kGemmBM - 1) / kGemmBM);
   p.n_tiles = static_cast<int>(rows_total / kGemmBN);
   p.tiles = p.m_tiles * p.n_tiles;
-  p.ksteps = static_cast<int>((k + kGemmBK - 1) / kGemmBK);
+  p.ksteps = static_cast<int>((k + step_k - 1) / step_k);
   const int tail = p.tiles % kGemmSlots;
   int s = tail > 0 ? kGemmSlots / tail : 1;
-  const int by_k = p.ksteps / kGemmMinSplitSteps;
+  const int by_k = p.ksteps / min_split_steps;
   if (s > by_k) s = by_k;
   if (s <= 1) {
     p.dp_tiles = p.tiles;
@@ -198,6 +199,30 @@ inline GemmPlan gemm_plan(int m, int64_t rows_total, int k) {
   }
   return p;
 }
+
+inline GemmPlan gemm_plan(int m, int64_t rows_total, int k) {
+  return tile_plan(m, rows_total, k, kGemmBK, kGemmMinSplitSteps);
+}
+
+// W4A4 tile GEMM (MXFP4 activations x MXFP4 weights on the block-scaled
+// MFMA): the same 128 x 256 tiles and tile plan, K stepping 128 codes per
+// stage, tail splits of at least 4 stages (512 codes, as for the W4A16 GEMM).
+constexpr int kW4BK = 128;
+constexpr int kW4MinSplitSteps = 4;
+
+inline GemmPlan w4a4_plan(int m, int64_t rows_total, int k) {
+  return tile_plan(m, rows_total, k, kW4BK, kW4MinSplitSteps);
+}
+
+// The quantized activations of a W4A4 call: codes [act_rows][act_k / 2]
+// (two codes per byte, low nibble first) and E8M0 scales in the prepared
+// weight's row-group layout [act_rows / 16][act_k / 32][16].  act_rows covers
+// whole 128-row tiles; rows from m on are never written (their results are
+// never stored), codes and scales from k to act_k are zero.
+inline int64_t w4a4_act_k(int k) { return round_up(k, kW4BK); }
+inline int64_t w4a4_act_rows(int m) { return round_up(m, kGemmBM); }
+inline int64_t w4a4_act_code_bytes(int m, int k) { return w4a4_act_rows(m) * w4a4_act_k(k) / 2; }
+inline int64_t w4a4_act_scale_bytes(int m, int k) { return w4a4_act_rows(m) * w4a4_act_k(k) / 32; }
 
 // Workspace of a prefill call: fp32 partial tiles [tail_tiles][splits][BM][BN].
 inline int64_t gemm_workspace_bytes(const GemmPlan& p) {
@@ -219,6 +244,10 @@ struct MfmaArgs {
   float gscale[2];
   GemmPlan plan;
   int act;                // 1: interleaved gate_up weight, y = silu(gate) * up [m][n_proj]
+  // W4A4 only: the quantized activations (w4a4_act_* layout), act_k codes per row.
+  const uint8_t* xq_codes;
+  const uint8_t* xq_scales;
+  int64_t act_k;
 };
 
 // Launchers (defined in the .hip files).  Each returns the hipError_t of its
@@ -234,6 +263,10 @@ hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts,
                              int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid,
                              dim3* block);
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
+hipError_t launch_tail_reduce(const MfmaArgs& a, hipStream_t stream);
+hipError_t launch_act_quant_mxfp4(const uint16_t* x, int m, int k, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t stream);
+hipError_t launch_w4a4(const MfmaArgs& a, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_argmax_reduce(const uint64_t* keys, int tiles, int m, int32_t* idx, uint16_t* val,
                                 hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,

@@ -34,18 +34,17 @@
 // 16-byte read.
 #include "fp4_common.hpp"
 #include "fp4_device.hpp"
+#include "gemm_common.hpp"
 #include "lds_copy.hpp"
 
 namespace fp4 {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = kGemmWavesM * 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 3;
-constexpr int kGroupM = 8;  // activation-row tiles per tile-order group
 constexpr int kAChunks = kGemmBM * kGemmBK * 2 / 16;  // 16-byte chunks of an x stage
 constexpr int kBChunks = kGemmBN * kGemmBK / 2 / 16;  // 16-byte chunks of a code stage
 constexpr int kAPer = kAChunks / kThreads;
@@ -332,34 +331,8 @@ __device__ __forceinline__ void pipeline_step(const Copier<FMT>& cp, int ks, int
   r.wf[1] = wn[1];
 }
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-// Buffer descriptor word 3 for raw (unformatted) 32-bit accesses.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-
 // silu(v) = v / (1 + e^-v), for the SwiGLU epilogue of an interleaved gate_up weight.
 __device__ __forceinline__ float act_silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
-
-// Output column of prepared weight row `row`, or -1 for a padding row.
-__device__ __forceinline__ int64_t out_col(const MfmaArgs& a, int64_t row, int& h) {
-  h = static_cast<int>(row / a.n_proj_pad);
-  const int64_t lr = row - static_cast<int64_t>(h) * a.n_proj_pad;
-  return lr < a.n_proj ? static_cast<int64_t>(h) * a.n_proj + lr : -1;
-}
-
-
-// (m_tile, n_tile) of tile t.  Tiles are ordered in groups of kGroupM
-// activation-row tiles, weight-tile-major inside a group, so the 64 tiles an
-// XCD holds at once form an 8 x 8 block that shares 8 x tiles and 8 weight
-// tiles in its L2 (x is re-read from outside the XCD once per 8 weight tiles).
-__device__ __forceinline__ void tile_coords(const GemmPlan& pl, int t, int64_t& m0, int64_t& n0) {
-  const int group = t / (kGroupM * pl.n_tiles);
-  const int in_group = t - group * kGroupM * pl.n_tiles;
-  const int rows = pl.m_tiles - group * kGroupM < kGroupM ? pl.m_tiles - group * kGroupM : kGroupM;
-  const int n_tile = in_group / rows;
-  const int m_tile = group * kGroupM + (in_group - n_tile * rows);
-  m0 = static_cast<int64_t>(m_tile) * kGemmBM;
-  n0 = static_cast<int64_t>(n_tile) * kGemmBN;
-}
 
 // acc = the (m0, n0) tile's sums over K steps [k_begin, k_end).
 template <int FMT>
@@ -592,7 +565,11 @@ hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* gri
     hipLaunchKernelGGL(gemm_kernel<kFmtMxfp4>, grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || units == 0) return e;
-  const unsigned reduce_blocks = static_cast<unsigned>(p.tail_tiles * (kReduceItems / kReduceThreads));
+  return launch_tail_reduce(a, stream);
+}
+
+hipError_t launch_tail_reduce(const MfmaArgs& a, hipStream_t stream) {
+  const unsigned reduce_blocks = static_cast<unsigned>(a.plan.tail_tiles * (kReduceItems / kReduceThreads));
   hipLaunchKernelGGL(tail_reduce_kernel, dim3(reduce_blocks), dim3(kReduceThreads), 0, stream, a);
   return hipGetLastError();
 }

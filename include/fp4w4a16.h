@@ -66,7 +66,8 @@ enum fp4_status {
 /* Which kernel a call ran (filled when the caller passes a non-null pointer). */
 typedef struct fp4_dispatch_info {
   int kernel;  /* 0 = VALU decode GEMV, 2 = MFMA decode GEMV (both m <= 8),
-                  1 = MFMA tile GEMM (m > 8), 3 = grouped MoE decode */
+                  1 = MFMA tile GEMM (m > 8), 3 = grouped MoE decode,
+                  4 = W4A4 MXFP4 tile GEMM (any m) */
   int splits;  /* K splits: decode kernels split every tile, the tile GEMM only
                   its tail tiles (1 = no split) */
   int grid_x;  /* decode: workgroups along the output rows; tile GEMM:
@@ -262,6 +263,74 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k,
                          const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
                          uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes,
                          hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
+ * W4A4 MXFP4 variant: activations quantized to MXFP4 at call time and
+ * contracted with an MXFP4 weight on the block-scaled MFMA.  A separate,
+ * opt-in numerics contract: the weight-only entry points above never use it.
+ * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list, W0 and W1:
+ * the compressed-tensors MXFP4 scheme with quantized input activations, run
+ * by a GEMM over 4-bit operands with block-32 E8M0 scales; the pages keep the
+ * weight-only GEMM as the default path ("re-verify 27B NVFP4 on the nvidia
+ * ModelOpt checkpoint" (vllm.cpp PR #178): the fp4-activation GEMM stays
+ * behind an opt-in switch).
+ *
+ * Activation quantization (per row, per 32 consecutive k; the OCP MX v1.0
+ * conversion, as the pages do not print the rule): scale byte
+ * s = max(E - 2, 0), E the biased exponent of the block's largest |x| as a
+ * bf16 (X = 2^(s - 127) = 2^(floor(log2 amax) - 2), at least 2^-127); code =
+ * nearest E2M1 value to x / X, ties to the even code, saturating at 6, sign
+ * bit of x.  A block holding an Inf or NaN gets s = 0xFF and zero codes (the
+ * y of such a row is unspecified).
+ *
+ * Quantized activation layout (fp4_w4a4_act_bytes): with
+ * R = round_up(m, 128) and K = round_up(k, 128),
+ *   codes  [R][K / 2]: two codes per byte, low nibble first;
+ *   scales [R / 16][K / 32][16]: for every group of 16 rows and every 32-code
+ *          block, the 16 rows' E8M0 bytes (the prepared weight's scale layout);
+ * rows m .. R-1 are not written; blocks at or past k get zero codes and byte 0.
+ */
+int fp4_w4a4_act_bytes(int m, int k, size_t* code_bytes_out, size_t* scale_bytes_out);
+
+/*
+ * Quantize bf16 x [m][k] (row-major) into codes_dev / scales_dev (layout
+ * above; buffers of fp4_w4a4_act_bytes(m, k) bytes, 16-byte aligned).  The
+ * quantizer fp4_w4a4_linear runs; exposed so its output can be checked.
+ */
+int fp4_quantize_act_mxfp4(const uint16_t* x_dev, int m, int k, uint8_t* codes_dev, uint8_t* scales_dev,
+                           hipStream_t stream);
+
+/*
+ * Workspace of fp4_w4a4_linear (projections 1) / fp4_w4a4_gate_up
+ * (projections 2, n = n_half): the quantized activations, then the tile
+ * GEMM's tail partials when its 128 x 256 tiles do not fill whole rounds of
+ * the chip.  Never needs zeroing.  Pure host function.
+ */
+int fp4_w4a4_workspace_bytes(int m, int n, int k, int projections, size_t* bytes_out);
+
+/*
+ * y = Q(x) * w^T with Q the activation quantization above and w the MXFP4
+ * weight prepared by fp4_prepare (fmt must be FP4_FMT_MXFP4; any other
+ * format is rejected with FP4_EFMT: the block-scaled MFMA takes only E8M0
+ * block-32 scales).  x_dev bf16 [m][k]; y_dev bf16 [m][n], rounded to nearest
+ * even from the float32 sums; workspace of fp4_w4a4_workspace_bytes(m, n, k, 1).
+ * Two launches (quantizer, tile GEMM) plus the tail reduce when the plan
+ * splits tail tiles.  Each 64-k block product of the MFMA is accumulated in
+ * float32; sums are in a fixed order given (m, n, k), so results are
+ * deterministic run to run.
+ */
+int fp4_w4a4_linear(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                    const uint8_t* prep_scales_dev, int n, int fmt, uint16_t* y_dev, void* workspace_dev,
+                    size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
+ * Fused gate_up of the W4A4 variant over the prepared [gate; up] weight
+ * (fp4_prepare_gate_up): y = [Q(x) gate^T | Q(x) up^T], bf16 [m][2 n_half].
+ * Workspace: fp4_w4a4_workspace_bytes(m, n_half, k, 2).
+ */
+int fp4_w4a4_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                     const uint8_t* prep_scales_dev, int n_half, int fmt, uint16_t* y_dev, void* workspace_dev,
+                     size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
  * Dequantize a prepared weight to float32 out_dev [n][k]:

@@ -202,3 +202,55 @@ def test_argmax_argument_checks(lib):
     need = fp4.fp4_argmax_workspace_bytes(1, 512, 256, NV)
     assert _argmax(lib, ws_bytes=need - 1) == ST["EWORKSPACE"]
     assert _argmax(lib, ws=None) == ST["EINVAL"]
+
+
+def _w4a4_workspace(m, n, k, projections=1):
+    # Quantized activations: rows padded to 128 tiles, k to 128 codes; codes
+    # (half a byte each) then one E8M0 byte per 32 codes; 256-byte aligned.
+    # Then the tail partials of the same 128 x 256 tile plan, K stepping 128
+    # codes and splits of at least 4 steps.
+    r, kk = -(-m // 128) * 128, -(-k // 128) * 128
+    act = -(-(r * kk // 2 + r * kk // 32) // 256) * 256
+    tiles = -(-m // 128) * (projections * (-(-n // 256) * 256) // 256)
+    tail = tiles % 512
+    s = min(512 // tail, -(-k // 128) // 4) if tail else 1
+    return act + (0 if s <= 1 else tail * s * 128 * 256 * 4)
+
+
+def test_w4a4_sizes():
+    assert fp4.fp4_w4a4_act_bytes(1, 256) == (128 * 128, 128 * 8)
+    assert fp4.fp4_w4a4_act_bytes(1024, 4096) == (1024 * 2048, 1024 * 128)
+    assert fp4.fp4_w4a4_act_bytes(129, 4064) == (256 * 2048, 256 * 128)
+    assert fp4.fp4_w4a4_workspace_bytes(1, 512, 256) == _w4a4_workspace(1, 512, 256) == 17408
+    # gate_up at m = 1024: 768 tiles, the 256 past the first round split in two.
+    assert fp4.fp4_w4a4_workspace_bytes(1024, 12288, 4096, 2) == _w4a4_workspace(1024, 12288, 4096, 2)
+    assert fp4.fp4_w4a4_workspace_bytes(1024, 12288, 4096, 2) == 2228224 + 256 * 2 * 131072
+    for m, n, k in [(16, 17408, 5120), (4096, 17408, 5120), (300, 300, 1056), (9, 5120, 17408)]:
+        assert fp4.fp4_w4a4_workspace_bytes(m, n, k) == _w4a4_workspace(m, n, k), (m, n, k)
+    assert fp4.fp4_w4a4_workspace_bytes(0, 512, 256) == 0
+
+
+def _w4a4(lib, m=16, k=256, n=512, fmt=MX, x=FAKE, c=FAKE, s=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.fp4_w4a4_linear(x, m, k, c, s, n, fmt, y, ws, ws_bytes, None, None)
+
+
+def test_w4a4_argument_checks(lib):
+    # NVFP4 weights (E4M3 block-16 scales) cannot feed the block-scaled MFMA.
+    assert _w4a4(lib, fmt=NV) == ST["EFMT"]
+    assert _w4a4(lib, fmt=9) == ST["EFMT"]
+    assert _w4a4(lib, k=48) == ST["EINVAL"]
+    assert _w4a4(lib, n=0) == ST["EINVAL"]
+    assert _w4a4(lib, m=-1) == ST["EINVAL"]
+    assert _w4a4(lib, x=None) == ST["EINVAL"]
+    assert _w4a4(lib, y=None) == ST["EINVAL"]
+    assert _w4a4(lib, ws=None) == ST["EINVAL"]      # the quantized activations live in the workspace
+    assert _w4a4(lib, x=FAKE + 2) == ST["EALIGN"]
+    assert _w4a4(lib, ws=FAKE + 8) == ST["EALIGN"]
+    assert _w4a4(lib, ws_bytes=fp4.fp4_w4a4_workspace_bytes(16, 512, 256) - 1) == ST["EWORKSPACE"]
+    assert _w4a4(lib, m=0, x=None, y=None, ws=None) == ST["OK"]
+    assert lib.fp4_w4a4_gate_up(FAKE, 16, 256, FAKE, FAKE, 512, NV, FAKE, FAKE, 1 << 30, None, None) == ST["EFMT"]
+    assert lib.fp4_quantize_act_mxfp4(FAKE, 4, 48, FAKE, FAKE, None) == ST["EINVAL"]
+    assert lib.fp4_quantize_act_mxfp4(FAKE, 4, 64, FAKE + 4, FAKE, None) == ST["EALIGN"]
+    assert lib.fp4_quantize_act_mxfp4(None, 0, 64, None, None, None) == ST["OK"]
+    sz = ctypes.c_size_t()
+    assert lib.fp4_w4a4_workspace_bytes(16, 512, 256, 3, ctypes.byref(sz)) == ST["EINVAL"]
