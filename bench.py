@@ -26,6 +26,9 @@ Workloads (synthetic weights and activations at the pages' shapes):
   o_proj         NVFP4, k=6144, n=5120
   prefill_nvfp4  NVFP4, k=5120, n=17408 (m=1024 by default)
   prefill_mxfp4  MXFP4, k=5120, n=17408
+  w4a4_gate_up   W4A4 variant (MXFP4 activations quantized per call x MXFP4
+                 weights, block-scaled MFMA), the gate_up shape at m=1024
+  w4a4_prefill   W4A4 variant, k=5120, n=17408, m=1024
   tiny           NVFP4, k=256, n=512
 
 Algorithmic bytes per call: packed codes (n*k/2) + scale bytes (n*k/g)
@@ -76,9 +79,15 @@ WORKLOADS = {
     "o_proj": (3, 0, 5120, 6144, 1, 8),
     "prefill_nvfp4": (4, 0, 17408, 5120, 1, 1024),
     "prefill_mxfp4": (4, 1, 17408, 5120, 1, 1024),
+    "w4a4_gate_up": (1, 1, 12288, 4096, 2, 1024),
+    "w4a4_prefill": (4, 1, 17408, 5120, 1, 1024),
     "tiny": (0, 0, 512, 256, 1, 1),
 }
-TENSOR = {"o_proj": 1, "prefill_mxfp4": 1}
+TENSOR = {"o_proj": 1, "prefill_mxfp4": 1, "w4a4_prefill": 1}
+# Workloads that run the W4A4 variant (activation quantizer + block-scaled MFMA GEMM).
+W4A4 = {"w4a4_gate_up", "w4a4_prefill"}
+W4A4_METRIC = "W4A4 MXFP4 linear TFLOP/s at M=1024 (opt-in variant: activations quantized to MXFP4)"
+FP4_MFMA_PEAK_TFLOPS = 10100.0
 # Workloads that run the greedy-argmax entry point (no logits written).
 ARGMAX = {"lm_head_argmax"}
 # Workloads that run the SwiGLU gate_up (interleaved weight, y = silu(gate) * up).
@@ -166,6 +175,9 @@ def cpu_baseline(name, xbs, host, budget_s):
                 oracle.gate_up_swiglu(x, host["packed"][0][sl], host["scales"][0][sl], host["packed"][1][sl],
                                       host["scales"][1][sl], k, fmt, host["g"][0], host["g"][1])
                 continue
+            if name in W4A4:
+                oracle.w4a4_linear(x, packed[sl], scales[sl], k)
+                continue
             y = oracle.linear(x, packed[sl], scales[sl], k, fmt, g)
             if name in ARGMAX:
                 oracle.greedy_argmax(y)
@@ -187,7 +199,7 @@ def cpu_baseline(name, xbs, host, budget_s):
         one_step(sl)
     dt = (time.perf_counter() - t0) / reps
     frac = sl.stop / (n * proj) * (2 if name in SWIGLU else 1)  # SwiGLU: the slice of both projections
-    if name.startswith("prefill"):
+    if name.startswith("prefill") or name in W4A4:
         value = sum(2.0 * m * sl.stop * k for m, _ in xs) / dt / 1e12
         unit = "TFLOP/s"
     else:
@@ -222,9 +234,11 @@ def cpu_baseline(name, xbs, host, budget_s):
     except Exception:
         threads = cores
     return {"value": round(value, 4), "unit": unit, "cores": int(threads or cores), "kind": "oracle",
-            "sample": "oracle.linear (dequant + float64 matmul) over weight rows [0, %d) of %d, one call per "
+            "sample": "%s over weight rows [0, %d) of %d, one call per "
                       "m in %s, %d timed repetitions; value scaled by the row fraction"
-                      % (sl.stop, n * proj, [m for m, _ in xs], reps),
+                      % ("oracle.w4a4_linear (activation quantization + dequant + float64 matmul)" if name in W4A4
+                         else "oracle.linear (dequant + float64 matmul)", sl.stop, n * proj, [m for m, _ in xs],
+                         reps),
             "host_cpus": cores, "single_thread": single}
 
 
@@ -419,7 +433,9 @@ def main():
         xb = synth.activations(wid, m, k)
         x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
         y = torch.empty((m, n if name in SWIGLU else nout), dtype=torch.bfloat16, device=dev)
-        if name in SWIGLU:
+        if name in W4A4:
+            ws_bytes = fp4.fp4_w4a4_workspace_bytes(m, n, k, proj)
+        elif name in SWIGLU:
             ws_bytes = fp4.fp4_swiglu_workspace_bytes(m, n, k, fmt)
         elif name in ARGMAX:
             ws_bytes = fp4.fp4_argmax_workspace_bytes(m, n, k, fmt)
@@ -432,7 +448,12 @@ def main():
 
     def call(d, i):
         c, s = weights[i % copies]
-        if name in SWIGLU:
+        if name in W4A4:
+            if proj == 2:
+                fp4.fp4_w4a4_gate_up(d["x"], c, s, n, y=d["y"], workspace=d["ws"], info=d["info"])
+            else:
+                fp4.fp4_w4a4_linear(d["x"], c, s, n, y=d["y"], workspace=d["ws"], info=d["info"])
+        elif name in SWIGLU:
             fp4.fp4_w4a16_gate_up_swiglu(d["x"], c, s, n, gs[0], gs[1], fmt, y=d["y"], workspace=d["ws"],
                                          info=d["info"])
         elif proj == 2:
@@ -489,10 +510,13 @@ def main():
         total_bytes += b * args.steps
         total_flops += f * args.steps
         info = d["info"]
-        kern = {0: "gemv_kernel", 2: "decode_mfma_kernel", 1: "gemm_kernel"}[info.kernel]
+        kern = {0: "gemv_kernel", 2: "decode_mfma_kernel", 1: "gemm_kernel", 4: "w4a4_gemm_kernel"}[info.kernel]
         us = ms_m * 1e3 / args.steps
-        kname = ("%s<%d,%s>" % (kern, m, "nvfp4" if fmt == 0 else "mxfp4") if info.kernel != 1
-                 else "%s<%s>" % (kern, "nvfp4" if fmt == 0 else "mxfp4"))
+        if info.kernel == 4:
+            kname = "act_quant_kernel + w4a4_gemm_kernel" + (" + tail_reduce_kernel" if info.splits > 1 else "")
+        else:
+            kname = ("%s<%d,%s>" % (kern, m, "nvfp4" if fmt == 0 else "mxfp4") if info.kernel != 1
+                     else "%s<%s>" % (kern, "nvfp4" if fmt == 0 else "mxfp4"))
         if name in ARGMAX:
             kname += " + argmax_reduce_kernel"
         if name in SWIGLU:
@@ -513,7 +537,16 @@ def main():
         t1 = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), n1, args.launch == "graph")
         if args.steps > n1:
             rows[j]["us_per_launch_differenced"] = round((d["t_ms"] - t1) * 1e3 / (args.steps - n1), 3)
-        if proj == 2 and name not in SWIGLU:
+        if name in W4A4:
+            # The activation quantizer alone (the first launch of each call).
+            qc, qs = fp4.fp4_w4a4_act_bytes(d["m"], k)
+            qct = torch.empty(qc, dtype=torch.uint8, device=dev)
+            qst = torch.empty(qs, dtype=torch.uint8, device=dev)
+            tq = timed_calls(torch, lambda i, d=d: fp4.fp4_quantize_act_mxfp4(d["x"], qct, qst), args.steps,
+                             args.launch == "graph")
+            rows[j]["us_act_quant"] = round(tq * 1e3 / args.steps, 3)
+            rows[j]["us_gemm_and_reduce"] = round(rows[j]["us_per_launch"] - rows[j]["us_act_quant"], 3)
+        if proj == 2 and name not in SWIGLU and name not in W4A4:
             cb, sb = fp4.fp4_prepared_bytes(n, k, fmt)
             yg = torch.empty((d["m"], n), dtype=torch.bfloat16, device=dev)
             yu = torch.empty((d["m"], n), dtype=torch.bfloat16, device=dev)
@@ -540,8 +573,9 @@ def main():
         unit = "GB/s"
     dom = max(rows, key=lambda r: r["us_per_launch"])
     if prefill:
-        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}
+        peak = FP4_MFMA_PEAK_TFLOPS if name in W4A4 else BF16_MFMA_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": peak, "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / peak, 4)}
     else:
         roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4)}
@@ -550,9 +584,10 @@ def main():
                  "traffic": read_traffic(name, dom["m"], kernel_source_hash())})
 
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "metric": W4A4_METRIC if name in W4A4 else METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4" if name in W4A4 else "bf16", "data": "synthetic",
         "config": {"workload": name, "fmt": "nvfp4" if fmt == 0 else "mxfp4", "m": ms, "n": nout, "k": k,
                    "projections": proj, "launch": args.launch, "rotated_weight_copies": copies,
                    "step": "one call at each m in the list", "per_m": rows,

@@ -197,7 +197,7 @@ size_t w4a4_workspace_for(int m, int n_proj, int k, int projections, size_t* par
   const int64_t act = fp4::round_up(fp4::w4a4_act_code_bytes(m, k) + fp4::w4a4_act_scale_bytes(m, k), 256);
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
   if (partial_offset) *partial_offset = static_cast<size_t>(act);
-  return static_cast<size_t>(act + fp4::gemm_workspace_bytes(fp4::w4a4_plan(m, rows_total, k)));
+  return static_cast<size_t>(act + fp4::gemm_workspace_bytes(fp4::w4a4_plan(m, rows_total, k), fp4::kW4BM));
 }
 
 // Shared body of fp4_w4a4_linear and fp4_w4a4_gate_up.

@@ -177,15 +177,16 @@ struct GemmPlan {
   int ksteps;      // K steps of a whole tile
 };
 
-// Plan over K steps of `step_k` codes, splits of at least `min_split_steps`.
-inline GemmPlan tile_plan(int m, int64_t rows_total, int k, int step_k, int min_split_steps) {
+// Plan over tiles of `bm` activation rows, K steps of `step_k` codes, `slots`
+// resident workgroups, splits of at least `min_split_steps`.
+inline GemmPlan tile_plan(int m, int64_t rows_total, int k, int step_k, int min_split_steps, int bm, int slots) {
   GemmPlan p;
-  p.m_tiles = static_cast<int>((m + kGemmBM - 1) / kGemmBM);
+  p.m_tiles = static_cast<int>((m + bm - 1) / bm);
   p.n_tiles = static_cast<int>(rows_total / kGemmBN);
   p.tiles = p.m_tiles * p.n_tiles;
   p.ksteps = static_cast<int>((k + step_k - 1) / step_k);
-  const int tail = p.tiles % kGemmSlots;
-  int s = tail > 0 ? kGemmSlots / tail : 1;
+  const int tail = p.tiles % slots;
+  int s = tail > 0 ? slots / tail : 1;
   const int by_k = p.ksteps / min_split_steps;
   if (s > by_k) s = by_k;
   if (s <= 1) {
@@ -201,32 +202,35 @@ inline GemmPlan tile_plan(int m, int64_t rows_total, int k, int step_k, int min_
 }
 
 inline GemmPlan gemm_plan(int m, int64_t rows_total, int k) {
-  return tile_plan(m, rows_total, k, kGemmBK, kGemmMinSplitSteps);
+  return tile_plan(m, rows_total, k, kGemmBK, kGemmMinSplitSteps, kGemmBM, kGemmSlots);
 }
 
 // W4A4 tile GEMM (MXFP4 activations x MXFP4 weights on the block-scaled
-// MFMA): the same 128 x 256 tiles and tile plan, K stepping 128 codes per
-// stage, tail splits of at least 4 stages (512 codes, as for the W4A16 GEMM).
+// MFMA): 256 x 256 tiles, one 8-wave workgroup per CU, K stepping 128 codes
+// per stage, tail splits of at least 4 stages (512 codes, as for the W4A16
+// GEMM).
+constexpr int kW4BM = 256;
 constexpr int kW4BK = 128;
+constexpr int kW4Slots = kTargetCUs;
 constexpr int kW4MinSplitSteps = 4;
 
 inline GemmPlan w4a4_plan(int m, int64_t rows_total, int k) {
-  return tile_plan(m, rows_total, k, kW4BK, kW4MinSplitSteps);
+  return tile_plan(m, rows_total, k, kW4BK, kW4MinSplitSteps, kW4BM, kW4Slots);
 }
 
 // The quantized activations of a W4A4 call: codes [act_rows][act_k / 2]
 // (two codes per byte, low nibble first) and E8M0 scales in the prepared
 // weight's row-group layout [act_rows / 16][act_k / 32][16].  act_rows covers
-// whole 128-row tiles; rows from m on are never written (their results are
+// whole 256-row tiles; rows from m on are never written (their results are
 // never stored), codes and scales from k to act_k are zero.
 inline int64_t w4a4_act_k(int k) { return round_up(k, kW4BK); }
-inline int64_t w4a4_act_rows(int m) { return round_up(m, kGemmBM); }
+inline int64_t w4a4_act_rows(int m) { return round_up(m, kW4BM); }
 inline int64_t w4a4_act_code_bytes(int m, int k) { return w4a4_act_rows(m) * w4a4_act_k(k) / 2; }
 inline int64_t w4a4_act_scale_bytes(int m, int k) { return w4a4_act_rows(m) * w4a4_act_k(k) / 32; }
 
-// Workspace of a prefill call: fp32 partial tiles [tail_tiles][splits][BM][BN].
-inline int64_t gemm_workspace_bytes(const GemmPlan& p) {
-  return static_cast<int64_t>(p.tail_tiles) * p.splits * kGemmBM * kGemmBN * 4;
+// Workspace of a prefill call: fp32 partial tiles [tail_tiles][splits][bm][BN].
+inline int64_t gemm_workspace_bytes(const GemmPlan& p, int bm = kGemmBM) {
+  return static_cast<int64_t>(p.tail_tiles) * p.splits * bm * kGemmBN * 4;
 }
 
 struct MfmaArgs {
@@ -263,7 +267,7 @@ hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts,
                              int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid,
                              dim3* block);
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
-hipError_t launch_tail_reduce(const MfmaArgs& a, hipStream_t stream);
+hipError_t launch_tail_reduce(const MfmaArgs& a, int bm, hipStream_t stream);
 hipError_t launch_act_quant_mxfp4(const uint16_t* x, int m, int k, uint8_t* codes, uint8_t* scales,
                                   hipStream_t stream);
 hipError_t launch_w4a4(const MfmaArgs& a, hipStream_t stream, dim3* grid, dim3* block);

@@ -1,7 +1,7 @@
 // Tile order and result stores shared by the prefill tile GEMMs (the W4A16
-// GEMM in mfma_gemm.hip and the W4A4 GEMM in w4a4.hip).  Both compute
-// kGemmBM x kGemmBN tiles of y with kGemmWavesM x 4 waves, wave (wm, wn)
-// holding activation rows [128 wm, +128) and weight rows [64 wn, +64) as
+// GEMM in mfma_gemm.hip: 128 x 256 tiles, 4 waves; the W4A4 GEMM in w4a4.hip:
+// 256 x 256 tiles, 8 waves).  Wave w = 4 wm + wn holds activation rows
+// [128 wm, +128) and weight rows [64 wn, +64) of its tile as
 // acc[i][j] (i: 32-row activation block, j: 32-row weight block) in the
 // 32 x 32 MFMA result layout with the weights as the A operand: result e of
 // lane l is weight row 8 (e / 4) + 4 (l / 32) + e % 4, activation row l % 32.
@@ -29,13 +29,14 @@ __device__ __forceinline__ int64_t out_col(const MfmaArgs& a, int64_t row, int& 
 // activation-row tiles, weight-tile-major inside a group, so the 64 tiles an
 // XCD holds at once form an 8 x 8 block that shares 8 x tiles and 8 weight
 // tiles in its L2 (x is re-read from outside the XCD once per 8 weight tiles).
+template <int BM = kGemmBM>
 __device__ __forceinline__ void tile_coords(const GemmPlan& pl, int t, int64_t& m0, int64_t& n0) {
   const int group = t / (kGroupM * pl.n_tiles);
   const int in_group = t - group * kGroupM * pl.n_tiles;
   const int rows = pl.m_tiles - group * kGroupM < kGroupM ? pl.m_tiles - group * kGroupM : kGroupM;
   const int n_tile = in_group / rows;
   const int m_tile = group * kGroupM + (in_group - n_tile * rows);
-  m0 = static_cast<int64_t>(m_tile) * kGemmBM;
+  m0 = static_cast<int64_t>(m_tile) * BM;
   n0 = static_cast<int64_t>(n_tile) * kGemmBN;
 }
 
@@ -49,67 +50,100 @@ __device__ __forceinline__ int dp_tile_of(const GemmPlan& pl, int bid) {
   return xcd * q + (xcd < rr ? xcd : rr) + bid / 8;
 }
 
-// Scale by the projection's global scale and store bf16 y, four consecutive
-// output columns (weight rows) of one activation row per lane and (i, j, e4).
-// (The W4A16 GEMM keeps this store and the partial store below written out in
-// its kernel body: formed through these helpers, its K loop's registers spill.)
-__device__ __forceinline__ void store_tile_bf16(const MfmaArgs& a, int64_t m0, int64_t n0, int wave,
-                                                const f32x16_t (&acc)[4][2]) {
-  const int lane = threadIdx.x & 63;
-  const int l32 = lane & 31;
-  const int lh = lane >> 5;
-  const int wm = wave / 4;
-  const int wn = wave % 4;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      int h;
-      const int64_t col = out_col(a, n0 + wn * 64 + 32 * j + 8 * e4 + 4 * lh, h);
-      if (col < 0) continue;
-      const float g = a.gscale[h];
-      const int64_t lr = col - static_cast<int64_t>(h) * a.n_proj;
-      const bool vec = lr + 4 <= a.n_proj && ((col | a.ldy) & 3) == 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * 128 + 32 * i + l32;
-        if (m >= a.m) continue;
-        uint16_t* dst = a.y + m * a.ldy + col;
-        const float v0 = acc[i][j][4 * e4] * g, v1 = acc[i][j][4 * e4 + 1] * g;
-        const float v2 = acc[i][j][4 * e4 + 2] * g, v3 = acc[i][j][4 * e4 + 3] * g;
-        if (vec) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(f32x2_to_bf16x2_rne(v0, v1), f32x2_to_bf16x2_rne(v2, v3));
-        } else {
-          const float w[4] = {v0, v1, v2, v3};
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2)
-            if (lr + q2 < a.n_proj) dst[q2] = f32_to_bf16_rne(w[q2]);
-        }
-      }
-    }
-}
+// Result stores through LDS.  In the MFMA result layout a lane holds 4
+// consecutive output columns of one activation row, and the 32 lanes of a
+// half-wave hold 32 different rows, so direct stores write 8-byte (bf16) or
+// 16-byte (fp32) pieces a row apart.  Instead each wave first writes its
+// fragments into a row-major tile in LDS (rows padded by 16 bytes, so the 32
+// rows a store instruction touches start in different banks), and the
+// workgroup then writes whole rows, 16 contiguous bytes per lane (measured
+// on MI355X for the W4A4 GEMM at m = 1024: the direct stores cost about a
+// third of the kernel's time).  `lds` is the workgroup's stage memory, free
+// once the K loop is done; every wave's K loop must have finished reading it
+// and no copy into it may be in flight.
+constexpr int kStageYRow = kGemmBN * 2 + 16;  // bytes per staged bf16 row
+constexpr int kStagePRow = kGemmBN * 4 + 16;  // bytes per staged fp32 row
 
-// Store tail unit u's fp32 partial tile [x row][weight row].  Buffer stores:
-// with plain stores the compiler's register allocation of the K loop spills.
-__device__ __forceinline__ void store_tile_partial(const MfmaArgs& a, int u, int wave, const f32x16_t (&acc)[4][2]) {
-  const int lane = threadIdx.x & 63;
+// bf16 y of a whole tile: BM x 256 outputs, scaled by the projection's global
+// scale (a tile never spans two projections: n_proj_pad is a multiple of 256).
+template <int BM, int THREADS>
+__device__ __forceinline__ void store_tile_bf16_staged(const MfmaArgs& a, int64_t m0, int64_t n0, int wave,
+                                                       const f32x16_t (&acc)[4][2], char* lds) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
   const int l32 = lane & 31;
   const int lh = lane >> 5;
   const int wm = wave / 4;
   const int wn = wave % 4;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      a.partial + static_cast<int64_t>(u) * kGemmBM * kGemmBN, 0, kGemmBM * kGemmBN * 4, kBufferRsrcWord3);
+  const int h = static_cast<int>(n0 / a.n_proj_pad);
+  const float g = h == 0 ? a.gscale[0] : a.gscale[1];
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int mr = wm * 128 + 32 * i + l32;
-        const int nr = wn * 64 + 32 * j + 8 * e4 + 4 * lh;
-        const f32x4_t v = {acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rsrc, (mr * kGemmBN + nr) * 4, 0, 0);
+        const int row = wm * 128 + 32 * i + l32;
+        const int col = wn * 64 + 32 * j + 8 * e4 + 4 * lh;
+        *reinterpret_cast<uint2*>(lds + row * kStageYRow + 2 * col) =
+            make_uint2(f32x2_to_bf16x2_rne(acc[i][j][4 * e4] * g, acc[i][j][4 * e4 + 1] * g),
+                       f32x2_to_bf16x2_rne(acc[i][j][4 * e4 + 2] * g, acc[i][j][4 * e4 + 3] * g));
       }
+  __syncthreads();
+  // Row r, 8-column chunk c: thread t takes chunk t % 32 of rows t / 32 + (THREADS / 32) q.
+  const int c8 = t & 31;
+  const int64_t lr = n0 - static_cast<int64_t>(h) * a.n_proj_pad + 8 * c8;  // column within the projection
+  const int64_t col = static_cast<int64_t>(h) * a.n_proj + lr;
+  const bool vec = lr + 8 <= a.n_proj && ((col | a.ldy) & 7) == 0;
+  if (lr >= a.n_proj) return;
+  for (int row = t >> 5; row < BM; row += THREADS / 32) {
+    const int64_t m = m0 + row;
+    if (m >= a.m) break;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + row * kStageYRow + 16 * c8);
+    uint16_t* dst = a.y + m * a.ldy + col;
+    if (vec) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 8 && lr + e < a.n_proj; ++e) dst[e] = static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
+    }
+  }
+}
+
+// fp32 partial tile of tail unit u, row-major [BM][256], staged 128 rows (one
+// row of waves) at a time.
+template <int BM, int THREADS>
+__device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int u, int wave,
+                                                          const f32x16_t (&acc)[4][2], char* lds) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int l32 = lane & 31;
+  const int lh = lane >> 5;
+  const int wm = wave / 4;
+  const int wn = wave % 4;
+  float* dst = a.partial + static_cast<int64_t>(u) * BM * kGemmBN;
+  for (int half = 0; half < BM / 128; ++half) {
+    __syncthreads();
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int row = 32 * i + l32;
+            const int col = wn * 64 + 32 * j + 8 * e4 + 4 * lh;
+            const f32x4_t v = {acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
+            *reinterpret_cast<f32x4_t*>(lds + row * kStagePRow + 4 * col) = v;
+          }
+    }
+    __syncthreads();
+    // 128 rows x 64 chunks of 4 floats: thread t takes chunk t % 64 of rows t / 64 + (THREADS / 64) q.
+    for (int row = t >> 6; row < 128; row += THREADS / 64)
+      *reinterpret_cast<f32x4_t*>(dst + (half * 128 + row) * kGemmBN + 4 * (t & 63)) =
+          *reinterpret_cast<const f32x4_t*>(lds + row * kStagePRow + 16 * (t & 63));
+  }
 }
 
 }  // namespace fp4

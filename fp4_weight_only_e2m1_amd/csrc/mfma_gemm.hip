@@ -474,20 +474,24 @@ void gemm_kernel(const MfmaArgs a) {
 // partial_{S-1}), added in split order (a fixed order: the output does not
 // depend on timing).  A separate launch, so every partial is complete and
 // visible when it starts; each thread takes one (x row, 4 weight rows) item of
-// one tail tile and keeps its S loads in flight kBatch at a time.
+// one tail tile and keeps its S loads in flight kBatch at a time.  BM: the
+// tile's activation rows (128 for the W4A16 GEMM, 256 for the W4A4 GEMM).
 constexpr int kReduceThreads = 256;
-constexpr int kReduceItems = kGemmBM * kGemmBN / 4;  // per tail tile
-static_assert(kReduceItems % kReduceThreads == 0, "reduce split");
+template <int BM>
+constexpr int kReduceItems = BM * kGemmBN / 4;  // per tail tile
+static_assert(kReduceItems<kGemmBM> % kReduceThreads == 0 && kReduceItems<kW4BM> % kReduceThreads == 0,
+              "reduce split");
 
+template <int BM>
 __global__ __launch_bounds__(kReduceThreads) void tail_reduce_kernel(const MfmaArgs a) {
   const GemmPlan& pl = a.plan;
   const int64_t gi = static_cast<int64_t>(blockIdx.x) * kReduceThreads + threadIdx.x;
-  const int tail_tile = static_cast<int>(gi / kReduceItems);
-  const int it = static_cast<int>(gi - static_cast<int64_t>(tail_tile) * kReduceItems);
+  const int tail_tile = static_cast<int>(gi / kReduceItems<BM>);
+  const int it = static_cast<int>(gi - static_cast<int64_t>(tail_tile) * kReduceItems<BM>);
   const int mr = it / (kGemmBN / 4);
   const int nr = 4 * (it % (kGemmBN / 4));
   int64_t m0, n0;
-  tile_coords(pl, pl.dp_tiles + tail_tile, m0, n0);
+  tile_coords<BM>(pl, pl.dp_tiles + tail_tile, m0, n0);
   const int64_t m = m0 + mr;
   if (m >= a.m) return;
   if (a.act) {
@@ -498,7 +502,7 @@ __global__ __launch_bounds__(kReduceThreads) void tail_reduce_kernel(const MfmaA
     const int64_t grow = n0 + nr;
     const int64_t col = (grow >> 5) * 16 + (grow & 15);
     if (col >= a.n_proj) return;
-    const int64_t unit_floats = static_cast<int64_t>(kGemmBM) * kGemmBN;
+    const int64_t unit_floats = static_cast<int64_t>(BM) * kGemmBN;
     const float* p = a.partial + static_cast<int64_t>(tail_tile) * pl.splits * unit_floats + mr * kGemmBN + nr;
     f32x4_t gsum = *reinterpret_cast<const f32x4_t*>(p);
     f32x4_t usum = *reinterpret_cast<const f32x4_t*>(p + 16);
@@ -525,7 +529,7 @@ __global__ __launch_bounds__(kReduceThreads) void tail_reduce_kernel(const MfmaA
   if (col < 0) return;
 
   constexpr int kBatch = 8;
-  const int64_t unit_floats = static_cast<int64_t>(kGemmBM) * kGemmBN;
+  const int64_t unit_floats = static_cast<int64_t>(BM) * kGemmBN;
   const float* p = a.partial + static_cast<int64_t>(tail_tile) * pl.splits * unit_floats + mr * kGemmBN + nr;
   f32x4_t sum = *reinterpret_cast<const f32x4_t*>(p);
   for (int s0 = 1; s0 < pl.splits; s0 += kBatch) {
@@ -565,12 +569,17 @@ hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* gri
     hipLaunchKernelGGL(gemm_kernel<kFmtMxfp4>, grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || units == 0) return e;
-  return launch_tail_reduce(a, stream);
+  return launch_tail_reduce(a, kGemmBM, stream);
 }
 
-hipError_t launch_tail_reduce(const MfmaArgs& a, hipStream_t stream) {
-  const unsigned reduce_blocks = static_cast<unsigned>(a.plan.tail_tiles * (kReduceItems / kReduceThreads));
-  hipLaunchKernelGGL(tail_reduce_kernel, dim3(reduce_blocks), dim3(kReduceThreads), 0, stream, a);
+hipError_t launch_tail_reduce(const MfmaArgs& a, int bm, hipStream_t stream) {
+  if (bm == kW4BM) {
+    const unsigned blocks = static_cast<unsigned>(a.plan.tail_tiles * (kReduceItems<kW4BM> / kReduceThreads));
+    hipLaunchKernelGGL(tail_reduce_kernel<kW4BM>, dim3(blocks), dim3(kReduceThreads), 0, stream, a);
+  } else {
+    const unsigned blocks = static_cast<unsigned>(a.plan.tail_tiles * (kReduceItems<kGemmBM> / kReduceThreads));
+    hipLaunchKernelGGL(tail_reduce_kernel<kGemmBM>, dim3(blocks), dim3(kReduceThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -20,16 +20,20 @@
 // byte 0xFF and zero codes.  x / X is exact in float32 (a power-of-two
 // scaling that stays below 8), so every decision matches an exact one.
 //
-// GEMM tile: as in the W4A16 GEMM, a workgroup of 4 waves computes 128
-// activation rows x 256 weight rows, wave w owning weight rows [64 w, +64)
-// and all 128 activation rows.  K advances 128 codes per stage; a stage holds
-// in LDS
-//   activation codes   128 rows x 64 bytes                     8 KiB
+// GEMM tile: a workgroup of 8 waves computes 256 activation rows x 256
+// weight rows, wave w = 4 wm + wn owning activation rows [128 wm, +128) and
+// weight rows [64 wn, +64).  K advances 128 codes per stage; a stage holds in
+// LDS
+//   activation codes   256 rows x 64 bytes                    16 KiB
 //   weight codes       256 rows x 64 bytes                    16 KiB
-//   activation scales  8 row groups x 4 blocks x 16 rows     512 B (stored twice)
+//   activation scales  16 row groups x 4 blocks x 16 rows      1 KiB
 //   weight scales      16 row groups x 4 blocks x 16 rows      1 KiB
-// copied by the load-to-LDS path, three stage buffers (78 KiB: two
-// workgroups per CU).
+// copied by the load-to-LDS path into four stage buffers (136 KiB: one
+// workgroup per CU), three stages in flight.  The stage loads run at the
+// latency of the L2 and beyond, so what bounds the MFMA rate is how many
+// flops each byte in flight feeds: a 256 x 256 tile feeds 1.5 times as many
+// as a 128 x 256 one (measured on MI355X: the 128 x 256 form with two
+// workgroups per CU reached 1.9 PFLOP/s on the gate_up shape at m = 1024).
 //
 // Operand layout of the instruction with 4-bit A and B (checked on MI355X
 // against a host product): lane l supplies row l % 32 of A and column l % 32
@@ -115,23 +119,26 @@ __global__ __launch_bounds__(kQuantThreads) void act_quant_kernel(const uint16_t
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kStages = 4;
 constexpr int kRowBytes = kW4BK / 2;             // code bytes of a row per stage
 constexpr int kRowChunks = kRowBytes / 16;       // 16-byte chunks (32-code blocks) of a row per stage
-constexpr int kAChunks = kGemmBM * kRowChunks;   // activation code chunks per stage
+constexpr int kAChunks = kW4BM * kRowChunks;     // activation code chunks per stage
 constexpr int kBChunks = kGemmBN * kRowChunks;   // weight code chunks per stage
 constexpr int kAPer = kAChunks / kThreads;
 constexpr int kBPer = kBChunks / kThreads;
 static_assert(kAChunks % kThreads == 0 && kBChunks % kThreads == 0, "stage split");
-static_assert(kGemmWavesM == 1 && kThreads == 64 * 4, "one row of four waves");
+static_assert(kThreads == 64 * 8 && kW4BM == 256 && kGemmBN == 256, "two rows of four waves");
 
 struct alignas(16) Stage {
   uint4 a[kAChunks];
   uint4 b[kBChunks];
-  uint4 sa[64];  // [row group 0..7][block 0..3][16 rows]; chunks 32..63 repeat 0..31
+  uint4 sa[64];  // [row group 0..15][block 0..3][16 rows]
   uint4 sb[64];  // [row group 0..15][block 0..3][16 rows]
 };
-static_assert(2 * 3 * sizeof(Stage) <= 160 * 1024, "two workgroups of three stages per CU");
+static_assert(kStages * sizeof(Stage) <= 160 * 1024, "one workgroup of four stages per CU");
+static_assert(kW4BM * kStageYRow <= kStages * sizeof(Stage) && 128 * kStagePRow <= kStages * sizeof(Stage),
+              "result staging fits in the stage buffers");
 
 // Code stages: row r holds its 4 chunks at 16-byte slots 4 r .. 4 r + 3,
 // chunk c in slot 4 r + (c ^ ((r >> 2) & 3)).  A fragment read has 16 lanes
@@ -142,7 +149,8 @@ static_assert(2 * 3 * sizeof(Stage) <= 160 * 1024, "two workgroups of three stag
 // order (lane l's 16 bytes land at 16 l past the wave's base), so the swizzle
 // is applied by choosing which global chunk each lane fetches.  Each lane keeps
 // 32-bit offsets from wave-uniform bases that advance with the stage.  Wave 0
-// also copies the weight scales, wave 1 the activation scales.
+// also copies the weight scales, wave 1 the activation scales (one 16-byte
+// chunk per lane: row group lane / 4, block lane % 4 of the stage).
 struct Copier {
   const uint8_t* xa;  // activation code row m0
   const uint8_t* wb;  // weight code row n0
@@ -171,11 +179,9 @@ struct Copier {
       const int c = (p & 3) ^ ((r >> 2) & 3);
       boff[i] = static_cast<uint32_t>(r * brow + 16 * c);
     }
-    // Scale chunk of a lane: row group lane / 4 (activations: (lane % 32) / 4),
-    // block lane % 4 of the stage.
     const int lane = t & 63;
     soff = wave == 0 ? static_cast<uint32_t>((lane >> 2) * a.ksegs * kRowGroup + 16 * (lane & 3))
-                     : static_cast<uint32_t>(((lane & 31) >> 2) * (a.act_k / 32) * kRowGroup + 16 * (lane & 3));
+                     : static_cast<uint32_t>((lane >> 2) * (a.act_k / 32) * kRowGroup + 16 * (lane & 3));
   }
 
   __device__ __forceinline__ void issue(int ks, Stage& sb, int wave) const {
@@ -218,8 +224,8 @@ __device__ __forceinline__ i32x8_t as_operand(uint4 q) {
 }
 
 // This lane's byte offsets inside a stage for one MFMA step: its code chunk
-// of activation row l % 32 (xo) and weight row 64 w + l % 32 (wo), and its
-// scale bytes (xso, wso).  Fragment i / j adds 32 rows: 2048 bytes of codes,
+// of activation row 128 wm + l % 32 (xo) and weight row 64 wn + l % 32 (wo),
+// and its scale bytes (xso, wso).  Fragment i / j adds 32 rows: 2048 bytes of codes,
 // 128 bytes of scales.
 struct LaneOffsets {
   uint32_t xo, wo, xso, wso;
@@ -252,26 +258,27 @@ __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][2])
 }
 
 // acc = the (m0, n0) tile's sums over stages [k_begin, k_end).  Stage ks
-// lives in buffer (ks - k_begin) % 3.  Each iteration waits for stage ks
+// lives in buffer (ks - k_begin) % 4.  Each iteration waits for stage ks
 // (and, through the barrier, for every wave to be done with stage ks - 1,
-// whose buffer it then refills with stage ks + 2) and runs the stage's two
+// whose buffer it then refills with stage ks + 3) and runs the stage's two
 // MFMA steps.  One loop body, so the accumulators keep their registers.
 __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t n0, int k_begin, int k_end,
-                                         Stage (&st)[3], f32x16_t (&acc)[4][2]) {
+                                         Stage (&st)[kStages], f32x16_t (&acc)[4][2]) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int l32 = lane & 31;
   const int lh = lane >> 5;
-  const int wr0 = wave * 64 + l32;
+  const int xr0 = (wave >> 2) * 128 + l32;  // activation row of this lane's first fragment
+  const int wr0 = (wave & 3) * 64 + l32;     // weight row of this lane's first fragment
   // Step s uses block c = 2 s + lh of the stage, in slot c ^ sw of the row
   // (sw = (row >> 2) & 3, the same for every row of this lane): step 1's
   // slot is step 0's with bit 1 flipped.
   const int sw = (l32 >> 2) & 3;
   LaneOffsets o0, o1;
-  o0.xo = static_cast<uint32_t>(16 * (4 * l32 + (lh ^ sw)));
+  o0.xo = static_cast<uint32_t>(16 * (4 * xr0 + (lh ^ sw)));
   o0.wo = static_cast<uint32_t>(16 * (4 * wr0 + (lh ^ sw)));
-  o0.xso = static_cast<uint32_t>((l32 >> 4) * 64 + 16 * lh + (l32 & 15));
+  o0.xso = static_cast<uint32_t>((xr0 >> 4) * 64 + 16 * lh + (xr0 & 15));
   o0.wso = static_cast<uint32_t>((wr0 >> 4) * 64 + 16 * lh + (wr0 & 15));
   o1.xo = o0.xo ^ 32u;
   o1.wo = o0.wo ^ 32u;
@@ -286,20 +293,25 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
   const Copier cp(a, m0, n0, t, wave);
   cp.issue(k_begin, st[0], wave);
   if (k_begin + 1 < k_end) cp.issue(k_begin + 1, st[1], wave);
+  if (k_begin + 2 < k_end) cp.issue(k_begin + 2, st[2], wave);
   int buf = 0;
   for (int ks = k_begin; ks < k_end; ++ks) {
-    if (ks + 1 < k_end)
+    // Stage ks landed when at most the copies of the (up to two) stages
+    // after it are in flight.
+    if (ks + 2 < k_end)
+      wait_stages_barrier<2>(wave);
+    else if (ks + 1 < k_end)
       wait_stages_barrier<1>(wave);
     else
       wait_stages_barrier<0>(wave);
-    const int fill = buf == 0 ? 2 : buf - 1;
-    if (ks + 2 < k_end) cp.issue(ks + 2, st[fill], wave);
+    const int fill = buf == 0 ? kStages - 1 : buf - 1;
+    if (ks + 3 < k_end) cp.issue(ks + 3, st[fill], wave);
     Frags f;
     read_step(st[buf], o0, f);
     mfma_step(f, acc);
     read_step(st[buf], o1, f);
     mfma_step(f, acc);
-    buf = buf == 2 ? 0 : buf + 1;
+    buf = buf == kStages - 1 ? 0 : buf + 1;
   }
 }
 
@@ -309,16 +321,16 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
 // K range of a tail tile into an fp32 partial, which the reduce launch adds.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void w4a4_gemm_kernel(const MfmaArgs a) {
-  __shared__ Stage st[3];
+  __shared__ Stage st[kStages];
   const GemmPlan& pl = a.plan;
   const int bid = blockIdx.x;
   const int wave = threadIdx.x >> 6;
   f32x16_t acc[4][2];
   if (bid < pl.dp_tiles) {
     int64_t m0, n0;
-    tile_coords(pl, dp_tile_of(pl, bid), m0, n0);
+    tile_coords<kW4BM>(pl, dp_tile_of(pl, bid), m0, n0);
     run_tile(a, m0, n0, 0, pl.ksteps, st, acc);
-    store_tile_bf16(a, m0, n0, wave, acc);
+    store_tile_bf16_staged<kW4BM, kThreads>(a, m0, n0, wave, acc, reinterpret_cast<char*>(st));
   }
   const int units = pl.tail_tiles * pl.splits;
   const int u = bid - (static_cast<int>(gridDim.x) - units);
@@ -326,10 +338,10 @@ void w4a4_gemm_kernel(const MfmaArgs a) {
   __syncthreads();  // the stage buffers are reused
   const int split = u % pl.splits;
   int64_t m0, n0;
-  tile_coords(pl, pl.dp_tiles + u / pl.splits, m0, n0);
+  tile_coords<kW4BM>(pl, pl.dp_tiles + u / pl.splits, m0, n0);
   run_tile(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
            static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
-  store_tile_partial(a, u, wave, acc);
+  store_tile_partial_staged<kW4BM, kThreads>(a, u, wave, acc, reinterpret_cast<char*>(st));
 }
 
 }  // namespace
@@ -353,7 +365,7 @@ hipError_t launch_w4a4(const MfmaArgs& a, hipStream_t stream, dim3* grid_out, di
   hipLaunchKernelGGL(w4a4_gemm_kernel, grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || units == 0) return e;
-  return launch_tail_reduce(a, stream);
+  return launch_tail_reduce(a, kW4BM, stream);
 }
 
 }  // namespace fp4

@@ -284,7 +284,7 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k,
  * y of such a row is unspecified).
  *
  * Quantized activation layout (fp4_w4a4_act_bytes): with
- * R = round_up(m, 128) and K = round_up(k, 128),
+ * R = round_up(m, 256) and K = round_up(k, 128),
  *   codes  [R][K / 2]: two codes per byte, low nibble first;
  *   scales [R / 16][K / 32][16]: for every group of 16 rows and every 32-code
  *          block, the 16 rows' E8M0 bytes (the prepared weight's scale layout);
@@ -303,8 +303,8 @@ int fp4_quantize_act_mxfp4(const uint16_t* x_dev, int m, int k, uint8_t* codes_d
 /*
  * Workspace of fp4_w4a4_linear (projections 1) / fp4_w4a4_gate_up
  * (projections 2, n = n_half): the quantized activations, then the tile
- * GEMM's tail partials when its 128 x 256 tiles do not fill whole rounds of
- * the chip.  Never needs zeroing.  Pure host function.
+ * GEMM's tail partials when its 256 x 256 tiles do not fill whole rounds of
+ * the chip (one tile per CU).  Never needs zeroing.  Pure host function.
  */
 int fp4_w4a4_workspace_bytes(int m, int n, int k, int projections, size_t* bytes_out);
 

@@ -205,26 +205,27 @@ def test_argmax_argument_checks(lib):
 
 
 def _w4a4_workspace(m, n, k, projections=1):
-    # Quantized activations: rows padded to 128 tiles, k to 128 codes; codes
-    # (half a byte each) then one E8M0 byte per 32 codes; 256-byte aligned.
-    # Then the tail partials of the same 128 x 256 tile plan, K stepping 128
-    # codes and splits of at least 4 steps.
-    r, kk = -(-m // 128) * 128, -(-k // 128) * 128
+    # Quantized activations: rows padded to 256-row tiles, k to 128 codes;
+    # codes (half a byte each) then one E8M0 byte per 32 codes; 256-byte
+    # aligned.  Then the tail partials of the 256 x 256 tile plan: 256
+    # workgroups resident (one per CU), K stepping 128 codes, splits of at
+    # least 4 steps.
+    r, kk = -(-m // 256) * 256, -(-k // 128) * 128
     act = -(-(r * kk // 2 + r * kk // 32) // 256) * 256
-    tiles = -(-m // 128) * (projections * (-(-n // 256) * 256) // 256)
-    tail = tiles % 512
-    s = min(512 // tail, -(-k // 128) // 4) if tail else 1
-    return act + (0 if s <= 1 else tail * s * 128 * 256 * 4)
+    tiles = -(-m // 256) * (projections * (-(-n // 256) * 256) // 256)
+    tail = tiles % 256
+    s = min(256 // tail, -(-k // 128) // 4) if tail else 1
+    return act + (0 if s <= 1 else tail * s * 256 * 256 * 4)
 
 
 def test_w4a4_sizes():
-    assert fp4.fp4_w4a4_act_bytes(1, 256) == (128 * 128, 128 * 8)
+    assert fp4.fp4_w4a4_act_bytes(1, 256) == (256 * 128, 256 * 8)
     assert fp4.fp4_w4a4_act_bytes(1024, 4096) == (1024 * 2048, 1024 * 128)
-    assert fp4.fp4_w4a4_act_bytes(129, 4064) == (256 * 2048, 256 * 128)
-    assert fp4.fp4_w4a4_workspace_bytes(1, 512, 256) == _w4a4_workspace(1, 512, 256) == 17408
-    # gate_up at m = 1024: 768 tiles, the 256 past the first round split in two.
+    assert fp4.fp4_w4a4_act_bytes(257, 4064) == (512 * 2048, 512 * 128)
+    assert fp4.fp4_w4a4_workspace_bytes(1, 512, 256) == _w4a4_workspace(1, 512, 256) == 34816
+    # gate_up at m = 1024: 384 tiles, the 128 past the first round split in two.
     assert fp4.fp4_w4a4_workspace_bytes(1024, 12288, 4096, 2) == _w4a4_workspace(1024, 12288, 4096, 2)
-    assert fp4.fp4_w4a4_workspace_bytes(1024, 12288, 4096, 2) == 2228224 + 256 * 2 * 131072
+    assert fp4.fp4_w4a4_workspace_bytes(1024, 12288, 4096, 2) == 2228224 + 128 * 2 * 262144
     for m, n, k in [(16, 17408, 5120), (4096, 17408, 5120), (300, 300, 1056), (9, 5120, 17408)]:
         assert fp4.fp4_w4a4_workspace_bytes(m, n, k) == _w4a4_workspace(m, n, k), (m, n, k)
     assert fp4.fp4_w4a4_workspace_bytes(0, 512, 256) == 0

@@ -21,7 +21,7 @@ MX = fp4.FMT_MXFP4
 def _unpack_act(codes, scales, m, k):
     """GPU quantized-activation buffers -> (codes [m, k], scale bytes [m, k/32]) in the oracle's form,
     plus the padding blocks (k .. K) of rows < m."""
-    r, kk = -(-m // 128) * 128, -(-k // 128) * 128
+    r, kk = -(-m // 256) * 256, -(-k // 128) * 128
     cb = codes.cpu().numpy()[: r * kk // 2].reshape(r, kk // 2)[:m]
     c = np.empty((m, kk), np.uint8)
     c[:, 0::2] = cb & 0x0F
@@ -94,9 +94,10 @@ def _w4a4_ref(xbits, packed, scales, k):
 @pytest.mark.parametrize("m,n,k", [
     (1, 512, 256),       # one tile, no split
     (17, 300, 1056),     # ragged rows, columns and k (k % 128 = 32)
-    (130, 1000, 4096),   # 2 x 4 tiles, ragged both ways
+    (130, 1000, 4096),   # 1 x 4 tiles, ragged both ways
     (16, 5120, 17408),   # 20 tiles: tail split along K
-    (300, 768, 2080),    # 3 x 3 tiles, k % 128 = 32
+    (300, 768, 2080),    # 2 x 3 tiles, k % 128 = 32
+    (600, 1024, 512),    # 3 x 4 tiles, ragged rows
 ])
 def test_w4a4_linear_parity(m, n, k):
     packed, scales, _ = synth.packed_weight(synth.TINY, 80, n, k, MX)
