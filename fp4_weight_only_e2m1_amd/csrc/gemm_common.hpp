@@ -111,11 +111,12 @@ __device__ __forceinline__ void store_tile_bf16_staged(const MfmaArgs& a, int64_
   }
 }
 
-// fp32 partial tile of tail unit u, row-major [BM][256], staged 128 rows (one
-// row of waves) at a time.
-template <int BM, int THREADS>
+// fp32 partial tile of tail unit u, row-major [BM][256], staged PASS rows at
+// a time (PASS a multiple of 32 dividing 128, or 128).
+template <int BM, int THREADS, int PASS>
 __device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int u, int wave,
                                                           const f32x16_t (&acc)[4][2], char* lds) {
+  static_assert(PASS % 32 == 0 && (128 % PASS == 0 || PASS % 128 == 0) && BM % PASS == 0, "pass rows");
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int l32 = lane & 31;
@@ -123,25 +124,26 @@ __device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int
   const int wm = wave / 4;
   const int wn = wave % 4;
   float* dst = a.partial + static_cast<int64_t>(u) * BM * kGemmBN;
-  for (int half = 0; half < BM / 128; ++half) {
+  for (int pass = 0; pass < BM / PASS; ++pass) {
     __syncthreads();
-    if (wm == half) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int row0 = wm * 128 + 32 * i;  // first tile row of fragment row i (wave-uniform)
+      if (row0 / PASS != pass) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const int row = 32 * i + l32;
-            const int col = wn * 64 + 32 * j + 8 * e4 + 4 * lh;
-            const f32x4_t v = {acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
-            *reinterpret_cast<f32x4_t*>(lds + row * kStagePRow + 4 * col) = v;
-          }
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int row = row0 - pass * PASS + l32;
+          const int col = wn * 64 + 32 * j + 8 * e4 + 4 * lh;
+          const f32x4_t v = {acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
+          *reinterpret_cast<f32x4_t*>(lds + row * kStagePRow + 4 * col) = v;
+        }
     }
     __syncthreads();
-    // 128 rows x 64 chunks of 4 floats: thread t takes chunk t % 64 of rows t / 64 + (THREADS / 64) q.
-    for (int row = t >> 6; row < 128; row += THREADS / 64)
-      *reinterpret_cast<f32x4_t*>(dst + (half * 128 + row) * kGemmBN + 4 * (t & 63)) =
+    // PASS rows x 64 chunks of 4 floats: thread t takes chunk t % 64 of rows t / 64 + (THREADS / 64) q.
+    for (int row = t >> 6; row < PASS; row += THREADS / 64)
+      *reinterpret_cast<f32x4_t*>(dst + (pass * PASS + row) * kGemmBN + 4 * (t & 63)) =
           *reinterpret_cast<const f32x4_t*>(lds + row * kStagePRow + 16 * (t & 63));
   }
 }

@@ -51,9 +51,10 @@ namespace fp4 {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Activation quantizer: one thread per (row, 32-code block); the threads of a
-// 16-thread group take the 16 rows of one row group, so each group writes 16
-// adjacent scale bytes.
+// Activation quantizer: four lanes per (row, 32-code block), each taking 8
+// consecutive values (one 16-byte load); consecutive lanes read consecutive
+// bytes of a row.  The block's amax is combined across the four lanes, each
+// lane writes its 8 codes (4 bytes) and the block's first lane its scale.
 
 constexpr int kQuantThreads = 256;
 
@@ -62,36 +63,36 @@ __global__ __launch_bounds__(kQuantThreads) void act_quant_kernel(const uint16_t
                                                                   uint8_t* __restrict__ scales) {
   const int64_t kb = act_k / 32;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kQuantThreads + threadIdx.x;
-  const int64_t groups = (m + kRowGroup - 1) / kRowGroup;
-  if (i >= groups * kb * kRowGroup) return;
-  const int r16 = static_cast<int>(i & 15);
-  const int64_t gb = i >> 4;  // (row group, block)
-  const int64_t g = gb / kb;
-  const int64_t blk = gb - g * kb;
-  const int64_t row = g * kRowGroup + r16;
+  const int q = static_cast<int>(i & 3);   // quarter of the block
+  const int64_t rb = i >> 2;               // (row, block)
+  const int64_t row = rb / kb;
+  const int64_t blk = rb - row * kb;
+  // Every lane of a 4-lane group has the same (row, block), so the group
+  // leaves together and the shuffles below see only active partners.
   if (row >= m) return;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  const bool real = blk * 32 < k;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (real) v = *reinterpret_cast<const uint4*>(x + row * k + blk * 32 + 8 * q);
+  const uint32_t h[4] = {v.x, v.y, v.z, v.w};
+  uint32_t amax = 0;
+  uint32_t nonfinite = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t b = (h[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
+    const uint32_t mag = b & 0x7FFFu;  // bf16 magnitudes order as integers
+    amax = mag > amax ? mag : amax;
+    nonfinite |= (b & 0x7F80u) == 0x7F80u;
+  }
+#pragma unroll
+  for (int d = 1; d < 4; d <<= 1) {
+    const uint32_t oa = static_cast<uint32_t>(__shfl_xor(static_cast<int>(amax), d, 4));
+    const uint32_t on = static_cast<uint32_t>(__shfl_xor(static_cast<int>(nonfinite), d, 4));
+    amax = oa > amax ? oa : amax;
+    nonfinite |= on;
+  }
   uint32_t sbyte = 0;
-  if (blk * 32 < k) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + row * k + blk * 32);
-    uint32_t h[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = src[q];
-      h[4 * q] = v.x;
-      h[4 * q + 1] = v.y;
-      h[4 * q + 2] = v.z;
-      h[4 * q + 3] = v.w;
-    }
-    uint32_t amax = 0;
-    bool nonfinite = false;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t b = (h[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
-      const uint32_t mag = b & 0x7FFFu;  // bf16 magnitudes order as integers
-      amax = mag > amax ? mag : amax;
-      nonfinite |= (b & 0x7F80u) == 0x7F80u;
-    }
+  uint32_t word = 0;
+  if (real) {
     if (nonfinite) {
       sbyte = 0xFFu;
     } else {
@@ -99,19 +100,19 @@ __global__ __launch_bounds__(kQuantThreads) void act_quant_kernel(const uint16_t
       sbyte = e > 2 ? e - 2 : 0;
       const float inv = __uint_as_float((254u - sbyte) << 23);  // 1 / X = 2^(127 - sbyte)
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
+      for (int j = 0; j < 8; ++j) {
         const uint32_t b = (h[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
-        const float v = __uint_as_float((b & 0x7FFFu) << 16) * inv;
+        const float f = __uint_as_float((b & 0x7FFFu) << 16) * inv;
         // Nearest E2M1 magnitude: each threshold is a midpoint of the grid;
         // at a midpoint the even code wins (> keeps the lower, >= takes the upper).
-        uint32_t c = (v > 0.25f) + (v >= 0.75f) + (v > 1.25f) + (v >= 1.75f) + (v > 2.5f) + (v >= 3.5f) + (v > 5.0f);
+        uint32_t c = (f > 0.25f) + (f >= 0.75f) + (f > 1.25f) + (f >= 1.75f) + (f > 2.5f) + (f >= 3.5f) + (f > 5.0f);
         c |= (b >> 12) & 8u;  // sign
-        w[j / 8] |= c << (4 * (j % 8));
+        word |= c << (4 * j);
       }
     }
   }
-  *reinterpret_cast<uint4*>(codes + row * (act_k / 2) + blk * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-  scales[i] = static_cast<uint8_t>(sbyte);  // [row group][block][16]
+  *reinterpret_cast<uint32_t*>(codes + row * (act_k / 2) + blk * 16 + 4 * q) = word;
+  if (q == 0) scales[((row >> 4) * kb + blk) * kRowGroup + (row & 15)] = static_cast<uint8_t>(sbyte);
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +342,7 @@ void w4a4_gemm_kernel(const MfmaArgs a) {
   tile_coords<kW4BM>(pl, pl.dp_tiles + u / pl.splits, m0, n0);
   run_tile(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
            static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
-  store_tile_partial_staged<kW4BM, kThreads>(a, u, wave, acc, reinterpret_cast<char*>(st));
+  store_tile_partial_staged<kW4BM, kThreads, 128>(a, u, wave, acc, reinterpret_cast<char*>(st));
 }
 
 }  // namespace
@@ -349,7 +350,7 @@ void w4a4_gemm_kernel(const MfmaArgs a) {
 hipError_t launch_act_quant_mxfp4(const uint16_t* x, int m, int k, uint8_t* codes, uint8_t* scales,
                                   hipStream_t stream) {
   const int64_t act_k = w4a4_act_k(k);
-  const int64_t items = (m + kRowGroup - 1) / kRowGroup * kRowGroup * (act_k / 32);
+  const int64_t items = static_cast<int64_t>(m) * (act_k / 32) * 4;
   const unsigned blocks = static_cast<unsigned>((items + kQuantThreads - 1) / kQuantThreads);
   hipLaunchKernelGGL(act_quant_kernel, dim3(blocks), dim3(kQuantThreads), 0, stream, x, m, k, act_k, codes, scales);
   return hipGetLastError();
