@@ -58,7 +58,8 @@ __device__ __forceinline__ int dp_tile_of(const GemmPlan& pl, int bid) {
 // rows a store instruction touches start in different banks), and the
 // workgroup then writes whole rows, 16 contiguous bytes per lane (measured
 // on MI355X for the W4A4 GEMM at m = 1024: the direct stores cost about a
-// third of the kernel's time).  `lds` is the workgroup's stage memory, free
+// third of the kernel's time; the W4A16 GEMM at m = 1024 likewise).  `lds` is
+// the workgroup's stage memory, free
 // once the K loop is done; every wave's K loop must have finished reading it
 // and no copy into it may be in flight.
 constexpr int kStageYRow = kGemmBN * 2 + 16;  // bytes per staged bf16 row

@@ -17,7 +17,10 @@
 // Stages are copied global -> LDS by the load-to-LDS path
 // (global_load_lds_dwordx4: each lane's 16 bytes land at lane * 16 after a
 // wave-uniform base), so no registers carry them; three stage buffers keep two
-// stages in flight while the third is consumed.
+// stages in flight while the third is consumed.  The K loop is one body with
+// the buffer index computed; results leave through LDS as whole rows
+// (gemm_common.hpp), which with a loop unrolled over the three buffers made
+// the compiler spill the accumulators.
 //
 // A wave decodes only its own 64 weight rows, so each code is decoded once per
 // workgroup per activation-row block.  E2M1 * S is exact in bf16 (at most 6
@@ -68,6 +71,11 @@ struct alignas(16) Stage {
   uint4 b[kBChunks];
   uint4 s[Cfg<FMT>::kSChunks];
 };
+
+static_assert(kGemmBM * kStageYRow <= kStages * sizeof(Stage<kFmtNvfp4>) &&
+                  64 * kStagePRow <= kStages * sizeof(Stage<kFmtNvfp4>) &&
+                  sizeof(Stage<kFmtNvfp4>) == sizeof(Stage<kFmtMxfp4>),
+              "result staging fits in the stage buffers");
 
 union Frag {
   bf16x8_t v;
@@ -337,8 +345,7 @@ __device__ __forceinline__ float act_silu(float v) { return v * __builtin_amdgcn
 // acc = the (m0, n0) tile's sums over K steps [k_begin, k_end).
 template <int FMT>
 __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t n0, int k_begin, int k_end,
-                                         Stage<FMT>& st0, Stage<FMT>& st1, Stage<FMT>& st2,
-                                         f32x16_t (&acc)[4][2]) {
+                                         Stage<FMT> (&st)[kStages], f32x16_t (&acc)[4][2]) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
@@ -359,9 +366,9 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
   const Copier<FMT> cp(a, m0, n0, t, wave);
   // Prologue: three stages in flight, wait for the first, read its codes
   // and step-0 fragments.
-  cp.issue(static_cast<int64_t>(k_begin) * kGemmBK, k_begin == ragged_ks, st0, wave);
-  if (k_begin + 1 < k_end) cp.issue(static_cast<int64_t>(k_begin + 1) * kGemmBK, k_begin + 1 == ragged_ks, st1, wave);
-  if (k_begin + 2 < k_end) cp.issue(static_cast<int64_t>(k_begin + 2) * kGemmBK, k_begin + 2 == ragged_ks, st2, wave);
+  cp.issue(static_cast<int64_t>(k_begin) * kGemmBK, k_begin == ragged_ks, st[0], wave);
+  if (k_begin + 1 < k_end) cp.issue(static_cast<int64_t>(k_begin + 1) * kGemmBK, k_begin + 1 == ragged_ks, st[1], wave);
+  if (k_begin + 2 < k_end) cp.issue(static_cast<int64_t>(k_begin + 2) * kGemmBK, k_begin + 2 == ragged_ks, st[2], wave);
   if (k_begin + 2 < k_end)
     wait_stages_barrier<2>(wave);
   else if (k_begin + 1 < k_end)
@@ -369,15 +376,16 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
   else
     wait_stages_barrier<0>(wave);
   Regs<FMT> r;
-  read_codes<FMT>(st0, wr0, lh, r);
-  read_x<FMT>(st0, xr0, lh, 0, r.xf);
+  read_codes<FMT>(st[0], wr0, lh, r);
+  read_x<FMT>(st[0], xr0, lh, 0, r.xf);
   decode_step<FMT>(r, 0, r.wf);
-  for (int ks = k_begin; ks < k_end; ks += kStages) {
-    pipeline_step<FMT>(cp, ks, k_end, ragged_ks, st0, st1, wave, xr0, wr0, lh, r, acc);
-    if (ks + 1 >= k_end) break;
-    pipeline_step<FMT>(cp, ks + 1, k_end, ragged_ks, st1, st2, wave, xr0, wr0, lh, r, acc);
-    if (ks + 2 >= k_end) break;
-    pipeline_step<FMT>(cp, ks + 2, k_end, ragged_ks, st2, st0, wave, xr0, wr0, lh, r, acc);
+  // One loop body with the buffer index computed, so the accumulators keep
+  // their registers from one stage to the next.
+  int cur = 0;
+  for (int ks = k_begin; ks < k_end; ++ks) {
+    const int nxt = cur == kStages - 1 ? 0 : cur + 1;
+    pipeline_step<FMT>(cp, ks, k_end, ragged_ks, st[cur], st[nxt], wave, xr0, wr0, lh, r, acc);
+    cur = nxt;
   }
 }
 
@@ -389,58 +397,17 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(const MfmaArgs a) {
-  __shared__ Stage<FMT> st0, st1, st2;
+  __shared__ Stage<FMT> st[kStages];
   const GemmPlan& pl = a.plan;
   const int bid = blockIdx.x;
-  const int t = threadIdx.x;
-  const int wave = t >> 6;
-  const int lane = t & 63;
-  const int l32 = lane & 31;
-  const int lh = lane >> 5;
-  const int wm = wave / 4;
-  const int wn = wave % 4;
+  const int wave = threadIdx.x >> 6;
   f32x16_t acc[4][2];
 
   if (bid < pl.dp_tiles) {
-    // XCD-aware order: workgroup b runs on XCD b % 8, so XCD x gets the ids
-    // x, x + 8, ...; give it the contiguous run of tiles starting at
-    // x * q + min(x, r) (q = tiles / 8, r = tiles % 8).
-    const int xcd = bid % 8;
-    const int q = pl.dp_tiles / 8;
-    const int rr = pl.dp_tiles % 8;
     int64_t m0, n0;
-    tile_coords(pl, xcd * q + (xcd < rr ? xcd : rr) + bid / 8, m0, n0);
-    run_tile<FMT>(a, m0, n0, 0, pl.ksteps, st0, st1, st2, acc);
-    // Scale by the projection's global scale and store bf16 y, four
-    // consecutive output columns (weight rows) of one activation row per lane
-    // and (i, j, e4).
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        int h;
-        const int64_t col = out_col(a, n0 + wn * 64 + 32 * j + 8 * e4 + 4 * lh, h);
-        if (col < 0) continue;
-        const float g = a.gscale[h];
-        const int64_t lr = col - static_cast<int64_t>(h) * a.n_proj;
-        const bool vec = lr + 4 <= a.n_proj && ((col | a.ldy) & 3) == 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t m = m0 + wm * 128 + 32 * i + l32;
-          if (m >= a.m) continue;
-          uint16_t* dst = a.y + m * a.ldy + col;
-          const float v0 = acc[i][j][4 * e4] * g, v1 = acc[i][j][4 * e4 + 1] * g;
-          const float v2 = acc[i][j][4 * e4 + 2] * g, v3 = acc[i][j][4 * e4 + 3] * g;
-          if (vec) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(f32x2_to_bf16x2_rne(v0, v1), f32x2_to_bf16x2_rne(v2, v3));
-          } else {
-            const float w[4] = {v0, v1, v2, v3};
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2)
-              if (lr + q2 < a.n_proj) dst[q2] = f32_to_bf16_rne(w[q2]);
-          }
-        }
-      }
+    tile_coords(pl, dp_tile_of(pl, bid), m0, n0);
+    run_tile<FMT>(a, m0, n0, 0, pl.ksteps, st, acc);
+    store_tile_bf16_staged<kGemmBM, kThreads>(a, m0, n0, wave, acc, reinterpret_cast<char*>(st));
   }
 
   const int units = pl.tail_tiles * pl.splits;
@@ -451,23 +418,8 @@ void gemm_kernel(const MfmaArgs a) {
   int64_t m0, n0;
   tile_coords(pl, pl.dp_tiles + u / pl.splits, m0, n0);
   run_tile<FMT>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
-                static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st0, st1, st2, acc);
-  // Store the K range's fp32 partial tile [x row][weight row].  Buffer
-  // stores: with plain stores the compiler's register allocation of the K
-  // loop spills.
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      a.partial + static_cast<int64_t>(u) * kGemmBM * kGemmBN, 0, kGemmBM * kGemmBN * 4, kBufferRsrcWord3);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int mr = wm * 128 + 32 * i + l32;
-        const int nr = wn * 64 + 32 * j + 8 * e4 + 4 * lh;
-        const f32x4_t v = {acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rsrc, (mr * kGemmBN + nr) * 4, 0, 0);
-      }
+                static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
+  store_tile_partial_staged<kGemmBM, kThreads, 64>(a, u, wave, acc, reinterpret_cast<char*>(st));
 }
 
 // Split-K finish of the tail tiles: y = G * (partial_0 + partial_1 + ... +
