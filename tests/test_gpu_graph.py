@@ -91,3 +91,39 @@ def test_graph_replay_argmax():
         torch.cuda.synchronize()
         assert got == idx.cpu().numpy().tolist(), rep
 
+
+
+def test_graph_replay_w4a4():
+    # The W4A4 call (quantizer, tile GEMM with K-split tail tiles, reduce)
+    # replayed from a graph with new activations gives the eager call's bytes.
+    n, k, m = 5120, 5120, 300
+    packed, scales, _ = synth.packed_weight(synth.TINY, 72, n, k, MX)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, MX)
+    ws = torch.full((fp4.fp4_w4a4_workspace_bytes(m, n, k),), 0xA5, dtype=torch.uint8, device=DEV)
+    x = x_dev(synth.activations(synth.TINY, m, k))
+    y_graph = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    y_eager = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    info = fp4.fp4_dispatch_info()
+
+    def call(y):
+        fp4.fp4_w4a4_linear(x, pc, ps, n, y=y, workspace=ws, info=info)
+
+    call(y_graph)
+    torch.cuda.synchronize()
+    assert info.kernel == 4 and info.splits > 1
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(y_graph)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    for rep in range(4):
+        xb = rng.standard_normal((m, k), dtype=np.float32)
+        x.copy_(x_dev((xb.view(np.uint32) >> 16).astype(np.uint16)))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = y_host_bits(y_graph)
+        call(y_eager)
+        want = y_host_bits(y_eager)
+        assert np.array_equal(got, want), "replay %d differs from eager" % rep
+        call(y_eager)
+        torch.cuda.synchronize()

@@ -93,6 +93,7 @@ def _w4a4_ref(xbits, packed, scales, k):
 
 @pytest.mark.parametrize("m,n,k", [
     (1, 512, 256),       # one tile, no split
+    (5, 256, 32),        # the smallest k: one 32-code block, 96 zero-padded codes per stage
     (17, 300, 1056),     # ragged rows, columns and k (k % 128 = 32)
     (130, 1000, 4096),   # 1 x 4 tiles, ragged both ways
     (16, 5120, 17408),   # 20 tiles: tail split along K
