@@ -69,21 +69,10 @@ size_t argmax_workspace_for(int m, int n, int k, int fmt, size_t* keys_offset) {
   return base + static_cast<size_t>(rows_total / decode_tile_rows(m, rows_total)) * m * 8;
 }
 
-// Tile plan of a SwiGLU gate_up call at m > 8: every tile runs as a one-split
-// "tail" unit, so its float32 results reach the reduce launch, which pairs
-// gate and up rows and applies the activation.
-fp4::GemmPlan act_gemm_plan(int m, int64_t rows_total, int k) {
-  fp4::GemmPlan p = fp4::gemm_plan(m, rows_total, k);
-  p.dp_tiles = 0;
-  p.tail_tiles = p.tiles;
-  p.splits = 1;
-  return p;
-}
-
 size_t act_workspace_for(int m, int n_half, int k, int fmt) {
   if (m <= fp4::kGemvMaxM) return workspace_for(m, n_half, k, fmt, 2);
   const int64_t rows_total = 2 * fp4::round_up(n_half, fp4::kRowAlign);
-  return static_cast<size_t>(fp4::gemm_workspace_bytes(act_gemm_plan(m, rows_total, k)));
+  return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
 }
 
 // Shared body of fp4_w4a16_linear, fp4_w4a16_gate_up, fp4_w4a16_linear_argmax
@@ -180,7 +169,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
     a.act = act;
-    a.plan = act ? act_gemm_plan(m, a.rows_total, k) : fp4::gemm_plan(m, a.rows_total, k);
+    a.plan = fp4::gemm_plan(m, a.rows_total, k);
     if (a.plan.tail_tiles > 0) a.partial = static_cast<float*>(ws);
     hipError_t e = fp4::launch_mfma(a, fmt, stream, &grid, &block);
     if (e != hipSuccess) return FP4_EHIP;

@@ -66,10 +66,12 @@ constexpr int kStageYRow = kGemmBN * 2 + 16;  // bytes per staged bf16 row
 constexpr int kStagePRow = kGemmBN * 4 + 16;  // bytes per staged fp32 row
 
 // bf16 y of a whole tile: BM x 256 outputs, scaled by the projection's global
-// scale (a tile never spans two projections: n_proj_pad is a multiple of 256).
-template <int BM, int THREADS>
+// scale (a tile never spans two projections: n_proj_pad is a multiple of 256),
+// staged PASS rows at a time (PASS a multiple of 32 dividing 128, or 128).
+template <int BM, int THREADS, int PASS = BM>
 __device__ __forceinline__ void store_tile_bf16_staged(const MfmaArgs& a, int64_t m0, int64_t n0, int wave,
                                                        const f32x16_t (&acc)[4][2], char* lds) {
+  static_assert(PASS % 32 == 0 && (128 % PASS == 0 || PASS % 128 == 0) && BM % PASS == 0, "pass rows");
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int l32 = lane & 31;
@@ -78,36 +80,111 @@ __device__ __forceinline__ void store_tile_bf16_staged(const MfmaArgs& a, int64_
   const int wn = wave % 4;
   const int h = static_cast<int>(n0 / a.n_proj_pad);
   const float g = h == 0 ? a.gscale[0] : a.gscale[1];
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int row = wm * 128 + 32 * i + l32;
-        const int col = wn * 64 + 32 * j + 8 * e4 + 4 * lh;
-        *reinterpret_cast<uint2*>(lds + row * kStageYRow + 2 * col) =
-            make_uint2(f32x2_to_bf16x2_rne(acc[i][j][4 * e4] * g, acc[i][j][4 * e4 + 1] * g),
-                       f32x2_to_bf16x2_rne(acc[i][j][4 * e4 + 2] * g, acc[i][j][4 * e4 + 3] * g));
-      }
-  __syncthreads();
   // Row r, 8-column chunk c: thread t takes chunk t % 32 of rows t / 32 + (THREADS / 32) q.
   const int c8 = t & 31;
   const int64_t lr = n0 - static_cast<int64_t>(h) * a.n_proj_pad + 8 * c8;  // column within the projection
   const int64_t col = static_cast<int64_t>(h) * a.n_proj + lr;
   const bool vec = lr + 8 <= a.n_proj && ((col | a.ldy) & 7) == 0;
-  if (lr >= a.n_proj) return;
-  for (int row = t >> 5; row < BM; row += THREADS / 32) {
-    const int64_t m = m0 + row;
-    if (m >= a.m) break;
-    const uint4 v = *reinterpret_cast<const uint4*>(lds + row * kStageYRow + 16 * c8);
-    uint16_t* dst = a.y + m * a.ldy + col;
-    if (vec) {
-      *reinterpret_cast<uint4*>(dst) = v;
-    } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      for (int e = 0; e < 8 && lr + e < a.n_proj; ++e) dst[e] = static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
+  for (int pass = 0; pass < BM / PASS; ++pass) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row0 = wm * 128 + 32 * i;  // first tile row of fragment row i (wave-uniform)
+      if (row0 / PASS != pass) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int row = row0 - pass * PASS + l32;
+          const int cc = wn * 64 + 32 * j + 8 * e4 + 4 * lh;
+          *reinterpret_cast<uint2*>(lds + row * kStageYRow + 2 * cc) =
+              make_uint2(f32x2_to_bf16x2_rne(acc[i][j][4 * e4] * g, acc[i][j][4 * e4 + 1] * g),
+                         f32x2_to_bf16x2_rne(acc[i][j][4 * e4 + 2] * g, acc[i][j][4 * e4 + 3] * g));
+        }
+    }
+    __syncthreads();
+    if (lr >= a.n_proj) continue;
+    for (int row = t >> 5; row < PASS; row += THREADS / 32) {
+      const int64_t m = m0 + pass * PASS + row;
+      if (m >= a.m) break;
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + row * kStageYRow + 16 * c8);
+      uint16_t* dst = a.y + m * a.ldy + col;
+      if (vec) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int e = 0; e < 8 && lr + e < a.n_proj; ++e) dst[e] = static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
+// SwiGLU gate_up on the interleaved weight (prepared row R is gate row
+// 16 (R / 32) + R % 16 when R % 32 < 16, else the up row with that index):
+// y[m][16 (R / 32) + R % 16] = bf16(silu(g) * u) with g, u the float32 sums
+// times their projections' global scales, for the tile's BM x 128 outputs.
+// The scaled sums are staged PASS rows at a time as float32 rows; each thread
+// then forms 8 consecutive outputs of one row (8 gate and the matching 8 up
+// values) and writes them as 16 bytes.  silu(v) = v / (1 + e^-v), computed as
+// the reduce launch computes it for split tiles.
+template <int BM, int THREADS, int PASS>
+__device__ __forceinline__ void store_tile_swiglu_staged(const MfmaArgs& a, int64_t m0, int64_t n0, int wave,
+                                                         const f32x16_t (&acc)[4][2], char* lds) {
+  static_assert(PASS % 32 == 0 && (128 % PASS == 0 || PASS % 128 == 0) && BM % PASS == 0, "pass rows");
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int l32 = lane & 31;
+  const int lh = lane >> 5;
+  const int wm = wave / 4;
+  const int wn = wave % 4;
+  // Output chunk of a thread: columns 8 c8 .. 8 c8 + 7 of the tile's 128.
+  const int c8 = t & 15;
+  const int g0 = 32 * (c8 >> 1) + 8 * (c8 & 1);  // staged column of its first gate value; up is 16 further
+  const int64_t col = n0 / 2 + 8 * c8;
+  const bool vec = col + 8 <= a.n_proj && ((col | a.ldy) & 7) == 0;
+  for (int pass = 0; pass < BM / PASS; ++pass) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row0 = wm * 128 + 32 * i;  // first tile row of fragment row i (wave-uniform)
+      if (row0 / PASS != pass) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int row = row0 - pass * PASS + l32;
+          const int cc = wn * 64 + 32 * j + 8 * e4 + 4 * lh;  // 4 rows of one 16-row gate or up group
+          const float g = (cc & 31) < 16 ? a.gscale[0] : a.gscale[1];
+          const f32x4_t v = {acc[i][j][4 * e4] * g, acc[i][j][4 * e4 + 1] * g, acc[i][j][4 * e4 + 2] * g,
+                             acc[i][j][4 * e4 + 3] * g};
+          *reinterpret_cast<f32x4_t*>(lds + row * kStagePRow + 4 * cc) = v;
+        }
+    }
+    __syncthreads();
+    if (col >= a.n_proj) continue;
+    for (int row = t >> 4; row < PASS; row += THREADS / 16) {
+      const int64_t m = m0 + pass * PASS + row;
+      if (m >= a.m) break;
+      const char* src = lds + row * kStagePRow + 4 * g0;
+      const f32x4_t ga = *reinterpret_cast<const f32x4_t*>(src);
+      const f32x4_t gb = *reinterpret_cast<const f32x4_t*>(src + 16);
+      const f32x4_t ua = *reinterpret_cast<const f32x4_t*>(src + 64);
+      const f32x4_t ub = *reinterpret_cast<const f32x4_t*>(src + 80);
+      const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      const float uv[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float y0 = gv[2 * q] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[2 * q])) * uv[2 * q];
+        const float y1 = gv[2 * q + 1] * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[2 * q + 1])) * uv[2 * q + 1];
+        w[q] = f32x2_to_bf16x2_rne(y0, y1);
+      }
+      uint16_t* dst = a.y + m * a.ldy + col;
+      if (vec) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        for (int e = 0; e < 8 && col + e < a.n_proj; ++e) dst[e] = static_cast<uint16_t>(w[e / 2] >> (16 * (e & 1)));
+      }
     }
   }
 }

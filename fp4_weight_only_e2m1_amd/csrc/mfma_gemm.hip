@@ -394,7 +394,7 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
 // tail_tiles x splits workgroups of the grid -- the last round, after their
 // own tile if they have one -- then each compute split u % splits of tail tile
 // u / splits and store it as an fp32 partial, which tail_reduce_kernel adds.
-template <int FMT>
+template <int FMT, bool ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(const MfmaArgs a) {
   __shared__ Stage<FMT> st[kStages];
@@ -407,7 +407,10 @@ void gemm_kernel(const MfmaArgs a) {
     int64_t m0, n0;
     tile_coords(pl, dp_tile_of(pl, bid), m0, n0);
     run_tile<FMT>(a, m0, n0, 0, pl.ksteps, st, acc);
-    store_tile_bf16_staged<kGemmBM, kThreads>(a, m0, n0, wave, acc, reinterpret_cast<char*>(st));
+    if constexpr (ACT)
+      store_tile_swiglu_staged<kGemmBM, kThreads, 64>(a, m0, n0, wave, acc, reinterpret_cast<char*>(st));
+    else
+      store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM>(a, m0, n0, wave, acc, reinterpret_cast<char*>(st));
   }
 
   const int units = pl.tail_tiles * pl.splits;
@@ -515,10 +518,17 @@ hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* gri
   const dim3 grid(static_cast<unsigned>(p.dp_tiles > units ? p.dp_tiles : units));
   if (grid_out) *grid_out = dim3(grid.x, static_cast<unsigned>(units));
   if (block_out) *block_out = block;
-  if (fmt == kFmtNvfp4)
-    hipLaunchKernelGGL(gemm_kernel<kFmtNvfp4>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(gemm_kernel<kFmtMxfp4>, grid, block, 0, stream, a);
+  if (fmt == kFmtNvfp4) {
+    if (a.act)
+      hipLaunchKernelGGL((gemm_kernel<kFmtNvfp4, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<kFmtNvfp4, false>), grid, block, 0, stream, a);
+  } else {
+    if (a.act)
+      hipLaunchKernelGGL((gemm_kernel<kFmtMxfp4, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<kFmtMxfp4, false>), grid, block, 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || units == 0) return e;
   return launch_tail_reduce(a, kGemmBM, stream);

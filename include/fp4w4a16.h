@@ -177,10 +177,11 @@ int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k,
  * rows in groups of 16 (prepared row R: gate row 16 (R / 32) + R % 16 when
  * R % 32 < 16, else the up row with that index) so that both operands of an
  * output are computed by one workgroup.  m <= 8: the decode kernels form y in
- * their epilogue; m > 8: the tile GEMM leaves every tile's float32 results in
- * the workspace and its reduce launch forms y.  Workspace:
- * fp4_swiglu_workspace_bytes (at m > 8, m x 2 n_half x 4 bytes, rounded to
- * tiles).  silu uses the hardware exp and reciprocal (about 1 ulp each).
+ * their epilogue; m > 8: the tile GEMM forms y in the epilogue of every whole
+ * tile, and its reduce launch forms y for the tail tiles split along K.
+ * Workspace: fp4_swiglu_workspace_bytes (the split-K partials and flags of
+ * the same plan as fp4_w4a16_gate_up).  silu uses the hardware exp and
+ * reciprocal (about 1 ulp each).
  * Reading taken: the pages name the MLP block after the fused gate_up but not
  * its activation; silu(gate) * up is the gated MLP of the model family they
  * run ("MXFP4 decode-graph + gate_up FUSION default-ON", vllm.cpp PR #54,

@@ -91,6 +91,8 @@ def test_workspace_bytes_policy():
     assert fp4.fp4_workspace_bytes(65536, 256, 5120, NV) == 0      # 512 tiles: one full round, no tail
     assert fp4.fp4_workspace_bytes(200, 300, 256, NV) == 0         # 4 K steps: too short to split
     assert fp4.fp4_workspace_bytes(9, 1024, 12288, MX, 2) == _prefill_workspace(9, 1024, 12288, 2)
+    # SwiGLU gate_up: the same plan as the fused gate_up.
+    assert fp4.fp4_swiglu_workspace_bytes(1024, 12288, 4096, MX) == fp4.fp4_workspace_bytes(1024, 12288, 4096, MX, 2)
     # The lm_head GEMV splits K=5120 (5 slabs of 1024) in two; splitting never depends on m.
     # splits * m * rows fp32 partials, then one 8-byte flag per (64-row tile, split).
     ws1 = fp4.fp4_workspace_bytes(1, 248320, 5120, NV)
