@@ -186,7 +186,8 @@ size_t w4a4_workspace_for(int m, int n_proj, int k, int projections, size_t* par
   const int64_t act = fp4::round_up(fp4::w4a4_act_code_bytes(m, k) + fp4::w4a4_act_scale_bytes(m, k), 256);
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
   if (partial_offset) *partial_offset = static_cast<size_t>(act);
-  return static_cast<size_t>(act + fp4::gemm_workspace_bytes(fp4::w4a4_plan(m, rows_total, k), fp4::kW4BM));
+  const fp4::GemmPlan p = fp4::w4a4_plan(m, rows_total, k);
+  return static_cast<size_t>(act + (p.mhalf ? 0 : fp4::gemm_workspace_bytes(p, fp4::kW4BM)));
 }
 
 // Shared body of fp4_w4a4_linear and fp4_w4a4_gate_up.
@@ -227,14 +228,15 @@ int run_w4a4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_
   a.ldy = static_cast<int64_t>(n_proj) * projections;
   a.gscale[0] = a.gscale[1] = 1.0f;
   a.plan = fp4::w4a4_plan(m, a.rows_total, k);
-  if (a.plan.tail_tiles > 0) a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + partial_offset);
+  if (a.plan.tail_tiles > 0 && !a.plan.mhalf)
+    a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + partial_offset);
   a.xq_codes = xq_codes;
   a.xq_scales = xq_scales;
   a.act_k = fp4::w4a4_act_k(k);
   dim3 grid, block;
   if (fp4::launch_w4a4(a, stream, &grid, &block) != hipSuccess) return FP4_EHIP;
-  if (info) *info = fp4_dispatch_info{4, a.plan.splits, static_cast<int>(grid.x), static_cast<int>(grid.y),
-                                      static_cast<int>(block.x)};
+  if (info) *info = fp4_dispatch_info{4, a.plan.mhalf ? 1 : a.plan.splits, static_cast<int>(grid.x),
+                                      static_cast<int>(grid.y), static_cast<int>(block.x)};
   return FP4_OK;
 }
 

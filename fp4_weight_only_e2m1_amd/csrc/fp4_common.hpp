@@ -175,12 +175,14 @@ struct GemmPlan {
   int tail_tiles;  // tiles computed as `splits` K ranges
   int splits;
   int ksteps;      // K steps of a whole tile
+  int mhalf;       // W4A4 only: tail tiles run as two halves of their rows over all of K instead
 };
 
 // Plan over tiles of `bm` activation rows, K steps of `step_k` codes, `slots`
 // resident workgroups, splits of at least `min_split_steps`.
 inline GemmPlan tile_plan(int m, int64_t rows_total, int k, int step_k, int min_split_steps, int bm, int slots) {
   GemmPlan p;
+  p.mhalf = 0;
   p.m_tiles = static_cast<int>((m + bm - 1) / bm);
   p.n_tiles = static_cast<int>(rows_total / kGemmBN);
   p.tiles = p.m_tiles * p.n_tiles;
@@ -214,8 +216,13 @@ constexpr int kW4BK = 128;
 constexpr int kW4Slots = kTargetCUs;
 constexpr int kW4MinSplitSteps = 4;
 
+// Where the plan would split each tail tile in two along K, the W4A4 GEMM
+// runs the two 128-row halves of the tile over all of K instead: the same
+// MFMA work per workgroup, no partial tiles to write, read back and add.
 inline GemmPlan w4a4_plan(int m, int64_t rows_total, int k) {
-  return tile_plan(m, rows_total, k, kW4BK, kW4MinSplitSteps, kW4BM, kW4Slots);
+  GemmPlan p = tile_plan(m, rows_total, k, kW4BK, kW4MinSplitSteps, kW4BM, kW4Slots);
+  if (p.splits == 2) p.mhalf = 1;
+  return p;
 }
 
 // The quantized activations of a W4A4 call: codes [act_rows][act_k / 2]

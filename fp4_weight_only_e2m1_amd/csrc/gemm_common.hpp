@@ -68,9 +68,11 @@ constexpr int kStagePRow = kGemmBN * 4 + 16;  // bytes per staged fp32 row
 // bf16 y of a whole tile: BM x 256 outputs, scaled by the projection's global
 // scale (a tile never spans two projections: n_proj_pad is a multiple of 256),
 // staged PASS rows at a time (PASS a multiple of 32 dividing 128, or 128).
-template <int BM, int THREADS, int PASS = BM>
+// FI: 32-row activation fragments per wave (wave w = 4 wm + wn holds tile rows
+// [32 FI wm, +32 FI)).
+template <int BM, int THREADS, int PASS = BM, int FI = 4>
 __device__ __forceinline__ void store_tile_bf16_staged(const MfmaArgs& a, int64_t m0, int64_t n0, int wave,
-                                                       const f32x16_t (&acc)[4][2], char* lds) {
+                                                       const f32x16_t (&acc)[FI][2], char* lds) {
   static_assert(PASS % 32 == 0 && (128 % PASS == 0 || PASS % 128 == 0) && BM % PASS == 0, "pass rows");
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -88,8 +90,8 @@ __device__ __forceinline__ void store_tile_bf16_staged(const MfmaArgs& a, int64_
   for (int pass = 0; pass < BM / PASS; ++pass) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row0 = wm * 128 + 32 * i;  // first tile row of fragment row i (wave-uniform)
+    for (int i = 0; i < FI; ++i) {
+      const int row0 = wm * 32 * FI + 32 * i;  // first tile row of fragment row i (wave-uniform)
       if (row0 / PASS != pass) continue;
 #pragma unroll
       for (int j = 0; j < 2; ++j)

@@ -124,17 +124,21 @@ constexpr int kThreads = 512;
 constexpr int kStages = 4;
 constexpr int kRowBytes = kW4BK / 2;             // code bytes of a row per stage
 constexpr int kRowChunks = kRowBytes / 16;       // 16-byte chunks (32-code blocks) of a row per stage
-constexpr int kAChunks = kW4BM * kRowChunks;     // activation code chunks per stage
+constexpr int kAChunks = kW4BM * kRowChunks;     // activation code chunks per stage (whole tile)
 constexpr int kBChunks = kGemmBN * kRowChunks;   // weight code chunks per stage
-constexpr int kAPer = kAChunks / kThreads;
 constexpr int kBPer = kBChunks / kThreads;
-static_assert(kAChunks % kThreads == 0 && kBChunks % kThreads == 0, "stage split");
+// Activation code chunks each thread copies per stage when the tile has
+// 64 FI activation rows (FI = 4: whole tiles; FI = 2: the half tiles of the
+// tail).
+template <int FI>
+constexpr int kAPer = 64 * FI * kRowChunks / kThreads;
+static_assert(kAChunks % kThreads == 0 && kBChunks % kThreads == 0 && kAPer<2> >= 1, "stage split");
 static_assert(kThreads == 64 * 8 && kW4BM == 256 && kGemmBN == 256, "two rows of four waves");
 
 struct alignas(16) Stage {
   uint4 a[kAChunks];
   uint4 b[kBChunks];
-  uint4 sa[64];  // [row group 0..15][block 0..3][16 rows]
+  uint4 sa[64];  // [row group 0..15][block 0..3][16 rows] (half tiles: row groups 0..7, then a repeat)
   uint4 sb[64];  // [row group 0..15][block 0..3][16 rows]
 };
 static_assert(kStages * sizeof(Stage) <= 160 * 1024, "one workgroup of four stages per CU");
@@ -152,12 +156,13 @@ static_assert(kW4BM * kStageYRow <= kStages * sizeof(Stage) && 128 * kStagePRow 
 // 32-bit offsets from wave-uniform bases that advance with the stage.  Wave 0
 // also copies the weight scales, wave 1 the activation scales (one 16-byte
 // chunk per lane: row group lane / 4, block lane % 4 of the stage).
+template <int FI>
 struct Copier {
   const uint8_t* xa;  // activation code row m0
   const uint8_t* wb;  // weight code row n0
   const uint8_t* xs;  // activation scale row group m0 / 16
   const uint8_t* ws;  // weight scale row group n0 / 16
-  uint32_t aoff[kAPer], boff[kBPer], soff;
+  uint32_t aoff[kAPer<FI>], boff[kBPer], soff;
 
   __device__ __forceinline__ Copier(const MfmaArgs& a, int64_t m0, int64_t n0, int t, int wave) {
     const int64_t arow = a.act_k / 2;
@@ -167,7 +172,7 @@ struct Copier {
     xs = a.xq_scales + (m0 / kRowGroup) * (a.act_k / 32) * kRowGroup;
     ws = a.scales + (n0 / kRowGroup) * a.ksegs * kRowGroup;
 #pragma unroll
-    for (int i = 0; i < kAPer; ++i) {
+    for (int i = 0; i < kAPer<FI>; ++i) {
       const int p = i * kThreads + t;
       const int r = p >> 2;
       const int c = (p & 3) ^ ((r >> 2) & 3);
@@ -181,8 +186,12 @@ struct Copier {
       boff[i] = static_cast<uint32_t>(r * brow + 16 * c);
     }
     const int lane = t & 63;
+    // Activation scales: 4 FI row groups; with FI = 2 lanes 32..63 repeat
+    // lanes 0..31 (into chunks 32..63, unused), so no lane reads past the
+    // tile's rows.
+    const int arg = FI == 4 ? lane >> 2 : (lane & 31) >> 2;
     soff = wave == 0 ? static_cast<uint32_t>((lane >> 2) * a.ksegs * kRowGroup + 16 * (lane & 3))
-                     : static_cast<uint32_t>((lane >> 2) * (a.act_k / 32) * kRowGroup + 16 * (lane & 3));
+                     : static_cast<uint32_t>(arg * (a.act_k / 32) * kRowGroup + 16 * (lane & 3));
   }
 
   __device__ __forceinline__ void issue(int ks, Stage& sb, int wave) const {
@@ -190,7 +199,7 @@ struct Copier {
     const uint32_t lb = lds_addr(sb.b) + 64 * 16 * wave;
     const uint8_t* xb = xa + static_cast<int64_t>(ks) * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kAPer; ++i) copy16_sbase(xb, aoff[i], la + i * kThreads * 16);
+    for (int i = 0; i < kAPer<FI>; ++i) copy16_sbase(xb, aoff[i], la + i * kThreads * 16);
     const uint8_t* wbk = wb + static_cast<int64_t>(ks) * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) copy16_sbase(wbk, boff[i], lb + i * kThreads * 16);
@@ -203,19 +212,20 @@ struct Copier {
 
 // Wait until this wave's copies of all but the newest `STAGES` stages have
 // landed, then join the workgroup barrier.
-template <int STAGES>
+template <int STAGES, int FI>
 __device__ __forceinline__ void wait_stages_barrier(int wave) {
   if (wave < 2)
-    wait_vm_barrier<STAGES * (kAPer + kBPer + 1)>();
+    wait_vm_barrier<STAGES * (kAPer<FI> + kBPer + 1)>();
   else
-    wait_vm_barrier<STAGES * (kAPer + kBPer)>();
+    wait_vm_barrier<STAGES * (kAPer<FI> + kBPer)>();
 }
 
-// The operands of one 64-k MFMA step: 2 weight and 4 activation fragments
+// The operands of one 64-k MFMA step: 2 weight and FI activation fragments
 // with their scale bytes.
+template <int FI>
 struct Frags {
-  i32x8_t w[2], x[4];
-  int ws[2], xs[4];
+  i32x8_t w[2], x[FI];
+  int ws[2], xs[FI];
 };
 
 __device__ __forceinline__ i32x8_t as_operand(uint4 q) {
@@ -232,7 +242,8 @@ struct LaneOffsets {
   uint32_t xo, wo, xso, wso;
 };
 
-__device__ __forceinline__ void read_step(const Stage& st, const LaneOffsets& o, Frags& f) {
+template <int FI>
+__device__ __forceinline__ void read_step(const Stage& st, const LaneOffsets& o, Frags<FI>& f) {
   const char* ca = reinterpret_cast<const char*>(st.a) + o.xo;
   const char* cb = reinterpret_cast<const char*>(st.b) + o.wo;
   const uint8_t* sa = reinterpret_cast<const uint8_t*>(st.sa) + o.xso;
@@ -243,15 +254,16 @@ __device__ __forceinline__ void read_step(const Stage& st, const LaneOffsets& o,
     f.ws[j] = sb[128 * j];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FI; ++i) {
     f.x[i] = as_operand(*reinterpret_cast<const uint4*>(ca + 2048 * i));
     f.xs[i] = sa[128 * i];
   }
 }
 
-__device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][2]) {
+template <int FI>
+__device__ __forceinline__ void mfma_step(const Frags<FI>& f, f32x16_t (&acc)[FI][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.w[j], f.x[i], acc[i][j], 4, 4, 0, f.ws[j], 0,
@@ -263,14 +275,15 @@ __device__ __forceinline__ void mfma_step(const Frags& f, f32x16_t (&acc)[4][2])
 // (and, through the barrier, for every wave to be done with stage ks - 1,
 // whose buffer it then refills with stage ks + 3) and runs the stage's two
 // MFMA steps.  One loop body, so the accumulators keep their registers.
+template <int FI>
 __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t n0, int k_begin, int k_end,
-                                         Stage (&st)[kStages], f32x16_t (&acc)[4][2]) {
+                                         Stage (&st)[kStages], f32x16_t (&acc)[FI][2]) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int l32 = lane & 31;
   const int lh = lane >> 5;
-  const int xr0 = (wave >> 2) * 128 + l32;  // activation row of this lane's first fragment
+  const int xr0 = (wave >> 2) * 32 * FI + l32;  // activation row of this lane's first fragment
   const int wr0 = (wave & 3) * 64 + l32;     // weight row of this lane's first fragment
   // Step s uses block c = 2 s + lh of the stage, in slot c ^ sw of the row
   // (sw = (row >> 2) & 3, the same for every row of this lane): step 1's
@@ -286,12 +299,12 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
   o1.xso = o0.xso + 32;
   o1.wso = o0.wso + 32;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  const Copier cp(a, m0, n0, t, wave);
+  const Copier<FI> cp(a, m0, n0, t, wave);
   cp.issue(k_begin, st[0], wave);
   if (k_begin + 1 < k_end) cp.issue(k_begin + 1, st[1], wave);
   if (k_begin + 2 < k_end) cp.issue(k_begin + 2, st[2], wave);
@@ -300,14 +313,14 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
     // Stage ks landed when at most the copies of the (up to two) stages
     // after it are in flight.
     if (ks + 2 < k_end)
-      wait_stages_barrier<2>(wave);
+      wait_stages_barrier<2, FI>(wave);
     else if (ks + 1 < k_end)
-      wait_stages_barrier<1>(wave);
+      wait_stages_barrier<1, FI>(wave);
     else
-      wait_stages_barrier<0>(wave);
+      wait_stages_barrier<0, FI>(wave);
     const int fill = buf == 0 ? kStages - 1 : buf - 1;
     if (ks + 3 < k_end) cp.issue(ks + 3, st[fill], wave);
-    Frags f;
+    Frags<FI> f;
     read_step(st[buf], o0, f);
     mfma_step(f, acc);
     read_step(st[buf], o1, f);
@@ -326,23 +339,34 @@ void w4a4_gemm_kernel(const MfmaArgs a) {
   const GemmPlan& pl = a.plan;
   const int bid = blockIdx.x;
   const int wave = threadIdx.x >> 6;
-  f32x16_t acc[4][2];
+  char* lds = reinterpret_cast<char*>(st);
   if (bid < pl.dp_tiles) {
+    f32x16_t acc[4][2];
     int64_t m0, n0;
     tile_coords<kW4BM>(pl, dp_tile_of(pl, bid), m0, n0);
-    run_tile(a, m0, n0, 0, pl.ksteps, st, acc);
-    store_tile_bf16_staged<kW4BM, kThreads>(a, m0, n0, wave, acc, reinterpret_cast<char*>(st));
+    run_tile<4>(a, m0, n0, 0, pl.ksteps, st, acc);
+    store_tile_bf16_staged<kW4BM, kThreads, kW4BM>(a, m0, n0, wave, acc, lds);
   }
   const int units = pl.tail_tiles * pl.splits;
   const int u = bid - (static_cast<int>(gridDim.x) - units);
   if (u < 0) return;
   __syncthreads();  // the stage buffers are reused
-  const int split = u % pl.splits;
   int64_t m0, n0;
   tile_coords<kW4BM>(pl, pl.dp_tiles + u / pl.splits, m0, n0);
-  run_tile(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
-           static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
-  store_tile_partial_staged<kW4BM, kThreads, 128>(a, u, wave, acc, reinterpret_cast<char*>(st));
+  if (pl.mhalf) {
+    // Half u % 2 of the tail tile's rows, over all of K, stored as bf16 y.
+    m0 += (kW4BM / 2) * (u % 2);
+    if (m0 >= a.m) return;
+    f32x16_t acc[2][2];
+    run_tile<2>(a, m0, n0, 0, pl.ksteps, st, acc);
+    store_tile_bf16_staged<kW4BM / 2, kThreads, kW4BM / 2, 2>(a, m0, n0, wave, acc, lds);
+    return;
+  }
+  const int split = u % pl.splits;
+  f32x16_t acc[4][2];
+  run_tile<4>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
+              static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
+  store_tile_partial_staged<kW4BM, kThreads, 128>(a, u, wave, acc, lds);
 }
 
 }  // namespace
@@ -365,7 +389,7 @@ hipError_t launch_w4a4(const MfmaArgs& a, hipStream_t stream, dim3* grid_out, di
   if (block_out) *block_out = block;
   hipLaunchKernelGGL(w4a4_gemm_kernel, grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || units == 0) return e;
+  if (e != hipSuccess || units == 0 || p.mhalf) return e;
   return launch_tail_reduce(a, kW4BM, stream);
 }
 

@@ -217,7 +217,9 @@ def _w4a4_workspace(m, n, k, projections=1):
     tiles = -(-m // 256) * (projections * (-(-n // 256) * 256) // 256)
     tail = tiles % 256
     s = min(256 // tail, -(-k // 128) // 4) if tail else 1
-    return act + (0 if s <= 1 else tail * s * 256 * 256 * 4)
+    # Where that split is two ways, the tail tiles run as two 128-row halves
+    # over all of K instead, with no partials.
+    return act + (0 if s <= 2 else tail * s * 256 * 256 * 4)
 
 
 def test_w4a4_sizes():
@@ -225,9 +227,11 @@ def test_w4a4_sizes():
     assert fp4.fp4_w4a4_act_bytes(1024, 4096) == (1024 * 2048, 1024 * 128)
     assert fp4.fp4_w4a4_act_bytes(257, 4064) == (512 * 2048, 512 * 128)
     assert fp4.fp4_w4a4_workspace_bytes(1, 512, 256) == _w4a4_workspace(1, 512, 256) == 34816
-    # gate_up at m = 1024: 384 tiles, the 128 past the first round split in two.
+    # gate_up at m = 1024: 384 tiles; the 128 past the first round run as row halves.
     assert fp4.fp4_w4a4_workspace_bytes(1024, 12288, 4096, 2) == _w4a4_workspace(1024, 12288, 4096, 2)
-    assert fp4.fp4_w4a4_workspace_bytes(1024, 12288, 4096, 2) == 2228224 + 128 * 2 * 262144
+    assert fp4.fp4_w4a4_workspace_bytes(1024, 12288, 4096, 2) == 2228224
+    # k = 5120, n = 17408: 16 tail tiles split 10 ways along K.
+    assert fp4.fp4_w4a4_workspace_bytes(1024, 17408, 5120) == 1024 * 2560 + 1024 * 160 + 16 * 10 * 262144
     for m, n, k in [(16, 17408, 5120), (4096, 17408, 5120), (300, 300, 1056), (9, 5120, 17408)]:
         assert fp4.fp4_w4a4_workspace_bytes(m, n, k) == _w4a4_workspace(m, n, k), (m, n, k)
     assert fp4.fp4_w4a4_workspace_bytes(0, 512, 256) == 0

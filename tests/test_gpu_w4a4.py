@@ -99,6 +99,7 @@ def _w4a4_ref(xbits, packed, scales, k):
     (16, 5120, 17408),   # 20 tiles: tail split along K
     (300, 768, 2080),    # 2 x 3 tiles, k % 128 = 32
     (600, 1024, 512),    # 3 x 4 tiles, ragged rows
+    (300, 15360, 1024),  # 120 tail tiles run as row halves; the second half of each lower tile is past m
 ])
 def test_w4a4_linear_parity(m, n, k):
     packed, scales, _ = synth.packed_weight(synth.TINY, 80, n, k, MX)
@@ -159,7 +160,8 @@ def test_w4a4_prefill_gate_up_shape_sampled():
     xbits = synth.activations(synth.GATE_UP, m, k)
     info = fp4.fp4_dispatch_info()
     y = y_host(fp4.fp4_w4a4_gate_up(x_dev(xbits), pc, ps, n_half, info=info))
-    assert info.kernel == 4 and info.splits == 2
+    # 384 tiles: 256 whole, then the 128 tail tiles as 256 row halves over all of K.
+    assert info.kernel == 4 and info.splits == 1 and (info.grid_x, info.grid_y) == (256, 256)
     rows = sample_rows(m, 24, seed=3)
     cols = sample_rows(n_half, 96, seed=4)
     x_s = oracle.bf16_bits_to_f32(xbits[rows])
