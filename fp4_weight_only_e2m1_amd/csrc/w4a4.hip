@@ -341,11 +341,19 @@ void w4a4_gemm_kernel(const MfmaArgs a) {
   const int wave = threadIdx.x >> 6;
   char* lds = reinterpret_cast<char*>(st);
   if (bid < pl.dp_tiles) {
-    f32x16_t acc[4][2];
     int64_t m0, n0;
     tile_coords<kW4BM>(pl, dp_tile_of(pl, bid), m0, n0);
-    run_tile<4>(a, m0, n0, 0, pl.ksteps, st, acc);
-    store_tile_bf16_staged<kW4BM, kThreads, kW4BM>(a, m0, n0, wave, acc, lds);
+    if (a.m - m0 <= kW4BM / 2) {
+      // A tile with at most 128 rows below m (small m, or the last row of
+      // tiles): only its upper half is computed.
+      f32x16_t acc[2][2];
+      run_tile<2>(a, m0, n0, 0, pl.ksteps, st, acc);
+      store_tile_bf16_staged<kW4BM / 2, kThreads, kW4BM / 2, 2>(a, m0, n0, wave, acc, lds);
+    } else {
+      f32x16_t acc[4][2];
+      run_tile<4>(a, m0, n0, 0, pl.ksteps, st, acc);
+      store_tile_bf16_staged<kW4BM, kThreads, kW4BM>(a, m0, n0, wave, acc, lds);
+    }
   }
   const int units = pl.tail_tiles * pl.splits;
   const int u = bid - (static_cast<int>(gridDim.x) - units);
