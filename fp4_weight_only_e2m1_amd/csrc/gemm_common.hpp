@@ -192,9 +192,11 @@ __device__ __forceinline__ void store_tile_swiglu_staged(const MfmaArgs& a, int6
 }
 
 // fp32 partial tile of tail unit u, row-major [BM][256], staged PASS rows at
-// a time (PASS a multiple of 32 dividing 128, or 128).
+// a time (PASS a multiple of 32 dividing 128, or 128).  Only the rows below m
+// are written (the reduce launch reads no others): at small m the partials
+// would otherwise outweigh the weights.
 template <int BM, int THREADS, int PASS>
-__device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int u, int wave,
+__device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int u, int64_t m0, int wave,
                                                           const f32x16_t (&acc)[4][2], char* lds) {
   static_assert(PASS % 32 == 0 && (128 % PASS == 0 || PASS % 128 == 0) && BM % PASS == 0, "pass rows");
   const int t = threadIdx.x;
@@ -204,7 +206,9 @@ __device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int
   const int wm = wave / 4;
   const int wn = wave % 4;
   float* dst = a.partial + static_cast<int64_t>(u) * BM * kGemmBN;
+  const int64_t valid = a.m - m0;  // tile rows below m
   for (int pass = 0; pass < BM / PASS; ++pass) {
+    if (pass * PASS >= valid) break;  // uniform: no barrier is skipped by part of the workgroup
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -222,7 +226,7 @@ __device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int
     }
     __syncthreads();
     // PASS rows x 64 chunks of 4 floats: thread t takes chunk t % 64 of rows t / 64 + (THREADS / 64) q.
-    for (int row = t >> 6; row < PASS; row += THREADS / 64)
+    for (int row = t >> 6; row < PASS && pass * PASS + row < valid; row += THREADS / 64)
       *reinterpret_cast<f32x4_t*>(dst + (pass * PASS + row) * kGemmBN + 4 * (t & 63)) =
           *reinterpret_cast<const f32x4_t*>(lds + row * kStagePRow + 16 * (t & 63));
   }

@@ -422,7 +422,7 @@ void gemm_kernel(const MfmaArgs a) {
   tile_coords(pl, pl.dp_tiles + u / pl.splits, m0, n0);
   run_tile<FMT>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
                 static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
-  store_tile_partial_staged<kGemmBM, kThreads, 64>(a, u, wave, acc, reinterpret_cast<char*>(st));
+  store_tile_partial_staged<kGemmBM, kThreads, 64>(a, u, m0, wave, acc, reinterpret_cast<char*>(st));
 }
 
 // Split-K finish of the tail tiles: y = G * (partial_0 + partial_1 + ... +

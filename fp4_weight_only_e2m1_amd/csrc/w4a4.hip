@@ -374,7 +374,7 @@ void w4a4_gemm_kernel(const MfmaArgs a) {
   f32x16_t acc[4][2];
   run_tile<4>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
               static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
-  store_tile_partial_staged<kW4BM, kThreads, 128>(a, u, wave, acc, lds);
+  store_tile_partial_staged<kW4BM, kThreads, 128>(a, u, m0, wave, acc, lds);
 }
 
 }  // namespace
