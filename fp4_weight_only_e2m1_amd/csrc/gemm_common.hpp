@@ -69,7 +69,9 @@ constexpr int kStagePRow = kGemmBN * 4 + 16;  // bytes per staged fp32 row
 // scale (a tile never spans two projections: n_proj_pad is a multiple of 256),
 // staged PASS rows at a time (PASS a multiple of 32 dividing 128, or 128).
 // FI: 32-row activation fragments per wave (wave w = 4 wm + wn holds tile rows
-// [32 FI wm, +32 FI)).
+// [32 FI wm, +32 FI)).  Rows of the tile no wave holds are staged with stale
+// LDS bytes; callers choose FI so that they lie at or past m and are never
+// stored.
 template <int BM, int THREADS, int PASS = BM, int FI = 4>
 __device__ __forceinline__ void store_tile_bf16_staged(const MfmaArgs& a, int64_t m0, int64_t n0, int wave,
                                                        const f32x16_t (&acc)[FI][2], char* lds) {
@@ -129,9 +131,9 @@ __device__ __forceinline__ void store_tile_bf16_staged(const MfmaArgs& a, int64_
 // then forms 8 consecutive outputs of one row (8 gate and the matching 8 up
 // values) and writes them as 16 bytes.  silu(v) = v / (1 + e^-v), computed as
 // the reduce launch computes it for split tiles.
-template <int BM, int THREADS, int PASS>
+template <int BM, int THREADS, int PASS, int FI = 4>
 __device__ __forceinline__ void store_tile_swiglu_staged(const MfmaArgs& a, int64_t m0, int64_t n0, int wave,
-                                                         const f32x16_t (&acc)[4][2], char* lds) {
+                                                         const f32x16_t (&acc)[FI][2], char* lds) {
   static_assert(PASS % 32 == 0 && (128 % PASS == 0 || PASS % 128 == 0) && BM % PASS == 0, "pass rows");
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -147,8 +149,8 @@ __device__ __forceinline__ void store_tile_swiglu_staged(const MfmaArgs& a, int6
   for (int pass = 0; pass < BM / PASS; ++pass) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row0 = wm * 128 + 32 * i;  // first tile row of fragment row i (wave-uniform)
+    for (int i = 0; i < FI; ++i) {
+      const int row0 = wm * 32 * FI + 32 * i;  // first tile row of fragment row i (wave-uniform)
       if (row0 / PASS != pass) continue;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -195,9 +197,9 @@ __device__ __forceinline__ void store_tile_swiglu_staged(const MfmaArgs& a, int6
 // a time (PASS a multiple of 32 dividing 128, or 128).  Only the rows below m
 // are written (the reduce launch reads no others): at small m the partials
 // would otherwise outweigh the weights.
-template <int BM, int THREADS, int PASS>
+template <int BM, int THREADS, int PASS, int FI = 4>
 __device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int u, int64_t m0, int wave,
-                                                          const f32x16_t (&acc)[4][2], char* lds) {
+                                                          const f32x16_t (&acc)[FI][2], char* lds) {
   static_assert(PASS % 32 == 0 && (128 % PASS == 0 || PASS % 128 == 0) && BM % PASS == 0, "pass rows");
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -211,8 +213,8 @@ __device__ __forceinline__ void store_tile_partial_staged(const MfmaArgs& a, int
     if (pass * PASS >= valid) break;  // uniform: no barrier is skipped by part of the workgroup
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row0 = wm * 128 + 32 * i;  // first tile row of fragment row i (wave-uniform)
+    for (int i = 0; i < FI; ++i) {
+      const int row0 = wm * 32 * FI + 32 * i;  // first tile row of fragment row i (wave-uniform)
       if (row0 / PASS != pass) continue;
 #pragma unroll
       for (int j = 0; j < 2; ++j)

@@ -96,18 +96,22 @@ __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ ((r >>
 // bank groups 2 r + slot (mod 16): rows r and r + 8 take opposite slots.
 __device__ __forceinline__ int b_slot(int r, int h) { return 2 * r + (h ^ ((r >> 3) & 1)); }
 
-// Load-to-LDS copies a wave issues per stage: x and codes, plus one for the
-// scales in wave 0.
-constexpr int kLoadsPerStage = kAPer + kBPer;
+// FI: 32-row activation blocks a tile computes (4 = all 128 rows; 1 or 2 for
+// calls with m <= 32 or 64, whose single row of tiles has no more rows).
+// Load-to-LDS copies a wave issues per stage: x (FI per thread for 32 FI
+// rows) and codes, plus one for the scales in wave 0.
+template <int FI>
+constexpr int kLoadsPerStage = FI * kAPer / 4 + kBPer;
+static_assert(kAPer == 4, "one x chunk per thread per 32-row block");
 
 // Wait until this wave's copies of all but the newest `stages` stages have
 // landed, then join the workgroup barrier.
-template <int STAGES>
+template <int STAGES, int FI>
 __device__ __forceinline__ void wait_stages_barrier(int wave) {
   if (wave == 0)
-    wait_vm_barrier<STAGES * (kLoadsPerStage + 1)>();
+    wait_vm_barrier<STAGES * (kLoadsPerStage<FI> + 1)>();
   else
-    wait_vm_barrier<STAGES * kLoadsPerStage>();
+    wait_vm_barrier<STAGES * kLoadsPerStage<FI>>();
 }
 
 // The stage copies of one workgroup tile.  Chunk positions in LDS are fixed by
@@ -121,15 +125,16 @@ __device__ __forceinline__ void wait_stages_barrier(int wave) {
 //   code k on.  So they are bf16 zeros, whatever x holds beyond its row.
 // Every lane issues every copy, so each wave has the same number in flight
 // per stage.
-template <int FMT>
+template <int FMT, int FI>
 struct Copier {
   static constexpr int P = Cfg<FMT>::P;
+  static constexpr int kXPer = FI * kAPer / 4;  // x chunks per thread per stage
   const uint16_t* xt;    // x row m0
   const uint8_t* ct;     // code row n0
   const uint8_t* st;     // scale row group n0 / 16
   const uint8_t* zeros;  // 16 zero bytes: code row n0 from code k on
-  uint32_t xoff[kAPer], coff[kBPer], soff;
-  int xk[kAPer];         // first k of this lane's x chunks within a stage
+  uint32_t xoff[kXPer], coff[kBPer], soff;
+  int xk[kXPer];         // first k of this lane's x chunks within a stage
   int k;
   uint32_t lds_wave_a, lds_wave_b;  // this wave's chunk offsets within a stage
 
@@ -141,7 +146,7 @@ struct Copier {
     st = a.scales + (n0 / kRowGroup) * a.ksegs * kRowGroup * P;
     zeros = ct + a.k / 2;
 #pragma unroll
-    for (int i = 0; i < kAPer; ++i) {
+    for (int i = 0; i < kXPer; ++i) {
       const int p = i * kThreads + t;
       const int r = p >> 3;
       const int c = (p & 7) ^ ((r >> 1) & 7);
@@ -172,10 +177,10 @@ struct Copier {
     if (!ragged) {
       const uint16_t* xb = xt + k0;
 #pragma unroll
-      for (int i = 0; i < kAPer; ++i) copy16_sbase(xb, xoff[i], la + i * kThreads * 16);
+      for (int i = 0; i < kXPer; ++i) copy16_sbase(xb, xoff[i], la + i * kThreads * 16);
     } else {
 #pragma unroll
-      for (int i = 0; i < kAPer; ++i) {
+      for (int i = 0; i < kXPer; ++i) {
         const void* src = k0 + xk[i] < k ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(xt + k0) + xoff[i])
                                          : static_cast<const void*>(zeros);
         copy16_vaddr(src, la + i * kThreads * 16);
@@ -218,16 +223,16 @@ constexpr int kSchedDsRead = 0x100;
 // Register state a wave carries from one stage to the next: the stage's
 // codes and scale bytes of its 2 x 32 weight rows, and, for the MFMA step
 // about to run, the 4 x fragments and 2 decoded weight fragments.
-template <int FMT>
+template <int FMT, int FI>
 struct Regs {
   uint4 code[2];
   uint32_t sc[2];
-  Frag xf[4], wf[2];
+  Frag xf[FI], wf[2];
 };
 
 // Read this wave's codes and scale bytes of a stage.
-template <int FMT>
-__device__ __forceinline__ void read_codes(const Stage<FMT>& st, int wr0, int lh, Regs<FMT>& r) {
+template <int FMT, int FI>
+__device__ __forceinline__ void read_codes(const Stage<FMT>& st, int wr0, int lh, Regs<FMT, FI>& r) {
   constexpr int P = Cfg<FMT>::P;
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(st.s);
 #pragma unroll
@@ -242,11 +247,11 @@ __device__ __forceinline__ void read_codes(const Stage<FMT>& st, int wr0, int lh
   }
 }
 
-// Read the x fragments of MFMA step kk (4 activation row blocks).
-template <int FMT>
-__device__ __forceinline__ void read_x(const Stage<FMT>& st, int xr0, int lh, int kk, Frag (&f)[4]) {
+// Read the x fragments of MFMA step kk (FI activation row blocks).
+template <int FMT, int FI>
+__device__ __forceinline__ void read_x(const Stage<FMT>& st, int xr0, int lh, int kk, Frag (&f)[FI]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FI; ++i) {
     const uint4 q = st.a[a_slot(xr0 + 32 * i, 4 * lh + kk)];
     f[i].u[0] = q.x;
     f[i].u[1] = q.y;
@@ -256,8 +261,8 @@ __device__ __forceinline__ void read_x(const Stage<FMT>& st, int xr0, int lh, in
 }
 
 // Decode the weight fragments of MFMA step kk from the carried codes.
-template <int FMT>
-__device__ __forceinline__ void decode_step(const Regs<FMT>& r, int kk, Frag (&f)[2]) {
+template <int FMT, int FI>
+__device__ __forceinline__ void decode_step(const Regs<FMT, FI>& r, int kk, Frag (&f)[2]) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint32_t word = kk == 0 ? r.code[j].x : kk == 1 ? r.code[j].y : kk == 2 ? r.code[j].z : r.code[j].w;
@@ -266,9 +271,10 @@ __device__ __forceinline__ void decode_step(const Regs<FMT>& r, int kk, Frag (&f
   }
 }
 
-__device__ __forceinline__ void mfma_step(const Frag (&wf)[2], const Frag (&xf)[4], f32x16_t (&acc)[4][2]) {
+template <int FI>
+__device__ __forceinline__ void mfma_step(const Frag (&wf)[2], const Frag (&xf)[FI], f32x16_t (&acc)[FI][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j].v, xf[i].v, acc[i][j], 0, 0, 0);
@@ -283,12 +289,12 @@ constexpr int kDecodeValu = FMT == kFmtMxfp4 ? 8 : 36;
 // The run ends with a full scheduling barrier: left free, the scheduler
 // merges consecutive steps and issues MFMAs on the same accumulator back to
 // back, each then waiting for the previous one's result.
-template <int FMT, int READS>
+template <int FMT, int READS, int MFMAS>
 __device__ __forceinline__ void schedule_step() {
-  constexpr int kValuPerMfma = (kDecodeValu<FMT> + 7) / 8;
+  constexpr int kValuPerMfma = (kDecodeValu<FMT> + MFMAS - 1) / MFMAS;
   __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
+  for (int q = 0; q < MFMAS; ++q) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
   }
@@ -304,37 +310,37 @@ __device__ __forceinline__ void schedule_step() {
 // ks + 1 (whose copies the wait before the barrier saw land) is complete in
 // `nxt`, so its codes and step-0 fragments are read and decoded under the
 // last MFMAs -- the next stage starts with its MFMAs ready to issue.
-template <int FMT>
-__device__ __forceinline__ void pipeline_step(const Copier<FMT>& cp, int ks, int k_end, int ragged_ks,
+template <int FMT, int FI>
+__device__ __forceinline__ void pipeline_step(const Copier<FMT, FI>& cp, int ks, int k_end, int ragged_ks,
                                               Stage<FMT>& cur, const Stage<FMT>& nxt, int wave, int xr0, int wr0,
-                                              int lh, Regs<FMT>& r, f32x16_t (&acc)[4][2]) {
-  Frag xn[4], wn[2];
+                                              int lh, Regs<FMT, FI>& r, f32x16_t (&acc)[FI][2]) {
+  Frag xn[FI], wn[2];
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
-    read_x<FMT>(cur, xr0, lh, kk + 1, xn);
-    decode_step<FMT>(r, kk + 1, wn);
-    mfma_step(r.wf, r.xf, acc);
-    schedule_step<FMT, 4>();
+    read_x<FMT, FI>(cur, xr0, lh, kk + 1, xn);
+    decode_step<FMT, FI>(r, kk + 1, wn);
+    mfma_step<FI>(r.wf, r.xf, acc);
+    schedule_step<FMT, FI, 2 * FI>();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.xf[i] = xn[i];
+    for (int i = 0; i < FI; ++i) r.xf[i] = xn[i];
     r.wf[0] = wn[0];
     r.wf[1] = wn[1];
   }
   // Stage ks + 1 landed when at most the copies of stage ks + 2 are in flight.
   if (ks + 2 < k_end)
-    wait_stages_barrier<1>(wave);
+    wait_stages_barrier<1, FI>(wave);
   else
-    wait_stages_barrier<0>(wave);
+    wait_stages_barrier<0, FI>(wave);
   if (ks + 3 < k_end) cp.issue(static_cast<int64_t>(ks + 3) * kGemmBK, ks + 3 == ragged_ks, cur, wave);
   // Unconditional, so it shares a basic block (and the interleaved schedule)
   // with the MFMAs; after the last stage it reads a stale buffer, unused.
-  read_codes<FMT>(nxt, wr0, lh, r);
-  read_x<FMT>(nxt, xr0, lh, 0, xn);
-  decode_step<FMT>(r, 0, wn);
-  mfma_step(r.wf, r.xf, acc);
-  schedule_step<FMT, 8>();
+  read_codes<FMT, FI>(nxt, wr0, lh, r);
+  read_x<FMT, FI>(nxt, xr0, lh, 0, xn);
+  decode_step<FMT, FI>(r, 0, wn);
+  mfma_step<FI>(r.wf, r.xf, acc);
+  schedule_step<FMT, 4 + FI, 2 * FI>();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.xf[i] = xn[i];
+  for (int i = 0; i < FI; ++i) r.xf[i] = xn[i];
   r.wf[0] = wn[0];
   r.wf[1] = wn[1];
 }
@@ -343,9 +349,9 @@ __device__ __forceinline__ void pipeline_step(const Copier<FMT>& cp, int ks, int
 __device__ __forceinline__ float act_silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // acc = the (m0, n0) tile's sums over K steps [k_begin, k_end).
-template <int FMT>
+template <int FMT, int FI>
 __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t n0, int k_begin, int k_end,
-                                         Stage<FMT> (&st)[kStages], f32x16_t (&acc)[4][2]) {
+                                         Stage<FMT> (&st)[kStages], f32x16_t (&acc)[FI][2]) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
@@ -357,34 +363,34 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
   const int ragged_ks = (a.k % kGemmBK) != 0 ? a.plan.ksteps - 1 : -1;
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const Copier<FMT> cp(a, m0, n0, t, wave);
+  const Copier<FMT, FI> cp(a, m0, n0, t, wave);
   // Prologue: three stages in flight, wait for the first, read its codes
   // and step-0 fragments.
   cp.issue(static_cast<int64_t>(k_begin) * kGemmBK, k_begin == ragged_ks, st[0], wave);
   if (k_begin + 1 < k_end) cp.issue(static_cast<int64_t>(k_begin + 1) * kGemmBK, k_begin + 1 == ragged_ks, st[1], wave);
   if (k_begin + 2 < k_end) cp.issue(static_cast<int64_t>(k_begin + 2) * kGemmBK, k_begin + 2 == ragged_ks, st[2], wave);
   if (k_begin + 2 < k_end)
-    wait_stages_barrier<2>(wave);
+    wait_stages_barrier<2, FI>(wave);
   else if (k_begin + 1 < k_end)
-    wait_stages_barrier<1>(wave);
+    wait_stages_barrier<1, FI>(wave);
   else
-    wait_stages_barrier<0>(wave);
-  Regs<FMT> r;
-  read_codes<FMT>(st[0], wr0, lh, r);
-  read_x<FMT>(st[0], xr0, lh, 0, r.xf);
-  decode_step<FMT>(r, 0, r.wf);
+    wait_stages_barrier<0, FI>(wave);
+  Regs<FMT, FI> r;
+  read_codes<FMT, FI>(st[0], wr0, lh, r);
+  read_x<FMT, FI>(st[0], xr0, lh, 0, r.xf);
+  decode_step<FMT, FI>(r, 0, r.wf);
   // One loop body with the buffer index computed, so the accumulators keep
   // their registers from one stage to the next.
   int cur = 0;
   for (int ks = k_begin; ks < k_end; ++ks) {
     const int nxt = cur == kStages - 1 ? 0 : cur + 1;
-    pipeline_step<FMT>(cp, ks, k_end, ragged_ks, st[cur], st[nxt], wave, xr0, wr0, lh, r, acc);
+    pipeline_step<FMT, FI>(cp, ks, k_end, ragged_ks, st[cur], st[nxt], wave, xr0, wr0, lh, r, acc);
     cur = nxt;
   }
 }
@@ -394,23 +400,24 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
 // tail_tiles x splits workgroups of the grid -- the last round, after their
 // own tile if they have one -- then each compute split u % splits of tail tile
 // u / splits and store it as an fp32 partial, which tail_reduce_kernel adds.
-template <int FMT, bool ACT>
+template <int FMT, bool ACT, int FI>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(const MfmaArgs a) {
   __shared__ Stage<FMT> st[kStages];
   const GemmPlan& pl = a.plan;
   const int bid = blockIdx.x;
   const int wave = threadIdx.x >> 6;
-  f32x16_t acc[4][2];
+  f32x16_t acc[FI][2];
+  char* lds = reinterpret_cast<char*>(st);
 
   if (bid < pl.dp_tiles) {
     int64_t m0, n0;
     tile_coords(pl, dp_tile_of(pl, bid), m0, n0);
-    run_tile<FMT>(a, m0, n0, 0, pl.ksteps, st, acc);
+    run_tile<FMT, FI>(a, m0, n0, 0, pl.ksteps, st, acc);
     if constexpr (ACT)
-      store_tile_swiglu_staged<kGemmBM, kThreads, 64>(a, m0, n0, wave, acc, reinterpret_cast<char*>(st));
+      store_tile_swiglu_staged<kGemmBM, kThreads, 64, FI>(a, m0, n0, wave, acc, lds);
     else
-      store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM>(a, m0, n0, wave, acc, reinterpret_cast<char*>(st));
+      store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, FI>(a, m0, n0, wave, acc, lds);
   }
 
   const int units = pl.tail_tiles * pl.splits;
@@ -420,9 +427,9 @@ void gemm_kernel(const MfmaArgs a) {
   const int split = u % pl.splits;
   int64_t m0, n0;
   tile_coords(pl, pl.dp_tiles + u / pl.splits, m0, n0);
-  run_tile<FMT>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
-                static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
-  store_tile_partial_staged<kGemmBM, kThreads, 64>(a, u, m0, wave, acc, reinterpret_cast<char*>(st));
+  run_tile<FMT, FI>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
+                    static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
+  store_tile_partial_staged<kGemmBM, kThreads, 64, FI>(a, u, m0, wave, acc, lds);
 }
 
 // Split-K finish of the tail tiles: y = G * (partial_0 + partial_1 + ... +
@@ -511,6 +518,17 @@ __global__ __launch_bounds__(kReduceThreads) void tail_reduce_kernel(const MfmaA
 
 }  // namespace
 
+// The kernel instance for (format, SwiGLU epilogue, activation blocks).
+template <int FMT, bool ACT>
+void launch_gemm_fi(const MfmaArgs& a, int fi, dim3 grid, dim3 block, hipStream_t stream) {
+  if (fi == 1)
+    hipLaunchKernelGGL((gemm_kernel<FMT, ACT, 1>), grid, block, 0, stream, a);
+  else if (fi == 2)
+    hipLaunchKernelGGL((gemm_kernel<FMT, ACT, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<FMT, ACT, 4>), grid, block, 0, stream, a);
+}
+
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
   const GemmPlan& p = a.plan;
   const dim3 block(kThreads);
@@ -518,16 +536,19 @@ hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* gri
   const dim3 grid(static_cast<unsigned>(p.dp_tiles > units ? p.dp_tiles : units));
   if (grid_out) *grid_out = dim3(grid.x, static_cast<unsigned>(units));
   if (block_out) *block_out = block;
+  // A call with m <= 32 (64) has one row of tiles with at most 32 (64) rows:
+  // its tiles compute 1 (2) of their 4 activation blocks.
+  const int fi = a.m <= 32 ? 1 : a.m <= 64 ? 2 : 4;
   if (fmt == kFmtNvfp4) {
     if (a.act)
-      hipLaunchKernelGGL((gemm_kernel<kFmtNvfp4, true>), grid, block, 0, stream, a);
+      launch_gemm_fi<kFmtNvfp4, true>(a, fi, grid, block, stream);
     else
-      hipLaunchKernelGGL((gemm_kernel<kFmtNvfp4, false>), grid, block, 0, stream, a);
+      launch_gemm_fi<kFmtNvfp4, false>(a, fi, grid, block, stream);
   } else {
     if (a.act)
-      hipLaunchKernelGGL((gemm_kernel<kFmtMxfp4, true>), grid, block, 0, stream, a);
+      launch_gemm_fi<kFmtMxfp4, true>(a, fi, grid, block, stream);
     else
-      hipLaunchKernelGGL((gemm_kernel<kFmtMxfp4, false>), grid, block, 0, stream, a);
+      launch_gemm_fi<kFmtMxfp4, false>(a, fi, grid, block, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || units == 0) return e;

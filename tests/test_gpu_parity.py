@@ -112,7 +112,7 @@ def test_gemv_matches_oracle(fmt, n, k, m):
 
 
 @pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 640, 2048), (NV, 300, 1056), (MX, 256, 5120)])
-@pytest.mark.parametrize("m", [9, 16, 33, 128, 200])
+@pytest.mark.parametrize("m", [9, 16, 32, 33, 64, 65, 128, 200])  # 32 and 64 bound the 1- and 2-block tiles
 def test_mfma_matches_oracle(fmt, n, k, m):
     packed, scales, g = _quantized(fmt, n, k)
     xbits = synth.activations(synth.TINY, m, k)
