@@ -1,10 +1,11 @@
 // Tile order and result stores shared by the prefill tile GEMMs (the W4A16
 // GEMM in mfma_gemm.hip: 128 x 256 tiles, 4 waves; the W4A4 GEMM in w4a4.hip:
-// 256 x 256 tiles, 8 waves).  Wave w = 4 wm + wn holds activation rows
-// [128 wm, +128) and weight rows [64 wn, +64) of its tile as
-// acc[i][j] (i: 32-row activation block, j: 32-row weight block) in the
-// 32 x 32 MFMA result layout with the weights as the A operand: result e of
-// lane l is weight row 8 (e / 4) + 4 (l / 32) + e % 4, activation row l % 32.
+// 256 x 256 tiles, 8 waves).  Wave w = 4 wm + wn holds FI 32-row activation
+// blocks, rows [32 FI wm, +32 FI) (FI = 4 for whole tiles), and weight rows
+// [64 wn, +64) of its tile as acc[i][j] (i: activation block, j: 32-row
+// weight block) in the 32 x 32 MFMA result layout with the weights as the A
+// operand: result e of lane l is weight row 8 (e / 4) + 4 (l / 32) + e % 4,
+// activation row l % 32.
 #pragma once
 
 #include "fp4_common.hpp"
@@ -14,8 +15,6 @@ namespace fp4 {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-// Buffer descriptor word 3 for raw (unformatted) 32-bit accesses.
-constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kGroupM = 8;  // activation-row tiles per tile-order group
 
 // Output column of prepared weight row `row`, or -1 for a padding row.

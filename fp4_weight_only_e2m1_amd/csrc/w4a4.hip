@@ -29,11 +29,14 @@
 //   activation scales  16 row groups x 4 blocks x 16 rows      1 KiB
 //   weight scales      16 row groups x 4 blocks x 16 rows      1 KiB
 // copied by the load-to-LDS path into four stage buffers (136 KiB: one
-// workgroup per CU), three stages in flight.  The stage loads run at the
-// latency of the L2 and beyond, so what bounds the MFMA rate is how many
-// flops each byte in flight feeds: a 256 x 256 tile feeds 1.5 times as many
-// as a 128 x 256 one (measured on MI355X: the 128 x 256 form with two
-// workgroups per CU reached 1.9 PFLOP/s on the gate_up shape at m = 1024).
+// workgroup per CU), three stages in flight.  Results leave through LDS as
+// whole rows (gemm_common.hpp).  Tiles past the last full round of
+// workgroups either run as two 128-row halves over all of K (where the plan
+// would split them two ways along K) or as K ranges whose partials a reduce
+// launch adds; a tile with at most 128 rows below m computes its upper half
+// only.  Measured on MI355X at the gate_up shape (m = 1024): 128 x 256 tiles
+// with direct stores 1.66 PFLOP/s, 256 x 256 tiles 1.78, results through LDS
+// 2.22, tail tiles as row halves 2.64.
 //
 // Operand layout of the instruction with 4-bit A and B (checked on MI355X
 // against a host product): lane l supplies row l % 32 of A and column l % 32
