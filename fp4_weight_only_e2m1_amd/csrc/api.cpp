@@ -170,10 +170,10 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
     a.act = act;
     a.plan = fp4::gemm_plan(m, a.rows_total, k);
-    if (a.plan.tail_tiles > 0) a.partial = static_cast<float*>(ws);
+    if (a.plan.tail_tiles > 0 && !a.plan.mhalf) a.partial = static_cast<float*>(ws);
     hipError_t e = fp4::launch_mfma(a, fmt, stream, &grid, &block);
     if (e != hipSuccess) return FP4_EHIP;
-    if (info) *info = fp4_dispatch_info{1, a.plan.splits, static_cast<int>(grid.x), static_cast<int>(grid.y),
+    if (info) *info = fp4_dispatch_info{1, a.plan.mhalf ? 1 : a.plan.splits, static_cast<int>(grid.x), static_cast<int>(grid.y),
                                         static_cast<int>(block.x)};
   }
   return FP4_OK;

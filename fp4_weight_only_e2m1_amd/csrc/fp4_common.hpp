@@ -175,7 +175,7 @@ struct GemmPlan {
   int tail_tiles;  // tiles computed as `splits` K ranges
   int splits;
   int ksteps;      // K steps of a whole tile
-  int mhalf;       // W4A4 only: tail tiles run as two halves of their rows over all of K instead
+  int mhalf;       // tail tiles run as two halves of their rows over all of K instead of K ranges
 };
 
 // Plan over tiles of `bm` activation rows, K steps of `step_k` codes, `slots`
@@ -203,8 +203,13 @@ inline GemmPlan tile_plan(int m, int64_t rows_total, int k, int step_k, int min_
   return p;
 }
 
+// Where the tail tiles would be split two ways along K, they run as their
+// two 64-row halves over all of K instead (no partials, no reduce launch), for
+// calls whose tiles compute all 128 rows (m > 64).
 inline GemmPlan gemm_plan(int m, int64_t rows_total, int k) {
-  return tile_plan(m, rows_total, k, kGemmBK, kGemmMinSplitSteps, kGemmBM, kGemmSlots);
+  GemmPlan p = tile_plan(m, rows_total, k, kGemmBK, kGemmMinSplitSteps, kGemmBM, kGemmSlots);
+  if (p.splits == 2 && m > 64) p.mhalf = 1;
+  return p;
 }
 
 // W4A4 tile GEMM (MXFP4 activations x MXFP4 weights on the block-scaled
@@ -237,6 +242,7 @@ inline int64_t w4a4_act_scale_bytes(int m, int k) { return w4a4_act_rows(m) * w4
 
 // Workspace of a prefill call: fp32 partial tiles [tail_tiles][splits][bm][BN].
 inline int64_t gemm_workspace_bytes(const GemmPlan& p, int bm = kGemmBM) {
+  if (p.mhalf) return 0;
   return static_cast<int64_t>(p.tail_tiles) * p.splits * bm * kGemmBN * 4;
 }
 

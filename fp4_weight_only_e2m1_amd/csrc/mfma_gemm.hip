@@ -427,6 +427,20 @@ void gemm_kernel(const MfmaArgs a) {
   const int split = u % pl.splits;
   int64_t m0, n0;
   tile_coords(pl, pl.dp_tiles + u / pl.splits, m0, n0);
+  if constexpr (FI == 4) {
+    if (pl.mhalf) {
+      // Half u % 2 of the tail tile's rows, over all of K, stored as y.
+      m0 += (kGemmBM / 2) * split;
+      if (m0 >= a.m) return;
+      f32x16_t acc2[2][2];
+      run_tile<FMT, 2>(a, m0, n0, 0, pl.ksteps, st, acc2);
+      if constexpr (ACT)
+        store_tile_swiglu_staged<kGemmBM / 2, kThreads, 64, 2>(a, m0, n0, wave, acc2, lds);
+      else
+        store_tile_bf16_staged<kGemmBM / 2, kThreads, kGemmBM / 2, 2>(a, m0, n0, wave, acc2, lds);
+      return;
+    }
+  }
   run_tile<FMT, FI>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
                     static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
   store_tile_partial_staged<kGemmBM, kThreads, 64, FI>(a, u, m0, wave, acc, lds);
@@ -551,7 +565,7 @@ hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* gri
       launch_gemm_fi<kFmtMxfp4, false>(a, fi, grid, block, stream);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || units == 0) return e;
+  if (e != hipSuccess || units == 0 || p.mhalf) return e;
   return launch_tail_reduce(a, kGemmBM, stream);
 }
 

@@ -123,6 +123,21 @@ def test_mfma_matches_oracle(fmt, n, k, m):
     assert_close(y_host(y), y_ref, "mfma fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
 
 
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 25600, 1024, 130), (MX, 30720, 2048, 200)])
+def test_tail_row_halves(fmt, n, k, m):
+    # 200 / 240 tiles of 128 x 256: the tail's two-way K split runs as two
+    # 64-row halves per tile over all of K, with no workspace and no reduce
+    # launch; at m = 130 the second half of the lower row of tiles is past m.
+    assert fp4.fp4_workspace_bytes(m, n, k, fmt) == 0
+    packed, scales, g = _quantized(fmt, n, k, tensor=6)
+    xbits = synth.activations(synth.TINY, m, k)
+    info = fp4.fp4_dispatch_info()
+    y = _run_linear(packed, scales, g, fmt, n, k, xbits, info)
+    assert info.kernel == 1 and info.splits == 1 and info.grid_y > 0
+    y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
+    assert_close(y_host(y), y_ref, "row halves fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
+
+
 @pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 2048, 1), (MX, 512, 2048, 4), (NV, 300, 5120, 8),
                                        (NV, 512, 2048, 16), (MX, 384, 1056, 40)])
 def test_one_hot_selects_weight_column(fmt, n, k, m):
