@@ -429,6 +429,7 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t
   moe.code_stride = ps.code_bytes;
   moe.scale_stride = ps.scale_bytes;
   moe.pairs = pairs;
+  moe.experts = experts;
   dim3 grid, block;
   const hipError_t e = fp4::launch_moe_decode(a, moe, experts, x_dev, pair_tokens_dev, tokens,
                                               static_cast<uint16_t*>(workspace_dev), fmt, stream, &grid, &block);

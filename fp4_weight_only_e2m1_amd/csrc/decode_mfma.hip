@@ -379,23 +379,68 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
   decode_tile<M, FMT, RB, NB>(a, blockIdx.x, blockIdx.y, M);
 }
 
-// Grouped MoE decode: workgroup (tile, e) computes 64-row tile `tile` of
-// expert e for the routed pairs [offsets[e], offsets[e + 1]) -- their x rows
-// gathered in pair order (x_sorted) and their outputs at the same pair rows
-// of y -- 8 pairs per pass.  Expert e's prepared weight sits at e times the
-// prepared size in the stacked buffers; an expert with no pairs exits.  The
+// Grouped MoE decode: workgroup (tile, s) computes 64-row tile `tile` of
+// the s-th expert that has routed pairs (in expert order) for its pairs
+// [offsets[e], offsets[e + 1]) -- their x rows gathered in pair order
+// (x_sorted) and their outputs at the same pair rows of y -- 8 pairs per pass.
+// The grid has min(experts, pairs) slots, at least as many as experts with
+// pairs in any non-decreasing offset table, so idle experts cost no
+// workgroups; a slot past the last such expert exits.  Expert e's prepared
+// weight sits at e times the prepared size in the stacked buffers.  The
 // offsets are clamped to [0, pairs], so no routing table can make a workgroup
 // read or write outside x_sorted and y.
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs base, const MoeArgs moe) {
-  const int e = blockIdx.y;
-  // Workgroup-uniform values: kept in scalar registers (the copy bases built
-  // from them must be).
-  int p0 = __builtin_amdgcn_readfirstlane(moe.offsets[e]);
-  int p1 = __builtin_amdgcn_readfirstlane(moe.offsets[e + 1]);
+__device__ __forceinline__ void moe_clamped_range(const MoeArgs& moe, int e, int& p0, int& p1) {
+  p0 = moe.offsets[e];
+  p1 = moe.offsets[e + 1];
   p0 = p0 < 0 ? 0 : p0 > moe.pairs ? moe.pairs : p0;
   p1 = p1 < p0 ? p0 : p1 > moe.pairs ? moe.pairs : p1;
-  if (p1 <= p0) return;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs base, const MoeArgs moe) {
+  // Find the slot's expert: wave 0 reads the offsets of 256 experts at a time
+  // (4 per lane, loads issued together) and counts those with pairs until it
+  // reaches the slot's; that expert's lane leaves its pair range in LDS.
+  __shared__ int s_expert, s_p0, s_p1;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int slot = blockIdx.y;
+    int seen = 0, found = -1;
+    if (lane == 0) s_expert = -1;
+    for (int b = 0; b < moe.experts && found < 0; b += 256) {
+      int q0[4], q1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        q0[j] = q1[j] = 0;
+        const int e = b + 64 * j + lane;
+        if (e < moe.experts) moe_clamped_range(moe, e, q0[j], q1[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned long long busy = __ballot(q1[j] > q0[j]);
+        const int count = __popcll(busy);
+        if (found < 0 && slot < seen + count) {
+          // The (slot - seen)-th set bit of `busy`.
+          unsigned long long m = busy;
+          for (int r = slot - seen; r > 0; --r) m &= m - 1;
+          found = b + 64 * j + __ffsll(static_cast<long long>(m)) - 1;
+          if (b + 64 * j + lane == found) {
+            s_expert = found;
+            s_p0 = q0[j];
+            s_p1 = q1[j];
+          }
+        }
+        seen += count;
+      }
+    }
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(s_expert);
+  if (e < 0) return;
+  // Workgroup-uniform values: kept in scalar registers (the copy bases built
+  // from them must be).
+  const int p0 = __builtin_amdgcn_readfirstlane(s_p0);
+  const int p1 = __builtin_amdgcn_readfirstlane(s_p1);
   GemvArgs a = base;
   a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
   a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
@@ -452,7 +497,8 @@ hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts,
                      tokens, moe.pairs, a.k, tokens_total, x_sorted);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid(static_cast<unsigned>(a.rows_total / kDecodeTileRows), static_cast<unsigned>(experts));
+  const int slots = experts < moe.pairs ? experts : moe.pairs;
+  const dim3 grid(static_cast<unsigned>(a.rows_total / kDecodeTileRows), static_cast<unsigned>(slots));
   if (grid_out) *grid_out = grid;
   if (block_out) *block_out = dim3(kThreads);
   if (fmt == kFmtNvfp4)

@@ -150,6 +150,7 @@ struct MoeArgs {
   int64_t code_stride;       // bytes between experts' prepared codes
   int64_t scale_stride;      // bytes between experts' prepared scales
   int pairs;
+  int experts;
 };
 
 // Prefill GEMM tiling.  A workgroup of kGemmWavesM x 4 waves computes a

@@ -246,8 +246,10 @@ int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k,
  * to [0, pairs] and a token id outside [0, tokens) reads a zero row, so no
  * table can make the kernels access memory outside these buffers.  Two
  * launches: a gather of the pairs' x rows, then one workgroup per (64-row
- * tile, expert) -- experts without pairs exit at once -- on the matrix cores
- * (the m = 3..8 decode kernel, up to 8 pairs of an expert per pass).  The sum
+ * tile, expert with pairs) on the matrix cores (the m = 3..8 decode kernel,
+ * up to 8 pairs of an expert per pass); the grid has min(experts, pairs)
+ * expert slots, enough for every expert with pairs when the offsets are
+ * non-decreasing (with other tables some experts may be skipped).  The sum
  * order of an output depends only on (k, fmt): a pair's result does not
  * depend on the other pairs.
  * Cite: "MXFP4 decode-graph + gate_up FUSION default-ON" (vllm.cpp PR #54),

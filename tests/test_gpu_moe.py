@@ -50,9 +50,27 @@ def test_moe_decode_matches_oracle(fmt, n, k, tokens, experts, topk):
     info = fp4.fp4_dispatch_info()
     y = fp4.fp4_w4a16_moe_decode(x_dev(xbits), pc, ps, n, experts, gs if fmt == NV else None, fmt,
                                  _i32(offsets), _i32(ptok), info=info)
-    assert info.kernel == 3 and info.grid_y == experts and info.grid_x == -(-n // 256) * 256 // 64
+    # One expert slot per expert that can have pairs: min(experts, pairs).
+    assert info.kernel == 3 and info.grid_y == min(experts, tokens * topk)
+    assert info.grid_x == -(-n // 256) * 256 // 64
     y_ref = oracle.moe_decode(oracle.bf16_bits_to_f32(xbits), host, k, fmt, offsets, ptok)
     assert_close(y_host(y), y_ref, "moe fmt=%d n=%d k=%d T=%d E=%d" % (fmt, n, k, tokens, experts))
+
+
+@pytest.mark.parametrize("fmt,tokens,experts,topk", [(NV, 1, 128, 8), (MX, 2, 100, 8), (NV, 3, 70, 5)])
+def test_moe_many_experts(fmt, tokens, experts, topk):
+    # More experts than one wave scans at once (64): the slot -> expert search
+    # crosses chunks, and most experts have no pairs.
+    n, k = 256, 512
+    host, pc, ps, gs = _stacked(experts, n, k, fmt, 3)
+    offsets, ptok = _routing(tokens, experts, topk, seed=experts + tokens)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    info = fp4.fp4_dispatch_info()
+    y = fp4.fp4_w4a16_moe_decode(x_dev(xbits), pc, ps, n, experts, gs if fmt == NV else None, fmt,
+                                 _i32(offsets), _i32(ptok), info=info)
+    assert info.grid_y == tokens * topk
+    y_ref = oracle.moe_decode(oracle.bf16_bits_to_f32(xbits), host, k, fmt, offsets, ptok)
+    assert_close(y_host(y), y_ref, "moe many experts E=%d" % experts)
 
 
 def test_moe_pairs_independent_and_long_expert():
