@@ -68,12 +68,14 @@ typedef struct fp4_dispatch_info {
   int kernel;  /* 0 = VALU decode GEMV, 2 = MFMA decode GEMV (both m <= 8),
                   1 = MFMA tile GEMM (m > 8), 3 = grouped MoE decode,
                   4 = W4A4 MXFP4 tile GEMM (any m) */
-  int splits;  /* K splits: decode kernels split every tile, the tile GEMM only
-                  its tail tiles (1 = no split) */
-  int grid_x;  /* decode: workgroups along the output rows; tile GEMM:
-                  workgroups of its whole-tile launch */
-  int grid_y;  /* decode: workgroups along the second grid axis; tile GEMM:
-                  workgroups of its tail launch (tail tiles x splits, 0 if none) */
+  int splits;  /* K splits: decode kernels split every tile, the tile GEMMs only
+                  their tail tiles (1 = no split; tail tiles run as row halves
+                  over all of K also report 1) */
+  int grid_x;  /* decode: workgroups along the output rows; tile GEMMs:
+                  workgroups of the launch */
+  int grid_y;  /* decode / MoE: workgroups along the second grid axis; tile
+                  GEMMs: workgroups that run the tail tiles (tail tiles x 2
+                  for row halves, x splits for K ranges; 0 if none) */
   int block;   /* threads per workgroup */
 } fp4_dispatch_info;
 
