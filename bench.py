@@ -22,6 +22,9 @@ Workloads (synthetic weights and activations at the pages' shapes):
   moe_gate_up    grouped MoE decode, NVFP4, 128 experts of n=1536, k=2048,
                  top-8 routing of m tokens (m = 1, 2, 4, 8); bytes counted
                  over the experts the routing activates
+  moe_prefill    the same experts and routing recipe at prefill sizes
+                 (m = 1024 tokens by default, 8192 pairs) on the grouped
+                 MoE tile GEMM; TFLOP/s = 2 * pairs * n * k / s
   down_proj      NVFP4, k=17408, n=5120
   o_proj         NVFP4, k=6144, n=5120
   prefill_nvfp4  NVFP4, k=5120, n=17408 (m=1024 by default)
@@ -75,6 +78,7 @@ WORKLOADS = {
     "lm_head": (2, 0, 248320, 5120, 1, 8),
     "lm_head_argmax": (2, 0, 248320, 5120, 1, 8),
     "moe_gate_up": (0, 0, 1536, 2048, 1, 8),
+    "moe_prefill": (0, 0, 1536, 2048, 1, 1024),
     "down_proj": (3, 0, 5120, 17408, 1, 8),
     "o_proj": (3, 0, 5120, 6144, 1, 8),
     "prefill_nvfp4": (4, 0, 17408, 5120, 1, 1024),
@@ -277,10 +281,17 @@ def moe_routing(np, tokens, seed):
 
 
 def run_moe(args, torch, np, fp4, synth):
-    """The grouped MoE decode workload: one fp4_w4a16_moe_decode call per step and m."""
+    """The grouped MoE workloads: one fp4_w4a16_moe_decode (moe_gate_up) or
+    fp4_w4a16_moe_prefill (moe_prefill) call per step and m tokens."""
     name = args.workload
-    wid, fmt, n, k, _, _ = WORKLOADS[name]
-    ms = [1, 2, 4, 8] if args.m is None else [int(v) for v in args.m.split(",")]
+    prefill = name == "moe_prefill"
+    wid, fmt, n, k, _, m_default = WORKLOADS[name]
+    if args.m is not None:
+        ms = [int(v) for v in args.m.split(",")]
+    else:
+        ms = [m_default] if prefill else [1, 2, 4, 8]
+    entry = fp4.fp4_w4a16_moe_prefill if prefill else fp4.fp4_w4a16_moe_decode
+    kname = ("moe_gemm_kernel<%s>" if prefill else "moe_decode_kernel<%s>") % ("nvfp4" if fmt == 0 else "mxfp4")
     dev = torch.device("cuda:0")
     host, codes, scales, gvals = [], [], [], []
     for e in range(MOE_DISTINCT):
@@ -312,12 +323,13 @@ def run_moe(args, torch, np, fp4, synth):
              "ws": torch.empty(fp4.fp4_moe_workspace_bytes(len(ptok), k), dtype=torch.uint8, device=dev),
              "info": fp4.fp4_dispatch_info()}
         d["bytes"] = len(active) * per_expert + 2 * m * k + 2 * len(ptok) * n
+        d["flops"] = 2.0 * len(ptok) * n * k
         per_m.append(d)
 
-    def call(d, i):
+    def call(d, i, fn=entry):
         c, s = weights[i % copies]
-        fp4.fp4_w4a16_moe_decode(d["x"], c, s, n, MOE_EXPERTS, gs if fmt == 0 else None, fmt, d["offsets"],
-                                 d["ptok"], y=d["y"], workspace=d["ws"], info=d["info"])
+        fn(d["x"], c, s, n, MOE_EXPERTS, gs if fmt == 0 else None, fmt, d["offsets"], d["ptok"], y=d["y"],
+           workspace=d["ws"], info=d["info"])
 
     for d in per_m:
         for i in range(args.warmup):
@@ -327,19 +339,38 @@ def run_moe(args, torch, np, fp4, synth):
     for d in per_m:
         d["t_ms"] = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), args.steps, args.launch == "graph")
     t_wall = time.perf_counter() - t_wall0
-    rows, total_ms, total_bytes = [], 0.0, 0
+    rows, total_ms, total_bytes, total_flops = [], 0.0, 0, 0.0
     for d in per_m:
         us = d["t_ms"] * 1e3 / args.steps
         total_ms += d["t_ms"]
         total_bytes += d["bytes"] * args.steps
+        total_flops += d["flops"] * args.steps
         info = d["info"]
-        rows.append({"m": d["m"], "kernel": "moe_decode_kernel<%s>" % ("nvfp4" if fmt == 0 else "mxfp4"),
-                     "us_per_launch": round(us, 3), "gbs": round(d["bytes"] / (us * 1e-6) / 1e9, 2),
-                     "pairs": d["pairs"], "active_experts": len(d["active"]),
-                     "grid": [info.grid_x, info.grid_y], "block": info.block, "algorithmic_bytes": d["bytes"]})
+        row = {"m": d["m"], "kernel": kname, "us_per_launch": round(us, 3),
+               "gbs": round(d["bytes"] / (us * 1e-6) / 1e9, 2), "tflops": round(d["flops"] / (us * 1e-6) / 1e12, 3),
+               "pairs": d["pairs"], "active_experts": len(d["active"]),
+               "grid": [info.grid_x, info.grid_y], "block": info.block, "algorithmic_bytes": d["bytes"],
+               "flops": d["flops"]}
+        if prefill and not args.no_crosscheck:
+            # The same routing through the decode route (8 pairs of an expert per pass over its weight).
+            t = timed_calls(torch, lambda i, d=d: call(d, i, fp4.fp4_w4a16_moe_decode), max(args.steps // 4, 5),
+                            args.launch == "graph")
+            row["us_decode_route"] = round(t * 1e3 / max(args.steps // 4, 5), 3)
+        rows.append(row)
     dom = max(rows, key=lambda r: r["us_per_launch"])
+    if prefill:
+        value, unit = round(total_flops / (total_ms * 1e-3) / 1e12, 3), "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4), "kernel": dom["kernel"], "m": dom["m"],
+                "avg_launch_us": dom["us_per_launch"], "units_per_launch": dom["flops"], "traffic": None}
+    else:
+        value, unit = round(total_bytes / (total_ms * 1e-3) / 1e9, 3), "GB/s"
+        roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4), "kernel": dom["kernel"], "m": dom["m"],
+                "avg_launch_us": dom["us_per_launch"], "units_per_launch": dom["algorithmic_bytes"],
+                "traffic": None}
     out = {
-        "metric": METRIC, "value": round(total_bytes / (total_ms * 1e-3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "fmt": "nvfp4" if fmt == 0 else "mxfp4", "m": ms, "n": n, "k": k,
@@ -347,10 +378,7 @@ def run_moe(args, torch, np, fp4, synth):
                    "launch": args.launch, "rotated_weight_copies": copies,
                    "step": "one grouped call per m (m tokens, top-%d routing)" % MOE_TOPK, "per_m": rows,
                    "wall_s_timed": round(t_wall, 4)},
-        "roofline": {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4), "kernel": dom["kernel"], "m": dom["m"],
-                     "avg_launch_us": dom["us_per_launch"], "units_per_launch": dom["algorithmic_bytes"],
-                     "traffic": None},
+        "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -358,16 +386,29 @@ def run_moe(args, torch, np, fp4, synth):
         d = per_m[0]
         xs = oracle.bf16_bits_to_f32(d["xb"])
         experts = [host[i] for i in rep_idx]
+        offsets_h, ptok_h = d["offsets_h"], d["ptok_h"]
+        if prefill:
+            # Bounded sample: the first 16 pairs of the call (the oracle
+            # dequantizes the expert's weight for every pair).
+            sp = min(16, len(ptok_h))
+            offsets_h = np.minimum(offsets_h, sp)
+            ptok_h = ptok_h[:sp]
         t0 = time.perf_counter()
         reps = 0
         while reps == 0 or (time.perf_counter() - t0 < args.cpu_budget and reps < 20):
-            oracle.moe_decode(xs, experts, k, fmt, d["offsets_h"], d["ptok_h"])
+            oracle.moe_decode(xs, experts, k, fmt, offsets_h, ptok_h)
             reps += 1
         dt = (time.perf_counter() - t0) / reps
-        out["cpu_baseline"] = {"value": round(d["bytes"] / dt / 1e9, 4), "unit": "GB/s",
-                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-                               "sample": "oracle.moe_decode of the m = %d call (%d pairs over %d experts), %d "
-                                         "repetitions" % (d["m"], d["pairs"], len(d["active"]), reps)}
+        if prefill:
+            out["cpu_baseline"] = {"value": round(2.0 * len(ptok_h) * n * k / dt / 1e12, 6), "unit": "TFLOP/s",
+                                   "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                   "sample": "oracle.moe_decode of the first %d pairs of the m = %d call, %d "
+                                             "repetitions" % (len(ptok_h), d["m"], reps)}
+        else:
+            out["cpu_baseline"] = {"value": round(d["bytes"] / dt / 1e9, 4), "unit": "GB/s",
+                                   "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                   "sample": "oracle.moe_decode of the m = %d call (%d pairs over %d experts), %d "
+                                             "repetitions" % (d["m"], d["pairs"], len(d["active"]), reps)}
     print(json.dumps(out), flush=True)
 
 
@@ -412,7 +453,7 @@ def main():
         return
 
     name = args.workload
-    if name == "moe_gate_up":
+    if name in ("moe_gate_up", "moe_prefill"):
         return run_moe(args, torch, np, fp4, synth)
     wid, fmt, n, k, proj, m_default = WORKLOADS[name]
     if args.m is None:

@@ -61,6 +61,8 @@ _SIGNATURES = {
     "fp4_moe_workspace_bytes": (_i, [_i, _i, ctypes.POINTER(_sz)]),
     "fp4_w4a16_moe_decode": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _sz, _vp,
                                   ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_w4a16_moe_prefill": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _sz, _vp,
+                                   ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_w4a4_act_bytes": (_i, [_i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "fp4_quantize_act_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "fp4_w4a4_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
@@ -332,6 +334,20 @@ def fp4_w4a16_moe_decode(x, prep_codes, prep_scales, n, experts, global_scales, 
     expert e owning pairs expert_offsets[e] .. expert_offsets[e + 1]).  prep_codes / prep_scales hold
     the experts' prepared weights stacked; global_scales is float32 [experts] (NVFP4) or None (MXFP4).
     Returns y bf16 [pairs, n]."""
+    return _moe("fp4_w4a16_moe_decode", x, prep_codes, prep_scales, n, experts, global_scales, fmt,
+                expert_offsets, pair_tokens, y, workspace, stream, info)
+
+
+def fp4_w4a16_moe_prefill(x, prep_codes, prep_scales, n, experts, global_scales, fmt, expert_offsets,
+                          pair_tokens, y=None, workspace=None, stream=None, info=None):
+    """Grouped MoE on the tile GEMM, for routings that give experts many pairs: the same arguments and
+    result as fp4_w4a16_moe_decode."""
+    return _moe("fp4_w4a16_moe_prefill", x, prep_codes, prep_scales, n, experts, global_scales, fmt,
+                expert_offsets, pair_tokens, y, workspace, stream, info)
+
+
+def _moe(name, x, prep_codes, prep_scales, n, experts, global_scales, fmt, expert_offsets, pair_tokens,
+         y, workspace, stream, info):
     _need(x, torch.bfloat16, "x")
     _need(prep_codes, torch.uint8, "prep_codes")
     _need(prep_scales, torch.uint8, "prep_scales")
@@ -357,7 +373,7 @@ def fp4_w4a16_moe_decode(x, prep_codes, prep_scales, n, experts, global_scales, 
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("fp4_w4a16_moe_decode", load_library().fp4_w4a16_moe_decode(
+    _check(name, getattr(load_library(), name)(
         _ptr(x), tokens, k, _ptr(prep_codes), _ptr(prep_scales), n, experts, _ptr(global_scales), fmt,
         _ptr(expert_offsets), _ptr(pair_tokens), pairs, _ptr(y), _ptr(workspace), ws_bytes, _stream(stream),
         None if info is None else ctypes.byref(info)))

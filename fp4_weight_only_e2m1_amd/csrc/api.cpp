@@ -242,6 +242,52 @@ int run_w4a4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_
 
 }  // namespace
 
+namespace {
+
+// Checks shared by the grouped MoE entry points; FP4_OK with *no_pairs set
+// means there is nothing to compute.
+int check_moe(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev,
+              int n, int experts, const float* global_scales_dev, int fmt, const int32_t* expert_offsets_dev,
+              const int32_t* pair_tokens_dev, int pairs, const uint16_t* y_dev, const void* workspace_dev,
+              size_t workspace_bytes, bool* no_pairs) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if (tokens < 0 || tokens > FP4_MAX_M || pairs < 0 || pairs > FP4_MAX_M) return FP4_EINVAL;
+  if (experts < 1 || experts > 65535) return FP4_EINVAL;
+  const bool mx = fmt == FP4_FMT_MXFP4;
+  *no_pairs = pairs == 0;
+  if (pairs == 0) return FP4_OK;
+  if (tokens == 0 || !x_dev || !prep_codes_dev || !prep_scales_dev || !expert_offsets_dev || !pair_tokens_dev ||
+      !y_dev || (!mx && !global_scales_dev))
+    return FP4_EINVAL;
+  if (!aligned16(x_dev) || !aligned16(prep_codes_dev) || !aligned16(prep_scales_dev) || !aligned16(y_dev) ||
+      reinterpret_cast<uintptr_t>(expert_offsets_dev) % 4 != 0 || reinterpret_cast<uintptr_t>(pair_tokens_dev) % 4 != 0 ||
+      (!mx && reinterpret_cast<uintptr_t>(global_scales_dev) % 4 != 0))
+    return FP4_EALIGN;
+  size_t need = 0;
+  if ((st = fp4_moe_workspace_bytes(pairs, k, &need))) return st;
+  if (workspace_bytes < need) return FP4_EWORKSPACE;
+  if (!workspace_dev) return FP4_EINVAL;
+  if (!aligned16(workspace_dev)) return FP4_EALIGN;
+  return FP4_OK;
+}
+
+fp4::MoeArgs moe_args(const fp4::PreparedShape& ps, int fmt, const float* global_scales_dev,
+                      const int32_t* expert_offsets_dev, int pairs, int experts, const void* workspace_dev) {
+  fp4::MoeArgs moe{};
+  moe.offsets = expert_offsets_dev;
+  moe.x_sorted = static_cast<const uint16_t*>(workspace_dev);
+  moe.gscales = fmt == FP4_FMT_MXFP4 ? nullptr : global_scales_dev;
+  moe.code_stride = ps.code_bytes;
+  moe.scale_stride = ps.scale_bytes;
+  moe.pairs = pairs;
+  moe.experts = experts;
+  return moe;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fp4_prepared_bytes(int n, int k, int fmt, size_t* code_bytes_out, size_t* scale_bytes_out) {
@@ -375,33 +421,20 @@ int fp4_moe_workspace_bytes(int pairs, int k, size_t* bytes_out) {
   return FP4_OK;
 }
 
+
 int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_codes_dev,
                          const uint8_t* prep_scales_dev, int n, int experts, const float* global_scales_dev, int fmt,
                          const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
                          uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
                          fp4_dispatch_info* info_out) {
-  int st = check_fmt(fmt);
+  bool no_pairs = false;
+  const int st = check_moe(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n, experts, global_scales_dev, fmt,
+                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, workspace_dev, workspace_bytes, &no_pairs);
   if (st) return st;
-  if ((st = check_nk(n, k))) return st;
-  if (tokens < 0 || tokens > FP4_MAX_M || pairs < 0 || pairs > FP4_MAX_M) return FP4_EINVAL;
-  if (experts < 1 || experts > 65535) return FP4_EINVAL;
-  const bool mx = fmt == FP4_FMT_MXFP4;
-  if (pairs == 0) {
+  if (no_pairs) {
     if (info_out) *info_out = fp4_dispatch_info{3, 1, 0, 0, 0};
     return FP4_OK;
   }
-  if (tokens == 0 || !x_dev || !prep_codes_dev || !prep_scales_dev || !expert_offsets_dev || !pair_tokens_dev ||
-      !y_dev || (!mx && !global_scales_dev))
-    return FP4_EINVAL;
-  if (!aligned16(x_dev) || !aligned16(prep_codes_dev) || !aligned16(prep_scales_dev) || !aligned16(y_dev) ||
-      reinterpret_cast<uintptr_t>(expert_offsets_dev) % 4 != 0 || reinterpret_cast<uintptr_t>(pair_tokens_dev) % 4 != 0 ||
-      (!mx && reinterpret_cast<uintptr_t>(global_scales_dev) % 4 != 0))
-    return FP4_EALIGN;
-  size_t need = 0;
-  if ((st = fp4_moe_workspace_bytes(pairs, k, &need))) return st;
-  if (workspace_bytes < need) return FP4_EWORKSPACE;
-  if (!workspace_dev) return FP4_EINVAL;
-  if (!aligned16(workspace_dev)) return FP4_EALIGN;
 
   const fp4::PreparedShape ps = fp4::prepared_shape(n, k, fmt);
   fp4::GemvArgs a{};
@@ -422,20 +455,57 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t
   a.ldy = n;
   a.gscale[0] = a.gscale[1] = 1.0f;
   a.tile_rows = fp4::kDecodeTileRows;
-  fp4::MoeArgs moe{};
-  moe.offsets = expert_offsets_dev;
-  moe.x_sorted = static_cast<const uint16_t*>(workspace_dev);
-  moe.gscales = mx ? nullptr : global_scales_dev;
-  moe.code_stride = ps.code_bytes;
-  moe.scale_stride = ps.scale_bytes;
-  moe.pairs = pairs;
-  moe.experts = experts;
+  const fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pairs, experts, workspace_dev);
   dim3 grid, block;
   const hipError_t e = fp4::launch_moe_decode(a, moe, experts, x_dev, pair_tokens_dev, tokens,
                                               static_cast<uint16_t*>(workspace_dev), fmt, stream, &grid, &block);
   if (e != hipSuccess) return FP4_EHIP;
   if (info_out) *info_out = fp4_dispatch_info{3, 1, static_cast<int>(grid.x), static_cast<int>(grid.y),
                                               static_cast<int>(block.x)};
+  return FP4_OK;
+}
+
+int fp4_w4a16_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_codes_dev,
+                          const uint8_t* prep_scales_dev, int n, int experts, const float* global_scales_dev, int fmt,
+                          const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
+                          uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
+                          fp4_dispatch_info* info_out) {
+  bool no_pairs = false;
+  const int st = check_moe(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n, experts, global_scales_dev, fmt,
+                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, workspace_dev, workspace_bytes, &no_pairs);
+  if (st) return st;
+  if (no_pairs) {
+    if (info_out) *info_out = fp4_dispatch_info{5, 1, 0, 0, 0};
+    return FP4_OK;
+  }
+  const fp4::PreparedShape ps = fp4::prepared_shape(n, k, fmt);
+  // Workgroups of the tile launch: every (activation tile slot, weight tile).
+  const int64_t wgs = fp4::moe_gemm_slots(pairs, experts) * (ps.n_pad / fp4::kGemmBN);
+  if (wgs * 256 >= (int64_t{1} << 32)) return FP4_EINVAL;
+
+  fp4::MfmaArgs a{};
+  a.codes = prep_codes_dev;
+  a.scales = prep_scales_dev;
+  a.y = y_dev;
+  a.m = pairs;
+  a.k = k;
+  a.k_pad = ps.k_pad;
+  a.kgroups = ps.kgroups;
+  a.ksegs = ps.ksegs;
+  a.n_proj = n;
+  a.n_proj_pad = ps.n_pad;
+  a.projections = 1;
+  a.rows_total = ps.n_pad;
+  a.ldy = n;
+  a.gscale[0] = a.gscale[1] = 1.0f;
+  a.plan = fp4::gemm_plan(fp4::kGemmBM, a.rows_total, k);  // only n_tiles and ksteps are used
+  const fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pairs, experts, workspace_dev);
+  if (fp4::launch_moe_gather(x_dev, pair_tokens_dev, pairs, k, tokens, static_cast<uint16_t*>(workspace_dev),
+                             stream) != hipSuccess)
+    return FP4_EHIP;
+  dim3 grid, block;
+  if (fp4::launch_moe_gemm(a, moe, fmt, stream, &grid, &block) != hipSuccess) return FP4_EHIP;
+  if (info_out) *info_out = fp4_dispatch_info{5, 1, static_cast<int>(grid.x), 0, static_cast<int>(block.x)};
   return FP4_OK;
 }
 

@@ -489,13 +489,18 @@ hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_moe_gather(const uint16_t* x, const int32_t* tokens, int pairs, int k, int tokens_total,
+                             uint16_t* x_sorted, hipStream_t stream) {
+  const int64_t chunks = static_cast<int64_t>(pairs) * (k / 8);
+  hipLaunchKernelGGL(moe_gather_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0, stream, x,
+                     tokens, pairs, k, tokens_total, x_sorted);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, const uint16_t* x, const int32_t* tokens,
                              int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid_out,
                              dim3* block_out) {
-  const int64_t chunks = static_cast<int64_t>(moe.pairs) * (a.k / 8);
-  hipLaunchKernelGGL(moe_gather_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0, stream, x,
-                     tokens, moe.pairs, a.k, tokens_total, x_sorted);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_moe_gather(x, tokens, moe.pairs, a.k, tokens_total, x_sorted, stream);
   if (e != hipSuccess) return e;
   const int slots = experts < moe.pairs ? experts : moe.pairs;
   const dim3 grid(static_cast<unsigned>(a.rows_total / kDecodeTileRows), static_cast<unsigned>(slots));

@@ -242,6 +242,14 @@ inline int64_t w4a4_act_code_bytes(int m, int k) { return w4a4_act_rows(m) * w4a
 inline int64_t w4a4_act_scale_bytes(int m, int k) { return w4a4_act_rows(m) * w4a4_act_k(k) / 32; }
 
 // Workspace of a prefill call: fp32 partial tiles [tail_tiles][splits][bm][BN].
+// Grouped MoE tile GEMM: an upper bound on the 128-row activation tiles of
+// all experts together, sum over experts e of ceil(c_e / 128) with c_e
+// routed pairs summing to `pairs`: at most pairs / 128 + (experts with
+// pairs), and no more experts than pairs can have pairs.
+inline int64_t moe_gemm_slots(int pairs, int experts) {
+  return (static_cast<int64_t>(pairs) + kGemmBM - 1) / kGemmBM + (experts < pairs ? experts : pairs);
+}
+
 inline int64_t gemm_workspace_bytes(const GemmPlan& p, int bm = kGemmBM) {
   if (p.mhalf) return 0;
   return static_cast<int64_t>(p.tail_tiles) * p.splits * bm * kGemmBN * 4;
@@ -280,7 +288,11 @@ hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, di
 hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, const uint16_t* x, const int32_t* tokens,
                              int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid,
                              dim3* block);
+hipError_t launch_moe_gather(const uint16_t* x, const int32_t* tokens, int pairs, int k, int tokens_total,
+                             uint16_t* x_sorted, hipStream_t stream);
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
+hipError_t launch_moe_gemm(const MfmaArgs& a, const MoeArgs& moe, int fmt, hipStream_t stream, dim3* grid,
+                           dim3* block);
 hipError_t launch_tail_reduce(const MfmaArgs& a, int bm, hipStream_t stream);
 hipError_t launch_act_quant_mxfp4(const uint16_t* x, int m, int k, uint8_t* codes, uint8_t* scales,
                                   hipStream_t stream);

@@ -446,6 +446,96 @@ void gemm_kernel(const MfmaArgs a) {
   store_tile_partial_staged<kGemmBM, kThreads, 64, FI>(a, u, m0, wave, acc, lds);
 }
 
+// Grouped MoE prefill: the routed (token, expert) pairs sorted by expert,
+// their x rows gathered in pair order (x_sorted), expert e owning pairs
+// [offsets[e], offsets[e + 1]).  Counted in expert order, expert e's c_e
+// pairs form ceil(c_e / 128) activation tiles of 128 of its gathered rows;
+// workgroup b computes weight-row tile b % n_tiles of the (b / n_tiles)-th
+// such tile, over all of K, with that expert's prepared weight, and stores
+// bf16 y at the same pair rows.  Each tile's sums are the dense GEMM's for
+// those rows (same K steps, same MFMA order), so a pair's output does not
+// depend on the other pairs.  The grid has moe_gemm_slots(pairs, experts)
+// tile slots, enough for every tile when the offsets are non-decreasing;
+// slots past the last tile exit.  Offsets are clamped to [0, pairs], so no
+// routing table can make a workgroup touch memory outside x_sorted and y.
+__device__ __forceinline__ void moe_range(const MoeArgs& moe, int e, int& p0, int& p1) {
+  p0 = moe.offsets[e];
+  p1 = moe.offsets[e + 1];
+  p0 = p0 < 0 ? 0 : p0 > moe.pairs ? moe.pairs : p0;
+  p1 = p1 < p0 ? p0 : p1 > moe.pairs ? moe.pairs : p1;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
+  __shared__ Stage<FMT> st[kStages];
+  __shared__ int s_expert, s_p0, s_p1, s_tile;
+  const int n_tiles = base.plan.n_tiles;
+  const int slot = static_cast<int>(blockIdx.x) / n_tiles;
+  const int n_tile = static_cast<int>(blockIdx.x) - slot * n_tiles;
+  // Wave 0 finds the slot's (expert, tile): 64 experts at a time, each lane
+  // takes one expert's tile count, an inclusive scan over the wave gives the
+  // tiles before each, and the lane whose range holds the slot records it.
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (lane == 0) s_expert = -1;
+    int before = 0;  // tiles of the experts scanned so far (wave-uniform)
+    for (int b = 0; b < moe.experts && before <= slot; b += 64) {
+      const int e = b + lane;
+      int p0 = 0, p1 = 0;
+      if (e < moe.experts) moe_range(moe, e, p0, p1);
+      const int tiles = (p1 - p0 + kGemmBM - 1) / kGemmBM;
+      int incl = tiles;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      const int first = before + incl - tiles;
+      if (slot >= first && slot < first + tiles) {
+        s_expert = e;
+        s_p0 = p0;
+        s_p1 = p1;
+        s_tile = slot - first;
+      }
+      before += __shfl(incl, 63);
+    }
+  }
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(s_expert);
+  if (e < 0) return;
+  const int p0 = __builtin_amdgcn_readfirstlane(s_p0);
+  const int p1 = __builtin_amdgcn_readfirstlane(s_p1);
+  const int tile = __builtin_amdgcn_readfirstlane(s_tile);
+  MfmaArgs a = base;
+  a.x = moe.x_sorted + static_cast<int64_t>(p0) * a.k;
+  a.y = base.y + static_cast<int64_t>(p0) * a.ldy;
+  a.m = p1 - p0;
+  a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
+  a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
+  a.gscale[0] = a.gscale[1] = moe.gscales ? moe.gscales[e] : 1.0f;
+  const int64_t m0 = static_cast<int64_t>(tile) * kGemmBM;
+  const int64_t n0 = static_cast<int64_t>(n_tile) * kGemmBN;
+  const int rows = a.m - static_cast<int>(m0);  // >= 1
+  const int wave = threadIdx.x >> 6;
+  char* lds = reinterpret_cast<char*>(st);
+  // A tile with at most 32 (64) rows computes only 1 (2) of its 4 activation
+  // blocks, as the dense kernel's instances for small m do.
+  if (rows > 64) {
+    f32x16_t acc[4][2];
+    run_tile<FMT, 4>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 4>(a, m0, n0, wave, acc, lds);
+  } else if (rows > 32) {
+    f32x16_t acc[2][2];
+    run_tile<FMT, 2>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 2>(a, m0, n0, wave, acc, lds);
+  } else {
+    f32x16_t acc[1][2];
+    run_tile<FMT, 1>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 1>(a, m0, n0, wave, acc, lds);
+  }
+}
+
 // Split-K finish of the tail tiles: y = G * (partial_0 + partial_1 + ... +
 // partial_{S-1}), added in split order (a fixed order: the output does not
 // depend on timing).  A separate launch, so every partial is complete and
@@ -567,6 +657,20 @@ hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* gri
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || units == 0 || p.mhalf) return e;
   return launch_tail_reduce(a, kGemmBM, stream);
+}
+
+hipError_t launch_moe_gemm(const MfmaArgs& a, const MoeArgs& moe, int fmt, hipStream_t stream, dim3* grid_out,
+                           dim3* block_out) {
+  const int64_t wgs = moe_gemm_slots(moe.pairs, moe.experts) * a.plan.n_tiles;
+  if (wgs <= 0 || wgs * kThreads >= (int64_t{1} << 32)) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(wgs)), block(kThreads);
+  if (grid_out) *grid_out = grid;
+  if (block_out) *block_out = block;
+  if (fmt == kFmtNvfp4)
+    hipLaunchKernelGGL(moe_gemm_kernel<kFmtNvfp4>, grid, block, 0, stream, a, moe);
+  else
+    hipLaunchKernelGGL(moe_gemm_kernel<kFmtMxfp4>, grid, block, 0, stream, a, moe);
+  return hipGetLastError();
 }
 
 hipError_t launch_tail_reduce(const MfmaArgs& a, int bm, hipStream_t stream) {

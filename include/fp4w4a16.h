@@ -67,7 +67,8 @@ enum fp4_status {
 typedef struct fp4_dispatch_info {
   int kernel;  /* 0 = VALU decode GEMV, 2 = MFMA decode GEMV (both m <= 8),
                   1 = MFMA tile GEMM (m > 8), 3 = grouped MoE decode,
-                  4 = W4A4 MXFP4 tile GEMM (any m) */
+                  4 = W4A4 MXFP4 tile GEMM (any m),
+                  5 = grouped MoE tile GEMM (prefill) */
   int splits;  /* K splits: decode kernels split every tile, the tile GEMMs only
                   their tail tiles (1 = no split; tail tiles run as row halves
                   over all of K also report 1) */
@@ -268,6 +269,31 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k,
                          const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
                          uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes,
                          hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
+ * Grouped MoE prefill: the same operation, arguments, workspace, checks and
+ * containment of routing data as fp4_w4a16_moe_decode, for routings that give
+ * experts many pairs (prefill batches): after the gather, one launch of the
+ * MFMA tile GEMM over 128-row tiles of each expert's gathered rows, so an
+ * expert's weight is read once per 128 of its pairs instead of once per 8.
+ * Workgroup slots: the tiles of all experts in expert order, at most
+ * ceil(pairs / 128) + min(experts, pairs) of them (every tile, when the
+ * offsets are non-decreasing), times ceil(n / 256) weight tiles; FP4_EINVAL
+ * when that grid would exceed 2^32 threads.  A tile's sums are the tile
+ * GEMM's (K in order, the dense call's MFMA accumulation), so a pair's result
+ * does not depend on the other pairs, and equals the dense fp4_w4a16_linear
+ * output of that expert where the dense call computes the row in a whole tile.
+ * Dispatch info: kernel 5, grid_x = workgroups launched.
+ * Cite: as fp4_w4a16_moe_decode; the pages' MoE model runs its grouped W4A16
+ * route at prefill sizes too ("MXFP4 decode-graph + gate_up FUSION
+ * default-ON" (vllm.cpp PR #54), step 3: prefill keeps its own path).
+ */
+int fp4_w4a16_moe_prefill(const uint16_t* x_dev, int tokens, int k,
+                          const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int experts,
+                          const float* global_scales_dev, int fmt,
+                          const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
+                          uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes,
+                          hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
  * W4A4 MXFP4 variant: activations quantized to MXFP4 at call time and

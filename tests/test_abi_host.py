@@ -261,3 +261,36 @@ def test_w4a4_argument_checks(lib):
     assert lib.fp4_quantize_act_mxfp4(None, 0, 64, None, None, None) == ST["OK"]
     sz = ctypes.c_size_t()
     assert lib.fp4_w4a4_workspace_bytes(16, 512, 256, 3, ctypes.byref(sz)) == ST["EINVAL"]
+
+
+def _moe(lib, name, tokens=4, k=256, n=512, experts=8, fmt=NV, x=FAKE, gs=FAKE, offsets=FAKE, ptok=FAKE,
+         pairs=16, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return getattr(lib, name)(x, tokens, k, FAKE, FAKE, n, experts, gs, fmt, offsets, ptok, pairs, y, ws, ws_bytes,
+                              None, None)
+
+
+@pytest.mark.parametrize("name", ["fp4_w4a16_moe_decode", "fp4_w4a16_moe_prefill"])
+def test_moe_argument_checks(lib, name):
+    assert _moe(lib, name, fmt=3) == ST["EFMT"]
+    assert _moe(lib, name, experts=0) == ST["EINVAL"]
+    assert _moe(lib, name, experts=65536) == ST["EINVAL"]
+    assert _moe(lib, name, pairs=-1) == ST["EINVAL"]
+    assert _moe(lib, name, k=100) == ST["EINVAL"]
+    assert _moe(lib, name, tokens=0) == ST["EINVAL"]
+    assert _moe(lib, name, gs=None) == ST["EINVAL"]            # NVFP4 needs the global scales
+    assert _moe(lib, name, offsets=None) == ST["EINVAL"]
+    assert _moe(lib, name, offsets=FAKE + 2) == ST["EALIGN"]
+    assert _moe(lib, name, ptok=FAKE + 1) == ST["EALIGN"]
+    assert _moe(lib, name, y=FAKE + 8) == ST["EALIGN"]
+    need = fp4.fp4_moe_workspace_bytes(16, 256)
+    assert need == 16 * 256 * 2
+    assert _moe(lib, name, ws_bytes=need - 1) == ST["EWORKSPACE"]
+    assert _moe(lib, name, ws=None) == ST["EINVAL"]
+    # No pairs: nothing to compute, nothing checked beyond the sizes.
+    assert _moe(lib, name, pairs=0, x=None, y=None, ws=None) == ST["OK"]
+
+
+def test_moe_prefill_grid_limit(lib):
+    # ceil(pairs / 128) + min(experts, pairs) tile slots x ceil(n / 256)
+    # weight tiles of 256 threads must stay below 2^32 threads.
+    assert _moe(lib, "fp4_w4a16_moe_prefill", pairs=1 << 20, experts=65535, n=1 << 24) == ST["EINVAL"]

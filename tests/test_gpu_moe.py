@@ -123,3 +123,132 @@ def test_moe_no_pairs_is_a_no_op():
                                  _i32([0, 0, 0]), torch.empty(0, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
     assert y.shape == (0, n)
+
+
+# ---- grouped MoE on the tile GEMM (fp4_w4a16_moe_prefill) ----
+
+def _oracle_moe(xbits, host, k, fmt, offsets, ptok):
+    """oracle.linear per expert over its pairs' x rows (the layer is row-wise,
+    so this is oracle.moe_decode's result, one weight dequantization per expert)."""
+    x = oracle.bf16_bits_to_f32(xbits)
+    n = host[0][0].shape[0]
+    y = np.zeros((len(ptok), n), dtype=np.float64)
+    for e, (packed, sc, g) in enumerate(host):
+        p0, p1 = int(offsets[e]), int(offsets[e + 1])
+        if p1 > p0:
+            y[p0:p1] = oracle.linear(x[ptok[p0:p1]], packed, sc, k, fmt, g)
+    return y
+
+
+def _slots(pairs, experts, n):
+    return (-(-pairs // 128) + min(experts, pairs)) * (-(-n // 256))
+
+
+def _offsets_from_counts(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("fmt,n,k,tokens,experts,topk", [
+    (NV, 768, 2048, 200, 8, 2),      # ~50 pairs per expert
+    (MX, 300, 1056, 150, 6, 3),      # ragged n and k, ~75 per expert
+    (NV, 520, 4096, 64, 16, 8),      # 32 per expert
+    (MX, 1024, 512, 40, 100, 8),     # 100 experts: the tile search crosses 64-expert chunks
+    (NV, 256, 512, 700, 4, 1),       # ~175 per expert: two tiles per expert
+])
+def test_moe_prefill_matches_oracle(fmt, n, k, tokens, experts, topk):
+    host, pc, ps, gs = _stacked(experts, n, k, fmt, 20)
+    offsets, ptok = _routing(tokens, experts, topk, seed=7 * tokens + experts)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    info = fp4.fp4_dispatch_info()
+    y = fp4.fp4_w4a16_moe_prefill(x_dev(xbits), pc, ps, n, experts, gs if fmt == NV else None, fmt,
+                                  _i32(offsets), _i32(ptok), info=info)
+    assert info.kernel == 5 and info.grid_x == _slots(len(ptok), experts, n) and info.block == 256
+    assert_close(y_host(y), _oracle_moe(xbits, host, k, fmt, offsets, ptok),
+                 "moe prefill fmt=%d n=%d k=%d T=%d E=%d" % (fmt, n, k, tokens, experts))
+
+
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_moe_prefill_tile_boundaries(fmt):
+    # Expert pair counts at the 32 / 64 / 128-row boundaries of the tiles and
+    # of their 1-, 2- and 4-block instances, with empty experts between.
+    counts = [0, 1, 31, 32, 0, 33, 64, 65, 127, 128, 129, 0, 257]
+    n, k, tokens = 256, 512, 97
+    experts = len(counts)
+    host, pc, ps, gs = _stacked(experts, n, k, fmt, 30)
+    offsets = _offsets_from_counts(counts)
+    ptok = np.random.default_rng(5).integers(0, tokens, size=int(offsets[-1])).astype(np.int32)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    y = fp4.fp4_w4a16_moe_prefill(x_dev(xbits), pc, ps, n, experts, gs if fmt == NV else None, fmt,
+                                  _i32(offsets), _i32(ptok))
+    assert_close(y_host(y), _oracle_moe(xbits, host, k, fmt, offsets, ptok), "moe prefill boundaries")
+
+
+def test_moe_prefill_equals_dense_linear_and_is_pair_independent():
+    # Expert 1 gets all 300 tokens in order: its rows are the dense m = 300
+    # call's (whole tiles, same MFMA order), bit for bit.  Dropping pairs
+    # (300 -> 200 rows: other tile sizes and instances) leaves every
+    # remaining pair's output bit for bit, and the decode route agrees within
+    # the tolerance.
+    fmt, n, k, experts, tokens = NV, 512, 1024, 3, 300
+    host, pc, ps, gs = _stacked(experts, n, k, fmt, 40)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    xd = x_dev(xbits)
+    full = [(0, 5), (0, 17)] + [(1, t) for t in range(tokens)] + [(2, 0), (2, 299)]
+    sub = [p for i, p in enumerate(full) if i % 3 != 2]
+
+    def run(pairs, entry):
+        e_of = np.array([p[0] for p in pairs])
+        offsets = np.searchsorted(e_of, np.arange(experts + 1)).astype(np.int32)
+        ptok = np.array([p[1] for p in pairs], dtype=np.int32)
+        return offsets, ptok, y_host_bits(entry(xd, pc, ps, n, experts, gs, fmt, _i32(offsets), _i32(ptok)))
+
+    off, ptok, y_full = run(full, fp4.fp4_w4a16_moe_prefill)
+    cb, sb = fp4.fp4_prepared_bytes(n, k, fmt)
+    dinfo = fp4.fp4_dispatch_info()
+    dense = y_host_bits(fp4.fp4_w4a16_linear(xd, pc[cb:2 * cb], ps[sb:2 * sb], n, float(host[1][2]), fmt,
+                                             info=dinfo))
+    assert dinfo.kernel == 1 and dinfo.splits == 1  # every row over all of K (no K-split partials)
+    assert np.array_equal(y_full[2:2 + tokens], dense)
+    _, _, y_sub = run(sub, fp4.fp4_w4a16_moe_prefill)
+    rows = {p: i for i, p in enumerate(full)}
+    for j, p in enumerate(sub):
+        assert np.array_equal(y_sub[j], y_full[rows[p]]), p
+    _, _, y_dec = run(full, fp4.fp4_w4a16_moe_decode)
+    y_ref = _oracle_moe(xbits, host, k, fmt, off, ptok)
+    assert_close(oracle.bf16_bits_to_f32(y_full).astype(np.float64), y_ref, "moe prefill full")
+    assert_close(oracle.bf16_bits_to_f32(y_dec).astype(np.float64), y_ref, "moe decode route, same routing")
+
+
+def test_moe_prefill_out_of_range_routing_is_contained():
+    fmt, n, k, experts, tokens = MX, 256, 1024, 3, 2
+    host, pc, ps, _ = _stacked(experts, n, k, fmt, 9)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    offsets = np.array([0, 2, 9, 1 << 30], dtype=np.int32)
+    ptok = np.array([0, -5, 1, 7], dtype=np.int32)
+    y = torch.full((4, n), 3.0, dtype=torch.bfloat16, device=DEV)
+    fp4.fp4_w4a16_moe_prefill(x_dev(xbits), pc, ps, n, experts, None, fmt, _i32(offsets), _i32(ptok), y=y)
+    got = y_host(y)
+    assert np.isfinite(got).all()
+    assert (got[1] == 0).all() and (got[3] == 0).all()
+    ref = oracle.moe_decode(oracle.bf16_bits_to_f32(xbits), host, k, fmt, [0, 2, 4, 4], [0, 0, 1, 0])
+    assert_close(got[[0, 2]], ref[[0, 2]], "moe prefill clamped")
+    # Decreasing offsets: experts 1 and 2 get empty ranges after clamping,
+    # and row 3, which no expert owns, is not written.
+    offsets = np.array([0, 3, 2, 2], dtype=np.int32)
+    ptok = np.array([0, 1, 0, 1], dtype=np.int32)
+    y = torch.full((4, n), 3.0, dtype=torch.bfloat16, device=DEV)
+    fp4.fp4_w4a16_moe_prefill(x_dev(xbits), pc, ps, n, experts, None, fmt, _i32(offsets), _i32(ptok), y=y)
+    got = y_host(y)
+    assert (got[3] == 3.0).all()
+    ref = _oracle_moe(xbits, host, k, fmt, [0, 3, 3, 3], ptok[:3])
+    assert_close(got[:3], ref, "moe prefill decreasing offsets")
+
+
+def test_moe_prefill_no_pairs_is_a_no_op():
+    fmt, n, k = NV, 256, 512
+    _, pc, ps, gs = _stacked(2, n, k, fmt, 11)
+    info = fp4.fp4_dispatch_info()
+    y = fp4.fp4_w4a16_moe_prefill(x_dev(synth.activations(synth.TINY, 1, k)), pc, ps, n, 2, gs, fmt,
+                                  _i32([0, 0, 0]), torch.empty(0, dtype=torch.int32, device=DEV), info=info)
+    torch.cuda.synchronize()
+    assert y.shape == (0, n) and info.kernel == 5 and info.grid_x == 0
