@@ -341,7 +341,7 @@ def fp4_w4a16_moe_decode(x, prep_codes, prep_scales, n, experts, global_scales, 
 def fp4_w4a16_moe_prefill(x, prep_codes, prep_scales, n, experts, global_scales, fmt, expert_offsets,
                           pair_tokens, y=None, workspace=None, stream=None, info=None):
     """Grouped MoE on the tile GEMM, for routings that give experts many pairs: the same arguments and
-    result as fp4_w4a16_moe_decode."""
+    result as fp4_w4a16_moe_decode (no workspace needed)."""
     return _moe("fp4_w4a16_moe_prefill", x, prep_codes, prep_scales, n, experts, global_scales, fmt,
                 expert_offsets, pair_tokens, y, workspace, stream, info)
 
@@ -369,7 +369,8 @@ def _moe(name, x, prep_codes, prep_scales, n, experts, global_scales, fmt, exper
     _need(y, torch.bfloat16, "y")
     if y.numel() != pairs * n:
         raise ValueError("y must hold pairs x n values")
-    need = fp4_moe_workspace_bytes(pairs, k)
+    # The tile route reads x directly; only the decode route gathers the rows.
+    need = 0 if name == "fp4_w4a16_moe_prefill" else fp4_moe_workspace_bytes(pairs, k)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

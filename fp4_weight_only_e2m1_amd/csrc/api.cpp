@@ -244,11 +244,12 @@ int run_w4a4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_
 
 namespace {
 
-// Checks shared by the grouped MoE entry points; FP4_OK with *no_pairs set
-// means there is nothing to compute.
+// Checks shared by the grouped MoE entry points (the workspace only where
+// the route gathers the x rows); FP4_OK with *no_pairs set means there is
+// nothing to compute.
 int check_moe(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev,
               int n, int experts, const float* global_scales_dev, int fmt, const int32_t* expert_offsets_dev,
-              const int32_t* pair_tokens_dev, int pairs, const uint16_t* y_dev, const void* workspace_dev,
+              const int32_t* pair_tokens_dev, int pairs, const uint16_t* y_dev, bool gathers, const void* workspace_dev,
               size_t workspace_bytes, bool* no_pairs) {
   int st = check_fmt(fmt);
   if (st) return st;
@@ -265,6 +266,7 @@ int check_moe(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_code
       reinterpret_cast<uintptr_t>(expert_offsets_dev) % 4 != 0 || reinterpret_cast<uintptr_t>(pair_tokens_dev) % 4 != 0 ||
       (!mx && reinterpret_cast<uintptr_t>(global_scales_dev) % 4 != 0))
     return FP4_EALIGN;
+  if (!gathers) return FP4_OK;
   size_t need = 0;
   if ((st = fp4_moe_workspace_bytes(pairs, k, &need))) return st;
   if (workspace_bytes < need) return FP4_EWORKSPACE;
@@ -274,10 +276,13 @@ int check_moe(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_code
 }
 
 fp4::MoeArgs moe_args(const fp4::PreparedShape& ps, int fmt, const float* global_scales_dev,
-                      const int32_t* expert_offsets_dev, int pairs, int experts, const void* workspace_dev) {
+                      const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int tokens, int pairs,
+                      int experts, const void* workspace_dev) {
   fp4::MoeArgs moe{};
   moe.offsets = expert_offsets_dev;
   moe.x_sorted = static_cast<const uint16_t*>(workspace_dev);
+  moe.tokens = pair_tokens_dev;
+  moe.tokens_total = tokens;
   moe.gscales = fmt == FP4_FMT_MXFP4 ? nullptr : global_scales_dev;
   moe.code_stride = ps.code_bytes;
   moe.scale_stride = ps.scale_bytes;
@@ -429,7 +434,8 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t
                          fp4_dispatch_info* info_out) {
   bool no_pairs = false;
   const int st = check_moe(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n, experts, global_scales_dev, fmt,
-                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, workspace_dev, workspace_bytes, &no_pairs);
+                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, true, workspace_dev, workspace_bytes,
+                           &no_pairs);
   if (st) return st;
   if (no_pairs) {
     if (info_out) *info_out = fp4_dispatch_info{3, 1, 0, 0, 0};
@@ -455,7 +461,8 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t
   a.ldy = n;
   a.gscale[0] = a.gscale[1] = 1.0f;
   a.tile_rows = fp4::kDecodeTileRows;
-  const fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pairs, experts, workspace_dev);
+  const fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pair_tokens_dev, tokens, pairs,
+                                    experts, workspace_dev);
   dim3 grid, block;
   const hipError_t e = fp4::launch_moe_decode(a, moe, experts, x_dev, pair_tokens_dev, tokens,
                                               static_cast<uint16_t*>(workspace_dev), fmt, stream, &grid, &block);
@@ -472,7 +479,8 @@ int fp4_w4a16_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_
                           fp4_dispatch_info* info_out) {
   bool no_pairs = false;
   const int st = check_moe(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n, experts, global_scales_dev, fmt,
-                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, workspace_dev, workspace_bytes, &no_pairs);
+                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, false, workspace_dev, workspace_bytes,
+                           &no_pairs);
   if (st) return st;
   if (no_pairs) {
     if (info_out) *info_out = fp4_dispatch_info{5, 1, 0, 0, 0};
@@ -499,10 +507,9 @@ int fp4_w4a16_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_
   a.ldy = n;
   a.gscale[0] = a.gscale[1] = 1.0f;
   a.plan = fp4::gemm_plan(fp4::kGemmBM, a.rows_total, k);  // only n_tiles and ksteps are used
-  const fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pairs, experts, workspace_dev);
-  if (fp4::launch_moe_gather(x_dev, pair_tokens_dev, pairs, k, tokens, static_cast<uint16_t*>(workspace_dev),
-                             stream) != hipSuccess)
-    return FP4_EHIP;
+  a.x = x_dev;
+  const fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pair_tokens_dev, tokens, pairs,
+                                    experts, nullptr);
   dim3 grid, block;
   if (fp4::launch_moe_gemm(a, moe, fmt, stream, &grid, &block) != hipSuccess) return FP4_EHIP;
   if (info_out) *info_out = fp4_dispatch_info{5, 1, static_cast<int>(grid.x), 0, static_cast<int>(block.x)};

@@ -145,7 +145,9 @@ struct GemvArgs {
 // Grouped MoE decode: routed (token, expert) pairs sorted by expert.
 struct MoeArgs {
   const int32_t* offsets;    // [experts + 1]: expert e's pairs are [offsets[e], offsets[e + 1])
-  const uint16_t* x_sorted;  // bf16 [pairs][k]: x row of each pair (gathered)
+  const uint16_t* x_sorted;  // bf16 [pairs][k]: x row of each pair (gathered; decode route)
+  const int32_t* tokens;     // [pairs]: x row of each pair (tile route, which reads x directly)
+  int tokens_total;          // rows of x
   const float* gscales;      // [experts] NVFP4 global scales, or null (MXFP4)
   int64_t code_stride;       // bytes between experts' prepared codes
   int64_t scale_stride;      // bytes between experts' prepared scales
@@ -274,6 +276,9 @@ struct MfmaArgs {
   const uint8_t* xq_codes;
   const uint8_t* xq_scales;
   int64_t act_k;
+  // Grouped MoE tile route only: tile row r reads x row row_tokens[r] (rows of x: tokens_total).
+  const int32_t* row_tokens;
+  int tokens_total;
 };
 
 // Launchers (defined in the .hip files).  Each returns the hipError_t of its

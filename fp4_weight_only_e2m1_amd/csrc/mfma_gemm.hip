@@ -125,11 +125,16 @@ __device__ __forceinline__ void wait_stages_barrier(int wave) {
 //   code k on.  So they are bf16 zeros, whatever x holds beyond its row.
 // Every lane issues every copy, so each wave has the same number in flight
 // per stage.
-template <int FMT, int FI>
+// GATHER (grouped MoE): tile row r is the x row of token row_tokens[m0 + r]
+// (rows past m repeat row m - 1), fetched through a per-lane address; a
+// token id outside [0, tokens_total) fetches row 0 instead, and the kernel
+// zeroes that row's sums (zero_rows_of_bad_tokens).
+template <int FMT, int FI, bool GATHER = false>
 struct Copier {
   static constexpr int P = Cfg<FMT>::P;
   static constexpr int kXPer = FI * kAPer / 4;  // x chunks per thread per stage
   const uint16_t* xt;    // x row m0
+  const uint8_t* xrow[GATHER ? kXPer : 1];  // GATHER: this lane's chunk of its row at k = 0
   const uint8_t* ct;     // code row n0
   const uint8_t* st;     // scale row group n0 / 16
   const uint8_t* zeros;  // 16 zero bytes: code row n0 from code k on
@@ -151,8 +156,15 @@ struct Copier {
       const int r = p >> 3;
       const int c = (p & 7) ^ ((r >> 1) & 7);
       const int64_t rr = m0 + r < a.m ? r : a.m - 1 - m0;
-      xoff[i] = static_cast<uint32_t>(rr * a.k * 2 + 16 * c);
       xk[i] = 8 * c;
+      if constexpr (GATHER) {
+        int tok = a.row_tokens[m0 + rr];
+        if (tok < 0 || tok >= a.tokens_total) tok = 0;
+        xrow[i] = reinterpret_cast<const uint8_t*>(a.x + static_cast<int64_t>(tok) * a.k) + 16 * c;
+        xoff[i] = 0;
+      } else {
+        xoff[i] = static_cast<uint32_t>(rr * a.k * 2 + 16 * c);
+      }
     }
 #pragma unroll
     for (int i = 0; i < kBPer; ++i) {
@@ -174,7 +186,14 @@ struct Copier {
   __device__ __forceinline__ void issue(int64_t k0, bool ragged, Stage<FMT>& sb, int wave) const {
     const uint32_t la = lds_addr(sb.a) + lds_wave_a;
     const uint32_t lb = lds_addr(sb.b) + lds_wave_b;
-    if (!ragged) {
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int i = 0; i < kXPer; ++i) {
+        const bool in_k = !ragged || k0 + xk[i] < k;
+        copy16_vaddr(in_k ? static_cast<const void*>(xrow[i] + 2 * k0) : static_cast<const void*>(zeros),
+                     la + i * kThreads * 16);
+      }
+    } else if (!ragged) {
       const uint16_t* xb = xt + k0;
 #pragma unroll
       for (int i = 0; i < kXPer; ++i) copy16_sbase(xb, xoff[i], la + i * kThreads * 16);
@@ -310,8 +329,8 @@ __device__ __forceinline__ void schedule_step() {
 // ks + 1 (whose copies the wait before the barrier saw land) is complete in
 // `nxt`, so its codes and step-0 fragments are read and decoded under the
 // last MFMAs -- the next stage starts with its MFMAs ready to issue.
-template <int FMT, int FI>
-__device__ __forceinline__ void pipeline_step(const Copier<FMT, FI>& cp, int ks, int k_end, int ragged_ks,
+template <int FMT, int FI, bool GATHER>
+__device__ __forceinline__ void pipeline_step(const Copier<FMT, FI, GATHER>& cp, int ks, int k_end, int ragged_ks,
                                               Stage<FMT>& cur, const Stage<FMT>& nxt, int wave, int xr0, int wr0,
                                               int lh, Regs<FMT, FI>& r, f32x16_t (&acc)[FI][2]) {
   Frag xn[FI], wn[2];
@@ -349,7 +368,7 @@ __device__ __forceinline__ void pipeline_step(const Copier<FMT, FI>& cp, int ks,
 __device__ __forceinline__ float act_silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // acc = the (m0, n0) tile's sums over K steps [k_begin, k_end).
-template <int FMT, int FI>
+template <int FMT, int FI, bool GATHER = false>
 __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t n0, int k_begin, int k_end,
                                          Stage<FMT> (&st)[kStages], f32x16_t (&acc)[FI][2]) {
   const int t = threadIdx.x;
@@ -369,7 +388,7 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const Copier<FMT, FI> cp(a, m0, n0, t, wave);
+  const Copier<FMT, FI, GATHER> cp(a, m0, n0, t, wave);
   // Prologue: three stages in flight, wait for the first, read its codes
   // and step-0 fragments.
   cp.issue(static_cast<int64_t>(k_begin) * kGemmBK, k_begin == ragged_ks, st[0], wave);
@@ -390,7 +409,7 @@ __device__ __forceinline__ void run_tile(const MfmaArgs& a, int64_t m0, int64_t 
   int cur = 0;
   for (int ks = k_begin; ks < k_end; ++ks) {
     const int nxt = cur == kStages - 1 ? 0 : cur + 1;
-    pipeline_step<FMT, FI>(cp, ks, k_end, ragged_ks, st[cur], st[nxt], wave, xr0, wr0, lh, r, acc);
+    pipeline_step<FMT, FI, GATHER>(cp, ks, k_end, ragged_ks, st[cur], st[nxt], wave, xr0, wr0, lh, r, acc);
     cur = nxt;
   }
 }
@@ -447,22 +466,45 @@ void gemm_kernel(const MfmaArgs a) {
 }
 
 // Grouped MoE prefill: the routed (token, expert) pairs sorted by expert,
-// their x rows gathered in pair order (x_sorted), expert e owning pairs
-// [offsets[e], offsets[e + 1]).  Counted in expert order, expert e's c_e
-// pairs form ceil(c_e / 128) activation tiles of 128 of its gathered rows;
+// expert e owning pairs [offsets[e], offsets[e + 1]), pair p reading x row
+// tokens[p].  Counted in expert order, expert e's c_e pairs form
+// ceil(c_e / 128) activation tiles of 128 of its pairs, whose x rows the
+// stage copies fetch straight from x (no gathered copy);
 // workgroup b computes weight-row tile b % n_tiles of the (b / n_tiles)-th
 // such tile, over all of K, with that expert's prepared weight, and stores
 // bf16 y at the same pair rows.  Each tile's sums are the dense GEMM's for
 // those rows (same K steps, same MFMA order), so a pair's output does not
 // depend on the other pairs.  The grid has moe_gemm_slots(pairs, experts)
 // tile slots, enough for every tile when the offsets are non-decreasing;
-// slots past the last tile exit.  Offsets are clamped to [0, pairs], so no
-// routing table can make a workgroup touch memory outside x_sorted and y.
+// slots past the last tile exit.  Offsets are clamped to [0, pairs] and
+// token ids outside [0, tokens_total) read zero rows, so no routing table can
+// make a workgroup touch memory outside x, the weights and y.
 __device__ __forceinline__ void moe_range(const MoeArgs& moe, int e, int& p0, int& p1) {
   p0 = moe.offsets[e];
   p1 = moe.offsets[e + 1];
   p0 = p0 < 0 ? 0 : p0 > moe.pairs ? moe.pairs : p0;
   p1 = p1 < p0 ? p0 : p1 > moe.pairs ? moe.pairs : p1;
+}
+
+// The sums of tile rows whose token id is outside [0, tokens_total) become
+// zero (their x rows were fetched from row 0): lane l holds activation row
+// 32 i + l % 32 of the tile in acc[i].
+template <int FI>
+__device__ __forceinline__ void zero_rows_of_bad_tokens(const MfmaArgs& a, int64_t m0, f32x16_t (&acc)[FI][2]) {
+  const int l32 = threadIdx.x & 31;
+#pragma unroll
+  for (int i = 0; i < FI; ++i) {
+    const int64_t m = m0 + 32 * i + l32;
+    if (m < a.m) {
+      const int tok = a.row_tokens[m];
+      if (tok < 0 || tok >= a.tokens_total) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      }
+    }
+  }
 }
 
 template <int FMT>
@@ -508,7 +550,8 @@ void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
   const int p1 = __builtin_amdgcn_readfirstlane(s_p1);
   const int tile = __builtin_amdgcn_readfirstlane(s_tile);
   MfmaArgs a = base;
-  a.x = moe.x_sorted + static_cast<int64_t>(p0) * a.k;
+  a.row_tokens = moe.tokens + p0;
+  a.tokens_total = moe.tokens_total;
   a.y = base.y + static_cast<int64_t>(p0) * a.ldy;
   a.m = p1 - p0;
   a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
@@ -523,15 +566,18 @@ void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
   // blocks, as the dense kernel's instances for small m do.
   if (rows > 64) {
     f32x16_t acc[4][2];
-    run_tile<FMT, 4>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    run_tile<FMT, 4, true>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    zero_rows_of_bad_tokens<4>(a, m0, acc);
     store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 4>(a, m0, n0, wave, acc, lds);
   } else if (rows > 32) {
     f32x16_t acc[2][2];
-    run_tile<FMT, 2>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    run_tile<FMT, 2, true>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    zero_rows_of_bad_tokens<2>(a, m0, acc);
     store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 2>(a, m0, n0, wave, acc, lds);
   } else {
     f32x16_t acc[1][2];
-    run_tile<FMT, 1>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    run_tile<FMT, 1, true>(a, m0, n0, 0, a.plan.ksteps, st, acc);
+    zero_rows_of_bad_tokens<1>(a, m0, acc);
     store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 1>(a, m0, n0, wave, acc, lds);
   }
 }

@@ -271,11 +271,13 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k,
                          hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
- * Grouped MoE prefill: the same operation, arguments, workspace, checks and
- * containment of routing data as fp4_w4a16_moe_decode, for routings that give
- * experts many pairs (prefill batches): after the gather, one launch of the
- * MFMA tile GEMM over 128-row tiles of each expert's gathered rows, so an
- * expert's weight is read once per 128 of its pairs instead of once per 8.
+ * Grouped MoE prefill: the same operation, arguments, checks and containment
+ * of routing data as fp4_w4a16_moe_decode, for routings that give experts
+ * many pairs (prefill batches): one launch of the MFMA tile GEMM over 128-row
+ * tiles of each expert's pairs, so an expert's weight is read once per 128 of
+ * its pairs instead of once per 8.  The tile's stage copies fetch each pair's
+ * x row straight from x_dev, so no workspace is used: workspace_dev and
+ * workspace_bytes are ignored (NULL and 0 are fine).
  * Workgroup slots: the tiles of all experts in expert order, at most
  * ceil(pairs / 128) + min(experts, pairs) of them (every tile, when the
  * offsets are non-decreasing), times ceil(n / 256) weight tiles; FP4_EINVAL
