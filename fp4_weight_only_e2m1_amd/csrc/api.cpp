@@ -36,10 +36,10 @@ size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
   // fill a round.
   if (m < 1) return 0;
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
-  if (m > fp4::kGemvMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
+  if (m > fp4::kDecodeMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
   const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
   const int splits = on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
-  const int tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(rows_total)
+  const int tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(rows_total, m)
                                 : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
   return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total, tile_rows));
 }
@@ -54,9 +54,9 @@ uint64_t next_token() {
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_EHIP; }
 
-// Rows per workgroup of the decode kernel m selects (m = 1..8).
+// Rows per workgroup of the decode kernel m selects (m = 1..16).
 int decode_tile_rows(int m, int64_t rows_total) {
-  return m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_tile_rows(rows_total)
+  return m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_tile_rows(rows_total, m)
                                    : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
 }
 
@@ -70,7 +70,7 @@ size_t argmax_workspace_for(int m, int n, int k, int fmt, size_t* keys_offset) {
 }
 
 size_t act_workspace_for(int m, int n_half, int k, int fmt) {
-  if (m <= fp4::kGemvMaxM) return workspace_for(m, n_half, k, fmt, 2);
+  if (m <= fp4::kDecodeMaxM) return workspace_for(m, n_half, k, fmt, 2);
   const int64_t rows_total = 2 * fp4::round_up(n_half, fp4::kRowAlign);
   return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
 }
@@ -88,9 +88,9 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
   if ((st = check_m(m))) return st;
   if (static_cast<int64_t>(n_proj) * projections > FP4_MAX_N) return FP4_EINVAL;
   const bool argmax = idx != nullptr;
-  if (argmax && (m > fp4::kGemvMaxM || projections != 1)) return FP4_EINVAL;
+  if (argmax && (m > fp4::kDecodeMaxM || projections != 1)) return FP4_EINVAL;
   if (m == 0) {
-    if (info) *info = fp4_dispatch_info{m <= fp4::kGemvMaxM ? 0 : 1, 0, 0, 0, 0};
+    if (info) *info = fp4_dispatch_info{0, 0, 0, 0, 0};
     return FP4_OK;
   }
   if (!x || !codes || !scales || (!y && !argmax)) return FP4_EINVAL;
@@ -110,7 +110,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
   const fp4::PreparedShape ps = fp4::prepared_shape(n_proj, k, fmt);
   const bool mx = fmt == FP4_FMT_MXFP4;
   dim3 grid, block;
-  if (m <= fp4::kGemvMaxM) {
+  if (m <= fp4::kDecodeMaxM) {
     fp4::GemvArgs a{};
     a.x = x;
     a.codes = codes;
@@ -405,7 +405,7 @@ int fp4_argmax_workspace_bytes(int m, int n, int k, int fmt, size_t* bytes_out) 
   int st = check_fmt(fmt);
   if (st) return st;
   if ((st = check_nk(n, k))) return st;
-  if (m < 0 || m > fp4::kGemvMaxM || !bytes_out) return FP4_EINVAL;
+  if (m < 0 || m > fp4::kDecodeMaxM || !bytes_out) return FP4_EINVAL;
   *bytes_out = m == 0 ? 0 : argmax_workspace_for(m, n, k, fmt, nullptr);
   return FP4_OK;
 }

@@ -82,7 +82,7 @@ __device__ __forceinline__ uint64_t argmax_key(uint16_t b, int64_t col) {
 // writes the tile's best key per row to keys[tile][m].  Every step is a
 // maximum, so the order does not matter.
 struct TileArgmax {
-  unsigned long long best[kGemvMaxM];
+  unsigned long long best[kDecodeMaxM];
 };
 template <int M>
 struct ArgmaxLocal {
@@ -92,7 +92,7 @@ template <int M>
 __device__ __forceinline__ void tile_argmax_begin(TileArgmax& ta, ArgmaxLocal<M>& l) {
 #pragma unroll
   for (int mm = 0; mm < M; ++mm) l.best[mm] = 0;
-  if (threadIdx.x < kGemvMaxM) ta.best[threadIdx.x] = 0ull;
+  if (threadIdx.x < kDecodeMaxM) ta.best[threadIdx.x] = 0ull;
   __syncthreads();
 }
 template <int M>

@@ -15,7 +15,8 @@
 // workgroups fit a CU, and more workgroups beat deeper per-workgroup
 // pipelines):
 //   codes   64 rows x 128 bytes  (8 KiB: one full 128-byte line per row)
-//   x       8 rows x 256 bf16    (4 KiB; rows >= m are never read back)
+//   x       XR rows x 256 bf16   (XR = 8 for m <= 8, else 16: 4 or 8 KiB;
+//                                 rows >= m are never read back)
 //   scales  of those codes       (1 KiB)
 // A wave then reads, per 128-code block, one 16-byte code chunk per lane,
 // decodes its 4 words and issues 4 MFMAs against x fragments read from LDS.
@@ -50,13 +51,18 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = kDecodeThreads;  // 4 waves
 constexpr int kStageK = kDecodeStageK;     // 256 codes
-constexpr int kXChunks = 8 * kStageK * 2 / 16;  // 256 x chunks per stage (8 rows)
-static_assert(kXChunks == kThreads, "one x copy per lane");
 static_assert(kStageK == 256, "layout below assumes stages of 256 codes");
 
-// Tile geometry for RB row blocks of 16 per wave (a 64 RB-row tile).
-template <int RB, int FMT>
+// x rows staged per stage for calls of up to M activation rows.
+template <int M>
+constexpr int kXRows = M > 8 ? 16 : 8;
+
+// Tile geometry for RB row blocks of 16 per wave (a 64 RB-row tile) and XR
+// staged x rows.
+template <int RB, int FMT, int XR>
 struct Geo {
+  static constexpr int kXChunks = XR * kStageK * 2 / 16;  // 256 or 512 x chunks per stage
+  static constexpr int kXPer = kXChunks / kThreads;        // x copies per lane: 1 or 2
   static constexpr int kRows = 64 * RB;
   static constexpr int kWChunks = kRows * kStageK / 2 / 16;  // 512 RB code chunks per stage
   static constexpr int kWPer = kWChunks / kThreads;           // 2 RB copies per lane
@@ -66,14 +72,14 @@ struct Geo {
   static constexpr int kSChunks = 64 * kSWaves;               // incl. unused duplicates
   // Load-to-LDS copies per lane per stage: codes and x, plus one scale chunk
   // in waves < kSWaves.
-  static constexpr int kLoads = kWPer + 1;
+  static constexpr int kLoads = kWPer + kXPer;
 };
 
-template <int RB, int FMT>
+template <int RB, int FMT, int XR>
 struct alignas(16) Stage {
-  uint4 w[Geo<RB, FMT>::kWChunks];
-  uint4 x[kXChunks];
-  uint4 s[Geo<RB, FMT>::kSChunks];
+  uint4 w[Geo<RB, FMT, XR>::kWChunks];
+  uint4 x[Geo<RB, FMT, XR>::kXChunks];
+  uint4 s[Geo<RB, FMT, XR>::kSChunks];
 };
 
 union Frag {
@@ -89,13 +95,13 @@ union Frag {
 // c ^ ((rr >> 1) & 7); the 16 lanes reading one chunk index of 16 consecutive
 // rows hit bank groups 8 (rr & 1) + slot, all distinct.
 __device__ __forceinline__ int w_slot(int rr, int c) { return rr * 8 + (c ^ ((rr >> 1) & 7)); }
-// x: row xr (0..7) holds 32 chunks of 8 bf16 at xr * 512, chunk ch in slot
-// ch ^ xr: the m <= 8 rows read together hit distinct bank groups.
+// x: row xr (0..XR-1) holds 32 chunks of 8 bf16 at xr * 512, chunk ch in
+// slot ch ^ xr: the rows read together hit distinct bank groups.
 __device__ __forceinline__ int x_slot(int xr, int ch) { return xr * 32 + (ch ^ xr); }
 
-template <int RB, int FMT, int STAGES>
+template <int RB, int FMT, int XR, int STAGES>
 __device__ __forceinline__ void wait_stages_barrier(int wave) {
-  using G = Geo<RB, FMT>;
+  using G = Geo<RB, FMT, XR>;
   if (wave < G::kSWaves)
     wait_vm_barrier<STAGES * (G::kLoads + 1)>();
   else
@@ -111,15 +117,16 @@ __device__ __forceinline__ void wait_stages_barrier(int wave) {
 // scales with the default policy.
 template <int M, int FMT, int RB>
 struct Copier {
-  using G = Geo<RB, FMT>;
+  static constexpr int XR = kXRows<M>;
+  using G = Geo<RB, FMT, XR>;
   static constexpr int P = G::P;
   const uint16_t* x;
   const uint8_t* ct;     // code row row0
   const uint8_t* st;     // scale row group row0 / 16
   const uint8_t* zeros;  // 16 zero bytes
-  uint32_t woff[G::kWPer], xoff, soff;
-  int xk;                // first code of this lane's x chunk within a stage
-  bool xrow_ok;
+  uint32_t woff[G::kWPer], xoff[G::kXPer], soff;
+  int xk[G::kXPer];      // first code of this lane's x chunks within a stage
+  bool xrow_ok[G::kXPer];
   int k;
   uint32_t lds_wave;     // this wave's 1 KiB slice of a stage area
 
@@ -137,11 +144,15 @@ struct Copier {
       const int c = (p & 7) ^ ((rr >> 1) & 7);
       woff[i] = static_cast<uint32_t>(rr * row_bytes + 16 * c);
     }
-    const int xr = t >> 5;
-    const int ch = (t & 31) ^ xr;
-    xrow_ok = xr < mrows;
-    xoff = xrow_ok ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
-    xk = 8 * ch;
+#pragma unroll
+    for (int i = 0; i < G::kXPer; ++i) {
+      const int p = i * kThreads + t;
+      const int xr = p >> 5;
+      const int ch = (p & 31) ^ xr;
+      xrow_ok[i] = xr < mrows;
+      xoff[i] = xrow_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
+      xk[i] = 8 * ch;
+    }
     // Scales of a stage: 4 RB row groups x 8 segments x 16 rows x P bytes,
     // 128 P contiguous bytes per row group (cpg chunks).  Lane l of scale
     // wave w lands at chunk 64 w + l of the stage's scale area and fetches
@@ -154,16 +165,19 @@ struct Copier {
     lds_wave = 64 * 16 * wave;
   }
 
-  __device__ __forceinline__ void issue(int64_t k0, Stage<RB, FMT>& sb, int wave) const {
+  __device__ __forceinline__ void issue(int64_t k0, Stage<RB, FMT, XR>& sb, int wave) const {
     const uint32_t lw = lds_addr(sb.w) + lds_wave;
     const uint8_t* cb = ct + k0 / 2;
 #pragma unroll
     for (int i = 0; i < G::kWPer; ++i) copy16_sbase_nt(cb, woff[i], lw + i * kThreads * 16);
-    const bool in_k = k0 + xk < k;
-    const void* xs = !xrow_ok ? static_cast<const void*>(x)
-                     : in_k   ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff)
-                              : static_cast<const void*>(zeros);
-    copy16_vaddr(xs, lds_addr(sb.x) + lds_wave);
+#pragma unroll
+    for (int i = 0; i < G::kXPer; ++i) {
+      const bool in_k = k0 + xk[i] < k;
+      const void* xs = !xrow_ok[i] ? static_cast<const void*>(x)
+                       : in_k      ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff[i])
+                                   : static_cast<const void*>(zeros);
+      copy16_vaddr(xs, lds_addr(sb.x) + lds_wave + i * kThreads * 16);
+    }
     if (wave < G::kSWaves) copy16_sbase(st + (k0 / 32) * kRowGroup * P, soff, lds_addr(sb.s) + lds_wave);
   }
 };
@@ -202,7 +216,7 @@ struct alignas(256) ZeroRow {
 // its RB row blocks; each x fragment read from LDS feeds RB MFMAs.  zrow: the
 // zero row the lanes of rows r >= m read instead of x.
 template <int M, int FMT, int RB>
-__device__ __forceinline__ void compute_stage(const Stage<RB, FMT>& sb, const uint4* zrow, int wave, int r, int g,
+__device__ __forceinline__ void compute_stage(const Stage<RB, FMT, kXRows<M>>& sb, const uint4* zrow, int wave, int r, int g,
                                               int mrows, f32x4_t (&acc)[RB]) {
   constexpr int P = scales_per_seg(FMT);
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sb.s);
@@ -245,16 +259,16 @@ __device__ __forceinline__ void compute_stage(const Stage<RB, FMT>& sb, const ui
 
 // Wait until stage s has landed -- with NB buffers, up to NB - 2 younger
 // stages stay in flight -- and join the workgroup barrier.
-template <int RB, int FMT, int NB>
+template <int RB, int FMT, int XR, int NB>
 __device__ __forceinline__ void wait_for_stage(int s, int s1, int wave) {
   if constexpr (NB > 2) {
     if (s + NB - 2 < s1) {
-      wait_stages_barrier<RB, FMT, NB - 2>(wave);
+      wait_stages_barrier<RB, FMT, XR, NB - 2>(wave);
       return;
     }
-    wait_for_stage<RB, FMT, NB - 1>(s, s1, wave);
+    wait_for_stage<RB, FMT, XR, NB - 1>(s, s1, wave);
   } else {
-    wait_stages_barrier<RB, FMT, 0>(wave);
+    wait_stages_barrier<RB, FMT, XR, 0>(wave);
   }
 }
 
@@ -263,9 +277,10 @@ __device__ __forceinline__ void wait_for_stage(int s, int s1, int wave) {
 // with stage s + NB - 1, consume `cur`.
 template <int M, int FMT, int RB, int NB>
 __device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB>& cp, int s, int s1,
-                                              const Stage<RB, FMT>& cur, Stage<RB, FMT>& prev, const uint4* zrow,
-                                              int wave, int r, int g, int mrows, f32x4_t (&acc)[RB]) {
-  wait_for_stage<RB, FMT, NB>(s, s1, wave);
+                                              const Stage<RB, FMT, kXRows<M>>& cur, Stage<RB, FMT, kXRows<M>>& prev,
+                                              const uint4* zrow, int wave, int r, int g, int mrows,
+                                              f32x4_t (&acc)[RB]) {
+  wait_for_stage<RB, FMT, kXRows<M>, NB>(s, s1, wave);
   if (s + NB - 1 < s1) cp.issue(static_cast<int64_t>(s + NB - 1) * kStageK, prev, wave);
   compute_stage<M, FMT, RB>(cur, zrow, wave, r, g, mrows, acc);
 }
@@ -274,9 +289,9 @@ __device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB>& cp, int 
 // launched per call; the rows of one expert in the grouped MoE launch).
 template <int M, int FMT, int RB, int NB>
 __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int split, int mrows) {
-  __shared__ Stage<RB, FMT> st[NB];
+  __shared__ Stage<RB, FMT, kXRows<M>> st[NB];
   __shared__ ZeroRow zero_row;
-  constexpr int kRows = Geo<RB, FMT>::kRows;
+  constexpr int kRows = Geo<RB, FMT, kXRows<M>>::kRows;
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -326,7 +341,7 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
       return;
     }
     if (a.keys) {
-      if (t < kGemvMaxM) ta.best[t] = 0ull;
+      if (t < kDecodeMaxM) ta.best[t] = 0ull;
       __syncthreads();
     }
 #pragma unroll
@@ -482,7 +497,23 @@ hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
     case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, FMT, RB, NB>), grid, block, 0, stream, a); break;
     case 7: hipLaunchKernelGGL((decode_mfma_kernel<7, FMT, RB, NB>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, FMT, RB, NB>), grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+    default:
+      // m = 9..16 (16-row x stages) run on 64-row tiles only.
+      if constexpr (RB == 1) {
+        switch (a.m) {
+          case 9: hipLaunchKernelGGL((decode_mfma_kernel<9, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 10: hipLaunchKernelGGL((decode_mfma_kernel<10, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 11: hipLaunchKernelGGL((decode_mfma_kernel<11, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 12: hipLaunchKernelGGL((decode_mfma_kernel<12, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 13: hipLaunchKernelGGL((decode_mfma_kernel<13, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 14: hipLaunchKernelGGL((decode_mfma_kernel<14, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 15: hipLaunchKernelGGL((decode_mfma_kernel<15, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 16: hipLaunchKernelGGL((decode_mfma_kernel<16, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          default: return hipErrorInvalidValue;
+        }
+      } else {
+        return hipErrorInvalidValue;
+      }
   }
   return hipGetLastError();
 }

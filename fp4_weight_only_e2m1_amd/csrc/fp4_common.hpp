@@ -25,6 +25,11 @@ constexpr int kTargetCUs = 256;      // MI355X compute units
 // m from which the decode path contracts on MFMA instead of VALU v_dot2
 // (measured crossover on MI355X: the VALU GEMV is faster at m = 1, 2).
 constexpr int kDecodeMfmaMinM = 3;
+// Largest m the decode path serves.  The MFMA decode kernel's 16x16x32 MFMA
+// computes 16 activation rows whatever m is (the rows past m read zeros), so
+// m = 9..16 costs it the same matrix-core work as m = 8 and only a second x
+// copy per stage (its x stages hold 16 rows instead of 8).
+constexpr int kDecodeMaxM = 16;
 // k-extent of one stage of the MFMA decode kernel (codes), and its LDS stage
 // buffers (all but one in flight).
 constexpr int kDecodeStageK = 256;
@@ -115,7 +120,11 @@ inline int decode_mfma_splits(int n_proj, int k) {
 // where 128-row tiles still leave thousands of workgroups.  Such layers are
 // never split along K (decode_mfma_splits), and the tile size changes which
 // rows a workgroup holds, never an output's summation order.
-inline int decode_mfma_tile_rows(int64_t rows_total) { return rows_total / kDecodeTileRows >= 2048 ? 128 : 64; }
+// Calls of more than 8 rows keep 64-row tiles: their 16-row x stages would
+// leave the 128-row tile one workgroup per CU.
+inline int decode_mfma_tile_rows(int64_t rows_total, int m) {
+  return m <= 8 && rows_total / kDecodeTileRows >= 2048 ? 128 : 64;
+}
 
 struct GemvArgs {
   const uint16_t* x;      // bf16 [m][k]

@@ -65,8 +65,8 @@ enum fp4_status {
 
 /* Which kernel a call ran (filled when the caller passes a non-null pointer). */
 typedef struct fp4_dispatch_info {
-  int kernel;  /* 0 = VALU decode GEMV, 2 = MFMA decode GEMV (both m <= 8),
-                  1 = MFMA tile GEMM (m > 8), 3 = grouped MoE decode,
+  int kernel;  /* 0 = VALU decode GEMV (m = 1, 2), 2 = MFMA decode GEMV
+                  (m = 3..16), 1 = MFMA tile GEMM (m > 16), 3 = grouped MoE decode,
                   4 = W4A4 MXFP4 tile GEMM (any m),
                   5 = grouped MoE tile GEMM (prefill) */
   int splits;  /* K splits: decode kernels split every tile, the tile GEMMs only
@@ -121,8 +121,8 @@ int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scale
 /*
  * Workspace a compute call needs, in bytes (0 when none), for split-K fp32
  * partials and arrival flags: the m = 1, 2 decode GEMV with k > 4096, the
- * m = 3..8 MFMA decode on layers of fewer than 8192 rows per projection, and
- * the m > 8 tile GEMM when its 128 x 256 output tiles do not fill whole
+ * m = 3..16 MFMA decode on layers of fewer than 8192 rows per projection, and
+ * the m > 16 tile GEMM when its 128 x 256 output tiles do not fill whole
  * rounds of the 512 workgroups resident on the chip (the tail tiles are then
  * split along K; at most 64 MiB).  It never needs zeroing.  `projections` is 1 for
  * fp4_w4a16_linear (n = output features) and 2 for fp4_w4a16_gate_up
@@ -141,8 +141,8 @@ int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* b
  *   info_out  optional, may be NULL.
  * Accumulation is float32.  The order of every sum depends only on (k, fmt, n)
  * and on which kernel m selects (fp4_dispatch_info.kernel) -- for the tile
- * GEMM (m > 8) also on m, which decides the tiles summed in K splits -- so
- * results are deterministic run to run, and for m <= 8 a row's result does
+ * GEMM (m > 16) also on m, which decides the tiles summed in K splits -- so
+ * results are deterministic run to run, and for m <= 16 a row's result does
  * not depend on the other rows of the call as long as m selects the same
  * kernel.
  * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list (the W4A16
@@ -179,8 +179,8 @@ int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k,
  * twice fp4_prepared_bytes(n_half, k, fmt)), which interleaves gate and up
  * rows in groups of 16 (prepared row R: gate row 16 (R / 32) + R % 16 when
  * R % 32 < 16, else the up row with that index) so that both operands of an
- * output are computed by one workgroup.  m <= 8: the decode kernels form y in
- * their epilogue; m > 8: the tile GEMM forms y in the epilogue of every whole
+ * output are computed by one workgroup.  m <= 16: the decode kernels form y in
+ * their epilogue; m > 16: the tile GEMM forms y in the epilogue of every whole
  * tile, and its reduce launch forms y for the tail tiles split along K.
  * Workspace: fp4_swiglu_workspace_bytes (the split-K partials and flags of
  * the same plan as fp4_w4a16_gate_up).  silu uses the hardware exp and
@@ -205,7 +205,7 @@ int fp4_w4a16_gate_up_swiglu(const uint16_t* x_dev, int m, int k,
  * Greedy token of a decode call: idx_out_dev[i] (int32) = the index j of the
  * largest logit y[i][j] -- the bf16 value fp4_w4a16_linear gives for the same
  * arguments -- and the lowest such j when several are equal; -0 equals +0
- * and a NaN counts as larger than every number.  m = 1..8 only (FP4_EINVAL
+ * and a NaN counts as larger than every number.  m = 1..16 only (FP4_EINVAL
  * otherwise).  The argmax is the decode kernels' epilogue: each workgroup
  * reduces its logits to one (value, index) per activation row, a second
  * launch reduces those over the workgroups.  A maximum under that total

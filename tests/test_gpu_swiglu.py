@@ -55,7 +55,7 @@ def test_swiglu_matches_oracle(fmt, nh, k, m):
     xbits = synth.activations(synth.TINY, m, k)
     info = fp4.fp4_dispatch_info()
     y = fp4.fp4_w4a16_gate_up_swiglu(x_dev(xbits), pc, ps, nh, float(gg), float(gu), fmt, info=info)
-    assert info.kernel == (0 if m < 3 else 2 if m <= 8 else 1)
+    assert info.kernel == (0 if m < 3 else 2 if m <= 16 else 1)
     ref = oracle.gate_up_swiglu(oracle.bf16_bits_to_f32(xbits), pg, sg, pu, su, k, fmt, gg, gu)
     assert_close(y_host(y), ref, "swiglu fmt=%d nh=%d k=%d m=%d" % (fmt, nh, k, m))
 
