@@ -63,6 +63,8 @@ _SIGNATURES = {
                                   ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_w4a16_moe_prefill": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _i, _vp, _vp, _sz, _vp,
                                    ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_w4a16_moe_prefill_swiglu": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp, _i, _vp, _vp,
+                                          ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_w4a4_act_bytes": (_i, [_i, _i, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "fp4_quantize_act_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "fp4_w4a4_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
@@ -344,6 +346,42 @@ def fp4_w4a16_moe_prefill(x, prep_codes, prep_scales, n, experts, global_scales,
     result as fp4_w4a16_moe_decode (no workspace needed)."""
     return _moe("fp4_w4a16_moe_prefill", x, prep_codes, prep_scales, n, experts, global_scales, fmt,
                 expert_offsets, pair_tokens, y, workspace, stream, info)
+
+
+def fp4_w4a16_moe_prefill_swiglu(x, prep_codes, prep_scales, n_half, experts, global_scales, fmt,
+                                 expert_offsets, pair_tokens, y=None, stream=None, info=None):
+    """Grouped MoE on the tile GEMM with the SwiGLU epilogue: every expert an interleaved gate_up
+    weight (fp4_prepare_gate_up_interleaved), y[p] = silu(x[t] @ gate_e.T) * (x[t] @ up_e.T) for
+    t = pair_tokens[p].  global_scales is float32 [experts, 2] (gate, up; NVFP4) or None (MXFP4).
+    Returns y bf16 [pairs, n_half]."""
+    _need(x, torch.bfloat16, "x")
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    _need(pair_tokens, torch.int32, "pair_tokens")
+    if global_scales is not None:
+        _need(global_scales, torch.float32, "global_scales")
+        if global_scales.numel() != 2 * experts:
+            raise ValueError("global_scales must hold experts x 2 values (gate, up)")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [tokens, k]")
+    tokens, k = x.shape
+    pairs = pair_tokens.numel()
+    cb, sb = fp4_prepared_bytes(n_half, k, fmt)
+    if prep_codes.numel() < experts * 2 * cb or prep_scales.numel() < experts * 2 * sb:
+        raise ValueError("stacked prepared buffers smaller than experts x 2 x fp4_prepared_bytes(n_half, k, fmt)")
+    if expert_offsets.numel() != experts + 1:
+        raise ValueError("expert_offsets must hold experts + 1 values")
+    if y is None:
+        y = torch.empty((pairs, n_half), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y")
+    if y.numel() != pairs * n_half:
+        raise ValueError("y must hold pairs x n_half values")
+    _check("fp4_w4a16_moe_prefill_swiglu", load_library().fp4_w4a16_moe_prefill_swiglu(
+        _ptr(x), tokens, k, _ptr(prep_codes), _ptr(prep_scales), n_half, experts, _ptr(global_scales), fmt,
+        _ptr(expert_offsets), _ptr(pair_tokens), pairs, _ptr(y), _stream(stream),
+        None if info is None else ctypes.byref(info)))
+    return y
 
 
 def _moe(name, x, prep_codes, prep_scales, n, experts, global_scales, fmt, expert_offsets, pair_tokens,

@@ -293,6 +293,61 @@ fp4::MoeArgs moe_args(const fp4::PreparedShape& ps, int fmt, const float* global
 
 }  // namespace
 
+namespace {
+
+// Grouped MoE on the tile GEMM: plain (each expert a weight of n_proj rows,
+// y [pairs][n_proj]) or act (each expert an interleaved gate_up pair of
+// n_proj rows each, y [pairs][n_proj] = silu(gate) * up).
+int run_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_codes_dev,
+                    const uint8_t* prep_scales_dev, int n_proj, bool act, int experts, const float* global_scales_dev,
+                    int fmt, const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
+                    uint16_t* y_dev, hipStream_t stream, fp4_dispatch_info* info_out) {
+  bool no_pairs = false;
+  const int st = check_moe(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n_proj, experts, global_scales_dev, fmt,
+                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, false, nullptr, 0, &no_pairs);
+  if (st) return st;
+  if (no_pairs) {
+    if (info_out) *info_out = fp4_dispatch_info{5, 1, 0, 0, 0};
+    return FP4_OK;
+  }
+  const int projections = act ? 2 : 1;
+  if (static_cast<int64_t>(n_proj) * projections > FP4_MAX_N) return FP4_EINVAL;
+  const fp4::PreparedShape ps = fp4::prepared_shape(n_proj, k, fmt);
+  const int64_t rows_total = ps.n_pad * projections;
+  // Workgroups of the tile launch: every (activation tile slot, weight tile).
+  const int64_t wgs = fp4::moe_gemm_slots(pairs, experts) * (rows_total / fp4::kGemmBN);
+  if (wgs * 256 >= (int64_t{1} << 32)) return FP4_EINVAL;
+
+  fp4::MfmaArgs a{};
+  a.x = x_dev;
+  a.codes = prep_codes_dev;
+  a.scales = prep_scales_dev;
+  a.y = y_dev;
+  a.m = pairs;
+  a.k = k;
+  a.k_pad = ps.k_pad;
+  a.kgroups = ps.kgroups;
+  a.ksegs = ps.ksegs;
+  a.n_proj = n_proj;
+  a.n_proj_pad = ps.n_pad;
+  a.projections = projections;
+  a.rows_total = rows_total;
+  a.ldy = n_proj;
+  a.gscale[0] = a.gscale[1] = 1.0f;
+  a.act = act ? 1 : 0;
+  a.plan = fp4::gemm_plan(fp4::kGemmBM, a.rows_total, k);  // only n_tiles and ksteps are used
+  fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pair_tokens_dev, tokens, pairs,
+                              experts, nullptr);
+  moe.code_stride *= projections;
+  moe.scale_stride *= projections;
+  dim3 grid, block;
+  if (fp4::launch_moe_gemm(a, moe, fmt, stream, &grid, &block) != hipSuccess) return FP4_EHIP;
+  if (info_out) *info_out = fp4_dispatch_info{5, 1, static_cast<int>(grid.x), 0, static_cast<int>(block.x)};
+  return FP4_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fp4_prepared_bytes(int n, int k, int fmt, size_t* code_bytes_out, size_t* scale_bytes_out) {
@@ -477,43 +532,19 @@ int fp4_w4a16_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_
                           const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
                           uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
                           fp4_dispatch_info* info_out) {
-  bool no_pairs = false;
-  const int st = check_moe(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n, experts, global_scales_dev, fmt,
-                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, false, workspace_dev, workspace_bytes,
-                           &no_pairs);
-  if (st) return st;
-  if (no_pairs) {
-    if (info_out) *info_out = fp4_dispatch_info{5, 1, 0, 0, 0};
-    return FP4_OK;
-  }
-  const fp4::PreparedShape ps = fp4::prepared_shape(n, k, fmt);
-  // Workgroups of the tile launch: every (activation tile slot, weight tile).
-  const int64_t wgs = fp4::moe_gemm_slots(pairs, experts) * (ps.n_pad / fp4::kGemmBN);
-  if (wgs * 256 >= (int64_t{1} << 32)) return FP4_EINVAL;
+  (void)workspace_dev;
+  (void)workspace_bytes;
+  return run_moe_prefill(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n, false, experts, global_scales_dev, fmt,
+                         expert_offsets_dev, pair_tokens_dev, pairs, y_dev, stream, info_out);
+}
 
-  fp4::MfmaArgs a{};
-  a.codes = prep_codes_dev;
-  a.scales = prep_scales_dev;
-  a.y = y_dev;
-  a.m = pairs;
-  a.k = k;
-  a.k_pad = ps.k_pad;
-  a.kgroups = ps.kgroups;
-  a.ksegs = ps.ksegs;
-  a.n_proj = n;
-  a.n_proj_pad = ps.n_pad;
-  a.projections = 1;
-  a.rows_total = ps.n_pad;
-  a.ldy = n;
-  a.gscale[0] = a.gscale[1] = 1.0f;
-  a.plan = fp4::gemm_plan(fp4::kGemmBM, a.rows_total, k);  // only n_tiles and ksteps are used
-  a.x = x_dev;
-  const fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pair_tokens_dev, tokens, pairs,
-                                    experts, nullptr);
-  dim3 grid, block;
-  if (fp4::launch_moe_gemm(a, moe, fmt, stream, &grid, &block) != hipSuccess) return FP4_EHIP;
-  if (info_out) *info_out = fp4_dispatch_info{5, 1, static_cast<int>(grid.x), 0, static_cast<int>(block.x)};
-  return FP4_OK;
+int fp4_w4a16_moe_prefill_swiglu(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_codes_dev,
+                                 const uint8_t* prep_scales_dev, int n_half, int experts,
+                                 const float* global_scales_dev, int fmt, const int32_t* expert_offsets_dev,
+                                 const int32_t* pair_tokens_dev, int pairs, uint16_t* y_dev, hipStream_t stream,
+                                 fp4_dispatch_info* info_out) {
+  return run_moe_prefill(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n_half, true, experts, global_scales_dev,
+                         fmt, expert_offsets_dev, pair_tokens_dev, pairs, y_dev, stream, info_out);
 }
 
 int fp4_w4a4_act_bytes(int m, int k, size_t* code_bytes_out, size_t* scale_bytes_out) {

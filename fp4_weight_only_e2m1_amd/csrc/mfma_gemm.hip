@@ -479,6 +479,9 @@ void gemm_kernel(const MfmaArgs a) {
 // slots past the last tile exit.  Offsets are clamped to [0, pairs] and
 // token ids outside [0, tokens_total) read zero rows, so no routing table can
 // make a workgroup touch memory outside x, the weights and y.
+// ACT: each expert's weight is an interleaved gate_up pair and y[p] =
+// silu(gate) * up (the SwiGLU epilogue of the dense tile GEMM), with the
+// expert's two NVFP4 global scales at gscales[2 e], gscales[2 e + 1].
 __device__ __forceinline__ void moe_range(const MoeArgs& moe, int e, int& p0, int& p1) {
   p0 = moe.offsets[e];
   p1 = moe.offsets[e + 1];
@@ -507,7 +510,7 @@ __device__ __forceinline__ void zero_rows_of_bad_tokens(const MfmaArgs& a, int64
   }
 }
 
-template <int FMT>
+template <int FMT, bool ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
   __shared__ Stage<FMT> st[kStages];
@@ -556,7 +559,8 @@ void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
   a.m = p1 - p0;
   a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
   a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
-  a.gscale[0] = a.gscale[1] = moe.gscales ? moe.gscales[e] : 1.0f;
+  a.gscale[0] = moe.gscales ? moe.gscales[ACT ? 2 * e : e] : 1.0f;
+  a.gscale[1] = moe.gscales ? moe.gscales[ACT ? 2 * e + 1 : e] : 1.0f;
   const int64_t m0 = static_cast<int64_t>(tile) * kGemmBM;
   const int64_t n0 = static_cast<int64_t>(n_tile) * kGemmBN;
   const int rows = a.m - static_cast<int>(m0);  // >= 1
@@ -568,17 +572,26 @@ void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
     f32x16_t acc[4][2];
     run_tile<FMT, 4, true>(a, m0, n0, 0, a.plan.ksteps, st, acc);
     zero_rows_of_bad_tokens<4>(a, m0, acc);
-    store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 4>(a, m0, n0, wave, acc, lds);
+    if constexpr (ACT)
+      store_tile_swiglu_staged<kGemmBM, kThreads, 64, 4>(a, m0, n0, wave, acc, lds);
+    else
+      store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 4>(a, m0, n0, wave, acc, lds);
   } else if (rows > 32) {
     f32x16_t acc[2][2];
     run_tile<FMT, 2, true>(a, m0, n0, 0, a.plan.ksteps, st, acc);
     zero_rows_of_bad_tokens<2>(a, m0, acc);
-    store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 2>(a, m0, n0, wave, acc, lds);
+    if constexpr (ACT)
+      store_tile_swiglu_staged<kGemmBM, kThreads, 64, 2>(a, m0, n0, wave, acc, lds);
+    else
+      store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 2>(a, m0, n0, wave, acc, lds);
   } else {
     f32x16_t acc[1][2];
     run_tile<FMT, 1, true>(a, m0, n0, 0, a.plan.ksteps, st, acc);
     zero_rows_of_bad_tokens<1>(a, m0, acc);
-    store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 1>(a, m0, n0, wave, acc, lds);
+    if constexpr (ACT)
+      store_tile_swiglu_staged<kGemmBM, kThreads, 64, 1>(a, m0, n0, wave, acc, lds);
+    else
+      store_tile_bf16_staged<kGemmBM, kThreads, kGemmBM, 1>(a, m0, n0, wave, acc, lds);
   }
 }
 
@@ -712,10 +725,17 @@ hipError_t launch_moe_gemm(const MfmaArgs& a, const MoeArgs& moe, int fmt, hipSt
   const dim3 grid(static_cast<unsigned>(wgs)), block(kThreads);
   if (grid_out) *grid_out = grid;
   if (block_out) *block_out = block;
-  if (fmt == kFmtNvfp4)
-    hipLaunchKernelGGL(moe_gemm_kernel<kFmtNvfp4>, grid, block, 0, stream, a, moe);
-  else
-    hipLaunchKernelGGL(moe_gemm_kernel<kFmtMxfp4>, grid, block, 0, stream, a, moe);
+  if (fmt == kFmtNvfp4) {
+    if (a.act)
+      hipLaunchKernelGGL((moe_gemm_kernel<kFmtNvfp4, true>), grid, block, 0, stream, a, moe);
+    else
+      hipLaunchKernelGGL((moe_gemm_kernel<kFmtNvfp4, false>), grid, block, 0, stream, a, moe);
+  } else {
+    if (a.act)
+      hipLaunchKernelGGL((moe_gemm_kernel<kFmtMxfp4, true>), grid, block, 0, stream, a, moe);
+    else
+      hipLaunchKernelGGL((moe_gemm_kernel<kFmtMxfp4, false>), grid, block, 0, stream, a, moe);
+  }
   return hipGetLastError();
 }
 

@@ -298,6 +298,30 @@ int fp4_w4a16_moe_prefill(const uint16_t* x_dev, int tokens, int k,
                           hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
+ * Grouped MoE prefill with the SwiGLU epilogue: each expert's weight is an
+ * interleaved gate_up pair (fp4_prepare_gate_up_interleaved of n_half rows
+ * per projection; experts stacked at twice fp4_prepared_bytes(n_half, k, fmt)
+ * apart), and for every routed pair p
+ *   y[p][j] = bf16(silu(g) * u),  g = x[pair_tokens[p]] . gate_e[j] * G_gate,
+ *                                 u = x[pair_tokens[p]] . up_e[j] * G_up,
+ * silu(v) = v / (1 + e^-v), as fp4_w4a16_gate_up_swiglu forms it.
+ *   global_scales_dev  float32 [experts][2] (gate, up) for NVFP4; ignored
+ *                      and may be NULL for MXFP4;
+ *   y_dev              bf16 [pairs][n_half].
+ * Other arguments, checks and the containment of routing data are
+ * fp4_w4a16_moe_prefill's; no workspace.  Dispatch info: kernel 5.
+ * Cite: the MLP step after the fused gate_up ("MXFP4 decode-graph + gate_up
+ * FUSION default-ON" (vllm.cpp PR #54), step 2) on the experts of the MoE
+ * model's grouped route (as fp4_w4a16_moe_decode); the activation is the
+ * reading fp4_w4a16_gate_up_swiglu takes.
+ */
+int fp4_w4a16_moe_prefill_swiglu(const uint16_t* x_dev, int tokens, int k,
+                                 const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n_half,
+                                 int experts, const float* global_scales_dev, int fmt,
+                                 const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
+                                 uint16_t* y_dev, hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
  * W4A4 MXFP4 variant: activations quantized to MXFP4 at call time and
  * contracted with an MXFP4 weight on the block-scaled MFMA.  A separate,
  * opt-in numerics contract: the weight-only entry points above never use it.

@@ -252,3 +252,104 @@ def test_moe_prefill_no_pairs_is_a_no_op():
                                   _i32([0, 0, 0]), torch.empty(0, dtype=torch.int32, device=DEV), info=info)
     torch.cuda.synchronize()
     assert y.shape == (0, n) and info.kernel == 5 and info.grid_x == 0
+
+
+# ---- grouped MoE tile route with the SwiGLU epilogue (fp4_w4a16_moe_prefill_swiglu) ----
+
+def _stacked_swiglu(experts, nh, k, fmt, seed):
+    host, codes, scales, gvals = [], [], [], []
+    for e in range(experts):
+        pg, sg, gg = synth.packed_weight(synth.TINY, 300 + seed + 2 * e, nh, k, fmt)
+        pu, su, gu = synth.packed_weight(synth.TINY, 301 + seed + 2 * e, nh, k, fmt)
+        pc, ps = fp4.fp4_prepare_gate_up_interleaved(u8(pg), u8(sg), u8(pu), u8(su), nh, k, fmt)
+        host.append((pg, sg, gg, pu, su, gu))
+        codes.append(pc)
+        scales.append(ps)
+        gvals += [float(gg), float(gu)]
+    gs = torch.tensor(gvals, dtype=torch.float32, device=DEV)
+    return host, torch.cat(codes), torch.cat(scales), gs
+
+
+def _oracle_moe_swiglu(xbits, host, k, fmt, offsets, ptok):
+    x = oracle.bf16_bits_to_f32(xbits)
+    y = np.zeros((len(ptok), host[0][0].shape[0]), dtype=np.float64)
+    for e, (pg, sg, gg, pu, su, gu) in enumerate(host):
+        p0, p1 = int(offsets[e]), int(offsets[e + 1])
+        if p1 > p0:
+            y[p0:p1] = oracle.gate_up_swiglu(x[ptok[p0:p1]], pg, sg, pu, su, k, fmt, gg, gu)
+    return y
+
+
+@pytest.mark.parametrize("fmt,nh,k,tokens,experts,topk", [
+    (NV, 384, 2048, 160, 8, 2),      # ~40 pairs per expert
+    (MX, 300, 1056, 150, 6, 3),      # ragged n_half and k
+    (NV, 256, 512, 700, 4, 1),       # two tiles per expert
+])
+def test_moe_prefill_swiglu_matches_oracle(fmt, nh, k, tokens, experts, topk):
+    host, pc, ps, gs = _stacked_swiglu(experts, nh, k, fmt, 0)
+    offsets, ptok = _routing(tokens, experts, topk, seed=11 * tokens + experts)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    info = fp4.fp4_dispatch_info()
+    y = fp4.fp4_w4a16_moe_prefill_swiglu(x_dev(xbits), pc, ps, nh, experts, gs if fmt == NV else None, fmt,
+                                         _i32(offsets), _i32(ptok), info=info)
+    assert info.kernel == 5 and info.grid_x == _slots(len(ptok), experts, 2 * (-(-nh // 256) * 256))
+    assert y.shape == (len(ptok), nh)
+    assert_close(y_host(y), _oracle_moe_swiglu(xbits, host, k, fmt, offsets, ptok),
+                 "moe swiglu fmt=%d nh=%d k=%d" % (fmt, nh, k))
+
+
+def test_moe_prefill_swiglu_equals_dense_swiglu():
+    # One expert with all 300 tokens in order: its rows are the dense SwiGLU
+    # gate_up call's bit for bit (every row over all of K, same epilogue).
+    fmt, nh, k, experts, tokens = NV, 256, 1024, 3, 300
+    host, pc, ps, gs = _stacked_swiglu(experts, nh, k, fmt, 50)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    xd = x_dev(xbits)
+    pairs = [(0, 4)] + [(1, t) for t in range(tokens)] + [(2, 7), (2, 8)]
+    e_of = np.array([p[0] for p in pairs])
+    offsets = np.searchsorted(e_of, np.arange(experts + 1)).astype(np.int32)
+    ptok = np.array([p[1] for p in pairs], dtype=np.int32)
+    y = y_host_bits(fp4.fp4_w4a16_moe_prefill_swiglu(xd, pc, ps, nh, experts, gs, fmt, _i32(offsets), _i32(ptok)))
+    cb, sb = fp4.fp4_prepared_bytes(nh, k, fmt)
+    dinfo = fp4.fp4_dispatch_info()
+    _, _, gg, _, _, gu = host[1]
+    dense = y_host_bits(fp4.fp4_w4a16_gate_up_swiglu(xd, pc[2 * cb:4 * cb], ps[2 * sb:4 * sb], nh, float(gg),
+                                                     float(gu), fmt, info=dinfo))
+    assert dinfo.kernel == 1 and dinfo.splits == 1
+    assert np.array_equal(y[1:1 + tokens], dense)
+    assert_close(oracle.bf16_bits_to_f32(y).astype(np.float64),
+                 _oracle_moe_swiglu(xbits, host, k, fmt, offsets, ptok), "moe swiglu vs dense")
+
+
+def test_moe_prefill_graph_replay():
+    # Serving loops replay captured calls: a graph of both MoE tile routes,
+    # replayed with new activations written in place between replays, gives
+    # the eager results bit for bit every time.
+    fmt, n, k, experts, tokens = NV, 512, 1024, 6, 96
+    host, pc, ps, gs = _stacked(experts, n, k, fmt, 60)
+    shost, spc, sps, sgs = _stacked_swiglu(experts, 256, k, fmt, 70)
+    offsets, ptok = _routing(tokens, experts, 2, seed=3)
+    off_d, ptok_d = _i32(offsets), _i32(ptok)
+    x = x_dev(synth.activations(synth.TINY, tokens, k))
+    y = torch.empty((len(ptok), n), dtype=torch.bfloat16, device=DEV)
+    ys = torch.empty((len(ptok), 256), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        fp4.fp4_w4a16_moe_prefill(x, pc, ps, n, experts, gs, fmt, off_d, ptok_d, y=y)
+        fp4.fp4_w4a16_moe_prefill_swiglu(x, spc, sps, 256, experts, sgs, fmt, off_d, ptok_d, y=ys)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        xb = synth.activations(synth.TINY + 1 + r, tokens, k)
+        x.copy_(x_dev(xb))
+        step()
+        want, wants = y_host_bits(y).copy(), y_host_bits(ys).copy()
+        y.fill_(7.0)
+        ys.fill_(7.0)
+        g.replay()
+        assert np.array_equal(y_host_bits(y), want), r
+        assert np.array_equal(y_host_bits(ys), wants), r
