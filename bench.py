@@ -25,6 +25,8 @@ Workloads (synthetic weights and activations at the pages' shapes):
   moe_prefill    the same experts and routing recipe at prefill sizes
                  (m = 1024 tokens by default, 8192 pairs) on the grouped
                  MoE tile GEMM; TFLOP/s = 2 * pairs * n * k / s
+  moe_prefill_swiglu  the same, each expert's 1536 rows taken as an
+                 interleaved gate_up pair of 768, y = silu(gate) * up
   down_proj      NVFP4, k=17408, n=5120
   o_proj         NVFP4, k=6144, n=5120
   prefill_nvfp4  NVFP4, k=5120, n=17408 (m=1024 by default)
@@ -79,6 +81,7 @@ WORKLOADS = {
     "lm_head_argmax": (2, 0, 248320, 5120, 1, 8),
     "moe_gate_up": (0, 0, 1536, 2048, 1, 8),
     "moe_prefill": (0, 0, 1536, 2048, 1, 1024),
+    "moe_prefill_swiglu": (0, 0, 1536, 2048, 1, 1024),
     "down_proj": (3, 0, 5120, 17408, 1, 8),
     "o_proj": (3, 0, 5120, 6144, 1, 8),
     "prefill_nvfp4": (4, 0, 17408, 5120, 1, 1024),
@@ -284,19 +287,34 @@ def run_moe(args, torch, np, fp4, synth):
     """The grouped MoE workloads: one fp4_w4a16_moe_decode (moe_gate_up) or
     fp4_w4a16_moe_prefill (moe_prefill) call per step and m tokens."""
     name = args.workload
-    prefill = name == "moe_prefill"
+    swiglu = name == "moe_prefill_swiglu"
+    prefill = name in ("moe_prefill", "moe_prefill_swiglu")
     wid, fmt, n, k, _, m_default = WORKLOADS[name]
+    n_out = n // 2 if swiglu else n
     if args.m is not None:
         ms = [int(v) for v in args.m.split(",")]
     else:
         ms = [m_default] if prefill else [1, 2, 4, 8]
-    entry = fp4.fp4_w4a16_moe_prefill if prefill else fp4.fp4_w4a16_moe_decode
-    kname = ("moe_gemm_kernel<%s>" if prefill else "moe_decode_kernel<%s>") % ("nvfp4" if fmt == 0 else "mxfp4")
+    if swiglu:
+        def entry(x, c, s, n_, experts, gsc, fmt_, offsets, ptok, y=None, workspace=None, info=None):
+            return fp4.fp4_w4a16_moe_prefill_swiglu(x, c, s, n_ // 2, experts, gsc, fmt_, offsets, ptok, y=y,
+                                                    info=info)
+    else:
+        entry = fp4.fp4_w4a16_moe_prefill if prefill else fp4.fp4_w4a16_moe_decode
+    kname = ("moe_gemm_kernel<%s>" if prefill else "moe_decode_kernel<%s>") % (
+        ("nvfp4" if fmt == 0 else "mxfp4") + (",swiglu" if swiglu else ""))
     dev = torch.device("cuda:0")
     host, codes, scales, gvals = [], [], [], []
     for e in range(MOE_DISTINCT):
         p, s, g = synth.packed_weight(wid, 200 + e, n, k, fmt)
-        pc, ps = fp4.fp4_prepare(torch.from_numpy(p).to(dev), torch.from_numpy(s).to(dev), n, k, fmt)
+        if swiglu:
+            # Rows [0, n/2) are the gate projection, [n/2, n) the up projection.
+            h = n // 2
+            pc, ps = fp4.fp4_prepare_gate_up_interleaved(
+                *(torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (p[:h], s[:h], p[h:], s[h:])),
+                h, k, fmt)
+        else:
+            pc, ps = fp4.fp4_prepare(torch.from_numpy(p).to(dev), torch.from_numpy(s).to(dev), n, k, fmt)
         host.append((p, s, g))
         codes.append(pc)
         scales.append(ps)
@@ -304,7 +322,8 @@ def run_moe(args, torch, np, fp4, synth):
     rep_idx = [e % MOE_DISTINCT for e in range(MOE_EXPERTS)]
     pc_all = torch.cat([codes[i] for i in rep_idx])
     ps_all = torch.cat([scales[i] for i in rep_idx])
-    gs = torch.tensor([gvals[i] for i in rep_idx], dtype=torch.float32, device=dev)
+    gs = torch.tensor([gvals[i] for i in rep_idx for _ in range(2 if swiglu else 1)], dtype=torch.float32,
+                      device=dev)
     footprint = pc_all.numel() + ps_all.numel()
     copies = max(2, math.ceil(ROTATE_BYTES / footprint))
     weights = [(pc_all, ps_all)] + [(pc_all.clone(), ps_all.clone()) for _ in range(copies - 1)]
@@ -319,10 +338,10 @@ def run_moe(args, torch, np, fp4, synth):
         d = {"m": m, "x": torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16), "xb": xb,
              "offsets": torch.from_numpy(offsets).to(dev), "ptok": torch.from_numpy(ptok).to(dev),
              "offsets_h": offsets, "ptok_h": ptok, "active": active, "pairs": len(ptok),
-             "y": torch.empty((len(ptok), n), dtype=torch.bfloat16, device=dev),
+             "y": torch.empty((len(ptok), n_out), dtype=torch.bfloat16, device=dev),
              "ws": torch.empty(fp4.fp4_moe_workspace_bytes(len(ptok), k), dtype=torch.uint8, device=dev),
              "info": fp4.fp4_dispatch_info()}
-        d["bytes"] = len(active) * per_expert + 2 * m * k + 2 * len(ptok) * n
+        d["bytes"] = len(active) * per_expert + 2 * m * k + 2 * len(ptok) * n_out
         d["flops"] = 2.0 * len(ptok) * n * k
         per_m.append(d)
 
@@ -351,7 +370,7 @@ def run_moe(args, torch, np, fp4, synth):
                "pairs": d["pairs"], "active_experts": len(d["active"]),
                "grid": [info.grid_x, info.grid_y], "block": info.block, "algorithmic_bytes": d["bytes"],
                "flops": d["flops"]}
-        if prefill and not args.no_crosscheck:
+        if prefill and not swiglu and not args.no_crosscheck:
             # The same routing through the decode route (8 pairs of an expert per pass over its weight).
             t = timed_calls(torch, lambda i, d=d: call(d, i, fp4.fp4_w4a16_moe_decode), max(args.steps // 4, 5),
                             args.launch == "graph")
@@ -393,17 +412,28 @@ def run_moe(args, torch, np, fp4, synth):
             sp = min(16, len(ptok_h))
             offsets_h = np.minimum(offsets_h, sp)
             ptok_h = ptok_h[:sp]
+
+        def oracle_call():
+            if not swiglu:
+                return oracle.moe_decode(xs, experts, k, fmt, offsets_h, ptok_h)
+            h = n // 2
+            for e, (p_, s_, g_) in enumerate(experts):
+                for q in range(int(offsets_h[e]), int(offsets_h[e + 1])):
+                    t_ = int(ptok_h[q])
+                    oracle.gate_up_swiglu(xs[t_:t_ + 1], p_[:h], s_[:h], p_[h:], s_[h:], k, fmt, g_, g_)
+
         t0 = time.perf_counter()
         reps = 0
         while reps == 0 or (time.perf_counter() - t0 < args.cpu_budget and reps < 20):
-            oracle.moe_decode(xs, experts, k, fmt, offsets_h, ptok_h)
+            oracle_call()
             reps += 1
         dt = (time.perf_counter() - t0) / reps
         if prefill:
             out["cpu_baseline"] = {"value": round(2.0 * len(ptok_h) * n * k / dt / 1e12, 6), "unit": "TFLOP/s",
                                    "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-                                   "sample": "oracle.moe_decode of the first %d pairs of the m = %d call, %d "
-                                             "repetitions" % (len(ptok_h), d["m"], reps)}
+                                   "sample": "%s of the first %d pairs of the m = %d call, %d repetitions"
+                                             % ("oracle.gate_up_swiglu per pair" if swiglu else "oracle.moe_decode",
+                                                len(ptok_h), d["m"], reps)}
         else:
             out["cpu_baseline"] = {"value": round(d["bytes"] / dt / 1e9, 4), "unit": "GB/s",
                                    "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
@@ -453,7 +483,7 @@ def main():
         return
 
     name = args.workload
-    if name in ("moe_gate_up", "moe_prefill"):
+    if name in ("moe_gate_up", "moe_prefill", "moe_prefill_swiglu"):
         return run_moe(args, torch, np, fp4, synth)
     wid, fmt, n, k, proj, m_default = WORKLOADS[name]
     if args.m is None:
