@@ -381,13 +381,14 @@ def run_moe(args, torch, np, fp4, synth):
         value, unit = round(total_flops / (total_ms * 1e-3) / 1e12, 3), "TFLOP/s"
         roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(dom["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4), "kernel": dom["kernel"], "m": dom["m"],
-                "avg_launch_us": dom["us_per_launch"], "units_per_launch": dom["flops"], "traffic": None}
+                "avg_launch_us": dom["us_per_launch"], "units_per_launch": dom["flops"],
+                "traffic": read_traffic(name, dom["m"], kernel_source_hash())}
     else:
         value, unit = round(total_bytes / (total_ms * 1e-3) / 1e9, 3), "GB/s"
         roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4), "kernel": dom["kernel"], "m": dom["m"],
                 "avg_launch_us": dom["us_per_launch"], "units_per_launch": dom["algorithmic_bytes"],
-                "traffic": None}
+                "traffic": read_traffic(name, dom["m"], kernel_source_hash())}
     out = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 6),
