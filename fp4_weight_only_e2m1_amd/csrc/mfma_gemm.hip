@@ -469,10 +469,14 @@ void gemm_kernel(const MfmaArgs a) {
 // expert e owning pairs [offsets[e], offsets[e + 1]), pair p reading x row
 // tokens[p].  Counted in expert order, expert e's c_e pairs form
 // ceil(c_e / 128) activation tiles of 128 of its pairs, whose x rows the
-// stage copies fetch straight from x (no gathered copy);
-// workgroup b computes weight-row tile b % n_tiles of the (b / n_tiles)-th
-// such tile, over all of K, with that expert's prepared weight, and stores
-// bf16 y at the same pair rows.  Each tile's sums are the dense GEMM's for
+// stage copies fetch straight from x (no gathered copy).  With T such tiles
+// in all, work item L < T n_tiles is weight-row tile L % n_tiles of the
+// (L / n_tiles)-th tile, computed over all of K with that expert's prepared
+// weight and stored as bf16 y at the same pair rows.  Items are dealt to the
+// workgroups XCD-aware: workgroup b runs on XCD b % 8, and each XCD gets a
+// contiguous run of items, so the weight tiles of one activation tile (which
+// share its x rows) and an expert's activation tiles (which share its weight)
+// meet in one L2; T is counted first, so idle slots leave no XCD short of work.  Each tile's sums are the dense GEMM's for
 // those rows (same K steps, same MFMA order), so a pair's output does not
 // depend on the other pairs.  The grid has moe_gemm_slots(pairs, experts)
 // tile slots, enough for every tile when the offsets are non-decreasing;
@@ -514,18 +518,36 @@ template <int FMT, bool ACT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
   __shared__ Stage<FMT> st[kStages];
-  __shared__ int s_expert, s_p0, s_p1, s_tile;
+  __shared__ int s_expert, s_p0, s_p1, s_tile, s_ntile;
   const int n_tiles = base.plan.n_tiles;
-  const int slot = static_cast<int>(blockIdx.x) / n_tiles;
-  const int n_tile = static_cast<int>(blockIdx.x) - slot * n_tiles;
-  // Wave 0 finds the slot's (expert, tile): 64 experts at a time, each lane
-  // takes one expert's tile count, an inclusive scan over the wave gives the
-  // tiles before each, and the lane whose range holds the slot records it.
+  // Wave 0 counts the tiles of all experts, maps this workgroup to its work
+  // item, then finds the item's (expert, tile): 64 experts at a time, each
+  // lane takes one expert's tile count, an inclusive scan over the wave gives
+  // the tiles before each, and the lane whose range holds the slot records it.
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     if (lane == 0) s_expert = -1;
+    int total = 0;  // wave-uniform
+    for (int b = 0; b < moe.experts; b += 64) {
+      const int e = b + lane;
+      int p0 = 0, p1 = 0;
+      if (e < moe.experts) moe_range(moe, e, p0, p1);
+      int tiles = (p1 - p0 + kGemmBM - 1) / kGemmBM;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) tiles += __shfl_xor(tiles, o);
+      total += tiles;
+    }
+    // Items dealt to XCDs in contiguous runs (XCD x: q or q + 1 items).
+    const int64_t items = static_cast<int64_t>(total) * n_tiles;
+    const int xcd = static_cast<int>(blockIdx.x % 8);
+    const int64_t q = items / 8, r = items % 8;
+    const int64_t j = blockIdx.x / 8;
+    const int64_t item = xcd * q + (xcd < r ? xcd : r) + j;
+    const bool live = j < q + (xcd < r ? 1 : 0);
+    const int slot = live ? static_cast<int>(item / n_tiles) : -1;
+    if (lane == 0) s_ntile = live ? static_cast<int>(item % n_tiles) : 0;
     int before = 0;  // tiles of the experts scanned so far (wave-uniform)
-    for (int b = 0; b < moe.experts && before <= slot; b += 64) {
+    for (int b = 0; b < moe.experts && slot >= 0 && before <= slot; b += 64) {
       const int e = b + lane;
       int p0 = 0, p1 = 0;
       if (e < moe.experts) moe_range(moe, e, p0, p1);
@@ -552,6 +574,7 @@ void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
   const int p0 = __builtin_amdgcn_readfirstlane(s_p0);
   const int p1 = __builtin_amdgcn_readfirstlane(s_p1);
   const int tile = __builtin_amdgcn_readfirstlane(s_tile);
+  const int n_tile = __builtin_amdgcn_readfirstlane(s_ntile);
   MfmaArgs a = base;
   a.row_tokens = moe.tokens + p0;
   a.tokens_total = moe.tokens_total;
