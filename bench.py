@@ -465,7 +465,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the layer's kernels run on a single MI355X and no "
-              "multi-GPU path is built (sharding over n is described in DESIGN.md).", file=sys.stderr)
+              "multi-GPU path is built (the layer would shard over its output rows, each GPU running the same "
+              "kernels on its share of the weight).", file=sys.stderr)
         sys.exit(2)
 
     import torch
