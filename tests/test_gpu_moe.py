@@ -353,3 +353,47 @@ def test_moe_prefill_graph_replay():
         g.replay()
         assert np.array_equal(y_host_bits(y), want), r
         assert np.array_equal(y_host_bits(ys), wants), r
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_moe_prefill_bench_workload_sampled(swiglu):
+    # The moe_prefill / moe_prefill_swiglu benchmark configuration: 128
+    # experts of 1536 rows (or 768 + 768 gate_up pairs) over k = 2048, NVFP4,
+    # 1024 tokens routed top-8 (8192 pairs), 8 distinct expert weights
+    # repeated over the 128.  The oracle checks every pair of 6 experts.
+    experts, topk, tokens, n, k, fmt, distinct = 128, 8, 1024, 1536, 2048, NV, 8
+    host, codes, scales, gv = [], [], [], []
+    for e in range(distinct):
+        p, s, g = synth.packed_weight(synth.TINY, 500 + e, n, k, fmt)
+        if swiglu:
+            h = n // 2
+            pc, ps = fp4.fp4_prepare_gate_up_interleaved(u8(p[:h]), u8(s[:h]), u8(p[h:]), u8(s[h:]), h, k, fmt)
+        else:
+            pc, ps = fp4.fp4_prepare(u8(p), u8(s), n, k, fmt)
+        host.append((p, s, g))
+        codes.append(pc)
+        scales.append(ps)
+        gv.append(float(g))
+    idx = [e % distinct for e in range(experts)]
+    pc_all, ps_all = torch.cat([codes[i] for i in idx]), torch.cat([scales[i] for i in idx])
+    gs = torch.tensor([gv[i] for i in idx for _ in range(2 if swiglu else 1)], dtype=torch.float32, device=DEV)
+    offsets, ptok = _routing(tokens, experts, topk, seed=77)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    if swiglu:
+        y = fp4.fp4_w4a16_moe_prefill_swiglu(x_dev(xbits), pc_all, ps_all, n // 2, experts, gs, fmt, _i32(offsets),
+                                             _i32(ptok))
+    else:
+        y = fp4.fp4_w4a16_moe_prefill(x_dev(xbits), pc_all, ps_all, n, experts, gs, fmt, _i32(offsets), _i32(ptok))
+    got = y_host(y)
+    assert np.isfinite(got).all()
+    x = oracle.bf16_bits_to_f32(xbits)
+    for e in (0, 1, 37, 64, 101, 127):
+        p0, p1 = int(offsets[e]), int(offsets[e + 1])
+        p, s, g = host[e % distinct]
+        xs = x[ptok[p0:p1]]
+        if swiglu:
+            h = n // 2
+            ref = oracle.gate_up_swiglu(xs, p[:h], s[:h], p[h:], s[h:], k, fmt, g, g)
+        else:
+            ref = oracle.linear(xs, p, s, k, fmt, g)
+        assert_close(got[p0:p1], ref, "moe bench workload expert %d swiglu=%s" % (e, swiglu))
