@@ -476,13 +476,14 @@ void gemm_kernel(const MfmaArgs a) {
 // workgroups XCD-aware: workgroup b runs on XCD b % 8, and each XCD gets a
 // contiguous run of items, so the weight tiles of one activation tile (which
 // share its x rows) and an expert's activation tiles (which share its weight)
-// meet in one L2; T is counted first, so idle slots leave no XCD short of work.  Each tile's sums are the dense GEMM's for
-// those rows (same K steps, same MFMA order), so a pair's output does not
-// depend on the other pairs.  The grid has moe_gemm_slots(pairs, experts)
-// tile slots, enough for every tile when the offsets are non-decreasing;
-// slots past the last tile exit.  Offsets are clamped to [0, pairs] and
-// token ids outside [0, tokens_total) read zero rows, so no routing table can
-// make a workgroup touch memory outside x, the weights and y.
+// meet in one L2; T is counted first, so idle slots leave no XCD short of
+// work.  Each tile's sums are the dense GEMM's for those rows (same K steps,
+// same MFMA order), so a pair's output does not depend on the other pairs.
+// The grid has moe_gemm_slots(pairs, experts) tile slots per weight tile,
+// enough for every tile when the offsets are non-decreasing; workgroups past
+// the dealt items exit.  Offsets are clamped to [0, pairs] and a token id
+// outside [0, tokens_total) gives a zero row, so no routing table can make a
+// workgroup touch memory outside x, the weights and y.
 // ACT: each expert's weight is an interleaved gate_up pair and y[p] =
 // silu(gate) * up (the SwiGLU epilogue of the dense tile GEMM), with the
 // expert's two NVFP4 global scales at gscales[2 e], gscales[2 e + 1].
