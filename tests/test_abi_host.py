@@ -299,3 +299,23 @@ def test_moe_prefill_grid_limit(lib):
     # ceil(pairs / 128) + min(experts, pairs) tile slots x ceil(n / 256)
     # weight tiles of 256 threads must stay below 2^32 threads.
     assert _moe(lib, "fp4_w4a16_moe_prefill", pairs=1 << 20, experts=65535, n=1 << 24) == ST["EINVAL"]
+
+
+def _moe_swiglu(lib, tokens=4, k=256, n_half=512, experts=8, fmt=NV, x=FAKE, gs=FAKE, offsets=FAKE, ptok=FAKE,
+                pairs=16, y=FAKE):
+    return lib.fp4_w4a16_moe_prefill_swiglu(x, tokens, k, FAKE, FAKE, n_half, experts, gs, fmt, offsets, ptok, pairs,
+                                            y, None, None)
+
+
+def test_moe_prefill_swiglu_argument_checks(lib):
+    assert _moe_swiglu(lib, fmt=2) == ST["EFMT"]
+    assert _moe_swiglu(lib, experts=0) == ST["EINVAL"]
+    assert _moe_swiglu(lib, n_half=0) == ST["EINVAL"]
+    assert _moe_swiglu(lib, k=48) == ST["EINVAL"]
+    assert _moe_swiglu(lib, gs=None) == ST["EINVAL"]           # NVFP4 needs the [experts][2] global scales
+    assert _moe_swiglu(lib, gs=FAKE + 2) == ST["EALIGN"]
+    assert _moe_swiglu(lib, x=FAKE + 8) == ST["EALIGN"]
+    assert _moe_swiglu(lib, ptok=None) == ST["EINVAL"]
+    # Two projections of n_half rows must fit the row limit.
+    assert _moe_swiglu(lib, n_half=(1 << 23) + 1) == ST["EINVAL"]
+    assert _moe_swiglu(lib, pairs=0, x=None, y=None) == ST["OK"]
