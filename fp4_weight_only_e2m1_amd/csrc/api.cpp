@@ -54,7 +54,7 @@ uint64_t next_token() {
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_EHIP; }
 
-// Rows per workgroup of the decode kernel m selects (m = 1..16).
+// Rows per workgroup of the decode kernel m selects (m = 1..32).
 int decode_tile_rows(int m, int64_t rows_total) {
   return m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_tile_rows(rows_total, m)
                                    : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
@@ -70,7 +70,7 @@ size_t argmax_workspace_for(int m, int n, int k, int fmt, size_t* keys_offset) {
 }
 
 size_t act_workspace_for(int m, int n_half, int k, int fmt) {
-  if (m <= fp4::kDecodeMaxM) return workspace_for(m, n_half, k, fmt, 2);
+  if (m <= fp4::kDecodeActMaxM) return workspace_for(m, n_half, k, fmt, 2);
   const int64_t rows_total = 2 * fp4::round_up(n_half, fp4::kRowAlign);
   return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
 }
@@ -110,7 +110,8 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
   const fp4::PreparedShape ps = fp4::prepared_shape(n_proj, k, fmt);
   const bool mx = fmt == FP4_FMT_MXFP4;
   dim3 grid, block;
-  if (m <= fp4::kDecodeMaxM) {
+  // The decode kernels' SwiGLU epilogue serves up to kDecodeActMaxM rows.
+  if (m <= (act ? fp4::kDecodeActMaxM : fp4::kDecodeMaxM)) {
     fp4::GemvArgs a{};
     a.x = x;
     a.codes = codes;

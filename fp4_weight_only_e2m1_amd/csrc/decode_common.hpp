@@ -132,14 +132,17 @@ __device__ __forceinline__ int il_proj(int64_t row) { return static_cast<int>((r
 __device__ __forceinline__ int64_t il_col(int64_t row) { return (row >> 5) * 16 + (row & 15); }
 __device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
+// [activation row][row within the tile], up to 128-row tiles; a placeholder
+// for the instances above kDecodeActMaxM rows, which never run the epilogue.
 template <int M>
 struct ActTile {
-  float v[M][128];  // [activation row][row within the tile], up to 128-row tiles
+  float v[M <= kDecodeActMaxM ? M : 1][M <= kDecodeActMaxM ? 128 : 1];
 };
 // y for the tile of `tile_rows` rows starting at prepared row row0, after
 // every thread has stored its results; all threads must call it.
 template <int M>
 __device__ __forceinline__ void act_store(ActTile<M>& at, const GemvArgs& a, int64_t row0, int tile_rows, int mrows) {
+  static_assert(M <= kDecodeActMaxM, "SwiGLU epilogue rows");
   __syncthreads();
   const int pairs = tile_rows / 2;
   for (int i = threadIdx.x; i < M * pairs; i += blockDim.x) {
@@ -240,16 +243,20 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
       for (int b = 0; b < kBatch; ++b)
         if (s0 + b < a.splits) s = s0 + b == 0 ? v[b] : s + v[b];
     }
-    if (a.act) {
-      at.v[m][row - tile * a.tile_rows] = s * (il_proj(row) == 0 ? a.gscale[0] : a.gscale[1]);
-      continue;
+    if constexpr (M <= kDecodeActMaxM) {
+      if (a.act) {
+        at.v[m][row - tile * a.tile_rows] = s * (il_proj(row) == 0 ? a.gscale[0] : a.gscale[1]);
+        continue;
+      }
     }
     const uint16_t yb = f32_to_bf16_rne(s * (h == 0 ? a.gscale[0] : a.gscale[1]));
     if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
     if (a.keys) tile_argmax_offer(al, m, argmax_key(yb, col));
   }
   if (a.keys) tile_argmax_end(ta, al, a.keys, tile);
-  if (a.act) act_store(at, a, tile * a.tile_rows, a.tile_rows, M);
+  if constexpr (M <= kDecodeActMaxM) {
+    if (a.act) act_store(at, a, tile * a.tile_rows, a.tile_rows, M);
+  }
 }
 
 }  // namespace fp4

@@ -15,8 +15,8 @@
 // workgroups fit a CU, and more workgroups beat deeper per-workgroup
 // pipelines):
 //   codes   64 rows x 128 bytes  (8 KiB: one full 128-byte line per row)
-//   x       XR rows x 256 bf16   (XR = 8 for m <= 8, else 16: 4 or 8 KiB;
-//                                 rows >= m are never read back)
+//   x       XR rows x 256 bf16   (XR = 8, 16 or 32 for m <= 8, 16, 32: 4, 8
+//                                 or 16 KiB; rows >= m are never read back)
 //   scales  of those codes       (1 KiB)
 // A wave then reads, per 128-code block, one 16-byte code chunk per lane,
 // decodes its 4 words and issues 4 MFMAs against x fragments read from LDS.
@@ -25,7 +25,9 @@
 // g = l / 16 of a 128-code block.  Word c (8 codes) of the lane's chunk is the
 // MFMA's B fragment for k index 8g..8g+7; the A fragment is x[r][same 8 codes]
 // (zero for r >= m).  Both operands use that k assignment, so each MFMA sums
-// exactly the 32 codes of words c of the 4 segments.
+// exactly the 32 codes of words c of the 4 segments.  Calls of more than 16
+// rows run a second MFMA per decoded fragment on activation rows 16 + r, into
+// a second accumulator (the same sums, in the same order, for those rows).
 //
 // K is split over workgroups when one K range per 64-row tile would leave the
 // chip underfilled; the split count depends on (k, rows per projection) only
@@ -55,7 +57,10 @@ static_assert(kStageK == 256, "layout below assumes stages of 256 codes");
 
 // x rows staged per stage for calls of up to M activation rows.
 template <int M>
-constexpr int kXRows = M > 8 ? 16 : 8;
+constexpr int kXRows = M > 16 ? 32 : M > 8 ? 16 : 8;
+// 16-row activation groups of an instance: one MFMA per group per fragment.
+template <int M>
+constexpr int kGroups = M > 16 ? 2 : 1;
 
 // Tile geometry for RB row blocks of 16 per wave (a 64 RB-row tile) and XR
 // staged x rows.
@@ -213,11 +218,13 @@ struct alignas(256) ZeroRow {
 };
 
 // One stage for this wave: 2 blocks of 128 codes x 4 MFMA steps for each of
-// its RB row blocks; each x fragment read from LDS feeds RB MFMAs.  zrow: the
-// zero row the lanes of rows r >= m read instead of x.
+// its RB row blocks and J activation groups; each x fragment read from LDS
+// feeds RB MFMAs, each decoded weight fragment J.  zrow: the zero row the
+// lanes of rows >= m read instead of x.
 template <int M, int FMT, int RB>
 __device__ __forceinline__ void compute_stage(const Stage<RB, FMT, kXRows<M>>& sb, const uint4* zrow, int wave, int r, int g,
-                                              int mrows, f32x4_t (&acc)[RB]) {
+                                              int mrows, f32x4_t (&acc)[RB][kGroups<M>]) {
+  constexpr int J = kGroups<M>;
   constexpr int P = scales_per_seg(FMT);
   const uint8_t* sbytes = reinterpret_cast<const uint8_t*>(sb.s);
 #pragma unroll
@@ -240,18 +247,24 @@ __device__ __forceinline__ void compute_stage(const Stage<RB, FMT, kXRows<M>>& s
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int ch = 16 * q + 4 * g + c;
-      const uint4 xv = r < mrows ? sb.x[x_slot(r, ch)] : zrow[ch];
-      Frag af;
-      af.u[0] = xv.x;
-      af.u[1] = xv.y;
-      af.u[2] = xv.z;
-      af.u[3] = xv.w;
+      Frag af[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int xr = 16 * j + r;
+        const uint4 xv = xr < mrows ? sb.x[x_slot(xr, ch)] : zrow[ch];
+        af[j].u[0] = xv.x;
+        af[j].u[1] = xv.y;
+        af[j].u[2] = xv.z;
+        af[j].u[3] = xv.w;
+      }
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         Frag wf;
         const uint32_t word = c == 0 ? code[b].x : c == 1 ? code[b].y : c == 2 ? code[b].z : code[b].w;
         decode_word<FMT>(word, c < 2 ? s0[b] : s1[b], wf);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, wf.v, acc[b], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j].v, wf.v, acc[b][j], 0, 0, 0);
       }
     }
   }
@@ -279,7 +292,7 @@ template <int M, int FMT, int RB, int NB>
 __device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB>& cp, int s, int s1,
                                               const Stage<RB, FMT, kXRows<M>>& cur, Stage<RB, FMT, kXRows<M>>& prev,
                                               const uint4* zrow, int wave, int r, int g, int mrows,
-                                              f32x4_t (&acc)[RB]) {
+                                              f32x4_t (&acc)[RB][kGroups<M>]) {
   wait_for_stage<RB, FMT, kXRows<M>, NB>(s, s1, wave);
   if (s + NB - 1 < s1) cp.issue(static_cast<int64_t>(s + NB - 1) * kStageK, prev, wave);
   compute_stage<M, FMT, RB>(cur, zrow, wave, r, g, mrows, acc);
@@ -303,9 +316,12 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
   const int s0 = static_cast<int>(static_cast<int64_t>(split) * ksteps / a.splits);
   const int s1 = static_cast<int>(static_cast<int64_t>(split + 1) * ksteps / a.splits);
 
-  f32x4_t acc[RB];
+  constexpr int J = kGroups<M>;
+  f32x4_t acc[RB][J];
 #pragma unroll
-  for (int b = 0; b < RB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (t < 32) zero_row.z[t] = make_uint4(0u, 0u, 0u, 0u);  // visible after the first stage barrier
   const Copier<M, FMT, RB> cp(a, row0, t, wave, mrows);
 #pragma unroll
@@ -320,25 +336,33 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
     }
   }
 
-  // Lane (r, g) holds C[m = 4g + i][row 16 (RB wave + b) + r] in acc[b][i].
+  // Lane (r, g) holds C[m = 16j + 4g + i][row 16 (RB wave + b) + r] in
+  // acc[b][j][i].
   if (a.splits == 1) {
     // Greedy-argmax keys: lane (r, g) only ever holds activation rows
-    // 4g .. 4g + 3, so each row's maximum is taken over the 16 lanes of
-    // group g (lane exchanges within the group), then across the waves.
+    // 16j + 4g .. 16j + 4g + 3, so each row's maximum is taken over the 16
+    // lanes of group g (lane exchanges within the group), then across the
+    // waves.
     __shared__ TileArgmax ta;
-    __shared__ ActTile<M> at;
-    uint64_t best[4] = {0, 0, 0, 0};
-    if (a.act) {
+    uint64_t best[J][4];
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const int rl = 16 * (RB * wave + b) + r;
-        const float gs = il_proj(row0 + rl) == 0 ? a.gscale[0] : a.gscale[1];
+    for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * g + i < mrows) at.v[4 * g + i][rl] = acc[b][i] * gs;
+      for (int i = 0; i < 4; ++i) best[j][i] = 0;
+    if constexpr (M <= kDecodeActMaxM) {
+      __shared__ ActTile<M> at;
+      if (a.act) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const int rl = 16 * (RB * wave + b) + r;
+          const float gs = il_proj(row0 + rl) == 0 ? a.gscale[0] : a.gscale[1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * g + i < mrows) at.v[4 * g + i][rl] = acc[b][0][i] * gs;
+        }
+        act_store(at, a, row0, kRows, mrows);
+        return;
       }
-      act_store(at, a, row0, kRows, mrows);
-      return;
     }
     if (a.keys) {
       if (t < kDecodeMaxM) ta.best[t] = 0ull;
@@ -351,27 +375,32 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
       const int64_t col = out_col(a, row, h);
       if (col >= 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 4 * g + i;
-          if (m < mrows) {
-            const uint16_t yb = f32_to_bf16_rne(acc[b][i] * (h == 0 ? a.gscale[0] : a.gscale[1]));
-            if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
-            const uint64_t key = argmax_key(yb, col);
-            if (key > best[i]) best[i] = key;
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 16 * j + 4 * g + i;
+            if (m < mrows) {
+              const uint16_t yb = f32_to_bf16_rne(acc[b][j][i] * (h == 0 ? a.gscale[0] : a.gscale[1]));
+              if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
+              const uint64_t key = argmax_key(yb, col);
+              if (key > best[j][i]) best[j][i] = key;
+            }
           }
-        }
       }
     }
     if (a.keys) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const uint64_t w = shfl_xor_u64(best[i], o);
-          if (w > best[i]) best[i] = w;
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {
+            const uint64_t w = shfl_xor_u64(best[j][i], o);
+            if (w > best[j][i]) best[j][i] = w;
+          }
+          const int m = 16 * j + 4 * g + i;
+          if (r == 0 && m < M) atomicMax(&ta.best[m], static_cast<unsigned long long>(best[j][i]));
         }
-        if (r == 0 && 4 * g + i < M) atomicMax(&ta.best[4 * g + i], static_cast<unsigned long long>(best[i]));
-      }
       __syncthreads();
       if (t < M) a.keys[static_cast<int64_t>(tile) * M + t] = ta.best[t];
     }
@@ -381,10 +410,13 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
   for (int b = 0; b < RB; ++b) {
     const int64_t row = row0 + 16 * (RB * wave + b) + r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * g + i;
-      if (m < M) store_partial(a.partial + (static_cast<int64_t>(split) * M + m) * a.rows_total + row, acc[b][i]);
-    }
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * j + 4 * g + i;
+        if (m < M)
+          store_partial(a.partial + (static_cast<int64_t>(split) * M + m) * a.rows_total + row, acc[b][j][i]);
+      }
   }
   splitk_finish<M>(a, tile, split);
 }
@@ -498,7 +530,7 @@ hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
     case 7: hipLaunchKernelGGL((decode_mfma_kernel<7, FMT, RB, NB>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, FMT, RB, NB>), grid, block, 0, stream, a); break;
     default:
-      // m = 9..16 (16-row x stages) run on 64-row tiles only.
+      // m = 9..32 (16- and 32-row x stages) run on 64-row tiles only.
       if constexpr (RB == 1) {
         switch (a.m) {
           case 9: hipLaunchKernelGGL((decode_mfma_kernel<9, FMT, RB, NB>), grid, block, 0, stream, a); break;
@@ -509,6 +541,22 @@ hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
           case 14: hipLaunchKernelGGL((decode_mfma_kernel<14, FMT, RB, NB>), grid, block, 0, stream, a); break;
           case 15: hipLaunchKernelGGL((decode_mfma_kernel<15, FMT, RB, NB>), grid, block, 0, stream, a); break;
           case 16: hipLaunchKernelGGL((decode_mfma_kernel<16, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 17: hipLaunchKernelGGL((decode_mfma_kernel<17, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 18: hipLaunchKernelGGL((decode_mfma_kernel<18, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 19: hipLaunchKernelGGL((decode_mfma_kernel<19, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 20: hipLaunchKernelGGL((decode_mfma_kernel<20, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 21: hipLaunchKernelGGL((decode_mfma_kernel<21, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 22: hipLaunchKernelGGL((decode_mfma_kernel<22, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 23: hipLaunchKernelGGL((decode_mfma_kernel<23, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 24: hipLaunchKernelGGL((decode_mfma_kernel<24, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 25: hipLaunchKernelGGL((decode_mfma_kernel<25, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 26: hipLaunchKernelGGL((decode_mfma_kernel<26, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 27: hipLaunchKernelGGL((decode_mfma_kernel<27, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 28: hipLaunchKernelGGL((decode_mfma_kernel<28, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 29: hipLaunchKernelGGL((decode_mfma_kernel<29, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 30: hipLaunchKernelGGL((decode_mfma_kernel<30, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 31: hipLaunchKernelGGL((decode_mfma_kernel<31, FMT, RB, NB>), grid, block, 0, stream, a); break;
+          case 32: hipLaunchKernelGGL((decode_mfma_kernel<32, FMT, RB, NB>), grid, block, 0, stream, a); break;
           default: return hipErrorInvalidValue;
         }
       } else {

@@ -27,9 +27,14 @@ constexpr int kTargetCUs = 256;      // MI355X compute units
 constexpr int kDecodeMfmaMinM = 3;
 // Largest m the decode path serves.  The MFMA decode kernel's 16x16x32 MFMA
 // computes 16 activation rows whatever m is (the rows past m read zeros), so
-// m = 9..16 costs it the same matrix-core work as m = 8 and only a second x
-// copy per stage (its x stages hold 16 rows instead of 8).
-constexpr int kDecodeMaxM = 16;
+// m = 9..16 costs it the same matrix-core work as m = 8 and only more x
+// copies per stage (x stages of 16 rows instead of 8); m = 17..32 runs two
+// MFMAs per decoded weight fragment (two 16-row groups, x stages of 32 rows).
+// The SwiGLU epilogue of the decode kernels serves up to kDecodeActMaxM rows
+// (its float32 tile in LDS would cost the 32-row instances a workgroup per
+// CU); SwiGLU calls with more rows take the tile GEMM.
+constexpr int kDecodeMaxM = 32;
+constexpr int kDecodeActMaxM = 16;
 // k-extent of one stage of the MFMA decode kernel (codes), and its LDS stage
 // buffers (all but one in flight).
 constexpr int kDecodeStageK = 256;

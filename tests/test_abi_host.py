@@ -84,17 +84,21 @@ def _prefill_workspace(m, n, k, projections=1):
 
 
 def test_workspace_bytes_policy():
-    # m > 16 runs the prefill GEMM, whose tail tiles split K.
-    assert fp4.fp4_workspace_bytes(17, 17408, 5120, NV) == _prefill_workspace(17, 17408, 5120) == 68 * 7 * 131072
-    # m = 9..16 still runs the MFMA decode kernel: 272 tiles, no split; the
-    # down_proj shape splits 6 ways as at m = 8, with partials for 16 rows.
+    # m > 32 runs the prefill GEMM, whose tail tiles split K.
+    assert fp4.fp4_workspace_bytes(33, 17408, 5120, NV) == _prefill_workspace(33, 17408, 5120) == 68 * 7 * 131072
+    # m = 9..32 still runs the MFMA decode kernel: 272 tiles, no split; the
+    # down_proj shape splits 6 ways as at m = 8, with partials for m rows.
     assert fp4.fp4_workspace_bytes(16, 17408, 5120, NV) == 0
+    assert fp4.fp4_workspace_bytes(32, 17408, 5120, NV) == 0
     assert fp4.fp4_workspace_bytes(16, 5120, 17408, NV) == 6 * 16 * 5120 * 4 + 5120 // 64 * 6 * 8
+    assert fp4.fp4_workspace_bytes(32, 5120, 17408, NV) == 6 * 32 * 5120 * 4 + 5120 // 64 * 6 * 8
+    # The SwiGLU gate_up leaves the decode kernels above 16 rows.
+    assert fp4.fp4_swiglu_workspace_bytes(17, 1024, 12288, MX) == _prefill_workspace(17, 1024, 12288, 2)
     assert fp4.fp4_workspace_bytes(1024, 17408, 5120, MX) == _prefill_workspace(1024, 17408, 5120) == 32 * 10 * 131072
     assert fp4.fp4_workspace_bytes(4096, 17408, 5120, NV) == _prefill_workspace(4096, 17408, 5120)
     assert fp4.fp4_workspace_bytes(65536, 256, 5120, NV) == 0      # 512 tiles: one full round, no tail
     assert fp4.fp4_workspace_bytes(200, 300, 256, NV) == 0         # 4 K steps: too short to split
-    assert fp4.fp4_workspace_bytes(17, 1024, 12288, MX, 2) == _prefill_workspace(17, 1024, 12288, 2)
+    assert fp4.fp4_workspace_bytes(33, 1024, 12288, MX, 2) == _prefill_workspace(33, 1024, 12288, 2)
     # SwiGLU gate_up: the same plan as the fused gate_up.
     assert fp4.fp4_swiglu_workspace_bytes(1024, 12288, 4096, MX) == fp4.fp4_workspace_bytes(1024, 12288, 4096, MX, 2)
     # The lm_head GEMV splits K=5120 (5 slabs of 1024) in two; splitting never depends on m.
@@ -197,8 +201,8 @@ def _argmax(lib, m=1, k=256, n=512, fmt=NV, x=FAKE, y=None, idx=FAKE, val=None, 
 
 def test_argmax_argument_checks(lib):
     sz = ctypes.c_size_t()
-    assert lib.fp4_argmax_workspace_bytes(17, 512, 256, NV, ctypes.byref(sz)) == ST["EINVAL"]
-    assert _argmax(lib, m=17) == ST["EINVAL"]         # decode rows only (m <= 16)
+    assert lib.fp4_argmax_workspace_bytes(33, 512, 256, NV, ctypes.byref(sz)) == ST["EINVAL"]
+    assert _argmax(lib, m=33) == ST["EINVAL"]         # decode rows only (m <= 32)
     assert _argmax(lib, idx=None) == ST["EINVAL"]
     assert _argmax(lib, x=None) == ST["EINVAL"]
     assert _argmax(lib, fmt=5) == ST["EFMT"]

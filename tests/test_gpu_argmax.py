@@ -38,7 +38,7 @@ def _prep(fmt, n, k, tensor):
 
 
 @pytest.mark.parametrize("fmt,n,k", SHAPES)
-@pytest.mark.parametrize("m", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 16, 32])
 def test_one_hot_argmax_exact(fmt, n, k, m):
     packed, scales, g, pc, ps = _prep(fmt, n, k, 80)
     ks = np.linspace(0, k - 1, m).astype(np.int64)

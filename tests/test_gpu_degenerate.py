@@ -1,5 +1,5 @@
 """Degenerate scale bytes and global scales through every compute kernel
-(VALU GEMV m = 1, MFMA decode m = 4 and 12, tile GEMM m = 40) against the
+(VALU GEMV m = 1, MFMA decode m = 4, 12 and 24, tile GEMM m = 40) against the
 oracle: zero, smallest, largest, negative and NaN block scales, blocks of
 the largest code, and G = 0.  The oracle defines these as the formats do (a
 NaN scale makes its block's weights NaN, and that output column NaN); the
@@ -54,7 +54,7 @@ def _compare(y, y_ref, what, extreme=(7,)):
 
 
 @pytest.mark.parametrize("fmt,g_mode", [(NV, "workload"), (NV, "zero"), (MX, "workload")])  # MXFP4 has no G
-@pytest.mark.parametrize("m", [1, 4, 12, 40])
+@pytest.mark.parametrize("m", [1, 4, 12, 24, 40])
 def test_degenerate_scales(fmt, m, g_mode):
     n, k = 300, 1056
     packed, scales, g = _degenerate_weight(fmt, n, k)
@@ -64,7 +64,7 @@ def test_degenerate_scales(fmt, m, g_mode):
     xbits = synth.activations(synth.TINY, m, k)
     info = fp4.fp4_dispatch_info()
     y = y_host(fp4.fp4_w4a16_linear(x_dev(xbits), pc, ps, n, float(g), fmt, info=info))
-    assert info.kernel == (0 if m < 3 else 2 if m <= 16 else 1)
+    assert info.kernel == (0 if m < 3 else 2 if m <= 32 else 1)
     y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
     nan_rows = {NV: (9, 13), MX: (5,)}[fmt]
     assert all(np.isnan(y_ref[:, r]).all() for r in nan_rows)

@@ -19,8 +19,8 @@ NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
 # name, workload, tensor, fmt, n, k, activation rows
 CASES = [
     ("tiny_nvfp4", synth.TINY, 0, NV, 512, 256, [1]),
-    ("lm_head", synth.LM_HEAD, 0, NV, 248320, 5120, [1, 8, 16]),
-    ("down_proj", synth.DECODE_27B, 0, NV, 5120, 17408, [1, 2, 4, 8, 16]),
+    ("lm_head", synth.LM_HEAD, 0, NV, 248320, 5120, [1, 8, 16, 32]),
+    ("down_proj", synth.DECODE_27B, 0, NV, 5120, 17408, [1, 2, 4, 8, 16, 32]),
     ("o_proj", synth.DECODE_27B, 1, NV, 5120, 6144, [1, 2, 4, 8]),
     ("prefill_nvfp4", synth.PREFILL, 0, NV, 17408, 5120, [256, 1024, 4096]),
     ("prefill_mxfp4", synth.PREFILL, 1, MX, 17408, 5120, [256, 1024, 4096]),
@@ -40,7 +40,7 @@ def test_full_size_sampled(name, workload, tensor, fmt, n, k, ms):
         assert_close(y[:, rows], y_ref, "%s m=%d" % (name, m))
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
 def test_gate_up_full_size(m):
     nh, k, fmt = 12288, 4096, MX
     pg, sg, gg = weight(synth.GATE_UP, 0, nh, k, fmt)

@@ -100,7 +100,7 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("fmt,n,k", SHAPES)
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 13, 16])  # 9..16: 16-row x stages
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 13, 16, 17, 24, 32])  # 9..16, 17..32: 16- and 32-row x stages
 def test_gemv_matches_oracle(fmt, n, k, m):
     packed, scales, g = _quantized(fmt, n, k)
     xbits = synth.activations(synth.TINY, m, k)
@@ -112,7 +112,7 @@ def test_gemv_matches_oracle(fmt, n, k, m):
 
 
 @pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 640, 2048), (NV, 300, 1056), (MX, 256, 5120)])
-@pytest.mark.parametrize("m", [17, 24, 32, 33, 64, 65, 128, 200])  # 32 and 64 bound the 1- and 2-block tiles
+@pytest.mark.parametrize("m", [33, 48, 64, 65, 128, 200])  # 64 bounds the 2-block tiles (1-block: SwiGLU, MoE)
 def test_mfma_matches_oracle(fmt, n, k, m):
     packed, scales, g = _quantized(fmt, n, k)
     xbits = synth.activations(synth.TINY, m, k)
@@ -155,7 +155,7 @@ def test_one_hot_selects_weight_column(fmt, n, k, m):
 
 
 @pytest.mark.parametrize("fmt,nh,k", [(MX, 640, 2048), (NV, 300, 1056), (MX, 1024, 4096), (NV, 256, 17408)])
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 12, 24])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 12, 20, 40])
 def test_gate_up_fused_equals_split(fmt, nh, k, m):
     pg, sg, gg = synth.packed_weight(synth.TINY, 60, nh, k, fmt)
     pu, su, gu = synth.packed_weight(synth.TINY, 61, nh, k, fmt)
@@ -175,13 +175,14 @@ def test_gemv_batch_invariance(fmt, n, k):
     # a call with more rows, bit for bit (the summation order never depends on m).
     packed, scales, g = _quantized(fmt, n, k)
     pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
-    # m = 9..16 stage 16 x rows instead of 8: same MFMA sums.
-    x16 = synth.activations(synth.TINY, 16, k)
-    y16 = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x16), pc, ps, n, float(g), fmt))
-    ylo = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x16[:DECODE_MFMA_MIN_M - 1]), pc, ps, n, float(g), fmt))
-    for m in range(1, 17):
-        ym = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x16[:m]), pc, ps, n, float(g), fmt))
-        ref = y16 if m >= DECODE_MFMA_MIN_M else ylo
+    # m = 9..16 stage 16 x rows instead of 8, m = 17..32 32 rows with a
+    # second MFMA per fragment: the same MFMA sums for every row.
+    x32 = synth.activations(synth.TINY, 32, k)
+    y32 = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x32), pc, ps, n, float(g), fmt))
+    ylo = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x32[:DECODE_MFMA_MIN_M - 1]), pc, ps, n, float(g), fmt))
+    for m in range(1, 33):
+        ym = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x32[:m]), pc, ps, n, float(g), fmt))
+        ref = y32 if m >= DECODE_MFMA_MIN_M else ylo
         assert np.array_equal(ym, ref[:m]), m
 
 

@@ -48,7 +48,7 @@ def test_interleaved_layout_bytes():
 
 
 @pytest.mark.parametrize("fmt,nh,k", [(MX, 640, 2048), (NV, 300, 1056), (NV, 256, 17408), (MX, 1024, 4096)])
-@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 16, 100, 300])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 16, 24, 100, 300])
 def test_swiglu_matches_oracle(fmt, nh, k, m):
     pg, sg, gg, pu, su, gu = _weights(fmt, nh, k, 1)
     pc, ps = fp4.fp4_prepare_gate_up_interleaved(u8(pg), u8(sg), u8(pu), u8(su), nh, k, fmt)
