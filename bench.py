@@ -637,7 +637,7 @@ def main():
             ts = timed_calls(torch, split_call, args.steps, args.launch == "graph")
             rows[j]["us_split_launches"] = round(ts * 1e3 / args.steps, 3)
 
-    # Rates follow the kernel that ran: the decode kernels (m <= 16) stream
+    # Rates follow the kernel that ran: the decode kernels (m <= 32) stream
     # the weights (GB/s against HBM), the tile GEMMs contract (TFLOP/s).
     prefill = any(d["info"].kernel in (1, 4) for d in per_m)
     if prefill:
