@@ -21,6 +21,7 @@ NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
 @pytest.mark.parametrize("fmt,n,k,m,split", [
     (NV, 512, 17408, 1, True),    # VALU GEMV, K split 5 ways
     (NV, 300, 5120, 8, True),     # MFMA decode, K split
+    (MX, 300, 5120, 24, True),    # MFMA decode, two 16-row activation groups, K split
     (MX, 8192, 1024, 4, False),   # MFMA decode, unsplit (128 row tiles)
     (NV, 512, 5120, 100, True),   # prefill GEMM, tail tiles split along K
 ])
