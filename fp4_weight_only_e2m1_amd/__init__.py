@@ -236,7 +236,7 @@ def fp4_argmax_workspace_bytes(m, n, k, fmt):
 
 def fp4_w4a16_linear_argmax(x, prep_codes, prep_scales, n, global_scale, fmt, logits=False, y=None,
                             idx=None, val=None, workspace=None, stream=None, info=None):
-    """Greedy token per activation row of the decode logits x @ w.T (m <= 16).
+    """Greedy token per activation row of the decode logits x @ w.T (m <= 32).
 
     Returns (idx int32 [m], val bf16 [m], y) where val holds the winning logits
     and y is the bf16 [m, n] logits when ``logits`` is true (or ``y`` is given),

@@ -1,7 +1,9 @@
 // C ABI of the W4A16 FP4 linear library: argument checks, dispatch on m, and
 // workspace sizing.  Every check runs on the host before any launch, so an
 // invalid call enqueues nothing; no HIP runtime call happens before the
-// arguments are known to be good.  The library keeps no global state.
+// arguments are known to be good.  The library allocates no device memory and
+// keeps no caches; its only state is the process-wide atomic call counter of
+// next_token(), whose values tag the split-K arrival flags in a workspace.
 //
 // Rejecting what it cannot run, instead of falling through to some other
 // path, follows the pages' lessons: an unknown scale layout is rejected rather

@@ -210,17 +210,18 @@ __device__ __forceinline__ void splitk_finish(const GemvArgs& a, int64_t tile, i
   }
   __syncthreads();
   if (!s_last) return;
-  for (int s = threadIdx.x; s < a.splits; s += kDecodeThreads)
+  for (int s = threadIdx.x; s < a.splits; s += blockDim.x)
     __hip_atomic_store(flags + s, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __shared__ TileArgmax ta;
   __shared__ ActTile<M> at;
   ArgmaxLocal<M> al;
   if (a.keys) tile_argmax_begin(ta, al);
-  // One buffer descriptor per split: partial[split] is [m][row], at most
-  // 8 x 2^24 floats, so 32-bit offsets suffice within it.
+  // One buffer descriptor per split: partial[split] is [M][rows_total] with
+  // M <= kDecodeMaxM = 32 and rows_total < 2^24 (FP4_MAX_N), i.e. under 2^29
+  // floats = 2^31 bytes, so 32-bit byte offsets suffice within it.
   const int64_t split_floats = static_cast<int64_t>(M) * a.rows_total;
   constexpr int kBatch = 8;
-  for (int i = threadIdx.x; i < M * a.tile_rows; i += kDecodeThreads) {
+  for (int i = threadIdx.x; i < M * a.tile_rows; i += blockDim.x) {
     const int m = i / a.tile_rows;
     const int64_t row = tile * a.tile_rows + (i - m * a.tile_rows);
     int h = 0;

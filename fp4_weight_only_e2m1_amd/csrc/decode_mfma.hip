@@ -1,4 +1,4 @@
-// Decode-shaped W4A16 FP4 GEMM on the matrix cores (m = 3..8 activation rows).
+// Decode-shaped W4A16 FP4 GEMM on the matrix cores (m = 3..32 activation rows).
 //
 // At m rows a VALU GEMV spends m/2 v_dot2 per weight on top of the decode, so
 // from m = 3 on it is bound by VALU issue before HBM.  Here the VALU only

@@ -1,4 +1,5 @@
-// Prefill-shaped W4A16 FP4 GEMM (m > 8 activation rows) on gfx950 bf16 MFMA.
+// Prefill-shaped W4A16 FP4 GEMM (m > 32 activation rows; SwiGLU gate_up and the
+// grouped MoE tile route also below that) on gfx950 bf16 MFMA.
 //
 // At large m the layer is a dense contraction (2*m*n*k flops over n*k/2 code
 // bytes), so it runs on the matrix cores.  The pages run prefill through a

@@ -66,8 +66,14 @@ __global__ __launch_bounds__(256) void prepare_scales_kernel(const uint8_t* __re
   for (int q = 0; q < P; ++q) o[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 
-// One thread per 8 consecutive weights (one 32-bit code word).
-//   NVFP4: fl32(fl32(E2M1 * S) * G); MXFP4: E2M1 * 2^(b-127).
+// One thread per 8 consecutive weights (one 32-bit code word), decoded with
+// the instruction sequences of the compute kernels:
+//   NVFP4: E2M1 -> f32 (v_cvt_scalef32_pk_f32_fp4, unit scale), times the
+//          E4M3 scale (v_cvt_f32_fp8), then times G: fl32(fl32(E2M1 * S) * G);
+//   MXFP4: E2M1 * 2^(b-127) -> bf16 in one v_cvt_scalef32_pk_bf16_fp4 with
+//          the E8M0 byte as the scale operand, widened exactly to f32.
+// (The compute kernels round the NVFP4 product to bf16, which is exact: it
+// has at most 6 significant bits; they apply G after the sum over k.)
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, int n, int k,
@@ -85,10 +91,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   f32x2_t p[4];
   if constexpr (FMT == kFmtMxfp4) {
     const float sop = e8m0_as_scale_operand(sb);
-    p[0] = cvt_fp4x2_f32<0>(word, sop);
-    p[1] = cvt_fp4x2_f32<1>(word, sop);
-    p[2] = cvt_fp4x2_f32<2>(word, sop);
-    p[3] = cvt_fp4x2_f32<3>(word, sop);
+    const uint32_t b[4] = {bf16x2_bits(cvt_fp4x2_bf16<0>(word, sop)), bf16x2_bits(cvt_fp4x2_bf16<1>(word, sop)),
+                           bf16x2_bits(cvt_fp4x2_bf16<2>(word, sop)), bf16x2_bits(cvt_fp4x2_bf16<3>(word, sop))};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j].x = __uint_as_float(b[j] << 16);
+      p[j].y = __uint_as_float(b[j] & 0xFFFF0000u);
+    }
   } else {
     const float s = e4m3_to_f32<0>(sb);
     p[0] = cvt_fp4x2_f32<0>(word, 1.0f);

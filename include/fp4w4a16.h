@@ -20,8 +20,11 @@
  *
  * Conventions for every entry point:
  *   - Pointers named *_dev are device pointers owned by the caller; the library
- *     never allocates, frees or caches device memory and keeps no global state,
- *     so calls are reentrant.  Out-parameters named *_out are host pointers.
+ *     never allocates, frees or caches device memory.  Its only state is a
+ *     process-wide atomic call counter (host memory) whose values tag the
+ *     split-K arrival flags a call writes into its workspace, so calls are
+ *     reentrant and may come from several host threads.  Out-parameters named
+ *     *_out are host pointers.
  *   - Device pointers must be 16-byte aligned.
  *   - Work is enqueued on `stream` and is asynchronous; argument checks happen
  *     on the host before anything is enqueued, and an invalid call enqueues
@@ -66,7 +69,8 @@ enum fp4_status {
 /* Which kernel a call ran (filled when the caller passes a non-null pointer). */
 typedef struct fp4_dispatch_info {
   int kernel;  /* 0 = VALU decode GEMV (m = 1, 2), 2 = MFMA decode GEMV
-                  (m = 3..16), 1 = MFMA tile GEMM (m > 16), 3 = grouped MoE decode,
+                  (m = 3..32; SwiGLU gate_up: m = 3..16), 1 = MFMA tile GEMM
+                  (m > 32; SwiGLU gate_up: m > 16), 3 = grouped MoE decode,
                   4 = W4A4 MXFP4 tile GEMM (any m),
                   5 = grouped MoE tile GEMM (prefill) */
   int splits;  /* K splits: decode kernels split every tile, the tile GEMMs only
@@ -90,7 +94,8 @@ typedef struct fp4_dispatch_info {
  *          (2 per row for NVFP4, 1 for MXFP4) are contiguous; zero padded.
  * A prepared gate_up weight is a prepared gate weight followed by a prepared
  * up weight, in both buffers (twice these sizes).
- * Pure host function; never touches the GPU.
+ * Host utility (no passage defines it): sizes the prepared buffers; pure host
+ * function, never touches the GPU.
  */
 int fp4_prepared_bytes(int n, int k, int fmt, size_t* code_bytes_out, size_t* scale_bytes_out);
 
@@ -121,12 +126,14 @@ int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scale
 /*
  * Workspace a compute call needs, in bytes (0 when none), for split-K fp32
  * partials and arrival flags: the m = 1, 2 decode GEMV with k > 4096, the
- * m = 3..16 MFMA decode on layers of fewer than 8192 rows per projection, and
- * the m > 16 tile GEMM when its 128 x 256 output tiles do not fill whole
+ * m = 3..32 MFMA decode on layers of fewer than 8192 rows per projection, and
+ * the m > 32 tile GEMM when its 128 x 256 output tiles do not fill whole
  * rounds of the 512 workgroups resident on the chip (the tail tiles are then
  * split along K; at most 64 MiB).  It never needs zeroing.  `projections` is 1 for
  * fp4_w4a16_linear (n = output features) and 2 for fp4_w4a16_gate_up
- * (n = n_half).  Pure host function.
+ * (n = n_half).
+ * Host utility (no passage defines it): sizes the workspace argument of the
+ * compute calls; pure host function, never touches the GPU.
  */
 int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* bytes_out);
 
@@ -141,10 +148,10 @@ int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* b
  *   info_out  optional, may be NULL.
  * Accumulation is float32.  The order of every sum depends only on (k, fmt, n)
  * and on which kernel m selects (fp4_dispatch_info.kernel) -- for the tile
- * GEMM (m > 16) also on m, which decides the tiles summed in K splits -- so
- * results are deterministic run to run, and for m <= 16 a row's result does
+ * GEMM (m > 32) also on m, which decides the tiles summed in K splits -- so
+ * results are deterministic run to run, and for m <= 32 a row's result does
  * not depend on the other rows of the call as long as m selects the same
- * kernel.
+ * kernel (m = 1, 2: the VALU GEMV; m = 3..32: the MFMA decode).
  * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list (the W4A16
  * entry points take bf16 x and the packed weight to bf16 y); "keep the ModelOpt
  * NVFP4 lm_head packed" (vllm.cpp PR #263), section "Why this row matters"
@@ -182,9 +189,11 @@ int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k,
  * output are computed by one workgroup.  m <= 16: the decode kernels form y in
  * their epilogue; m > 16: the tile GEMM forms y in the epilogue of every whole
  * tile, and its reduce launch forms y for the tail tiles split along K.
- * Workspace: fp4_swiglu_workspace_bytes (the split-K partials and flags of
- * the same plan as fp4_w4a16_gate_up).  silu uses the hardware exp and
- * reciprocal (about 1 ulp each).
+ * Workspace: fp4_swiglu_workspace_bytes.  At m <= 16 it equals
+ * fp4_workspace_bytes(m, n_half, k, fmt, 2) (the decode kernels' split-K
+ * partials and flags); at m = 17..32 the SwiGLU call runs the tile GEMM while
+ * fp4_w4a16_gate_up runs the decode kernel, so the two sizes differ there.
+ * silu uses the hardware exp and reciprocal (about 1 ulp each).
  * Reading taken: the pages name the MLP block after the fused gate_up but not
  * its activation; silu(gate) * up is the gated MLP of the model family they
  * run ("MXFP4 decode-graph + gate_up FUSION default-ON", vllm.cpp PR #54,
@@ -205,8 +214,8 @@ int fp4_w4a16_gate_up_swiglu(const uint16_t* x_dev, int m, int k,
  * Greedy token of a decode call: idx_out_dev[i] (int32) = the index j of the
  * largest logit y[i][j] -- the bf16 value fp4_w4a16_linear gives for the same
  * arguments -- and the lowest such j when several are equal; -0 equals +0
- * and a NaN counts as larger than every number.  m = 1..16 only (FP4_EINVAL
- * otherwise).  The argmax is the decode kernels' epilogue: each workgroup
+ * and a NaN counts as larger than every number.  m = 1..32 only (the decode
+ * kernels; FP4_EINVAL otherwise).  The argmax is the decode kernels' epilogue: each workgroup
  * reduces its logits to one (value, index) per activation row, a second
  * launch reduces those over the workgroups.  A maximum under that total
  * order does not depend on the reduction order, so the result is
@@ -391,15 +400,21 @@ int fp4_w4a4_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_co
 
 /*
  * Dequantize a prepared weight to float32 out_dev [n][k]:
- * out = fl32(fl32(E2M1 * S) * G), G = 1 for MXFP4.  Uses the same decoders as
- * the compute kernels; exists so tests can compare the decode bit for bit.
+ * out = fl32(fl32(E2M1 * S) * G), G = 1 for MXFP4.  It decodes with the
+ * instruction sequences of the compute kernels' weight decode (NVFP4: E2M1 to
+ * f32 at unit scale, times the E4M3 scale; MXFP4: E2M1 times 2^(b-127) to
+ * bf16 in one conversion with the E8M0 byte as its scale operand), then
+ * multiplies by G, which the compute kernels apply after the sum over k
+ * instead.  The compute kernels' own decode is pinned separately: a one-hot
+ * x makes each output a single decoded weight.
  * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list (the CPU
  * dequant reference the device GEMM is checked against).
  */
 int fp4_dequantize(const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int k,
                    float global_scale, int fmt, float* out_dev, hipStream_t stream);
 
-/* A static, human-readable name for a status code. */
+/* A static, human-readable name for a status code.  Host utility (no passage
+ * defines it); never touches the GPU. */
 const char* fp4_status_string(int status);
 
 #ifdef __cplusplus

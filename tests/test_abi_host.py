@@ -99,8 +99,14 @@ def test_workspace_bytes_policy():
     assert fp4.fp4_workspace_bytes(65536, 256, 5120, NV) == 0      # 512 tiles: one full round, no tail
     assert fp4.fp4_workspace_bytes(200, 300, 256, NV) == 0         # 4 K steps: too short to split
     assert fp4.fp4_workspace_bytes(33, 1024, 12288, MX, 2) == _prefill_workspace(33, 1024, 12288, 2)
-    # SwiGLU gate_up: the same plan as the fused gate_up.
+    # SwiGLU gate_up: the same plan as the fused gate_up, except at 17..32
+    # rows, where the SwiGLU call takes the tile GEMM and gate_up the decode kernel.
     assert fp4.fp4_swiglu_workspace_bytes(1024, 12288, 4096, MX) == fp4.fp4_workspace_bytes(1024, 12288, 4096, MX, 2)
+    for m in (1, 2, 8, 16):
+        assert fp4.fp4_swiglu_workspace_bytes(m, 1024, 12288, MX) == fp4.fp4_workspace_bytes(m, 1024, 12288, MX, 2)
+    for m in (17, 24, 32):
+        assert fp4.fp4_swiglu_workspace_bytes(m, 1024, 12288, MX) == _prefill_workspace(m, 1024, 12288, 2)
+        assert fp4.fp4_swiglu_workspace_bytes(m, 1024, 12288, MX) != fp4.fp4_workspace_bytes(m, 1024, 12288, MX, 2)
     # The lm_head GEMV splits K=5120 (5 slabs of 1024) in two; splitting never depends on m.
     # splits * m * rows fp32 partials, then one 8-byte flag per (64-row tile, split).
     ws1 = fp4.fp4_workspace_bytes(1, 248320, 5120, NV)
@@ -201,8 +207,14 @@ def _argmax(lib, m=1, k=256, n=512, fmt=NV, x=FAKE, y=None, idx=FAKE, val=None, 
 
 def test_argmax_argument_checks(lib):
     sz = ctypes.c_size_t()
+    # The documented limit: m = 1..32 (the decode kernels), FP4_EINVAL above.
+    assert lib.fp4_argmax_workspace_bytes(32, 512, 256, NV, ctypes.byref(sz)) == ST["OK"]
+    assert sz.value == 8 * 32 * 8      # 8 tiles of 64 rows, one key per (tile, row), no split
     assert lib.fp4_argmax_workspace_bytes(33, 512, 256, NV, ctypes.byref(sz)) == ST["EINVAL"]
     assert _argmax(lib, m=33) == ST["EINVAL"]         # decode rows only (m <= 32)
+    # m = 32 passes every check (the failure left is the missing workspace).
+    assert _argmax(lib, m=32, ws=None) == ST["EINVAL"]
+    assert _argmax(lib, m=32, ws_bytes=8 * 32 * 8 - 1) == ST["EWORKSPACE"]
     assert _argmax(lib, idx=None) == ST["EINVAL"]
     assert _argmax(lib, x=None) == ST["EINVAL"]
     assert _argmax(lib, fmt=5) == ST["EFMT"]
