@@ -7,6 +7,14 @@ Prints ONE JSON line (rank 0, one GPU):
 A step is one call of the layer at each activation-row count m in the list
 (default m = 1, 2, 4, 8 for the decode workloads, 1024 for prefill), on
 synthetic activations, with the prepared weights already resident in HBM.
+
+The default run (--workload suite) times every config of the metric in turn:
+the MXFP4 fused gate_up (the headline: value, ms_per_step, roofline and
+cpu_baseline are its own) at m = 1, 2, 4, 8, then the NVFP4 lm_head, down_proj
+and o_proj at m = 1, 2, 4, 8 and the NVFP4 and MXFP4 prefill GEMM at m = 1024.
+Every config's rate, fraction of its roofline peak and time per call per m
+also go out as flat scalar keys, e.g. "lm_head_m8_gbs", "lm_head_m8_frac",
+"lm_head_m8_us", "prefill_nvfp4_m1024_tflops".
 Each m is timed with its own HIP events; by default the timed calls are
 replayed from a captured HIP graph so the per-call launch gaps of the host
 runtime do not count against the kernels.
@@ -14,7 +22,8 @@ The weights are rotated over enough device copies (>= 1 GiB in total) that
 the 256 MB Infinity Cache cannot hold them, so the bytes come from HBM.
 
 Workloads (synthetic weights and activations at the pages' shapes):
-  gate_up        MXFP4 fused gate_up, k=4096, n=2x12288          (default)
+  suite          the default: the configs listed above, one after another
+  gate_up        MXFP4 fused gate_up, k=4096, n=2x12288          (headline)
   gate_up_swiglu the same weight interleaved, y = silu(gate) * up [m, 12288]
   lm_head        NVFP4 packed lm_head, k=5120, n=248320
   lm_head_argmax the same head with the fused greedy argmax (token ids out,
@@ -443,55 +452,11 @@ def run_moe(args, torch, np, fp4, synth):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gate_up", choices=sorted(WORKLOADS))
-    ap.add_argument("--m", default=None,
-                    help="activation rows, comma separated (default: 1,2,4,8 for decode, 1024 for prefill)")
-    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
-                    help="replay the timed calls from a captured HIP graph, or launch them one by one")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-crosscheck", action="store_true",
-                    help="skip the differencing and split-launch cross-checks (e.g. under a counter "
-                         "profiler, where their launches would mix with the timed ones)")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run 10 plain device-to-device copies of MIB MiB (reference for the HBM "
-                         "byte counters) and exit")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the layer's kernels run on a single MI355X and no "
-              "multi-GPU path is built (the layer would shard over its output rows, each GPU running the same "
-              "kernels on its share of the weight).", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import numpy as np
-    import fp4_weight_only_e2m1_amd as fp4
-    import synth
-
-    if args.calibrate_copy:
-        nbytes = args.calibrate_copy << 20
-        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(10):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 10}), flush=True)
-        return
-
-    name = args.workload
-    if name in ("moe_gate_up", "moe_prefill", "moe_prefill_swiglu"):
-        return run_moe(args, torch, np, fp4, synth)
+def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
+    """Time one dense workload (every m of `ms`, one call each per step) and
+    return its result: per-m rows, totals, the rate, the roofline of the
+    dominant kernel and, when asked, the oracle's CPU baseline."""
     wid, fmt, n, k, proj, m_default = WORKLOADS[name]
-    if args.m is None:
-        ms = [1, 2, 4, 8] if m_default <= 8 else [m_default]
-    else:
-        ms = [int(v) for v in args.m.split(",")]
     dev = torch.device("cuda:0")
     pc, ps, gs, x0, xb0, host = make_inputs(name, ms[0], torch, fp4, synth)
 
@@ -606,7 +571,7 @@ def main():
     # * fused gate_up only: the same step with the gate and up halves launched
     #   separately (two calls per step, the halves of the same prepared weight).
     n1 = max(1, args.steps // 4)
-    for j, d in enumerate(per_m if not args.no_crosscheck else []):
+    for j, d in enumerate(per_m if crosscheck else []):
         t1 = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), n1, args.launch == "graph")
         if args.steps > n1:
             rows[j]["us_per_launch_differenced"] = round((d["t_ms"] - t1) * 1e3 / (args.steps - n1), 3)
@@ -658,21 +623,120 @@ def main():
                  "units_per_launch": dom["flops"] if prefill else dom["algorithmic_bytes"],
                  "traffic": read_traffic(name, dom["m"], kernel_source_hash())})
 
-    out = {
-        "metric": W4A4_METRIC if name in W4A4 else METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 6),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp4" if name in W4A4 else "bf16", "data": "synthetic",
-        "config": {"workload": name, "fmt": "nvfp4" if fmt == 0 else "mxfp4", "m": ms, "n": nout, "k": k,
-                   "projections": proj, "launch": args.launch, "rotated_weight_copies": copies,
-                   "step": "one call at each m in the list", "per_m": rows,
-                   "wall_s_timed": round(t_wall, 4)},
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(name, [(d["m"], d["xb"]) for d in per_m], host, args.cpu_budget)
+    res = {"name": name, "fmt": fmt, "n": nout, "k": k, "proj": proj, "ms": ms, "rows": rows,
+           "total_ms": total_ms, "value": value, "unit": unit, "roofline": roof, "copies": copies,
+           "t_wall": t_wall, "cpu_baseline": None}
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(name, [(d["m"], d["xb"]) for d in per_m], host, args.cpu_budget)
+    del weights, per_m, graphs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+# The default run: the headline workload (the metric's M = 1..8 decode
+# config) with its cross-checks and CPU baseline, then every other config of
+# the metric at its own m values.  Each config's rates also go out as flat
+# scalar keys of the JSON line (see suite_keys).
+SUITE = [("gate_up", [1, 2, 4, 8]), ("lm_head", [1, 2, 4, 8]), ("down_proj", [1, 2, 4, 8]),
+         ("o_proj", [1, 2, 4, 8]), ("prefill_nvfp4", [1024]), ("prefill_mxfp4", [1024])]
+
+
+def suite_keys(res):
+    """Flat scalar keys of one config's result: per m, the rate (GB/s for the
+    decode kernels, TFLOP/s for the tile GEMMs), its fraction of the roofline
+    peak and the time per call."""
+    out = {}
+    for r in res["rows"]:
+        tile = r["kernel"].startswith("gemm_kernel") or r["kernel"].startswith("act_quant")
+        key = "%s_m%d" % (res["name"], r["m"])
+        if tile:
+            peak = FP4_MFMA_PEAK_TFLOPS if res["name"] in W4A4 else BF16_MFMA_PEAK_TFLOPS
+            out[key + "_tflops"] = r["tflops"]
+            out[key + "_frac"] = round(r["tflops"] / peak, 4)
+        else:
+            out[key + "_gbs"] = r["gbs"]
+            out[key + "_frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+        out[key + "_us"] = r["us_per_launch"]
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="suite", choices=["suite"] + sorted(WORKLOADS),
+                    help="suite (default): every config of the metric, headline gate_up first")
+    ap.add_argument("--m", default=None,
+                    help="activation rows, comma separated (default: 1,2,4,8 for decode, 1024 for prefill)")
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="replay the timed calls from a captured HIP graph, or launch them one by one")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-crosscheck", action="store_true",
+                    help="skip the differencing and split-launch cross-checks (e.g. under a counter "
+                         "profiler, where their launches would mix with the timed ones)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device-to-device copies of MIB MiB (reference for the HBM "
+                         "byte counters) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the layer's kernels run on a single MI355X and no "
+              "multi-GPU path is built (the layer would shard over its output rows, each GPU running the same "
+              "kernels on its share of the weight).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import numpy as np
+    import fp4_weight_only_e2m1_amd as fp4
+    import synth
+
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 10}), flush=True)
+        return
+
+    name = args.workload
+    if name in ("moe_gate_up", "moe_prefill", "moe_prefill_swiglu"):
+        return run_moe(args, torch, np, fp4, synth)
+    if name == "suite":
+        results = [run_dense(args, w, wms, torch, np, fp4, synth, crosscheck=(j == 0 and not args.no_crosscheck),
+                             with_cpu=(j == 0 and not args.no_cpu_baseline))
+                   for j, (w, wms) in enumerate(SUITE)]
     else:
-        out["cpu_baseline"] = None
+        wid, fmt, n, k, proj, m_default = WORKLOADS[name]
+        if args.m is None:
+            ms = [1, 2, 4, 8] if m_default <= 8 else [m_default]
+        else:
+            ms = [int(v) for v in args.m.split(",")]
+        results = [run_dense(args, name, ms, torch, np, fp4, synth, crosscheck=not args.no_crosscheck,
+                             with_cpu=not args.no_cpu_baseline)]
+    head = results[0]
+    out = {
+        "metric": W4A4_METRIC if head["name"] in W4A4 else METRIC, "value": round(head["value"], 3),
+        "unit": head["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["total_ms"] / args.steps, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4" if head["name"] in W4A4 else "bf16", "data": "synthetic",
+        "config": {"workload": head["name"], "fmt": "nvfp4" if head["fmt"] == 0 else "mxfp4", "m": head["ms"],
+                   "n": head["n"], "k": head["k"], "projections": head["proj"], "launch": args.launch,
+                   "rotated_weight_copies": head["copies"], "step": "one call at each m in the list",
+                   "per_m": head["rows"], "wall_s_timed": round(head["t_wall"], 4),
+                   "suite": [{"workload": r["name"], "m": r["ms"], "n": r["n"], "k": r["k"],
+                              "value": round(r["value"], 3), "unit": r["unit"], "per_m": r["rows"]}
+                             for r in results[1:]]},
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+    }
+    for r in results:
+        out.update(suite_keys(r))
     print(json.dumps(out), flush=True)
 
 
