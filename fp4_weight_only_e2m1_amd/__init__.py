@@ -49,6 +49,8 @@ _SIGNATURES = {
     "fp4_workspace_bytes": (_i, [_i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fp4_w4a16_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _i, _vp, _vp, _sz, _vp,
                               ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_w4a16_linear_noalloc": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _i, _vp, _vp,
+                                      ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_w4a16_gate_up": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _f, _i, _vp, _vp, _sz, _vp,
                                ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_argmax_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
@@ -208,6 +210,26 @@ def fp4_w4a16_linear(x, prep_codes, prep_scales, n, global_scale, fmt, y=None, w
     _check("fp4_w4a16_linear", load_library().fp4_w4a16_linear(
         _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n, float(global_scale), fmt, _ptr(y),
         _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
+    return y
+
+
+def fp4_w4a16_linear_noalloc(x, prep_codes, prep_scales, n, global_scale, fmt, y, stream=None, info=None):
+    """fp4_w4a16_linear with the library's own scratch as its workspace: the
+    call allocates nothing, so y (bf16 [m, n]) must be given.  Calls that may
+    overlap on one GPU share that scratch and race."""
+    _need(x, torch.bfloat16, "x")
+    _need(y, torch.bfloat16, "y")
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    if x.dim() != 2 or y.numel() != x.shape[0] * n:
+        raise ValueError("x must be [m, k] and y hold m x n values")
+    k = x.shape[1]
+    cb, sb = fp4_prepared_bytes(n, k, fmt)
+    if prep_codes.numel() < cb or prep_scales.numel() < sb:
+        raise ValueError("prepared buffers smaller than fp4_prepared_bytes(n, k, fmt)")
+    _check("fp4_w4a16_linear_noalloc", load_library().fp4_w4a16_linear_noalloc(
+        _ptr(x), x.shape[0], k, _ptr(prep_codes), _ptr(prep_scales), n, float(global_scale), fmt, _ptr(y),
+        _stream(stream), None if info is None else ctypes.byref(info)))
     return y
 
 

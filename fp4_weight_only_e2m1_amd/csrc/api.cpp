@@ -14,8 +14,17 @@
 #include "../../include/fp4w4a16.h"
 
 #include <atomic>
+#include <mutex>
 
 #include "fp4_common.hpp"
+
+// Device memory the library owns, for fp4_w4a16_linear_noalloc only: a
+// file-scope array that every GPU holds its own copy of until the process
+// ends.  Host code never uses the array's name as an address (in host code
+// it is a stand-in, not device memory); it uses the address
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+constexpr size_t kNoallocScratchBytes = size_t{64} << 20;  // = FP4_NOALLOC_SCRATCH_BYTES
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -55,6 +64,25 @@ uint64_t next_token() {
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_EHIP; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FP4_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP4_OK;
+}
 
 // Rows per workgroup of the decode kernel m selects (m = 1..32).
 int decode_tile_rows(int m, int64_t rows_total) {
@@ -413,6 +441,29 @@ int fp4_w4a16_linear(const uint16_t* x_dev, int m, int k, const uint8_t* prep_co
   const float g[1] = {global_scale};
   return run_linear(x_dev, m, k, prep_codes_dev, prep_scales_dev, n, 1, g, fmt, y_dev, workspace_dev,
                     workspace_bytes, stream, info_out);
+}
+
+int fp4_w4a16_linear_noalloc(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                             const uint8_t* prep_scales_dev, int n, float global_scale, int fmt, uint16_t* y_dev,
+                             hipStream_t stream, fp4_dispatch_info* info_out) {
+  // Every argument check runs before the scratch lookup (the first HIP call),
+  // so an invalid call touches neither the GPU nor the scratch.
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if ((st = check_m(m))) return st;
+  if (m == 0) {
+    if (info_out) *info_out = fp4_dispatch_info{0, 0, 0, 0, 0};
+    return FP4_OK;
+  }
+  if (!x_dev || !prep_codes_dev || !prep_scales_dev || !y_dev) return FP4_EINVAL;
+  if (!aligned16(x_dev) || !aligned16(prep_codes_dev) || !aligned16(prep_scales_dev) || !aligned16(y_dev))
+    return FP4_EALIGN;
+  if (workspace_for(m, n, k, fmt, 1) > kNoallocScratchBytes) return FP4_EWORKSPACE;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  return fp4_w4a16_linear(x_dev, m, k, prep_codes_dev, prep_scales_dev, n, global_scale, fmt, y_dev, ws,
+                          kNoallocScratchBytes, stream, info_out);
 }
 
 int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,

@@ -164,6 +164,33 @@ int fp4_w4a16_linear(const uint16_t* x_dev, int m, int k,
                      hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
+ * fp4_w4a16_linear without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks, kernels, plan and
+ * results as fp4_w4a16_linear -- bit for bit -- except that the split-K
+ * partials and arrival flags (or the tile GEMM's tail partials) live in a
+ * scratch array the library owns: FP4_NOALLOC_SCRATCH_BYTES of device memory
+ * per GPU, reserved when the library's code is loaded and held until the
+ * process ends.  The call allocates nothing (no hipMalloc or hipFree).
+ *   - A call whose fp4_workspace_bytes(m, n, k, fmt, 1) exceeds the scratch
+ *     size returns FP4_EWORKSPACE and enqueues nothing (the decode shapes
+ *     need at most a few MiB; the tile GEMM's tail partials at most 64 MiB).
+ *   - Nothing in the scratch has to start at zero: the split-K flags carry a
+ *     per-call token and every partial is written before it is read.
+ *   - All calls on one GPU share its scratch: calls that may run at the same
+ *     time on that GPU (on different streams, or from several host threads
+ *     without ordering) race and give undefined results.  Calls ordered on
+ *     one stream are safe.
+ *   - The first call on a device looks up the scratch address for that
+ *     device (the current device); a failure returns FP4_EHIP.
+ */
+#define FP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fp4_w4a16_linear_noalloc(const uint16_t* x_dev, int m, int k,
+                             const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n,
+                             float global_scale, int fmt, uint16_t* y_dev,
+                             hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
  * Fused gate_up: y[:, 0:n_half] = x * gate^T, y[:, n_half:2 n_half] = x * up^T,
  * in one launch over the prepared [gate; up] weight (fp4_prepare_gate_up).
  * global_gate / global_up are the two NVFP4 global scales (ignored for MXFP4).
