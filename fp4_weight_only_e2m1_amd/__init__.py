@@ -32,7 +32,7 @@ class Fp4Error(RuntimeError):
 
 class fp4_dispatch_info(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("splits", ctypes.c_int), ("grid_x", ctypes.c_int),
-                ("grid_y", ctypes.c_int), ("block", ctypes.c_int)]
+                ("grid_y", ctypes.c_int), ("block", ctypes.c_int), ("xcds", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -47,6 +47,7 @@ _SIGNATURES = {
     "fp4_prepare": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "fp4_prepare_gate_up": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp]),
     "fp4_workspace_bytes": (_i, [_i, _i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "fp4_plan": (_i, [_i, _i, _i, _i, _i, _i, ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_w4a16_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _i, _vp, _vp, _sz, _vp,
                               ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_w4a16_linear_noalloc": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _i, _vp, _vp,
@@ -131,6 +132,13 @@ def fp4_workspace_bytes(m, n, k, fmt, projections=1):
     out = _sz()
     _check("fp4_workspace_bytes", load_library().fp4_workspace_bytes(m, n, k, fmt, projections, ctypes.byref(out)))
     return out.value
+
+
+def fp4_plan(m, n, k, fmt, projections=1, cus=256):
+    """The fp4_dispatch_info a W4A16 call would report on a device of `cus` compute units (host only)."""
+    info = fp4_dispatch_info()
+    _check("fp4_plan", load_library().fp4_plan(m, n, k, fmt, projections, cus, ctypes.byref(info)))
+    return info
 
 
 def fp4_prepare(codes, scales, n, k, fmt, prep_codes=None, prep_scales=None, stream=None):

@@ -71,6 +71,25 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxDevices] = {};
 
+// XCDs of the current device, from its compute-unit count (looked up once
+// per device and kept).  Only the tile GEMMs' tile order uses it.
+std::atomic<int> g_xcds[kMaxDevices] = {};
+
+int device_xcds(int* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4_EHIP;
+  int x = g_xcds[dev].load(std::memory_order_relaxed);
+  if (x == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return FP4_EHIP;
+    x = fp4::xcds_of(cus);
+    g_xcds[dev].store(x, std::memory_order_relaxed);
+  }
+  *out = x;
+  return FP4_OK;
+}
+
 int noalloc_scratch(void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4_EHIP;
@@ -180,8 +199,10 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
       if (e != hipSuccess) return FP4_EHIP;
     }
     if (info) *info = fp4_dispatch_info{on_mfma ? 2 : 0, a.splits, static_cast<int>(grid.x),
-                                        static_cast<int>(grid.y), static_cast<int>(block.x)};
+                                        static_cast<int>(grid.y), static_cast<int>(block.x), 0};
   } else {
+    int xcds = 0;
+    if ((st = device_xcds(&xcds))) return st;
     fp4::MfmaArgs a{};
     a.x = x;
     a.codes = codes;
@@ -200,12 +221,12 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
     a.act = act;
-    a.plan = fp4::gemm_plan(m, a.rows_total, k);
-    if (a.plan.tail_tiles > 0 && !a.plan.mhalf) a.partial = static_cast<float*>(ws);
+    a.plan = fp4::gemm_plan(m, a.rows_total, k, xcds);
+    if (a.plan.tail_tiles > 0) a.partial = static_cast<float*>(ws);
     hipError_t e = fp4::launch_mfma(a, fmt, stream, &grid, &block);
     if (e != hipSuccess) return FP4_EHIP;
-    if (info) *info = fp4_dispatch_info{1, a.plan.mhalf ? 1 : a.plan.splits, static_cast<int>(grid.x), static_cast<int>(grid.y),
-                                        static_cast<int>(block.x)};
+    if (info) *info = fp4_dispatch_info{1, a.plan.splits, static_cast<int>(grid.x),
+                                        static_cast<int>(grid.y), static_cast<int>(block.x), xcds};
   }
   return FP4_OK;
 }
@@ -238,6 +259,8 @@ int run_w4a4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y) || !aligned16(ws)) return FP4_EALIGN;
   size_t partial_offset = 0;
   if (ws_bytes < w4a4_workspace_for(m, n_proj, k, projections, &partial_offset)) return FP4_EWORKSPACE;
+  int xcds = 0;
+  if ((st = device_xcds(&xcds))) return st;
 
   const fp4::PreparedShape ps = fp4::prepared_shape(n_proj, k, fmt);
   uint8_t* xq_codes = static_cast<uint8_t*>(ws);
@@ -258,7 +281,7 @@ int run_w4a4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_
   a.rows_total = ps.n_pad * projections;
   a.ldy = static_cast<int64_t>(n_proj) * projections;
   a.gscale[0] = a.gscale[1] = 1.0f;
-  a.plan = fp4::w4a4_plan(m, a.rows_total, k);
+  a.plan = fp4::w4a4_plan(m, a.rows_total, k, xcds);
   if (a.plan.tail_tiles > 0 && !a.plan.mhalf)
     a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + partial_offset);
   a.xq_codes = xq_codes;
@@ -267,7 +290,7 @@ int run_w4a4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_
   dim3 grid, block;
   if (fp4::launch_w4a4(a, stream, &grid, &block) != hipSuccess) return FP4_EHIP;
   if (info) *info = fp4_dispatch_info{4, a.plan.mhalf ? 1 : a.plan.splits, static_cast<int>(grid.x),
-                                      static_cast<int>(grid.y), static_cast<int>(block.x)};
+                                      static_cast<int>(grid.y), static_cast<int>(block.x), xcds};
   return FP4_OK;
 }
 
@@ -348,6 +371,8 @@ int run_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_t* pre
   // Workgroups of the tile launch: every (activation tile slot, weight tile).
   const int64_t wgs = fp4::moe_gemm_slots(pairs, experts) * (rows_total / fp4::kGemmBN);
   if (wgs * 256 >= (int64_t{1} << 32)) return FP4_EINVAL;
+  int xcds = 0;
+  if (int e = device_xcds(&xcds)) return e;
 
   fp4::MfmaArgs a{};
   a.x = x_dev;
@@ -366,14 +391,14 @@ int run_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_t* pre
   a.ldy = n_proj;
   a.gscale[0] = a.gscale[1] = 1.0f;
   a.act = act ? 1 : 0;
-  a.plan = fp4::gemm_plan(fp4::kGemmBM, a.rows_total, k);  // only n_tiles and ksteps are used
+  a.plan = fp4::gemm_plan(fp4::kGemmBM, a.rows_total, k, xcds);  // only n_tiles, ksteps and xcds are used
   fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pair_tokens_dev, tokens, pairs,
                               experts, nullptr);
   moe.code_stride *= projections;
   moe.scale_stride *= projections;
   dim3 grid, block;
   if (fp4::launch_moe_gemm(a, moe, fmt, stream, &grid, &block) != hipSuccess) return FP4_EHIP;
-  if (info_out) *info_out = fp4_dispatch_info{5, 1, static_cast<int>(grid.x), 0, static_cast<int>(block.x)};
+  if (info_out) *info_out = fp4_dispatch_info{5, 1, static_cast<int>(grid.x), 0, static_cast<int>(block.x), xcds};
   return FP4_OK;
 }
 
@@ -422,6 +447,34 @@ int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scale
   e = fp4::launch_prepare(up_codes_dev, up_scales_dev, n_half, k, fmt, prep_codes_dev + s.code_bytes,
                           prep_scales_dev + s.scale_bytes, stream);
   return to_status(e);
+}
+
+int fp4_plan(int m, int n, int k, int fmt, int projections, int cus, fp4_dispatch_info* info_out) {
+  int st = check_fmt(fmt);
+  if (st) return st;
+  if ((st = check_nk(n, k))) return st;
+  if ((st = check_m(m))) return st;
+  if ((projections != 1 && projections != 2) || cus < 1 || !info_out) return FP4_EINVAL;
+  if (static_cast<int64_t>(n) * projections > FP4_MAX_N) return FP4_EINVAL;
+  if (m == 0) {
+    *info_out = fp4_dispatch_info{0, 0, 0, 0, 0, 0};
+    return FP4_OK;
+  }
+  const int64_t rows_total = projections * fp4::round_up(n, fp4::kRowAlign);
+  if (m <= fp4::kDecodeMaxM) {
+    // The decode kernels: grid (row tiles, K splits), as run_linear launches them.
+    const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
+    const int splits = on_mfma ? fp4::decode_mfma_splits(n, k) : fp4::gemv_splits(n, k, fmt);
+    *info_out = fp4_dispatch_info{on_mfma ? 2 : 0, splits, static_cast<int>(rows_total / decode_tile_rows(m, rows_total)),
+                                  splits, fp4::kDecodeThreads, 0};
+    return FP4_OK;
+  }
+  const int xcds = fp4::xcds_of(cus);
+  const fp4::GemmPlan p = fp4::gemm_plan(m, rows_total, k, xcds);
+  const int units = p.tail_tiles * p.splits;
+  *info_out = fp4_dispatch_info{1, p.splits, p.dp_tiles > units ? p.dp_tiles : units, units,
+                                fp4::kGemmThreads, xcds};
+  return FP4_OK;
 }
 
 int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* bytes_out) {

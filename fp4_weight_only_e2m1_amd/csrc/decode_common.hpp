@@ -7,7 +7,6 @@
 
 namespace fp4 {
 
-constexpr int kDecodeThreads = 256;
 constexpr int kChunksPerSlab = kSlabK / 8;  // 16-byte chunks of x (8 bf16) per slab
 
 // First and one-past-last slab of K split `split`.
@@ -162,6 +161,24 @@ __device__ __forceinline__ void act_store(ActTile<M>& at, const GemvArgs& a, int
 // a local L2 line.  Ordering comes from waiting for those stores to complete
 // (s_waitcnt 0) before the next step, not from device-scope fences, which on
 // this target write back and invalidate the whole L2.
+//
+// Why this is a correct publication under the AMDGPU memory model (the LLVM
+// AMDGPUUsage code sequences for the GFX942 family, which gfx950 follows):
+// an agent-scope monotonic load or store is the plain instruction with sc1
+// set; an agent-scope release store adds "buffer_wbl2 sc1; s_waitcnt
+// vmcnt(0)" before it, and an agent-scope acquire load adds "s_waitcnt
+// vmcnt(0); buffer_inv sc1" after it.  The wbl2 writes back L2 lines dirtied
+// by non-atomic stores, and the inv drops L2 lines that non-atomic loads could
+// otherwise hit stale; both exist only to make non-atomic data coherent.  Here
+// every store a reader depends on (partials, flags) and every load that
+// depends on a flag (partials) is itself an sc1 agent-scope access, so no
+// non-atomic data is published and the two cache operations have nothing to
+// do.  What remains of release/acquire is the ordering, and it is explicit:
+// a workgroup's partial stores are complete (s_waitcnt vmcnt(0)) before its
+// flag store is issued, and the partial loads are issued only after the flag
+// loads have returned and been compared (s_waitcnt, then a branch on their
+// values), so a workgroup that sees every flag reads every partial from the
+// coherence point after it was written.
 __device__ __forceinline__ void store_partial(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

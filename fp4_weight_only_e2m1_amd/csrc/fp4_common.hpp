@@ -19,9 +19,18 @@ constexpr int kSlabK = 1024;
 constexpr int kRowGroup = 16;        // rows whose scale bytes are interleaved
 constexpr int kGemvTeams = 8;        // 32-lane teams per 256-thread GEMV workgroup
 constexpr int kDecodeTileRows = 64;  // rows of an MFMA-decode workgroup
+constexpr int kDecodeThreads = 256;  // threads of a decode workgroup (GEMV and MFMA decode)
 constexpr int kGemvMaxSlabsPerSplit = 4;  // x staged in LDS: 8 rows * 4096 k * 2 B = 64 KiB
 constexpr int kGemvMaxM = 8;
-constexpr int kTargetCUs = 256;      // MI355X compute units
+constexpr int kTargetCUs = 256;      // MI355X compute units: the nominal machine of every plan
+// Compute units per XCD on MI355X (8 XCDs of 32 CUs).  Workgroup b of a launch
+// is dispatched to XCD b % (number of XCDs).
+constexpr int kCUsPerXcd = 32;
+// XCDs of a device (or partition) of `cus` compute units, 1..8.
+inline int xcds_of(int cus) {
+  const int x = cus / kCUsPerXcd;
+  return x < 1 ? 1 : x > 8 ? 8 : x;
+}
 // m from which the decode path contracts on MFMA instead of VALU v_dot2
 // (measured crossover on MI355X: the VALU GEMV is faster at m = 1, 2).
 constexpr int kDecodeMfmaMinM = 3;
@@ -177,9 +186,13 @@ constexpr int kGemmWavesM = 1;
 constexpr int kGemmBM = 128 * kGemmWavesM;
 constexpr int kGemmBN = 256;
 constexpr int kGemmBK = 64;
+constexpr int kGemmThreads = kGemmWavesM * 4 * 64;
 constexpr int kGemmSlots = kTargetCUs * (kGemmWavesM == 1 ? 2 : 1);
-// Fewest K steps a split of a tail tile is given.
-constexpr int kGemmMinSplitSteps = 8;
+// Fewest K steps a split of a tail tile is given: 20 (1280 codes).  Measured
+// on MI355X for the 17408 x 5120 prefill GEMM, 4 splits of its 80 steps beat
+// 8 to 10 shorter ones by 1.5 to 2.5 % at m = 1024 and 2048: the shorter tail
+// saves less than writing, reading back and adding more partial tiles costs.
+constexpr int kGemmMinSplitSteps = 20;
 
 // How a prefill call's tiles are spread over the resident workgroups.  Tiles
 // are taken whole while they fill complete rounds of kGemmSlots workgroups
@@ -192,7 +205,8 @@ struct GemmPlan {
   int tail_tiles;  // tiles computed as `splits` K ranges
   int splits;
   int ksteps;      // K steps of a whole tile
-  int mhalf;       // tail tiles run as two halves of their rows over all of K instead of K ranges
+  int mhalf;       // W4A4 only: tail tiles run as two halves of their rows over all of K instead of K ranges
+  int xcds;        // XCDs the tile order deals the data-parallel tiles over
 };
 
 // Plan over tiles of `bm` activation rows, K steps of `step_k` codes, `slots`
@@ -200,6 +214,7 @@ struct GemmPlan {
 inline GemmPlan tile_plan(int m, int64_t rows_total, int k, int step_k, int min_split_steps, int bm, int slots) {
   GemmPlan p;
   p.mhalf = 0;
+  p.xcds = 8;
   p.m_tiles = static_cast<int>((m + bm - 1) / bm);
   p.n_tiles = static_cast<int>(rows_total / kGemmBN);
   p.tiles = p.m_tiles * p.n_tiles;
@@ -220,19 +235,30 @@ inline GemmPlan tile_plan(int m, int64_t rows_total, int k, int step_k, int min_
   return p;
 }
 
-// Where the tail tiles would be split two ways along K, they run as their
-// two 64-row halves over all of K instead (no partials, no reduce launch), for
-// calls whose tiles compute all 128 rows (m > 64).
-inline GemmPlan gemm_plan(int m, int64_t rows_total, int k) {
+// A tail that would be split only two ways runs as whole tiles instead, one
+// per CU beside an idle workgroup slot.  Measured on MI355X this beats both
+// the two K halves (partials and a reduce launch) and the two 64-row halves
+// over all of K (each decoding the whole weight tile): 17408 x 5120 at
+// m = 1408: 1112 vs 1007 TFLOP/s; 5120 x 17408 at m = 1280 (200 tiles):
+// 926 vs 790; 24576 x 4096 at m = 1024: 5 to 9 % faster.
+// The tiling, the tail and its split count come from the nominal 256-CU
+// machine (kGemmSlots) whatever the device, so an output's summation order
+// never depends on the device; only the XCD deal of the tile order (`xcds`,
+// from the device's CU count) does.
+inline GemmPlan gemm_plan(int m, int64_t rows_total, int k, int xcds = 8) {
   GemmPlan p = tile_plan(m, rows_total, k, kGemmBK, kGemmMinSplitSteps, kGemmBM, kGemmSlots);
-  if (p.splits == 2 && m > 64) p.mhalf = 1;
+  if (p.splits == 2) {
+    p.dp_tiles = p.tiles;
+    p.tail_tiles = 0;
+    p.splits = 1;
+  }
+  p.xcds = xcds;
   return p;
 }
 
 // W4A4 tile GEMM (MXFP4 activations x MXFP4 weights on the block-scaled
 // MFMA): 256 x 256 tiles, one 8-wave workgroup per CU, K stepping 128 codes
-// per stage, tail splits of at least 4 stages (512 codes, as for the W4A16
-// GEMM).
+// per stage, tail splits of at least 4 stages (512 codes).
 constexpr int kW4BM = 256;
 constexpr int kW4BK = 128;
 constexpr int kW4Slots = kTargetCUs;
@@ -241,9 +267,13 @@ constexpr int kW4MinSplitSteps = 4;
 // Where the plan would split each tail tile in two along K, the W4A4 GEMM
 // runs the two 128-row halves of the tile over all of K instead: the same
 // MFMA work per workgroup, no partial tiles to write, read back and add.
-inline GemmPlan w4a4_plan(int m, int64_t rows_total, int k) {
+// Unlike the W4A16 GEMM's, its half tiles decode no weights, and running the
+// tail whole instead measured slower on MI355X (5120 x 17408 at m = 1536:
+// 1790 vs 2090 TFLOP/s; 12288 x 4096 at m = 2048: 2240 vs 2350).
+inline GemmPlan w4a4_plan(int m, int64_t rows_total, int k, int xcds = 8) {
   GemmPlan p = tile_plan(m, rows_total, k, kW4BK, kW4MinSplitSteps, kW4BM, kW4Slots);
   if (p.splits == 2) p.mhalf = 1;
+  p.xcds = xcds;
   return p;
 }
 

@@ -40,13 +40,15 @@ __device__ __forceinline__ void tile_coords(const GemmPlan& pl, int t, int64_t& 
 }
 
 // Data-parallel tile `t` of workgroup `bid` < dp_tiles.  Workgroup b runs on
-// XCD b % 8, so XCD x gets the ids x, x + 8, ...; it is given the contiguous
-// run of tiles starting at x * q + min(x, r) (q = tiles / 8, r = tiles % 8).
+// XCD b % X (X = pl.xcds), so XCD x gets the ids x, x + X, ...; it is given
+// the contiguous run of tiles starting at x * q + min(x, r) (q = tiles / X,
+// r = tiles % X).
 __device__ __forceinline__ int dp_tile_of(const GemmPlan& pl, int bid) {
-  const int xcd = bid % 8;
-  const int q = pl.dp_tiles / 8;
-  const int rr = pl.dp_tiles % 8;
-  return xcd * q + (xcd < rr ? xcd : rr) + bid / 8;
+  const int nx = pl.xcds;
+  const int xcd = bid % nx;
+  const int q = pl.dp_tiles / nx;
+  const int rr = pl.dp_tiles % nx;
+  return xcd * q + (xcd < rr ? xcd : rr) + bid / nx;
 }
 
 // Result stores through LDS.  In the MFMA result layout a lane holds 4

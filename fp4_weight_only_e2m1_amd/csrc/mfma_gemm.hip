@@ -47,7 +47,8 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = kGemmWavesM * 4;
-constexpr int kThreads = kWaves * 64;
+constexpr int kThreads = kGemmThreads;
+static_assert(kThreads == kWaves * 64, "one wave per 64 threads");
 constexpr int kStages = 3;
 constexpr int kAChunks = kGemmBM * kGemmBK * 2 / 16;  // 16-byte chunks of an x stage
 constexpr int kBChunks = kGemmBN * kGemmBK / 2 / 16;  // 16-byte chunks of a code stage
@@ -447,20 +448,6 @@ void gemm_kernel(const MfmaArgs a) {
   const int split = u % pl.splits;
   int64_t m0, n0;
   tile_coords(pl, pl.dp_tiles + u / pl.splits, m0, n0);
-  if constexpr (FI == 4) {
-    if (pl.mhalf) {
-      // Half u % 2 of the tail tile's rows, over all of K, stored as y.
-      m0 += (kGemmBM / 2) * split;
-      if (m0 >= a.m) return;
-      f32x16_t acc2[2][2];
-      run_tile<FMT, 2>(a, m0, n0, 0, pl.ksteps, st, acc2);
-      if constexpr (ACT)
-        store_tile_swiglu_staged<kGemmBM / 2, kThreads, 64, 2>(a, m0, n0, wave, acc2, lds);
-      else
-        store_tile_bf16_staged<kGemmBM / 2, kThreads, kGemmBM / 2, 2>(a, m0, n0, wave, acc2, lds);
-      return;
-    }
-  }
   run_tile<FMT, FI>(a, m0, n0, static_cast<int>(static_cast<int64_t>(split) * pl.ksteps / pl.splits),
                     static_cast<int>(static_cast<int64_t>(split + 1) * pl.ksteps / pl.splits), st, acc);
   store_tile_partial_staged<kGemmBM, kThreads, 64, FI>(a, u, m0, wave, acc, lds);
@@ -474,7 +461,8 @@ void gemm_kernel(const MfmaArgs a) {
 // in all, work item L < T n_tiles is weight-row tile L % n_tiles of the
 // (L / n_tiles)-th tile, computed over all of K with that expert's prepared
 // weight and stored as bf16 y at the same pair rows.  Items are dealt to the
-// workgroups XCD-aware: workgroup b runs on XCD b % 8, and each XCD gets a
+// workgroups XCD-aware: workgroup b runs on XCD b % X (X = plan.xcds, from the
+// device's compute units), and each XCD gets a
 // contiguous run of items, so the weight tiles of one activation tile (which
 // share its x rows) and an expert's activation tiles (which share its weight)
 // meet in one L2; T is counted first, so idle slots leave no XCD short of
@@ -541,9 +529,10 @@ void moe_gemm_kernel(const MfmaArgs base, const MoeArgs moe) {
     }
     // Items dealt to XCDs in contiguous runs (XCD x: q or q + 1 items).
     const int64_t items = static_cast<int64_t>(total) * n_tiles;
-    const int xcd = static_cast<int>(blockIdx.x % 8);
-    const int64_t q = items / 8, r = items % 8;
-    const int64_t j = blockIdx.x / 8;
+    const int nx = base.plan.xcds;
+    const int xcd = static_cast<int>(blockIdx.x % nx);
+    const int64_t q = items / nx, r = items % nx;
+    const int64_t j = blockIdx.x / nx;
     const int64_t item = xcd * q + (xcd < r ? xcd : r) + j;
     const bool live = j < q + (xcd < r ? 1 : 0);
     const int slot = live ? static_cast<int>(item / n_tiles) : -1;
@@ -739,7 +728,7 @@ hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* gri
       launch_gemm_fi<kFmtMxfp4, false>(a, fi, grid, block, stream);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || units == 0 || p.mhalf) return e;
+  if (e != hipSuccess || units == 0) return e;
   return launch_tail_reduce(a, kGemmBM, stream);
 }
 

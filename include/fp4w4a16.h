@@ -74,15 +74,31 @@ typedef struct fp4_dispatch_info {
                   4 = W4A4 MXFP4 tile GEMM (any m),
                   5 = grouped MoE tile GEMM (prefill) */
   int splits;  /* K splits: decode kernels split every tile, the tile GEMMs only
-                  their tail tiles (1 = no split; tail tiles run as row halves
-                  over all of K also report 1) */
+                  their tail tiles (1 = no split; W4A4 tail tiles run as row
+                  halves over all of K also report 1) */
   int grid_x;  /* decode: workgroups along the output rows; tile GEMMs:
                   workgroups of the launch */
   int grid_y;  /* decode / MoE: workgroups along the second grid axis; tile
-                  GEMMs: workgroups that run the tail tiles (tail tiles x 2
-                  for row halves, x splits for K ranges; 0 if none) */
+                  GEMMs: workgroups that run the tail tiles (tail tiles x
+                  splits for K ranges, x 2 for W4A4 row halves; 0 if none) */
   int block;   /* threads per workgroup */
+  int xcds;    /* tile GEMMs: the XCDs their tile order was dealt over, from the
+                  device's compute-unit count (1 to 8; 32 CUs per XCD); 0 for
+                  the decode kernels, whose workgroups own fixed row tiles */
 } fp4_dispatch_info;
+
+/*
+ * The launch plan a W4A16 call would use on a device (or partition) with
+ * `cus` compute units, without running it: what fp4_w4a16_linear
+ * (projections = 1, n rows) or fp4_w4a16_gate_up (projections = 2, n rows per
+ * half) fills into its fp4_dispatch_info on such a device.  Tile sizes and
+ * K-split counts are those of the full 256-CU MI355X on every device, so an
+ * output's summation order (and every output bit) never depends on the
+ * device; only the XCD deal of the tile GEMMs' tile order follows `cus`.
+ * Host utility (no passage defines it): pure host function, never touches
+ * the GPU.  FP4_EINVAL for sizes out of range, cus < 1 or a null out.
+ */
+int fp4_plan(int m, int n, int k, int fmt, int projections, int cus, fp4_dispatch_info* info_out);
 
 /*
  * Size of a prepared weight of n rows and k columns.

@@ -76,16 +76,17 @@ def test_prepared_bytes_rejects(lib, n, k, fmt, bad):
 def _prefill_workspace(m, n, k, projections=1):
     # Prefill tiles are 128 x 256; 512 workgroups are resident at once.  Tiles
     # that do not fill a whole round are split along K (at most 512 / tail
-    # ways, at least 8 K steps of 64 each) into fp32 partial tiles.
+    # ways, at least 20 K steps of 64 each) into fp32 partial tiles.
     tiles = -(-m // 128) * (projections * (-(-n // 256) * 256) // 256)
+    # A tail that would split only two ways runs whole.
     tail = tiles % 512
-    s = min(512 // tail, -(-k // 64) // 8) if tail else 1
-    return 0 if s <= 1 else tail * s * 128 * 256 * 4
+    s = min(512 // tail, -(-k // 64) // 20) if tail else 1
+    return 0 if s <= 2 else tail * s * 128 * 256 * 4
 
 
 def test_workspace_bytes_policy():
     # m > 32 runs the prefill GEMM, whose tail tiles split K.
-    assert fp4.fp4_workspace_bytes(33, 17408, 5120, NV) == _prefill_workspace(33, 17408, 5120) == 68 * 7 * 131072
+    assert fp4.fp4_workspace_bytes(33, 17408, 5120, NV) == _prefill_workspace(33, 17408, 5120) == 68 * 4 * 131072
     # m = 9..32 still runs the MFMA decode kernel: 272 tiles, no split; the
     # down_proj shape splits 6 ways as at m = 8, with partials for m rows.
     assert fp4.fp4_workspace_bytes(16, 17408, 5120, NV) == 0
@@ -94,7 +95,7 @@ def test_workspace_bytes_policy():
     assert fp4.fp4_workspace_bytes(32, 5120, 17408, NV) == 6 * 32 * 5120 * 4 + 5120 // 64 * 6 * 8
     # The SwiGLU gate_up leaves the decode kernels above 16 rows.
     assert fp4.fp4_swiglu_workspace_bytes(17, 1024, 12288, MX) == _prefill_workspace(17, 1024, 12288, 2)
-    assert fp4.fp4_workspace_bytes(1024, 17408, 5120, MX) == _prefill_workspace(1024, 17408, 5120) == 32 * 10 * 131072
+    assert fp4.fp4_workspace_bytes(1024, 17408, 5120, MX) == _prefill_workspace(1024, 17408, 5120) == 32 * 4 * 131072
     assert fp4.fp4_workspace_bytes(4096, 17408, 5120, NV) == _prefill_workspace(4096, 17408, 5120)
     assert fp4.fp4_workspace_bytes(65536, 256, 5120, NV) == 0      # 512 tiles: one full round, no tail
     assert fp4.fp4_workspace_bytes(200, 300, 256, NV) == 0         # 4 K steps: too short to split
@@ -124,6 +125,47 @@ def test_workspace_bytes_policy():
     two = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 2)
     assert two == 2 * one
     assert fp4.fp4_workspace_bytes(1, 512, 256, NV) == 0
+
+
+def test_plan_follows_cu_count_only_in_the_xcd_deal():
+    # A device of fewer compute units (a partition, a smaller part) gets the
+    # same kernel, tiles and K splits -- so the same summation order and the
+    # same output bits -- and only deals the tile GEMM's tiles over its own XCDs
+    # (32 CUs each).
+    shapes = [(1024, 17408, 5120, NV, 1), (1024, 17408, 5120, MX, 1), (4096, 17408, 5120, NV, 1),
+              (33, 1024, 12288, MX, 2), (200, 248320, 5120, NV, 1), (1024, 12288, 4096, MX, 2),
+              (1, 12288, 4096, MX, 2), (8, 5120, 17408, NV, 1), (24, 5120, 6144, NV, 1), (2, 248320, 5120, NV, 1)]
+    for m, n, k, fmt, proj in shapes:
+        full = fp4.fp4_plan(m, n, k, fmt, proj, 256).as_dict()
+        for cus, xcds in [(256, 8), (304, 8), (224, 7), (128, 4), (64, 2), (32, 1), (20, 1)]:
+            got = fp4.fp4_plan(m, n, k, fmt, proj, cus).as_dict()
+            want = dict(full, xcds=xcds if m > 32 else 0)
+            assert got == want, (m, n, k, cus, got, want)
+    # The plans the headline shapes run: the 17408 x 5120 prefill GEMM at
+    # m = 1024 has 8 x 68 = 544 tiles: 512 whole, 32 tail tiles in 4 K splits.
+    p = fp4.fp4_plan(1024, 17408, 5120, NV, 1, 256)
+    assert (p.kernel, p.splits, p.grid_x, p.grid_y, p.block, p.xcds) == (1, 4, 512, 128, 256, 8)
+    # gate_up 2 x 12288 x 4096 at m = 1024: 768 tiles; a tail of 256 would
+    # split only two ways, so all 768 run whole.
+    p = fp4.fp4_plan(1024, 12288, 4096, MX, 2, 256)
+    assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (1, 1, 768, 0)
+    assert fp4.fp4_workspace_bytes(1024, 12288, 4096, MX, 2) == 0
+    # Decode: the MFMA kernel on 64-row tiles, down_proj split 6 ways along K.
+    p = fp4.fp4_plan(8, 5120, 17408, NV, 1, 32)
+    assert (p.kernel, p.splits, p.grid_x, p.grid_y, p.block, p.xcds) == (2, 6, 80, 6, 256, 0)
+    p = fp4.fp4_plan(1, 248320, 5120, NV, 1, 256)
+    assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (0, 2, 248320 // 64, 2)
+    p = fp4.fp4_plan(0, 512, 256, NV, 1, 256)
+    assert p.as_dict() == dict(kernel=0, splits=0, grid_x=0, grid_y=0, block=0, xcds=0)
+
+
+@pytest.mark.parametrize("args", [(1, 512, 256, NV, 1, 0), (1, 512, 256, NV, 3, 256), (-1, 512, 256, NV, 1, 256),
+                                  (1, 0, 256, NV, 1, 256), (1, 512, 48, NV, 1, 256)])
+def test_plan_rejects(lib, args):
+    info = fp4.fp4_dispatch_info()
+    assert lib.fp4_plan(*args, ctypes.byref(info)) == ST["EINVAL"]
+    assert lib.fp4_plan(1, 512, 256, 5, 1, 256, ctypes.byref(info)) == ST["EFMT"]
+    assert lib.fp4_plan(1, 512, 256, NV, 1, 256, None) == ST["EINVAL"]
 
 
 FAKE = 0x10000  # an aligned address that is never dereferenced: every call below fails validation first

@@ -106,8 +106,8 @@ CASES = [
     # Tile GEMM: 64 rows (2-block instances), 128 rows (4-block instances).
     ("gemm m=64", 64, 64, [list(range(64))], 1, False),
     ("gemm m=128", 128, 128, [list(range(128))], 1, False),
-    # Tile GEMM with k = 2048 on one tile: its K split 4 ways, summed by the reduce launch.
-    ("gemm m=40 split", 40, 2048, [[48 * j + (j % 16) for j in range(40)]], 1, True),
+    # Tile GEMM with k = 5120 on one tile: its K split 4 ways, summed by the reduce launch.
+    ("gemm m=40 split", 40, 5120, [[128 * j + (j % 16) for j in range(40)]], 1, True),
 ]
 
 

@@ -123,19 +123,21 @@ def test_mfma_matches_oracle(fmt, n, k, m):
     assert_close(y_host(y), y_ref, "mfma fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
 
 
-@pytest.mark.parametrize("fmt,n,k,m", [(NV, 25600, 1024, 130), (MX, 30720, 2048, 200)])
-def test_tail_row_halves(fmt, n, k, m):
-    # 200 / 240 tiles of 128 x 256: the tail's two-way K split runs as two
-    # 64-row halves per tile over all of K, with no workspace and no reduce
-    # launch; at m = 130 the second half of the lower row of tiles is past m.
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 25600, 2560, 130), (MX, 30720, 4096, 200)])
+def test_two_way_tail_runs_whole(fmt, n, k, m):
+    # 200 / 240 tiles of 128 x 256 against 512 workgroup slots: a tail that
+    # would split only two ways along K runs as whole tiles, with no
+    # workspace and no reduce launch; at m = 130 most of the lower row of
+    # tiles is past m.
     assert fp4.fp4_workspace_bytes(m, n, k, fmt) == 0
     packed, scales, g = _quantized(fmt, n, k, tensor=6)
     xbits = synth.activations(synth.TINY, m, k)
     info = fp4.fp4_dispatch_info()
     y = _run_linear(packed, scales, g, fmt, n, k, xbits, info)
-    assert info.kernel == 1 and info.splits == 1 and info.grid_y > 0
+    tiles = -(-m // 128) * (n // 256)
+    assert (info.kernel, info.splits, info.grid_x, info.grid_y) == (1, 1, tiles, 0)
     y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
-    assert_close(y_host(y), y_ref, "row halves fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
+    assert_close(y_host(y), y_ref, "whole tail fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
 
 
 @pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 2048, 1), (MX, 512, 2048, 4), (NV, 300, 5120, 8),
@@ -200,7 +202,7 @@ def test_deterministic_and_workspace_poison(fmt, n, k, m):
 
 
 @pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 17408, 1), (NV, 640, 6144, 2), (MX, 1024, 5120, 1),
-                                        (NV, 512, 5120, 100), (MX, 300, 4096, 300), (NV, 256, 2080, 40)])
+                                        (NV, 512, 5120, 100), (MX, 300, 4096, 300), (NV, 256, 3872, 40)])
 def test_split_k_handshake_repeated(fmt, n, k, m):
     # The split-K finish exchanges partials between workgroups in one launch
     # (decode GEMV splits; prefill tail tiles, the last case with a ragged

@@ -60,11 +60,11 @@ def test_swiglu_matches_oracle(fmt, nh, k, m):
     assert_close(y_host(y), ref, "swiglu fmt=%d nh=%d k=%d m=%d" % (fmt, nh, k, m))
 
 
-@pytest.mark.parametrize("fmt,nh,k,m", [(MX, 12288, 1024, 130), (NV, 12288, 1024, 200)])
-def test_swiglu_tail_row_halves(fmt, nh, k, m):
-    # 192 tiles of 128 x 256 past no full round: their two-way K split runs
-    # as two 64-row halves over all of K (no workspace); at m = 130 the second
-    # half of the lower row of tiles is past m.
+@pytest.mark.parametrize("fmt,nh,k,m", [(MX, 12288, 2560, 130), (NV, 12288, 2560, 200)])
+def test_swiglu_two_way_tail_runs_whole(fmt, nh, k, m):
+    # 192 tiles of 128 x 256 past no full round: a tail that would split only
+    # two ways along K runs as whole tiles (no workspace); at m = 130 most of
+    # the lower row of tiles is past m.
     assert fp4.fp4_swiglu_workspace_bytes(m, nh, k, fmt) == 0
     test_swiglu_matches_oracle(fmt, nh, k, m)
 

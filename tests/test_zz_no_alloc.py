@@ -37,7 +37,7 @@ def _noalloc(lib, x, pc, ps, n, g, fmt, y, info):
 PAIRS = [
     [(NV, 5120, 17408, 8), (NV, 5120, 6144, 4)],    # MFMA decode, 6 then 3 K splits
     [(MX, 1024, 8192, 2), (NV, 512, 5120, 1)],      # VALU GEMV, K split in two
-    [(NV, 4096, 5120, 300), (MX, 512, 2048, 40)],   # tile GEMM, split tail tiles
+    [(NV, 4096, 5120, 300), (MX, 512, 4096, 40)],   # tile GEMM, split tail tiles
 ]
 
 
