@@ -56,6 +56,10 @@ from .reference import (
     quantize_act_mxfp4,
     dequantize_act_mxfp4,
     w4a4_linear,
+    e4m3fn_nearest_even,
+    quantize_act_nvfp4,
+    dequantize_act_nvfp4,
+    w4a4_nvfp4_linear,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
 )
@@ -67,5 +71,6 @@ __all__ = [
     "FMT_NVFP4", "FMT_MXFP4", "GROUP",
     "unpack_codes", "dequantize", "linear", "linear_rows", "gate_up", "greedy_argmax", "moe_decode", "silu", "gate_up_swiglu",
     "e2m1_nearest_even", "quantize_act_mxfp4", "dequantize_act_mxfp4", "w4a4_linear",
+    "e4m3fn_nearest_even", "quantize_act_nvfp4", "dequantize_act_nvfp4", "w4a4_nvfp4_linear",
     "linear_f64_bruteforce", "bf16_bits_to_f32", "f32_to_bf16_bits",
 ]

@@ -275,3 +275,102 @@ def w4a4_linear(x, packed, scales, k):
     xq = dequantize_act_mxfp4(xc, xs)
     w = dequantize(packed, scales, k, FMT_MXFP4).astype(np.float64)
     return xq @ w.T
+
+
+# --- W4A4 variant: NVFP4 activations against NVFP4 weights ------------------
+#
+# The pages' other W4A4 arm is ModelOpt's: an NVFP4 checkpoint carries a
+# per-tensor activation scale (input_scale); consuming it sets the GEMM's
+# alpha (0.0078125 on the pages' checkpoint) and routes the layer to a GEMM
+# over 4-bit activations instead of the weight-only one ("keep the ModelOpt
+# NVFP4 lm_head packed", vllm.cpp PR #263, section "Round-1 findings
+# resolved", item 1; "re-verify 27B NVFP4 on the nvidia ModelOpt checkpoint",
+# vllm.cpp PR #178, section "W4A16 is the default for ModelOpt").  The pages
+# keep it behind an opt-in switch for A/B runs; here it is a separate, opt-in
+# entry point.
+#
+# Readings taken where the pages are silent (they name the scale and alpha,
+# not the activation quantizer):
+# * The activations are quantized per row, per block of 16 consecutive k, by
+#   the same two-level NVFP4 rule as the weights, with G_x = input_scale (a
+#   float32 per-tensor scale that multiplies, like the weights' G):
+#     s = fl32(fl32(amax / 6) / G_x)        amax = max |x| over the block
+#     S = E4M3FN(s)                          nearest, ties to even, saturating at 448
+#     q = fl32(S * G_x)
+#     code = E2M1(fl32(x / q))               nearest, ties to the even code,
+#                                            saturating at 6, sign bit of x
+#   every step in float32 (each division and product correctly rounded), so
+#   each decision is taken on the float32 value.  A block with q == 0 gets
+#   code 0 (sign kept) for every element.
+# * A block holding an Inf or NaN gets scale byte 0x7F (E4M3FN NaN) and codes
+#   0 (sign kept), so its products are NaN.
+# * alpha = fl32(G_x * G_w) multiplies the sum, as G_w alone does in the
+#   weight-only product: y = alpha * sum_k (E2M1(cx) S_x)(E2M1(cw) S_w),
+#   the sum exact (float64 here).
+
+# Positive finite E4M3FN magnitudes, increasing (bytes 0x00..0x7E).
+_E4M3_MAGS = E4M3FN_TABLE[:0x7F].astype(np.float64)
+
+
+def e4m3fn_nearest_even(v):
+    """E4M3FN bytes of non-negative float64 values: nearest magnitude, ties to
+    the even byte, saturating at 448 (+Inf included).  Vectorized form of
+    ``e4m3fn_encode`` for non-negative inputs (the two are checked against
+    each other)."""
+    mag = np.asarray(v, dtype=np.float64)
+    lo = np.clip(np.searchsorted(_E4M3_MAGS, mag, side="right") - 1, 0, 0x7E)
+    hi = np.minimum(lo + 1, 0x7E)
+    d_lo = mag - _E4M3_MAGS[lo]
+    d_hi = _E4M3_MAGS[hi] - mag
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    return np.where(take_hi, hi, lo).astype(np.uint8)
+
+
+def quantize_act_nvfp4(x, input_scale):
+    """NVFP4 quantization of activation rows with a per-tensor scale.
+
+    x: float32 [M, K] holding bf16 values, K a multiple of 16; input_scale:
+    the float32 G_x.  Returns (codes uint8 [M, K], one E2M1 code per element;
+    scales uint8 [M, K/16], E4M3FN bytes), block by block as the readings
+    above state.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    gx = np.float32(input_scale)
+    m, k = x.shape
+    if k % 16:
+        raise ValueError("K must be a multiple of 16")
+    codes = np.zeros((m, k), dtype=np.uint8)
+    scales = np.zeros((m, k // 16), dtype=np.uint8)
+    sign = (np.signbit(x).astype(np.uint8) << 3)
+    with np.errstate(over="ignore", under="ignore", divide="ignore", invalid="ignore"):
+        for b in range(k // 16):
+            blk = x[:, 16 * b:16 * b + 16]
+            finite = np.all(np.isfinite(blk), axis=1)
+            amax = np.max(np.abs(np.where(np.isfinite(blk), blk, np.float32(0))), axis=1).astype(np.float32)
+            s = ((amax / np.float32(6)).astype(np.float32) / gx).astype(np.float32)
+            sb = e4m3fn_nearest_even(s.astype(np.float64))
+            q = (E4M3FN_TABLE[sb] * gx).astype(np.float32)
+            r = (blk / q[:, None]).astype(np.float32)
+            c = e2m1_nearest_even(np.where((q > 0)[:, None], r, np.float32(0)).astype(np.float64)) & 0x7
+            c = np.where((finite & (q > 0))[:, None], c, 0).astype(np.uint8)
+            codes[:, 16 * b:16 * b + 16] = c | sign[:, 16 * b:16 * b + 16]
+            scales[:, b] = np.where(finite, sb, 0x7F)
+    return codes, scales
+
+
+def dequantize_act_nvfp4(codes, scales):
+    """float64 [M, K]: E2M1(code) * S, S the E4M3FN block scale (NaN for byte 0x7F / 0xFF), no G_x."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    sv = E4M3FN_TABLE[np.asarray(scales, dtype=np.uint8)].astype(np.float64)
+    return E2M1_TABLE[codes].astype(np.float64) * np.repeat(sv, 16, axis=1)
+
+
+def w4a4_nvfp4_linear(x, packed, scales, k, global_scale, input_scale):
+    """W4A4 NVFP4 product: alpha * (Q(x) @ w.T) in float64, Q = ``quantize_act_nvfp4``
+    without G_x, w the NVFP4 weight [N, K] without G_w, alpha = fl32(G_x * G_w)."""
+    xc, xs = quantize_act_nvfp4(x, input_scale)
+    xq = dequantize_act_nvfp4(xc, xs)
+    w = dequantize(packed, scales, k, FMT_NVFP4, 1.0).astype(np.float64)
+    alpha = float(np.float32(np.float32(input_scale) * np.float32(global_scale)))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return (xq @ w.T) * alpha
