@@ -11,7 +11,8 @@ synthetic activations, with the prepared weights already resident in HBM.
 The default run (--workload suite) times every config of the metric in turn:
 the MXFP4 fused gate_up (the headline: value, ms_per_step, roofline and
 cpu_baseline are its own) at m = 1, 2, 4, 8, then the NVFP4 lm_head, down_proj
-and o_proj at m = 1, 2, 4, 8 and the NVFP4 and MXFP4 prefill GEMM at m = 1024.
+and o_proj at m = 1, 2, 4, 8, the NVFP4 and MXFP4 prefill GEMM at m = 1024,
+and the two opt-in W4A4 variants at the prefill shape, m = 1024.
 Every config's rate, fraction of its roofline peak and time per call per m
 also go out as flat scalar keys, e.g. "lm_head_m8_gbs", "lm_head_m8_frac",
 "lm_head_m8_us", "prefill_nvfp4_m1024_tflops".
@@ -43,6 +44,10 @@ Workloads (synthetic weights and activations at the pages' shapes):
   w4a4_gate_up   W4A4 variant (MXFP4 activations quantized per call x MXFP4
                  weights, block-scaled MFMA), the gate_up shape at m=1024
   w4a4_prefill   W4A4 variant, k=5120, n=17408, m=1024
+  w4a4_nvfp4_prefill  NVFP4 W4A4 variant (activations quantized to NVFP4 with
+                 the batch's calibrated per-tensor scale amax / (6 * 448),
+                 contracted as exact bf16 by the W4A16 kernels), the NVFP4
+                 prefill weight, m=1024
   tiny           NVFP4, k=256, n=512
 
 Algorithmic bytes per call: packed codes (n*k/2) + scale bytes (n*k/g)
@@ -97,12 +102,18 @@ WORKLOADS = {
     "prefill_mxfp4": (4, 1, 17408, 5120, 1, 1024),
     "w4a4_gate_up": (1, 1, 12288, 4096, 2, 1024),
     "w4a4_prefill": (4, 1, 17408, 5120, 1, 1024),
+    "w4a4_nvfp4_prefill": (4, 0, 17408, 5120, 1, 1024),
     "tiny": (0, 0, 512, 256, 1, 1),
 }
 TENSOR = {"o_proj": 1, "prefill_mxfp4": 1, "w4a4_prefill": 1}
 # Workloads that run the W4A4 variant (activation quantizer + block-scaled MFMA GEMM).
 W4A4 = {"w4a4_gate_up", "w4a4_prefill"}
 W4A4_METRIC = "W4A4 MXFP4 linear TFLOP/s at M=1024 (opt-in variant: activations quantized to MXFP4)"
+# Workloads that run the NVFP4 W4A4 variant (per-tensor input scale, activations
+# quantized to NVFP4 and contracted by the W4A16 kernels as exact bf16 values).
+W4A4_NV = {"w4a4_nvfp4_prefill"}
+W4A4_NV_METRIC = ("W4A4 NVFP4 linear TFLOP/s at M=1024 (opt-in variant: activations quantized to NVFP4 with a "
+                  "per-tensor input scale)")
 FP4_MFMA_PEAK_TFLOPS = 10100.0
 # Workloads that run the greedy-argmax entry point (no logits written).
 ARGMAX = {"lm_head_argmax"}
@@ -194,6 +205,10 @@ def cpu_baseline(name, xbs, host, budget_s):
             if name in W4A4:
                 oracle.w4a4_linear(x, packed[sl], scales[sl], k)
                 continue
+            if name in W4A4_NV:
+                oracle.w4a4_nvfp4_linear(x, packed[sl], scales[sl], k, g,
+                                         np.float32(np.float32(np.max(np.abs(x))) / np.float32(6 * 448)))
+                continue
             y = oracle.linear(x, packed[sl], scales[sl], k, fmt, g)
             if name in ARGMAX:
                 oracle.greedy_argmax(y)
@@ -215,7 +230,7 @@ def cpu_baseline(name, xbs, host, budget_s):
         one_step(sl)
     dt = (time.perf_counter() - t0) / reps
     frac = sl.stop / (n * proj) * (2 if name in SWIGLU else 1)  # SwiGLU: the slice of both projections
-    if name.startswith("prefill") or name in W4A4:
+    if name.startswith("prefill") or name in W4A4 or name in W4A4_NV:
         value = sum(2.0 * m * sl.stop * k for m, _ in xs) / dt / 1e12
         unit = "TFLOP/s"
     else:
@@ -253,7 +268,9 @@ def cpu_baseline(name, xbs, host, budget_s):
             "sample": "%s over weight rows [0, %d) of %d, one call per "
                       "m in %s, %d timed repetitions; value scaled by the row fraction"
                       % ("oracle.w4a4_linear (activation quantization + dequant + float64 matmul)" if name in W4A4
-                         else "oracle.linear (dequant + float64 matmul)", sl.stop, n * proj, [m for m, _ in xs],
+                         else "oracle.w4a4_nvfp4_linear (activation quantization + dequant + float64 matmul)"
+                         if name in W4A4_NV else "oracle.linear (dequant + float64 matmul)", sl.stop, n * proj,
+                         [m for m, _ in xs],
                          reps),
             "host_cpus": cores, "single_thread": single}
 
@@ -473,6 +490,8 @@ def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
         y = torch.empty((m, n if name in SWIGLU else nout), dtype=torch.bfloat16, device=dev)
         if name in W4A4:
             ws_bytes = fp4.fp4_w4a4_workspace_bytes(m, n, k, proj)
+        elif name in W4A4_NV:
+            ws_bytes = fp4.fp4_w4a4_nvfp4_workspace_bytes(m, n, k, proj)
         elif name in SWIGLU:
             ws_bytes = fp4.fp4_swiglu_workspace_bytes(m, n, k, fmt)
         elif name in ARGMAX:
@@ -480,7 +499,10 @@ def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
         else:
             ws_bytes = fp4.fp4_workspace_bytes(m, n, k, fmt, proj)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-        per_m.append({"m": m, "x": x, "xb": xb, "y": y, "ws": ws, "info": fp4.fp4_dispatch_info(),
+        # NVFP4 W4A4: the per-tensor input scale a calibration over this batch gives, amax / (6 * 448).
+        amax = float(np.max(np.abs((xb.astype(np.uint32) << 16).view(np.float32))))
+        gx = float(np.float32(np.float32(amax) / np.float32(6 * 448)))
+        per_m.append({"m": m, "x": x, "xb": xb, "y": y, "ws": ws, "info": fp4.fp4_dispatch_info(), "gx": gx,
                       "idx": torch.empty(m, dtype=torch.int32, device=dev),
                       "val": torch.empty(m, dtype=torch.bfloat16, device=dev)})
 
@@ -491,6 +513,8 @@ def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
                 fp4.fp4_w4a4_gate_up(d["x"], c, s, n, y=d["y"], workspace=d["ws"], info=d["info"])
             else:
                 fp4.fp4_w4a4_linear(d["x"], c, s, n, y=d["y"], workspace=d["ws"], info=d["info"])
+        elif name in W4A4_NV:
+            fp4.fp4_w4a4_nvfp4_linear(d["x"], c, s, n, gs[0], d["gx"], y=d["y"], workspace=d["ws"], info=d["info"])
         elif name in SWIGLU:
             fp4.fp4_w4a16_gate_up_swiglu(d["x"], c, s, n, gs[0], gs[1], fmt, y=d["y"], workspace=d["ws"],
                                          info=d["info"])
@@ -557,6 +581,8 @@ def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
                      else "%s<%s>" % (kern, "nvfp4" if fmt == 0 else "mxfp4"))
         if name in ARGMAX:
             kname += " + argmax_reduce_kernel"
+        if name in W4A4_NV:
+            kname = "act_nvfp4_kernel + " + kname
         if name in SWIGLU:
             kname += " swiglu" if info.kernel != 1 else " + tail_reduce_kernel swiglu"
         rows.append({"m": m, "kernel": kname,
@@ -584,6 +610,18 @@ def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
                              args.launch == "graph")
             rows[j]["us_act_quant"] = round(tq * 1e3 / args.steps, 3)
             rows[j]["us_gemm_and_reduce"] = round(rows[j]["us_per_launch"] - rows[j]["us_act_quant"], 3)
+        if name in W4A4_NV:
+            # The same W4A16 call on x alone (the launches after the quantizer).
+            wsb = fp4.fp4_workspace_bytes(d["m"], n, k, fmt, 1)
+            wsl = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+
+            def w4a16_call(i, d=d, wsl=wsl):
+                c, s = weights[(args.warmup + i) % copies]
+                fp4.fp4_w4a16_linear(d["x"], c, s, n, gs[0], fmt, y=d["y"], workspace=wsl)
+
+            tw = timed_calls(torch, w4a16_call, args.steps, args.launch == "graph")
+            rows[j]["us_w4a16_call"] = round(tw * 1e3 / args.steps, 3)
+            rows[j]["us_quantizer"] = round(rows[j]["us_per_launch"] - rows[j]["us_w4a16_call"], 3)
         if proj == 2 and name not in SWIGLU and name not in W4A4:
             cb, sb = fp4.fp4_prepared_bytes(n, k, fmt)
             yg = torch.empty((d["m"], n), dtype=torch.bfloat16, device=dev)
@@ -639,7 +677,8 @@ def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
 # the metric at its own m values.  Each config's rates also go out as flat
 # scalar keys of the JSON line (see suite_keys).
 SUITE = [("gate_up", [1, 2, 4, 8]), ("lm_head", [1, 2, 4, 8]), ("down_proj", [1, 2, 4, 8]),
-         ("o_proj", [1, 2, 4, 8]), ("prefill_nvfp4", [1024]), ("prefill_mxfp4", [1024])]
+         ("o_proj", [1, 2, 4, 8]), ("prefill_nvfp4", [1024]), ("prefill_mxfp4", [1024]),
+         ("w4a4_nvfp4_prefill", [1024]), ("w4a4_prefill", [1024])]
 
 
 def suite_keys(res):
@@ -648,7 +687,7 @@ def suite_keys(res):
     peak and the time per call."""
     out = {}
     for r in res["rows"]:
-        tile = r["kernel"].startswith("gemm_kernel") or r["kernel"].startswith("act_quant")
+        tile = "gemm_kernel" in r["kernel"]
         key = "%s_m%d" % (res["name"], r["m"])
         if tile:
             peak = FP4_MFMA_PEAK_TFLOPS if res["name"] in W4A4 else BF16_MFMA_PEAK_TFLOPS
@@ -720,7 +759,8 @@ def main():
                              with_cpu=not args.no_cpu_baseline)]
     head = results[0]
     out = {
-        "metric": W4A4_METRIC if head["name"] in W4A4 else METRIC, "value": round(head["value"], 3),
+        "metric": (W4A4_METRIC if head["name"] in W4A4 else W4A4_NV_METRIC if head["name"] in W4A4_NV else METRIC),
+        "value": round(head["value"], 3),
         "unit": head["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["total_ms"] / args.steps, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

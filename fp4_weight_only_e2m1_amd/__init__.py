@@ -73,6 +73,12 @@ _SIGNATURES = {
     "fp4_w4a4_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
     "fp4_w4a4_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp, ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_w4a4_gate_up": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp, ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_quantize_act_nvfp4": (_i, [_vp, _i, _i, _f, _vp, _vp, _vp]),
+    "fp4_w4a4_nvfp4_workspace_bytes": (_i, [_i, _i, _i, _i, ctypes.POINTER(_sz)]),
+    "fp4_w4a4_nvfp4_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _f, _vp, _vp, _sz, _vp,
+                                   ctypes.POINTER(fp4_dispatch_info)]),
+    "fp4_w4a4_nvfp4_gate_up": (_i, [_vp, _i, _i, _vp, _vp, _i, _f, _f, _f, _vp, _vp, _sz, _vp,
+                                    ctypes.POINTER(fp4_dispatch_info)]),
     "fp4_dequantize": (_i, [_vp, _vp, _i, _i, _f, _i, _vp, _vp]),
     "fp4_status_string": (ctypes.c_char_p, [_i]),
 }
@@ -515,6 +521,69 @@ def fp4_w4a4_gate_up(x, prep_codes, prep_scales, n_half, fmt=FMT_MXFP4, y=None, 
         _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n_half, fmt, _ptr(y), _ptr(workspace), ws_bytes,
         _stream(stream), None if info is None else ctypes.byref(info)))
     return y
+
+
+def fp4_quantize_act_nvfp4(x, input_scale, codes=None, scales=None, stream=None):
+    """NVFP4 quantization of bf16 x [m, k] with the per-tensor input_scale, as the NVFP4 W4A4 variant
+    does it; returns (codes uint8 [m, k/2], scales uint8 [m, k/16])."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m, k]")
+    m, k = x.shape
+    if codes is None:
+        codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    if codes.numel() < m * (k // 2) or scales.numel() < m * (k // 16):
+        raise ValueError("codes / scales smaller than [m, k/2] / [m, k/16]")
+    _check("fp4_quantize_act_nvfp4", load_library().fp4_quantize_act_nvfp4(
+        _ptr(x), m, k, float(input_scale), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def fp4_w4a4_nvfp4_workspace_bytes(m, n, k, projections=1):
+    out = _sz()
+    _check("fp4_w4a4_nvfp4_workspace_bytes", load_library().fp4_w4a4_nvfp4_workspace_bytes(
+        m, n, k, projections, ctypes.byref(out)))
+    return out.value
+
+
+def fp4_w4a4_nvfp4_linear(x, prep_codes, prep_scales, n, global_scale, input_scale, y=None, workspace=None,
+                          stream=None, info=None):
+    """NVFP4 W4A4 variant: y = alpha * (Q(x) @ w.T), alpha = input_scale * global_scale, w a prepared NVFP4 weight."""
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    k = x.shape[1]
+    cb, sb = fp4_prepared_bytes(n, k, FMT_NVFP4)
+    if prep_codes.numel() < cb or prep_scales.numel() < sb:
+        raise ValueError("prepared buffers smaller than fp4_prepared_bytes(n, k, FMT_NVFP4)")
+    m, y, workspace, ws_bytes = _linear_common(x, n, workspace, fp4_w4a4_nvfp4_workspace_bytes(x.shape[0], n, k, 1),
+                                               y)
+    _check("fp4_w4a4_nvfp4_linear", load_library().fp4_w4a4_nvfp4_linear(
+        _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n, float(global_scale), float(input_scale), _ptr(y),
+        _ptr(workspace), ws_bytes, _stream(stream), None if info is None else ctypes.byref(info)))
+    return y
+
+
+def fp4_w4a4_nvfp4_gate_up(x, prep_codes, prep_scales, n_half, gate_global_scale, up_global_scale, input_scale,
+                           y=None, workspace=None, stream=None, info=None):
+    """NVFP4 W4A4 fused gate_up: returns bf16 [m, 2*n_half] = [alpha_g Q(x) @ gate.T | alpha_u Q(x) @ up.T]."""
+    _need(prep_codes, torch.uint8, "prep_codes")
+    _need(prep_scales, torch.uint8, "prep_scales")
+    k = x.shape[1]
+    cb, sb = fp4_prepared_bytes(n_half, k, FMT_NVFP4)
+    if prep_codes.numel() < 2 * cb or prep_scales.numel() < 2 * sb:
+        raise ValueError("prepared buffers smaller than twice fp4_prepared_bytes(n_half, k, FMT_NVFP4)")
+    m, y, workspace, ws_bytes = _linear_common(
+        x, 2 * n_half, workspace, fp4_w4a4_nvfp4_workspace_bytes(x.shape[0], n_half, k, 2), y)
+    _check("fp4_w4a4_nvfp4_gate_up", load_library().fp4_w4a4_nvfp4_gate_up(
+        _ptr(x), m, k, _ptr(prep_codes), _ptr(prep_scales), n_half, float(gate_global_scale),
+        float(up_global_scale), float(input_scale), _ptr(y), _ptr(workspace), ws_bytes, _stream(stream),
+        None if info is None else ctypes.byref(info)))
+    return y
+
 
 def fp4_dequantize(prep_codes, prep_scales, n, k, global_scale, fmt, out=None, stream=None):
     """Dequantize a prepared weight to float32 [n, k] with the kernels' decoders."""

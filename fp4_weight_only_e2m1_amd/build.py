@@ -15,12 +15,16 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4w4a16.so")
-SOURCES = ["api.cpp", "prepare.hip", "gemv.hip", "decode_mfma.hip", "mfma_gemm.hip", "argmax.hip", "w4a4.hip"]
+SOURCES = ["api.cpp", "prepare.hip", "gemv.hip", "decode_mfma.hip", "mfma_gemm.hip", "argmax.hip", "w4a4.hip",
+           "act_nvfp4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed FP32 VALU ops.
+# -fhip-fp32-correctly-rounded-divide-sqrt: float32 division is the IEEE
+# correctly rounded one (the activation quantizers decide codes on quotients).
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall", "-Werror",
+         "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]
 

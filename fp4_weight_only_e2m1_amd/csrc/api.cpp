@@ -14,6 +14,7 @@
 #include "../../include/fp4w4a16.h"
 
 #include <atomic>
+#include <cmath>
 #include <mutex>
 
 #include "fp4_common.hpp"
@@ -292,6 +293,46 @@ int run_w4a4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_
   if (info) *info = fp4_dispatch_info{4, a.plan.mhalf ? 1 : a.plan.splits, static_cast<int>(grid.x),
                                       static_cast<int>(grid.y), static_cast<int>(block.x), xcds};
   return FP4_OK;
+}
+
+// Workspace of an NVFP4 W4A4 call: the quantized activations as bf16 [m][k]
+// (256-byte aligned), then the W4A16 call's own workspace.
+size_t w4a4_nvfp4_workspace_for(int m, int n_proj, int k, int projections, size_t* linear_offset) {
+  const size_t xhat = m < 1 ? 0 : static_cast<size_t>(fp4::round_up(int64_t{2} * m * k, 256));
+  if (linear_offset) *linear_offset = xhat;
+  return xhat + workspace_for(m, n_proj, k, FP4_FMT_NVFP4, projections);
+}
+
+// A per-tensor activation scale the quantizer can divide by: finite, > 0.
+bool valid_input_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+// Shared body of fp4_w4a4_nvfp4_linear and fp4_w4a4_nvfp4_gate_up: quantize
+// x into the workspace, then the W4A16 call on it with alpha = G_x * G_w.
+int run_w4a4_nvfp4(const uint16_t* x, int m, int k, const uint8_t* codes, const uint8_t* scales, int n_proj,
+                   int projections, const float* gw, float input_scale, uint16_t* y, void* ws, size_t ws_bytes,
+                   hipStream_t stream, fp4_dispatch_info* info) {
+  int st = check_nk(n_proj, k);
+  if (st) return st;
+  if ((st = check_m(m))) return st;
+  if (static_cast<int64_t>(n_proj) * projections > FP4_MAX_N) return FP4_EINVAL;
+  if (!valid_input_scale(input_scale)) return FP4_EINVAL;
+  if (m == 0) {
+    if (info) *info = fp4_dispatch_info{0, 0, 0, 0, 0, 0};
+    return FP4_OK;
+  }
+  if (!x || !codes || !scales || !y || !ws) return FP4_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y) || !aligned16(ws)) return FP4_EALIGN;
+  size_t off = 0;
+  if (ws_bytes < w4a4_nvfp4_workspace_for(m, n_proj, k, projections, &off)) return FP4_EWORKSPACE;
+  // Every check of the W4A16 call below has passed above (its workspace
+  // starts 256-byte aligned at `off`), so only a runtime error can stop it
+  // after the quantizer is enqueued.
+  uint16_t* xhat = static_cast<uint16_t*>(ws);
+  if (fp4::launch_act_nvfp4(x, m, k, input_scale, xhat, nullptr, nullptr, stream) != hipSuccess) return FP4_EHIP;
+  float alpha[2] = {1.0f, 1.0f};
+  for (int p = 0; p < projections; ++p) alpha[p] = input_scale * gw[p];  // one float32 product
+  return run_linear(xhat, m, k, codes, scales, n_proj, projections, alpha, FP4_FMT_NVFP4, y,
+                    static_cast<char*>(ws) + off, ws_bytes - off, stream, info);
 }
 
 }  // namespace
@@ -693,6 +734,44 @@ int fp4_w4a4_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_co
                      size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out) {
   return run_w4a4(x_dev, m, k, prep_codes_dev, prep_scales_dev, n_half, 2, fmt, y_dev, workspace_dev, workspace_bytes,
                   stream, info_out);
+}
+
+int fp4_quantize_act_nvfp4(const uint16_t* x_dev, int m, int k, float input_scale, uint8_t* codes_dev,
+                           uint8_t* scales_dev, hipStream_t stream) {
+  if (m < 0 || m > FP4_MAX_M || k < 32 || k > FP4_MAX_K || k % 32 != 0) return FP4_EINVAL;
+  if (!valid_input_scale(input_scale)) return FP4_EINVAL;
+  if (m == 0) return FP4_OK;
+  if (!x_dev || !codes_dev || !scales_dev) return FP4_EINVAL;
+  if (!aligned16(x_dev) || !aligned16(codes_dev) || !aligned16(scales_dev)) return FP4_EALIGN;
+  return to_status(fp4::launch_act_nvfp4(x_dev, m, k, input_scale, nullptr, codes_dev, scales_dev, stream));
+}
+
+int fp4_w4a4_nvfp4_workspace_bytes(int m, int n, int k, int projections, size_t* bytes_out) {
+  int st = check_nk(n, k);
+  if (st) return st;
+  if ((st = check_m(m))) return st;
+  if (projections != 1 && projections != 2) return FP4_EINVAL;
+  if (static_cast<int64_t>(n) * projections > FP4_MAX_N || !bytes_out) return FP4_EINVAL;
+  *bytes_out = w4a4_nvfp4_workspace_for(m, n, k, projections, nullptr);
+  return FP4_OK;
+}
+
+int fp4_w4a4_nvfp4_linear(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                          const uint8_t* prep_scales_dev, int n, float global_scale, float input_scale,
+                          uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
+                          fp4_dispatch_info* info_out) {
+  const float g[1] = {global_scale};
+  return run_w4a4_nvfp4(x_dev, m, k, prep_codes_dev, prep_scales_dev, n, 1, g, input_scale, y_dev, workspace_dev,
+                        workspace_bytes, stream, info_out);
+}
+
+int fp4_w4a4_nvfp4_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                           const uint8_t* prep_scales_dev, int n_half, float gate_global_scale,
+                           float up_global_scale, float input_scale, uint16_t* y_dev, void* workspace_dev,
+                           size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out) {
+  const float g[2] = {gate_global_scale, up_global_scale};
+  return run_w4a4_nvfp4(x_dev, m, k, prep_codes_dev, prep_scales_dev, n_half, 2, g, input_scale, y_dev,
+                        workspace_dev, workspace_bytes, stream, info_out);
 }
 
 int fp4_dequantize(const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev, int n, int k, float global_scale,

@@ -346,6 +346,11 @@ hipError_t launch_tail_reduce(const MfmaArgs& a, int bm, hipStream_t stream);
 hipError_t launch_act_quant_mxfp4(const uint16_t* x, int m, int k, uint8_t* codes, uint8_t* scales,
                                   hipStream_t stream);
 hipError_t launch_w4a4(const MfmaArgs& a, hipStream_t stream, dim3* grid, dim3* block);
+// NVFP4 activation quantizer with per-tensor scale gx: xhat non-null writes
+// the quantized activations as bf16 [m][k] (E2M1(code) * S, no gx); else
+// codes [m][k/2] (two per byte, low nibble first) and E4M3FN scales [m][k/16].
+hipError_t launch_act_nvfp4(const uint16_t* x, int m, int k, float gx, uint16_t* xhat, uint8_t* codes,
+                            uint8_t* scales, hipStream_t stream);
 hipError_t launch_argmax_reduce(const uint64_t* keys, int tiles, int m, int32_t* idx, uint16_t* val,
                                 hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n, int k, int fmt,

@@ -442,6 +442,70 @@ int fp4_w4a4_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_co
                      size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out);
 
 /*
+ * NVFP4 W4A4 variant (ModelOpt's): an NVFP4 checkpoint's per-tensor
+ * activation scale input_scale (G_x) sets alpha = G_x * G_w and routes the
+ * layer to a GEMM over 4-bit activations; the pages keep that arm behind an
+ * opt-in switch ("keep the ModelOpt NVFP4 lm_head packed", vllm.cpp PR #263,
+ * section "Round-1 findings resolved", item 1; "re-verify 27B NVFP4 on the
+ * nvidia ModelOpt checkpoint", vllm.cpp PR #178, section "W4A16 is the
+ * default for ModelOpt").  Separate, opt-in entry points; the weight-only
+ * path never calls them.
+ *
+ * Activation quantizer Q (the weights' two-level NVFP4 rule with G_x; the
+ * pages name the scale, not the rule): per row and block of 16 k,
+ *   s = fl32(fl32(amax / 6) / G_x), S = E4M3FN(s) nearest-even saturating at
+ *   448, q = fl32(S * G_x), code = E2M1(fl32(x / q)) nearest-even saturating
+ *   at 6 with the sign of x (code 0 where q == 0); a block holding an Inf or
+ *   NaN gets scale byte 0x7F and codes 0.  Correctly rounded float32 steps.
+ *
+ * fp4_quantize_act_nvfp4 writes Q(x) as codes_dev uint8 [m][k/2] (two codes
+ * per byte, low nibble first) and scales_dev uint8 [m][k/16] (E4M3FN bytes,
+ * row-major); it is the quantizer the products run, exposed so its output can
+ * be checked.  input_scale must be finite and > 0 (else FP4_EINVAL); k % 32 == 0.
+ */
+int fp4_quantize_act_nvfp4(const uint16_t* x_dev, int m, int k, float input_scale, uint8_t* codes_dev,
+                           uint8_t* scales_dev, hipStream_t stream);
+
+/*
+ * Workspace of fp4_w4a4_nvfp4_linear (projections 1) / fp4_w4a4_nvfp4_gate_up
+ * (projections 2, n = n_half): the quantized activations as bf16 [m][k]
+ * (rounded up to 256 bytes), then the W4A16 call's workspace
+ * (fp4_workspace_bytes with FP4_FMT_NVFP4).  Never needs zeroing.  Pure host
+ * function.
+ */
+int fp4_w4a4_nvfp4_workspace_bytes(int m, int n, int k, int projections, size_t* bytes_out);
+
+/*
+ * y = alpha * (Q(x) w^T), alpha = fl32(input_scale * global_scale), with Q
+ * as above (without G_x) and w the NVFP4 weight prepared by fp4_prepare
+ * (without G_w).  x_dev bf16 [m][k]; y_dev bf16 [m][n] rounded to nearest even
+ * from the float32 results.
+ * gfx950's block-scaled MFMA takes E8M0 scales per 32 elements only, not
+ * NVFP4's E4M3 scales per 16, so Q(x) is written to the workspace as bf16
+ * E2M1(code) * S -- exact -- and the W4A16 kernels (the kernel m selects,
+ * reported in info_out) contract it with the weight and apply alpha after the
+ * sum: the same products and float32 accumulation as a GEMM over the 4-bit
+ * operands.  Two or more launches (quantizer, then the W4A16 call).
+ * Errors as fp4_w4a16_linear, plus FP4_EINVAL for an input_scale that is not
+ * finite and > 0; the weight is NVFP4 (no format argument).
+ */
+int fp4_w4a4_nvfp4_linear(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                          const uint8_t* prep_scales_dev, int n, float global_scale, float input_scale,
+                          uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
+                          fp4_dispatch_info* info_out);
+
+/*
+ * Fused gate_up of the NVFP4 W4A4 variant over the prepared [gate; up] NVFP4
+ * weight (fp4_prepare_gate_up): y = [alpha_g Q(x) gate^T | alpha_u Q(x) up^T],
+ * bf16 [m][2 n_half], alpha_g = fl32(input_scale * gate_global_scale),
+ * alpha_u likewise.  Workspace: fp4_w4a4_nvfp4_workspace_bytes(m, n_half, k, 2).
+ */
+int fp4_w4a4_nvfp4_gate_up(const uint16_t* x_dev, int m, int k, const uint8_t* prep_codes_dev,
+                           const uint8_t* prep_scales_dev, int n_half, float gate_global_scale,
+                           float up_global_scale, float input_scale, uint16_t* y_dev, void* workspace_dev,
+                           size_t workspace_bytes, hipStream_t stream, fp4_dispatch_info* info_out);
+
+/*
  * Dequantize a prepared weight to float32 out_dev [n][k]:
  * out = fl32(fl32(E2M1 * S) * G), G = 1 for MXFP4.  It decodes with the
  * instruction sequences of the compute kernels' weight decode (NVFP4: E2M1 to

@@ -377,3 +377,31 @@ def test_moe_prefill_swiglu_argument_checks(lib):
     # Two projections of n_half rows must fit the row limit.
     assert _moe_swiglu(lib, n_half=(1 << 23) + 1) == ST["EINVAL"]
     assert _moe_swiglu(lib, pairs=0, x=None, y=None) == ST["OK"]
+
+
+def test_w4a4_nvfp4_sizes_and_argument_checks(lib):
+    # Workspace: the bf16 quantized activations (256-byte aligned), then the
+    # W4A16 call's own workspace.
+    for m, n, k, proj in [(1, 5120, 17408, 1), (8, 5120, 17408, 1), (1024, 17408, 5120, 1), (3, 12288, 4096, 2)]:
+        want = -(-2 * m * k // 256) * 256 + fp4.fp4_workspace_bytes(m, n, k, NV, proj)
+        assert fp4.fp4_w4a4_nvfp4_workspace_bytes(m, n, k, proj) == want
+    assert fp4.fp4_w4a4_nvfp4_workspace_bytes(0, 512, 256) == 0
+    info = fp4.fp4_dispatch_info()
+
+    def lin(m=4, k=256, n=512, gx=0.01, ws=FAKE, ws_bytes=1 << 30, x=FAKE, y=FAKE):
+        return lib.fp4_w4a4_nvfp4_linear(x, m, k, FAKE, FAKE, n, 1.0, gx, y, ws, ws_bytes, None, ctypes.byref(info))
+
+    for gx in (0.0, -1.0, float("inf"), float("nan")):
+        assert lin(gx=gx) == ST["EINVAL"]
+        assert lib.fp4_quantize_act_nvfp4(FAKE, 4, 256, ctypes.c_float(gx), FAKE, FAKE, None) == ST["EINVAL"]
+    assert lin(k=48) == ST["EINVAL"]
+    assert lin(m=-1) == ST["EINVAL"]
+    assert lin(ws=None) == ST["EINVAL"]
+    assert lin(x=FAKE + 8) == ST["EALIGN"]
+    assert lin(ws_bytes=2 * 4 * 256 - 1) == ST["EWORKSPACE"]
+    assert lin(m=0, x=None, y=None, ws=None, ws_bytes=0) == ST["OK"]
+    assert lib.fp4_quantize_act_nvfp4(FAKE, 4, 48, ctypes.c_float(1.0), FAKE, FAKE, None) == ST["EINVAL"]
+    assert lib.fp4_quantize_act_nvfp4(FAKE + 4, 4, 64, ctypes.c_float(1.0), FAKE, FAKE, None) == ST["EALIGN"]
+    assert lib.fp4_quantize_act_nvfp4(None, 0, 64, ctypes.c_float(1.0), None, None, None) == ST["OK"]
+    assert lib.fp4_w4a4_nvfp4_gate_up(FAKE, 4, 256, FAKE, FAKE, (1 << 23) + 1, 1.0, 1.0, 0.01, FAKE, FAKE, 1 << 30,
+                                      None, None) == ST["EINVAL"]

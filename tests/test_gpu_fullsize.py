@@ -2,7 +2,8 @@
 launch configuration the benchmark times.  The oracle computes a sample of
 output columns one by one (every activation row, a few hundred weight rows
 spread over n, plus both ends); fused gate_up is also checked bit for bit
-against the two separate launches at full size."""
+against the two separate launches at full size, and the SwiGLU gate_up on the
+same weights at decode and prefill row counts."""
 
 import numpy as np
 import pytest
@@ -10,7 +11,7 @@ import pytest
 import fp4_weight_only_e2m1_amd as fp4
 import oracle
 import synth
-from gpu_util import assert_close, prepared, sample_rows, weight, x_dev, y_host, y_host_bits
+from gpu_util import assert_close, prepared, sample_rows, u8, weight, x_dev, y_host, y_host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +65,27 @@ def test_gate_up_full_size(m):
     ref_u = oracle.linear_rows(x, pu, su, k, fmt, gu, rows)
     assert_close(np.concatenate([yf[:, rows], yf[:, nh + rows]], axis=1),
                  np.concatenate([ref_g, ref_u], axis=1), "gate_up m=%d" % m)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 1024])
+def test_swiglu_gate_up_full_size(m):
+    # The SwiGLU gate_up on the benchmark's 2 x 12288 x 4096 MXFP4 weights,
+    # through each kernel the benchmark times (GEMV, MFMA decode, tile GEMM):
+    # sampled output columns against the oracle on the same weight rows (each
+    # column depends only on its gate and up rows).
+    nh, k, fmt = 12288, 4096, MX
+    pg, sg, gg = weight(synth.GATE_UP, 0, nh, k, fmt)
+    pu, su, gu = weight(synth.GATE_UP, 1, nh, k, fmt)
+    pc, ps = fp4.fp4_prepare_gate_up_interleaved(u8(pg), u8(sg), u8(pu), u8(su), nh, k, fmt)
+    xbits = synth.activations(synth.GATE_UP, m, k)
+    info = fp4.fp4_dispatch_info()
+    y = y_host(fp4.fp4_w4a16_gate_up_swiglu(x_dev(xbits), pc, ps, nh, float(gg), float(gu), fmt, info=info))
+    assert info.kernel == (0 if m < 3 else 2 if m <= 16 else 1)
+    rows = sample_rows(nh, 384, seed=100 + m)
+    ref = oracle.gate_up_swiglu(oracle.bf16_bits_to_f32(xbits), pg[rows], sg[rows], pu[rows], su[rows], k, fmt,
+                                gg, gu)
+    assert np.isfinite(y).all()
+    assert_close(y[:, rows], ref, "swiglu gate_up m=%d" % m)
 
 
 @pytest.mark.parametrize("m", [1, 2, 4, 8])
