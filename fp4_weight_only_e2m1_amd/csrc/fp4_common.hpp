@@ -115,16 +115,19 @@ inline int gemv_splits(int n_proj, int k, int fmt) {
 // (8192 rows) run unsplit: the split-K finish costs a few microseconds of
 // round trips, more than the extra workgroups win there (measured on MI355X:
 // gate_up m=4 13.7 -> 12.4 us unsplit).  Smaller layers (5120 rows: 80 tiles)
-// split K so that one projection has about 512 workgroups, keeping at least 8
-// stages of 256 codes per split.  A function of (rows per projection, k)
-// only, so the summation order is the same at every m the kernel serves and
-// in the fused gate_up launch as in the separate ones.
+// split K so that one projection has about 512 workgroups, keeping at least 4
+// stages of 256 codes per split.  (Measured on MI355X for the 5120 x 6144
+// layer: 6 splits of 4 stages 8.8 to 9.9 us at m = 3..8, 3 splits of 8
+// stages 9.8 to 10.5; more than 512 workgroups or fewer than 4 stages per
+// split were slower.)  A function of (rows per projection, k) only, so the
+// summation order is the same at every m the kernel serves and in the fused
+// gate_up launch as in the separate ones.
 inline int decode_mfma_splits(int n_proj, int k) {
   const int64_t tiles = round_up(n_proj, kRowAlign) / kDecodeTileRows;
   if (tiles >= 128) return 1;
   const int ksteps = static_cast<int>((k + kDecodeStageK - 1) / kDecodeStageK);
   int s = static_cast<int>(512 / tiles);
-  if (s > ksteps / 8) s = ksteps / 8;
+  if (s > ksteps / 4) s = ksteps / 4;
   return s < 1 ? 1 : s;
 }
 

@@ -115,11 +115,11 @@ def test_workspace_bytes_policy():
     flags = 248320 // 64 * 2 * 8
     assert ws1 == 2 * 1 * 248320 * 4 + flags
     # m >= 3 runs the MFMA decode kernel: 64-row tiles, K split only for layers
-    # under 128 tiles, to about 512 workgroups (at least 8 stages of 256 codes each).
+    # under 128 tiles, to about 512 workgroups (at least 4 stages of 256 codes each).
     assert ws8 == 0                                             # 3880 tiles: no split
     down = fp4.fp4_workspace_bytes(8, 5120, 17408, NV)          # 80 tiles: 6 splits
     assert down == 6 * 8 * 5120 * 4 + 5120 // 64 * 6 * 8
-    assert fp4.fp4_workspace_bytes(5, 5120, 6144, NV) == 3 * 5 * 5120 * 4 + 80 * 3 * 8  # 24 stages: 3 splits
+    assert fp4.fp4_workspace_bytes(5, 5120, 6144, NV) == 6 * 5 * 5120 * 4 + 80 * 6 * 8  # 24 stages: 6 splits
     # gate_up: two projections, each split like the separate linear.
     one = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 1)
     two = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 2)

@@ -101,8 +101,8 @@ CASES = [
     ("decode m=16", 16, 32, [list(range(16))], 2, False),
     ("decode m=32", 32, 64, [list(range(32))], 2, False),
     ("decode m=3", 3, 32, [[c, c + 5, c + 10] for c in range(0, 16, 3)], 2, False),
-    # MFMA decode with k = 8192 on 4 tiles: four K splits; ones in every split.
-    ("decode m=8 split", 8, 8192, [[2048 * (j % 4) + 17 * j + c for j in range(8)] for c in (0, 8)], 2, True),
+    # MFMA decode with k = 8192 on 4 tiles: eight K splits; row j's one in split j.
+    ("decode m=8 split", 8, 8192, [[1024 * j + 17 * j + c for j in range(8)] for c in (0, 8)], 2, True),
     # Tile GEMM: 64 rows (2-block instances), 128 rows (4-block instances).
     ("gemm m=64", 64, 64, [list(range(64))], 1, False),
     ("gemm m=128", 128, 128, [list(range(128))], 1, False),

@@ -66,9 +66,9 @@ def assert_green_then_red(y, ref, reds, what):
 LINEAR = [
     (NV, 512, 2048, 1, 0, False),     # VALU GEMV
     (MX, 384, 8192, 2, 0, True),      # VALU GEMV, K split in two
-    (NV, 512, 2048, 8, 2, False),     # MFMA decode
+    (NV, 8192, 2048, 8, 2, False),    # MFMA decode (128 tiles: unsplit)
     (NV, 256, 17408, 4, 2, True),     # MFMA decode, K split
-    (MX, 640, 2048, 24, 2, False),    # MFMA decode, two activation groups
+    (MX, 640, 1024, 24, 2, False),    # MFMA decode, two activation groups
     (NV, 1024, 1024, 200, 1, False),  # tile GEMM
     (MX, 256, 5120, 100, 1, True),    # tile GEMM, split tail tile
 ]
