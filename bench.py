@@ -18,7 +18,11 @@ also go out as flat scalar keys, e.g. "lm_head_m8_gbs", "lm_head_m8_frac",
 "lm_head_m8_us", "prefill_nvfp4_m1024_tflops".
 Each m is timed with its own HIP events; by default the timed calls are
 replayed from a captured HIP graph so the per-call launch gaps of the host
-runtime do not count against the kernels.
+runtime do not count against the kernels.  Right before the timed region the
+same calls are replayed, untimed, for --preroll-ms (default 50 ms): the GPU's
+clock ramps up over the first milliseconds of a burst after idle, and 20
+timed prefill calls straight after idle measured 214 µs each against 175 µs
+under sustained load.
 The weights are rotated over enough device copies (>= 1 GiB in total) that
 the 256 MB Infinity Cache cannot hold them, so the bytes come from HBM.
 
@@ -275,10 +279,10 @@ def cpu_baseline(name, xbs, host, budget_s):
             "host_cpus": cores, "single_thread": single}
 
 
-def timed_calls(torch, fn, count, graph):
+def timed_calls(torch, fn, count, graph, preroll_ms=0.0):
     """Milliseconds for `count` calls fn(0..count-1) on the current stream:
-    one replay of a graph that captured them (after an untimed replay), or
-    direct launches."""
+    one replay of a graph that captured them (after an untimed replay, and
+    untimed replays for preroll_ms of wall time), or direct launches."""
     stream = torch.cuda.current_stream()
     g = None
     if graph:
@@ -287,6 +291,16 @@ def timed_calls(torch, fn, count, graph):
             for i in range(count):
                 fn(i)
         g.replay()
+    t_pre = time.perf_counter()
+    while preroll_ms > 0:
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(count):
+                fn(i)
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_pre >= preroll_ms * 1e-3:
+            break
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -382,7 +396,8 @@ def run_moe(args, torch, np, fp4, synth):
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for d in per_m:
-        d["t_ms"] = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), args.steps, args.launch == "graph")
+        d["t_ms"] = timed_calls(torch, lambda i, d=d: call(d, args.warmup + i), args.steps, args.launch == "graph",
+                                args.preroll_ms)
     t_wall = time.perf_counter() - t_wall0
     rows, total_ms, total_bytes, total_flops = [], 0.0, 0, 0.0
     for d in per_m:
@@ -542,6 +557,21 @@ def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
         for g in graphs:   # one untimed replay each
             g.replay()
         torch.cuda.synchronize()
+
+    # Untimed pre-roll right before the timed region: the same calls for at
+    # least --preroll-ms of wall time, so the timed calls run at the clock the
+    # GPU holds under sustained load rather than on its ramp up from idle.
+    t_pre = time.perf_counter()
+    while True:
+        for j, d in enumerate(per_m):
+            if graphs:
+                graphs[j].replay()
+            else:
+                for i in range(args.steps):
+                    call(d, args.warmup + i)
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_pre >= args.preroll_ms * 1e-3:
+            break
 
     stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in per_m]
@@ -712,6 +742,9 @@ def main():
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="replay the timed calls from a captured HIP graph, or launch them one by one")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--preroll-ms", type=float, default=50.0,
+                    help="untimed replays of the timed calls right before the timed region, in ms of wall time "
+                         "(the GPU clock ramps up over the first milliseconds of a burst)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-crosscheck", action="store_true",
                     help="skip the differencing and split-launch cross-checks (e.g. under a counter "
