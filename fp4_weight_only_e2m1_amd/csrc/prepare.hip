@@ -171,11 +171,19 @@ __global__ __launch_bounds__(256) void prepare_scales_il_kernel(const uint8_t* _
 
 }  // namespace
 
+// Workgroups of a one-dimensional launch of `items` threads in groups of 256,
+// or 0 when that exceeds the grid's x limit (sizes no device could hold).
+inline unsigned blocks_for(int64_t items) {
+  const int64_t b = (items + 255) / 256;
+  return b > 0x7FFFFFFF ? 0u : static_cast<unsigned>(b);
+}
+
 hipError_t launch_prepare_interleaved(const uint8_t* gate_codes, const uint8_t* gate_scales, const uint8_t* up_codes,
                                       const uint8_t* up_scales, int n, int k, int fmt, uint8_t* prep_codes,
                                       uint8_t* prep_scales, hipStream_t stream) {
   const PreparedShape s = prepared_shape(n, k, fmt);
   const int64_t code_chunks = 2 * s.n_pad * (s.k_pad / 32);
+  if (blocks_for(code_chunks) == 0 || blocks_for((2 * s.n_pad / kRowGroup) * s.ksegs) == 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(prepare_codes_il_kernel, dim3(static_cast<unsigned>((code_chunks + 255) / 256)), dim3(256), 0,
                      stream, gate_codes, up_codes, n, k, s.n_pad, s.k_pad, prep_codes);
   hipError_t e = hipGetLastError();
@@ -196,6 +204,7 @@ hipError_t launch_prepare(const uint8_t* codes, const uint8_t* scales, int n, in
                           uint8_t* prep_codes, uint8_t* prep_scales, hipStream_t stream) {
   const PreparedShape s = prepared_shape(n, k, fmt);
   const int64_t code_chunks = s.n_pad * (s.k_pad / 32);
+  if (blocks_for(code_chunks) == 0 || blocks_for((s.n_pad / kRowGroup) * s.ksegs) == 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(prepare_codes_kernel, dim3(static_cast<unsigned>((code_chunks + 255) / 256)), dim3(256), 0,
                      stream, codes, n, k, s.n_pad, s.k_pad, prep_codes);
   hipError_t e = hipGetLastError();
@@ -216,7 +225,8 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int n, in
                           float* out, hipStream_t stream) {
   const PreparedShape s = prepared_shape(n, k, fmt);
   const int64_t items = static_cast<int64_t>(n) * (k / 8);
-  const dim3 grid(static_cast<unsigned>((items + 255) / 256));
+  if (blocks_for(items) == 0) return hipErrorInvalidValue;
+  const dim3 grid(blocks_for(items));
   if (fmt == kFmtNvfp4)
     hipLaunchKernelGGL(dequant_kernel<kFmtNvfp4>, grid, dim3(256), 0, stream, codes, scales, n, k, s.k_pad,
                        s.ksegs, gscale, out);
