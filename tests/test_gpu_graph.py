@@ -128,3 +128,41 @@ def test_graph_replay_w4a4():
         assert np.array_equal(got, want), "replay %d differs from eager" % rep
         call(y_eager)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n,k,m", [(5120, 6144, 4), (512, 5120, 100)])
+def test_graph_replay_w4a4_nvfp4(n, k, m):
+    # The NVFP4 W4A4 call (quantizer into the workspace, then the W4A16 call on
+    # it: the MFMA decode with a K split, or the tile GEMM with split tail
+    # tiles and the reduce) replayed from a graph with new activations gives
+    # the eager call's bytes, on a workspace that starts poisoned.
+    packed, scales, g = synth.packed_weight(synth.TINY, 73, n, k, NV)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, NV)
+    ws = torch.full((fp4.fp4_w4a4_nvfp4_workspace_bytes(m, n, k),), 0xA5, dtype=torch.uint8, device=DEV)
+    x = x_dev(synth.activations(synth.TINY, m, k))
+    y_graph = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    y_eager = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    info = fp4.fp4_dispatch_info()
+
+    def call(y):
+        fp4.fp4_w4a4_nvfp4_linear(x, pc, ps, n, float(g), 0.004, y=y, workspace=ws, info=info)
+
+    call(y_graph)
+    torch.cuda.synchronize()
+    assert info.splits > 1, info.as_dict()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(y_graph)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(10)
+    for rep in range(4):
+        xb = rng.standard_normal((m, k), dtype=np.float32)
+        x.copy_(x_dev((xb.view(np.uint32) >> 16).astype(np.uint16)))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = y_host_bits(y_graph)
+        call(y_eager)
+        want = y_host_bits(y_eager)
+        assert np.array_equal(got, want), "replay %d differs from eager" % rep
+        call(y_eager)
+        torch.cuda.synchronize()

@@ -220,3 +220,16 @@ def test_prefill_shape_sampled(m):
     ref = oracle.w4a4_nvfp4_linear(x, packed[rows], scales[rows], k, gw, gx)
     assert np.isfinite(y).all()
     assert_close(y[:, rows], ref, "w4a4 nvfp4 prefill m=%d" % m)
+
+
+@pytest.mark.parametrize("n,k,m", [(5120, 6144, 8), (512, 5120, 100), (300, 1056, 1)])
+def test_deterministic_on_poisoned_workspace(n, k, m):
+    packed, scales, gw = _weights(n, k, 4)
+    pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, NV)
+    xd = x_dev(synth.activations(synth.TINY, m, k))
+    need = fp4.fp4_w4a4_nvfp4_workspace_bytes(m, n, k)
+    outs = []
+    for fill in (0x00, 0xFF, 0x7F, 0x5A):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        outs.append(y_host_bits(fp4.fp4_w4a4_nvfp4_linear(xd, pc, ps, n, float(gw), 0.003, workspace=ws)))
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
