@@ -602,7 +602,8 @@ def run_dense(args, name, ms, torch, np, fp4, synth, crosscheck, with_cpu):
         total_bytes += b * args.steps
         total_flops += f * args.steps
         info = d["info"]
-        kern = {0: "gemv_kernel", 2: "decode_mfma_kernel", 1: "gemm_kernel", 4: "w4a4_gemm_kernel"}[info.kernel]
+        kern = {0: "gemv_kernel", 2: "decode_mfma_kernel", 1: "gemm_kernel", 4: "w4a4_gemm_kernel",
+                6: "decode_kw_kernel"}[info.kernel]
         us = ms_m * 1e3 / args.steps
         if info.kernel == 4:
             kname = "act_quant_kernel + w4a4_gemm_kernel" + (" + tail_reduce_kernel" if info.splits > 1 else "")

@@ -42,13 +42,18 @@ int check_nk(int n, int k) {
 
 int check_m(int m) { return (m < 0 || m > FP4_MAX_M) ? FP4_EINVAL : FP4_OK; }
 
-size_t workspace_for(int m, int n_proj, int k, int fmt, int projections) {
+// Whether a decode call takes the wave-split kernel.  The SwiGLU epilogue
+// (act) stays on the 64-row kernels, whose tiles hold both rows of an output.
+bool uses_kw(int m, int n_proj, int k, bool act) { return !act && fp4::decode_kw_used(n_proj, k, m); }
+
+size_t workspace_for(int m, int n_proj, int k, int fmt, int projections, bool act = false) {
   // Both decode kernels split K across workgroups for some shapes (partials
   // + flags); the prefill GEMM splits K only for the tail tiles that do not
   // fill a round.
   if (m < 1) return 0;
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
   if (m > fp4::kDecodeMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
+  if (uses_kw(m, n_proj, k, act)) return 0;
   const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
   const int splits = on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
   const int tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(rows_total, m)
@@ -104,7 +109,7 @@ int noalloc_scratch(void** out) {
   return FP4_OK;
 }
 
-// Rows per workgroup of the decode kernel m selects (m = 1..32).
+// Rows per workgroup of the 64-row-family decode kernel m selects (m = 1..32).
 int decode_tile_rows(int m, int64_t rows_total) {
   return m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_tile_rows(rows_total, m)
                                    : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
@@ -116,11 +121,12 @@ size_t argmax_workspace_for(int m, int n, int k, int fmt, size_t* keys_offset) {
   const size_t base = fp4::round_up(static_cast<int64_t>(workspace_for(m, n, k, fmt, 1)), 256);
   const int64_t rows_total = fp4::round_up(n, fp4::kRowAlign);
   if (keys_offset) *keys_offset = base;
-  return base + static_cast<size_t>(rows_total / decode_tile_rows(m, rows_total)) * m * 8;
+  const int tile_rows = uses_kw(m, n, k, false) ? fp4::kKwRows : decode_tile_rows(m, rows_total);
+  return base + static_cast<size_t>(rows_total / tile_rows) * m * 8;
 }
 
 size_t act_workspace_for(int m, int n_half, int k, int fmt) {
-  if (m <= fp4::kDecodeActMaxM) return workspace_for(m, n_half, k, fmt, 2);
+  if (m <= fp4::kDecodeActMaxM) return workspace_for(m, n_half, k, fmt, 2, true);
   const int64_t rows_total = 2 * fp4::round_up(n_half, fp4::kRowAlign);
   return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
 }
@@ -173,9 +179,10 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.k_pad = ps.k_pad;
     a.kgroups = ps.kgroups;
     a.ksegs = ps.ksegs;
-    const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
+    const bool kw = uses_kw(m, n_proj, k, act != 0);
+    const bool on_mfma = m >= fp4::kDecodeMfmaMinM || kw;
     a.nslab = static_cast<int>(ps.k_pad / fp4::kSlabK);
-    a.splits = on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
+    a.splits = kw ? 1 : on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
     a.n_proj = n_proj;
     a.n_proj_pad = ps.n_pad;
     a.projections = projections;
@@ -184,22 +191,23 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
     a.act = act;
-    a.tile_rows = decode_tile_rows(m, a.rows_total);
-    if (on_mfma && a.tile_rows != fp4::kDecodeTileRows && a.splits != 1) return FP4_EINVAL;
+    a.tile_rows = kw ? fp4::kKwRows : decode_tile_rows(m, a.rows_total);
+    if (on_mfma && !kw && a.tile_rows != fp4::kDecodeTileRows && a.splits != 1) return FP4_EINVAL;
     if (a.splits > 1) {
       a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
                                             static_cast<int64_t>(a.splits) * m * a.rows_total * 4);
       a.token = next_token();
     }
     if (argmax) a.keys = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + keys_offset);
-    hipError_t e = on_mfma ? fp4::launch_decode_mfma(a, fmt, stream, &grid, &block)
-                           : fp4::launch_gemv(a, fmt, stream, &grid, &block);
+    hipError_t e = kw        ? fp4::launch_decode_kw(a, fmt, stream, &grid, &block)
+                   : on_mfma ? fp4::launch_decode_mfma(a, fmt, stream, &grid, &block)
+                             : fp4::launch_gemv(a, fmt, stream, &grid, &block);
     if (e != hipSuccess) return FP4_EHIP;
     if (argmax) {
       e = fp4::launch_argmax_reduce(a.keys, static_cast<int>(grid.x), m, idx, val, stream);
       if (e != hipSuccess) return FP4_EHIP;
     }
-    if (info) *info = fp4_dispatch_info{on_mfma ? 2 : 0, a.splits, static_cast<int>(grid.x),
+    if (info) *info = fp4_dispatch_info{kw ? 6 : on_mfma ? 2 : 0, a.splits, static_cast<int>(grid.x),
                                         static_cast<int>(grid.y), static_cast<int>(block.x), 0};
   } else {
     int xcds = 0;
@@ -504,6 +512,10 @@ int fp4_plan(int m, int n, int k, int fmt, int projections, int cus, fp4_dispatc
   const int64_t rows_total = projections * fp4::round_up(n, fp4::kRowAlign);
   if (m <= fp4::kDecodeMaxM) {
     // The decode kernels: grid (row tiles, K splits), as run_linear launches them.
+    if (uses_kw(m, n, k, false)) {
+      *info_out = fp4_dispatch_info{6, 1, static_cast<int>(rows_total / fp4::kKwRows), 1, fp4::kDecodeThreads, 0};
+      return FP4_OK;
+    }
     const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
     const int splits = on_mfma ? fp4::decode_mfma_splits(n, k) : fp4::gemv_splits(n, k, fmt);
     *info_out = fp4_dispatch_info{on_mfma ? 2 : 0, splits, static_cast<int>(rows_total / decode_tile_rows(m, rows_total)),

@@ -220,9 +220,13 @@ struct alignas(256) ZeroRow {
 // One stage for this wave: 2 blocks of 128 codes x 4 MFMA steps for each of
 // its RB row blocks and J activation groups; each x fragment read from LDS
 // feeds RB MFMAs, each decoded weight fragment J.  zrow: the zero row the
-// lanes of rows >= m read instead of x.
-template <int M, int FMT, int RB>
-__device__ __forceinline__ void compute_stage(const Stage<RB, FMT, kXRows<M>>& sb, const uint4* zrow, int wave, int r, int g,
+// lanes of rows >= m read instead of x.  XW > 0 (the wave-split kernel, whose
+// stages hold XW x rows and no zero row): the lanes of activation row r read
+// staged row r mod XW instead; rows past m then hold other rows' or stale
+// values, which only reach outputs of rows past m (row r of the product
+// depends on row r of x alone), and those are never stored.
+template <int M, int FMT, int RB, typename StageT, int XW = 0>
+__device__ __forceinline__ void compute_stage(const StageT& sb, const uint4* zrow, int wave, int r, int g,
                                               int mrows, f32x4_t (&acc)[RB][kGroups<M>]) {
   constexpr int J = kGroups<M>;
   constexpr int P = scales_per_seg(FMT);
@@ -251,7 +255,11 @@ __device__ __forceinline__ void compute_stage(const Stage<RB, FMT, kXRows<M>>& s
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int xr = 16 * j + r;
-        const uint4 xv = xr < mrows ? sb.x[x_slot(xr, ch)] : zrow[ch];
+        uint4 xv;
+        if constexpr (XW > 0)
+          xv = sb.x[x_slot(xr & (XW - 1), ch)];
+        else
+          xv = xr < mrows ? sb.x[x_slot(xr, ch)] : zrow[ch];
         af[j].u[0] = xv.x;
         af[j].u[1] = xv.y;
         af[j].u[2] = xv.z;
@@ -426,6 +434,219 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a)
   decode_tile<M, FMT, RB, NB>(a, blockIdx.x, blockIdx.y, M);
 }
 
+// ---------------------------------------------------------------------------
+// Wave-split decode: K split over the waves of one workgroup, for the layers
+// decode_kw_used selects (too few rows to fill the chip with whole-K tiles,
+// m <= kKwMaxM).
+//
+// A workgroup owns 16 rows.  Wave w streams stages [w S / 4, (w + 1) S / 4)
+// of the S = ceil(k / 256) stages through NB stage buffers of its own --
+//   codes   16 rows x 128 bytes   (2 KiB: one full 128-byte line per row)
+//   x       XR rows x 256 bf16    (XR = 2, 4, 8 for m <= 2, 4, 8)
+//   scales  16 rows x 8 segments x P bytes (256 B NVFP4, 128 B MXFP4)
+// -- and waits only for its own copies: no workgroup barrier in the loop.
+// The lanes, fragments and MFMAs of a stage are those of the 64-row kernel
+// for one row block.  At the end the four waves' sums of each output are
+// added in LDS in wave order, so an output's summation order is: its wave's
+// stages in order (MFMA accumulation), then the waves 0, 1, 2, 3 in order.
+// That order depends on k alone: the same at every m this kernel serves and
+// in the fused gate_up launch as in the separate ones.  No partials leave
+// the workgroup, so the call needs no workspace and no cross-workgroup
+// finish.
+template <int M>
+constexpr int kKwXRows = M <= 2 ? 2 : M <= 4 ? 4 : 8;
+
+template <int FMT, int XR>
+struct alignas(16) KwStage {
+  uint4 w[16 * 8];
+  uint4 x[XR * 32];
+  uint4 s[8 * scales_per_seg(FMT)];
+};
+
+template <int M, int FMT>
+struct KwCopier {
+  static constexpr int XR = kKwXRows<M>;
+  static constexpr int P = scales_per_seg(FMT);
+  static constexpr int kXPer = XR / 2;      // x copies per lane per stage (2 rows per copy)
+  static constexpr int kSLanes = 8 * P;     // lanes that copy a stage's scales
+  static constexpr int kLoads = 2 + kXPer + 1;
+  const uint16_t* x;
+  const uint8_t* ct;     // code row row0
+  const uint8_t* st;     // scale row group row0 / 16
+  const uint8_t* zeros;  // 16 zero bytes
+  uint32_t woff[2], xoff[kXPer];
+  int xk[kXPer];
+  bool xrow_ok[kXPer];
+  int k, lane;
+
+  __device__ __forceinline__ KwCopier(const GemvArgs& a, int64_t row0, int lane_, int mrows) {
+    const int64_t row_bytes = a.k_pad / 2;
+    k = a.k;
+    lane = lane_;
+    x = a.x;
+    ct = a.codes + row0 * row_bytes;
+    st = a.scales + (row0 / kRowGroup) * a.ksegs * kRowGroup * P;
+    zeros = ct + a.k / 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = i * 64 + lane;
+      const int rr = p >> 3;
+      const int c = (p & 7) ^ ((rr >> 1) & 7);
+      woff[i] = static_cast<uint32_t>(rr * row_bytes + 16 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int p = i * 64 + lane;
+      const int xr = p >> 5;
+      const int ch = (p & 31) ^ xr;
+      xrow_ok[i] = xr < mrows;
+      xoff[i] = xrow_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
+      xk[i] = 8 * ch;
+    }
+  }
+
+  // Copies of the stage at code k0 into sb: codes (non-temporal), x (chunks
+  // at or past k from the codes' zero padding; rows >= m fetch the first
+  // chunk of x, never read back into a stored output), and the scales by the
+  // first kSLanes lanes.
+  __device__ __forceinline__ void issue(int64_t k0, KwStage<FMT, XR>& sb) const {
+    const uint8_t* cb = ct + k0 / 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy16_sbase_nt(cb, woff[i], lds_addr(sb.w) + i * 64 * 16);
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const bool in_k = k0 + xk[i] < k;
+      const void* xs = !xrow_ok[i] ? static_cast<const void*>(x)
+                       : in_k      ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff[i])
+                                   : static_cast<const void*>(zeros);
+      copy16_vaddr(xs, lds_addr(sb.x) + i * 64 * 16);
+    }
+    if (lane < kSLanes) copy16_sbase(st + (k0 / 32) * kRowGroup * P, static_cast<uint32_t>(16 * lane), lds_addr(sb.s));
+  }
+};
+
+// Wait until at most N of this wave's vector-memory operations are in flight
+// and its LDS operations are done (no barrier: the wave-split kernel's waves
+// consume only the copies they issued).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// Wait for stage s of a wave's range ending at s1: up to NB - 2 younger
+// stages stay in flight.
+template <int LOADS, int NB>
+__device__ __forceinline__ void kw_wait(int s, int s1) {
+  if constexpr (NB > 2) {
+    if (s + NB - 2 < s1) {
+      wait_vm<(NB - 2) * LOADS>();
+      return;
+    }
+    kw_wait<LOADS, NB - 1>(s, s1);
+  } else {
+    wait_vm<0>();
+  }
+}
+
+template <int M, int FMT, int NB>
+__global__ __launch_bounds__(kThreads) void decode_kw_kernel(const GemvArgs a) {
+  using C = KwCopier<M, FMT>;
+  using S = KwStage<FMT, C::XR>;
+  __shared__ S st[kKwWaves][NB];
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kKwRows;
+  const int ksteps = (a.k + kDecodeStageK - 1) / kDecodeStageK;
+  const int s0 = wave * ksteps / kKwWaves;
+  const int s1 = (wave + 1) * ksteps / kKwWaves;
+
+  f32x4_t acc[1][1];
+  acc[0][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  S* mine = st[wave];
+  const C cp(a, row0, lane, M);
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j)
+    if (s0 + j < s1) cp.issue(static_cast<int64_t>(s0 + j) * kDecodeStageK, mine[j]);
+  for (int s = s0; s < s1; s += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int ss = s + j;
+      if (ss >= s1) break;
+      kw_wait<C::kLoads, NB>(ss, s1);
+      if (ss + NB - 1 < s1) cp.issue(static_cast<int64_t>(ss + NB - 1) * kDecodeStageK, mine[(j + NB - 1) % NB]);
+      compute_stage<M, FMT, 1, S, C::XR>(mine[j], nullptr, 0, r, g, M, acc);
+    }
+  }
+
+  // Every copy of this wave has landed (the last wait was for all of them),
+  // so its first stage buffer takes its sums: lane (r, g) holds
+  // C[m = 4 g + i][row r] in acc[0][0][i].
+  float* red = reinterpret_cast<float*>(&mine[0]);
+  *reinterpret_cast<f32x4_t*>(red + 4 * lane) = acc[0][0];
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4_t sum = acc[0][0];
+#pragma unroll
+  for (int w = 1; w < kKwWaves; ++w) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(&st[w][0]) + 4 * lane);
+    sum[0] += v[0];
+    sum[1] += v[1];
+    sum[2] += v[2];
+    sum[3] += v[3];
+  }
+  // Lane (r, g) now holds y[4 g + i][row r] (before the global scale).
+  // Greedy-argmax keys: each activation row's maximum over the tile's 16 rows
+  // is taken over the 16 lanes of its group g (a maximum: any order).
+  const int64_t row = row0 + r;
+  int h;
+  const int64_t col = out_col(a, row, h);
+  const float gs = h == 0 ? a.gscale[0] : a.gscale[1];
+  uint64_t best[4] = {0, 0, 0, 0};
+  if (col >= 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * g + i;
+      if (m < M) {
+        const uint16_t yb = f32_to_bf16_rne(sum[i] * gs);
+        if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
+        best[i] = argmax_key(yb, col);
+      }
+    }
+  }
+  if (a.keys) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const uint64_t w = shfl_xor_u64(best[i], o);
+        if (w > best[i]) best[i] = w;
+      }
+      const int m = 4 * g + i;
+      if (r == 0 && m < M) a.keys[static_cast<int64_t>(blockIdx.x) * M + m] = best[i];
+    }
+  }
+}
+
+template <int FMT>
+hipError_t launch_kw_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
+  switch (a.m) {
+    case 1: hipLaunchKernelGGL((decode_kw_kernel<1, FMT, kKwBuffers>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_kw_kernel<2, FMT, kKwBuffers>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((decode_kw_kernel<3, FMT, kKwBuffers>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_kw_kernel<4, FMT, kKwBuffers>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((decode_kw_kernel<5, FMT, kKwBuffers>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((decode_kw_kernel<6, FMT, kKwBuffers>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((decode_kw_kernel<7, FMT, kKwBuffers>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_kw_kernel<8, FMT, kKwBuffers>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 // Grouped MoE decode: workgroup (tile, s) computes 64-row tile `tile` of
 // the s-th expert that has routed pairs (in expert order) for its pairs
 // [offsets[e], offsets[e + 1]) -- their x rows gathered in pair order
@@ -590,6 +811,16 @@ hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts,
   else
     hipLaunchKernelGGL(moe_decode_kernel<kFmtMxfp4>, grid, dim3(kThreads), 0, stream, a, moe);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_kw(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
+  if (a.tile_rows != kKwRows || a.splits != 1 || a.act || a.m < 1 || a.m > kKwMaxM ||
+      a.rows_total % kKwRows != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.rows_total / kKwRows));
+  if (grid_out) *grid_out = grid;
+  if (block_out) *block_out = dim3(kThreads);
+  return fmt == kFmtNvfp4 ? launch_kw_fmt<kFmtNvfp4>(a, grid, stream) : launch_kw_fmt<kFmtMxfp4>(a, grid, stream);
 }
 
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {

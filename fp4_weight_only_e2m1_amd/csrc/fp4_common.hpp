@@ -131,6 +131,43 @@ inline int decode_mfma_splits(int n_proj, int k) {
   return s < 1 ? 1 : s;
 }
 
+// Wave-split decode (decode_kw_kernel): a 256-thread workgroup owns 16 rows
+// and its 4 waves split K, each streaming its quarter through kKwBuffers
+// stage buffers of its own (two in flight; measured on MI355X, 4 or 5 buffers
+// were slower).  16-row tiles give a 5120-row layer 320 workgroups with no
+// cross-workgroup split-K finish, at the price of staging x once per 16 rows
+// instead of once per 64 (at m = 8, twice the code bytes per stage).
+constexpr int kKwWaves = 4;
+constexpr int kKwRows = 16;
+constexpr int kKwMaxM = 8;
+constexpr int kKwBuffers = 3;
+constexpr int kKwMaxSteps = 32;
+// Whether a decode call of m rows without the SwiGLU epilogue runs on the
+// wave-split kernel: m <= 8, layers of fewer than 128 64-row tiles per
+// projection (those the 64-row kernels split along K across workgroups, or
+// leave with few workgroups), and at most kKwMaxSteps stages of 256 codes
+// (8 per wave).  Measured on MI355X (NVFP4, HIP-graph replay, m = 1 / 4, in
+// us, wave-split against the VALU GEMV or the 64-row MFMA decode):
+//   n = 5120, k = 1024:  3.5 / 4.0   against 4.1 / 5.4
+//   n = 2048, k = 4096:  4.4 / 4.7   against 6.0 / 7.0
+//   n = 5120, k = 6144:  7.3 / 8.4   against 9.1 / 8.9
+//   n = 7168, k = 8192:  9.3 / 11.2  against 10.8 / 12.3
+//   n = 5120, k = 12288: 12.1 / 13.7 against 11.2 / 12.4  (not taken)
+//   n = 5120, k = 17408: 16.3 / 18.8 against 14.6 / 15.8  (not taken)
+// With 16 or more stages per wave, the 320 workgroups on 256 CUs (a fifth of
+// the CUs run two) cost more than the finish saves.  Larger layers keep the
+// 64-row kernels: on the fused 2 x 12288 x 4096 gate_up the wave-split
+// kernel measured 10.9 / 13.6 / 17.3 us at m = 1 / 4 / 8 against 11.8 /
+// 13.0 / 13.3 (x staged per 16 rows costs twice the code bytes at m = 8), and
+// on the 248320-row head 126 / 148 against 109 / 132.  A function of (rows
+// per projection, k, m): the fused gate_up launch and the separate ones take
+// the same kernel.
+inline bool decode_kw_used(int n_proj, int k, int m) {
+  const int64_t tiles = round_up(n_proj, kRowAlign) / kDecodeTileRows;
+  const int ksteps = static_cast<int>((k + kDecodeStageK - 1) / kDecodeStageK);
+  return m >= 1 && m <= kKwMaxM && tiles < 128 && ksteps <= kKwMaxSteps;
+}
+
 // Rows of an MFMA-decode workgroup: 64 (one 16-row block per wave), or 128
 // (two blocks per wave, each x fragment read from LDS feeding two MFMAs: half
 // the x copies per weight byte) for layers of at least 2048 64-row tiles,
@@ -337,6 +374,7 @@ hipError_t launch_prepare_interleaved(const uint8_t* gate_codes, const uint8_t* 
                                       uint8_t* prep_scales, hipStream_t stream);
 hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
+hipError_t launch_decode_kw(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, const uint16_t* x, const int32_t* tokens,
                              int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid,
                              dim3* block);

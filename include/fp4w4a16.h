@@ -72,7 +72,12 @@ typedef struct fp4_dispatch_info {
                   (m = 3..32; SwiGLU gate_up: m = 3..16), 1 = MFMA tile GEMM
                   (m > 32; SwiGLU gate_up: m > 16), 3 = grouped MoE decode,
                   4 = W4A4 MXFP4 tile GEMM (any m),
-                  5 = grouped MoE tile GEMM (prefill) */
+                  5 = grouped MoE tile GEMM (prefill),
+                  6 = wave-split MFMA decode GEMV: m = 1..8 on layers of
+                  fewer than 8192 rows per projection (n rounded up to 256)
+                  with k <= 8192, instead of kernels 0 and 2 (not for the
+                  SwiGLU gate_up); 16-row workgroups whose four waves split
+                  K and add their sums in the workgroup */
   int splits;  /* K splits: decode kernels split every tile, the tile GEMMs only
                   their tail tiles (1 = no split; W4A4 tail tiles run as row
                   halves over all of K also report 1) */
@@ -142,7 +147,8 @@ int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scale
 /*
  * Workspace a compute call needs, in bytes (0 when none), for split-K fp32
  * partials and arrival flags: the m = 1, 2 decode GEMV with k > 4096, the
- * m = 3..32 MFMA decode on layers of fewer than 8192 rows per projection, and
+ * m = 3..32 MFMA decode on layers of fewer than 8192 rows per projection
+ * (except where the wave-split kernel runs: m <= 8 with k <= 8192), and
  * the m > 32 tile GEMM when its 128 x 256 output tiles do not fill whole
  * rounds of the 512 workgroups resident on the chip (the tail tiles are then
  * split along K; at most 64 MiB).  It never needs zeroing.  `projections` is 1 for
@@ -167,7 +173,9 @@ int fp4_workspace_bytes(int m, int n, int k, int fmt, int projections, size_t* b
  * GEMM (m > 32) also on m, which decides the tiles summed in K splits -- so
  * results are deterministic run to run, and for m <= 32 a row's result does
  * not depend on the other rows of the call as long as m selects the same
- * kernel (m = 1, 2: the VALU GEMV; m = 3..32: the MFMA decode).
+ * kernel (m = 1, 2: the VALU GEMV; m = 3..32: the MFMA decode; on the layers
+ * the wave-split kernel serves, m = 1..8 on it and m = 9..32 on the MFMA
+ * decode).
  * Cite: "native MXFP4 keep-quant" (vllm.cpp PR #38), commit list (the W4A16
  * entry points take bf16 x and the packed weight to bf16 y); "keep the ModelOpt
  * NVFP4 lm_head packed" (vllm.cpp PR #263), section "Why this row matters"
@@ -229,13 +237,17 @@ int fp4_w4a16_gate_up(const uint16_t* x_dev, int m, int k,
  * twice fp4_prepared_bytes(n_half, k, fmt)), which interleaves gate and up
  * rows in groups of 16 (prepared row R: gate row 16 (R / 32) + R % 16 when
  * R % 32 < 16, else the up row with that index) so that both operands of an
- * output are computed by one workgroup.  m <= 16: the decode kernels form y in
- * their epilogue; m > 16: the tile GEMM forms y in the epilogue of every whole
- * tile, and its reduce launch forms y for the tail tiles split along K.
- * Workspace: fp4_swiglu_workspace_bytes.  At m <= 16 it equals
- * fp4_workspace_bytes(m, n_half, k, fmt, 2) (the decode kernels' split-K
- * partials and flags); at m = 17..32 the SwiGLU call runs the tile GEMM while
- * fp4_w4a16_gate_up runs the decode kernel, so the two sizes differ there.
+ * output are computed by one workgroup.  m <= 16: the decode kernels 0 and 2
+ * form y in their epilogue (never the wave-split kernel 6, whose 16-row
+ * workgroups would hold only gate or only up rows); m > 16: the tile GEMM
+ * forms y in the epilogue of every whole tile, and its reduce launch forms y
+ * for the tail tiles split along K.
+ * Workspace: fp4_swiglu_workspace_bytes.  At m <= 16 it is the split-K
+ * partials and flags of kernels 0 and 2 for the 2 n_half rows -- equal to
+ * fp4_workspace_bytes(m, n_half, k, fmt, 2) except where fp4_w4a16_gate_up
+ * runs the wave-split kernel, which needs none; at m = 17..32 the SwiGLU call
+ * runs the tile GEMM while fp4_w4a16_gate_up runs the decode kernel, so the
+ * two sizes differ there.
  * silu uses the hardware exp and reciprocal (about 1 ulp each).
  * Reading taken: the pages name the MLP block after the fused gate_up but not
  * its activation; silu(gate) * up is the gated MLP of the model family they
@@ -258,7 +270,8 @@ int fp4_w4a16_gate_up_swiglu(const uint16_t* x_dev, int m, int k,
  * largest logit y[i][j] -- the bf16 value fp4_w4a16_linear gives for the same
  * arguments -- and the lowest such j when several are equal; -0 equals +0
  * and a NaN counts as larger than every number.  m = 1..32 only (the decode
- * kernels; FP4_EINVAL otherwise).  The argmax is the decode kernels' epilogue: each workgroup
+ * kernels; FP4_EINVAL otherwise).  The argmax is the epilogue of the decode
+ * kernel fp4_w4a16_linear picks for the same arguments (0, 2 or 6): each workgroup
  * reduces its logits to one (value, index) per activation row, a second
  * launch reduces those over the workgroups.  A maximum under that total
  * order does not depend on the reduction order, so the result is

@@ -69,3 +69,15 @@ def sample_rows(n, count, seed=0):
     rows = set(rng.choice(n, size=min(count, n), replace=False).tolist())
     rows.update([0, 1, n - 1, n - 2] if n > 2 else range(n))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def decode_kernel(n, k, m, act=False):
+    """Dispatch-info kernel of a decode call (m = 1..32) on a layer of n rows
+    per projection: 6, the wave-split MFMA decode, for m <= 8 on layers of
+    fewer than 128 64-row tiles with at most 32 K stages of 256 codes (not
+    for the SwiGLU epilogue); else 0, the VALU GEMV, at m = 1, 2 and 2, the
+    64-row MFMA decode, at m = 3..32."""
+    tiles = -(-n // 256) * 256 // 64
+    if not act and 1 <= m <= 8 and tiles < 128 and -(-k // 256) <= 32:
+        return 6
+    return 0 if m < 3 else 2

@@ -119,7 +119,24 @@ def test_workspace_bytes_policy():
     assert ws8 == 0                                             # 3880 tiles: no split
     down = fp4.fp4_workspace_bytes(8, 5120, 17408, NV)          # 80 tiles: 6 splits
     assert down == 6 * 8 * 5120 * 4 + 5120 // 64 * 6 * 8
-    assert fp4.fp4_workspace_bytes(5, 5120, 6144, NV) == 6 * 5 * 5120 * 4 + 80 * 6 * 8  # 24 stages: 6 splits
+    # Layers under 128 tiles with k <= 8192 take the wave-split kernel at
+    # m = 1..8 (K split over the waves of one workgroup: no workspace), the
+    # 64-row kernel above 8 rows (24 stages: 6 splits).
+    for m in range(1, 9):
+        assert fp4.fp4_workspace_bytes(m, 5120, 6144, NV) == 0
+        assert fp4.fp4_workspace_bytes(m, 2048, 1024, MX, 2) == 0
+    assert fp4.fp4_workspace_bytes(9, 5120, 6144, NV) == 6 * 9 * 5120 * 4 + 80 * 6 * 8
+    assert fp4.fp4_workspace_bytes(8, 5120, 8192, NV) == 0
+    assert fp4.fp4_workspace_bytes(8, 5120, 8448, NV) == 6 * 8 * 5120 * 4 + 80 * 6 * 8   # 33 stages
+    assert fp4.fp4_workspace_bytes(8, 8192, 4096, NV) == 0                                 # 128 tiles: unsplit
+    # Greedy argmax on the wave-split kernel: no partials, one key per
+    # (16-row tile, activation row).
+    assert fp4.fp4_argmax_workspace_bytes(4, 5000, 2048, NV) == 5120 // 16 * 4 * 8
+    # The SwiGLU gate_up stays on the 64-row kernel (its 16-row tiles would
+    # hold only gate or only up rows): 2048 rows per half, 32 tiles each,
+    # 16 stages: min(512 / 32, 16 / 4) = 4 splits over 4096 rows.
+    assert fp4.fp4_swiglu_workspace_bytes(4, 2048, 4096, NV) == 4 * 4 * 4096 * 4 + 4096 // 64 * 4 * 8
+    assert fp4.fp4_workspace_bytes(4, 2048, 4096, NV, 2) == 0
     # gate_up: two projections, each split like the separate linear.
     one = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 1)
     two = fp4.fp4_workspace_bytes(4, 12288, 4096, MX, 2)
@@ -155,6 +172,15 @@ def test_plan_follows_cu_count_only_in_the_xcd_deal():
     assert (p.kernel, p.splits, p.grid_x, p.grid_y, p.block, p.xcds) == (2, 6, 80, 6, 256, 0)
     p = fp4.fp4_plan(1, 248320, 5120, NV, 1, 256)
     assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (0, 2, 248320 // 64, 2)
+    # o_proj (5120 x 6144): the wave-split kernel at m = 1..8, 320 16-row
+    # workgroups; the 64-row MFMA decode split 6 ways above.
+    for m in (1, 2, 4, 8):
+        p = fp4.fp4_plan(m, 5120, 6144, NV, 1, 256)
+        assert (p.kernel, p.splits, p.grid_x, p.grid_y, p.block, p.xcds) == (6, 1, 320, 1, 256, 0)
+    p = fp4.fp4_plan(9, 5120, 6144, NV, 1, 256)
+    assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (2, 6, 80, 6)
+    p = fp4.fp4_plan(4, 5120, 6144, MX, 2, 256)
+    assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (6, 1, 640, 1)
     p = fp4.fp4_plan(0, 512, 256, NV, 1, 256)
     assert p.as_dict() == dict(kernel=0, splits=0, grid_x=0, grid_y=0, block=0, xcds=0)
 
@@ -218,7 +244,7 @@ def test_split_count_independent_of_m_and_fusion():
     # m within a kernel: the VALU GEMV (m = 1, 2; 64-row tiles for layers of at
     # least 512 of them, else 32-row tiles) and the MFMA decode kernel (m = 3..8,
     # 64-row tiles).
-    for n, k, fmt in [(5120, 17408, NV), (5120, 6144, NV), (12288, 4096, MX), (248320, 5120, NV)]:
+    for n, k, fmt in [(5120, 17408, NV), (7168, 12288, NV), (12288, 4096, MX), (248320, 5120, NV)]:
         rows = -(-n // 256) * 256
         for ms, tile in [(range(1, 3), 64 if rows // 64 >= 512 else 32), (range(3, 9), 64)]:
             counts = set()
@@ -238,8 +264,8 @@ def test_argmax_workspace_bytes():
     assert fp4.fp4_argmax_workspace_bytes(1, 248320, 5120, NV) == -(-base // 256) * 256 + 3880 * 1 * 8
     # lm_head m = 8: the MFMA decode on 128-row tiles (1940), unsplit.
     assert fp4.fp4_argmax_workspace_bytes(8, 248320, 5120, NV) == 1940 * 8 * 8
-    # A small layer at m = 4: 64-row tiles, 8 of them, no split.
-    assert fp4.fp4_argmax_workspace_bytes(4, 512, 256, MX) == 8 * 4 * 8
+    # A small layer at m = 4: the wave-split kernel, 16-row tiles, 32 of them.
+    assert fp4.fp4_argmax_workspace_bytes(4, 512, 256, MX) == 32 * 4 * 8
     assert fp4.fp4_argmax_workspace_bytes(0, 512, 256, MX) == 0
 
 

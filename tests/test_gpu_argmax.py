@@ -3,8 +3,8 @@ the oracle: exact on one-hot activations (the logits are then single weights,
 full of exact ties), and on random activations equal to the argmax of the
 unfused call's own logits, whose winner is also within the layer's tolerance
 of the oracle's maximum.  Covers the VALU GEMV (split and unsplit), the MFMA
-decode (64-row tiles split and unsplit, 128-row tiles) and poisoned
-workspaces."""
+decode (64-row tiles split and unsplit, 128-row tiles), the wave-split MFMA
+decode and poisoned workspaces."""
 
 import numpy as np
 import pytest
@@ -13,15 +13,17 @@ import torch
 import fp4_weight_only_e2m1_amd as fp4
 import oracle
 import synth
-from gpu_util import DEV, tolerance_violations, u8, x_dev, y_host_bits
+from gpu_util import DEV, decode_kernel, tolerance_violations, u8, x_dev, y_host_bits
 
 pytestmark = pytest.mark.gpu
 
 NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
 
-# (fmt, n, k): GEMV unsplit / split, MFMA split (small layer), MFMA unsplit
-# 64-row tiles, MFMA 128-row tiles; ragged n throughout.
-SHAPES = [(NV, 1000, 1024), (MX, 777, 5120), (NV, 5000, 2048), (MX, 9000, 512), (NV, 131000, 256)]
+# (fmt, n, k): small layers (the wave-split kernel at m <= 8), k past 8192
+# (GEMV and MFMA decode split along K), MFMA unsplit 64-row tiles, MFMA
+# 128-row tiles; ragged n throughout.
+SHAPES = [(NV, 1000, 1024), (MX, 777, 5120), (NV, 5000, 2048), (NV, 1000, 9216), (MX, 9000, 512),
+          (NV, 131000, 256)]
 
 
 def _zero_canon(bits):
@@ -47,7 +49,7 @@ def test_one_hot_argmax_exact(fmt, n, k, m):
     xbits = oracle.f32_to_bf16_bits(x)
     info = fp4.fp4_dispatch_info()
     idx, val, y = fp4.fp4_w4a16_linear_argmax(x_dev(xbits), pc, ps, n, float(g), fmt, logits=True, info=info)
-    assert info.kernel == (0 if m < 3 else 2)
+    assert info.kernel == decode_kernel(n, k, m)
     # Logits are bf16(w[:, k_i]) exactly (G is applied after the sum; -0 sums to +0).
     w = oracle.dequantize(packed, scales, k, fmt, g)
     logit_bits = _zero_canon(oracle.f32_to_bf16_bits(np.ascontiguousarray(w[:, ks].T)))
@@ -84,7 +86,8 @@ def test_argmax_matches_unfused_logits_and_oracle(fmt, n, k, m):
         assert y_ref[i, got[i]] >= top - (2.0 ** -7 * abs(top) + 1e-3 * rms), i
 
 
-@pytest.mark.parametrize("fmt,n,k,m", [(NV, 5000, 2048, 4), (MX, 777, 5120, 1), (NV, 131000, 256, 8)])
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 5000, 2048, 4), (MX, 777, 5120, 1), (NV, 131000, 256, 8),
+                                       (NV, 1000, 9216, 1), (NV, 1000, 9216, 5)])
 def test_argmax_workspace_poison_and_repeat(fmt, n, k, m):
     _, _, g, pc, ps = _prep(fmt, n, k, 82)
     xd = x_dev(synth.activations(synth.TINY, m, k))

@@ -13,7 +13,7 @@ import torch
 import fp4_weight_only_e2m1_amd as fp4
 import oracle
 import synth
-from gpu_util import assert_close, u8, x_dev, y_host
+from gpu_util import assert_close, decode_kernel, u8, x_dev, y_host
 
 pytestmark = pytest.mark.gpu
 
@@ -55,8 +55,9 @@ def _compare(y, y_ref, what, extreme=(7,)):
 
 @pytest.mark.parametrize("fmt,g_mode", [(NV, "workload"), (NV, "zero"), (MX, "workload")])  # MXFP4 has no G
 @pytest.mark.parametrize("m", [1, 4, 12, 24, 40])
-def test_degenerate_scales(fmt, m, g_mode):
-    n, k = 300, 1056
+@pytest.mark.parametrize("k", [1056, 8448])   # m <= 8: the wave-split kernel; past 32 K stages, the 64-row kernels
+def test_degenerate_scales(fmt, m, g_mode, k):
+    n = 300
     packed, scales, g = _degenerate_weight(fmt, n, k)
     if g_mode == "zero":
         g = np.float32(0.0)
@@ -64,7 +65,7 @@ def test_degenerate_scales(fmt, m, g_mode):
     xbits = synth.activations(synth.TINY, m, k)
     info = fp4.fp4_dispatch_info()
     y = y_host(fp4.fp4_w4a16_linear(x_dev(xbits), pc, ps, n, float(g), fmt, info=info))
-    assert info.kernel == (0 if m < 3 else 2 if m <= 32 else 1)
+    assert info.kernel == (decode_kernel(n, k, m) if m <= 32 else 1)
     y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
     nan_rows = {NV: (9, 13), MX: (5,)}[fmt]
     assert all(np.isnan(y_ref[:, r]).all() for r in nan_rows)

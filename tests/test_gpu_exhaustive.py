@@ -13,8 +13,9 @@ bit for bit; a row that holds an infinite or NaN weight anywhere in [0, k)
 gives NaN (0 * inf and NaN propagate), and a zero sum is +0 (the other
 products include +0).  So all 16 codes x 256 scale bytes go through each
 kernel's decoder -- the VALU GEMV (m = 1, 2), the MFMA decode on 64- and
-128-row tiles, with and without a K split, and the tile GEMM, whole tiles
-and split tail tiles -- for both formats and several global scales.
+128-row tiles, with and without a K split, the wave-split MFMA decode, and
+the tile GEMM, whole tiles and split tail tiles -- for both formats and
+several global scales.
 Expected values come from the oracle's decode (oracle.dequantize); the
 IEEE rule for the NaN rows is applied on top of it here.
 """
@@ -89,32 +90,38 @@ def run(packed, scales, n, k, fmt, g, cols, kernel, splits=None, grid_x=None):
     return got
 
 
-# (m, k, column sets, kernel, split expected): each set is one call; together
-# they cover codes 0..15 (the code of column c is c % 16).
+# (n, m, k, column sets, kernel, split expected): each set is one call;
+# together they cover codes 0..15 (the code of column c is c % 16).  Layers
+# of fewer than 8192 rows with k <= 8192 run the wave-split kernel at m <= 8;
+# the 64-row kernels are reached with 8192 rows or k past 8192.
 CASES = [
     # VALU GEMV: one or two rows, one column per row.
-    ("gemv m=1", 1, 32, [[c] for c in range(16)], 0, False),
-    ("gemv m=2", 2, 32, [[2 * c, 2 * c + 17] for c in range(8)], 0, False),
-    # VALU GEMV with k = 8192: two K splits; the ones sit in the second split.
-    ("gemv m=1 split", 1, 8192, [[4096 + 37 * c] for c in range(16)], 0, True),
+    ("gemv m=1", 8192, 1, 32, [[c] for c in range(16)], 0, False),
+    ("gemv m=2", 8192, 2, 32, [[2 * c, 2 * c + 17] for c in range(8)], 0, False),
+    # VALU GEMV with k = 8448: three K splits; the ones sit in the second split.
+    ("gemv m=1 split", 256, 1, 8448, [[4096 + 37 * c] for c in range(16)], 0, True),
     # MFMA decode, 64-row tiles: 16 rows (one activation group), 32 rows (two), 3 rows.
-    ("decode m=16", 16, 32, [list(range(16))], 2, False),
-    ("decode m=32", 32, 64, [list(range(32))], 2, False),
-    ("decode m=3", 3, 32, [[c, c + 5, c + 10] for c in range(0, 16, 3)], 2, False),
-    # MFMA decode with k = 8192 on 4 tiles: eight K splits; row j's one in split j.
-    ("decode m=8 split", 8, 8192, [[1024 * j + 17 * j + c for j in range(8)] for c in (0, 8)], 2, True),
+    ("decode m=16", 256, 16, 32, [list(range(16))], 2, False),
+    ("decode m=32", 256, 32, 64, [list(range(32))], 2, False),
+    ("decode m=3", 8192, 3, 32, [[c, c + 5, c + 10] for c in range(0, 16, 3)], 2, False),
+    # MFMA decode with k = 8448 on 4 tiles: eight K splits; row j's one in split j.
+    ("decode m=8 split", 256, 8, 8448, [[1024 * j + 17 * j + c for j in range(8)] for c in (0, 8)], 2, True),
+    # Wave-split MFMA decode: one stage (waves 1..3 idle), the ones in all four
+    # waves' K quarters (k = 1024: one stage each), and 8 stages per wave.
+    ("wave-split m=1", 256, 1, 32, [[c] for c in range(16)], 6, False),
+    ("wave-split m=4", 256, 4, 1024, [[256 * w + 4 * q + w for w in range(4)] for q in range(4)], 6, False),
+    ("wave-split m=8", 256, 8, 8192, [[1024 * j + 17 * j + c for j in range(8)] for c in (0, 8)], 6, False),
     # Tile GEMM: 64 rows (2-block instances), 128 rows (4-block instances).
-    ("gemm m=64", 64, 64, [list(range(64))], 1, False),
-    ("gemm m=128", 128, 128, [list(range(128))], 1, False),
+    ("gemm m=64", 256, 64, 64, [list(range(64))], 1, False),
+    ("gemm m=128", 256, 128, 128, [list(range(128))], 1, False),
     # Tile GEMM with k = 5120 on one tile: its K split 4 ways, summed by the reduce launch.
-    ("gemm m=40 split", 40, 5120, [[128 * j + (j % 16) for j in range(40)]], 1, True),
+    ("gemm m=40 split", 256, 40, 5120, [[128 * j + (j % 16) for j in range(40)]], 1, True),
 ]
 
 
 @pytest.mark.parametrize("fmt", [NV, MX])
-@pytest.mark.parametrize("name,m,k,colsets,kernel,split", CASES, ids=[c[0] for c in CASES])
-def test_exhaustive_table_through_kernel(fmt, name, m, k, colsets, kernel, split):
-    n = 256
+@pytest.mark.parametrize("name,n,m,k,colsets,kernel,split", CASES, ids=[c[0] for c in CASES])
+def test_exhaustive_table_through_kernel(fmt, name, n, m, k, colsets, kernel, split):
     packed, scales = table_weight(fmt, n, k)
     for g in G_VALUES[fmt]:
         for cols in colsets:

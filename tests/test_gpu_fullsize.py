@@ -22,7 +22,7 @@ CASES = [
     ("tiny_nvfp4", synth.TINY, 0, NV, 512, 256, [1]),
     ("lm_head", synth.LM_HEAD, 0, NV, 248320, 5120, [1, 8, 16, 32]),
     ("down_proj", synth.DECODE_27B, 0, NV, 5120, 17408, [1, 2, 4, 8, 16, 32]),
-    ("o_proj", synth.DECODE_27B, 1, NV, 5120, 6144, [1, 2, 4, 8]),
+    ("o_proj", synth.DECODE_27B, 1, NV, 5120, 6144, [1, 2, 4, 8, 16]),
     ("prefill_nvfp4", synth.PREFILL, 0, NV, 17408, 5120, [256, 1024, 4096]),
     ("prefill_mxfp4", synth.PREFILL, 1, MX, 17408, 5120, [256, 1024, 4096]),
 ]

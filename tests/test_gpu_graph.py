@@ -1,9 +1,9 @@
 """HIP-graph replay of the layer: a captured call replayed several times, with
 new activations written in place and eager calls on the same workspace in
 between, must give every time the bytes an eager call gives for the same
-inputs.  Covers the split-K finish of both decode kernels (whose arrival
-flags carry a token fixed at capture time) and the prefill GEMM's tail
-reduce, next to an unsplit call."""
+inputs.  Covers the split-K finish of both 64-row-family decode kernels
+(whose arrival flags carry a token fixed at capture time), the wave-split
+decode and the prefill GEMM's tail reduce, next to an unsplit call."""
 
 import numpy as np
 import pytest
@@ -20,7 +20,8 @@ NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
 
 @pytest.mark.parametrize("fmt,n,k,m,split", [
     (NV, 512, 17408, 1, True),    # VALU GEMV, K split 5 ways
-    (NV, 300, 5120, 8, True),     # MFMA decode, K split
+    (NV, 300, 9216, 8, True),     # MFMA decode, K split
+    (NV, 300, 5120, 8, False),    # wave-split MFMA decode
     (MX, 300, 5120, 24, True),    # MFMA decode, two 16-row activation groups, K split
     (MX, 8192, 1024, 4, False),   # MFMA decode, unsplit (128 row tiles)
     (NV, 512, 5120, 100, True),   # prefill GEMM, tail tiles split along K
@@ -61,10 +62,11 @@ def test_graph_replay_matches_eager(fmt, n, k, m, split):
         torch.cuda.synchronize()
 
 
-def test_graph_replay_argmax():
-    # The greedy-argmax call (decode kernel epilogue + reduce launch) replayed
-    # from a graph with new activations gives the eager call's token ids.
-    fmt, n, k, m = NV, 9000, 5120, 2
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 9000, 5120, 2), (NV, 5000, 2048, 6)])
+def test_graph_replay_argmax(fmt, n, k, m):
+    # The greedy-argmax call (decode kernel epilogue + reduce launch; the VALU
+    # GEMV with a K split, the wave-split MFMA decode) replayed from a graph
+    # with new activations gives the eager call's token ids.
     packed, scales, g = synth.packed_weight(synth.TINY, 71, n, k, fmt)
     pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
     ws = torch.full((fp4.fp4_argmax_workspace_bytes(m, n, k, fmt),), 0xA5, dtype=torch.uint8, device=DEV)
@@ -130,12 +132,13 @@ def test_graph_replay_w4a4():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("n,k,m", [(5120, 6144, 4), (512, 5120, 100)])
-def test_graph_replay_w4a4_nvfp4(n, k, m):
+@pytest.mark.parametrize("n,k,m,split", [(5120, 9216, 4, True), (5120, 6144, 4, False), (512, 5120, 100, True)])
+def test_graph_replay_w4a4_nvfp4(n, k, m, split):
     # The NVFP4 W4A4 call (quantizer into the workspace, then the W4A16 call on
-    # it: the MFMA decode with a K split, or the tile GEMM with split tail
-    # tiles and the reduce) replayed from a graph with new activations gives
-    # the eager call's bytes, on a workspace that starts poisoned.
+    # it: the MFMA decode with a K split, the wave-split MFMA decode, or the
+    # tile GEMM with split tail tiles and the reduce) replayed from a graph
+    # with new activations gives the eager call's bytes, on a workspace that
+    # starts poisoned.
     packed, scales, g = synth.packed_weight(synth.TINY, 73, n, k, NV)
     pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, NV)
     ws = torch.full((fp4.fp4_w4a4_nvfp4_workspace_bytes(m, n, k),), 0xA5, dtype=torch.uint8, device=DEV)
@@ -149,7 +152,7 @@ def test_graph_replay_w4a4_nvfp4(n, k, m):
 
     call(y_graph)
     torch.cuda.synchronize()
-    assert info.splits > 1, info.as_dict()
+    assert (info.splits > 1) == split, info.as_dict()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         call(y_graph)

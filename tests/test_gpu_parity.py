@@ -10,13 +10,12 @@ import torch
 import fp4_weight_only_e2m1_amd as fp4
 import oracle
 import synth
-from gpu_util import DEV, assert_close, u8, x_dev, y_host, y_host_bits
+from gpu_util import DEV, assert_close, decode_kernel, u8, x_dev, y_host, y_host_bits
 
 pytestmark = pytest.mark.gpu
 
 NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
 GS = {NV: 16, MX: 32}
-DECODE_MFMA_MIN_M = 3   # m at which the decode path switches from v_dot2 to MFMA
 
 
 def _canon_bits(a):
@@ -96,6 +95,8 @@ SHAPES = [
     (MX, 257, 96),      # k below one slab
     (NV, 256, 5120),    # k split in two (lm_head's k)
     (NV, 128, 17408),   # many splits (down_proj's k)
+    (NV, 640, 9216),    # past the wave-split kernel's 32 K stages: the 64-row kernels, K split
+    (MX, 8192, 1056),   # 128 64-row tiles: the 64-row kernels, unsplit, ragged last stage
 ]
 
 
@@ -106,7 +107,7 @@ def test_gemv_matches_oracle(fmt, n, k, m):
     xbits = synth.activations(synth.TINY, m, k)
     info = fp4.fp4_dispatch_info()
     y = _run_linear(packed, scales, g, fmt, n, k, xbits, info)
-    assert info.kernel == (0 if m < DECODE_MFMA_MIN_M else 2)
+    assert info.kernel == decode_kernel(n, k, m)
     y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
     assert_close(y_host(y), y_ref, "gemv fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
 
@@ -141,7 +142,8 @@ def test_two_way_tail_runs_whole(fmt, n, k, m):
 
 
 @pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 2048, 1), (MX, 512, 2048, 4), (NV, 300, 5120, 8),
-                                       (NV, 512, 2048, 16), (MX, 384, 1056, 40)])
+                                       (NV, 512, 2048, 16), (MX, 384, 1056, 40), (NV, 8192, 1024, 1),
+                                       (MX, 8448, 2048, 5), (NV, 640, 9216, 2), (MX, 640, 9216, 7)])
 def test_one_hot_selects_weight_column(fmt, n, k, m):
     # x row i = e_{k_i}: y[i, :] is bf16(w[:, k_i]) exactly (the global scale is
     # applied after the sum, and every other product is zero).
@@ -171,24 +173,31 @@ def test_gate_up_fused_equals_split(fmt, nh, k, m):
     assert_close(oracle.bf16_bits_to_f32(y).astype(np.float64), y_ref, "gate_up")
 
 
-@pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 384, 3072), (NV, 256, 17408), (NV, 300, 5120)])
+@pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 384, 3072), (NV, 256, 17408), (NV, 300, 5120),
+                                     (MX, 8192, 1056)])
 def test_gemv_batch_invariance(fmt, n, k):
     # Within one decode kernel, row i of an m-row call equals the same row of
-    # a call with more rows, bit for bit (the summation order never depends on m).
+    # a call with more rows, bit for bit (the summation order never depends on
+    # m): each call is compared with the call of the most rows that runs on
+    # the same kernel.  (MFMA decode: m = 9..16 stage 16 x rows instead of 8,
+    # m = 17..32 32 rows with a second MFMA per fragment -- the same MFMA sums
+    # for every row; wave-split: x rows staged 2, 4 or 8 at a time.)
     packed, scales, g = _quantized(fmt, n, k)
     pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
-    # m = 9..16 stage 16 x rows instead of 8, m = 17..32 32 rows with a
-    # second MFMA per fragment: the same MFMA sums for every row.
     x32 = synth.activations(synth.TINY, 32, k)
-    y32 = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x32), pc, ps, n, float(g), fmt))
-    ylo = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x32[:DECODE_MFMA_MIN_M - 1]), pc, ps, n, float(g), fmt))
+    ys, kernels = {}, {}
     for m in range(1, 33):
-        ym = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x32[:m]), pc, ps, n, float(g), fmt))
-        ref = y32 if m >= DECODE_MFMA_MIN_M else ylo
-        assert np.array_equal(ym, ref[:m]), m
+        info = fp4.fp4_dispatch_info()
+        ys[m] = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x32[:m]), pc, ps, n, float(g), fmt, info=info))
+        kernels[m] = info.kernel
+        assert info.kernel == decode_kernel(n, k, m), m
+    for m in range(1, 33):
+        top = max(q for q in range(1, 33) if kernels[q] == kernels[m])
+        assert np.array_equal(ys[m], ys[top][:m]), (m, top)
 
 
-@pytest.mark.parametrize("fmt,n,k,m", [(NV, 300, 5120, 8), (MX, 256, 17408, 3), (NV, 640, 2048, 64)])
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 300, 5120, 8), (MX, 256, 17408, 3), (NV, 640, 2048, 64),
+                                       (NV, 640, 9216, 8), (MX, 640, 9216, 1)])
 def test_deterministic_and_workspace_poison(fmt, n, k, m):
     packed, scales, g = _quantized(fmt, n, k)
     pc, ps = fp4.fp4_prepare(u8(packed), u8(scales), n, k, fmt)
@@ -201,11 +210,12 @@ def test_deterministic_and_workspace_poison(fmt, n, k, m):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-@pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 17408, 1), (NV, 640, 6144, 2), (MX, 1024, 5120, 1),
-                                        (NV, 512, 5120, 100), (MX, 300, 4096, 300), (NV, 256, 3872, 40)])
+@pytest.mark.parametrize("fmt,n,k,m", [(NV, 512, 17408, 1), (NV, 640, 9216, 2), (MX, 1024, 9216, 1),
+                                        (NV, 640, 9216, 6), (NV, 512, 5120, 100), (MX, 300, 4096, 300),
+                                        (NV, 256, 3872, 40)])
 def test_split_k_handshake_repeated(fmt, n, k, m):
     # The split-K finish exchanges partials between workgroups in one launch
-    # (decode GEMV splits; prefill tail tiles, the last case with a ragged
+    # (decode GEMV and MFMA decode splits; prefill tail tiles, the last case with a ragged
     # final K step); 40 back-to-back calls on one workspace must all give the
     # same bytes.
     packed, scales, g = _quantized(fmt, n, k, tensor=5)

@@ -14,12 +14,14 @@ pytestmark = pytest.mark.gpu
 NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
 
 # (m, n, k, fmt, projections): the GEMV, the MFMA decode on 64- and 128-row
-# tiles with and without K splits, the tile GEMM whole, with split tail tiles
+# tiles with and without K splits, the wave-split MFMA decode, the tile GEMM
+# whole, with split tail tiles
 # and with a two-way tail run whole, linear and fused gate_up.
 SHAPES = [(1, 12288, 4096, MX, 2), (2, 248320, 5120, NV, 1), (1, 5120, 17408, NV, 1), (8, 5120, 17408, NV, 1),
           (8, 248320, 5120, NV, 1), (24, 5120, 6144, NV, 1), (4, 12288, 4096, MX, 2), (33, 17408, 5120, NV, 1),
           (1024, 17408, 5120, NV, 1), (1024, 17408, 5120, MX, 1), (1024, 12288, 4096, MX, 2),
-          (1280, 5120, 17408, NV, 1), (4096, 4096, 5120, NV, 1)]
+          (1280, 5120, 17408, NV, 1), (4096, 4096, 5120, NV, 1), (4, 5120, 6144, NV, 1), (1, 2048, 4096, MX, 2),
+          (8, 300, 1056, NV, 1)]
 
 
 def test_plan_matches_the_calls():

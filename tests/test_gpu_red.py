@@ -2,7 +2,7 @@
 the oracle must fail against a mutated oracle.
 
 For every family of parity test (the VALU GEMV, the MFMA decode with and
-without a K split, the tile GEMM whole and with split tail tiles, the fused
+without a K split, the wave-split MFMA decode, the tile GEMM whole and with split tail tiles, the fused
 gate_up, the greedy argmax, the grouped MoE and the SwiGLU gate_up), the GPU
 result is first checked green against the oracle with the layer's tolerance,
 then the same comparison is run against the oracle evaluated on mutated
@@ -64,8 +64,10 @@ def assert_green_then_red(y, ref, reds, what):
 
 # (fmt, n, k, m, kernel, split): one case per kernel path.
 LINEAR = [
-    (NV, 512, 2048, 1, 0, False),     # VALU GEMV
-    (MX, 384, 8192, 2, 0, True),      # VALU GEMV, K split in two
+    (NV, 8192, 1024, 1, 0, False),    # VALU GEMV
+    (MX, 384, 8448, 2, 0, True),      # VALU GEMV, K split in three
+    (NV, 640, 6144, 4, 6, False),     # wave-split MFMA decode
+    (MX, 300, 1056, 8, 6, False),     # wave-split MFMA decode, ragged n and last stage
     (NV, 8192, 2048, 8, 2, False),    # MFMA decode (128 tiles: unsplit)
     (NV, 256, 17408, 4, 2, True),     # MFMA decode, K split
     (MX, 640, 1024, 24, 2, False),    # MFMA decode, two activation groups

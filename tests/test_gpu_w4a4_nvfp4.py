@@ -2,9 +2,9 @@
 quantizer bit for bit (random rows at several per-tensor scales, every E4M3
 scale value and every midpoint between two of them, every E2M1 midpoint at
 each of those scales, degenerate blocks), the product within the layer's
-tolerance on each W4A16 kernel it runs (GEMV, MFMA decode, tile GEMM with and
-without split tail tiles), bit for bit equal to the weight-only product where
-the activations are exactly NVFP4, the fused gate_up equal to two calls, RED
+tolerance on each W4A16 kernel it runs (GEMV, MFMA decode, wave-split MFMA
+decode, tile GEMM with and without split tail tiles), bit for bit equal to
+the weight-only product where the activations are exactly NVFP4, the fused gate_up equal to two calls, RED
 checks, and sampled outputs at the prefill shape."""
 
 import numpy as np
@@ -111,9 +111,11 @@ def _weights(n, k, seed):
 
 # (n, k, m, kernel, tail split): one case per W4A16 kernel the product runs.
 LINEAR = [
-    (512, 2048, 1, 0, False),      # VALU GEMV
-    (384, 8192, 2, 0, False),      # VALU GEMV, K split in two
-    (300, 1056, 8, 2, False),      # MFMA decode, ragged n and k
+    (8192, 1024, 1, 0, False),     # VALU GEMV
+    (384, 8448, 2, 0, False),      # VALU GEMV, K split in three
+    (512, 2048, 1, 6, False),      # wave-split MFMA decode
+    (300, 1056, 8, 6, False),      # wave-split MFMA decode, ragged n and k
+    (8192, 1024, 4, 2, False),     # MFMA decode, unsplit
     (256, 17408, 4, 2, False),     # MFMA decode, K split
     (640, 2048, 24, 2, False),     # MFMA decode, two activation groups
     (1024, 1024, 200, 1, False),   # tile GEMM

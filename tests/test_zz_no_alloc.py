@@ -32,11 +32,11 @@ def _noalloc(lib, x, pc, ps, n, g, fmt, y, info):
 
 
 # Pairs of calls: the second smaller than the first.  Each call needs a
-# workspace: split-K decode (GEMV m = 1, 2; MFMA decode m = 3..32 on small
-# layers) or split tail tiles of the tile GEMM.
+# workspace: split-K decode (GEMV m = 1, 2 and MFMA decode m = 3..32 on small
+# layers past the wave-split kernel's k) or split tail tiles of the tile GEMM.
 PAIRS = [
-    [(NV, 5120, 17408, 8), (NV, 5120, 6144, 4)],    # MFMA decode, 6 K splits each
-    [(MX, 1024, 8192, 2), (NV, 512, 5120, 1)],      # VALU GEMV, K split in two
+    [(NV, 5120, 17408, 8), (NV, 5120, 9216, 4)],    # MFMA decode, 6 K splits each
+    [(MX, 1024, 9216, 2), (NV, 512, 9216, 1)],      # VALU GEMV, K split in three
     [(NV, 4096, 5120, 300), (MX, 512, 4096, 40)],   # tile GEMM, split tail tiles
 ]
 
