@@ -44,7 +44,7 @@ int check_m(int m) { return (m < 0 || m > FP4_MAX_M) ? FP4_EINVAL : FP4_OK; }
 
 // Whether a decode call takes the wave-split kernel.  The SwiGLU epilogue
 // (act) stays on the 64-row kernels, whose tiles hold both rows of an output.
-bool uses_kw(int m, int n_proj, int k, bool act) { return !act && fp4::decode_kw_used(n_proj, k, m); }
+bool uses_kw(int m, int n_proj, int k, int fmt, bool act) { return !act && fp4::decode_kw_used(n_proj, k, fmt, m); }
 
 size_t workspace_for(int m, int n_proj, int k, int fmt, int projections, bool act = false) {
   // Both decode kernels split K across workgroups for some shapes (partials
@@ -53,7 +53,7 @@ size_t workspace_for(int m, int n_proj, int k, int fmt, int projections, bool ac
   if (m < 1) return 0;
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
   if (m > fp4::kDecodeMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
-  if (uses_kw(m, n_proj, k, act)) return 0;
+  if (uses_kw(m, n_proj, k, fmt, act)) return 0;
   const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
   const int splits = on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
   const int tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(rows_total, m)
@@ -121,7 +121,7 @@ size_t argmax_workspace_for(int m, int n, int k, int fmt, size_t* keys_offset) {
   const size_t base = fp4::round_up(static_cast<int64_t>(workspace_for(m, n, k, fmt, 1)), 256);
   const int64_t rows_total = fp4::round_up(n, fp4::kRowAlign);
   if (keys_offset) *keys_offset = base;
-  const int tile_rows = uses_kw(m, n, k, false) ? fp4::kKwRows : decode_tile_rows(m, rows_total);
+  const int tile_rows = uses_kw(m, n, k, fmt, false) ? fp4::kKwRows : decode_tile_rows(m, rows_total);
   return base + static_cast<size_t>(rows_total / tile_rows) * m * 8;
 }
 
@@ -179,7 +179,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.k_pad = ps.k_pad;
     a.kgroups = ps.kgroups;
     a.ksegs = ps.ksegs;
-    const bool kw = uses_kw(m, n_proj, k, act != 0);
+    const bool kw = uses_kw(m, n_proj, k, fmt, act != 0);
     const bool on_mfma = m >= fp4::kDecodeMfmaMinM || kw;
     a.nslab = static_cast<int>(ps.k_pad / fp4::kSlabK);
     a.splits = kw ? 1 : on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
@@ -512,7 +512,7 @@ int fp4_plan(int m, int n, int k, int fmt, int projections, int cus, fp4_dispatc
   const int64_t rows_total = projections * fp4::round_up(n, fp4::kRowAlign);
   if (m <= fp4::kDecodeMaxM) {
     // The decode kernels: grid (row tiles, K splits), as run_linear launches them.
-    if (uses_kw(m, n, k, false)) {
+    if (uses_kw(m, n, k, fmt, false)) {
       *info_out = fp4_dispatch_info{6, 1, static_cast<int>(rows_total / fp4::kKwRows), 1, fp4::kDecodeThreads, 0};
       return FP4_OK;
     }

@@ -143,29 +143,37 @@ constexpr int kKwMaxM = 8;
 constexpr int kKwBuffers = 3;
 constexpr int kKwMaxSteps = 32;
 // Whether a decode call of m rows without the SwiGLU epilogue runs on the
-// wave-split kernel: m <= 8, layers of fewer than 128 64-row tiles per
-// projection (those the 64-row kernels split along K across workgroups, or
-// leave with few workgroups), and at most kKwMaxSteps stages of 256 codes
-// (8 per wave).  Measured on MI355X (NVFP4, HIP-graph replay, m = 1 / 4, in
-// us, wave-split against the VALU GEMV or the 64-row MFMA decode):
-//   n = 5120, k = 1024:  3.5 / 4.0   against 4.1 / 5.4
-//   n = 2048, k = 4096:  4.4 / 4.7   against 6.0 / 7.0
-//   n = 5120, k = 6144:  7.3 / 8.4   against 9.1 / 8.9
-//   n = 7168, k = 8192:  9.3 / 11.2  against 10.8 / 12.3
-//   n = 5120, k = 12288: 12.1 / 13.7 against 11.2 / 12.4  (not taken)
-//   n = 5120, k = 17408: 16.3 / 18.8 against 14.6 / 15.8  (not taken)
-// With 16 or more stages per wave, the 320 workgroups on 256 CUs (a fifth of
-// the CUs run two) cost more than the finish saves.  Larger layers keep the
-// 64-row kernels: on the fused 2 x 12288 x 4096 gate_up the wave-split
-// kernel measured 10.9 / 13.6 / 17.3 us at m = 1 / 4 / 8 against 11.8 /
-// 13.0 / 13.3 (x staged per 16 rows costs twice the code bytes at m = 8), and
-// on the 248320-row head 126 / 148 against 109 / 132.  A function of (rows
-// per projection, k, m): the fused gate_up launch and the separate ones take
-// the same kernel.
-inline bool decode_kw_used(int n_proj, int k, int m) {
+// wave-split kernel: at most kKwMaxSteps stages of 256 codes (8 per wave),
+// and either m <= 8 on a layer of fewer than 128 64-row tiles per projection
+// (those the 64-row kernels split along K across workgroups, or leave with
+// few workgroups), or, for MXFP4, m <= 2 on fewer than 256 such tiles.
+// Measured on MI355X (HIP-graph replay, in us, wave-split against the VALU
+// GEMV or the 64-row MFMA decode):
+//   NVFP4 n = 5120, k = 1024,  m = 1 / 4: 3.5 / 4.0   against 4.1 / 5.4
+//   NVFP4 n = 2048, k = 4096,  m = 1 / 4: 4.4 / 4.7   against 6.0 / 7.0
+//   NVFP4 n = 5120, k = 6144,  m = 1 / 4: 7.3 / 8.4   against 9.1 / 8.9
+//   NVFP4 n = 7168, k = 8192,  m = 1 / 4: 9.3 / 11.2  against 10.8 / 12.3
+//   MXFP4 n = 12288, k = 4096, m = 1 / 2: 6.6 / 7.2   against 7.9 / 8.9
+//   MXFP4 fused gate_up 2 x 12288 x 4096, m = 1 / 2: 11.3-11.7 / 11.9 against
+//     11.9-12.6 / 12.7-12.9
+// and not taken where it lost:
+//   NVFP4 n = 5120, k = 12288, m = 1 / 4: 12.1-12.8 / 13.7 against 11.2 / 12.4
+//   NVFP4 n = 5120, k = 17408, m = 1 / 4: 16.3 / 18.8 against 14.6 / 15.8
+//   (16 or more stages per wave: the 320 workgroups on 256 CUs, a fifth of
+//   the CUs running two, cost more than the finish saves);
+//   MXFP4 fused gate_up 2 x 12288 x 4096, m = 4 / 8: 13.6 / 17.3 against
+//   13.0 / 13.3 (x staged per 16 rows costs twice the code bytes at m = 8);
+//   NVFP4 fused gate_up 2 x 12288 x 4096, m = 1: 15.0-15.6 against 12.3-12.5
+//   (the NVFP4 decode's VALU work over 1536 workgroups);
+//   the 248320-row head at m = 1 / 4: 126 / 148 against 109 / 132.
+// A function of (rows per projection, k, format, m): the fused gate_up
+// launch and the separate ones take the same kernel.
+inline bool decode_kw_used(int n_proj, int k, int fmt, int m) {
   const int64_t tiles = round_up(n_proj, kRowAlign) / kDecodeTileRows;
   const int ksteps = static_cast<int>((k + kDecodeStageK - 1) / kDecodeStageK);
-  return m >= 1 && m <= kKwMaxM && tiles < 128 && ksteps <= kKwMaxSteps;
+  const bool small_layer = m <= kKwMaxM && tiles < 128;
+  const bool mxfp4_gemv_rows = fmt == kFmtMxfp4 && m <= 2 && tiles < 256;
+  return m >= 1 && ksteps <= kKwMaxSteps && (small_layer || mxfp4_gemv_rows);
 }
 
 // Rows of an MFMA-decode workgroup: 64 (one 16-row block per wave), or 128

@@ -73,11 +73,12 @@ typedef struct fp4_dispatch_info {
                   (m > 32; SwiGLU gate_up: m > 16), 3 = grouped MoE decode,
                   4 = W4A4 MXFP4 tile GEMM (any m),
                   5 = grouped MoE tile GEMM (prefill),
-                  6 = wave-split MFMA decode GEMV: m = 1..8 on layers of
-                  fewer than 8192 rows per projection (n rounded up to 256)
-                  with k <= 8192, instead of kernels 0 and 2 (not for the
-                  SwiGLU gate_up); 16-row workgroups whose four waves split
-                  K and add their sums in the workgroup */
+                  6 = wave-split MFMA decode GEMV, instead of kernels 0 and
+                  2 where k <= 8192: m = 1..8 on layers of fewer than 8192
+                  rows per projection (n rounded up to 256), and for MXFP4
+                  also m = 1, 2 on fewer than 16384 (not for the SwiGLU
+                  gate_up); 16-row workgroups whose four waves split K and
+                  add their sums in the workgroup */
   int splits;  /* K splits: decode kernels split every tile, the tile GEMMs only
                   their tail tiles (1 = no split; W4A4 tail tiles run as row
                   halves over all of K also report 1) */
@@ -148,7 +149,7 @@ int fp4_prepare_gate_up(const uint8_t* gate_codes_dev, const uint8_t* gate_scale
  * Workspace a compute call needs, in bytes (0 when none), for split-K fp32
  * partials and arrival flags: the m = 1, 2 decode GEMV with k > 4096, the
  * m = 3..32 MFMA decode on layers of fewer than 8192 rows per projection
- * (except where the wave-split kernel runs: m <= 8 with k <= 8192), and
+ * (except where the wave-split kernel runs, kernel 6 of fp4_dispatch_info), and
  * the m > 32 tile GEMM when its 128 x 256 output tiles do not fill whole
  * rounds of the 512 workgroups resident on the chip (the tail tiles are then
  * split along K; at most 64 MiB).  It never needs zeroing.  `projections` is 1 for

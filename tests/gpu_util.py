@@ -71,13 +71,16 @@ def sample_rows(n, count, seed=0):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def decode_kernel(n, k, m, act=False):
+def decode_kernel(fmt, n, k, m, act=False):
     """Dispatch-info kernel of a decode call (m = 1..32) on a layer of n rows
-    per projection: 6, the wave-split MFMA decode, for m <= 8 on layers of
-    fewer than 128 64-row tiles with at most 32 K stages of 256 codes (not
-    for the SwiGLU epilogue); else 0, the VALU GEMV, at m = 1, 2 and 2, the
-    64-row MFMA decode, at m = 3..32."""
+    per projection: 6, the wave-split MFMA decode, for at most 32 K stages of
+    256 codes and either m <= 8 on layers of fewer than 128 64-row tiles or,
+    for MXFP4, m <= 2 on fewer than 256 (never for the SwiGLU epilogue);
+    else 0, the VALU GEMV, at m = 1, 2 and 2, the 64-row MFMA decode, at
+    m = 3..32."""
     tiles = -(-n // 256) * 256 // 64
-    if not act and 1 <= m <= 8 and tiles < 128 and -(-k // 256) <= 32:
+    small = m <= 8 and tiles < 128
+    mx_rows = fmt == fp4.FMT_MXFP4 and m <= 2 and tiles < 256
+    if not act and m >= 1 and -(-k // 256) <= 32 and (small or mx_rows):
         return 6
     return 0 if m < 3 else 2

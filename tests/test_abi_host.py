@@ -181,6 +181,15 @@ def test_plan_follows_cu_count_only_in_the_xcd_deal():
     assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (2, 6, 80, 6)
     p = fp4.fp4_plan(4, 5120, 6144, MX, 2, 256)
     assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (6, 1, 640, 1)
+    # The MXFP4 gate_up (2 x 12288 x 4096): the wave-split kernel at m = 1, 2
+    # (1536 workgroups), the 64-row MFMA decode from m = 3; NVFP4 keeps the GEMV.
+    for m in (1, 2):
+        p = fp4.fp4_plan(m, 12288, 4096, MX, 2, 256)
+        assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (6, 1, 1536, 1)
+        assert fp4.fp4_plan(m, 12288, 4096, NV, 2, 256).kernel == 0
+    assert fp4.fp4_plan(3, 12288, 4096, MX, 2, 256).as_dict()["kernel"] == 2
+    assert fp4.fp4_plan(1, 16384, 4096, MX, 1, 256).kernel == 0      # 256 tiles
+    assert fp4.fp4_plan(1, 12288, 8448, MX, 1, 256).kernel == 0      # 33 K stages
     p = fp4.fp4_plan(0, 512, 256, NV, 1, 256)
     assert p.as_dict() == dict(kernel=0, splits=0, grid_x=0, grid_y=0, block=0, xcds=0)
 

@@ -49,7 +49,7 @@ def test_one_hot_argmax_exact(fmt, n, k, m):
     xbits = oracle.f32_to_bf16_bits(x)
     info = fp4.fp4_dispatch_info()
     idx, val, y = fp4.fp4_w4a16_linear_argmax(x_dev(xbits), pc, ps, n, float(g), fmt, logits=True, info=info)
-    assert info.kernel == decode_kernel(n, k, m)
+    assert info.kernel == decode_kernel(fmt, n, k, m)
     # Logits are bf16(w[:, k_i]) exactly (G is applied after the sum; -0 sums to +0).
     w = oracle.dequantize(packed, scales, k, fmt, g)
     logit_bits = _zero_canon(oracle.f32_to_bf16_bits(np.ascontiguousarray(w[:, ks].T)))

@@ -65,7 +65,7 @@ def test_degenerate_scales(fmt, m, g_mode, k):
     xbits = synth.activations(synth.TINY, m, k)
     info = fp4.fp4_dispatch_info()
     y = y_host(fp4.fp4_w4a16_linear(x_dev(xbits), pc, ps, n, float(g), fmt, info=info))
-    assert info.kernel == (decode_kernel(n, k, m) if m <= 32 else 1)
+    assert info.kernel == (decode_kernel(fmt, n, k, m) if m <= 32 else 1)
     y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
     nan_rows = {NV: (9, 13), MX: (5,)}[fmt]
     assert all(np.isnan(y_ref[:, r]).all() for r in nan_rows)

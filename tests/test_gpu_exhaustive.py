@@ -92,12 +92,13 @@ def run(packed, scales, n, k, fmt, g, cols, kernel, splits=None, grid_x=None):
 
 # (n, m, k, column sets, kernel, split expected): each set is one call;
 # together they cover codes 0..15 (the code of column c is c % 16).  Layers
-# of fewer than 8192 rows with k <= 8192 run the wave-split kernel at m <= 8;
-# the 64-row kernels are reached with 8192 rows or k past 8192.
+# of fewer than 8192 rows with k <= 8192 run the wave-split kernel at m <= 8
+# (MXFP4 at m <= 2 up to 16383 rows); the 64-row kernels are reached with
+# more rows or k past 8192.
 CASES = [
     # VALU GEMV: one or two rows, one column per row.
-    ("gemv m=1", 8192, 1, 32, [[c] for c in range(16)], 0, False),
-    ("gemv m=2", 8192, 2, 32, [[2 * c, 2 * c + 17] for c in range(8)], 0, False),
+    ("gemv m=1", 16384, 1, 32, [[c] for c in range(16)], 0, False),
+    ("gemv m=2", 16384, 2, 32, [[2 * c, 2 * c + 17] for c in range(8)], 0, False),
     # VALU GEMV with k = 8448: three K splits; the ones sit in the second split.
     ("gemv m=1 split", 256, 1, 8448, [[4096 + 37 * c] for c in range(16)], 0, True),
     # MFMA decode, 64-row tiles: 16 rows (one activation group), 32 rows (two), 3 rows.

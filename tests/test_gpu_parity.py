@@ -96,7 +96,7 @@ SHAPES = [
     (NV, 256, 5120),    # k split in two (lm_head's k)
     (NV, 128, 17408),   # many splits (down_proj's k)
     (NV, 640, 9216),    # past the wave-split kernel's 32 K stages: the 64-row kernels, K split
-    (MX, 8192, 1056),   # 128 64-row tiles: the 64-row kernels, unsplit, ragged last stage
+    (MX, 16384, 1056),  # 256 64-row tiles: the 64-row kernels, unsplit, ragged last stage
 ]
 
 
@@ -107,7 +107,7 @@ def test_gemv_matches_oracle(fmt, n, k, m):
     xbits = synth.activations(synth.TINY, m, k)
     info = fp4.fp4_dispatch_info()
     y = _run_linear(packed, scales, g, fmt, n, k, xbits, info)
-    assert info.kernel == decode_kernel(n, k, m)
+    assert info.kernel == decode_kernel(fmt, n, k, m)
     y_ref = oracle.linear(oracle.bf16_bits_to_f32(xbits), packed, scales, k, fmt, g)
     assert_close(y_host(y), y_ref, "gemv fmt=%d n=%d k=%d m=%d" % (fmt, n, k, m))
 
@@ -174,7 +174,7 @@ def test_gate_up_fused_equals_split(fmt, nh, k, m):
 
 
 @pytest.mark.parametrize("fmt,n,k", [(NV, 512, 256), (MX, 384, 3072), (NV, 256, 17408), (NV, 300, 5120),
-                                     (MX, 8192, 1056)])
+                                     (MX, 8192, 1056), (MX, 16384, 1056)])
 def test_gemv_batch_invariance(fmt, n, k):
     # Within one decode kernel, row i of an m-row call equals the same row of
     # a call with more rows, bit for bit (the summation order never depends on
@@ -190,7 +190,7 @@ def test_gemv_batch_invariance(fmt, n, k):
         info = fp4.fp4_dispatch_info()
         ys[m] = y_host_bits(fp4.fp4_w4a16_linear(x_dev(x32[:m]), pc, ps, n, float(g), fmt, info=info))
         kernels[m] = info.kernel
-        assert info.kernel == decode_kernel(n, k, m), m
+        assert info.kernel == decode_kernel(fmt, n, k, m), m
     for m in range(1, 33):
         top = max(q for q in range(1, 33) if kernels[q] == kernels[m])
         assert np.array_equal(ys[m], ys[top][:m]), (m, top)
