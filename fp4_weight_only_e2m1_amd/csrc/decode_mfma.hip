@@ -548,8 +548,12 @@ __device__ __forceinline__ void kw_wait(int s, int s1) {
   }
 }
 
+// One 16-row tile of a wave-split call with mrows <= M activation rows (M when
+// launched per call; the rows of one expert's pass in the grouped MoE
+// launch).  All threads of the workgroup call it; it reuses its stage buffers
+// on the next call only after a workgroup barrier.
 template <int M, int FMT, int NB>
-__global__ __launch_bounds__(kThreads) void decode_kw_kernel(const GemvArgs a) {
+__device__ __forceinline__ void kw_tile(const GemvArgs& a, int64_t tile, int mrows) {
   using C = KwCopier<M, FMT>;
   using S = KwStage<FMT, C::XR>;
   __shared__ S st[kKwWaves][NB];
@@ -558,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void decode_kw_kernel(const GemvArgs a) {
   const int lane = t & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kKwRows;
+  const int64_t row0 = tile * kKwRows;
   const int ksteps = (a.k + kDecodeStageK - 1) / kDecodeStageK;
   const int s0 = wave * ksteps / kKwWaves;
   const int s1 = (wave + 1) * ksteps / kKwWaves;
@@ -566,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void decode_kw_kernel(const GemvArgs a) {
   f32x4_t acc[1][1];
   acc[0][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   S* mine = st[wave];
-  const C cp(a, row0, lane, M);
+  const C cp(a, row0, lane, mrows);
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j)
     if (s0 + j < s1) cp.issue(static_cast<int64_t>(s0 + j) * kDecodeStageK, mine[j]);
@@ -577,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void decode_kw_kernel(const GemvArgs a) {
       if (ss >= s1) break;
       kw_wait<C::kLoads, NB>(ss, s1);
       if (ss + NB - 1 < s1) cp.issue(static_cast<int64_t>(ss + NB - 1) * kDecodeStageK, mine[(j + NB - 1) % NB]);
-      compute_stage<M, FMT, 1, S, C::XR>(mine[j], nullptr, 0, r, g, M, acc);
+      compute_stage<M, FMT, 1, S, C::XR>(mine[j], nullptr, 0, r, g, mrows, acc);
     }
   }
 
@@ -587,47 +591,53 @@ __global__ __launch_bounds__(kThreads) void decode_kw_kernel(const GemvArgs a) {
   float* red = reinterpret_cast<float*>(&mine[0]);
   *reinterpret_cast<f32x4_t*>(red + 4 * lane) = acc[0][0];
   __syncthreads();
-  if (wave != 0) return;
-  f32x4_t sum = acc[0][0];
+  if (wave == 0) {
+    f32x4_t sum = acc[0][0];
 #pragma unroll
-  for (int w = 1; w < kKwWaves; ++w) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(&st[w][0]) + 4 * lane);
-    sum[0] += v[0];
-    sum[1] += v[1];
-    sum[2] += v[2];
-    sum[3] += v[3];
-  }
-  // Lane (r, g) now holds y[4 g + i][row r] (before the global scale).
-  // Greedy-argmax keys: each activation row's maximum over the tile's 16 rows
-  // is taken over the 16 lanes of its group g (a maximum: any order).
-  const int64_t row = row0 + r;
-  int h;
-  const int64_t col = out_col(a, row, h);
-  const float gs = h == 0 ? a.gscale[0] : a.gscale[1];
-  uint64_t best[4] = {0, 0, 0, 0};
-  if (col >= 0) {
+    for (int w = 1; w < kKwWaves; ++w) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(&st[w][0]) + 4 * lane);
+      sum[0] += v[0];
+      sum[1] += v[1];
+      sum[2] += v[2];
+      sum[3] += v[3];
+    }
+    // Lane (r, g) now holds y[4 g + i][row r] (before the global scale).
+    // Greedy-argmax keys: each activation row's maximum over the tile's 16
+    // rows is taken over the 16 lanes of its group g (a maximum: any order).
+    const int64_t row = row0 + r;
+    int h;
+    const int64_t col = out_col(a, row, h);
+    const float gs = h == 0 ? a.gscale[0] : a.gscale[1];
+    uint64_t best[4] = {0, 0, 0, 0};
+    if (col >= 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * g + i;
-      if (m < M) {
-        const uint16_t yb = f32_to_bf16_rne(sum[i] * gs);
-        if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
-        best[i] = argmax_key(yb, col);
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < mrows) {
+          const uint16_t yb = f32_to_bf16_rne(sum[i] * gs);
+          if (a.y) a.y[static_cast<int64_t>(m) * a.ldy + col] = yb;
+          best[i] = argmax_key(yb, col);
+        }
+      }
+    }
+    if (a.keys) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const uint64_t w = shfl_xor_u64(best[i], o);
+          if (w > best[i]) best[i] = w;
+        }
+        const int m = 4 * g + i;
+        if (r == 0 && m < M) a.keys[tile * M + m] = best[i];
       }
     }
   }
-  if (a.keys) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const uint64_t w = shfl_xor_u64(best[i], o);
-        if (w > best[i]) best[i] = w;
-      }
-      const int m = 4 * g + i;
-      if (r == 0 && m < M) a.keys[static_cast<int64_t>(blockIdx.x) * M + m] = best[i];
-    }
-  }
+}
+
+template <int M, int FMT, int NB>
+__global__ __launch_bounds__(kThreads) void decode_kw_kernel(const GemvArgs a) {
+  kw_tile<M, FMT, NB>(a, blockIdx.x, M);
 }
 
 template <int FMT>
@@ -664,15 +674,16 @@ __device__ __forceinline__ void moe_clamped_range(const MoeArgs& moe, int e, int
   p1 = p1 < p0 ? p0 : p1 > moe.pairs ? moe.pairs : p1;
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs base, const MoeArgs moe) {
-  // Find the slot's expert: wave 0 reads the offsets of 256 experts at a time
-  // (4 per lane, loads issued together) and counts those with pairs until it
-  // reaches the slot's; that expert's lane leaves its pair range in LDS.
+// The expert of grid slot `slot`: the slot-th expert (in expert order) that
+// has routed pairs, and its clamped pair range, or e = -1 past the last such
+// expert.  Wave 0 reads the offsets of 256 experts at a time (4 per lane,
+// loads issued together) and counts those with pairs until it reaches the
+// slot's; that expert's lane leaves its pair range in LDS.  All threads call
+// it; the results are workgroup-uniform.
+__device__ __forceinline__ void moe_slot_expert(const MoeArgs& moe, int slot, int& e_out, int& p0_out, int& p1_out) {
   __shared__ int s_expert, s_p0, s_p1;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    const int slot = blockIdx.y;
     int seen = 0, found = -1;
     if (lane == 0) s_expert = -1;
     for (int b = 0; b < moe.experts && found < 0; b += 256) {
@@ -703,12 +714,20 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs bas
     }
   }
   __syncthreads();
-  const int e = __builtin_amdgcn_readfirstlane(s_expert);
-  if (e < 0) return;
   // Workgroup-uniform values: kept in scalar registers (the copy bases built
   // from them must be).
-  const int p0 = __builtin_amdgcn_readfirstlane(s_p0);
-  const int p1 = __builtin_amdgcn_readfirstlane(s_p1);
+  e_out = __builtin_amdgcn_readfirstlane(s_expert);
+  p0_out = __builtin_amdgcn_readfirstlane(s_p0);
+  p1_out = __builtin_amdgcn_readfirstlane(s_p1);
+}
+
+// Grouped MoE decode, 64-row tiles: workgroup (tile, s) runs tile `tile` of
+// the s-th expert with pairs, 8 pairs per pass (decode_tile).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs base, const MoeArgs moe) {
+  int e, p0, p1;
+  moe_slot_expert(moe, blockIdx.y, e, p0, p1);
+  if (e < 0) return;
   GemvArgs a = base;
   a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
   a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
