@@ -46,10 +46,11 @@ int check_m(int m) { return (m < 0 || m > FP4_MAX_M) ? FP4_EINVAL : FP4_OK; }
 // (act) stays on the 64-row kernels, whose tiles hold both rows of an output.
 bool uses_kw(int m, int n_proj, int k, int fmt, bool act) { return !act && fp4::decode_kw_used(n_proj, k, fmt, m); }
 
+// act: the SwiGLU gate_up (never on the wave-split kernel).
 size_t workspace_for(int m, int n_proj, int k, int fmt, int projections, bool act = false) {
-  // Both decode kernels split K across workgroups for some shapes (partials
-  // + flags); the prefill GEMM splits K only for the tail tiles that do not
-  // fill a round.
+  // The VALU GEMV and the 64-row MFMA decode split K across workgroups for
+  // some shapes (partials + flags; the wave-split kernel never does); the
+  // prefill GEMM splits K only for the tail tiles that do not fill a round.
   if (m < 1) return 0;
   const int64_t rows_total = projections * fp4::round_up(n_proj, fp4::kRowAlign);
   if (m > fp4::kDecodeMaxM) return static_cast<size_t>(fp4::gemm_workspace_bytes(fp4::gemm_plan(m, rows_total, k)));
