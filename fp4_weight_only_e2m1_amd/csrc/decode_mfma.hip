@@ -740,6 +740,29 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs bas
   }
 }
 
+// Grouped MoE decode of a single token on the wave-split kernel: workgroup
+// (tile, s) runs 16-row tile `tile` of the s-th expert with pairs, one pair
+// per pass -- each pass exactly fp4_w4a16_linear's m = 1 call on that
+// expert's weight where that call takes the wave-split kernel, so a pair's
+// output equals it bit for bit.  With one token the routing activates few
+// experts (top-k of them), whose 64-row tiles would leave most CUs idle.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void moe_decode_kw_kernel(const GemvArgs base, const MoeArgs moe) {
+  int e, p0, p1;
+  moe_slot_expert(moe, blockIdx.y, e, p0, p1);
+  if (e < 0) return;
+  GemvArgs a = base;
+  a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
+  a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
+  a.gscale[0] = a.gscale[1] = moe.gscales ? moe.gscales[e] : 1.0f;
+  for (int c = p0; c < p1; ++c) {
+    a.x = moe.x_sorted + static_cast<int64_t>(c) * a.k;
+    a.y = base.y + static_cast<int64_t>(c) * a.ldy;
+    kw_tile<1, FMT, kKwBuffers>(a, blockIdx.x, 1);
+    __syncthreads();  // the stage buffers are reused by the next pass
+  }
+}
+
 // x_sorted[p] = x[tokens[p]]: 16-byte chunks, one per thread.  A token id
 // outside [0, tokens_total) gathers a zero row.
 __global__ __launch_bounds__(256) void moe_gather_kernel(const uint16_t* x, const int32_t* tokens, int pairs, int k,
@@ -822,13 +845,21 @@ hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts,
   hipError_t e = launch_moe_gather(x, tokens, moe.pairs, a.k, tokens_total, x_sorted, stream);
   if (e != hipSuccess) return e;
   const int slots = experts < moe.pairs ? experts : moe.pairs;
-  const dim3 grid(static_cast<unsigned>(a.rows_total / kDecodeTileRows), static_cast<unsigned>(slots));
+  // One token: the experts the wave-split kernel takes at m = 1 run on it.
+  const bool kw = tokens_total == 1 && decode_kw_used(a.n_proj, a.k, fmt, 1);
+  const dim3 grid(static_cast<unsigned>(a.rows_total / (kw ? kKwRows : kDecodeTileRows)), static_cast<unsigned>(slots));
   if (grid_out) *grid_out = grid;
   if (block_out) *block_out = dim3(kThreads);
-  if (fmt == kFmtNvfp4)
+  if (kw) {
+    if (fmt == kFmtNvfp4)
+      hipLaunchKernelGGL(moe_decode_kw_kernel<kFmtNvfp4>, grid, dim3(kThreads), 0, stream, a, moe);
+    else
+      hipLaunchKernelGGL(moe_decode_kw_kernel<kFmtMxfp4>, grid, dim3(kThreads), 0, stream, a, moe);
+  } else if (fmt == kFmtNvfp4) {
     hipLaunchKernelGGL(moe_decode_kernel<kFmtNvfp4>, grid, dim3(kThreads), 0, stream, a, moe);
-  else
+  } else {
     hipLaunchKernelGGL(moe_decode_kernel<kFmtMxfp4>, grid, dim3(kThreads), 0, stream, a, moe);
+  }
   return hipGetLastError();
 }
 
