@@ -740,13 +740,15 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs bas
   }
 }
 
-// Grouped MoE decode of a single token on the wave-split kernel: workgroup
-// (tile, s) runs 16-row tile `tile` of the s-th expert with pairs, one pair
-// per pass -- each pass exactly fp4_w4a16_linear's m = 1 call on that
-// expert's weight where that call takes the wave-split kernel, so a pair's
-// output equals it bit for bit.  With one token the routing activates few
-// experts (top-k of them), whose 64-row tiles would leave most CUs idle.
-template <int FMT>
+// Grouped MoE decode of one or two tokens on the wave-split kernel:
+// workgroup (tile, s) runs 16-row tile `tile` of the s-th expert with pairs,
+// up to M pairs per pass (M = the token count: one pass per expert for any
+// routing of distinct experts per token) -- each pass exactly
+// fp4_w4a16_linear's call on that many rows of the expert's weight where that
+// call takes the wave-split kernel, so a pair's output equals it bit for bit.
+// With one or two tokens the routing activates few experts, whose 64-row
+// tiles would leave most CUs idle.
+template <int M, int FMT>
 __global__ __launch_bounds__(kThreads) void moe_decode_kw_kernel(const GemvArgs base, const MoeArgs moe) {
   int e, p0, p1;
   moe_slot_expert(moe, blockIdx.y, e, p0, p1);
@@ -755,10 +757,10 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kw_kernel(const GemvArgs 
   a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
   a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
   a.gscale[0] = a.gscale[1] = moe.gscales ? moe.gscales[e] : 1.0f;
-  for (int c = p0; c < p1; ++c) {
-    a.x = moe.x_sorted + static_cast<int64_t>(c) * a.k;
-    a.y = base.y + static_cast<int64_t>(c) * a.ldy;
-    kw_tile<1, FMT, kKwBuffers>(a, blockIdx.x, 1);
+  for (int c0 = p0; c0 < p1; c0 += M) {
+    a.x = moe.x_sorted + static_cast<int64_t>(c0) * a.k;
+    a.y = base.y + static_cast<int64_t>(c0) * a.ldy;
+    kw_tile<M, FMT, kKwBuffers>(a, blockIdx.x, p1 - c0 < M ? p1 - c0 : M);
     __syncthreads();  // the stage buffers are reused by the next pass
   }
 }
@@ -845,16 +847,20 @@ hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts,
   hipError_t e = launch_moe_gather(x, tokens, moe.pairs, a.k, tokens_total, x_sorted, stream);
   if (e != hipSuccess) return e;
   const int slots = experts < moe.pairs ? experts : moe.pairs;
-  // One token: the experts the wave-split kernel takes at m = 1 run on it.
-  const bool kw = tokens_total == 1 && decode_kw_used(a.n_proj, a.k, fmt, 1);
+  // One or two tokens: the experts the wave-split kernel takes at that m run on it.
+  const bool kw = tokens_total <= 2 && decode_kw_used(a.n_proj, a.k, fmt, tokens_total);
   const dim3 grid(static_cast<unsigned>(a.rows_total / (kw ? kKwRows : kDecodeTileRows)), static_cast<unsigned>(slots));
   if (grid_out) *grid_out = grid;
   if (block_out) *block_out = dim3(kThreads);
   if (kw) {
-    if (fmt == kFmtNvfp4)
-      hipLaunchKernelGGL(moe_decode_kw_kernel<kFmtNvfp4>, grid, dim3(kThreads), 0, stream, a, moe);
+    if (tokens_total == 1 && fmt == kFmtNvfp4)
+      hipLaunchKernelGGL((moe_decode_kw_kernel<1, kFmtNvfp4>), grid, dim3(kThreads), 0, stream, a, moe);
+    else if (tokens_total == 1)
+      hipLaunchKernelGGL((moe_decode_kw_kernel<1, kFmtMxfp4>), grid, dim3(kThreads), 0, stream, a, moe);
+    else if (fmt == kFmtNvfp4)
+      hipLaunchKernelGGL((moe_decode_kw_kernel<2, kFmtNvfp4>), grid, dim3(kThreads), 0, stream, a, moe);
     else
-      hipLaunchKernelGGL(moe_decode_kw_kernel<kFmtMxfp4>, grid, dim3(kThreads), 0, stream, a, moe);
+      hipLaunchKernelGGL((moe_decode_kw_kernel<2, kFmtMxfp4>), grid, dim3(kThreads), 0, stream, a, moe);
   } else if (fmt == kFmtNvfp4) {
     hipLaunchKernelGGL(moe_decode_kernel<kFmtNvfp4>, grid, dim3(kThreads), 0, stream, a, moe);
   } else {

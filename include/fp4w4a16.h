@@ -316,14 +316,15 @@ int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k,
  * table can make the kernels access memory outside these buffers.  Two
  * launches: a gather of the pairs' x rows, then one workgroup per (row tile,
  * expert with pairs) on the matrix cores: the m = 3..8 decode kernel on
- * 64-row tiles, up to 8 pairs of an expert per pass; with a single token
- * (tokens = 1), on experts the wave-split kernel takes at m = 1, that kernel
- * on 16-row tiles, one pair per pass, each pair's output then equal to
- * fp4_w4a16_linear's m = 1 output on its expert's weight bit for bit.  The
+ * 64-row tiles, up to 8 pairs of an expert per pass; with one or two tokens
+ * (tokens <= 2), on experts the wave-split kernel takes at m = tokens, that
+ * kernel on 16-row tiles, up to `tokens` pairs per pass, each pair's output
+ * then equal to fp4_w4a16_linear's output for that token on its expert's
+ * weight bit for bit (when the expert's pairs are the same tokens).  The
  * grid has min(experts, pairs) expert slots, enough for every expert with
  * pairs when the offsets are non-decreasing (with other tables some experts
  * may be skipped); dispatch info kernel 3, grid_x = row tiles.  The sum order
- * of an output depends only on (n, k, fmt) and on whether tokens is 1: a
+ * of an output depends only on (n, k, fmt) and on whether tokens <= 2: a
  * pair's result does not depend on the other pairs.
  * Cite: "MXFP4 decode-graph + gate_up FUSION default-ON" (vllm.cpp PR #54),
  * the later commit on the dense-template marlin port: the dense projections

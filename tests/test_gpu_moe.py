@@ -42,16 +42,16 @@ def _i32(a):
 
 
 def _moe_tile_rows(tokens, n, k):
-    # A single token's experts run on the wave-split kernel (16-row tiles)
+    # The experts of one or two tokens run on the wave-split kernel (16-row tiles)
     # where it takes them (fewer than 128 64-row tiles, at most 32 K stages of
     # 256); otherwise 64-row tiles.
     small = -(-n // 256) * 256 // 64 < 128 and -(-k // 256) <= 32
-    return 16 if tokens == 1 and small else 64
+    return 16 if tokens <= 2 and small else 64
 
 
 @pytest.mark.parametrize("fmt,n,k", [(NV, 768, 2048), (MX, 300, 1056), (NV, 520, 4096), (MX, 1024, 512),
                                      (MX, 300, 8448)])
-@pytest.mark.parametrize("tokens,experts,topk", [(1, 16, 4), (4, 16, 4), (8, 32, 8), (8, 4, 3)])
+@pytest.mark.parametrize("tokens,experts,topk", [(1, 16, 4), (2, 16, 4), (4, 16, 4), (8, 32, 8), (8, 4, 3)])
 def test_moe_decode_matches_oracle(fmt, n, k, tokens, experts, topk):
     host, pc, ps, gs = _stacked(experts, n, k, fmt, 0)
     offsets, ptok = _routing(tokens, experts, topk, seed=tokens * 100 + experts)
@@ -82,13 +82,15 @@ def test_moe_many_experts(fmt, tokens, experts, topk):
     assert_close(y_host(y), y_ref, "moe many experts E=%d" % experts)
 
 
-@pytest.mark.parametrize("fmt,n,k,experts,topk", [(NV, 1536, 2048, 24, 8), (MX, 300, 1056, 16, 5)])
-def test_moe_decode_one_token_equals_linear_per_expert(fmt, n, k, experts, topk):
-    # One token: each routed pair runs on the wave-split kernel as the m = 1
-    # fp4_w4a16_linear call on its expert's weight does, bit for bit.
+@pytest.mark.parametrize("fmt,n,k,experts,topk,tokens", [(NV, 1536, 2048, 24, 8, 1), (MX, 300, 1056, 16, 5, 1),
+                                                          (NV, 1536, 2048, 24, 8, 2), (MX, 300, 1056, 6, 5, 2)])
+def test_moe_decode_few_tokens_equals_linear_per_expert(fmt, n, k, experts, topk, tokens):
+    # One or two tokens: each expert's pairs run on the wave-split kernel as
+    # the fp4_w4a16_linear call on its expert's weight and those tokens does,
+    # bit for bit.
     host, pc, ps, gs = _stacked(experts, n, k, fmt, 21)
-    offsets, ptok = _routing(1, experts, topk, seed=77)
-    xbits = synth.activations(synth.TINY, 1, k)
+    offsets, ptok = _routing(tokens, experts, topk, seed=77)
+    xbits = synth.activations(synth.TINY, tokens, k)
     xd = x_dev(xbits)
     info = fp4.fp4_dispatch_info()
     y = y_host_bits(fp4.fp4_w4a16_moe_decode(xd, pc, ps, n, experts, gs if fmt == NV else None, fmt, _i32(offsets),
@@ -96,12 +98,14 @@ def test_moe_decode_one_token_equals_linear_per_expert(fmt, n, k, experts, topk)
     assert info.kernel == 3 and info.grid_x == -(-n // 256) * 256 // 16
     cb, sb = fp4.fp4_prepared_bytes(n, k, fmt)
     for e in range(experts):
-        for p in range(offsets[e], offsets[e + 1]):
-            ye = y_host_bits(fp4.fp4_w4a16_linear(xd, pc[e * cb:(e + 1) * cb], ps[e * sb:(e + 1) * sb], n,
-                                                  float(host[e][2]), fmt))
-            assert np.array_equal(y[p], ye[0]), (e, p)
+        toks = ptok[offsets[e]:offsets[e + 1]]
+        if len(toks) == 0:
+            continue
+        ye = y_host_bits(fp4.fp4_w4a16_linear(x_dev(xbits[toks]), pc[e * cb:(e + 1) * cb], ps[e * sb:(e + 1) * sb], n,
+                                              float(host[e][2]), fmt))
+        assert np.array_equal(y[offsets[e]:offsets[e + 1]], ye), e
     y_ref = oracle.moe_decode(oracle.bf16_bits_to_f32(xbits), host, k, fmt, offsets, ptok)
-    assert_close(oracle.bf16_bits_to_f32(y).astype(np.float64), y_ref, "moe one token")
+    assert_close(oracle.bf16_bits_to_f32(y).astype(np.float64), y_ref, "moe few tokens")
 
 
 def test_moe_pairs_independent_and_long_expert():
