@@ -440,3 +440,20 @@ def test_w4a4_nvfp4_sizes_and_argument_checks(lib):
     assert lib.fp4_quantize_act_nvfp4(None, 0, 64, ctypes.c_float(1.0), None, None, None) == ST["OK"]
     assert lib.fp4_w4a4_nvfp4_gate_up(FAKE, 4, 256, FAKE, FAKE, (1 << 23) + 1, 1.0, 1.0, 0.01, FAKE, FAKE, 1 << 30,
                                       None, None) == ST["EINVAL"]
+
+
+def test_decode_dispatch_rule_over_a_grid():
+    # The decode kernel fp4_plan reports (the one the calls take, checked on
+    # the GPU by test_gpu_plan) against the rule the GPU tests restate
+    # (gpu_util.decode_kernel), over rows, k, formats, m and both layouts.
+    from gpu_util import decode_kernel
+    for fmt in (NV, MX):
+        for n in (17, 300, 2048, 5120, 7936, 8192, 12288, 16128, 16384, 131072):
+            for k in (32, 544, 1056, 6144, 8192, 8448, 17408):
+                for m in (1, 2, 3, 4, 8, 9, 16, 32):
+                    for proj in (1, 2):
+                        p = fp4.fp4_plan(m, n, k, fmt, proj, 256)
+                        assert p.kernel == decode_kernel(fmt, n, k, m), (fmt, n, k, m, proj, p.as_dict())
+                        if p.kernel == 6:
+                            assert (p.splits, p.grid_x, p.block) == (1, proj * (-(-n // 256) * 256) // 16, 256)
+                            assert fp4.fp4_workspace_bytes(m, n, k, fmt, proj) == 0
