@@ -57,7 +57,7 @@ size_t workspace_for(int m, int n_proj, int k, int fmt, int projections, bool ac
   if (uses_kw(m, n_proj, k, fmt, act)) return 0;
   const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
   const int splits = on_mfma ? fp4::decode_mfma_splits(n_proj, k) : fp4::gemv_splits(n_proj, k, fmt);
-  const int tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(rows_total, m)
+  const int tile_rows = on_mfma ? fp4::decode_mfma_tile_rows(rows_total, m, splits)
                                 : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
   return static_cast<size_t>(fp4::decode_workspace_bytes(splits, m, rows_total, tile_rows));
 }
@@ -110,9 +110,10 @@ int noalloc_scratch(void** out) {
   return FP4_OK;
 }
 
-// Rows per workgroup of the 64-row-family decode kernel m selects (m = 1..32).
-int decode_tile_rows(int m, int64_t rows_total) {
-  return m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_tile_rows(rows_total, m)
+// Rows per workgroup of the 64-row-family decode kernel m selects (m = 1..32)
+// for a call of `splits` K splits.
+int decode_tile_rows(int m, int64_t rows_total, int splits) {
+  return m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_tile_rows(rows_total, m, splits)
                                    : fp4::kGemvTeams * fp4::gemv_rows_per_team(rows_total);
 }
 
@@ -122,7 +123,8 @@ size_t argmax_workspace_for(int m, int n, int k, int fmt, size_t* keys_offset) {
   const size_t base = fp4::round_up(static_cast<int64_t>(workspace_for(m, n, k, fmt, 1)), 256);
   const int64_t rows_total = fp4::round_up(n, fp4::kRowAlign);
   if (keys_offset) *keys_offset = base;
-  const int tile_rows = uses_kw(m, n, k, fmt, false) ? fp4::kKwRows : decode_tile_rows(m, rows_total);
+  const int splits = m >= fp4::kDecodeMfmaMinM ? fp4::decode_mfma_splits(n, k) : fp4::gemv_splits(n, k, fmt);
+  const int tile_rows = uses_kw(m, n, k, fmt, false) ? fp4::kKwRows : decode_tile_rows(m, rows_total, splits);
   return base + static_cast<size_t>(rows_total / tile_rows) * m * 8;
 }
 
@@ -192,7 +194,7 @@ int run_linear(const uint16_t* x, int m, int k, const uint8_t* codes, const uint
     a.gscale[0] = mx ? 1.0f : gscales[0];
     a.gscale[1] = mx ? 1.0f : gscales[projections > 1 ? 1 : 0];
     a.act = act;
-    a.tile_rows = kw ? fp4::kKwRows : decode_tile_rows(m, a.rows_total);
+    a.tile_rows = kw ? fp4::kKwRows : decode_tile_rows(m, a.rows_total, a.splits);
     if (on_mfma && !kw && a.tile_rows != fp4::kDecodeTileRows && a.splits != 1) return FP4_EINVAL;
     if (a.splits > 1) {
       a.flags = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) +
@@ -519,8 +521,9 @@ int fp4_plan(int m, int n, int k, int fmt, int projections, int cus, fp4_dispatc
     }
     const bool on_mfma = m >= fp4::kDecodeMfmaMinM;
     const int splits = on_mfma ? fp4::decode_mfma_splits(n, k) : fp4::gemv_splits(n, k, fmt);
-    *info_out = fp4_dispatch_info{on_mfma ? 2 : 0, splits, static_cast<int>(rows_total / decode_tile_rows(m, rows_total)),
-                                  splits, fp4::kDecodeThreads, 0};
+    const int tile_rows = decode_tile_rows(m, rows_total, splits);
+    const int threads = on_mfma && tile_rows == 96 ? 384 : fp4::kDecodeThreads;  // 96-row tiles: six waves
+    *info_out = fp4_dispatch_info{on_mfma ? 2 : 0, splits, static_cast<int>(rows_total / tile_rows), splits, threads, 0};
     return FP4_OK;
   }
   const int xcds = fp4::xcds_of(cus);

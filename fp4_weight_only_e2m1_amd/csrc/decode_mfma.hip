@@ -20,6 +20,12 @@
 //   scales  of those codes       (1 KiB)
 // A wave then reads, per 128-code block, one 16-byte code chunk per lane,
 // decodes its 4 words and issues 4 MFMAs against x fragments read from LDS.
+// The same code serves two other tile shapes (decode_mfma_tile_rows):
+// 128-row tiles, whose waves own two 16-row blocks each (every x fragment
+// read from LDS feeds two MFMAs), and 96-row tiles of six waves, launched
+// where 64-row tiles would give CUs unequal workgroup counts (the 24576-row
+// fused gate_up: 256 workgroups, one per CU, instead of 384); there waves
+// 0..3 copy x and the others the scales, and MXFP4 keeps 4 stage buffers.
 //
 // Lane l handles row r = l % 16 of the wave's rows and the 32-code segment
 // g = l / 16 of a 128-code block.  Word c (8 codes) of the lane's chunk is the
@@ -62,29 +68,36 @@ constexpr int kXRows = M > 16 ? 32 : M > 8 ? 16 : 8;
 template <int M>
 constexpr int kGroups = M > 16 ? 2 : 1;
 
-// Tile geometry for RB row blocks of 16 per wave (a 64 RB-row tile) and XR
-// staged x rows.
-template <int RB, int FMT, int XR>
+// Tile geometry for W waves of RB row blocks of 16 (a 16 RB W-row tile) and
+// XR staged x rows.  Every lane copies 2 RB code chunks per stage; the x
+// chunks are copied one per lane by the first kXWaves waves (all of them
+// when there are at least as many chunks as lanes), and the scale chunks by
+// kSWaves waves from kSWave0 on -- waves without x copies where there are
+// enough of those, so that the copies per wave stay even.
+template <int RB, int FMT, int XR, int W>
 struct Geo {
-  static constexpr int kXChunks = XR * kStageK * 2 / 16;  // 256 or 512 x chunks per stage
-  static constexpr int kXPer = kXChunks / kThreads;        // x copies per lane: 1 or 2
-  static constexpr int kRows = 64 * RB;
-  static constexpr int kWChunks = kRows * kStageK / 2 / 16;  // 512 RB code chunks per stage
-  static constexpr int kWPer = kWChunks / kThreads;           // 2 RB copies per lane
+  static constexpr int kThr = 64 * W;
+  static constexpr int kXChunks = XR * kStageK * 2 / 16;  // 256, 512 or 1024 x chunks per stage
+  static constexpr int kXWaves = kXChunks >= kThr ? W : kXChunks / 64;
+  static constexpr int kXPer = kXChunks / (64 * kXWaves);  // x copies per lane of those waves
+  static constexpr int kRows = 16 * RB * W;
+  static constexpr int kWChunks = kRows * kStageK / 2 / 16;  // code chunks per stage
+  static constexpr int kWPer = kWChunks / kThr;               // 2 RB copies per lane
   static constexpr int P = scales_per_seg(FMT);
-  static constexpr int kSReal = 32 * P * RB;                  // scale chunks of a stage
-  static constexpr int kSWaves = kSReal > 64 ? kSReal / 64 : 1;  // waves that copy them
+  static constexpr int kSReal = 8 * P * RB * W;               // scale chunks of a stage
+  static constexpr int kSWaves = (kSReal + 63) / 64;          // waves that copy them
+  static constexpr int kSWave0 = W - kXWaves >= kSWaves ? W - kSWaves : 0;
   static constexpr int kSChunks = 64 * kSWaves;               // incl. unused duplicates
-  // Load-to-LDS copies per lane per stage: codes and x, plus one scale chunk
-  // in waves < kSWaves.
-  static constexpr int kLoads = kWPer + kXPer;
+  static_assert(kXChunks % (64 * kXWaves) == 0 && kWChunks % kThr == 0, "copy split");
+  __device__ static constexpr bool has_x(int wave) { return kXWaves == W || wave < kXWaves; }
+  __device__ static constexpr bool has_s(int wave) { return wave >= kSWave0 && wave < kSWave0 + kSWaves; }
 };
 
-template <int RB, int FMT, int XR>
+template <int RB, int FMT, int XR, int W>
 struct alignas(16) Stage {
-  uint4 w[Geo<RB, FMT, XR>::kWChunks];
-  uint4 x[Geo<RB, FMT, XR>::kXChunks];
-  uint4 s[Geo<RB, FMT, XR>::kSChunks];
+  uint4 w[Geo<RB, FMT, XR, W>::kWChunks];
+  uint4 x[Geo<RB, FMT, XR, W>::kXChunks];
+  uint4 s[Geo<RB, FMT, XR, W>::kSChunks];
 };
 
 union Frag {
@@ -104,13 +117,22 @@ __device__ __forceinline__ int w_slot(int rr, int c) { return rr * 8 + (c ^ ((rr
 // slot ch ^ xr: the rows read together hit distinct bank groups.
 __device__ __forceinline__ int x_slot(int xr, int ch) { return xr * 32 + (ch ^ xr); }
 
-template <int RB, int FMT, int XR, int STAGES>
+// Wait until this wave's copies of all but the STAGES youngest stages have
+// landed, then join the workgroup barrier.
+template <int RB, int FMT, int XR, int W, int STAGES>
 __device__ __forceinline__ void wait_stages_barrier(int wave) {
-  using G = Geo<RB, FMT, XR>;
-  if (wave < G::kSWaves)
-    wait_vm_barrier<STAGES * (G::kLoads + 1)>();
-  else
-    wait_vm_barrier<STAGES * G::kLoads>();
+  using G = Geo<RB, FMT, XR, W>;
+  if (G::has_x(wave)) {
+    if (G::has_s(wave))
+      wait_vm_barrier<STAGES * (G::kWPer + G::kXPer + 1)>();
+    else
+      wait_vm_barrier<STAGES * (G::kWPer + G::kXPer)>();
+  } else {
+    if (G::has_s(wave))
+      wait_vm_barrier<STAGES * (G::kWPer + 1)>();
+    else
+      wait_vm_barrier<STAGES * G::kWPer>();
+  }
 }
 
 // The stage copies of one workgroup: 32-bit lane offsets from wave-uniform
@@ -120,10 +142,10 @@ __device__ __forceinline__ void wait_stages_barrier(int wave) {
 // code rows: every code row then holds at least 32 zero codes from code k on.
 // Code chunks are fetched with the non-temporal hint (read once); x and the
 // scales with the default policy.
-template <int M, int FMT, int RB>
+template <int M, int FMT, int RB, int W>
 struct Copier {
   static constexpr int XR = kXRows<M>;
-  using G = Geo<RB, FMT, XR>;
+  using G = Geo<RB, FMT, XR, W>;
   static constexpr int P = G::P;
   const uint16_t* x;
   const uint8_t* ct;     // code row row0
@@ -133,7 +155,8 @@ struct Copier {
   int xk[G::kXPer];      // first code of this lane's x chunks within a stage
   bool xrow_ok[G::kXPer];
   int k;
-  uint32_t lds_wave;     // this wave's 1 KiB slice of a stage area
+  uint32_t lds_wave;     // this wave's 1 KiB slice of the code and x areas
+  uint32_t lds_swave;    // this wave's 1 KiB slice of the scale area
 
   __device__ __forceinline__ Copier(const GemvArgs& a, int64_t row0, int t, int wave, int mrows) {
     const int64_t row_bytes = a.k_pad / 2;
@@ -144,46 +167,50 @@ struct Copier {
     zeros = ct + a.k / 2;
 #pragma unroll
     for (int i = 0; i < G::kWPer; ++i) {
-      const int p = i * kThreads + t;
+      const int p = i * G::kThr + t;
       const int rr = p >> 3;
       const int c = (p & 7) ^ ((rr >> 1) & 7);
       woff[i] = static_cast<uint32_t>(rr * row_bytes + 16 * c);
     }
 #pragma unroll
     for (int i = 0; i < G::kXPer; ++i) {
-      const int p = i * kThreads + t;
+      const int p = i * 64 * G::kXWaves + t;
       const int xr = p >> 5;
       const int ch = (p & 31) ^ xr;
       xrow_ok[i] = xr < mrows;
       xoff[i] = xrow_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
       xk[i] = 8 * ch;
     }
-    // Scales of a stage: 4 RB row groups x 8 segments x 16 rows x P bytes,
+    // Scales of a stage: RB W row groups x 8 segments x 16 rows x P bytes,
     // 128 P contiguous bytes per row group (cpg chunks).  Lane l of scale
-    // wave w lands at chunk 64 w + l of the stage's scale area and fetches
-    // chunk (64 w + l) mod kSReal; when kSReal < 64 (MXFP4, 64-row tiles) the
-    // upper lanes fetch duplicates into unused chunks.
+    // wave kSWave0 + v lands at chunk 64 v + l of the stage's scale area and
+    // fetches chunk (64 v + l) mod kSReal; where kSReal is not a multiple of
+    // 64 the upper lanes fetch duplicates into unused chunks.
     const int lane = t & 63;
     const int cpg = 8 * P;
-    const int q = (64 * (wave < G::kSWaves ? wave : 0) + lane) % G::kSReal;
+    const int sv = G::has_s(wave) ? wave - G::kSWave0 : 0;
+    const int q = (64 * sv + lane) % G::kSReal;
     soff = static_cast<uint32_t>((q / cpg) * a.ksegs * kRowGroup * P + 16 * (q % cpg));
     lds_wave = 64 * 16 * wave;
+    lds_swave = 64 * 16 * sv;
   }
 
-  __device__ __forceinline__ void issue(int64_t k0, Stage<RB, FMT, XR>& sb, int wave) const {
+  __device__ __forceinline__ void issue(int64_t k0, Stage<RB, FMT, XR, W>& sb, int wave) const {
     const uint32_t lw = lds_addr(sb.w) + lds_wave;
     const uint8_t* cb = ct + k0 / 2;
 #pragma unroll
-    for (int i = 0; i < G::kWPer; ++i) copy16_sbase_nt(cb, woff[i], lw + i * kThreads * 16);
+    for (int i = 0; i < G::kWPer; ++i) copy16_sbase_nt(cb, woff[i], lw + i * G::kThr * 16);
+    if (G::has_x(wave)) {
 #pragma unroll
-    for (int i = 0; i < G::kXPer; ++i) {
-      const bool in_k = k0 + xk[i] < k;
-      const void* xs = !xrow_ok[i] ? static_cast<const void*>(x)
-                       : in_k      ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff[i])
-                                   : static_cast<const void*>(zeros);
-      copy16_vaddr(xs, lds_addr(sb.x) + lds_wave + i * kThreads * 16);
+      for (int i = 0; i < G::kXPer; ++i) {
+        const bool in_k = k0 + xk[i] < k;
+        const void* xs = !xrow_ok[i] ? static_cast<const void*>(x)
+                         : in_k      ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff[i])
+                                     : static_cast<const void*>(zeros);
+        copy16_vaddr(xs, lds_addr(sb.x) + lds_wave + i * 64 * G::kXWaves * 16);
+      }
     }
-    if (wave < G::kSWaves) copy16_sbase(st + (k0 / 32) * kRowGroup * P, soff, lds_addr(sb.s) + lds_wave);
+    if (G::has_s(wave)) copy16_sbase(st + (k0 / 32) * kRowGroup * P, soff, lds_addr(sb.s) + lds_swave);
   }
 };
 
@@ -280,39 +307,40 @@ __device__ __forceinline__ void compute_stage(const StageT& sb, const uint4* zro
 
 // Wait until stage s has landed -- with NB buffers, up to NB - 2 younger
 // stages stay in flight -- and join the workgroup barrier.
-template <int RB, int FMT, int XR, int NB>
+template <int RB, int FMT, int XR, int W, int NB>
 __device__ __forceinline__ void wait_for_stage(int s, int s1, int wave) {
   if constexpr (NB > 2) {
     if (s + NB - 2 < s1) {
-      wait_stages_barrier<RB, FMT, XR, NB - 2>(wave);
+      wait_stages_barrier<RB, FMT, XR, W, NB - 2>(wave);
       return;
     }
-    wait_for_stage<RB, FMT, XR, NB - 1>(s, s1, wave);
+    wait_for_stage<RB, FMT, XR, W, NB - 1>(s, s1, wave);
   } else {
-    wait_stages_barrier<RB, FMT, XR, 0>(wave);
+    wait_stages_barrier<RB, FMT, XR, W, 0>(wave);
   }
 }
 
 // Step for stage s in buffer `cur`: wait for it at the workgroup barrier,
 // refill the buffer consumed one step ago (`prev`; every wave is past it)
 // with stage s + NB - 1, consume `cur`.
-template <int M, int FMT, int RB, int NB>
-__device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB>& cp, int s, int s1,
-                                              const Stage<RB, FMT, kXRows<M>>& cur, Stage<RB, FMT, kXRows<M>>& prev,
-                                              const uint4* zrow, int wave, int r, int g, int mrows,
-                                              f32x4_t (&acc)[RB][kGroups<M>]) {
-  wait_for_stage<RB, FMT, kXRows<M>, NB>(s, s1, wave);
+template <int M, int FMT, int RB, int NB, int W>
+__device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB, W>& cp, int s, int s1,
+                                              const Stage<RB, FMT, kXRows<M>, W>& cur,
+                                              Stage<RB, FMT, kXRows<M>, W>& prev, const uint4* zrow, int wave, int r,
+                                              int g, int mrows, f32x4_t (&acc)[RB][kGroups<M>]) {
+  wait_for_stage<RB, FMT, kXRows<M>, W, NB>(s, s1, wave);
   if (s + NB - 1 < s1) cp.issue(static_cast<int64_t>(s + NB - 1) * kStageK, prev, wave);
   compute_stage<M, FMT, RB>(cur, zrow, wave, r, g, mrows, acc);
 }
 
 // One (tile, split) of a decode call with mrows <= M activation rows (M when
-// launched per call; the rows of one expert in the grouped MoE launch).
-template <int M, int FMT, int RB, int NB>
+// launched per call; the rows of one expert in the grouped MoE launch), on a
+// workgroup of W waves.
+template <int M, int FMT, int RB, int NB, int W>
 __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int split, int mrows) {
-  __shared__ Stage<RB, FMT, kXRows<M>> st[NB];
+  __shared__ Stage<RB, FMT, kXRows<M>, W> st[NB];
   __shared__ ZeroRow zero_row;
-  constexpr int kRows = Geo<RB, FMT, kXRows<M>>::kRows;
+  constexpr int kRows = Geo<RB, FMT, kXRows<M>, W>::kRows;
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -331,7 +359,7 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
 #pragma unroll
     for (int j = 0; j < J; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (t < 32) zero_row.z[t] = make_uint4(0u, 0u, 0u, 0u);  // visible after the first stage barrier
-  const Copier<M, FMT, RB> cp(a, row0, t, wave, mrows);
+  const Copier<M, FMT, RB, W> cp(a, row0, t, wave, mrows);
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j)
     if (s0 + j < s1) cp.issue(static_cast<int64_t>(s0 + j) * kStageK, st[j], wave);
@@ -339,8 +367,8 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (s + j >= s1) break;
-      pipeline_step<M, FMT, RB, NB>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g, mrows,
-                                    acc);
+      pipeline_step<M, FMT, RB, NB, W>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g,
+                                       mrows, acc);
     }
   }
 
@@ -429,9 +457,9 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
   splitk_finish<M>(a, tile, split);
 }
 
-template <int M, int FMT, int RB, int NB>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const GemvArgs a) {
-  decode_tile<M, FMT, RB, NB>(a, blockIdx.x, blockIdx.y, M);
+template <int M, int FMT, int RB, int NB, int W>
+__global__ __launch_bounds__(64 * W) void decode_mfma_kernel(const GemvArgs a) {
+  decode_tile<M, FMT, RB, NB, W>(a, blockIdx.x, blockIdx.y, M);
 }
 
 // ---------------------------------------------------------------------------
@@ -735,7 +763,7 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs bas
   for (int c0 = p0; c0 < p1; c0 += kGemvMaxM) {
     a.x = moe.x_sorted + static_cast<int64_t>(c0) * a.k;
     a.y = base.y + static_cast<int64_t>(c0) * a.ldy;
-    decode_tile<kGemvMaxM, FMT, 1, kDecodeBuffers>(a, blockIdx.x, 0, p1 - c0 < kGemvMaxM ? p1 - c0 : kGemvMaxM);
+    decode_tile<kGemvMaxM, FMT, 1, kDecodeBuffers, 4>(a, blockIdx.x, 0, p1 - c0 < kGemvMaxM ? p1 - c0 : kGemvMaxM);
     __syncthreads();  // the stage buffers are reused by the next pass
   }
 }
@@ -783,52 +811,59 @@ __global__ __launch_bounds__(256) void moe_gather_kernel(const uint16_t* x, cons
       *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(tok) * k + 8 * c);
 }
 
-template <int FMT, int RB>
-hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
-  const dim3 block(kThreads);
-  constexpr int NB = kDecodeBuffers;
-  switch (a.m) {
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, FMT, RB, NB>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, FMT, RB, NB>), grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, FMT, RB, NB>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, FMT, RB, NB>), grid, block, 0, stream, a); break;
-    case 7: hipLaunchKernelGGL((decode_mfma_kernel<7, FMT, RB, NB>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, FMT, RB, NB>), grid, block, 0, stream, a); break;
-    default:
-      // m = 9..32 (16- and 32-row x stages) run on 64-row tiles only.
-      if constexpr (RB == 1) {
-        switch (a.m) {
-          case 9: hipLaunchKernelGGL((decode_mfma_kernel<9, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 10: hipLaunchKernelGGL((decode_mfma_kernel<10, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 11: hipLaunchKernelGGL((decode_mfma_kernel<11, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 12: hipLaunchKernelGGL((decode_mfma_kernel<12, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 13: hipLaunchKernelGGL((decode_mfma_kernel<13, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 14: hipLaunchKernelGGL((decode_mfma_kernel<14, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 15: hipLaunchKernelGGL((decode_mfma_kernel<15, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 16: hipLaunchKernelGGL((decode_mfma_kernel<16, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 17: hipLaunchKernelGGL((decode_mfma_kernel<17, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 18: hipLaunchKernelGGL((decode_mfma_kernel<18, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 19: hipLaunchKernelGGL((decode_mfma_kernel<19, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 20: hipLaunchKernelGGL((decode_mfma_kernel<20, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 21: hipLaunchKernelGGL((decode_mfma_kernel<21, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 22: hipLaunchKernelGGL((decode_mfma_kernel<22, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 23: hipLaunchKernelGGL((decode_mfma_kernel<23, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 24: hipLaunchKernelGGL((decode_mfma_kernel<24, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 25: hipLaunchKernelGGL((decode_mfma_kernel<25, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 26: hipLaunchKernelGGL((decode_mfma_kernel<26, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 27: hipLaunchKernelGGL((decode_mfma_kernel<27, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 28: hipLaunchKernelGGL((decode_mfma_kernel<28, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 29: hipLaunchKernelGGL((decode_mfma_kernel<29, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 30: hipLaunchKernelGGL((decode_mfma_kernel<30, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 31: hipLaunchKernelGGL((decode_mfma_kernel<31, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          case 32: hipLaunchKernelGGL((decode_mfma_kernel<32, FMT, RB, NB>), grid, block, 0, stream, a); break;
-          default: return hipErrorInvalidValue;
-        }
-      } else {
-        return hipErrorInvalidValue;
-      }
-  }
+// Launch of the m-row instance on tiles of RB 16-row blocks per wave and W
+// waves: m = 3..32 on 64-row tiles (RB = 1, W = 4), m = 3..8 on 96-row (RB =
+// 1, W = 6) and 128-row (RB = 2, W = 4) tiles.
+template <int M, int FMT, int RB, int W>
+hipError_t launch_m(const GemvArgs& a, dim3 grid, hipStream_t stream) {
+  constexpr int NB = W == 6 ? decode_buffers_96(FMT) : kDecodeBuffers;
+  hipLaunchKernelGGL((decode_mfma_kernel<M, FMT, RB, NB, W>), grid, dim3(64 * W), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int FMT, int RB, int W>
+hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
+  switch (a.m) {
+    case 3: return launch_m<3, FMT, RB, W>(a, grid, stream);
+    case 4: return launch_m<4, FMT, RB, W>(a, grid, stream);
+    case 5: return launch_m<5, FMT, RB, W>(a, grid, stream);
+    case 6: return launch_m<6, FMT, RB, W>(a, grid, stream);
+    case 7: return launch_m<7, FMT, RB, W>(a, grid, stream);
+    case 8: return launch_m<8, FMT, RB, W>(a, grid, stream);
+    default:
+      break;
+  }
+  if constexpr (RB == 1 && W == 4) {
+    switch (a.m) {
+      case 9: return launch_m<9, FMT, RB, W>(a, grid, stream);
+      case 10: return launch_m<10, FMT, RB, W>(a, grid, stream);
+      case 11: return launch_m<11, FMT, RB, W>(a, grid, stream);
+      case 12: return launch_m<12, FMT, RB, W>(a, grid, stream);
+      case 13: return launch_m<13, FMT, RB, W>(a, grid, stream);
+      case 14: return launch_m<14, FMT, RB, W>(a, grid, stream);
+      case 15: return launch_m<15, FMT, RB, W>(a, grid, stream);
+      case 16: return launch_m<16, FMT, RB, W>(a, grid, stream);
+      case 17: return launch_m<17, FMT, RB, W>(a, grid, stream);
+      case 18: return launch_m<18, FMT, RB, W>(a, grid, stream);
+      case 19: return launch_m<19, FMT, RB, W>(a, grid, stream);
+      case 20: return launch_m<20, FMT, RB, W>(a, grid, stream);
+      case 21: return launch_m<21, FMT, RB, W>(a, grid, stream);
+      case 22: return launch_m<22, FMT, RB, W>(a, grid, stream);
+      case 23: return launch_m<23, FMT, RB, W>(a, grid, stream);
+      case 24: return launch_m<24, FMT, RB, W>(a, grid, stream);
+      case 25: return launch_m<25, FMT, RB, W>(a, grid, stream);
+      case 26: return launch_m<26, FMT, RB, W>(a, grid, stream);
+      case 27: return launch_m<27, FMT, RB, W>(a, grid, stream);
+      case 28: return launch_m<28, FMT, RB, W>(a, grid, stream);
+      case 29: return launch_m<29, FMT, RB, W>(a, grid, stream);
+      case 30: return launch_m<30, FMT, RB, W>(a, grid, stream);
+      case 31: return launch_m<31, FMT, RB, W>(a, grid, stream);
+      case 32: return launch_m<32, FMT, RB, W>(a, grid, stream);
+      default:
+        break;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -880,13 +915,16 @@ hipError_t launch_decode_kw(const GemvArgs& a, int fmt, hipStream_t stream, dim3
 }
 
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid_out, dim3* block_out) {
-  if (a.tile_rows != 64 && a.tile_rows != 128) return hipErrorInvalidValue;
+  if (a.tile_rows != 64 && a.tile_rows != 96 && a.tile_rows != 128) return hipErrorInvalidValue;
+  if (a.rows_total % a.tile_rows != 0 || (a.tile_rows != 64 && (a.splits != 1 || a.m > 8))) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(a.rows_total / a.tile_rows), static_cast<unsigned>(a.splits));
+  const int waves = a.tile_rows == 96 ? 6 : 4;
   if (grid_out) *grid_out = grid;
-  if (block_out) *block_out = dim3(kThreads);
-  if (a.tile_rows == 128)
-    return fmt == kFmtNvfp4 ? launch_fmt<kFmtNvfp4, 2>(a, grid, stream) : launch_fmt<kFmtMxfp4, 2>(a, grid, stream);
-  return fmt == kFmtNvfp4 ? launch_fmt<kFmtNvfp4, 1>(a, grid, stream) : launch_fmt<kFmtMxfp4, 1>(a, grid, stream);
+  if (block_out) *block_out = dim3(64 * waves);
+  const bool nv = fmt == kFmtNvfp4;
+  if (a.tile_rows == 128) return nv ? launch_fmt<kFmtNvfp4, 2, 4>(a, grid, stream) : launch_fmt<kFmtMxfp4, 2, 4>(a, grid, stream);
+  if (a.tile_rows == 96) return nv ? launch_fmt<kFmtNvfp4, 1, 6>(a, grid, stream) : launch_fmt<kFmtMxfp4, 1, 6>(a, grid, stream);
+  return nv ? launch_fmt<kFmtNvfp4, 1, 4>(a, grid, stream) : launch_fmt<kFmtMxfp4, 1, 4>(a, grid, stream);
 }
 
 }  // namespace fp4

@@ -48,6 +48,13 @@ constexpr int kDecodeActMaxM = 16;
 // buffers (all but one in flight).
 constexpr int kDecodeStageK = 256;
 constexpr int kDecodeBuffers = 3;
+// Stage buffers of the 96-row MFMA decode tiles, whose launches give each CU
+// one workgroup, so LDS leaves room for a deeper pipeline: 4 for MXFP4, 3 for
+// NVFP4.  Measured on MI355X on the 24576 x 4096 fused gate_up (HIP-graph
+// replay, medians of repeated runs, us, 3 / 4 / 5 buffers): MXFP4 m = 4
+// 12.5 / 12.1 / 12.6, m = 8 12.5 / 12.1 / 12.7; NVFP4 m = 4 16.7 / 17.2 /
+// 17.5, m = 8 16.6 / 17.2 / 17.4.
+inline constexpr int decode_buffers_96(int fmt) { return fmt == kFmtMxfp4 ? 4 : kDecodeBuffers; }
 
 inline constexpr int group_size(int fmt) { return fmt == kFmtNvfp4 ? 16 : 32; }
 // Scale bytes per 32-code segment of a row: 2 for NVFP4, 1 for MXFP4.
@@ -176,16 +183,31 @@ inline bool decode_kw_used(int n_proj, int k, int fmt, int m) {
   return m >= 1 && ksteps <= kKwMaxSteps && (small_layer || mxfp4_gemv_rows);
 }
 
-// Rows of an MFMA-decode workgroup: 64 (one 16-row block per wave), or 128
-// (two blocks per wave, each x fragment read from LDS feeding two MFMAs: half
-// the x copies per weight byte) for layers of at least 2048 64-row tiles,
-// where 128-row tiles still leave thousands of workgroups.  Such layers are
-// never split along K (decode_mfma_splits), and the tile size changes which
-// rows a workgroup holds, never an output's summation order.
-// Calls of more than 8 rows keep 64-row tiles: their 16-row x stages would
-// leave the 128-row tile one workgroup per CU.
-inline int decode_mfma_tile_rows(int64_t rows_total, int m) {
-  return m <= 8 && rows_total / kDecodeTileRows >= 2048 ? 128 : 64;
+// Rows of an MFMA-decode workgroup: 64 (four waves of one 16-row block), 96
+// (six such waves) or 128 (four waves of two blocks, each x fragment read
+// from LDS feeding two MFMAs: half the x copies per weight byte).
+//  - 128 for layers of at least 2048 64-row tiles, where 128-row tiles still
+//    leave thousands of workgroups.  Such layers are never split along K
+//    (decode_mfma_splits).
+//  - 96 for unsplit layers whose 64-row tiles would give some CUs more
+//    workgroups than others and whose 96-row tiles put fewer rows on the
+//    busiest CU (the 24576-row fused gate_up: 384 64-row tiles leave half of
+//    the 256 CUs two, 256 96-row tiles give each CU one), with a third less
+//    x staged per weight byte than 64-row tiles.
+//  - 64 otherwise, and for calls of more than 8 rows: their 16-row x stages
+//    would leave larger tiles one workgroup per CU.
+// The tile size changes which rows a workgroup holds, never an output's
+// summation order (every wave streams its rows' stages in order), so the
+// choice may follow the total rows of a launch.
+inline int decode_mfma_tile_rows(int64_t rows_total, int m, int splits) {
+  if (m > 8) return 64;
+  if (rows_total / kDecodeTileRows >= 2048) return 128;
+  if (splits == 1 && rows_total % 96 == 0) {
+    const int64_t busiest64 = (rows_total / 64 + kTargetCUs - 1) / kTargetCUs * 64;
+    const int64_t busiest96 = (rows_total / 96 + kTargetCUs - 1) / kTargetCUs * 96;
+    if (busiest96 < busiest64) return 96;
+  }
+  return 64;
 }
 
 struct GemvArgs {

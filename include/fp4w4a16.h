@@ -69,7 +69,12 @@ enum fp4_status {
 /* Which kernel a call ran (filled when the caller passes a non-null pointer). */
 typedef struct fp4_dispatch_info {
   int kernel;  /* 0 = VALU decode GEMV (m = 1, 2), 2 = MFMA decode GEMV
-                  (m = 3..32; SwiGLU gate_up: m = 3..16), 1 = MFMA tile GEMM
+                  (m = 3..32; SwiGLU gate_up: m = 3..16; row tiles of 64
+                  rows, or at m <= 8 of 128 rows on launches of at least
+                  131072 rows and of 96 rows, 384 threads, on unsplit
+                  launches whose rows are a multiple of 96 that 64-row
+                  tiles would spread unevenly over 256 CUs, such as the
+                  2 x 12288-row gate_up), 1 = MFMA tile GEMM
                   (m > 32; SwiGLU gate_up: m > 16), 3 = grouped MoE decode,
                   4 = W4A4 MXFP4 tile GEMM (any m),
                   5 = grouped MoE tile GEMM (prefill),

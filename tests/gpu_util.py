@@ -84,3 +84,31 @@ def decode_kernel(fmt, n, k, m, act=False):
     if not act and m >= 1 and -(-k // 256) <= 32 and (small or mx_rows):
         return 6
     return 0 if m < 3 else 2
+
+
+def decode_splits(n, k):
+    """K splits of the MFMA decode (kernel 2) on a layer of n rows per
+    projection: none for at least 128 64-row tiles, else about 512 workgroups
+    per projection with at least 4 stages of 256 codes per split."""
+    tiles = -(-n // 256) * 256 // 64
+    if tiles >= 128:
+        return 1
+    return max(1, min(512 // tiles, -(-k // 256) // 4))
+
+
+def decode_tile_rows(n, k, m, proj):
+    """Rows per workgroup of the MFMA decode (kernel 2): 128 for launches of at
+    least 2048 64-row tiles, 96 (six waves) for unsplit launches whose rows are
+    a multiple of 96 and whose busiest of 256 CUs holds fewer rows on 96-row
+    tiles than on 64-row ones (both at m <= 8 only), else 64."""
+    rows = proj * (-(-n // 256) * 256)
+    if m > 8:
+        return 64
+    if rows // 64 >= 2048:
+        return 128
+    if decode_splits(n, k) == 1 and rows % 96 == 0:
+        busiest64 = -(-(rows // 64) // 256) * 64
+        busiest96 = -(-(rows // 96) // 256) * 96
+        if busiest96 < busiest64:
+            return 96
+    return 64

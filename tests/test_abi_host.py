@@ -182,12 +182,22 @@ def test_plan_follows_cu_count_only_in_the_xcd_deal():
     p = fp4.fp4_plan(4, 5120, 6144, MX, 2, 256)
     assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (6, 1, 640, 1)
     # The MXFP4 gate_up (2 x 12288 x 4096): the wave-split kernel at m = 1, 2
-    # (1536 workgroups), the 64-row MFMA decode from m = 3; NVFP4 keeps the GEMV.
+    # (1536 workgroups), the MFMA decode from m = 3: on 96-row tiles (256
+    # six-wave workgroups) at m = 3..8, on 64-row tiles from m = 9; the
+    # separate 12288-row halves keep 64-row tiles.  NVFP4 keeps the GEMV at
+    # m = 1, 2.
     for m in (1, 2):
         p = fp4.fp4_plan(m, 12288, 4096, MX, 2, 256)
         assert (p.kernel, p.splits, p.grid_x, p.grid_y) == (6, 1, 1536, 1)
         assert fp4.fp4_plan(m, 12288, 4096, NV, 2, 256).kernel == 0
-    assert fp4.fp4_plan(3, 12288, 4096, MX, 2, 256).as_dict()["kernel"] == 2
+    for m in range(3, 9):
+        for fmt in (NV, MX):
+            p = fp4.fp4_plan(m, 12288, 4096, fmt, 2, 256)
+            assert (p.kernel, p.splits, p.grid_x, p.grid_y, p.block) == (2, 1, 256, 1, 384)
+            p = fp4.fp4_plan(m, 12288, 4096, fmt, 1, 256)
+            assert (p.kernel, p.splits, p.grid_x, p.grid_y, p.block) == (2, 1, 192, 1, 256)
+    p = fp4.fp4_plan(9, 12288, 4096, MX, 2, 256)
+    assert (p.kernel, p.splits, p.grid_x, p.grid_y, p.block) == (2, 1, 384, 1, 256)
     assert fp4.fp4_plan(1, 16384, 4096, MX, 1, 256).kernel == 0      # 256 tiles
     assert fp4.fp4_plan(1, 12288, 8448, MX, 1, 256).kernel == 0      # 33 K stages
     p = fp4.fp4_plan(0, 512, 256, NV, 1, 256)
@@ -446,14 +456,22 @@ def test_decode_dispatch_rule_over_a_grid():
     # The decode kernel fp4_plan reports (the one the calls take, checked on
     # the GPU by test_gpu_plan) against the rule the GPU tests restate
     # (gpu_util.decode_kernel), over rows, k, formats, m and both layouts.
-    from gpu_util import decode_kernel
+    from gpu_util import decode_kernel, decode_splits, decode_tile_rows
+    tiles96 = 0
     for fmt in (NV, MX):
-        for n in (17, 300, 2048, 5120, 7936, 8192, 12288, 16128, 16384, 131072):
+        for n in (17, 300, 2048, 5120, 7936, 8192, 8448, 9216, 12288, 16128, 16384, 131072):
             for k in (32, 544, 1056, 6144, 8192, 8448, 17408):
                 for m in (1, 2, 3, 4, 8, 9, 16, 32):
                     for proj in (1, 2):
                         p = fp4.fp4_plan(m, n, k, fmt, proj, 256)
                         assert p.kernel == decode_kernel(fmt, n, k, m), (fmt, n, k, m, proj, p.as_dict())
+                        rows = proj * (-(-n // 256) * 256)
                         if p.kernel == 6:
-                            assert (p.splits, p.grid_x, p.block) == (1, proj * (-(-n // 256) * 256) // 16, 256)
+                            assert (p.splits, p.grid_x, p.block) == (1, rows // 16, 256)
                             assert fp4.fp4_workspace_bytes(m, n, k, fmt, proj) == 0
+                        if p.kernel == 2:
+                            tr = decode_tile_rows(n, k, m, proj)
+                            want = (decode_splits(n, k), rows // tr, decode_splits(n, k), 384 if tr == 96 else 256)
+                            assert (p.splits, p.grid_x, p.grid_y, p.block) == want, (fmt, n, k, m, proj, p.as_dict())
+                            tiles96 += tr == 96
+    assert tiles96 > 0

@@ -3,7 +3,7 @@ the oracle: exact on one-hot activations (the logits are then single weights,
 full of exact ties), and on random activations equal to the argmax of the
 unfused call's own logits, whose winner is also within the layer's tolerance
 of the oracle's maximum.  Covers the VALU GEMV (split and unsplit), the MFMA
-decode (64-row tiles split and unsplit, 128-row tiles), the wave-split MFMA
+decode (64-row tiles split and unsplit, 96- and 128-row tiles), the wave-split MFMA
 decode and poisoned workspaces."""
 
 import numpy as np
@@ -21,9 +21,10 @@ NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
 
 # (fmt, n, k): small layers (the wave-split kernel at m <= 8), k past 8192
 # (GEMV and MFMA decode split along K), MFMA unsplit 64-row tiles, MFMA
-# 128-row tiles; ragged n throughout.
+# 128-row tiles, MFMA 96-row tiles (16800 rows pad to 16896); ragged n
+# throughout.
 SHAPES = [(NV, 1000, 1024), (MX, 777, 5120), (NV, 5000, 2048), (NV, 1000, 9216), (MX, 9000, 512),
-          (NV, 131000, 256)]
+          (NV, 131000, 256), (MX, 16800, 544)]
 
 
 def _zero_canon(bits):

@@ -8,7 +8,7 @@ grouping a kernel adds them -- is a multiple of 2^-3 below 2^20 and exactly
 representable in float32.  Each output is then bf16(exact sum * G), one
 rounding, whatever the kernel: the oracle's float64 result rounded once to
 bf16 must equal the kernel's bits, on every kernel route (VALU GEMV, MFMA
-decode split and unsplit, wave-split MFMA decode with idle waves and ragged
+decode split and unsplit on 64- and 96-row tiles, wave-split MFMA decode with idle waves and ragged
 last stages, tile GEMM whole and with K-split tail tiles)."""
 
 import numpy as np
@@ -37,6 +37,8 @@ CASES = [
     (MX, 640, 9216, 2, 0),     # VALU GEMV, K split
     (NV, 640, 9216, 4, 2),     # MFMA decode, K split
     (MX, 8192, 1056, 8, 2),    # MFMA decode, unsplit
+    (NV, 16896, 1056, 8, 2),   # MFMA decode, 96-row tiles
+    (MX, 18432, 800, 4, 2),    # MFMA decode, 96-row tiles, ragged last stage
     (NV, 300, 1056, 16, 2),    # MFMA decode, 16 x rows
     (MX, 300, 1056, 24, 2),    # MFMA decode, two activation groups
     (NV, 512, 5120, 100, 1),   # tile GEMM, K-split tail tile

@@ -24,6 +24,7 @@ NV, MX = fp4.FMT_NVFP4, fp4.FMT_MXFP4
     (NV, 300, 5120, 8, False),    # wave-split MFMA decode
     (MX, 300, 5120, 24, True),    # MFMA decode, two 16-row activation groups, K split
     (MX, 8192, 1024, 4, False),   # MFMA decode, unsplit (128 row tiles)
+    (MX, 16896, 1024, 8, False),  # MFMA decode on 96-row tiles
     (NV, 512, 5120, 100, True),   # prefill GEMM, tail tiles split along K
 ])
 def test_graph_replay_matches_eager(fmt, n, k, m, split):
