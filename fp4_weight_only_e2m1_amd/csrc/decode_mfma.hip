@@ -15,8 +15,8 @@
 // workgroups fit a CU, and more workgroups beat deeper per-workgroup
 // pipelines):
 //   codes   64 rows x 128 bytes  (8 KiB: one full 128-byte line per row)
-//   x       XR rows x 256 bf16   (XR = 8, 16 or 32 for m <= 8, 16, 32: 4, 8
-//                                 or 16 KiB; rows >= m are never read back)
+//   x       XR rows x 256 bf16   (XR = 4, 8, 16 or 32 for m <= 4, 8, 16, 32:
+//                                 2 to 16 KiB; rows >= m are never read back)
 //   scales  of those codes       (1 KiB)
 // A wave then reads, per 128-code block, one 16-byte code chunk per lane,
 // decodes its 4 words and issues 4 MFMAs against x fragments read from LDS.
@@ -61,9 +61,13 @@ constexpr int kThreads = kDecodeThreads;  // 4 waves
 constexpr int kStageK = kDecodeStageK;     // 256 codes
 static_assert(kStageK == 256, "layout below assumes stages of 256 codes");
 
-// x rows staged per stage for calls of up to M activation rows.
+// x rows staged per stage for calls of up to M activation rows: the next
+// power of two from 4 (staging 4 rows instead of 8 at m = 3, 4 halves the x
+// copies; measured on MI355X, us: MXFP4 24576 x 4096 m = 4 12.1 -> 11.9,
+// the NVFP4 248320 x 5120 head m = 4 128.9 -> 127.0, NVFP4 5120 x 17408
+// m = 4 15.6 -> 15.0).
 template <int M>
-constexpr int kXRows = M > 16 ? 32 : M > 8 ? 16 : 8;
+constexpr int kXRows = M > 16 ? 32 : M > 8 ? 16 : M > 4 ? 8 : 4;
 // 16-row activation groups of an instance: one MFMA per group per fragment.
 template <int M>
 constexpr int kGroups = M > 16 ? 2 : 1;

@@ -69,6 +69,7 @@ LINEAR = [
     (NV, 640, 6144, 4, 6, False),     # wave-split MFMA decode
     (MX, 300, 1056, 8, 6, False),     # wave-split MFMA decode, ragged n and last stage
     (NV, 8192, 2048, 8, 2, False),    # MFMA decode (128 tiles: unsplit)
+    (MX, 16896, 544, 4, 2, False),    # MFMA decode on 96-row tiles
     (NV, 256, 17408, 4, 2, True),     # MFMA decode, K split
     (MX, 640, 1024, 24, 2, False),    # MFMA decode, two activation groups
     (NV, 1024, 1024, 200, 1, False),  # tile GEMM
