@@ -51,6 +51,22 @@ __device__ __forceinline__ int dp_tile_of(const GemmPlan& pl, int bid) {
   return xcd * q + (xcd < rr ? xcd : rr) + bid / nx;
 }
 
+// Position of workgroup `bid` among the workgroups [first, end) of a launch
+// when those are numbered XCD by XCD (all of XCD 0's in launch order, then
+// XCD 1's, ...; workgroup b runs on XCD b % nx), so that consecutive work
+// items given to consecutive positions share an XCD and its L2.  A bijection
+// of [first, end) onto [0, end - first).
+__device__ __forceinline__ int xcd_major_index(int bid, int first, int end, int nx) {
+  const int x = bid % nx;
+  int idx = 0;
+  for (int x2 = 0; x2 < x; ++x2) {
+    const int f = first + ((x2 - first % nx) + nx) % nx;  // first workgroup >= first on XCD x2
+    if (f < end) idx += (end - f + nx - 1) / nx;
+  }
+  const int fx = first + ((x - first % nx) + nx) % nx;
+  return idx + (bid - fx) / nx;
+}
+
 // Result stores through LDS.  In the MFMA result layout a lane holds 4
 // consecutive output columns of one activation row, and the 32 lanes of a
 // half-wave hold 32 different rows, so direct stores write 8-byte (bf16) or
