@@ -443,7 +443,8 @@ def _moe(name, x, prep_codes, prep_scales, n, experts, global_scales, fmt, exper
     _need(y, torch.bfloat16, "y")
     if y.numel() != pairs * n:
         raise ValueError("y must hold pairs x n values")
-    # The tile route reads x directly; only the decode route gathers the rows.
+    # Both routes read each pair's x row by its token id (the size query
+    # reports 0 bytes).
     need = 0 if name == "fp4_w4a16_moe_prefill" else fp4_moe_workspace_bytes(pairs, k)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)

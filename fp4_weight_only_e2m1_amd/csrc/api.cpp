@@ -350,13 +350,12 @@ int run_w4a4_nvfp4(const uint16_t* x, int m, int k, const uint8_t* codes, const 
 
 namespace {
 
-// Checks shared by the grouped MoE entry points (the workspace only where
-// the route gathers the x rows); FP4_OK with *no_pairs set means there is
+// Checks shared by the grouped MoE entry points (both routes read x by
+// token id and take no workspace); FP4_OK with *no_pairs set means there is
 // nothing to compute.
 int check_moe(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_codes_dev, const uint8_t* prep_scales_dev,
               int n, int experts, const float* global_scales_dev, int fmt, const int32_t* expert_offsets_dev,
-              const int32_t* pair_tokens_dev, int pairs, const uint16_t* y_dev, bool gathers, const void* workspace_dev,
-              size_t workspace_bytes, bool* no_pairs) {
+              const int32_t* pair_tokens_dev, int pairs, const uint16_t* y_dev, bool* no_pairs) {
   int st = check_fmt(fmt);
   if (st) return st;
   if ((st = check_nk(n, k))) return st;
@@ -372,21 +371,14 @@ int check_moe(const uint16_t* x_dev, int tokens, int k, const uint8_t* prep_code
       reinterpret_cast<uintptr_t>(expert_offsets_dev) % 4 != 0 || reinterpret_cast<uintptr_t>(pair_tokens_dev) % 4 != 0 ||
       (!mx && reinterpret_cast<uintptr_t>(global_scales_dev) % 4 != 0))
     return FP4_EALIGN;
-  if (!gathers) return FP4_OK;
-  size_t need = 0;
-  if ((st = fp4_moe_workspace_bytes(pairs, k, &need))) return st;
-  if (workspace_bytes < need) return FP4_EWORKSPACE;
-  if (!workspace_dev) return FP4_EINVAL;
-  if (!aligned16(workspace_dev)) return FP4_EALIGN;
   return FP4_OK;
 }
 
 fp4::MoeArgs moe_args(const fp4::PreparedShape& ps, int fmt, const float* global_scales_dev,
                       const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int tokens, int pairs,
-                      int experts, const void* workspace_dev) {
+                      int experts) {
   fp4::MoeArgs moe{};
   moe.offsets = expert_offsets_dev;
-  moe.x_sorted = static_cast<const uint16_t*>(workspace_dev);
   moe.tokens = pair_tokens_dev;
   moe.tokens_total = tokens;
   moe.gscales = fmt == FP4_FMT_MXFP4 ? nullptr : global_scales_dev;
@@ -410,7 +402,7 @@ int run_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_t* pre
                     uint16_t* y_dev, hipStream_t stream, fp4_dispatch_info* info_out) {
   bool no_pairs = false;
   const int st = check_moe(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n_proj, experts, global_scales_dev, fmt,
-                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, false, nullptr, 0, &no_pairs);
+                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, &no_pairs);
   if (st) return st;
   if (no_pairs) {
     if (info_out) *info_out = fp4_dispatch_info{5, 1, 0, 0, 0};
@@ -445,7 +437,7 @@ int run_moe_prefill(const uint16_t* x_dev, int tokens, int k, const uint8_t* pre
   a.act = act ? 1 : 0;
   a.plan = fp4::gemm_plan(fp4::kGemmBM, a.rows_total, k, xcds);  // only n_tiles, ksteps and xcds are used
   fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pair_tokens_dev, tokens, pairs,
-                              experts, nullptr);
+                              experts);
   moe.code_stride *= projections;
   moe.scale_stride *= projections;
   dim3 grid, block;
@@ -641,7 +633,7 @@ int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k, const uint8_t* 
 
 int fp4_moe_workspace_bytes(int pairs, int k, size_t* bytes_out) {
   if (pairs < 0 || pairs > FP4_MAX_M || k <= 0 || k > FP4_MAX_K || k % 32 != 0 || !bytes_out) return FP4_EINVAL;
-  *bytes_out = static_cast<size_t>(fp4::round_up(static_cast<int64_t>(pairs) * k * 2, 256));
+  *bytes_out = 0;  // the decode kernels fetch each pair's x row by its token id
   return FP4_OK;
 }
 
@@ -651,10 +643,11 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t
                          const int32_t* expert_offsets_dev, const int32_t* pair_tokens_dev, int pairs,
                          uint16_t* y_dev, void* workspace_dev, size_t workspace_bytes, hipStream_t stream,
                          fp4_dispatch_info* info_out) {
+  (void)workspace_dev;
+  (void)workspace_bytes;
   bool no_pairs = false;
   const int st = check_moe(x_dev, tokens, k, prep_codes_dev, prep_scales_dev, n, experts, global_scales_dev, fmt,
-                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, true, workspace_dev, workspace_bytes,
-                           &no_pairs);
+                           expert_offsets_dev, pair_tokens_dev, pairs, y_dev, &no_pairs);
   if (st) return st;
   if (no_pairs) {
     if (info_out) *info_out = fp4_dispatch_info{3, 1, 0, 0, 0};
@@ -663,6 +656,7 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t
 
   const fp4::PreparedShape ps = fp4::prepared_shape(n, k, fmt);
   fp4::GemvArgs a{};
+  a.x = x_dev;
   a.codes = prep_codes_dev;
   a.scales = prep_scales_dev;
   a.y = y_dev;
@@ -681,10 +675,9 @@ int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k, const uint8_t
   a.gscale[0] = a.gscale[1] = 1.0f;
   a.tile_rows = fp4::kDecodeTileRows;
   const fp4::MoeArgs moe = moe_args(ps, fmt, global_scales_dev, expert_offsets_dev, pair_tokens_dev, tokens, pairs,
-                                    experts, workspace_dev);
+                                    experts);
   dim3 grid, block;
-  const hipError_t e = fp4::launch_moe_decode(a, moe, experts, x_dev, pair_tokens_dev, tokens,
-                                              static_cast<uint16_t*>(workspace_dev), fmt, stream, &grid, &block);
+  const hipError_t e = fp4::launch_moe_decode(a, moe, experts, tokens, fmt, stream, &grid, &block);
   if (e != hipSuccess) return FP4_EHIP;
   if (info_out) *info_out = fp4_dispatch_info{3, 1, static_cast<int>(grid.x), static_cast<int>(grid.y),
                                               static_cast<int>(block.x)};

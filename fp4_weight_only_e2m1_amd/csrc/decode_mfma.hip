@@ -139,6 +139,31 @@ __device__ __forceinline__ void wait_stages_barrier(int wave) {
   }
 }
 
+// x row that activation row xr of a call (or of a grouped MoE pass) reads:
+// xr itself, or the pass's token id for it.  Rows past m (ok false) and
+// token ids outside [0, tokens_total) read row 0: the former are never
+// stored, the latter have their sums zeroed (bad_token_rows).
+__device__ __forceinline__ int x_row_of(const GemvArgs& a, int xr, bool ok) {
+  if (!ok) return 0;
+  if (!a.row_tokens) return xr;
+  const int tok = a.row_tokens[xr];
+  return tok < 0 || tok >= a.tokens_total ? 0 : tok;
+}
+
+// Bit r set: activation row r (< mrows <= 32) of a grouped MoE pass has a
+// token id outside [0, tokens_total), so its outputs are zero (the sums of a
+// zero x row).  0 outside the grouped MoE decode.  Workgroup-uniform.
+__device__ __forceinline__ uint32_t bad_token_rows(const GemvArgs& a, int mrows) {
+  uint32_t bad = 0;
+  if (a.row_tokens) {
+    for (int r = 0; r < mrows; ++r) {
+      const int tok = a.row_tokens[r];
+      if (tok < 0 || tok >= a.tokens_total) bad |= 1u << r;
+    }
+  }
+  return bad;
+}
+
 // The stage copies of one workgroup: 32-bit lane offsets from wave-uniform
 // bases that advance with k.  x rows >= m all fetch the first 16 bytes of x
 // (never read back).  In a stage that straddles k (k not a multiple of 256),
@@ -146,7 +171,7 @@ __device__ __forceinline__ void wait_stages_barrier(int wave) {
 // code rows: every code row then holds at least 32 zero codes from code k on.
 // Code chunks are fetched with the non-temporal hint (read once); x and the
 // scales with the default policy.
-template <int M, int FMT, int RB, int W>
+template <int M, int FMT, int RB, int W, bool GATHER = false>
 struct Copier {
   static constexpr int XR = kXRows<M>;
   using G = Geo<RB, FMT, XR, W>;
@@ -156,6 +181,7 @@ struct Copier {
   const uint8_t* st;     // scale row group row0 / 16
   const uint8_t* zeros;  // 16 zero bytes
   uint32_t woff[G::kWPer], xoff[G::kXPer], soff;
+  const uint8_t* xrp[GATHER ? G::kXPer : 1];  // GATHER: this lane's x chunk at k = 0
   int xk[G::kXPer];      // first code of this lane's x chunks within a stage
   bool xrow_ok[G::kXPer];
   int k;
@@ -182,7 +208,13 @@ struct Copier {
       const int xr = p >> 5;
       const int ch = (p & 31) ^ xr;
       xrow_ok[i] = xr < mrows;
-      xoff[i] = xrow_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
+      if constexpr (GATHER) {
+        xrp[i] = reinterpret_cast<const uint8_t*>(a.x + static_cast<int64_t>(x_row_of(a, xr, xrow_ok[i])) * a.k) +
+                 16 * ch;
+        xoff[i] = 0;
+      } else {
+        xoff[i] = xrow_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
+      }
       xk[i] = 8 * ch;
     }
     // Scales of a stage: RB W row groups x 8 segments x 16 rows x P bytes,
@@ -199,6 +231,13 @@ struct Copier {
     lds_swave = 64 * 16 * sv;
   }
 
+  __device__ __forceinline__ const void* x_src(int i, int64_t k0) const {
+    if constexpr (GATHER)
+      return xrp[i] + 2 * k0;
+    else
+      return reinterpret_cast<const uint8_t*>(x + k0) + xoff[i];
+  }
+
   __device__ __forceinline__ void issue(int64_t k0, Stage<RB, FMT, XR, W>& sb, int wave) const {
     const uint32_t lw = lds_addr(sb.w) + lds_wave;
     const uint8_t* cb = ct + k0 / 2;
@@ -209,7 +248,7 @@ struct Copier {
       for (int i = 0; i < G::kXPer; ++i) {
         const bool in_k = k0 + xk[i] < k;
         const void* xs = !xrow_ok[i] ? static_cast<const void*>(x)
-                         : in_k      ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff[i])
+                         : in_k      ? x_src(i, k0)
                                      : static_cast<const void*>(zeros);
         copy16_vaddr(xs, lds_addr(sb.x) + lds_wave + i * 64 * G::kXWaves * 16);
       }
@@ -327,8 +366,8 @@ __device__ __forceinline__ void wait_for_stage(int s, int s1, int wave) {
 // Step for stage s in buffer `cur`: wait for it at the workgroup barrier,
 // refill the buffer consumed one step ago (`prev`; every wave is past it)
 // with stage s + NB - 1, consume `cur`.
-template <int M, int FMT, int RB, int NB, int W>
-__device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB, W>& cp, int s, int s1,
+template <int M, int FMT, int RB, int NB, int W, bool GATHER>
+__device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB, W, GATHER>& cp, int s, int s1,
                                               const Stage<RB, FMT, kXRows<M>, W>& cur,
                                               Stage<RB, FMT, kXRows<M>, W>& prev, const uint4* zrow, int wave, int r,
                                               int g, int mrows, f32x4_t (&acc)[RB][kGroups<M>]) {
@@ -339,8 +378,9 @@ __device__ __forceinline__ void pipeline_step(const Copier<M, FMT, RB, W>& cp, i
 
 // One (tile, split) of a decode call with mrows <= M activation rows (M when
 // launched per call; the rows of one expert in the grouped MoE launch), on a
-// workgroup of W waves.
-template <int M, int FMT, int RB, int NB, int W>
+// workgroup of W waves; GATHER: the grouped MoE decode, activation row r
+// being x row a.row_tokens[r].
+template <int M, int FMT, int RB, int NB, int W, bool GATHER = false>
 __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int split, int mrows) {
   __shared__ Stage<RB, FMT, kXRows<M>, W> st[NB];
   __shared__ ZeroRow zero_row;
@@ -363,7 +403,8 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
 #pragma unroll
     for (int j = 0; j < J; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (t < 32) zero_row.z[t] = make_uint4(0u, 0u, 0u, 0u);  // visible after the first stage barrier
-  const Copier<M, FMT, RB, W> cp(a, row0, t, wave, mrows);
+  const uint32_t bad = GATHER ? bad_token_rows(a, mrows) : 0u;
+  const Copier<M, FMT, RB, W, GATHER> cp(a, row0, t, wave, mrows);
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j)
     if (s0 + j < s1) cp.issue(static_cast<int64_t>(s0 + j) * kStageK, st[j], wave);
@@ -371,13 +412,22 @@ __device__ __forceinline__ void decode_tile(const GemvArgs& a, int tile, int spl
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (s + j >= s1) break;
-      pipeline_step<M, FMT, RB, NB, W>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g,
+      pipeline_step<M, FMT, RB, NB, W, GATHER>(cp, s + j, s1, st[j], st[(j + NB - 1) % NB], zero_row.z, wave, r, g,
                                        mrows, acc);
     }
   }
 
   // Lane (r, g) holds C[m = 16j + 4g + i][row 16 (RB wave + b) + r] in
   // acc[b][j][i].
+  if (GATHER && bad) {
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((bad >> (16 * j + 4 * g + i)) & 1u) acc[b][j][i] = 0.0f;
+  }
   if (a.splits == 1) {
     // Greedy-argmax keys: lane (r, g) only ever holds activation rows
     // 16j + 4g .. 16j + 4g + 3, so each row's maximum is taken over the 16
@@ -495,7 +545,7 @@ struct alignas(16) KwStage {
   uint4 s[8 * scales_per_seg(FMT)];
 };
 
-template <int M, int FMT>
+template <int M, int FMT, bool GATHER = false>
 struct KwCopier {
   static constexpr int XR = kKwXRows<M>;
   static constexpr int P = scales_per_seg(FMT);
@@ -507,6 +557,7 @@ struct KwCopier {
   const uint8_t* st;     // scale row group row0 / 16
   const uint8_t* zeros;  // 16 zero bytes
   uint32_t woff[2], xoff[kXPer];
+  const uint8_t* xrp[GATHER ? kXPer : 1];  // GATHER: this lane's x chunk at k = 0
   int xk[kXPer];
   bool xrow_ok[kXPer];
   int k, lane;
@@ -532,9 +583,22 @@ struct KwCopier {
       const int xr = p >> 5;
       const int ch = (p & 31) ^ xr;
       xrow_ok[i] = xr < mrows;
-      xoff[i] = xrow_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
+      if constexpr (GATHER) {
+        xrp[i] = reinterpret_cast<const uint8_t*>(a.x + static_cast<int64_t>(x_row_of(a, xr, xrow_ok[i])) * a.k) +
+                 16 * ch;
+        xoff[i] = 0;
+      } else {
+        xoff[i] = xrow_ok[i] ? static_cast<uint32_t>((static_cast<int64_t>(xr) * a.k + 8 * ch) * 2) : 0u;
+      }
       xk[i] = 8 * ch;
     }
+  }
+
+  __device__ __forceinline__ const void* x_src(int i, int64_t k0) const {
+    if constexpr (GATHER)
+      return xrp[i] + 2 * k0;
+    else
+      return reinterpret_cast<const uint8_t*>(x + k0) + xoff[i];
   }
 
   // Copies of the stage at code k0 into sb: codes (non-temporal), x (chunks
@@ -549,7 +613,7 @@ struct KwCopier {
     for (int i = 0; i < kXPer; ++i) {
       const bool in_k = k0 + xk[i] < k;
       const void* xs = !xrow_ok[i] ? static_cast<const void*>(x)
-                       : in_k      ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(x + k0) + xoff[i])
+                       : in_k      ? x_src(i, k0)
                                    : static_cast<const void*>(zeros);
       copy16_vaddr(xs, lds_addr(sb.x) + i * 64 * 16);
     }
@@ -584,9 +648,9 @@ __device__ __forceinline__ void kw_wait(int s, int s1) {
 // launched per call; the rows of one expert's pass in the grouped MoE
 // launch).  All threads of the workgroup call it; it reuses its stage buffers
 // on the next call only after a workgroup barrier.
-template <int M, int FMT, int NB>
+template <int M, int FMT, int NB, bool GATHER = false>
 __device__ __forceinline__ void kw_tile(const GemvArgs& a, int64_t tile, int mrows) {
-  using C = KwCopier<M, FMT>;
+  using C = KwCopier<M, FMT, GATHER>;
   using S = KwStage<FMT, C::XR>;
   __shared__ S st[kKwWaves][NB];
   const int t = threadIdx.x;
@@ -602,6 +666,7 @@ __device__ __forceinline__ void kw_tile(const GemvArgs& a, int64_t tile, int mro
   f32x4_t acc[1][1];
   acc[0][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   S* mine = st[wave];
+  const uint32_t bad = GATHER ? bad_token_rows(a, mrows) : 0u;
   const C cp(a, row0, lane, mrows);
 #pragma unroll
   for (int j = 0; j < NB - 1; ++j)
@@ -620,6 +685,11 @@ __device__ __forceinline__ void kw_tile(const GemvArgs& a, int64_t tile, int mro
   // Every copy of this wave has landed (the last wait was for all of them),
   // so its first stage buffer takes its sums: lane (r, g) holds
   // C[m = 4 g + i][row r] in acc[0][0][i].
+  if (GATHER && bad) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if ((bad >> (4 * g + i)) & 1u) acc[0][0][i] = 0.0f;
+  }
   float* red = reinterpret_cast<float*>(&mine[0]);
   *reinterpret_cast<f32x4_t*>(red + 4 * lane) = acc[0][0];
   __syncthreads();
@@ -691,14 +761,16 @@ hipError_t launch_kw_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
 
 // Grouped MoE decode: workgroup (tile, s) computes 64-row tile `tile` of
 // the s-th expert that has routed pairs (in expert order) for its pairs
-// [offsets[e], offsets[e + 1]) -- their x rows gathered in pair order
-// (x_sorted) and their outputs at the same pair rows of y -- 8 pairs per pass.
+// [offsets[e], offsets[e + 1]) -- the stage copies fetch each pair's x row by
+// its token id (GemvArgs::row_tokens), and the outputs go to the same pair
+// rows of y -- 8 pairs per pass.
 // The grid has min(experts, pairs) slots, at least as many as experts with
 // pairs in any non-decreasing offset table, so idle experts cost no
 // workgroups; a slot past the last such expert exits.  Expert e's prepared
 // weight sits at e times the prepared size in the stacked buffers.  The
-// offsets are clamped to [0, pairs], so no routing table can make a workgroup
-// read or write outside x_sorted and y.
+// offsets are clamped to [0, pairs] and a token id outside [0, tokens_total)
+// reads zeros, so no routing table can make a workgroup read or write outside
+// x and y.
 __device__ __forceinline__ void moe_clamped_range(const MoeArgs& moe, int e, int& p0, int& p1) {
   p0 = moe.offsets[e];
   p1 = moe.offsets[e + 1];
@@ -764,10 +836,12 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kernel(const GemvArgs bas
   a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
   a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
   a.gscale[0] = a.gscale[1] = moe.gscales ? moe.gscales[e] : 1.0f;
+  a.tokens_total = moe.tokens_total;
   for (int c0 = p0; c0 < p1; c0 += kGemvMaxM) {
-    a.x = moe.x_sorted + static_cast<int64_t>(c0) * a.k;
+    a.row_tokens = moe.tokens + c0;
     a.y = base.y + static_cast<int64_t>(c0) * a.ldy;
-    decode_tile<kGemvMaxM, FMT, 1, kDecodeBuffers, 4>(a, blockIdx.x, 0, p1 - c0 < kGemvMaxM ? p1 - c0 : kGemvMaxM);
+    decode_tile<kGemvMaxM, FMT, 1, kDecodeBuffers, 4, true>(a, blockIdx.x, 0,
+                                                           p1 - c0 < kGemvMaxM ? p1 - c0 : kGemvMaxM);
     __syncthreads();  // the stage buffers are reused by the next pass
   }
 }
@@ -789,30 +863,13 @@ __global__ __launch_bounds__(kThreads) void moe_decode_kw_kernel(const GemvArgs 
   a.codes = base.codes + static_cast<int64_t>(e) * moe.code_stride;
   a.scales = base.scales + static_cast<int64_t>(e) * moe.scale_stride;
   a.gscale[0] = a.gscale[1] = moe.gscales ? moe.gscales[e] : 1.0f;
+  a.tokens_total = moe.tokens_total;
   for (int c0 = p0; c0 < p1; c0 += M) {
-    a.x = moe.x_sorted + static_cast<int64_t>(c0) * a.k;
+    a.row_tokens = moe.tokens + c0;
     a.y = base.y + static_cast<int64_t>(c0) * a.ldy;
-    kw_tile<M, FMT, kKwBuffers>(a, blockIdx.x, p1 - c0 < M ? p1 - c0 : M);
+    kw_tile<M, FMT, kKwBuffers, true>(a, blockIdx.x, p1 - c0 < M ? p1 - c0 : M);
     __syncthreads();  // the stage buffers are reused by the next pass
   }
-}
-
-// x_sorted[p] = x[tokens[p]]: 16-byte chunks, one per thread.  A token id
-// outside [0, tokens_total) gathers a zero row.
-__global__ __launch_bounds__(256) void moe_gather_kernel(const uint16_t* x, const int32_t* tokens, int pairs, int k,
-                                                         int tokens_total, uint16_t* x_sorted) {
-  const int64_t chunks = static_cast<int64_t>(k) / 8;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= chunks * pairs) return;
-  const int p = static_cast<int>(i / chunks);
-  const int64_t c = i - static_cast<int64_t>(p) * chunks;
-  const int tok = tokens[p];
-  if (tok < 0 || tok >= tokens_total) {
-    *reinterpret_cast<uint4*>(x_sorted + static_cast<int64_t>(p) * k + 8 * c) = make_uint4(0u, 0u, 0u, 0u);
-    return;
-  }
-  *reinterpret_cast<uint4*>(x_sorted + static_cast<int64_t>(p) * k + 8 * c) =
-      *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(tok) * k + 8 * c);
 }
 
 // Launch of the m-row instance on tiles of RB 16-row blocks per wave and W
@@ -872,19 +929,8 @@ hipError_t launch_fmt(const GemvArgs& a, dim3 grid, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_moe_gather(const uint16_t* x, const int32_t* tokens, int pairs, int k, int tokens_total,
-                             uint16_t* x_sorted, hipStream_t stream) {
-  const int64_t chunks = static_cast<int64_t>(pairs) * (k / 8);
-  hipLaunchKernelGGL(moe_gather_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0, stream, x,
-                     tokens, pairs, k, tokens_total, x_sorted);
-  return hipGetLastError();
-}
-
-hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, const uint16_t* x, const int32_t* tokens,
-                             int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid_out,
-                             dim3* block_out) {
-  hipError_t e = launch_moe_gather(x, tokens, moe.pairs, a.k, tokens_total, x_sorted, stream);
-  if (e != hipSuccess) return e;
+hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, int tokens_total, int fmt,
+                             hipStream_t stream, dim3* grid_out, dim3* block_out) {
   const int slots = experts < moe.pairs ? experts : moe.pairs;
   // One or two tokens: the experts the wave-split kernel takes at that m run on it.
   const bool kw = tokens_total <= 2 && decode_kw_used(a.n_proj, a.k, fmt, tokens_total);

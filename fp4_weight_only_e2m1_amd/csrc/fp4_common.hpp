@@ -233,13 +233,16 @@ struct GemvArgs {
   int64_t ldy;            // projections * n_proj
   float gscale[2];        // global scale per projection (1 for MXFP4)
   int tile_rows;          // rows per workgroup (the split-K finish tile)
+  // Grouped MoE decode: activation row r of a pass is x row row_tokens[r]
+  // (a token id outside [0, tokens_total) reads zeros); null: row r of x.
+  const int32_t* row_tokens;
+  int tokens_total;
 };
 
 // Grouped MoE decode: routed (token, expert) pairs sorted by expert.
 struct MoeArgs {
   const int32_t* offsets;    // [experts + 1]: expert e's pairs are [offsets[e], offsets[e + 1])
-  const uint16_t* x_sorted;  // bf16 [pairs][k]: x row of each pair (gathered; decode route)
-  const int32_t* tokens;     // [pairs]: x row of each pair (tile route, which reads x directly)
+  const int32_t* tokens;     // [pairs]: x row of each pair (both routes read x directly)
   int tokens_total;          // rows of x
   const float* gscales;      // [experts] NVFP4 global scales, or null (MXFP4)
   int64_t code_stride;       // bytes between experts' prepared codes
@@ -405,11 +408,8 @@ hipError_t launch_prepare_interleaved(const uint8_t* gate_codes, const uint8_t* 
 hipError_t launch_gemv(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_decode_mfma(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_decode_kw(const GemvArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
-hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, const uint16_t* x, const int32_t* tokens,
-                             int tokens_total, uint16_t* x_sorted, int fmt, hipStream_t stream, dim3* grid,
-                             dim3* block);
-hipError_t launch_moe_gather(const uint16_t* x, const int32_t* tokens, int pairs, int k, int tokens_total,
-                             uint16_t* x_sorted, hipStream_t stream);
+hipError_t launch_moe_decode(const GemvArgs& a, const MoeArgs& moe, int experts, int tokens_total, int fmt,
+                             hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_mfma(const MfmaArgs& a, int fmt, hipStream_t stream, dim3* grid, dim3* block);
 hipError_t launch_moe_gemm(const MfmaArgs& a, const MoeArgs& moe, int fmt, hipStream_t stream, dim3* grid,
                            dim3* block);

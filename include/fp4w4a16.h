@@ -315,12 +315,14 @@ int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k,
  *                      expert e's are [offsets[e], offsets[e + 1]);
  *   pair_tokens_dev    int32 [pairs]: the token (row of x) of each pair;
  *   y_dev              bf16 [pairs][n];
- *   workspace_dev      fp4_moe_workspace_bytes(pairs, k) (the gathered x rows).
+ *   workspace_dev / workspace_bytes  unused (fp4_moe_workspace_bytes reports
+ *                      0 bytes); may be NULL / 0.
  * Device-side routing data is not validated on the host: offsets are clamped
  * to [0, pairs] and a token id outside [0, tokens) reads a zero row, so no
- * table can make the kernels access memory outside these buffers.  Two
- * launches: a gather of the pairs' x rows, then one workgroup per (row tile,
- * expert with pairs) on the matrix cores: the m = 3..8 decode kernel on
+ * table can make the kernels access memory outside these buffers.  One
+ * launch: a workgroup per (row tile, expert with pairs) on the matrix cores,
+ * whose stage copies fetch each pair's x row by its token id: the m = 3..8
+ * decode kernel on
  * 64-row tiles, up to 8 pairs of an expert per pass; with one or two tokens
  * (tokens <= 2), on experts the wave-split kernel takes at m = tokens, that
  * kernel on 16-row tiles, up to `tokens` pairs per pass, each pair's output
@@ -337,6 +339,13 @@ int fp4_w4a16_linear_argmax(const uint16_t* x_dev, int m, int k,
  * per-expert product; "re-verify 27B NVFP4 on the nvidia ModelOpt checkpoint"
  * (vllm.cpp PR #178), section on the 35B result: the MoE model's grouped
  * W4A16 operations have their own test gates.
+ */
+/*
+ * Workspace of fp4_w4a16_moe_decode for `pairs` routed pairs of k values:
+ * 0 bytes, since the kernels fetch each pair's x row by its token id.
+ * FP4_EINVAL for pairs or k out of range or k not a multiple of 32.
+ * Host utility (no passage defines it): pure host function, never touches the
+ * GPU.
  */
 int fp4_moe_workspace_bytes(int pairs, int k, size_t* bytes_out);
 int fp4_w4a16_moe_decode(const uint16_t* x_dev, int tokens, int k,
