@@ -406,7 +406,10 @@ def run_moe(args, torch, np, fp4, synth):
         total_bytes += d["bytes"] * args.steps
         total_flops += d["flops"] * args.steps
         info = d["info"]
-        row = {"m": d["m"], "kernel": kname, "us_per_launch": round(us, 3),
+        # The decode route runs the wave-split kernel (16-row tiles) for one or two tokens where it serves.
+        kw = not prefill and info.grid_x * 16 == (n + 255) // 256 * 256
+        row = {"m": d["m"], "kernel": kname.replace("moe_decode_kernel", "moe_decode_kw_kernel") if kw else kname,
+               "us_per_launch": round(us, 3),
                "gbs": round(d["bytes"] / (us * 1e-6) / 1e9, 2), "tflops": round(d["flops"] / (us * 1e-6) / 1e12, 3),
                "pairs": d["pairs"], "active_experts": len(d["active"]),
                "grid": [info.grid_x, info.grid_y], "block": info.block, "algorithmic_bytes": d["bytes"],
