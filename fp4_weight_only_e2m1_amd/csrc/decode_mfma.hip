@@ -74,7 +74,7 @@ constexpr int kGroups = M > 16 ? 2 : 1;
 
 // Tile geometry for W waves of RB row blocks of 16 (a 16 RB W-row tile) and
 // XR staged x rows.  Every lane copies 2 RB code chunks per stage; the x
-// chunks are copied one per lane by the first kXWaves waves (all of them
+// chunks are copied kXPer per lane by the first kXWaves waves (all of them
 // when there are at least as many chunks as lanes), and the scale chunks by
 // kSWaves waves from kSWave0 on -- waves without x copies where there are
 // enough of those, so that the copies per wave stay even.

@@ -234,7 +234,8 @@ struct GemvArgs {
   float gscale[2];        // global scale per projection (1 for MXFP4)
   int tile_rows;          // rows per workgroup (the split-K finish tile)
   // Grouped MoE decode: activation row r of a pass is x row row_tokens[r]
-  // (a token id outside [0, tokens_total) reads zeros); null: row r of x.
+  // (a token id outside [0, tokens_total) gives zero outputs); null: row r
+  // of x.
   const int32_t* row_tokens;
   int tokens_total;
 };
