@@ -151,6 +151,40 @@ def test_moe_out_of_range_routing_is_contained():
     assert_close(got[[0, 2]], ref[[0, 2]], "moe clamped")
 
 
+@pytest.mark.parametrize("fmt", [NV, MX])
+def test_moe_bad_token_ids_on_64_row_tiles(fmt):
+    # Five tokens (the 64-row tile route): pairs whose token id lies outside
+    # x give exactly zero outputs, one expert mixing good and bad pairs in a
+    # pass; the good pairs match the oracle, and each equals bit for bit the
+    # dense call on its expert's weight at m = 9 (the unsplit 64-row MFMA
+    # decode, the route's summation order; the dense call takes the
+    # wave-split kernel at m <= 8 on this layer).
+    n, k, experts, tokens = 320, 1056, 3, 5
+    host, pc, ps, gs = _stacked(experts, n, k, fmt, 13)
+    xbits = synth.activations(synth.TINY, tokens, k)
+    offsets = np.array([0, 3, 7, 9], dtype=np.int32)
+    ptok = np.array([4, -1, 0, 2, 5, 1, 1 << 20, 3, -7], dtype=np.int32)
+    good = [0, 2, 3, 5, 7]
+    info = fp4.fp4_dispatch_info()
+    y = fp4.fp4_w4a16_moe_decode(x_dev(xbits), pc, ps, n, experts, gs if fmt == NV else None, fmt, _i32(offsets),
+                                 _i32(ptok), info=info)
+    assert info.kernel == 3 and info.grid_x == 512 // 64, info.as_dict()
+    bits = y_host_bits(y)
+    for p in (1, 4, 6, 8):
+        assert (bits[p] & 0x7FFF == 0).all(), p
+    ref = oracle.moe_decode(oracle.bf16_bits_to_f32(xbits), host, k, fmt, offsets, np.where(
+        (ptok >= 0) & (ptok < tokens), ptok, 0))
+    assert_close(oracle.bf16_bits_to_f32(bits[good]).astype(np.float64), ref[good], "moe bad tokens")
+    for p in good:
+        e = int(np.searchsorted(offsets, p, side="right") - 1)
+        x9 = np.repeat(xbits[ptok[p]:ptok[p] + 1], 9, axis=0)
+        dinfo = fp4.fp4_dispatch_info()
+        w = fp4.fp4_w4a16_linear(x_dev(x9), pc[e * pc.numel() // experts:], ps[e * ps.numel() // experts:], n,
+                                 float(host[e][2]), fmt, info=dinfo)
+        assert (dinfo.kernel, dinfo.splits, dinfo.grid_x) == (2, 1, 512 // 64), dinfo.as_dict()
+        assert np.array_equal(y_host_bits(w)[0], bits[p]), p
+
+
 def test_moe_no_pairs_is_a_no_op():
     fmt, n, k = NV, 256, 512
     _, pc, ps, gs = _stacked(2, n, k, fmt, 11)
